@@ -1,0 +1,10 @@
+"""CPU float64 oracle for the KDA state recurrence — test infrastructure.
+
+Only tests, the package's smoke check and the benchmark's CPU-baseline leg may
+import this package.  The GPU library never imports it and it imports nothing
+from the GPU library.  Every function is pinned by the CPU-only tests in
+tests/test_oracle_pins.py against closed forms, brute force and the values the
+pages print.
+"""
+from .kda_oracle import *  # noqa: F401,F403
+from .kda_oracle import __all__  # noqa: F401
