@@ -1,0 +1,201 @@
+/*
+ * kda.h — C ABI of the KDA (Kimi Delta Attention) state-recurrence library
+ * for AMD MI355X (gfx950).
+ *
+ * Pages cited (titles as published; sections as named on the page):
+ *   [Serve demo]  "【轻量化复刻大模型 / KIMI K3】Serve 模块交互式演示"
+ *   [KDA cache]   "Kimi Linear 的 KDA 缓存：SGLang、vLLM 与 Mooncake Store 全链路"
+ *
+ * The recurrence, per head, with state S (dk x dv, fp32):
+ *   decay    S~ = diag(exp(a_t)) S                 a_t: one log-decay per key channel
+ *   error    d  = v_t - S~^T k_t                   (formed after the decay)
+ *   write    S  = S~ + beta_t k_t d^T
+ *   readout  o_t = S^T q_t                         (after the write)
+ * [KDA cache] "KDA 的递推与充分状态" fixes decay-then-error; [Serve demo] §1.3
+ * bounds a_t to [g_min, 0] (a log value, hence the exp) and beta_t to [0, 1].
+ *
+ * Conventions shared by every entry point
+ *  - Tensors are caller-owned device memory (any allocator), dense row-major,
+ *    in the shapes stated per call.  The library never allocates device
+ *    memory; the prefill work list lives in a caller-provided workspace.
+ *  - Token-indexed tensors are token-packed: q, k, a [T, H, dk], v [T, H, dv],
+ *    beta [T, H], o [T, H, dv].
+ *  - States are fp32 in the canonical layout [.., H, dk, dv] (dv fastest).
+ *  - Inputs q, k, v, a, beta share one dtype (KDA_F32 or KDA_BF16); the
+ *    output o has that dtype too.  Arithmetic is fp32 (prefill contractions
+ *    take bf16 operands with fp32 accumulation; see kda_chunk_prefill).
+ *  - Supported head sizes: dk, dv in {16, 32, 64, 128}.
+ *  - stream is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *    work; they return before it runs.  They hold no state between calls and
+ *    may be called from several host threads.
+ *  - Errors: every argument a call can see on the host is validated before
+ *    anything is enqueued, so a non-zero status means nothing was written.
+ *    Values that live in device memory (n_accepted, slots) cannot be checked
+ *    there; they are checked by the kernel, which skips the offending item
+ *    and raises *err_flag (when err_flag is not NULL).  No call throws.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_EINVAL = -1,       /* a bad shape, size, pointer or offset array        */
+  KDA_EUNSUPPORTED = -2, /* valid request outside what the kernels cover      */
+  KDA_EALIAS = -3,       /* an output overlaps an input that must stay intact */
+  KDA_EWORKSPACE = -4,   /* workspace missing or smaller than required        */
+  KDA_EHIP = -5          /* the HIP runtime reported an error on enqueue      */
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/* State layouts: KV = [.., dk, dv] (canonical), VK = [.., dv, dk] (the
+ * transposed layout some kernels and state pools use, [KDA cache] "先统一记号"). */
+typedef enum { KDA_LAYOUT_KV = 0, KDA_LAYOUT_VK = 1 } kda_layout;
+
+/* Version of the page layout written by pack and by checkpoint emission. */
+#define KDA_PAGE_LAYOUT_VERSION 1
+
+const char* kda_status_string(int status);
+
+/* Text describing the most recent failure on the calling host thread ("" if
+ * none).  The pointer stays valid until the next call on that thread. */
+const char* kda_last_error(void);
+
+/* Largest chunk the prefill accepts, and the chunk it is tuned for. */
+#define KDA_MAX_CHUNK 64
+
+/*
+ * kda_snapshot_cost_ratio — bytes of one per-step state snapshot over bytes of
+ * one per-step draft projection, H*dk*dv / (H*(3*dk + dv + 1)); independent of
+ * the draft length ([Serve demo] §1.1).  Host-only helper; returns a negative
+ * value for non-positive sizes.
+ */
+double kda_snapshot_cost_ratio(int32_t H, int32_t dk, int32_t dv);
+
+/*
+ * kda_decode_step — one token per session, state updated IN PLACE
+ * ([Serve demo] §1.3 kda_step).
+ *   q, k, a : [B, H, dk]   v : [B, H, dv]   beta : [B, H]   (in_dtype)
+ *   state   : [B, H, dk, dv] fp32, read and overwritten
+ *   o       : [B, H, dv] (in_dtype), must not overlap state or the inputs
+ * B may be 0 (nothing is enqueued).
+ */
+int kda_decode_step(const void* q, const void* k, const void* v, const void* a,
+                    const void* beta, kda_dtype in_dtype, int32_t B, int32_t H,
+                    int32_t dk, int32_t dv, float* state, void* o, void* stream);
+
+/*
+ * kda_verify_and_replay — clone the committed state and replay the first
+ * n_accepted[b] draft steps of session b ([Serve demo] §1.2; Tab 3 §6.4 for
+ * the n = partial / all / 0 cases).
+ *   committed : [B, H, dk, dv] fp32, READ ONLY (shared in the cache; never written)
+ *   q, k, a   : [t_draft, B, H, dk]   v : [t_draft, B, H, dv]   beta : [t_draft, B, H]
+ *               (the draft-projection layout (draft, B, H, D), [Serve demo] Tab 4)
+ *   n_accepted: device int32 [B]; values outside 0..t_draft are clamped and
+ *               raise *err_flag
+ *   s_new     : [B, H, dk, dv] fp32, the state after n_accepted[b] steps
+ *               (a bit-exact copy of committed[b] when n_accepted[b] = 0)
+ *   o         : [B, H, t_draft, dv] (in_dtype); rows i >= n_accepted[b] are 0
+ *   err_flag  : device int32, may be NULL; set to 1 on a clamped n_accepted
+ * s_new and o must not overlap committed (KDA_EALIAS) nor each other.
+ */
+int kda_verify_and_replay(const float* committed, const void* q, const void* k,
+                          const void* v, const void* a, const void* beta,
+                          kda_dtype in_dtype, const int32_t* n_accepted, int32_t B,
+                          int32_t H, int32_t dk, int32_t dv, int32_t t_draft,
+                          float* s_new, void* o, int32_t* err_flag, void* stream);
+
+/*
+ * kda_pack_heads — write state[b] into page slot slot[b] of a flat page pool,
+ * head after head, and zero the rest of the page ([Serve demo] §1.5 pack_heads
+ * and Tab 7 store_kda: "the rest of the page is zero padding").
+ *   state     : [B, H, dk, dv] (KV) or [B, H, dv, dk] (VK), fp32
+ *   slot      : device int32 [B]; out-of-range slots are skipped and raise *err_flag
+ *   page_pool : fp32 [n_slots, page_elems], page_elems >= H*dk*dv
+ *   Page element h*dk*dv + i*dv + j holds S[h, i, j] (i over dk, j over dv).
+ * Distinct b must name distinct slots (not checked: slots live on the device).
+ */
+int kda_pack_heads(const float* state, kda_layout src_layout, int32_t B, int32_t H,
+                   int32_t dk, int32_t dv, const int32_t* slot, float* page_pool,
+                   int64_t page_elems, int64_t n_slots, int32_t* err_flag, void* stream);
+
+/* kda_unpack_heads — the inverse: page slot slot[b] -> state[b] in dst_layout.
+ * Bit-exact ([Serve demo] §1.5 unpack_heads, "lossless"). */
+int kda_unpack_heads(const float* page_pool, int64_t page_elems, int64_t n_slots,
+                     const int32_t* slot, int32_t B, int32_t H, int32_t dk, int32_t dv,
+                     kda_layout dst_layout, float* state, int32_t* err_flag, void* stream);
+
+/*
+ * kda_chunk_prefill — token-packed variable-length prefill from committed
+ * states, with exact checkpoints written into page slots.
+ *
+ * The chunked form ([KDA cache] "预填充为什么能分块并行": transitions inside a
+ * chunk are diagonal-minus-rank-one and compress, through a WY representation
+ * and a UT transform, into matrix products plus a small lower-triangular
+ * solve) gives the recurrence's result up to rounding.  Contractions use bf16
+ * MFMA operands with fp32 accumulation; the state is carried in fp32.
+ *
+ *   q, k, a  : [T_tot, H, dk]   v : [T_tot, H, dv]   beta : [T_tot, H]  (in_dtype)
+ *   chunk    : 1..KDA_MAX_CHUNK, a multiple of 16 (64 is the tuned size)
+ *   cu_seqlens_host : host int32 [n_seqs + 1]; cu[0] = 0, non-decreasing,
+ *              cu[n_seqs] = T_tot.  Zero-length sequences are allowed.
+ *   s0       : [n_seqs, H, dk, dv] fp32 committed states, READ ONLY, or NULL
+ *              for zero states.  Outputs must not overlap it (KDA_EALIAS).
+ *   o        : [T_tot, H, dv] (in_dtype)
+ *   s_final  : [n_seqs, H, dk, dv] fp32 or NULL
+ *   Checkpoints ([KDA cache] "Kimi K3 预览版与 vLLM 的细粒度检查点": one slot
+ *   holds one exact boundary, e.g. the tail C(P6976)):
+ *   ckpt_cu_host   : host int32 [n_seqs + 1], offsets into the two arrays below
+ *                    (NULL when n_ckpt = 0)
+ *   ckpt_pos_host  : host int32 [n_ckpt]; per sequence strictly increasing token
+ *                    counts p, 1 <= p <= len: the state after exactly p tokens
+ *   ckpt_slot_host : host int32 [n_ckpt]; page slot of each checkpoint, distinct,
+ *                    0 <= slot < n_slots
+ *   page_pool      : fp32 [n_slots, page_elems], page_elems >= H*dk*dv; a slot
+ *                    is written in the pack layout and zero-padded
+ *   workspace      : device memory of at least kda_chunk_prefill_workspace_size
+ *                    bytes, 256-byte aligned; contents on entry are ignored
+ * Sizes: T_tot < 2^31 tokens, H*dk*dv < 2^31.
+ */
+int kda_chunk_prefill_workspace_size(int32_t n_seqs, int64_t total_tokens, int32_t H,
+                                     int32_t dk, int32_t dv, int32_t chunk, int64_t n_ckpt,
+                                     size_t* bytes);
+
+int kda_chunk_prefill(const void* q, const void* k, const void* v, const void* a,
+                      const void* beta, kda_dtype in_dtype, int32_t H, int32_t dk,
+                      int32_t dv, int32_t chunk, const int32_t* cu_seqlens_host,
+                      int32_t n_seqs, const float* s0, void* o, float* s_final,
+                      const int32_t* ckpt_cu_host, const int32_t* ckpt_pos_host,
+                      const int32_t* ckpt_slot_host, int64_t n_ckpt, float* page_pool,
+                      int64_t page_elems, int64_t n_slots, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/*
+ * kda_chunk_prefill_split — kda_chunk_prefill with an explicit number of
+ * workgroups per (sequence, head) chain: the dv columns of the state are
+ * independent in the recurrence (column j of S depends only on column j of
+ * v), so a chain can be split into dv_split column tiles that each redo the
+ * key-side chunk work.  dv_split in {1, 2, 4, 8} with dv / dv_split a
+ * multiple of 16, or 0 to let the library choose from the sequence lengths.
+ */
+int kda_chunk_prefill_split(const void* q, const void* k, const void* v, const void* a,
+                            const void* beta, kda_dtype in_dtype, int32_t H, int32_t dk,
+                            int32_t dv, int32_t chunk, const int32_t* cu_seqlens_host,
+                            int32_t n_seqs, const float* s0, void* o, float* s_final,
+                            const int32_t* ckpt_cu_host, const int32_t* ckpt_pos_host,
+                            const int32_t* ckpt_slot_host, int64_t n_ckpt, float* page_pool,
+                            int64_t page_elems, int64_t n_slots, void* workspace,
+                            size_t workspace_bytes, int32_t dv_split, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

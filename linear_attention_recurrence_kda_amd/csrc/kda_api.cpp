@@ -1,0 +1,221 @@
+// The extern "C" entry points of include/kda.h: argument validation (all of
+// it before the first enqueue, so a failing call writes nothing), the prefill
+// work list, and dispatch to the kernel launchers.
+#include "../../include/kda.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <numeric>
+#include <string>
+#include <unordered_set>
+#include <vector>
+
+#include "kda_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return KDA_OK;
+}
+
+bool supported_dim(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+size_t elem_size(kda_dtype t) { return t == KDA_BF16 ? 2 : 4; }
+
+bool valid_dtype(int t) { return t == KDA_F32 || t == KDA_BF16; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+  const void* p;
+  size_t bytes;
+  const char* name;
+};
+
+bool overlap(const Range& x, const Range& y) {
+  if (x.p == nullptr || y.p == nullptr || x.bytes == 0 || y.bytes == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(x.p), a1 = a0 + x.bytes;
+  const uintptr_t b0 = reinterpret_cast<uintptr_t>(y.p), b1 = b0 + y.bytes;
+  return a0 < b1 && b0 < a1;
+}
+
+// Every output must be disjoint from every input and from every other output.
+int check_disjoint(const std::vector<Range>& outs, const std::vector<Range>& ins) {
+  for (size_t i = 0; i < outs.size(); ++i) {
+    for (const Range& in : ins)
+      if (overlap(outs[i], in))
+        return fail(KDA_EALIAS, "output '%s' overlaps input '%s'", outs[i].name, in.name);
+    for (size_t j = i + 1; j < outs.size(); ++j)
+      if (overlap(outs[i], outs[j]))
+        return fail(KDA_EALIAS, "outputs '%s' and '%s' overlap", outs[i].name, outs[j].name);
+  }
+  return KDA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(KDA_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+constexpr int64_t kMaxGridY = 65535;
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(int status) {
+  switch (status) {
+    case KDA_OK: return "ok";
+    case KDA_EINVAL: return "invalid argument";
+    case KDA_EUNSUPPORTED: return "unsupported configuration";
+    case KDA_EALIAS: return "output aliases a protected input";
+    case KDA_EWORKSPACE: return "workspace missing or too small";
+    case KDA_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* kda_last_error(void) { return g_last_error.c_str(); }
+
+double kda_snapshot_cost_ratio(int32_t H, int32_t dk, int32_t dv) {
+  if (H <= 0 || dk <= 0 || dv <= 0) return -1.0;
+  const double snap = static_cast<double>(H) * dk * dv;
+  const double proj = static_cast<double>(H) * (3.0 * dk + dv + 1.0);
+  return snap / proj;
+}
+
+int kda_decode_step(const void* q, const void* k, const void* v, const void* a,
+                    const void* beta, kda_dtype in_dtype, int32_t B, int32_t H, int32_t dk,
+                    int32_t dv, float* state, void* o, void* stream) {
+  if (!valid_dtype(in_dtype)) return fail(KDA_EINVAL, "in_dtype %d", static_cast<int>(in_dtype));
+  if (B < 0 || H <= 0) return fail(KDA_EINVAL, "B=%d H=%d", B, H);
+  if (!supported_dim(dk) || !supported_dim(dv))
+    return fail(KDA_EUNSUPPORTED, "dk=%d dv=%d (supported: 16, 32, 64, 128)", dk, dv);
+  if (B == 0) return ok();
+  if (!q || !k || !v || !a || !beta || !state || !o) return fail(KDA_EINVAL, "null pointer");
+  if (!aligned16(state)) return fail(KDA_EINVAL, "state must be 16-byte aligned");
+  const size_t es = elem_size(in_dtype), bh = static_cast<size_t>(B) * H;
+  const std::vector<Range> ins = {{q, bh * dk * es, "q"},   {k, bh * dk * es, "k"},
+                                  {v, bh * dv * es, "v"},   {a, bh * dk * es, "a"},
+                                  {beta, bh * es, "beta"}};
+  int st = check_disjoint({{state, bh * dk * dv * 4, "state"}, {o, bh * dv * es, "o"}}, ins);
+  if (st) return st;
+  kda::SweepArgs p{};
+  p.s_in = state;
+  p.s_out = state;
+  p.q = q; p.k = k; p.v = v; p.a = a; p.beta = beta;
+  p.n_accepted = nullptr;
+  p.t_draft = 1; p.B = B; p.H = H; p.dk = dk; p.dv = dv;
+  p.bf16 = in_dtype == KDA_BF16;
+  p.o = o; p.o_steps = 1;
+  p.err_flag = nullptr;
+  p.stream = static_cast<hipStream_t>(stream);
+  return hip_status(kda::launch_sweep(p), "decode launch");
+}
+
+int kda_verify_and_replay(const float* committed, const void* q, const void* k, const void* v,
+                          const void* a, const void* beta, kda_dtype in_dtype,
+                          const int32_t* n_accepted, int32_t B, int32_t H, int32_t dk,
+                          int32_t dv, int32_t t_draft, float* s_new, void* o,
+                          int32_t* err_flag, void* stream) {
+  if (!valid_dtype(in_dtype)) return fail(KDA_EINVAL, "in_dtype %d", static_cast<int>(in_dtype));
+  if (B < 0 || H <= 0 || t_draft <= 0) return fail(KDA_EINVAL, "B=%d H=%d t_draft=%d", B, H, t_draft);
+  if (!supported_dim(dk) || !supported_dim(dv))
+    return fail(KDA_EUNSUPPORTED, "dk=%d dv=%d (supported: 16, 32, 64, 128)", dk, dv);
+  if (B == 0) return ok();
+  if (!committed || !q || !k || !v || !a || !beta || !n_accepted || !s_new || !o)
+    return fail(KDA_EINVAL, "null pointer");
+  if (!aligned16(committed) || !aligned16(s_new))
+    return fail(KDA_EINVAL, "committed and s_new must be 16-byte aligned");
+  const size_t es = elem_size(in_dtype), bh = static_cast<size_t>(B) * H;
+  const size_t tb = static_cast<size_t>(t_draft) * bh;
+  const std::vector<Range> ins = {
+      {committed, bh * dk * dv * 4, "committed"}, {q, tb * dk * es, "q"}, {k, tb * dk * es, "k"},
+      {v, tb * dv * es, "v"}, {a, tb * dk * es, "a"}, {beta, tb * es, "beta"},
+      {n_accepted, static_cast<size_t>(B) * 4, "n_accepted"}};
+  std::vector<Range> outs = {{s_new, bh * dk * dv * 4, "s_new"}, {o, tb * dv * es, "o"}};
+  if (err_flag) outs.push_back({err_flag, 4, "err_flag"});
+  int st = check_disjoint(outs, ins);
+  if (st) return st;
+  kda::SweepArgs p{};
+  p.s_in = committed;
+  p.s_out = s_new;
+  p.q = q; p.k = k; p.v = v; p.a = a; p.beta = beta;
+  p.n_accepted = n_accepted;
+  p.t_draft = t_draft; p.B = B; p.H = H; p.dk = dk; p.dv = dv;
+  p.bf16 = in_dtype == KDA_BF16;
+  p.o = o; p.o_steps = t_draft;
+  p.err_flag = err_flag;
+  p.stream = static_cast<hipStream_t>(stream);
+  return hip_status(kda::launch_sweep(p), "replay launch");
+}
+
+static int pack_common(const float* src, float* dst, kda_layout layout, int32_t B, int32_t H,
+                       int32_t dk, int32_t dv, const int32_t* slot, int64_t page_elems,
+                       int64_t n_slots, int32_t* err_flag, bool unpack, void* stream) {
+  if (layout != KDA_LAYOUT_KV && layout != KDA_LAYOUT_VK)
+    return fail(KDA_EINVAL, "layout %d", static_cast<int>(layout));
+  if (B < 0 || H <= 0 || n_slots < 0) return fail(KDA_EINVAL, "B=%d H=%d n_slots=%lld", B, H,
+                                                  static_cast<long long>(n_slots));
+  if (!supported_dim(dk) || !supported_dim(dv))
+    return fail(KDA_EUNSUPPORTED, "dk=%d dv=%d (supported: 16, 32, 64, 128)", dk, dv);
+  const int64_t hkv = static_cast<int64_t>(H) * dk * dv;
+  if (page_elems < hkv) return fail(KDA_EINVAL, "page_elems %lld < H*dk*dv %lld",
+                                    static_cast<long long>(page_elems), static_cast<long long>(hkv));
+  if (page_elems % 4) return fail(KDA_EUNSUPPORTED, "page_elems must be a multiple of 4");
+  if (B > kMaxGridY || H > kMaxGridY) return fail(KDA_EUNSUPPORTED, "B or H above 65535");
+  if (B == 0) return ok();
+  if (!src || !dst || !slot) return fail(KDA_EINVAL, "null pointer");
+  if (!aligned16(src) || !aligned16(dst)) return fail(KDA_EINVAL, "buffers must be 16-byte aligned");
+  const size_t state_bytes = static_cast<size_t>(B) * hkv * 4;
+  const size_t pool_bytes = static_cast<size_t>(n_slots) * page_elems * 4;
+  const Range state_r{unpack ? dst : src, state_bytes, "state"};
+  const Range pool_r{unpack ? src : dst, pool_bytes, "page_pool"};
+  const Range slot_r{slot, static_cast<size_t>(B) * 4, "slot"};
+  std::vector<Range> outs = {unpack ? state_r : pool_r};
+  if (err_flag) outs.push_back({err_flag, 4, "err_flag"});
+  int st = check_disjoint(outs, {unpack ? pool_r : state_r, slot_r});
+  if (st) return st;
+  kda::PackArgs p{};
+  p.src = src; p.dst = dst; p.slot = slot;
+  p.B = B; p.H = H; p.dk = dk; p.dv = dv;
+  p.vk = layout == KDA_LAYOUT_VK;
+  p.unpack = unpack;
+  p.page_elems = page_elems; p.n_slots = n_slots;
+  p.err_flag = err_flag;
+  p.stream = static_cast<hipStream_t>(stream);
+  return hip_status(kda::launch_pack(p), unpack ? "unpack launch" : "pack launch");
+}
+
+int kda_pack_heads(const float* state, kda_layout src_layout, int32_t B, int32_t H, int32_t dk,
+                   int32_t dv, const int32_t* slot, float* page_pool, int64_t page_elems,
+                   int64_t n_slots, int32_t* err_flag, void* stream) {
+  return pack_common(state, page_pool, src_layout, B, H, dk, dv, slot, page_elems, n_slots,
+                     err_flag, false, stream);
+}
+
+int kda_unpack_heads(const float* page_pool, int64_t page_elems, int64_t n_slots,
+                     const int32_t* slot, int32_t B, int32_t H, int32_t dk, int32_t dv,
+                     kda_layout dst_layout, float* state, int32_t* err_flag, void* stream) {
+  return pack_common(page_pool, state, dst_layout, B, H, dk, dv, slot, page_elems, n_slots,
+                     err_flag, true, stream);
+}
+
+}  // extern "C"

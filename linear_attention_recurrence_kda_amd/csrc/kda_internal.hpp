@@ -1,0 +1,58 @@
+// Host-side launch interface between the C ABI layer (kda_api.cpp) and the
+// kernel files.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+// Decode (t_draft = 1, n_accepted = nullptr, s_in == s_out) and replay.
+struct SweepArgs {
+  const float* s_in;
+  float* s_out;
+  const void *q, *k, *v, *a, *beta;
+  const int32_t* n_accepted;  // nullptr: every session runs t_draft steps
+  int t_draft, B, H, dk, dv;
+  bool bf16;
+  void* o;
+  int o_steps;  // rows per (b, h) in o: 1 for decode, t_draft for replay
+  int32_t* err_flag;
+  hipStream_t stream;
+};
+hipError_t launch_sweep(const SweepArgs& p);
+
+// Pack (state -> pages) and unpack (pages -> state).
+struct PackArgs {
+  const float* src;
+  float* dst;
+  const int32_t* slot;
+  int B, H, dk, dv;
+  bool vk;      // the state side uses the [.., dv, dk] layout
+  bool unpack;  // pages -> state
+  int64_t page_elems, n_slots;
+  int32_t* err_flag;
+  hipStream_t stream;
+};
+hipError_t launch_pack(const PackArgs& p);
+
+// Chunked prefill.  The work list (device, inside the workspace) is built by
+// the host layer; see kda_prefill.hip for its format.
+struct PrefillArgs {
+  const void *q, *k, *v, *a, *beta;
+  bool bf16;
+  int H, dk, dv, chunk;
+  const float* s0;
+  void* o;
+  float* s_final;
+  float* page_pool;
+  int64_t page_elems;
+  const int32_t* work;  // device work list
+  int n_chains;         // (sequence, head) chains, padded to a multiple of 8
+  int dv_tiles;         // workgroups per chain (split of dv)
+  hipStream_t stream;
+};
+hipError_t launch_prefill(const PrefillArgs& p);
+
+}  // namespace kda

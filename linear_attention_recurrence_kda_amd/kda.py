@@ -1,0 +1,270 @@
+"""Thin Python binding of the KDA C ABI (include/kda.h) over ctypes.
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, their pointers and the current HIP stream are passed to the
+library, and a non-zero status raises KDAError with the library's message.
+Every step of the computation runs in the HIP kernels of libkda.so; there is
+no fallback.  If the library has not been built, loading it raises.
+"""
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkda.so")
+
+KDA_OK, KDA_EINVAL, KDA_EUNSUPPORTED, KDA_EALIAS, KDA_EWORKSPACE, KDA_EHIP = 0, -1, -2, -3, -4, -5
+KDA_F32, KDA_BF16 = 0, 1
+KDA_LAYOUT_KV, KDA_LAYOUT_VK = 0, 1
+
+_vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_i32p = ctypes.POINTER(ctypes.c_int32)
+
+# name -> (restype, argtypes); mirrors include/kda.h
+SIGNATURES = {
+    "kda_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "kda_last_error": (ctypes.c_char_p, []),
+    "kda_snapshot_cost_ratio": (ctypes.c_double, [_i32, _i32, _i32]),
+    "kda_decode_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int, _i32, _i32, _i32,
+                                       _i32, _vp, _vp, _vp]),
+    "kda_verify_and_replay": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _i32,
+                                             _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "kda_pack_heads": (ctypes.c_int, [_vp, ctypes.c_int, _i32, _i32, _i32, _i32, _vp, _vp, _i64,
+                                      _i64, _vp, _vp]),
+    "kda_unpack_heads": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i32, _i32, _i32, _i32, ctypes.c_int,
+                                        _vp, _vp, _vp]),
+    "kda_chunk_prefill_workspace_size": (ctypes.c_int, [_i32, _i64, _i32, _i32, _i32, _i32, _i64,
+                                                        ctypes.POINTER(_sz)]),
+    "kda_chunk_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int, _i32, _i32, _i32,
+                                         _i32, _i32p, _i32, _vp, _vp, _vp, _i32p, _i32p, _i32p,
+                                         _i64, _vp, _i64, _i64, _vp, _sz, _vp]),
+    "kda_chunk_prefill_split": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int, _i32, _i32,
+                                               _i32, _i32, _i32p, _i32, _vp, _vp, _vp, _i32p, _i32p,
+                                               _i32p, _i64, _vp, _i64, _i64, _vp, _sz, _i32, _vp]),
+}
+
+_lib = None
+_bound = {}
+
+
+class KDAError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"KDA status {status}: {message}")
+        self.status = status
+
+
+class _Lib:
+    """libkda.so with each entry point typed from SIGNATURES on first use."""
+
+    def __init__(self, cdll):
+        self._cdll = cdll
+
+    def __getattr__(self, name):
+        fn = _bound.get(name)
+        if fn is None:
+            res, args = SIGNATURES[name]
+            fn = getattr(self._cdll, name)
+            fn.restype, fn.argtypes = res, args
+            _bound[name] = fn
+        return fn
+
+
+def lib():
+    """Load libkda.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m linear_attention_recurrence_kda_amd.build`")
+        _lib = _Lib(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def _check(status):
+    if status != KDA_OK:
+        msg = lib().kda_last_error().decode()
+        raise KDAError(status, msg or lib().kda_status_string(status).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return KDA_F32
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    raise TypeError(f"inputs must be float32 or bfloat16, got {t.dtype}")
+
+
+def _expect(t, shape, dtype, name, device):
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _i32_array(seq):
+    arr = (ctypes.c_int32 * max(1, len(seq)))(*[int(x) for x in seq])
+    return arr
+
+
+def snapshot_cost_ratio(H, dk, dv):
+    return lib().kda_snapshot_cost_ratio(H, dk, dv)
+
+
+def decode_step(q, k, v, a, beta, state, o=None):
+    """One token per session; state [B,H,dk,dv] fp32 is updated in place.
+    q, k, a [B,H,dk], v [B,H,dv], beta [B,H]; returns o [B,H,dv]."""
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    for t, shp, n in ((q, (B, H, dk), "q"), (k, (B, H, dk), "k"), (a, (B, H, dk), "a"),
+                      (v, (B, H, dv), "v"), (beta, (B, H), "beta")):
+        _expect(t, shp, dt, n, dev)
+    _expect(state, (B, H, dk, dv), torch.float32, "state", dev)
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=dt, device=dev)
+    _expect(o, (B, H, dv), dt, "o", dev)
+    _check(lib().kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta), _dtype_code(q),
+                                 B, H, dk, dv, _ptr(state), _ptr(o), _stream(dev)))
+    return o
+
+
+def verify_and_replay(committed, q, k, v, a, beta, n_accepted, s_new=None, o=None, err_flag=None):
+    """Clone committed [B,H,dk,dv] and replay n_accepted[b] draft steps.
+    Projections in (t_draft, B, H, D) layout; n_accepted int32 [B] on the device.
+    Returns (s_new [B,H,dk,dv] fp32, o [B,H,t_draft,dv])."""
+    Td, B, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    for t, shp, n in ((q, (Td, B, H, dk), "q"), (k, (Td, B, H, dk), "k"),
+                      (a, (Td, B, H, dk), "a"), (v, (Td, B, H, dv), "v"),
+                      (beta, (Td, B, H), "beta")):
+        _expect(t, shp, dt, n, dev)
+    _expect(committed, (B, H, dk, dv), torch.float32, "committed", dev)
+    _expect(n_accepted, (B,), torch.int32, "n_accepted", dev)
+    if s_new is None:
+        s_new = torch.empty_like(committed)
+    if o is None:
+        o = torch.empty((B, H, Td, dv), dtype=dt, device=dev)
+    _expect(s_new, (B, H, dk, dv), torch.float32, "s_new", dev)
+    _expect(o, (B, H, Td, dv), dt, "o", dev)
+    if err_flag is not None:
+        _expect(err_flag, (1,), torch.int32, "err_flag", dev)
+    _check(lib().kda_verify_and_replay(_ptr(committed), _ptr(q), _ptr(k), _ptr(v), _ptr(a),
+                                       _ptr(beta), _dtype_code(q), _ptr(n_accepted), B, H, dk, dv,
+                                       Td, _ptr(s_new), _ptr(o), _ptr(err_flag), _stream(dev)))
+    return s_new, o
+
+
+def pack_heads(state, slot, page_pool, layout=KDA_LAYOUT_KV, err_flag=None, dk=None, dv=None):
+    """state [B,H,dk,dv] (KV) or [B,H,dv,dk] (VK) fp32 -> page_pool[slot[b]] (zero padded)."""
+    B, H = state.shape[:2]
+    if layout == KDA_LAYOUT_KV:
+        dk, dv = state.shape[2], state.shape[3]
+    else:
+        dv, dk = state.shape[2], state.shape[3]
+    dev = state.device
+    _expect(state, tuple(state.shape), torch.float32, "state", dev)
+    _expect(slot, (B,), torch.int32, "slot", dev)
+    n_slots, page_elems = page_pool.shape
+    _expect(page_pool, (n_slots, page_elems), torch.float32, "page_pool", dev)
+    if err_flag is not None:
+        _expect(err_flag, (1,), torch.int32, "err_flag", dev)
+    _check(lib().kda_pack_heads(_ptr(state), layout, B, H, dk, dv, _ptr(slot), _ptr(page_pool),
+                                page_elems, n_slots, _ptr(err_flag), _stream(dev)))
+    return page_pool
+
+
+def unpack_heads(page_pool, slot, H, dk, dv, layout=KDA_LAYOUT_KV, state=None, err_flag=None):
+    """page_pool[slot[b]] -> state [B,H,dk,dv] (KV) or [B,H,dv,dk] (VK) fp32."""
+    dev = page_pool.device
+    B = slot.shape[0]
+    n_slots, page_elems = page_pool.shape
+    _expect(page_pool, (n_slots, page_elems), torch.float32, "page_pool", dev)
+    _expect(slot, (B,), torch.int32, "slot", dev)
+    shp = (B, H, dk, dv) if layout == KDA_LAYOUT_KV else (B, H, dv, dk)
+    if state is None:
+        state = torch.empty(shp, dtype=torch.float32, device=dev)
+    _expect(state, shp, torch.float32, "state", dev)
+    if err_flag is not None:
+        _expect(err_flag, (1,), torch.int32, "err_flag", dev)
+    _check(lib().kda_unpack_heads(_ptr(page_pool), page_elems, n_slots, _ptr(slot), B, H, dk, dv,
+                                  layout, _ptr(state), _ptr(err_flag), _stream(dev)))
+    return state
+
+
+def prefill_workspace_size(n_seqs, total_tokens, H, dk, dv, chunk, n_ckpt):
+    out = ctypes.c_size_t(0)
+    _check(lib().kda_chunk_prefill_workspace_size(n_seqs, total_tokens, H, dk, dv, chunk, n_ckpt,
+                                                  ctypes.byref(out)))
+    return out.value
+
+
+def chunk_prefill(q, k, v, a, beta, cu_seqlens, s0=None, chunk=64, checkpoints=None,
+                  ckpt_slots=None, page_pool=None, o=None, s_final=None, want_final=True,
+                  workspace=None, dv_split=0):
+    """Token-packed varlen prefill.
+
+    q, k, a [T,H,dk], v [T,H,dv], beta [T,H] (float32 or bfloat16, same dtype)
+    cu_seqlens: host sequence of N+1 offsets; s0 [N,H,dk,dv] fp32 or None
+    checkpoints: per sequence a list of token counts (or None);
+    ckpt_slots: per sequence a list of page slots, same shape as checkpoints;
+    page_pool [n_slots, page_elems] fp32 receives the checkpoint states.
+    Returns (o [T,H,dv], s_final [N,H,dk,dv] or None).
+    """
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    for t, shp, n in ((q, (T, H, dk), "q"), (k, (T, H, dk), "k"), (a, (T, H, dk), "a"),
+                      (v, (T, H, dv), "v"), (beta, (T, H), "beta")):
+        _expect(t, shp, dt, n, dev)
+    cu = [int(x) for x in cu_seqlens]
+    N = len(cu) - 1
+    if s0 is not None:
+        _expect(s0, (N, H, dk, dv), torch.float32, "s0", dev)
+    if o is None:
+        o = torch.empty((T, H, dv), dtype=dt, device=dev)
+    _expect(o, (T, H, dv), dt, "o", dev)
+    if s_final is None and want_final:
+        s_final = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    if s_final is not None:
+        _expect(s_final, (N, H, dk, dv), torch.float32, "s_final", dev)
+    ck_cu, ck_pos, ck_slot = [0], [], []
+    if checkpoints is not None:
+        if ckpt_slots is None or page_pool is None:
+            raise ValueError("checkpoints need ckpt_slots and page_pool")
+        if len(checkpoints) != N or len(ckpt_slots) != N:
+            raise ValueError("checkpoints and ckpt_slots need one list per sequence")
+        for pos, sl in zip(checkpoints, ckpt_slots):
+            if len(pos) != len(sl):
+                raise ValueError("each sequence needs one slot per checkpoint")
+            ck_pos += list(pos)
+            ck_slot += list(sl)
+            ck_cu.append(len(ck_pos))
+    else:
+        ck_cu = [0] * (N + 1)
+    n_ckpt = len(ck_pos)
+    n_slots, page_elems = (0, 0) if page_pool is None else page_pool.shape
+    if page_pool is not None:
+        _expect(page_pool, (n_slots, page_elems), torch.float32, "page_pool", dev)
+    need = prefill_workspace_size(N, T, H, dk, dv, chunk, n_ckpt)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    fn = lib().kda_chunk_prefill_split
+    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta), _dtype_code(q), H, dk, dv, chunk,
+              _i32_array(cu), N, _ptr(s0), _ptr(o), _ptr(s_final), _i32_array(ck_cu),
+              _i32_array(ck_pos), _i32_array(ck_slot), n_ckpt, _ptr(page_pool), page_elems,
+              n_slots, _ptr(workspace), workspace.numel(), dv_split, _stream(dev)))
+    return o, s_final

@@ -1,0 +1,49 @@
+"""Tolerances of the GPU-vs-oracle parity tests.
+
+fp32 inputs and outputs: max |got - want| <= 1e-4 * max |want| (outputs and
+states).  bf16 inputs with an fp32 state: relative Frobenius error
+||got - want|| / ||want|| <= 1e-2.  The oracle always reads the inputs exactly
+as the GPU does (bf16 values rounded once by the input generator).
+"""
+import numpy as np
+import torch
+
+FP32_MAXABS_REL = 1e-4
+BF16_FROB_REL = 1e-2
+
+
+def to_np(t):
+    if isinstance(t, torch.Tensor):
+        return t.detach().float().cpu().numpy().astype(np.float64)
+    return np.asarray(t, dtype=np.float64)
+
+
+def max_abs_rel(got, want):
+    got, want = to_np(got), to_np(want)
+    scale = np.max(np.abs(want))
+    return float(np.max(np.abs(got - want)) / scale) if scale > 0 else float(np.max(np.abs(got)))
+
+
+def frob_rel(got, want):
+    got, want = to_np(got), to_np(want)
+    n = np.linalg.norm(want)
+    return float(np.linalg.norm(got - want) / n) if n > 0 else float(np.linalg.norm(got))
+
+
+def assert_parity(got, want, dtype, what=""):
+    if dtype == "fp32":
+        e = max_abs_rel(got, want)
+        assert e <= FP32_MAXABS_REL, f"{what}: max-abs error {e:.3e} x max|want| > {FP32_MAXABS_REL}"
+    else:
+        e = frob_rel(got, want)
+        assert e <= BF16_FROB_REL, f"{what}: relative Frobenius error {e:.3e} > {BF16_FROB_REL}"
+    return e
+
+
+def dev_tensor(x, dtype, device="cuda"):
+    """float32 numpy -> device tensor of the run dtype ("fp32" or "bf16"; exact for
+    values the input generator already rounded to bf16)."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+    return t.to(device)

@@ -1,0 +1,90 @@
+"""CPU-only checks of the C ABI: the library loads, exports every entry point
+that include/kda.h declares, and rejects bad arguments with a status before it
+touches the GPU (no kernel is launched by these tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_attention_recurrence_kda_amd import kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+           if f.endswith(".h")]
+
+
+def _declared():
+    names = set()
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"^[A-Za-z_][\w \*]*?\b(kda_\w+)\s*\(", text, flags=re.M))
+    return names
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(kda.LIB_PATH):
+        pytest.fail("libkda.so is not built (python -m linear_attention_recurrence_kda_amd.build)")
+    return kda.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert {"kda_chunk_prefill", "kda_decode_step", "kda_verify_and_replay", "kda_pack_heads",
+            "kda_unpack_heads", "kda_chunk_prefill_workspace_size"} <= names
+    cdll = ctypes.CDLL(kda.LIB_PATH)
+    missing = [n for n in sorted(names) if not hasattr(cdll, n)]
+    assert not missing, f"declared but not exported: {missing}"
+    assert set(kda.SIGNATURES) == names, "binding signatures out of sync with the header"
+
+
+def test_status_strings_and_ratio(L):
+    assert L.kda_status_string(0) == b"ok"
+    assert L.kda_status_string(-3).startswith(b"output aliases")
+    assert abs(L.kda_snapshot_cost_ratio(16, 32, 32) - 1024 / 129) < 1e-15
+    assert abs(L.kda_snapshot_cost_ratio(2, 8, 8) - 64 / 33) < 1e-15
+    assert L.kda_snapshot_cost_ratio(0, 8, 8) < 0
+
+
+P = ctypes.c_void_p
+
+
+def _fake(i):
+    return P(0x10000000 * (i + 1))  # distinct, never dereferenced
+
+
+def test_decode_validation(L):
+    q, k, v, a, b, s, o = (_fake(i) for i in range(7))
+    assert L.kda_decode_step(q, k, v, a, b, 0, 2, 2, 24, 16, s, o, None) == kda.KDA_EUNSUPPORTED
+    assert L.kda_decode_step(q, k, v, a, b, 0, -1, 2, 16, 16, s, o, None) == kda.KDA_EINVAL
+    assert L.kda_decode_step(q, k, v, a, b, 7, 2, 2, 16, 16, s, o, None) == kda.KDA_EINVAL
+    assert L.kda_decode_step(None, k, v, a, b, 0, 2, 2, 16, 16, s, o, None) == kda.KDA_EINVAL
+    # o overlapping the state
+    assert L.kda_decode_step(q, k, v, a, b, 0, 2, 2, 16, 16, s, s, None) == kda.KDA_EALIAS
+    assert b"overlap" in L.kda_last_error()
+    # misaligned state
+    assert L.kda_decode_step(q, k, v, a, b, 0, 2, 2, 16, 16, P(0x10000004), o, None) == kda.KDA_EINVAL
+    # empty batch: nothing to do, status ok
+    assert L.kda_decode_step(q, k, v, a, b, 0, 0, 2, 16, 16, s, o, None) == kda.KDA_OK
+
+
+def test_replay_validation(L):
+    c, q, k, v, a, b, n, s, o = (_fake(i) for i in range(9))
+    args = lambda **kw: [kw.get("c", c), q, k, v, a, b, 0, n, 2, 2, 16, 16, kw.get("td", 4),
+                         kw.get("s", s), kw.get("o", o), None, None]
+    assert L.kda_verify_and_replay(*args(td=0)) == kda.KDA_EINVAL
+    assert L.kda_verify_and_replay(*args(s=c)) == kda.KDA_EALIAS
+    assert L.kda_verify_and_replay(*args(o=c)) == kda.KDA_EALIAS
+    assert L.kda_verify_and_replay(*args(o=s)) == kda.KDA_EALIAS
+
+
+def test_pack_validation(L):
+    st, sl, pool = _fake(0), _fake(1), _fake(2)
+    H, d = 2, 16
+    assert L.kda_pack_heads(st, 0, 1, H, d, d, sl, pool, H * d * d - 4, 4, None, None) == kda.KDA_EINVAL
+    assert L.kda_pack_heads(st, 0, 1, H, d, d, sl, pool, H * d * d + 2, 4, None, None) == kda.KDA_EUNSUPPORTED
+    assert L.kda_pack_heads(st, 5, 1, H, d, d, sl, pool, H * d * d, 4, None, None) == kda.KDA_EINVAL
+    assert L.kda_pack_heads(st, 0, 1, H, d, d, sl, st, H * d * d, 4, None, None) == kda.KDA_EALIAS
+    assert L.kda_unpack_heads(pool, H * d * d, 4, sl, 1, H, d, d, 0, pool, None, None) == kda.KDA_EALIAS
