@@ -143,7 +143,13 @@ int kda_unpack_heads(const float* page_pool, int64_t page_elems, int64_t n_slots
  * MFMA operands with fp32 accumulation; the state is carried in fp32.
  *
  *   q, k, a  : [T_tot, H, dk]   v : [T_tot, H, dv]   beta : [T_tot, H]  (in_dtype)
- *   chunk    : 1..KDA_MAX_CHUNK, a multiple of 16 (64 is the tuned size)
+ *   chunk    : a multiple of 16 up to KDA_MAX_CHUNK (64 is the tuned size for
+ *              bf16); fp32 inputs take at most 32 (their operands stay fp32,
+ *              split into bf16 high and low parts, so fp32 I/O keeps
+ *              fp32-level accuracy)
+ *   Log-decays must satisfy a >= -160/chunk per token and channel (a >= -2.5
+ *   at chunk 64): the chunk's scaled operands, referenced to the middle row of
+ *   the chunk, then stay below e^80 and are finite in bf16 and fp32.
  *   cu_seqlens_host : host int32 [n_seqs + 1]; cu[0] = 0, non-decreasing,
  *              cu[n_seqs] = T_tot.  Zero-length sequences are allowed.
  *   s0       : [n_seqs, H, dk, dv] fp32 committed states, READ ONLY, or NULL

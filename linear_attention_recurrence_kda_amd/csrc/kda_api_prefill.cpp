@@ -1,0 +1,244 @@
+// extern "C" prefill entry points: validation of every host-visible argument,
+// the device work list (built on the host, copied into the caller's
+// workspace), the choice of dv split, and the launch.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <numeric>
+#include <unordered_set>
+#include <vector>
+
+#include "kda_hostutil.hpp"
+#include "kda_internal.hpp"
+
+using namespace kda_host;
+
+namespace {
+
+constexpr int kCUs = 256;  // MI355X compute units (one prefill workgroup per CU)
+
+int64_t round8(int64_t x) { return (x + 7) / 8 * 8; }
+
+size_t work_ints(int32_t n_seqs, int32_t H, int64_t n_ckpt) {
+  return static_cast<size_t>(2 * round8(static_cast<int64_t>(n_seqs) * H) + 4 * n_seqs + 2 * n_ckpt);
+}
+
+bool valid_tile(int32_t dv, int32_t split) {
+  if (split != 1 && split != 2 && split != 4 && split != 8) return false;
+  if (dv % split) return false;
+  const int t = dv / split;
+  return t == 16 || t == 32 || t == 64;
+}
+
+// Chunks of one sequence: chunks never cross a checkpoint position.
+int64_t seq_chunks(int32_t len, const int32_t* pos, int32_t npos, int32_t chunk) {
+  int64_t c = 0;
+  int32_t prev = 0;
+  for (int32_t i = 0; i <= npos; ++i) {
+    const int32_t next = i < npos ? pos[i] : len;
+    c += (next - prev + chunk - 1) / chunk;
+    prev = next;
+  }
+  return c;
+}
+
+// Pick the dv split from a per-chunk cost model (MFMA tile counts): key-side
+// work (Gram products, W) is repeated by every split, value-side work scales
+// with the tile width; the chip time is the larger of the total work over the
+// CUs and the longest chain.
+int choose_split(int32_t dk, int32_t dv, int64_t total_chunks, int64_t max_chunks) {
+  int best = 0;
+  double best_t = 0;
+  for (int split : {1, 2, 4, 8}) {
+    if (!valid_tile(dv, split)) continue;
+    const double tile = static_cast<double>(dv) / split;
+    const double cost = 1.5 * dk + (3.0 * dk / 8 + 12.0) * tile / 16.0;
+    const double t = std::max(static_cast<double>(total_chunks) * split * cost / kCUs,
+                              static_cast<double>(max_chunks) * cost);
+    if (best == 0 || t < best_t * 0.999) {
+      best = split;
+      best_t = t;
+    }
+  }
+  return best;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_chunk_prefill_workspace_size(int32_t n_seqs, int64_t total_tokens, int32_t H, int32_t dk,
+                                     int32_t dv, int32_t chunk, int64_t n_ckpt, size_t* bytes) {
+  if (!bytes) return fail(KDA_EINVAL, "bytes is null");
+  if (n_seqs < 0 || total_tokens < 0 || H <= 0 || n_ckpt < 0)
+    return fail(KDA_EINVAL, "n_seqs=%d total_tokens=%lld H=%d n_ckpt=%lld", n_seqs,
+                static_cast<long long>(total_tokens), H, static_cast<long long>(n_ckpt));
+  if (!supported_dim(dk) || !supported_dim(dv))
+    return fail(KDA_EUNSUPPORTED, "dk=%d dv=%d (supported: 16, 32, 64, 128)", dk, dv);
+  if (chunk < 16 || chunk > KDA_MAX_CHUNK || chunk % 16)
+    return fail(KDA_EUNSUPPORTED, "chunk=%d (a multiple of 16 up to %d)", chunk, KDA_MAX_CHUNK);
+  *bytes = (work_ints(n_seqs, H, n_ckpt) * 4 + 255) / 256 * 256;
+  return ok();
+}
+
+int kda_chunk_prefill_split(const void* q, const void* k, const void* v, const void* a,
+                            const void* beta, kda_dtype in_dtype, int32_t H, int32_t dk,
+                            int32_t dv, int32_t chunk, const int32_t* cu, int32_t n_seqs,
+                            const float* s0, void* o, float* s_final, const int32_t* ck_cu,
+                            const int32_t* ck_pos, const int32_t* ck_slot, int64_t n_ckpt,
+                            float* page_pool, int64_t page_elems, int64_t n_slots,
+                            void* workspace, size_t workspace_bytes, int32_t dv_split,
+                            void* stream) {
+  if (!valid_dtype(in_dtype)) return fail(KDA_EINVAL, "in_dtype %d", static_cast<int>(in_dtype));
+  if (n_seqs < 0 || H <= 0 || n_ckpt < 0)
+    return fail(KDA_EINVAL, "n_seqs=%d H=%d n_ckpt=%lld", n_seqs, H, static_cast<long long>(n_ckpt));
+  if (!supported_dim(dk) || !supported_dim(dv))
+    return fail(KDA_EUNSUPPORTED, "dk=%d dv=%d (supported: 16, 32, 64, 128)", dk, dv);
+  if (chunk < 16 || chunk > KDA_MAX_CHUNK || chunk % 16)
+    return fail(KDA_EUNSUPPORTED, "chunk=%d (a multiple of 16 up to %d)", chunk, KDA_MAX_CHUNK);
+  if (in_dtype == KDA_F32 && chunk > 32)
+    return fail(KDA_EUNSUPPORTED, "chunk=%d: fp32 inputs take chunks of at most 32 rows", chunk);
+  const int64_t hkv = static_cast<int64_t>(H) * dk * dv;
+  if (hkv >= (int64_t{1} << 31)) return fail(KDA_EUNSUPPORTED, "H*dk*dv must be below 2^31");
+  if (n_seqs == 0) return ok();
+  if (!cu) return fail(KDA_EINVAL, "cu_seqlens is null");
+  if (cu[0] != 0) return fail(KDA_EINVAL, "cu_seqlens[0] = %d, must be 0", cu[0]);
+  for (int32_t i = 0; i < n_seqs; ++i)
+    if (cu[i + 1] < cu[i]) return fail(KDA_EINVAL, "cu_seqlens decreases at %d", i);
+  const int64_t T = cu[n_seqs];
+
+  // Checkpoints.
+  if (n_ckpt > 0 && (!ck_cu || !ck_pos || !ck_slot || !page_pool))
+    return fail(KDA_EINVAL, "checkpoints need ckpt_cu, ckpt_pos, ckpt_slot and page_pool");
+  if (ck_cu) {
+    if (ck_cu[0] != 0 || ck_cu[n_seqs] != n_ckpt)
+      return fail(KDA_EINVAL, "ckpt_cu must start at 0 and end at n_ckpt");
+    for (int32_t i = 0; i < n_seqs; ++i) {
+      if (ck_cu[i + 1] < ck_cu[i]) return fail(KDA_EINVAL, "ckpt_cu decreases at %d", i);
+      const int32_t len = cu[i + 1] - cu[i];
+      for (int32_t c = ck_cu[i]; c < ck_cu[i + 1]; ++c) {
+        if (ck_pos[c] < 1 || ck_pos[c] > len)
+          return fail(KDA_EINVAL, "checkpoint %d of sequence %d at %d outside 1..%d", c - ck_cu[i], i,
+                      ck_pos[c], len);
+        if (c > ck_cu[i] && ck_pos[c] <= ck_pos[c - 1])
+          return fail(KDA_EINVAL, "checkpoints of sequence %d not strictly increasing", i);
+      }
+    }
+  } else if (n_ckpt != 0) {
+    return fail(KDA_EINVAL, "n_ckpt > 0 without ckpt_cu");
+  }
+  if (n_ckpt > 0) {
+    if (page_elems < hkv) return fail(KDA_EINVAL, "page_elems %lld < H*dk*dv %lld",
+                                      static_cast<long long>(page_elems), static_cast<long long>(hkv));
+    std::unordered_set<int32_t> seen;
+    for (int64_t c = 0; c < n_ckpt; ++c) {
+      if (ck_slot[c] < 0 || ck_slot[c] >= n_slots)
+        return fail(KDA_EINVAL, "checkpoint slot %d outside 0..%lld", ck_slot[c],
+                    static_cast<long long>(n_slots) - 1);
+      if (!seen.insert(ck_slot[c]).second) return fail(KDA_EINVAL, "checkpoint slot %d repeated", ck_slot[c]);
+    }
+  }
+
+  // Split.
+  int64_t total_chunks = 0, max_chunks = 0;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    const int32_t len = cu[i + 1] - cu[i];
+    const int32_t c0 = ck_cu ? ck_cu[i] : 0, c1 = ck_cu ? ck_cu[i + 1] : 0;
+    const int64_t c = seq_chunks(len, ck_pos ? ck_pos + c0 : nullptr, c1 - c0, chunk);
+    total_chunks += c * H;
+    max_chunks = std::max(max_chunks, c);
+  }
+  int split = dv_split;
+  if (split == 0) split = choose_split(dk, dv, total_chunks, max_chunks);
+  if (!valid_tile(dv, split))
+    return fail(KDA_EUNSUPPORTED, "dv_split=%d with dv=%d (dv/split must be 16, 32 or 64)", dv_split, dv);
+
+  // Buffers.
+  const size_t es = elem_size(in_dtype);
+  if (T > 0 && (!q || !k || !v || !a || !beta || !o)) return fail(KDA_EINVAL, "null input or output");
+  const size_t need = (work_ints(n_seqs, H, n_ckpt) * 4 + 255) / 256 * 256;
+  if (!workspace || workspace_bytes < need)
+    return fail(KDA_EWORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) & 3u) return fail(KDA_EINVAL, "workspace misaligned");
+  const size_t tok = static_cast<size_t>(T) * H;
+  const size_t sbytes = static_cast<size_t>(n_seqs) * hkv * 4;
+  const std::vector<Range> ins = {{q, tok * dk * es, "q"}, {k, tok * dk * es, "k"},
+                                  {v, tok * dv * es, "v"}, {a, tok * dk * es, "a"},
+                                  {beta, tok * es, "beta"}, {s0, s0 ? sbytes : 0, "s0"}};
+  const std::vector<Range> outs = {
+      {o, tok * dv * es, "o"}, {s_final, s_final ? sbytes : 0, "s_final"},
+      {page_pool, n_ckpt > 0 ? static_cast<size_t>(n_slots) * page_elems * 4 : 0, "page_pool"},
+      {workspace, need, "workspace"}};
+  int st = check_disjoint(outs, ins);
+  if (st) return st;
+
+  // Work list: chains longest sequence first, padded to whole XCD rounds.
+  std::vector<int32_t> order(n_seqs);
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
+    return cu[x + 1] - cu[x] > cu[y + 1] - cu[y];
+  });
+  const int64_t n_chains = round8(static_cast<int64_t>(n_seqs) * H);
+  if (n_chains * split >= (int64_t{1} << 31)) return fail(KDA_EUNSUPPORTED, "too many chains");
+  std::vector<int32_t> work(work_ints(n_seqs, H, n_ckpt), 0);
+  int32_t* chains = work.data();
+  int32_t* seqinfo = chains + 2 * n_chains;
+  int32_t* wpos = seqinfo + 4 * n_seqs;
+  int32_t* wslot = wpos + n_ckpt;
+  int64_t c = 0;
+  for (int32_t s : order)
+    for (int32_t h = 0; h < H; ++h, ++c) {
+      chains[2 * c] = s;
+      chains[2 * c + 1] = h;
+    }
+  for (; c < n_chains; ++c) {
+    chains[2 * c] = -1;
+    chains[2 * c + 1] = 0;
+  }
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    seqinfo[4 * i] = cu[i];
+    seqinfo[4 * i + 1] = cu[i + 1];
+    seqinfo[4 * i + 2] = ck_cu ? ck_cu[i] : 0;
+    seqinfo[4 * i + 3] = ck_cu ? ck_cu[i + 1] : 0;
+  }
+  for (int64_t i = 0; i < n_ckpt; ++i) {
+    wpos[i] = ck_pos[i];
+    wslot[i] = ck_slot[i];
+  }
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  // Pageable source: the runtime has consumed it when the call returns.
+  hipError_t e = hipMemcpyAsync(workspace, work.data(), work.size() * 4, hipMemcpyHostToDevice, hs);
+  if (e != hipSuccess) return hip_status(e, "work list copy");
+
+  const int32_t* dwork = static_cast<const int32_t*>(workspace);
+  kda::PrefillArgs p{};
+  p.q = q; p.k = k; p.v = v; p.a = a; p.beta = beta;
+  p.bf16 = in_dtype == KDA_BF16;
+  p.H = H; p.dk = dk; p.dv = dv; p.chunk = chunk;
+  p.s0 = s0; p.o = o; p.s_final = s_final;
+  p.page_pool = page_pool; p.page_elems = page_elems;
+  p.chains = dwork;
+  p.seqinfo = dwork + 2 * n_chains;
+  p.ck_pos = p.seqinfo + 4 * n_seqs;
+  p.ck_slot = p.ck_pos + n_ckpt;
+  p.n_chains = static_cast<int>(n_chains);
+  p.dv_tiles = split;
+  p.stream = hs;
+  return hip_status(kda::launch_prefill(p), "prefill launch");
+}
+
+int kda_chunk_prefill(const void* q, const void* k, const void* v, const void* a,
+                      const void* beta, kda_dtype in_dtype, int32_t H, int32_t dk, int32_t dv,
+                      int32_t chunk, const int32_t* cu_seqlens_host, int32_t n_seqs,
+                      const float* s0, void* o, float* s_final, const int32_t* ckpt_cu_host,
+                      const int32_t* ckpt_pos_host, const int32_t* ckpt_slot_host, int64_t n_ckpt,
+                      float* page_pool, int64_t page_elems, int64_t n_slots, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return kda_chunk_prefill_split(q, k, v, a, beta, in_dtype, H, dk, dv, chunk, cu_seqlens_host,
+                                 n_seqs, s0, o, s_final, ckpt_cu_host, ckpt_pos_host,
+                                 ckpt_slot_host, n_ckpt, page_pool, page_elems, n_slots, workspace,
+                                 workspace_bytes, 0, stream);
+}
+
+}  // extern "C"

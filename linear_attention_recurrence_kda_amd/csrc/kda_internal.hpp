@@ -37,8 +37,12 @@ struct PackArgs {
 };
 hipError_t launch_pack(const PackArgs& p);
 
-// Chunked prefill.  The work list (device, inside the workspace) is built by
-// the host layer; see kda_prefill.hip for its format.
+// Chunked prefill.  The work list lives in the caller's workspace; the host
+// layer (kda_api_prefill.cpp) builds it:
+//   chains [n_chains][2]  (sequence or -1 for padding, head), longest first,
+//                         n_chains a multiple of 8 (one XCD round)
+//   seqinfo [n_seqs][4]   (first token, end token, first ckpt, end ckpt)
+//   ck_pos / ck_slot      per-sequence token counts and page slots
 struct PrefillArgs {
   const void *q, *k, *v, *a, *beta;
   bool bf16;
@@ -48,9 +52,9 @@ struct PrefillArgs {
   float* s_final;
   float* page_pool;
   int64_t page_elems;
-  const int32_t* work;  // device work list
-  int n_chains;         // (sequence, head) chains, padded to a multiple of 8
-  int dv_tiles;         // workgroups per chain (split of dv)
+  const int32_t *chains, *seqinfo, *ck_pos, *ck_slot;
+  int n_chains;  // padded
+  int dv_tiles;  // workgroups per chain (split of dv)
   hipStream_t stream;
 };
 hipError_t launch_prefill(const PrefillArgs& p);
