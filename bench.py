@@ -1,0 +1,377 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA hot path on one MI355X.
+
+A timed step is one pass of the prefill path over the variable-length
+workload (16 sequences with log-uniform lengths in [1024, 32768], H=32,
+dk=dv=128, bf16 inputs, fp32 states from nonzero committed S0, chunk 64,
+checkpoints at every 4096 tokens plus the exact tail written into page
+slots) followed by packing the 16 final states into page slots.  `value` is
+that step's whole-job throughput in tokens/s with inputs resident in HBM.
+
+In the same run, and reported under "parts": the single-sequence prefill
+(T=8192, checkpoints every 512), 64 in-place decode steps (B=256 sessions),
+verify-and-replay (B=64, H=16, d=32, 8 drafts) and pack/unpack of 16
+checkpoint states, each with its algorithmic bytes or flops against the
+MI355X peaks, plus the float64 CPU oracle timed on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only a,b] [--no-cpu]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s (MFMA %) + decode/replay state GB/s (HBM %), H=32 d=128"
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PROFILES = os.path.join(ROOT, "profiles")
+PREFILL_SRC = os.path.join(ROOT, "linear_attention_recurrence_kda_amd", "csrc", "kda_prefill.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- work counts
+def prefill_flops(tokens, H, dk, dv, C):
+    """Algorithmic flops of the chunk form per token-head (dense tiles):
+    Gram products 4C*dk, W 2C*dk, Ut 2C*dv, U, QS and state update 6*dk*dv,
+    A_qk U 2C*dv, triangular inverse C^2/3."""
+    return tokens * H * (6 * C * dk + 4 * C * dv + 6 * dk * dv + C * C / 3.0)
+
+
+def prefill_bytes(tokens, H, dk, dv, n_seqs, n_ckpt, in_bytes=2, s0=True, final=True):
+    """Compulsory HBM bytes: q, k, a, v, beta read and o written once, S0
+    read, checkpoints and final states written (fp32)."""
+    state = H * dk * dv * 4
+    b = tokens * H * ((3 * dk + dv + 1) * in_bytes + dv * in_bytes)
+    b += n_ckpt * state + (n_seqs * state if s0 else 0) + (n_seqs * state if final else 0)
+    return b
+
+
+def decode_bytes(B, H, dk, dv, in_bytes=2):
+    return 2 * B * H * dk * dv * 4 + B * H * (3 * dk + dv + 1) * in_bytes + B * H * dv * in_bytes
+
+
+def replay_bytes(B, H, dk, dv, t_draft, n_acc, in_bytes=4):
+    return (2 * B * H * dk * dv * 4 + int(np.sum(n_acc)) * H * (3 * dk + dv + 1) * in_bytes
+            + B * H * t_draft * dv * in_bytes)
+
+
+# ---------------------------------------------------------------- helpers
+class Timer:
+    """Wall clock around K steps plus HIP events around one kernel call per
+    step, all on torch's current stream (the stream the library launches on)."""
+
+    def __init__(self, torch, steps):
+        self.torch = torch
+        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(steps)]
+
+    def kernel_ms(self):
+        return float(np.mean([a.elapsed_time(b) for a, b in self.ev]))
+
+
+def run_steps(torch, fn, steps, warmup, kernel_fn=None):
+    for _ in range(warmup):
+        fn(None)
+    torch.cuda.synchronize()
+    tm = Timer(torch, steps)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fn(tm.ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall / steps * 1e3, tm.kernel_ms()
+
+
+def src_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def committed_traffic(name, kernel_src):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, valid
+    only while the kernel source is unchanged (else None)."""
+    p = os.path.join(PROFILES, f"{name}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("kernel_src_sha256_16") != src_hash(kernel_src):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------- parts
+def bench_prefill(torch, kda, inputs, w, steps, warmup, pack_final, label):
+    d = {n: torch.from_numpy(w[n]).to(torch.bfloat16).cuda() for n in ("q", "k", "v", "a", "beta")}
+    H, dk = w["k"].shape[1:]
+    dv = w["v"].shape[2]
+    cu = w["cu_seqlens"]
+    N = len(cu) - 1
+    T = int(cu[-1])
+    s0 = None if w["s0"] is None else torch.from_numpy(w["s0"]).cuda()
+    ck = w["checkpoints"]
+    n_ck = sum(len(c) for c in ck)
+    slots, i = [], 0
+    for c in ck:
+        slots.append(list(range(i, i + len(c))))
+        i += len(c)
+    page = H * dk * dv
+    pool = torch.zeros((n_ck + N, page), dtype=torch.float32, device="cuda")
+    final_slots = torch.arange(n_ck, n_ck + N, dtype=torch.int32, device="cuda")
+    o = torch.empty((T, H, dv), dtype=torch.bfloat16, device="cuda")
+    sf = torch.empty((N, H, dk, dv), dtype=torch.float32, device="cuda")
+    ws = torch.empty(kda.prefill_workspace_size(N, T, H, dk, dv, 64, n_ck), dtype=torch.uint8,
+                     device="cuda")
+
+    def step(ev):
+        if ev is not None:
+            ev[0].record()
+        kda.chunk_prefill(d["q"], d["k"], d["v"], d["a"], d["beta"], cu, s0=s0, chunk=64,
+                          checkpoints=ck, ckpt_slots=slots, page_pool=pool, o=o, s_final=sf,
+                          workspace=ws)
+        if ev is not None:
+            ev[1].record()
+        if pack_final:
+            kda.pack_heads(sf, final_slots, pool)
+
+    ms, kms = run_steps(torch, step, steps, warmup)
+    flops = prefill_flops(T, H, dk, dv, 64)
+    byts = prefill_bytes(T, H, dk, dv, N, n_ck, s0=s0 is not None)
+    res = {
+        "workload": label, "tokens": T, "n_seqs": N, "n_ckpt": n_ck,
+        "ms_per_step": ms, "kernel_ms": kms,
+        "tokens_per_s": T / (ms * 1e-3),
+        "kernel_tokens_per_s": T / (kms * 1e-3),
+        "algo_gflop": flops / 1e9, "algo_gbytes": byts / 1e9,
+        "mfma_tflops": flops / (kms * 1e-3) / 1e12,
+        "mfma_frac": flops / (kms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        "hbm_gbs": byts / (kms * 1e-3) / 1e9,
+        "hbm_frac": byts / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+    }
+    # roofline: min(peak MFMA, I * BW) with I = flops / bytes
+    t_roof = max(flops / (BF16_PEAK_TFLOPS * 1e12), byts / (HBM_PEAK_GBS * 1e9))
+    res["roofline_frac"] = t_roof / (kms * 1e-3)
+    del d, pool, o, sf, ws
+    return res
+
+
+def bench_decode(torch, kda, inputs, steps, warmup):
+    B, H, dk, dv, n_tok = 256, 32, 128, 128, 64
+    state = torch.from_numpy(inputs.decode_state(2, B, H, dk, dv, 0.05)).cuda()
+    toks = []
+    for s in range(n_tok):
+        t = inputs.decode_step_inputs(s, 2, B, H, dk, dv, "bf16")
+        toks.append({n: torch.from_numpy(x).to(torch.bfloat16).cuda() for n, x in t.items()})
+    o = torch.empty((B, H, dv), dtype=torch.bfloat16, device="cuda")
+
+    # One timed step = the 64 in-place decode steps; events bracket the 64 launches.
+    def step(ev):
+        if ev is not None:
+            ev[0].record()
+        for t in toks:
+            kda.decode_step(t["q"], t["k"], t["v"], t["a"], t["beta"], state, o)
+        if ev is not None:
+            ev[1].record()
+
+    ms, kms = run_steps(torch, step, max(2, steps // 2), max(1, warmup // 2))
+    per_launch_ms = kms / n_tok
+    byts = decode_bytes(B, H, dk, dv)
+    res = {"workload": "decode: B=256, H=32, dk=dv=128, bf16 in, fp32 state, 64 in-place steps",
+           "us_per_decode_step": per_launch_ms * 1e3, "algo_gbytes_per_step": byts / 1e9,
+           "hbm_gbs": byts / (per_launch_ms * 1e-3) / 1e9,
+           "hbm_frac": byts / (per_launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "tokens_per_s": B / (per_launch_ms * 1e-3)}
+    del state, toks
+    return res
+
+
+def bench_replay(torch, kda, inputs, steps, warmup, shape="pages"):
+    if shape == "pages":
+        w = inputs.replay_workload()
+        dt, tdt, label = "fp32", torch.float32, "replay: B=64, H=16, dk=dv=32, 8 drafts, fp32"
+    else:
+        w = inputs.replay_workload(wid=11, B=256, H=32, dk=128, dv=128, t_draft=8, dtype="bf16")
+        dt, tdt, label = "bf16", torch.bfloat16, "replay: B=256, H=32, dk=dv=128, 8 drafts, bf16"
+    d = {n: torch.from_numpy(w[n]).to(tdt).cuda() for n in ("q", "k", "v", "a", "beta")}
+    committed = torch.from_numpy(w["committed"]).cuda()
+    n = torch.from_numpy(w["n_accepted"]).cuda()
+    s_new = torch.empty_like(committed)
+    Td, B, H, dk = w["q"].shape
+    dv = w["v"].shape[-1]
+    o = torch.empty((B, H, Td, dv), dtype=tdt, device="cuda")
+
+    reps = 20  # back-to-back calls between one event pair
+
+    def step(ev):
+        if ev is not None:
+            ev[0].record()
+        for _ in range(reps):
+            kda.verify_and_replay(committed, d["q"], d["k"], d["v"], d["a"], d["beta"], n, s_new, o)
+        if ev is not None:
+            ev[1].record()
+
+    ms, kms = run_steps(torch, step, steps, warmup)
+    kms /= reps
+    byts = replay_bytes(B, H, dk, dv, Td, w["n_accepted"], 4 if dt == "fp32" else 2)
+    return {"workload": label, "us_per_call": kms * 1e3, "algo_mbytes": byts / 1e6,
+            "hbm_gbs": byts / (kms * 1e-3) / 1e9,
+            "hbm_frac": byts / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
+def bench_pack(torch, kda, steps, warmup):
+    B, H, d = 16, 32, 128
+    g = torch.Generator(device="cuda").manual_seed(3)
+    state = torch.randn((B, H, d, d), device="cuda", generator=g)
+    pool = torch.zeros((B, H * d * d), device="cuda")
+    slots = torch.arange(B, dtype=torch.int32, device="cuda")
+    back = torch.empty_like(state)
+
+    reps = 10
+
+    def step(ev):
+        if ev is not None:
+            ev[0].record()
+        for _ in range(reps):
+            kda.pack_heads(state, slots, pool)
+            kda.unpack_heads(pool, slots, H, d, d, state=back)
+        if ev is not None:
+            ev[1].record()
+
+    ms, kms = run_steps(torch, step, steps, warmup)
+    kms /= reps
+    byts = 2 * (2 * B * H * d * d * 4)  # pack and unpack, each reads and writes 16 states
+    return {"workload": "pack+unpack: 16 states of H=32, dk=dv=128 fp32 into 2 MiB pages",
+            "us_per_pack_unpack": kms * 1e3, "hbm_gbs": byts / (kms * 1e-3) / 1e9,
+            "hbm_frac": byts / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
+def copy_calibration(torch):
+    """A plain 1 GiB device copy of known size (the scale for HBM counters)."""
+    x = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    x.fill_(1.0)
+    y.copy_(x)
+    torch.cuda.synchronize()
+    return {"bytes_read": x.numel() * 4, "bytes_written": y.numel() * 4}
+
+
+def cpu_baseline(inputs, w):
+    """The float64 oracle, untouched, on the first 2048 tokens of the longest
+    sequence of the workload (all 32 heads), on one thread."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    n = int(np.argmax(w["lengths"]))
+    lo = int(w["cu_seqlens"][n])
+    L = 2048
+    sl = {f: w[f][lo:lo + L] for f in ("q", "k", "v", "a", "beta")}
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        oracle.kda_recurrent(sl["q"], sl["k"], sl["v"], sl["a"], sl["beta"], w["s0"][n])
+        dt = time.perf_counter() - t0
+    return {"value": L / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"float64 oracle kda_recurrent over the first {L} tokens of the longest "
+                      f"sequence (all 32 heads, dk=dv=128) of the same workload; {dt:.1f} s"}
+
+
+# ---------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--only", default="", help="comma list of: prefill4, prefill3, decode, replay, "
+                                               "replay_big, pack, copycal")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--json-out", default="")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the KDA hot path here has no multi-GPU step "
+              "(every GPU box has one MI355X); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from linear_attention_recurrence_kda_amd import inputs, kda
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    kda.lib()  # fails loudly if the HIP library is not built
+    only = set(x for x in args.only.split(",") if x)
+    want = (lambda p: not only or p in only)
+
+    parts = {}
+    w4 = None
+    if want("prefill4") or (not only and not args.no_cpu):
+        log("generating the varlen prefill workload ...")
+        w4 = inputs.workload4()
+    if want("prefill4"):
+        log("prefill (varlen) ...")
+        parts["prefill_varlen"] = bench_prefill(
+            torch, kda, inputs, w4, args.steps, args.warmup, True,
+            "varlen prefill: 16 seqs, len~logU[1024,32768], H=32, dk=dv=128, bf16, S0~N(0,0.1^2), "
+            "chunk 64, ckpt every 4096 + tail, final states packed")
+    if want("prefill3"):
+        log("prefill (single sequence) ...")
+        parts["prefill_single"] = bench_prefill(
+            torch, kda, inputs, inputs.workload3(), args.steps, args.warmup, False,
+            "single-sequence prefill: T=8192, H=32, dk=dv=128, bf16, S0=0, chunk 64, ckpt every 512")
+    if want("decode"):
+        log("decode ...")
+        parts["decode"] = bench_decode(torch, kda, inputs, args.steps, args.warmup)
+    if want("replay"):
+        log("replay ...")
+        parts["replay"] = bench_replay(torch, kda, inputs, args.steps, args.warmup)
+    if want("replay_big"):
+        log("replay (large) ...")
+        parts["replay_large"] = bench_replay(torch, kda, inputs, args.steps, args.warmup, "big")
+    if want("pack"):
+        log("pack ...")
+        parts["pack"] = bench_pack(torch, kda, args.steps, args.warmup)
+    if "copycal" in only:
+        parts["copy_calibration"] = copy_calibration(torch)
+
+    head = parts.get("prefill_varlen")
+    line = {"metric": METRIC, "value": None, "unit": "tokens/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": None,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic"}
+    if head is not None:
+        line["value"] = head["tokens_per_s"]
+        line["ms_per_step"] = head["ms_per_step"]
+        line["config"] = {"workload": head["workload"], "tokens": head["tokens"],
+                          "n_seqs": head["n_seqs"], "H": 32, "dk": 128, "dv": 128, "chunk": 64,
+                          "n_ckpt": head["n_ckpt"], "parallelism": "single GPU"}
+        kbytes = head["algo_gbytes"] * 1e9
+        line["roofline"] = {
+            "kernel": "prefill_kernel<128,64,bf16>", "bound": "hbm",
+            "achieved": head["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": head["hbm_frac"],
+            "traffic": committed_traffic("prefill_varlen", PREFILL_SRC),
+            "algo_bytes_per_launch": kbytes, "kernel_ms": head["kernel_ms"],
+            "mfma_tflops": head["mfma_tflops"], "mfma_frac": head["mfma_frac"],
+            "roofline_frac": head["roofline_frac"]}
+    if not args.no_cpu and w4 is not None and not only:
+        log("cpu baseline (float64 oracle) ...")
+        line["cpu_baseline"] = cpu_baseline(inputs, w4)
+    line["parts"] = parts
+    s = json.dumps(line)
+    print(s, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(s + "\n")
+
+
+if __name__ == "__main__":
+    main()

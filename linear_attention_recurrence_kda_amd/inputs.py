@@ -17,7 +17,9 @@ descriptions'):
   beta = sigmoid(z'), z' ~ N(0, 1), in [0, 1] (same section).
 """
 
+import concurrent.futures as cf
 import math
+import os
 
 import numpy as np
 
@@ -51,40 +53,59 @@ def round_to_bf16(x, inplace=False):
     return x
 
 
-def _normal(rng, shape):
-    return rng.standard_normal(size=shape, dtype=np.float32)
+_POOL = None
 
 
-def _l2_normalise(x):
-    n = np.sqrt(np.einsum("...i,...i->...", x, x, dtype=np.float32))
-    x /= n[..., None]
-    return x
+def _pool():
+    global _POOL
+    if _POOL is None:
+        _POOL = cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1))
+    return _POOL
 
 
 def _sigmoid(z):
-    return (1.0 / (1.0 + np.exp(-z.astype(np.float64)))).astype(np.float32)
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def _fill(wid, block, field, out, dtype, g_min):
+    """Draw one field of one block into the float32 array `out` (in place)."""
+    _rng(wid, field, block).standard_normal(out=out, dtype=np.float32)
+    if field in (_Q, _K):  # L2-normalise over the key dimension
+        out /= np.sqrt(np.einsum("...i,...i->...", out, out))[..., None]
+    elif field == _ZA:     # a = g_min * sigmoid(z)
+        out[...] = np.float32(g_min) * _sigmoid(out)
+    elif field == _ZB:     # beta = sigmoid(z)
+        out[...] = _sigmoid(out)
+    if dtype == "bf16":
+        round_to_bf16(out, inplace=True)
+    elif dtype != "fp32":
+        raise ValueError("dtype must be 'bf16' or 'fp32'")
+
+
+_FIELDS = (("q", _Q), ("k", _K), ("v", _V), ("a", _ZA), ("beta", _ZB))
+
+
+def _shapes(lead, H, dk, dv):
+    return {"q": lead + (H, dk), "k": lead + (H, dk), "v": lead + (H, dv), "a": lead + (H, dk),
+            "beta": lead + (H,)}
 
 
 def token_inputs(wid, block, shape_lead, H, dk, dv, dtype, g_min=-1.0):
     """q, k, a of shape shape_lead + (H, dk), v of shape shape_lead + (H, dv),
     beta of shape shape_lead + (H,), drawn from the streams of (wid, block)."""
-    lead = tuple(shape_lead)
-    q = _l2_normalise(_normal(_rng(wid, _Q, block), lead + (H, dk)))
-    k = _l2_normalise(_normal(_rng(wid, _K, block), lead + (H, dk)))
-    v = _normal(_rng(wid, _V, block), lead + (H, dv))
-    a = (g_min * _sigmoid(_normal(_rng(wid, _ZA, block), lead + (H, dk)))).astype(np.float32)
-    beta = _sigmoid(_normal(_rng(wid, _ZB, block), lead + (H,)))
-    out = {"q": q, "k": k, "v": v, "a": a, "beta": beta}
-    if dtype == "bf16":
-        out = {n: round_to_bf16(x, inplace=True) for n, x in out.items()}
-    elif dtype != "fp32":
-        raise ValueError("dtype must be 'bf16' or 'fp32'")
+    shp = _shapes(tuple(shape_lead), H, dk, dv)
+    out = {n: np.empty(shp[n], dtype=np.float32) for n, _ in _FIELDS}
+    jobs = [_pool().submit(_fill, wid, block, f, out[n], dtype, g_min) for n, f in _FIELDS]
+    for j in jobs:
+        j.result()
     return out
 
 
 def state_normal(wid, block, shape, std):
     """Committed / resident fp32 state with N(0, std^2) entries."""
-    return (std * _normal(_rng(wid, _S0, block), tuple(shape))).astype(np.float32)
+    x = _rng(wid, _S0, block).standard_normal(size=tuple(shape), dtype=np.float32)
+    x *= np.float32(std)
+    return x
 
 
 # ---------------------------------------------------------------------------
@@ -110,15 +131,22 @@ def prefill_checkpoints(lengths, every, tail=True):
 
 def prefill_workload(wid, lengths, H, dk, dv, dtype, s0_std=None, ckpt_every=None,
                      ckpt_tail=True, g_min=-1.0):
-    """A full token-packed prefill batch.  Sequence n draws from block n."""
+    """A full token-packed prefill batch.  Sequence n draws from block n; the
+    fields of all sequences are drawn in parallel, straight into place."""
     cu = np.zeros(len(lengths) + 1, dtype=np.int32)
     cu[1:] = np.cumsum(lengths)
-    fields = {n: [] for n in ("q", "k", "v", "a", "beta")}
+    T = int(cu[-1])
+    shp = _shapes((T,), H, dk, dv)
+    out = {n: np.empty(shp[n], dtype=np.float32) for n, _ in _FIELDS}
+    jobs = []
     for n, L in enumerate(lengths):
-        t = token_inputs(wid, n, (L,), H, dk, dv, dtype, g_min)
-        for f in fields:
-            fields[f].append(t[f])
-    out = {f: np.concatenate(x, axis=0) for f, x in fields.items()}
+        if L == 0:
+            continue
+        lo, hi = int(cu[n]), int(cu[n + 1])
+        jobs += [_pool().submit(_fill, wid, n, f, out[name][lo:hi], dtype, g_min)
+                 for name, f in _FIELDS]
+    for j in jobs:
+        j.result()
     out["cu_seqlens"] = cu
     out["s0"] = None if s0_std is None else np.stack(
         [state_normal(wid, n, (H, dk, dv), s0_std) for n in range(len(lengths))])
