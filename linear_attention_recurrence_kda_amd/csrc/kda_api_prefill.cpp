@@ -23,11 +23,13 @@ size_t work_ints(int32_t n_seqs, int32_t H, int64_t n_ckpt) {
   return static_cast<size_t>(2 * round8(static_cast<int64_t>(n_seqs) * H) + 4 * n_seqs + 2 * n_ckpt);
 }
 
-bool valid_tile(int32_t dv, int32_t split) {
+// dv columns per workgroup: 16..64, or 128 for bf16 inputs (fp32 operands of a
+// 128-column tile do not fit in LDS).
+bool valid_tile(int32_t dv, int32_t split, bool bf16) {
   if (split != 1 && split != 2 && split != 4 && split != 8) return false;
   if (dv % split) return false;
   const int t = dv / split;
-  return t == 16 || t == 32 || t == 64;
+  return t == 16 || t == 32 || t == 64 || (t == 128 && bf16);
 }
 
 // Chunks of one sequence: chunks never cross a checkpoint position.
@@ -46,11 +48,11 @@ int64_t seq_chunks(int32_t len, const int32_t* pos, int32_t npos, int32_t chunk)
 // work (Gram products, W) is repeated by every split, value-side work scales
 // with the tile width; the chip time is the larger of the total work over the
 // CUs and the longest chain.
-int choose_split(int32_t dk, int32_t dv, int64_t total_chunks, int64_t max_chunks) {
+int choose_split(int32_t dk, int32_t dv, bool bf16, int64_t total_chunks, int64_t max_chunks) {
   int best = 0;
   double best_t = 0;
   for (int split : {1, 2, 4, 8}) {
-    if (!valid_tile(dv, split)) continue;
+    if (!valid_tile(dv, split, bf16)) continue;
     const double tile = static_cast<double>(dv) / split;
     const double cost = 1.5 * dk + (3.0 * dk / 8 + 12.0) * tile / 16.0;
     const double t = std::max(static_cast<double>(total_chunks) * split * cost / kCUs,
@@ -149,13 +151,19 @@ int kda_chunk_prefill_split(const void* q, const void* k, const void* v, const v
     max_chunks = std::max(max_chunks, c);
   }
   int split = dv_split;
-  if (split == 0) split = choose_split(dk, dv, total_chunks, max_chunks);
-  if (!valid_tile(dv, split))
-    return fail(KDA_EUNSUPPORTED, "dv_split=%d with dv=%d (dv/split must be 16, 32 or 64)", dv_split, dv);
+  const bool bf16 = in_dtype == KDA_BF16;
+  if (split == 0) split = choose_split(dk, dv, bf16, total_chunks, max_chunks);
+  if (!valid_tile(dv, split, bf16))
+    return fail(KDA_EUNSUPPORTED, "dv_split=%d with dv=%d (dv/split must be 16, 32, 64, or 128 for bf16)",
+                dv_split, dv);
 
   // Buffers.
   const size_t es = elem_size(in_dtype);
   if (T > 0 && (!q || !k || !v || !a || !beta || !o)) return fail(KDA_EINVAL, "null input or output");
+  // The kernel reads q, k, a, v as pairs of consecutive elements.
+  for (const void* ptr : {q, k, v, a})
+    if (reinterpret_cast<uintptr_t>(ptr) % (2 * es))
+      return fail(KDA_EINVAL, "q, k, v, a must be aligned to two elements");
   const size_t need = (work_ints(n_seqs, H, n_ckpt) * 4 + 255) / 256 * 256;
   if (!workspace || workspace_bytes < need)
     return fail(KDA_EWORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);

@@ -1,4 +1,4 @@
-// Chunked KDA prefill with checkpoint emission, bf16 MFMA on gfx950.
+// Chunked KDA prefill with checkpoint emission, MFMA on gfx950.
 //
 // Math.  The "Kimi Linear 的 KDA 缓存" page (section "预填充为什么能分块并行")
 // notes that inside a chunk every state transition is a diagonal matrix minus
@@ -14,20 +14,29 @@
 //   U   = Ut - W S
 //   O   = (q*g) S + lower(Qp Km^T) U,         Qp_r = q_r*e^{G_r-G_m}
 //   S  <- diag(g_n) S + (k*g_n/g)^T U
-// The reference row m sits mid-chunk, so every scaled operand stays within
-// e^{+-|a|*C/2}: finite in bf16/fp32 for per-token log-decays a >= -2.5 at a
-// chunk of 64.  Every other scaled operand is bounded by 1.
+// The reference G_m is the cumulative sum through the middle 16-row block
+// boundary, so every scaled Gram operand stays within e^{+-|a|*C/2}: finite in
+// bf16/fp32 for per-token log-decays a >= -2.5 at a chunk of 64.  Every other
+// scaled operand is bounded by 1.
 //
 // Mapping.  One workgroup (4 waves) runs one (sequence, head) chain over a
 // DVT-wide tile of the dv columns (the columns of S are independent in the
 // recurrence, so a chain can be split over several workgroups that each redo
 // the key-side work).  The fp32 state tile lives in MFMA accumulators for the
-// whole sequence; a bf16 transposed copy in LDS feeds the contractions.  All
-// contractions use v_mfma_f32_16x16x32_bf16 with operands staged in LDS.
-// T is inverted in fp32: the four 16x16 diagonal blocks by forward
-// substitution, the off-diagonal blocks by block recursion.
-// Workgroups are placed so the tiles of one chain share an XCD (and its L2),
-// and chains run longest sequence first.
+// whole sequence; a transposed copy in LDS feeds the contractions.  All
+// contractions use v_mfma_f32_16x16x32_bf16 with operands staged in LDS: bf16
+// inputs stage bf16 operands; fp32 inputs stage fp32 operands and split each
+// into a bf16 high and low part, taking three products (hi*hi + hi*lo +
+// lo*hi, about 2^-16 relative error) so that fp32 I/O keeps fp32-level
+// accuracy (fp32 operands double the LDS footprint, so that path caps the
+// chunk at 32 rows).
+// T is built per wave without workgroup barriers: wave I inverts the 16x16
+// diagonal blocks it needs by forward substitution (64 lanes = 4 blocks x 16
+// columns) and then its block column T_RI = -T_RR sum_J L_RJ T_JI with
+// fp32-split MFMA.
+// The next chunk's raw inputs are loaded into registers while the current
+// chunk computes.  Workgroups are placed so the tiles of one chain share an
+// XCD (and its L2), and chains run longest sequence first.
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
 
@@ -39,8 +48,6 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kThreads = 256;
 
 // Operand storage: bf16 (bf16 inputs, chunk up to 64) or fp32 (fp32 inputs,
 // chunk up to 32).  Rows of LDS operand buffers are padded by 16 bytes.
@@ -85,71 +92,42 @@ __device__ __forceinline__ void put8(float* p, const float* x) {
   *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
   *reinterpret_cast<float4*>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
 }
-
-struct Params {
-  const void *q, *k, *v, *a, *beta;
-  const float* s0;
-  void* o;
-  float* s_final;
-  float* page_pool;
-  int64_t page_elems;
-  const int32_t* chains;   // [n_chains][2] = (sequence or -1, head)
-  const int32_t* seqinfo;  // [n_seqs][4]  = (tok_lo, tok_hi, ck_lo, ck_hi)
-  const int32_t* ck_pos;   // [n_ckpt] token counts from the sequence start
-  const int32_t* ck_slot;  // [n_ckpt]
-  int H, dv, chunk, dv_tiles;
-};
-
-template <int DK, int DVT, typename ST>
-struct Smem {
-  static constexpr int MAXC = Op<ST>::MAXC;
-  static constexpr int LDK = DK + Op<ST>::PAD;   // row length of [*][DK] buffers
-  static constexpr int LC = MAXC + Op<ST>::PAD;  // row length of [*][chunk] buffers
-  static constexpr int LF = MAXC + 1;            // row length of fp32 [chunk][chunk]
-  union {
-    struct {  // key-side operands of the Gram products (mid-chunk reference)
-      ST kpm[MAXC][LDK], qpm[MAXC][LDK], kmm[MAXC][LDK];
-    } gram;
-    struct {  // chunk-start scaled operands of the propagation
-      ST bkpT[DK][LC];      // (beta * k * g)^T
-      ST qp[MAXC][LDK];     // q * g
-      ST khT[DK][LC];       // (k * g_n / g)^T
-    } prop;
-  } u;
-  ST bvT[DVT][LC];          // (beta * v)^T, this workgroup's columns
-  ST sT[DVT][LDK];          // S^T
-  union {
-    float Lf[MAXC][LF];     // diag(beta) strict_lower(A_kk), fp32
-    ST w[MAXC][LDK];        // W, row-major
-  } lw;
-  float Tf[MAXC][LF];       // T in fp32 (upper blocks: scratch)
-  ST Tb[MAXC][LC];          // T
-  ST aqk[MAXC][LC];         // lower(Qp Km^T)
-  ST uT[DVT][LC];           // U^T
-  float tot[MAXC / 16][DK]; // per-16-row-block sums of a
-  float gmid[DK], gend[DK], gexp[DK];
-  float beta[MAXC];
-};
+template <int N, typename ST>
+__device__ __forceinline__ void putn(ST* p, const float* x) {
+  if constexpr (N == 8) put8(p, x);
+  else if constexpr (N == 4) put4(p, x);
+  else if constexpr (N == 2) put2(p, x[0], x[1]);
+  else put(p, x[0]);
+}
 
 __device__ __forceinline__ bf16x8 zero8() { return __builtin_bit_cast(bf16x8, i32x4{0, 0, 0, 0}); }
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-// acc += A[0:16, 0:kvalid] * Bt[0:16, 0:kvalid]^T for 16-row slabs A (row
-// stride lda) and Bt (row stride ldb) in LDS.  Lane l ends with rows
-// 4*(l/16)+0..3 of column l%16 of the 16x16 result.
-__device__ __forceinline__ f32x4 tile_mma(f32x4 acc, const __bf16* A, int lda, const __bf16* Bt,
-                                          int ldb, int kvalid, int lane) {
+// Orders this wave's LDS writes before its later LDS reads across lanes.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// acc_t += A_t[0:16, 0:kvalid] * Bt_t[0:16, 0:kvalid]^T for NT independent
+// tiles sharing one K loop (16-row slabs in LDS, row strides lda / ldb).
+// Lane l ends with rows 4*(l/16)+0..3 of column l%16 of each 16x16 result.
+template <int NT>
+__device__ __forceinline__ void tiles_mma(f32x4* acc, const __bf16* const* A, int lda,
+                                          const __bf16* const* Bt, int ldb, int kvalid, int lane) {
   const int row = lane & 15, kk = (lane >> 4) * 8;
-  const __bf16* ap = A + row * lda + kk;
-  const __bf16* bp = Bt + row * ldb + kk;
   for (int k0 = 0; k0 < kvalid; k0 += 32) {
-    bf16x8 fa = zero8(), fb = zero8();
-    if (k0 + kk < kvalid) {
-      fa = *reinterpret_cast<const bf16x8*>(ap + k0);
-      fb = *reinterpret_cast<const bf16x8*>(bp + k0);
+    bf16x8 fa[NT], fb[NT];
+    const bool ok = k0 + kk < kvalid;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      fa[t] = ok ? *reinterpret_cast<const bf16x8*>(A[t] + row * lda + kk + k0) : zero8();
+      fb[t] = ok ? *reinterpret_cast<const bf16x8*>(Bt[t] + row * ldb + kk + k0) : zero8();
     }
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb, acc, 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[t], fb[t], acc[t], 0, 0, 0);
   }
-  return acc;
 }
 
 // fp32 operands: x = hi + lo with hi = bf16(x), lo = bf16(x - hi); the product
@@ -165,48 +143,158 @@ __device__ __forceinline__ void split8(const float* p, bf16x8& hi, bf16x8& lo) {
   }
 }
 
-__device__ __forceinline__ f32x4 tile_mma(f32x4 acc, const float* A, int lda, const float* Bt,
-                                          int ldb, int kvalid, int lane) {
+template <int NT>
+__device__ __forceinline__ void tiles_mma(f32x4* acc, const float* const* A, int lda,
+                                          const float* const* Bt, int ldb, int kvalid, int lane) {
   const int row = lane & 15, kk = (lane >> 4) * 8;
-  const float* ap = A + row * lda + kk;
-  const float* bp = Bt + row * ldb + kk;
   for (int k0 = 0; k0 < kvalid; k0 += 32) {
-    bf16x8 ah = zero8(), al = zero8(), bh = zero8(), bl = zero8();
-    if (k0 + kk < kvalid) {
-      split8(ap + k0, ah, al);
-      split8(bp + k0, bh, bl);
+    const bool ok = k0 + kk < kvalid;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      bf16x8 ah = zero8(), al = zero8(), bh = zero8(), bl = zero8();
+      if (ok) {
+        split8(A[t] + row * lda + kk + k0, ah, al);
+        split8(Bt[t] + row * ldb + kk + k0, bh, bl);
+      }
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc[t], 0, 0, 0);
     }
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
   }
+}
+
+template <typename ST>
+__device__ __forceinline__ f32x4 tile_mma(f32x4 acc, const ST* A, int lda, const ST* Bt, int ldb,
+                                          int kvalid, int lane) {
+  tiles_mma<1>(&acc, &A, lda, &Bt, ldb, kvalid, lane);
   return acc;
 }
 
-__device__ __forceinline__ float ld(const float* p, size_t i) { return p[i]; }
-__device__ __forceinline__ float ld(const bf16raw* p, size_t i) { return to_f32(p[i]); }
+struct Params {
+  const void *q, *k, *v, *a, *beta;
+  const float* s0;
+  void* o;
+  float* s_final;
+  float* page_pool;
+  int64_t page_elems;
+  const int32_t* chains;   // [n_chains][2] = (sequence or -1, head)
+  const int32_t* seqinfo;  // [n_seqs][4]  = (tok_lo, tok_hi, ck_lo, ck_hi)
+  const int32_t* ck_pos;   // [n_ckpt] token counts from the sequence start
+  const int32_t* ck_slot;  // [n_ckpt]
+  int H, dv, chunk, dv_tiles;
+};
 
+template <typename ST>
+struct TScratch {  // one wave's workspace for its block column of T
+  static constexpr int MAXC = Op<ST>::MAXC;
+  float diag[4][16][20];      // T_RR, row-major, for R = I .. I+3
+  float colT[16][MAXC + 4];   // colT[i][j] = T[j][16 I + i]
+  float PT[16][20];           // P^T of the current step
+};
+
+template <int DK, int DVT, typename ST, int NG>
+struct Smem {
+  static constexpr int MAXC = Op<ST>::MAXC;
+  static constexpr int LDK = DK + Op<ST>::PAD;   // row length of [*][DK] buffers
+  static constexpr int LC = MAXC + Op<ST>::PAD;  // row length of [*][chunk] buffers
+  static constexpr int LF = MAXC + 4;            // row length of fp32 [chunk][chunk]
+  union {
+    struct {  // key-side operands of the Gram products (mid-chunk reference)
+      ST kpm[MAXC][LDK], qpm[MAXC][LDK], kmm[MAXC][LDK];
+    } gram;
+    TScratch<ST> ts[4];
+    struct {  // chunk-start scaled operands of the propagation
+      ST bkpT[DK][LC];      // (beta * k * g)^T
+      ST qp[MAXC][LDK];     // q * g
+      ST khT[DK][LC];       // (k * g_n / g)^T
+    } prop;
+  } u;
+  union {                   // (beta*v)^T is dead once Ut is formed; U^T follows it
+    ST bvT[DVT][LC];        // (beta * v)^T, this workgroup's columns
+    ST uT[DVT][LC];         // U^T
+  } buf;
+  ST sT[DVT][LDK];          // S^T
+  union {
+    float Lf[MAXC][LF];     // diag(beta) strict_lower(A_kk), fp32
+    ST w[MAXC][LDK];        // W, row-major
+  } lw;
+  ST Tb[MAXC][LC];          // T
+  ST aqk[MAXC][LC];         // lower(Qp Km^T)
+  float tot[NG][DK];        // per-row-group sums of a
+  float gexp[DK];           // g_n
+  __attribute__((aligned(16))) float beta[MAXC];
+};
 
 template <typename InT>
-struct StoreOf {
-  using type = __bf16;
+struct Traits;
+template <>
+struct Traits<bf16raw> {
+  using ST = __bf16;
+  using Pair = uint32_t;  // two consecutive bf16 values
+  static __device__ __forceinline__ Pair load(const bf16raw* p, size_t off) {
+    return *reinterpret_cast<const uint32_t*>(p + off);
+  }
+  static __device__ __forceinline__ float2 unpack(Pair x) {
+    return make_float2(__uint_as_float(x << 16), __uint_as_float(x & 0xffff0000u));
+  }
+  static __device__ __forceinline__ Pair zero() { return 0u; }
 };
 template <>
-struct StoreOf<float> {
-  using type = float;
+struct Traits<float> {
+  using ST = float;
+  using Pair = float2;
+  static __device__ __forceinline__ Pair load(const float* p, size_t off) {
+    return *reinterpret_cast<const float2*>(p + off);
+  }
+  static __device__ __forceinline__ float2 unpack(Pair x) { return x; }
+  static __device__ __forceinline__ Pair zero() { return make_float2(0.f, 0.f); }
 };
 
-template <int DK, int DVT, typename InT>
-__global__ __launch_bounds__(kThreads, 1) void prefill_kernel(Params p) {
-  using ST = typename StoreOf<InT>::type;
-  using SM = Smem<DK, DVT, ST>;
-  constexpr int HK = DK / 2;  // channel pairs
-  constexpr int LDK = SM::LDK, LC = SM::LC;
-  constexpr int NCT = DK / 16, NJT = DVT / 16;
-  constexpr int NST = NCT * NJT, NS = (NST + 3) / 4;
+// Raw chunk inputs held in registers from the prefetch to their use.
+template <typename InT, int RPG, int RV>
+struct Raw {
+  using Pair = typename Traits<InT>::Pair;
+  Pair k[RPG], q[RPG], a[RPG];  // rows g*RPG .. +RPG, channels 2cp, 2cp+1
+  Pair v[RV];                   // rows rv0 .. rv0+RV-1, columns 2jp, 2jp+1 of the tile
+  float vb[RV];                 // beta of those rows
+  float b;                      // beta of row tid
+};
+
+__device__ __forceinline__ float ld1(const float* p, size_t i) { return p[i]; }
+__device__ __forceinline__ float ld1(const bf16raw* p, size_t i) { return to_f32(p[i]); }
+
+// Thread and tile mappings of one workgroup of NW waves.
+template <int DK, int DVT, typename ST, int NW>
+struct Shape {
+  static constexpr int NT = 64 * NW;                  // threads
+  static constexpr int MAXC = Op<ST>::MAXC;
+  static constexpr int HK = DK / 2;                   // channel pairs
+  static constexpr int RPG = (MAXC * HK / NT) > 0 ? MAXC * HK / NT : 1;  // rows per prep thread
+  static constexpr int NG = MAXC / RPG;               // prep row groups
+  static constexpr int VP = DVT / 2;                  // column pairs of the tile
+  static constexpr int RV = (MAXC * VP / NT) > 0 ? MAXC * VP / NT : 1;   // rows per v thread
+  static constexpr int NCT = DK / 16, NJT = DVT / 16;
+  static constexpr int NST = NCT * NJT;               // state tiles
+  static constexpr int NS = (NST + NW - 1) / NW;      // state tiles per wave
+  static constexpr int NUT = (4 * NJT + NW - 1) / NW; // (row block, column tile) pairs per wave
+  static_assert(RPG <= 8 && RV <= 8 && 16 % RPG == 0, "mapping");
+};
+
+template <int DK, int DVT, typename InT, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(Params p) {
+  using TR = Traits<InT>;
+  using ST = typename TR::ST;
+  using SH = Shape<DK, DVT, ST, NW>;
+  using SM = Smem<DK, DVT, ST, SH::NG>;
+  constexpr int NT = SH::NT, MAXC = SH::MAXC, HK = SH::HK, RPG = SH::RPG, NG = SH::NG;
+  constexpr int VP = SH::VP, RV = SH::RV, NCT = SH::NCT, NJT = SH::NJT;
+  constexpr int NST = SH::NST, NS = SH::NS, NUT = SH::NUT;
+  constexpr int LDK = SM::LDK, LC = SM::LC, LF = SM::LF;
   __shared__ __attribute__((aligned(16))) SM sm;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // Wave index in a scalar register, so per-wave tile loops branch on scalars.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = p.H, dv = p.dv;
 
   // Workgroup -> (chain, dv tile): the tiles of a chain land on one XCD.
@@ -227,13 +315,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(Params p) {
   const InT* __restrict__ gb = static_cast<const InT*>(p.beta);
   InT* __restrict__ go = static_cast<InT*>(p.o);
 
-  // State tile: accumulator tile s = wave + 4u covers rows 16*(s/NJT) and
+  // State tile: accumulator tile s = wave + NW*u covers rows 16*(s/NJT) and
   // columns j0 + 16*(s%NJT).
   f32x4 S[NS];
 #pragma unroll
   for (int u = 0; u < NS; ++u) {
-    const int s = wave + 4 * u;
-    S[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int s = wave + NW * u;
+    S[u] = zero4();
     if (s < NST && p.s0 != nullptr) {
       const int c0 = 16 * (s / NJT) + 4 * (lane >> 4), j = j0 + 16 * (s % NJT) + (lane & 15);
 #pragma unroll
@@ -243,7 +331,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(Params p) {
   auto write_sT = [&]() {
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
-      const int s = wave + 4 * u;
+      const int s = wave + NW * u;
       if (s < NST) {
         const int c0 = 16 * (s / NJT) + 4 * (lane >> 4), jl = 16 * (s % NJT) + (lane & 15);
         const float x[4] = {S[u][0], S[u][1], S[u][2], S[u][3]};
@@ -254,7 +342,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(Params p) {
   auto store_state = [&](float* dst) {  // dst points at this head's [DK][dv] block
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
-      const int s = wave + 4 * u;
+      const int s = wave + NW * u;
       if (s < NST) {
         const int c0 = 16 * (s / NJT) + 4 * (lane >> 4), j = j0 + 16 * (s % NJT) + (lane & 15);
 #pragma unroll
@@ -268,257 +356,332 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(Params p) {
   if (tile == 0 && h == 0 && p.page_elems > hkv) {
     for (int c = ck_lo; c < ck_hi; ++c) {
       float* pg = p.page_pool + static_cast<int64_t>(p.ck_slot[c]) * p.page_elems;
-      for (int64_t e = hkv + tid; e < p.page_elems; e += kThreads) pg[e] = 0.f;
+      for (int64_t e = hkv + tid; e < p.page_elems; e += NT) pg[e] = 0.f;
     }
   }
 
-  // Prep mapping: thread -> channel pair cp, 16-row block g.
+  // Prep mapping: thread -> channel pair cp, row group g (rows g*RPG ..).
   const int cp = tid % HK, g = tid / HK;
-  const int c0p = 2 * cp;
+  const int c0p = 2 * cp, r0 = g * RPG;
+  // v-tile mapping: thread -> column pair jp, rows rv0 .. rv0+RV-1.
+  const int jp = tid % VP, rv0 = (tid / VP) * RV;
+
+  // Chunk end from its start: at most `chunk` rows, never past a checkpoint.
+  auto chunk_end = [&](int t, int c) {
+    int e = min(t + p.chunk, hi);
+    if (c < ck_hi) e = min(e, lo + p.ck_pos[c]);
+    return e;
+  };
+  // Issue the loads of rows [t, t+n) into registers (addresses clamped to
+  // valid rows; rows past n are masked when unpacked).
+  Raw<InT, RPG, RV> raw;
+  auto issue = [&](int t, int n) {
+    if (g < NG && r0 < n) {
+      const size_t base = (static_cast<size_t>(t) * H + h) * DK + c0p;
+      const size_t rstride = static_cast<size_t>(H) * DK;
+#pragma unroll
+      for (int rr = 0; rr < RPG; ++rr) {
+        const size_t off = base + static_cast<size_t>(min(r0 + rr, n - 1)) * rstride;
+        raw.k[rr] = TR::load(gk, off);
+        raw.q[rr] = TR::load(gq, off);
+        raw.a[rr] = TR::load(ga, off);
+      }
+    }
+    if (rv0 < n && tid < (MAXC / RV) * VP) {
+#pragma unroll
+      for (int e = 0; e < RV; ++e) {
+        const size_t tr = static_cast<size_t>(t + min(rv0 + e, n - 1)) * H + h;
+        raw.v[e] = TR::load(gv, tr * dv + j0 + 2 * jp);
+        raw.vb[e] = ld1(gb, tr);
+      }
+    }
+    if (tid < n) raw.b = ld1(gb, static_cast<size_t>(t + tid) * H + h);
+  };
 
   int t0 = lo, ck = ck_lo;
+  int end = t0 < hi ? chunk_end(t0, ck) : t0;
+  if (t0 < hi) issue(t0, end - t0);
+
   while (t0 < hi) {
-    int end = min(t0 + p.chunk, hi);
-    if (ck < ck_hi) end = min(end, lo + p.ck_pos[ck]);
     const int n = end - t0;
     const int nb = (n + 15) >> 4;
-    const bool act = g < nb;
+    const int ngc = 16 * nb / RPG;  // row groups covering the chunk's blocks
+    const bool act = g < ngc;
+    const bool is_ck = ck < ck_hi && end == lo + p.ck_pos[ck];
+    const int ckn = ck + (is_ck ? 1 : 0);
+    const int t0n = end;
+    const int endn = t0n < hi ? chunk_end(t0n, ckn) : t0n;
 
-    // ---- load the chunk; per-block cumulative sums of a -------------------
-    float kr[16][2], qr[16][2], gr[16][2];
+    // ---- unpack the chunk; per-group cumulative sums of a ----------------
+    // k and q stay packed in `raw` (rows past n zeroed) until the next
+    // chunk's loads are issued; gr holds the running sums of a.
+    float gr[RPG][2];
     if (act) {
       float run0 = 0.f, run1 = 0.f;
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int r = 16 * g + rr;
-        float k0 = 0.f, k1 = 0.f, q0 = 0.f, q1 = 0.f, a0 = 0.f, a1 = 0.f;
-        if (r < n) {
-          const size_t off = (static_cast<size_t>(t0 + r) * H + h) * DK + c0p;
-          k0 = ld(gk, off); k1 = ld(gk, off + 1);
-          q0 = ld(gq, off); q1 = ld(gq, off + 1);
-          a0 = ld(ga, off); a1 = ld(ga, off + 1);
-        }
-        run0 += a0; run1 += a1;
-        kr[rr][0] = k0; kr[rr][1] = k1; qr[rr][0] = q0; qr[rr][1] = q1;
+      for (int rr = 0; rr < RPG; ++rr) {
+        const bool valid = r0 + rr < n;
+        if (!valid) { raw.k[rr] = TR::zero(); raw.q[rr] = TR::zero(); }
+        const float2 aa = TR::unpack(valid ? raw.a[rr] : TR::zero());
+        run0 += aa.x; run1 += aa.y;
         gr[rr][0] = run0; gr[rr][1] = run1;
       }
       sm.tot[g][c0p] = run0;
       sm.tot[g][c0p + 1] = run1;
     }
-    if (tid < 16 * nb) sm.beta[tid] = tid < n ? ld(gb, static_cast<size_t>(t0 + tid) * H + h) : 0.f;
-    // (beta * v)^T for this tile: thread -> (column j, 8 consecutive rows).
-    for (int idx = tid; idx < DVT * 2 * nb; idx += kThreads) {
-      const int j = idx % DVT, rb = idx / DVT;
-      float x[8];
+    if (tid < 16 * nb) sm.beta[tid] = tid < n ? raw.b : 0.f;
+    if (rv0 < 16 * nb && tid < (MAXC / RV) * VP) {
+      float x0[RV], x1[RV];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int r = 8 * rb + e;
-        x[e] = 0.f;
-        if (r < n) {
-          const size_t tr = static_cast<size_t>(t0 + r) * H + h;
-          x[e] = ld(gb, tr) * ld(gv, tr * dv + j0 + j);
-        }
+      for (int e = 0; e < RV; ++e) {
+        const bool valid = rv0 + e < n;
+        const float2 vv = TR::unpack(valid ? raw.v[e] : TR::zero());
+        const float b = valid ? raw.vb[e] : 0.f;
+        x0[e] = b * vv.x;
+        x1[e] = b * vv.y;
       }
-      put8(&sm.bvT[j][8 * rb], x);
+      putn<RV>(&sm.buf.bvT[2 * jp][rv0], x0);
+      putn<RV>(&sm.buf.bvT[2 * jp + 1][rv0], x1);
     }
     __syncthreads();
 
-    // ---- cumulative sums across blocks; reference rows --------------------
-    const int mrow = 8 * nb;  // mid-chunk reference row
+    // ---- cumulative sums across groups; Gram operands ---------------------
+    // Reference: end of 16-row block nb/2 - 1 (chunk start when nb = 1).
+    float ge0 = 0.f, ge1 = 0.f;  // G at the chunk's last row
     if (act) {
-      float pre0 = 0.f, pre1 = 0.f;
-      for (int gg = 0; gg < g; ++gg) { pre0 += sm.tot[gg][c0p]; pre1 += sm.tot[gg][c0p + 1]; }
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) { gr[rr][0] += pre0; gr[rr][1] += pre1; }
-      if (g == (mrow >> 4)) {
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr)
-          if (rr == (mrow & 15)) { sm.gmid[c0p] = gr[rr][0]; sm.gmid[c0p + 1] = gr[rr][1]; }
+      float pre0 = 0.f, pre1 = 0.f, rf0 = 0.f, rf1 = 0.f;
+      const int gref = 16 * (nb >> 1) / RPG;
+      for (int gg = 0; gg < ngc; ++gg) {
+        const float t0v = sm.tot[gg][c0p], t1v = sm.tot[gg][c0p + 1];
+        if (gg < g) { pre0 += t0v; pre1 += t1v; }
+        if (gg < gref) { rf0 += t0v; rf1 += t1v; }
+        ge0 += t0v; ge1 += t1v;
       }
-      if (g == nb - 1) {
-        sm.gend[c0p] = gr[15][0]; sm.gend[c0p + 1] = gr[15][1];
-        sm.gexp[c0p] = fast_exp(gr[15][0]); sm.gexp[c0p + 1] = fast_exp(gr[15][1]);
-      }
-    }
-    __syncthreads();
-
-    // ---- Gram operands (mid-chunk reference) ------------------------------
-    if (act) {
-      const float m0 = sm.gmid[c0p], m1 = sm.gmid[c0p + 1];
+      if (g == 0) { sm.gexp[c0p] = fast_exp(ge0); sm.gexp[c0p + 1] = fast_exp(ge1); }
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int r = 16 * g + rr;
-        const float d0 = gr[rr][0] - m0, d1 = gr[rr][1] - m1;
+      for (int rr = 0; rr < RPG; ++rr) {
+        gr[rr][0] += pre0; gr[rr][1] += pre1;
+        const int r = r0 + rr;
+        const float d0 = gr[rr][0] - rf0, d1 = gr[rr][1] - rf1;
         const float up0 = fast_exp(d0), up1 = fast_exp(d1);
         const float dn0 = fast_exp(-d0), dn1 = fast_exp(-d1);
-        put2(&sm.u.gram.kpm[r][c0p], kr[rr][0] * up0, kr[rr][1] * up1);
-        put2(&sm.u.gram.qpm[r][c0p], qr[rr][0] * up0, qr[rr][1] * up1);
-        put2(&sm.u.gram.kmm[r][c0p], kr[rr][0] * dn0, kr[rr][1] * dn1);
+        const float2 kk = TR::unpack(raw.k[rr]), qq = TR::unpack(raw.q[rr]);
+        put2(&sm.u.gram.kpm[r][c0p], kk.x * up0, kk.y * up1);
+        put2(&sm.u.gram.qpm[r][c0p], qq.x * up0, qq.y * up1);
+        put2(&sm.u.gram.kmm[r][c0p], kk.x * dn0, kk.y * dn1);
       }
     }
     __syncthreads();
 
     // ---- Gram products: L = diag(beta) strict_lower(A_kk), Aqk = lower(A_qk)
     {
-      const int ntri = nb * (nb + 1) / 2;
-      for (int tt = wave; tt < 2 * ntri; tt += 4) {
-        const bool qk = tt >= ntri;
-        int x = qk ? tt - ntri : tt, R = 0;
-        while (x > R) { x -= R + 1; ++R; }
-        const int I = x;
-        const ST* A = qk ? &sm.u.gram.qpm[16 * R][0] : &sm.u.gram.kpm[16 * R][0];
-        f32x4 acc = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, A, LDK, &sm.u.gram.kmm[16 * I][0], LDK,
-                             DK, lane);
-        const int col = 16 * I + (lane & 15);
+      const int ntri = nb * (nb + 1) / 2, ntiles = 2 * ntri;
+      for (int t2 = wave; t2 < ntiles; t2 += 2 * NW) {
+        const int cnt = t2 + NW < ntiles ? 2 : 1;
+        int Rr[2], Ii[2];
+        bool qk[2];
+        const ST* A[2];
+        const ST* B[2];
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int row = 16 * R + 4 * (lane >> 4) + rr;
-          if (qk) put(&sm.aqk[row][col], row >= col ? acc[rr] : 0.f);
-          else sm.lw.Lf[row][col] = row > col ? sm.beta[row] * acc[rr] : 0.f;
+        for (int t = 0; t < 2; ++t) {
+          const int x0 = min(t2 + NW * t, ntiles - 1);
+          qk[t] = x0 >= ntri;
+          int x = qk[t] ? x0 - ntri : x0, R = 0;
+          while (x > R) { x -= R + 1; ++R; }
+          Rr[t] = R; Ii[t] = x;
+          A[t] = qk[t] ? &sm.u.gram.qpm[16 * R][0] : &sm.u.gram.kpm[16 * R][0];
+          B[t] = &sm.u.gram.kmm[16 * x][0];
+        }
+        f32x4 acc[2] = {zero4(), zero4()};
+        if (cnt == 2) tiles_mma<2>(acc, A, LDK, B, LDK, DK, lane);
+        else tiles_mma<1>(acc, A, LDK, B, LDK, DK, lane);
+        for (int t = 0; t < cnt; ++t) {
+          const int col = 16 * Ii[t] + (lane & 15), row0 = 16 * Rr[t] + 4 * (lane >> 4);
+          if (qk[t]) {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+              put(&sm.aqk[row0 + rr][col], row0 + rr >= col ? acc[t][rr] : 0.f);
+          } else {
+            const float4 bt = *reinterpret_cast<const float4*>(&sm.beta[row0]);
+            const float b4[4] = {bt.x, bt.y, bt.z, bt.w};
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+              sm.lw.Lf[row0 + rr][col] = row0 + rr > col ? b4[rr] * acc[t][rr] : 0.f;
+          }
         }
       }
     }
     __syncthreads();
 
-    // ---- propagation operands (chunk-start reference) ---------------------
-    if (act) {
-      const float n0 = sm.gend[c0p], n1 = sm.gend[c0p + 1];
-      float bk0[16], bk1[16], kh0[16], kh1[16];
+    // ---- T = (I + L)^{-1}, one block column per wave ----------------------
+    if (wave < nb) {
+      const int I = wave;
+      TScratch<ST>& ts = sm.u.ts[wave];
+      // Diagonal inverses T_RR for R = I .. nb-1: lane = 16*(R-I) + column.
+      {
+        const int blk = lane >> 4, R = I + blk, j = lane & 15;
+        if (R < nb) {
+          float x[16];
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int r = 16 * g + rr;
-        const float e0 = fast_exp(gr[rr][0]), e1 = fast_exp(gr[rr][1]);
-        const float b = sm.beta[r];
-        bk0[rr] = b * kr[rr][0] * e0;
-        bk1[rr] = b * kr[rr][1] * e1;
-        kh0[rr] = kr[rr][0] * fast_exp(n0 - gr[rr][0]);
-        kh1[rr] = kr[rr][1] * fast_exp(n1 - gr[rr][1]);
-        put2(&sm.u.prop.qp[r][c0p], qr[rr][0] * e0, qr[rr][1] * e1);
+          for (int r = 0; r < 16; ++r) {
+            float s = (r == j) ? 1.f : 0.f;
+#pragma unroll
+            for (int i = 0; i < r; ++i) s -= sm.lw.Lf[16 * R + r][16 * R + i] * x[i];
+            x[r] = s;
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) ts.diag[blk][r][j] = x[r];
+          if (blk == 0) {
+#pragma unroll
+            for (int r = 0; r < 16; r += 4) {
+              *reinterpret_cast<float4*>(&ts.colT[j][16 * I + r]) =
+                  make_float4(x[r], x[r + 1], x[r + 2], x[r + 3]);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) put(&sm.Tb[16 * I + r][16 * I + j], x[r]);
+          }
+        }
       }
+      wave_sync();
+      // Block column: T_RI = -T_RR * sum_{J=I}^{R-1} L_RJ T_JI.
+      for (int R = I + 1; R < nb; ++R) {
+        const f32x4 P = tile_mma<float>(zero4(), &sm.lw.Lf[16 * R][16 * I], LF, &ts.colT[0][16 * I],
+                                        MAXC + 4, 16 * (R - I), lane);
+        *reinterpret_cast<float4*>(&ts.PT[lane & 15][4 * (lane >> 4)]) = make_float4(P[0], P[1], P[2], P[3]);
+        wave_sync();
+        const f32x4 Tn = tile_mma<float>(zero4(), &ts.diag[R - I][0][0], 20, &ts.PT[0][0], 20, 16, lane);
+        *reinterpret_cast<float4*>(&ts.colT[lane & 15][16 * R + 4 * (lane >> 4)]) =
+            make_float4(-Tn[0], -Tn[1], -Tn[2], -Tn[3]);
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        put8(&sm.u.prop.bkpT[c0p][16 * g + 8 * hb], bk0 + 8 * hb);
-        put8(&sm.u.prop.bkpT[c0p + 1][16 * g + 8 * hb], bk1 + 8 * hb);
-        put8(&sm.u.prop.khT[c0p][16 * g + 8 * hb], kh0 + 8 * hb);
-        put8(&sm.u.prop.khT[c0p + 1][16 * g + 8 * hb], kh1 + 8 * hb);
+        for (int rr = 0; rr < 4; ++rr) put(&sm.Tb[16 * R + 4 * (lane >> 4) + rr][16 * I + (lane & 15)], -Tn[rr]);
+        wave_sync();
       }
-    }
-    // ---- T = (I + L)^{-1}: diagonal 16x16 blocks by forward substitution --
-    if (wave < nb && lane < 16) {
-      const int R = wave, j = lane;
-      float x[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float s = (r == j) ? 1.f : 0.f;
-#pragma unroll
-        for (int i = 0; i < r; ++i) s -= sm.lw.Lf[16 * R + r][16 * R + i] * x[i];
-        x[r] = s;
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sm.Tf[16 * R + r][16 * R + j] = x[r];
-    }
-    __syncthreads();
-    // Off-diagonal blocks by distance d: T_RI = -T_RR * sum_{J=I}^{R-1} L_RJ T_JI.
-    for (int d = 1; d < nb; ++d) {
-      for (int e = tid; e < (nb - d) * 256; e += kThreads) {
-        const int I = e >> 8, R = I + d, r = (e >> 4) & 15, jc = e & 15;
-        float s = 0.f;
-        for (int J = I; J < R; ++J)
-#pragma unroll
-          for (int x = 0; x < 16; ++x) s += sm.lw.Lf[16 * R + r][16 * J + x] * sm.Tf[16 * J + x][16 * I + jc];
-        sm.Tf[16 * I + r][16 * R + jc] = s;  // upper block (I, R): scratch
-      }
-      __syncthreads();
-      for (int e = tid; e < (nb - d) * 256; e += kThreads) {
-        const int I = e >> 8, R = I + d, r = (e >> 4) & 15, jc = e & 15;
-        float s = 0.f;
-#pragma unroll
-        for (int x = 0; x < 16; ++x) s -= sm.Tf[16 * R + r][16 * R + x] * sm.Tf[16 * I + x][16 * R + jc];
-        sm.Tf[16 * R + r][16 * I + jc] = s;
-      }
-      __syncthreads();
-    }
-    for (int e = tid; e < 16 * nb * 16 * nb; e += kThreads) {
-      const int r = e / (16 * nb), i = e % (16 * nb);
-      put(&sm.Tb[r][i], i <= r ? sm.Tf[r][i] : 0.f);
     }
     __syncthreads();
 
-    // ---- W^T = (beta k g)^T T^T (stored as W row-major); Ut = T (beta V) ---
-    for (int tw = wave; tw < NCT * nb; tw += 4) {
-      const int ct = tw / nb, R = tw % nb;
-      const f32x4 acc = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, &sm.u.prop.bkpT[16 * ct][0], LC,
-                                 &sm.Tb[16 * R][0], LC, 16 * (R + 1), lane);
-      const float x[4] = {acc[0], acc[1], acc[2], acc[3]};
-      put4(&sm.lw.w[16 * R + (lane & 15)][16 * ct + 4 * (lane >> 4)], x);
-    }
-    f32x4 ut[NJT];
-    if (wave < nb) {
+    // ---- propagation operands (chunk-start reference); next chunk's loads --
+    if (act) {
+      float bk0[RPG], bk1[RPG], kh0[RPG], kh1[RPG];
 #pragma unroll
-      for (int jt = 0; jt < NJT; ++jt)
-        ut[jt] = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, &sm.Tb[16 * wave][0], LC, &sm.bvT[16 * jt][0],
-                          LC, 16 * (wave + 1), lane);
+      for (int rr = 0; rr < RPG; ++rr) {
+        const int r = r0 + rr;
+        const float e0 = fast_exp(gr[rr][0]), e1 = fast_exp(gr[rr][1]);
+        const float b = sm.beta[r];
+        const float2 kk = TR::unpack(raw.k[rr]), qq = TR::unpack(raw.q[rr]);
+        bk0[rr] = b * kk.x * e0;
+        bk1[rr] = b * kk.y * e1;
+        kh0[rr] = kk.x * fast_exp(ge0 - gr[rr][0]);
+        kh1[rr] = kk.y * fast_exp(ge1 - gr[rr][1]);
+        put2(&sm.u.prop.qp[r][c0p], qq.x * e0, qq.y * e1);
+      }
+      putn<RPG>(&sm.u.prop.bkpT[c0p][r0], bk0);
+      putn<RPG>(&sm.u.prop.bkpT[c0p + 1][r0], bk1);
+      putn<RPG>(&sm.u.prop.khT[c0p][r0], kh0);
+      putn<RPG>(&sm.u.prop.khT[c0p + 1][r0], kh1);
+    }
+    if (t0n < hi) issue(t0n, endn - t0n);
+    __syncthreads();
+
+    // ---- W^T = (beta k g)^T T^T (stored as W row-major); Ut = T (beta V) ---
+    for (int x = wave; x < NCT * nb; x += NW) {
+      const int ct = x / nb, R = x % nb;
+      const f32x4 acc = tile_mma<ST>(zero4(), &sm.u.prop.bkpT[16 * ct][0], LC, &sm.Tb[16 * R][0], LC,
+                                     16 * (R + 1), lane);
+      const float v4[4] = {acc[0], acc[1], acc[2], acc[3]};
+      put4(&sm.lw.w[16 * R + (lane & 15)][16 * ct + 4 * (lane >> 4)], v4);
+    }
+    // This wave's (row block, column tile) pairs: x = wave + NW*m < nb*NJT.
+    f32x4 ut[NUT];
+#pragma unroll
+    for (int m = 0; m < NUT; ++m) {
+      const int x = wave + NW * m;
+      ut[m] = zero4();
+      if (x < nb * NJT) {
+        const int R = x / NJT, jt = x % NJT;
+        ut[m] = tile_mma<ST>(ut[m], &sm.Tb[16 * R][0], LC, &sm.buf.bvT[16 * jt][0], LC, 16 * (R + 1), lane);
+      }
     }
     __syncthreads();
 
     // ---- U = Ut - W S  (stored transposed) --------------------------------
-    if (wave < nb) {
 #pragma unroll
-      for (int jt = 0; jt < NJT; ++jt) {
-        const f32x4 ws = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, &sm.lw.w[16 * wave][0], LDK,
-                                  &sm.sT[16 * jt][0], LDK, DK, lane);
-        float x[4];
+    for (int m = 0; m < NUT; ++m) {
+      const int x = wave + NW * m;
+      if (x < nb * NJT) {
+        const int R = x / NJT, jt = x % NJT;
+        const f32x4 ws = tile_mma<ST>(zero4(), &sm.lw.w[16 * R][0], LDK, &sm.sT[16 * jt][0], LDK, DK, lane);
+        float v4[4];
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) x[rr] = ut[jt][rr] - ws[rr];
-        put4(&sm.uT[16 * jt + (lane & 15)][16 * wave + 4 * (lane >> 4)], x);
+        for (int rr = 0; rr < 4; ++rr) v4[rr] = ut[m][rr] - ws[rr];
+        put4(&sm.buf.uT[16 * jt + (lane & 15)][16 * R + 4 * (lane >> 4)], v4);
       }
     }
     __syncthreads();
 
     // ---- O = (q g) S + Aqk U;  S <- diag(g_n) S + (k g_n/g)^T U ------------
-    if (wave < nb) {
 #pragma unroll
-      for (int jt = 0; jt < NJT; ++jt) {
-        f32x4 acc = tile_mma(f32x4{0.f, 0.f, 0.f, 0.f}, &sm.u.prop.qp[16 * wave][0], LDK,
-                             &sm.sT[16 * jt][0], LDK, DK, lane);
-        acc = tile_mma(acc, &sm.aqk[16 * wave][0], LC, &sm.uT[16 * jt][0], LC, 16 * (wave + 1),
-                       lane);
+    for (int m = 0; m < NUT; ++m) {
+      const int x = wave + NW * m;
+      if (x < nb * NJT) {
+        const int R = x / NJT, jt = x % NJT;
+        f32x4 acc = tile_mma<ST>(zero4(), &sm.u.prop.qp[16 * R][0], LDK, &sm.sT[16 * jt][0], LDK, DK, lane);
+        acc = tile_mma<ST>(acc, &sm.aqk[16 * R][0], LC, &sm.buf.uT[16 * jt][0], LC, 16 * (R + 1), lane);
         const int j = j0 + 16 * jt + (lane & 15);
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const int r = 16 * wave + 4 * (lane >> 4) + rr;
+          const int r = 16 * R + 4 * (lane >> 4) + rr;
           if (r < n) go[(static_cast<size_t>(t0 + r) * H + h) * dv + j] = from_f32<InT>(acc[rr]);
         }
       }
     }
+    {
+      const ST* A[NS];
+      const ST* B[NS];
 #pragma unroll
-    for (int u = 0; u < NS; ++u) {
-      const int s = wave + 4 * u;
-      if (s < NST) {
+      for (int u = 0; u < NS; ++u) {
+        const int s = min(wave + NW * u, NST - 1);
         const int ct = s / NJT, jt = s % NJT;
         const int c0 = 16 * ct + 4 * (lane >> 4);
+        if (wave + NW * u < NST) {
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) S[u][rr] *= sm.gexp[c0 + rr];
-        S[u] = tile_mma(S[u], &sm.u.prop.khT[16 * ct][0], LC, &sm.uT[16 * jt][0], LC, 16 * nb, lane);
+          for (int rr = 0; rr < 4; ++rr) S[u][rr] *= sm.gexp[c0 + rr];
+        }
+        A[u] = &sm.u.prop.khT[16 * ct][0];
+        B[u] = &sm.buf.uT[16 * jt][0];
+      }
+      // Batches of at most four tiles keep the operand fragments in registers.
+      constexpr int NB4 = NS < 4 ? NS : 4;
+#pragma unroll
+      for (int u0 = 0; u0 < NS; u0 += NB4) {
+        if (wave + NW * (u0 + NB4 - 1) < NST) {
+          tiles_mma<NB4>(S + u0, A + u0, LC, B + u0, LC, 16 * nb, lane);
+        } else {
+#pragma unroll
+          for (int u = u0; u < u0 + NB4; ++u)
+            if (wave + NW * u < NST) S[u] = tile_mma<ST>(S[u], A[u], LC, B[u], LC, 16 * nb, lane);
+        }
       }
     }
     __syncthreads();
     write_sT();
 
-    if (ck < ck_hi && end == lo + p.ck_pos[ck]) {
+    if (is_ck) {
       store_state(p.page_pool + static_cast<int64_t>(p.ck_slot[ck]) * p.page_elems +
                   static_cast<int64_t>(h) * DK * dv);
-      ++ck;
     }
-    t0 = end;
+    t0 = t0n;
+    end = endn;
+    ck = ckn;
   }
   if (p.s_final != nullptr) store_state(p.s_final + state_off);
 }
 
+constexpr int kWaves = 8;
+
 template <int DK, int DVT, typename InT>
 hipError_t launch_t(const PrefillArgs& a, const Params& prm) {
   const dim3 grid(static_cast<unsigned>(a.n_chains) * static_cast<unsigned>(a.dv_tiles));
-  hipLaunchKernelGGL((prefill_kernel<DK, DVT, InT>), grid, dim3(kThreads), 0, a.stream, prm);
+  hipLaunchKernelGGL((prefill_kernel<DK, DVT, InT, kWaves>), grid, dim3(64 * kWaves), 0, a.stream, prm);
   return hipGetLastError();
 }
 
@@ -533,6 +696,9 @@ hipError_t launch_dvt(const PrefillArgs& a, const Params& prm) {
     case 16: return launch_dt<DK, 16>(a, prm);
     case 32: return launch_dt<DK, 32>(a, prm);
     case 64: return launch_dt<DK, 64>(a, prm);
+    case 128:
+      if (a.bf16) return launch_t<DK, 128, bf16raw>(a, prm);  // fp32 operands do not fit LDS
+      break;
   }
   return hipErrorInvalidValue;
 }

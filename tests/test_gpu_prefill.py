@@ -93,7 +93,7 @@ def test_varlen_ragged_with_checkpoints(dk, dv, dtype, chunk):
     _check(w, dtype, o, sf, pool, slots)
 
 
-@pytest.mark.parametrize("split", [2, 4, 8])
+@pytest.mark.parametrize("split", [1, 2, 4, 8])
 def test_explicit_dv_splits_agree(split):
     w = inputs.prefill_workload(40, [200, 77], 2, 128, 128, "bf16", s0_std=0.1, ckpt_every=64)
     o, sf, pool, slots = _run(w, "bf16", 64, dv_split=split)
