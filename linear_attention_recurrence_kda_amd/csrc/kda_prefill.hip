@@ -163,12 +163,41 @@ __device__ __forceinline__ void tiles_mma(f32x4* acc, const float* const* A, int
   }
 }
 
+// fp32 operands rounded once to bf16 (single product), for paths whose other
+// operands are bf16 already.
+__device__ __forceinline__ void round8(const float* p, bf16x8& hi) {
+  const float4 x0 = *reinterpret_cast<const float4*>(p);
+  const float4 x1 = *reinterpret_cast<const float4*>(p + 4);
+  const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) hi[i] = static_cast<__bf16>(x[i]);
+}
+
+__device__ __forceinline__ f32x4 tile_mma_round(f32x4 acc, const float* A, int lda, const float* Bt,
+                                                int ldb, int kvalid, int lane) {
+  const int row = lane & 15, kk = (lane >> 4) * 8;
+  for (int k0 = 0; k0 < kvalid; k0 += 32) {
+    bf16x8 ah = zero8(), bh = zero8();
+    if (k0 + kk < kvalid) {
+      round8(A + row * lda + kk + k0, ah);
+      round8(Bt + row * ldb + kk + k0, bh);
+    }
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+  }
+  return acc;
+}
+
 template <typename ST>
 __device__ __forceinline__ f32x4 tile_mma(f32x4 acc, const ST* A, int lda, const ST* Bt, int ldb,
                                           int kvalid, int lane) {
   tiles_mma<1>(&acc, &A, lda, &Bt, ldb, kvalid, lane);
   return acc;
 }
+
+template <typename ST>
+constexpr bool kSplitT = false;
+template <>
+constexpr bool kSplitT<float> = true;
 
 struct Params {
   const void *q, *k, *v, *a, *beta;
@@ -378,13 +407,16 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(Params p) {
   auto issue = [&](int t, int n) {
     if (g < NG && r0 < n) {
       const size_t base = (static_cast<size_t>(t) * H + h) * DK + c0p;
-      const size_t rstride = static_cast<size_t>(H) * DK;
+      const InT* pk = gk + base;
+      const InT* pq = gq + base;
+      const InT* pa = ga + base;
+      const int rstride = H * DK;  // a chunk spans < 2^31 elements
 #pragma unroll
       for (int rr = 0; rr < RPG; ++rr) {
-        const size_t off = base + static_cast<size_t>(min(r0 + rr, n - 1)) * rstride;
-        raw.k[rr] = TR::load(gk, off);
-        raw.q[rr] = TR::load(gq, off);
-        raw.a[rr] = TR::load(ga, off);
+        const int off = min(r0 + rr, n - 1) * rstride;
+        raw.k[rr] = TR::load(pk, off);
+        raw.q[rr] = TR::load(pq, off);
+        raw.a[rr] = TR::load(pa, off);
       }
     }
     if (rv0 < n && tid < (MAXC / RV) * VP) {
@@ -415,7 +447,8 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(Params p) {
     // ---- unpack the chunk; per-group cumulative sums of a ----------------
     // k and q stay packed in `raw` (rows past n zeroed) until the next
     // chunk's loads are issued; gr holds the running sums of a.
-    float gr[RPG][2];
+    float gr[RPG][2];   // cumulative log-decay, then e^{G - G_m} (after the Gram operands)
+    float gd[RPG][2];   // e^{G_m - G}
     if (act) {
       float run0 = 0.f, run1 = 0.f;
 #pragma unroll
@@ -448,8 +481,9 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(Params p) {
     // ---- cumulative sums across groups; Gram operands ---------------------
     // Reference: end of 16-row block nb/2 - 1 (chunk start when nb = 1).
     float ge0 = 0.f, ge1 = 0.f;  // G at the chunk's last row
+    float rf0 = 0.f, rf1 = 0.f;  // G at the reference row
     if (act) {
-      float pre0 = 0.f, pre1 = 0.f, rf0 = 0.f, rf1 = 0.f;
+      float pre0 = 0.f, pre1 = 0.f;
       const int gref = 16 * (nb >> 1) / RPG;
       for (int gg = 0; gg < ngc; ++gg) {
         const float t0v = sm.tot[gg][c0p], t1v = sm.tot[gg][c0p + 1];
@@ -465,6 +499,8 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(Params p) {
         const float d0 = gr[rr][0] - rf0, d1 = gr[rr][1] - rf1;
         const float up0 = fast_exp(d0), up1 = fast_exp(d1);
         const float dn0 = fast_exp(-d0), dn1 = fast_exp(-d1);
+        gr[rr][0] = up0; gr[rr][1] = up1;
+        gd[rr][0] = dn0; gd[rr][1] = dn1;
         const float2 kk = TR::unpack(raw.k[rr]), qq = TR::unpack(raw.q[rr]);
         put2(&sm.u.gram.kpm[r][c0p], kk.x * up0, kk.y * up1);
         put2(&sm.u.gram.qpm[r][c0p], qq.x * up0, qq.y * up1);
@@ -521,13 +557,25 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(Params p) {
       {
         const int blk = lane >> 4, R = I + blk, j = lane & 15;
         if (R < nb) {
-          float x[16];
+          // Right-looking: once x[i] is final, fold it into every later row.
+          // Column i+1 of L is loaded while column i is applied; the
+          // scheduling barrier keeps at most two columns in registers.
+          float x[16], lc[16], ln[16];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float s = (r == j) ? 1.f : 0.f;
+          for (int r = 0; r < 16; ++r) x[r] = (r == j) ? 1.f : 0.f;
 #pragma unroll
-            for (int i = 0; i < r; ++i) s -= sm.lw.Lf[16 * R + r][16 * R + i] * x[i];
-            x[r] = s;
+          for (int r = 1; r < 16; ++r) lc[r] = sm.lw.Lf[16 * R + r][16 * R];
+#pragma unroll
+          for (int i = 0; i < 15; ++i) {
+            if (i + 1 < 15) {
+#pragma unroll
+              for (int r = i + 2; r < 16; ++r) ln[r] = sm.lw.Lf[16 * R + r][16 * R + i + 1];
+            }
+#pragma unroll
+            for (int r = i + 1; r < 16; ++r) x[r] -= lc[r] * x[i];
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int r = i + 2; r < 16; ++r) lc[r] = ln[r];
           }
 #pragma unroll
           for (int r = 0; r < 16; ++r) ts.diag[blk][r][j] = x[r];
@@ -545,11 +593,18 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(Params p) {
       wave_sync();
       // Block column: T_RI = -T_RR * sum_{J=I}^{R-1} L_RJ T_JI.
       for (int R = I + 1; R < nb; ++R) {
-        const f32x4 P = tile_mma<float>(zero4(), &sm.lw.Lf[16 * R][16 * I], LF, &ts.colT[0][16 * I],
-                                        MAXC + 4, 16 * (R - I), lane);
+        // bf16 inputs: one bf16 product (T is stored in bf16 anyway); fp32
+        // inputs: hi/lo split products.
+        const f32x4 P = kSplitT<ST>
+            ? tile_mma<float>(zero4(), &sm.lw.Lf[16 * R][16 * I], LF, &ts.colT[0][16 * I], MAXC + 4,
+                              16 * (R - I), lane)
+            : tile_mma_round(zero4(), &sm.lw.Lf[16 * R][16 * I], LF, &ts.colT[0][16 * I], MAXC + 4,
+                             16 * (R - I), lane);
         *reinterpret_cast<float4*>(&ts.PT[lane & 15][4 * (lane >> 4)]) = make_float4(P[0], P[1], P[2], P[3]);
         wave_sync();
-        const f32x4 Tn = tile_mma<float>(zero4(), &ts.diag[R - I][0][0], 20, &ts.PT[0][0], 20, 16, lane);
+        const f32x4 Tn = kSplitT<ST>
+            ? tile_mma<float>(zero4(), &ts.diag[R - I][0][0], 20, &ts.PT[0][0], 20, 16, lane)
+            : tile_mma_round(zero4(), &ts.diag[R - I][0][0], 20, &ts.PT[0][0], 20, 16, lane);
         *reinterpret_cast<float4*>(&ts.colT[lane & 15][16 * R + 4 * (lane >> 4)]) =
             make_float4(-Tn[0], -Tn[1], -Tn[2], -Tn[3]);
 #pragma unroll
@@ -561,17 +616,20 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(Params p) {
 
     // ---- propagation operands (chunk-start reference); next chunk's loads --
     if (act) {
+      // e^{G} = e^{G - G_m} e^{G_m} and e^{G_n - G} = e^{G_m - G} e^{G_n - G_m}.
+      const float em0 = fast_exp(rf0), em1 = fast_exp(rf1);
+      const float en0 = fast_exp(ge0 - rf0), en1 = fast_exp(ge1 - rf1);
       float bk0[RPG], bk1[RPG], kh0[RPG], kh1[RPG];
 #pragma unroll
       for (int rr = 0; rr < RPG; ++rr) {
         const int r = r0 + rr;
-        const float e0 = fast_exp(gr[rr][0]), e1 = fast_exp(gr[rr][1]);
+        const float e0 = gr[rr][0] * em0, e1 = gr[rr][1] * em1;
         const float b = sm.beta[r];
         const float2 kk = TR::unpack(raw.k[rr]), qq = TR::unpack(raw.q[rr]);
         bk0[rr] = b * kk.x * e0;
         bk1[rr] = b * kk.y * e1;
-        kh0[rr] = kk.x * fast_exp(ge0 - gr[rr][0]);
-        kh1[rr] = kk.y * fast_exp(ge1 - gr[rr][1]);
+        kh0[rr] = kk.x * (gd[rr][0] * en0);
+        kh1[rr] = kk.y * (gd[rr][1] * en1);
         put2(&sm.u.prop.qp[r][c0p], qq.x * e0, qq.y * e1);
       }
       putn<RPG>(&sm.u.prop.bkpT[c0p][r0], bk0);

@@ -15,7 +15,10 @@
 //   o_j = r_j + beta d_j (k . q)          (= S_new^T q)
 // The sums over i (the key dimension) are split over row groups: partial sums
 // in registers, a cross-lane butterfly inside the wave, then LDS across
-// waves.  Replay (the "verify_and_replay" of §1.2) runs n_accepted such steps
+// waves.  State stores are nontemporal (the state is streamed once per call
+// and is larger than the caches); an out-of-place sweep also loads the
+// committed state nontemporally, while an in-place one (decode) keeps plain
+// loads, which measured fastest on MI355X for the read-then-overwrite pattern.  Replay (the "verify_and_replay" of §1.2) runs n_accepted such steps
 // on the register-resident state, reading a committed state it never writes.
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
@@ -23,17 +26,28 @@
 namespace kda {
 namespace {
 
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
 template <int DK, int DV>
 struct SweepShape {
-  static constexpr int CG = DV / 4;                       // float4 column groups
-  static constexpr int NT = (CG * DK < 256) ? CG * DK : 256;  // threads
-  static constexpr int RG = NT / CG;                      // row groups
-  static constexpr int RPT = DK / RG;                     // rows per thread
-  static constexpr int NW = NT / kWave;                   // waves (>= 1)
-  static_assert(DV % 4 == 0 && NT % kWave == 0 && DK % RG == 0, "shape");
+  static constexpr int CG = DV / 4;                    // float4 column groups
+  static constexpr int TARGET = DK * DV / 16;          // about 16 state values per thread
+  static constexpr int NT = TARGET < 64 ? 64 : (TARGET > 256 ? 256 : TARGET);  // threads
+  static constexpr int RG = NT / CG;                   // row groups
+  static constexpr int RPT = DK / RG;                  // rows per thread
+  static constexpr int NW = NT / kWave;                // waves
+  static constexpr int EK = (DK + NT - 1) / NT;        // key-side inputs per thread
+  static constexpr int EV = (DV + NT - 1) / NT;        // value inputs per thread
+  static_assert(DV % 4 == 0 && NT % kWave == 0 && RG * CG == NT && DK % RG == 0, "shape");
 };
 
-template <int DK, int DV, typename InT>
+// Orders this wave's LDS writes before its later LDS reads across lanes.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <int DK, int DV, typename InT, bool INPLACE>
 __global__ __launch_bounds__((SweepShape<DK, DV>::NT)) void sweep_kernel(
     const float* s_in, float* s_out, const InT* __restrict__ q, const InT* __restrict__ k,
     const InT* __restrict__ v, const InT* __restrict__ a, const InT* __restrict__ beta,
@@ -41,6 +55,7 @@ __global__ __launch_bounds__((SweepShape<DK, DV>::NT)) void sweep_kernel(
     int o_steps, int32_t* __restrict__ err_flag) {
   using Sh = SweepShape<DK, DV>;
   constexpr int CG = Sh::CG, RG = Sh::RG, RPT = Sh::RPT, NW = Sh::NW, NT = Sh::NT;
+  constexpr int EK = Sh::EK, EV = Sh::EV;
 
   const int bh = blockIdx.x;  // b * H + h
   const int b = bh / H;
@@ -50,9 +65,10 @@ __global__ __launch_bounds__((SweepShape<DK, DV>::NT)) void sweep_kernel(
   const int lane = tid % kWave;
   const int wave = tid / kWave;
 
-  __shared__ float s_k[DK], s_q[DK], s_e[DK], s_v[DV];
-  __shared__ float s_beta;
-  __shared__ float s_red[NW > 1 ? NW : 1][CG][9];
+  // Step inputs, double-buffered: step i+1 is fetched while step i computes.
+  __shared__ float s_k[2][DK], s_q[2][DK], s_e[2][DK], s_v[2][DV];
+  __shared__ float s_beta[2];
+  __shared__ float s_red[NW][CG][9];
 
   int n = t_draft;
   if (n_accepted != nullptr) {
@@ -69,28 +85,68 @@ __global__ __launch_bounds__((SweepShape<DK, DV>::NT)) void sweep_kernel(
 #pragma unroll
   for (int m = 0; m < RPT; ++m) {
     const int r = rg + m * RG;
-    S[m] = *reinterpret_cast<const float4*>(s_in + sbase + static_cast<size_t>(r) * DV + 4 * cg);
+    const f32x4v* sp = reinterpret_cast<const f32x4v*>(s_in + sbase + static_cast<size_t>(r) * DV + 4 * cg);
+    const f32x4v x = INPLACE ? *sp : __builtin_nontemporal_load(sp);
+    S[m] = make_float4(x[0], x[1], x[2], x[3]);
   }
 
-  for (int i = 0; i < n; ++i) {
+  float rk[EK], rq[EK], ra[EK], rv[EV], rb = 0.f;
+  auto fetch = [&](int i) {  // step i's inputs into registers
     const size_t tok = static_cast<size_t>(i) * B * H + bh;  // (i, b, h) in (Td, B, H)
-    __syncthreads();  // previous step's readers of the LDS inputs are done
-    for (int x = tid; x < DK; x += NT) {
-      s_k[x] = to_f32(k[tok * DK + x]);
-      s_q[x] = to_f32(q[tok * DK + x]);
-      s_e[x] = fast_exp(to_f32(a[tok * DK + x]));
+#pragma unroll
+    for (int e = 0; e < EK; ++e) {
+      const int x = tid + e * NT;
+      if (x < DK) {
+        rk[e] = to_f32(k[tok * DK + x]);
+        rq[e] = to_f32(q[tok * DK + x]);
+        ra[e] = to_f32(a[tok * DK + x]);
+      }
     }
-    for (int x = tid; x < DV; x += NT) s_v[x] = to_f32(v[tok * DV + x]);
-    if (tid == 0) s_beta = to_f32(beta[tok]);
-    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < EV; ++e) {
+      const int x = tid + e * NT;
+      if (x < DV) rv[e] = to_f32(v[tok * DV + x]);
+    }
+    if (tid == 0) rb = to_f32(beta[tok]);
+  };
+  auto stash = [&](int buf) {  // registers -> LDS buffer
+#pragma unroll
+    for (int e = 0; e < EK; ++e) {
+      const int x = tid + e * NT;
+      if (x < DK) {
+        s_k[buf][x] = rk[e];
+        s_q[buf][x] = rq[e];
+        s_e[buf][x] = fast_exp(ra[e]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < EV; ++e) {
+      const int x = tid + e * NT;
+      if (x < DV) s_v[buf][x] = rv[e];
+    }
+    if (tid == 0) s_beta[buf] = rb;
+  };
+  auto sync = [&]() {
+    if constexpr (NW > 1) __syncthreads();
+    else wave_sync();
+  };
+
+  if (n > 0) {
+    fetch(0);
+    stash(0);
+    sync();
+  }
+  for (int i = 0; i < n; ++i) {
+    const int cur = i & 1;
+    if (i + 1 < n) fetch(i + 1);
 
     // Partial sums over this thread's rows.
     float pk[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f}, kq = 0.f;
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
       const int r = rg + m * RG;
-      const float e = s_e[r], kr = s_k[r] * e, qr = s_q[r] * e;
-      kq += s_k[r] * s_q[r];
+      const float e = s_e[cur][r], kr = s_k[cur][r] * e, qr = s_q[cur][r] * e;
+      kq += s_k[cur][r] * s_q[cur][r];
       pk[0] += kr * S[m].x; pk[1] += kr * S[m].y; pk[2] += kr * S[m].z; pk[3] += kr * S[m].w;
       pq[0] += qr * S[m].x; pq[1] += qr * S[m].y; pq[2] += qr * S[m].z; pq[3] += qr * S[m].w;
     }
@@ -128,17 +184,17 @@ __global__ __launch_bounds__((SweepShape<DK, DV>::NT)) void sweep_kernel(
       }
     }
 
-    const float bt = s_beta;
+    const float bt = s_beta[cur];
     float d[4], out[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      d[c] = s_v[4 * cg + c] - pk[c];
+      d[c] = s_v[cur][4 * cg + c] - pk[c];
       out[c] = pq[c] + bt * d[c] * kq;
     }
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
       const int r = rg + m * RG;
-      const float e = s_e[r], bk = bt * s_k[r];
+      const float e = s_e[cur][r], bk = bt * s_k[cur][r];
       S[m].x = e * S[m].x + bk * d[0];
       S[m].y = e * S[m].y + bk * d[1];
       S[m].z = e * S[m].z + bk * d[2];
@@ -149,6 +205,8 @@ __global__ __launch_bounds__((SweepShape<DK, DV>::NT)) void sweep_kernel(
 #pragma unroll
       for (int c = 0; c < 4; ++c) op[c] = from_f32<InT>(out[c]);
     }
+    if (i + 1 < n) stash(cur ^ 1);
+    sync();  // step i's readers are done; step i+1's inputs are visible
   }
 
   // Rows past the accepted prefix are zero.
@@ -163,7 +221,8 @@ __global__ __launch_bounds__((SweepShape<DK, DV>::NT)) void sweep_kernel(
 #pragma unroll
   for (int m = 0; m < RPT; ++m) {
     const int r = rg + m * RG;
-    *reinterpret_cast<float4*>(s_out + sbase + static_cast<size_t>(r) * DV + 4 * cg) = S[m];
+    const f32x4v x = {S[m].x, S[m].y, S[m].z, S[m].w};
+    __builtin_nontemporal_store(x, reinterpret_cast<f32x4v*>(s_out + sbase + static_cast<size_t>(r) * DV + 4 * cg));
   }
 }
 
@@ -171,11 +230,18 @@ template <int DK, int DV, typename InT>
 hipError_t launch_sweep_t(const SweepArgs& p) {
   using Sh = SweepShape<DK, DV>;
   const dim3 grid(static_cast<unsigned>(p.B) * static_cast<unsigned>(p.H));
-  hipLaunchKernelGGL((sweep_kernel<DK, DV, InT>), grid, dim3(Sh::NT), 0, p.stream, p.s_in,
-                     p.s_out, static_cast<const InT*>(p.q), static_cast<const InT*>(p.k),
-                     static_cast<const InT*>(p.v), static_cast<const InT*>(p.a),
-                     static_cast<const InT*>(p.beta), p.n_accepted, p.t_draft, p.B, p.H,
-                     static_cast<InT*>(p.o), p.o_steps, p.err_flag);
+  if (p.s_in == p.s_out)
+    hipLaunchKernelGGL((sweep_kernel<DK, DV, InT, true>), grid, dim3(Sh::NT), 0, p.stream, p.s_in,
+                       p.s_out, static_cast<const InT*>(p.q), static_cast<const InT*>(p.k),
+                       static_cast<const InT*>(p.v), static_cast<const InT*>(p.a),
+                       static_cast<const InT*>(p.beta), p.n_accepted, p.t_draft, p.B, p.H,
+                       static_cast<InT*>(p.o), p.o_steps, p.err_flag);
+  else
+    hipLaunchKernelGGL((sweep_kernel<DK, DV, InT, false>), grid, dim3(Sh::NT), 0, p.stream, p.s_in,
+                       p.s_out, static_cast<const InT*>(p.q), static_cast<const InT*>(p.k),
+                       static_cast<const InT*>(p.v), static_cast<const InT*>(p.a),
+                       static_cast<const InT*>(p.beta), p.n_accepted, p.t_draft, p.B, p.H,
+                       static_cast<InT*>(p.o), p.o_steps, p.err_flag);
   return hipGetLastError();
 }
 
