@@ -284,6 +284,44 @@ def cpu_baseline(inputs, w):
                       f"sequence (all 32 heads, dk=dv=128) of the same workload; {dt:.1f} s"}
 
 
+def write_traffic(fetch_csv, write_csv, name="prefill_varlen"):
+    """Turn two rocprofv3 counter passes into the traffic figure reported above.
+
+    fetch_csv / write_csv: counter_collection CSVs of a FETCH_SIZE pass and a
+    WRITE_SIZE pass over `bench.py --only prefill4,copycal --steps 1 --warmup 0
+    --no-cpu` (KiB per dispatch).  The calibration copy of that run (1 GiB
+    read and written) scales the counters to bytes.  Writes
+    profiles/<name>_traffic.json, stamped with the kernel source hash."""
+    import csv
+
+    def per_kernel(path, counter):
+        out = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)
+        return out
+
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    kname = next(k for k in fetch if "prefill_kernel" in k)
+    f_pre = float(np.mean(fetch[kname]))
+    w_pre = float(np.mean(write[kname]))
+    f_cp = max(v for k, vals in fetch.items() if "prefill" not in k for v in vals)
+    w_cp = max(v for k, vals in write.items() if "prefill" not in k for v in vals)
+    copy_bytes = float(1 << 30)
+    res = {"kernel": kname, "fetch_bytes_raw": f_pre, "write_bytes_raw": w_pre,
+           "copy_fetch_bytes_raw": f_cp, "copy_write_bytes_raw": w_cp,
+           "fetch_scale": copy_bytes / f_cp, "write_scale": copy_bytes / w_cp,
+           "hbm_bytes_per_launch": f_pre * copy_bytes / f_cp + w_pre * copy_bytes / w_cp,
+           "kernel_src_sha256_16": src_hash(PREFILL_SRC),
+           "command": "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out> -o fetch -- "
+                      "python3 <repo>/bench.py --only prefill4,copycal --steps 1 --warmup 0 --no-cpu "
+                      "(then the same with WRITE_SIZE)"}
+    out = os.path.join(PROFILES, f"{name}_traffic.json")
+    with open(out, "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res, indent=1))
+
+
 # ---------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -294,7 +332,12 @@ def main():
                                                "replay_big, pack, copycal")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--json-out", default="")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/prefill_varlen_traffic.json from two counter passes")
     args = ap.parse_args()
+    if args.traffic:
+        write_traffic(*args.traffic)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the KDA hot path here has no multi-GPU step "
