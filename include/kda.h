@@ -154,7 +154,7 @@ int kda_unpack_heads(const float* page_pool, int64_t page_elems, int64_t n_slots
  *              cu[n_seqs] = T_tot.  Zero-length sequences are allowed.
  *   s0       : [n_seqs, H, dk, dv] fp32 committed states, READ ONLY, or NULL
  *              for zero states.  Outputs must not overlap it (KDA_EALIAS).
- *   o        : [T_tot, H, dv] (in_dtype)
+ *   o        : [T_tot, H, dv] (in_dtype), 16-byte aligned (KDA_EINVAL otherwise)
  *   s_final  : [n_seqs, H, dk, dv] fp32 or NULL
  *   Checkpoints ([KDA cache] "Kimi K3 预览版与 vLLM 的细粒度检查点": one slot
  *   holds one exact boundary, e.g. the tail C(P6976)):
@@ -168,7 +168,7 @@ int kda_unpack_heads(const float* page_pool, int64_t page_elems, int64_t n_slots
  *                    is written in the pack layout and zero-padded
  *   workspace      : device memory of at least kda_chunk_prefill_workspace_size
  *                    bytes, 256-byte aligned; contents on entry are ignored
- * Sizes: T_tot < 2^31 tokens, H*dk*dv < 2^31.
+ * Sizes: T_tot < 2^31 tokens, H*dk*dv < 2^31, H*max(dk, dv) <= 2^24.
  */
 int kda_chunk_prefill_workspace_size(int32_t n_seqs, int64_t total_tokens, int32_t H,
                                      int32_t dk, int32_t dv, int32_t chunk, int64_t n_ckpt,
@@ -188,8 +188,9 @@ int kda_chunk_prefill(const void* q, const void* k, const void* v, const void* a
  * workgroups per (sequence, head) chain: the dv columns of the state are
  * independent in the recurrence (column j of S depends only on column j of
  * v), so a chain can be split into dv_split column tiles that each redo the
- * key-side chunk work.  dv_split in {1, 2, 4, 8} with dv / dv_split a
- * multiple of 16, or 0 to let the library choose from the sequence lengths.
+ * key-side chunk work.  dv_split in {1, 2, 4, 8} with dv / dv_split one of
+ * 16, 32 or 64 (so dv = 128 takes at least 2), or 0 to let the library
+ * choose from the sequence lengths.  Other values: KDA_EUNSUPPORTED.
  */
 int kda_chunk_prefill_split(const void* q, const void* k, const void* v, const void* a,
                             const void* beta, kda_dtype in_dtype, int32_t H, int32_t dk,

@@ -23,13 +23,13 @@ size_t work_ints(int32_t n_seqs, int32_t H, int64_t n_ckpt) {
   return static_cast<size_t>(2 * round8(static_cast<int64_t>(n_seqs) * H) + 4 * n_seqs + 2 * n_ckpt);
 }
 
-// dv columns per workgroup: 16..64, or 128 for bf16 inputs (fp32 operands of a
-// 128-column tile do not fit in LDS).
-bool valid_tile(int32_t dv, int32_t split, bool bf16) {
+// dv columns per workgroup: 16, 32 or 64 (a 128-column tile's operands do
+// not fit in LDS).
+bool valid_tile(int32_t dv, int32_t split) {
   if (split != 1 && split != 2 && split != 4 && split != 8) return false;
   if (dv % split) return false;
   const int t = dv / split;
-  return t == 16 || t == 32 || t == 64 || (t == 128 && bf16);
+  return t == 16 || t == 32 || t == 64;
 }
 
 // Chunks of one sequence: chunks never cross a checkpoint position.
@@ -45,14 +45,14 @@ int64_t seq_chunks(int32_t len, const int32_t* pos, int32_t npos, int32_t chunk)
 }
 
 // Pick the dv split from a per-chunk cost model (MFMA tile counts): key-side
-// work (Gram products, W) is repeated by every split, value-side work scales
+// work (Gram products, T) is repeated by every split, value-side work scales
 // with the tile width; the chip time is the larger of the total work over the
 // CUs and the longest chain.
-int choose_split(int32_t dk, int32_t dv, bool bf16, int64_t total_chunks, int64_t max_chunks) {
+int choose_split(int32_t dk, int32_t dv, int64_t total_chunks, int64_t max_chunks) {
   int best = 0;
   double best_t = 0;
   for (int split : {1, 2, 4, 8}) {
-    if (!valid_tile(dv, split, bf16)) continue;
+    if (!valid_tile(dv, split)) continue;
     const double tile = static_cast<double>(dv) / split;
     const double cost = 1.5 * dk + (3.0 * dk / 8 + 12.0) * tile / 16.0;
     const double t = std::max(static_cast<double>(total_chunks) * split * cost / kCUs,
@@ -102,6 +102,9 @@ int kda_chunk_prefill_split(const void* q, const void* k, const void* v, const v
     return fail(KDA_EUNSUPPORTED, "chunk=%d: fp32 inputs take chunks of at most 32 rows", chunk);
   const int64_t hkv = static_cast<int64_t>(H) * dk * dv;
   if (hkv >= (int64_t{1} << 31)) return fail(KDA_EUNSUPPORTED, "H*dk*dv must be below 2^31");
+  // The kernel addresses one chunk's rows with 32-bit byte offsets.
+  if (static_cast<int64_t>(H) * std::max(dk, dv) > (int64_t{1} << 24))
+    return fail(KDA_EUNSUPPORTED, "H*max(dk, dv) must be at most 2^24");
   if (n_seqs == 0) return ok();
   if (!cu) return fail(KDA_EINVAL, "cu_seqlens is null");
   if (cu[0] != 0) return fail(KDA_EINVAL, "cu_seqlens[0] = %d, must be 0", cu[0]);
@@ -152,9 +155,9 @@ int kda_chunk_prefill_split(const void* q, const void* k, const void* v, const v
   }
   int split = dv_split;
   const bool bf16 = in_dtype == KDA_BF16;
-  if (split == 0) split = choose_split(dk, dv, bf16, total_chunks, max_chunks);
-  if (!valid_tile(dv, split, bf16))
-    return fail(KDA_EUNSUPPORTED, "dv_split=%d with dv=%d (dv/split must be 16, 32, 64, or 128 for bf16)",
+  if (split == 0) split = choose_split(dk, dv, total_chunks, max_chunks);
+  if (!valid_tile(dv, split))
+    return fail(KDA_EUNSUPPORTED, "dv_split=%d with dv=%d (dv/split must be 16, 32 or 64)",
                 dv_split, dv);
 
   // Buffers.
@@ -164,6 +167,8 @@ int kda_chunk_prefill_split(const void* q, const void* k, const void* v, const v
   for (const void* ptr : {q, k, v, a})
     if (reinterpret_cast<uintptr_t>(ptr) % (2 * es))
       return fail(KDA_EINVAL, "q, k, v, a must be aligned to two elements");
+  // Output rows are written in 16-byte pieces.
+  if (reinterpret_cast<uintptr_t>(o) % 16) return fail(KDA_EINVAL, "o must be 16-byte aligned");
   const size_t need = (work_ints(n_seqs, H, n_ckpt) * 4 + 255) / 256 * 256;
   if (!workspace || workspace_bytes < need)
     return fail(KDA_EWORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);

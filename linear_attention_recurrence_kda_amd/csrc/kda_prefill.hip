@@ -10,10 +10,12 @@
 //   G_r = sum_{i<=r} a_i (per key channel),  g_r = exp(G_r)
 //   L   = diag(beta) strict_lower(Kp Km^T),   Kp_r = k_r*e^{G_r-G_m}, Km_i = k_i*e^{G_m-G_i}
 //   T   = (I + L)^{-1}                        (unit lower triangular)
-//   W   = T diag(beta) (k*g),   Ut = T diag(beta) V
-//   U   = Ut - W S
+//   Z   = diag(beta) (V - (k*g) S)            (the residual at the chunk start)
+//   U   = T Z
 //   O   = (q*g) S + lower(Qp Km^T) U,         Qp_r = q_r*e^{G_r-G_m}
 //   S  <- diag(g_n) S + (k*g_n/g)^T U
+// (U = T diag(beta) V - (T diag(beta) (k*g)) S is the WY form; taking the
+// residual first needs no W = T diag(beta) (k*g) at all.)
 // The reference G_m is the cumulative sum through the middle 16-row block
 // boundary, so every scaled Gram operand stays within e^{+-|a|*C/2}: finite in
 // bf16/fp32 for per-token log-decays a >= -2.5 at a chunk of 64.  Every other
@@ -163,28 +165,13 @@ __device__ __forceinline__ void tiles_mma(f32x4* acc, const float* const* A, int
   }
 }
 
-// fp32 operands rounded once to bf16 (single product), for paths whose other
-// operands are bf16 already.
+// fp32 operands rounded once to bf16.
 __device__ __forceinline__ void round8(const float* p, bf16x8& hi) {
   const float4 x0 = *reinterpret_cast<const float4*>(p);
   const float4 x1 = *reinterpret_cast<const float4*>(p + 4);
   const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
   for (int i = 0; i < 8; ++i) hi[i] = static_cast<__bf16>(x[i]);
-}
-
-__device__ __forceinline__ f32x4 tile_mma_round(f32x4 acc, const float* A, int lda, const float* Bt,
-                                                int ldb, int kvalid, int lane) {
-  const int row = lane & 15, kk = (lane >> 4) * 8;
-  for (int k0 = 0; k0 < kvalid; k0 += 32) {
-    bf16x8 ah = zero8(), bh = zero8();
-    if (k0 + kk < kvalid) {
-      round8(A + row * lda + kk + k0, ah);
-      round8(Bt + row * ldb + kk + k0, bh);
-    }
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
-  }
-  return acc;
 }
 
 template <typename ST>
@@ -194,10 +181,25 @@ __device__ __forceinline__ f32x4 tile_mma(f32x4 acc, const ST* A, int lda, const
   return acc;
 }
 
-template <typename ST>
-constexpr bool kSplitT = false;
-template <>
-constexpr bool kSplitT<float> = true;
+// A fp32 (LDS) times B stored as bf16: A rounded once to bf16.
+__device__ __forceinline__ f32x4 tile_mma_fb(f32x4 acc, const float* A, int lda, const __bf16* Bt,
+                                             int ldb, int kvalid, int lane) {
+  const int row = lane & 15, kk = (lane >> 4) * 8;
+  for (int k0 = 0; k0 < kvalid; k0 += 32) {
+    bf16x8 ah = zero8(), bh = zero8();
+    if (k0 + kk < kvalid) {
+      round8(A + row * lda + kk + k0, ah);
+      bh = *reinterpret_cast<const bf16x8*>(Bt + row * ldb + kk + k0);
+    }
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+  }
+  return acc;
+}
+// A fp32 times B fp32: hi/lo split (fp32 inputs).
+__device__ __forceinline__ f32x4 tile_mma_fb(f32x4 acc, const float* A, int lda, const float* Bt,
+                                             int ldb, int kvalid, int lane) {
+  return tile_mma<float>(acc, A, lda, Bt, ldb, kvalid, lane);
+}
 
 struct Params {
   const void *q, *k, *v, *a, *beta;
@@ -215,10 +217,10 @@ struct Params {
 
 template <typename ST>
 struct TScratch {  // one wave's workspace for its block column of T
-  static constexpr int MAXC = Op<ST>::MAXC;
-  float diag[4][16][20];      // T_RR, row-major, for R = I .. I+3
-  float colT[16][MAXC + 4];   // colT[i][j] = T[j][16 I + i]
-  float PT[16][20];           // P^T of the current step
+  static constexpr int MAXC = Op<ST>::MAXC, PAD = Op<ST>::PAD;
+  ST diag[MAXC / 16][16][16 + PAD];  // T_RR, row-major, for R = I .. nb-1
+  ST colT[16][MAXC + PAD];    // colT[i][j] = T[j][16 I + i]
+  ST PT[16][16 + PAD];        // P^T of the current step
 };
 
 template <int DK, int DVT, typename ST, int NG>
@@ -231,21 +233,24 @@ struct Smem {
     struct {  // key-side operands of the Gram products (mid-chunk reference)
       ST kpm[MAXC][LDK], qpm[MAXC][LDK], kmm[MAXC][LDK];
     } gram;
-    TScratch<ST> ts[4];
     struct {  // chunk-start scaled operands of the propagation
-      ST bkpT[DK][LC];      // (beta * k * g)^T
+      ST kp[MAXC][LDK];     // k * g
       ST qp[MAXC][LDK];     // q * g
       ST khT[DK][LC];       // (k * g_n / g)^T
     } prop;
   } u;
-  union {                   // (beta*v)^T is dead once Ut is formed; U^T follows it
-    ST bvT[DVT][LC];        // (beta * v)^T, this workgroup's columns
+  TScratch<ST> ts[MAXC / 16];  // block columns of T (written while prop is)
+  union {                   // v^T is dead once Z is formed; U^T follows it
+    ST vT[DVT][LC];         // v^T, this workgroup's columns
     ST uT[DVT][LC];         // U^T
   } buf;
+  union __attribute__((aligned(16))) {  // Z^T is dead once U is formed; O follows it
+    ST zT[DVT][LC];         // Z^T
+    ST o[MAXC][DVT + Op<ST>::PAD];  // this chunk's outputs, row-major
+  } zo;
   ST sT[DVT][LDK];          // S^T
-  union {
+  struct {
     float Lf[MAXC][LF];     // diag(beta) strict_lower(A_kk), fp32
-    ST w[MAXC][LDK];        // W, row-major
   } lw;
   ST Tb[MAXC][LC];          // T
   ST aqk[MAXC][LC];         // lower(Qp Km^T)
@@ -260,8 +265,8 @@ template <>
 struct Traits<bf16raw> {
   using ST = __bf16;
   using Pair = uint32_t;  // two consecutive bf16 values
-  static __device__ __forceinline__ Pair load(const bf16raw* p, size_t off) {
-    return *reinterpret_cast<const uint32_t*>(p + off);
+  static __device__ __forceinline__ Pair load(const char* p) {
+    return *reinterpret_cast<const uint32_t*>(p);
   }
   static __device__ __forceinline__ float2 unpack(Pair x) {
     return make_float2(__uint_as_float(x << 16), __uint_as_float(x & 0xffff0000u));
@@ -272,8 +277,8 @@ template <>
 struct Traits<float> {
   using ST = float;
   using Pair = float2;
-  static __device__ __forceinline__ Pair load(const float* p, size_t off) {
-    return *reinterpret_cast<const float2*>(p + off);
+  static __device__ __forceinline__ Pair load(const char* p) {
+    return *reinterpret_cast<const float2*>(p);
   }
   static __device__ __forceinline__ float2 unpack(Pair x) { return x; }
   static __device__ __forceinline__ Pair zero() { return make_float2(0.f, 0.f); }
@@ -285,12 +290,10 @@ struct Raw {
   using Pair = typename Traits<InT>::Pair;
   Pair k[RPG], q[RPG], a[RPG];  // rows g*RPG .. +RPG, channels 2cp, 2cp+1
   Pair v[RV];                   // rows rv0 .. rv0+RV-1, columns 2jp, 2jp+1 of the tile
-  float vb[RV];                 // beta of those rows
-  float b;                      // beta of row tid
+  InT b;                        // beta of row tid
+  // Values stay in their stored form until used: converting at the load
+  // would make the wave wait for the loads it has just issued.
 };
-
-__device__ __forceinline__ float ld1(const float* p, size_t i) { return p[i]; }
-__device__ __forceinline__ float ld1(const bf16raw* p, size_t i) { return to_f32(p[i]); }
 
 // Thread and tile mappings of one workgroup of NW waves.
 template <int DK, int DVT, typename ST, int NW>
@@ -313,6 +316,7 @@ template <int DK, int DVT, typename InT, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(Params p) {
   using TR = Traits<InT>;
   using ST = typename TR::ST;
+  using Pair = typename TR::Pair;
   using SH = Shape<DK, DVT, ST, NW>;
   using SM = Smem<DK, DVT, ST, SH::NG>;
   constexpr int NT = SH::NT, MAXC = SH::MAXC, HK = SH::HK, RPG = SH::RPG, NG = SH::NG;
@@ -401,38 +405,62 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(Params p) {
     if (c < ck_hi) e = min(e, lo + p.ck_pos[c]);
     return e;
   };
-  // Issue the loads of rows [t, t+n) into registers (addresses clamped to
-  // valid rows; rows past n are masked when unpacked).
+  // Issue the loads of rows [t, t+n) into registers.  Each chunk's base
+  // addresses are wave-uniform; per-lane byte offsets inside a chunk are
+  // loop-invariant 32-bit values (the host bounds H * max(dk, dv) so that a
+  // chunk spans less than 4 GiB), clamped to the chunk's last row.  Rows
+  // past n are masked when unpacked.
+  constexpr uint32_t ES = sizeof(InT);
+  const uint32_t rsk = static_cast<uint32_t>(H) * DK * ES;  // row strides, bytes
+  const uint32_t rsv = static_cast<uint32_t>(H) * dv * ES;
+  const uint32_t rsb = static_cast<uint32_t>(H) * ES;
+  const uint32_t ok0 = r0 * rsk + c0p * ES;
+  const uint32_t ov0 = rv0 * rsv + 2 * jp * ES;
+  // The loads go out in three parts, each as soon as the previous chunk's
+  // values are dead, so that no phase queues a chunk's worth of loads:
+  // part 0 (a, v, beta) after the unpack, part 1 (k) and part 2 (q) after the
+  // propagation operands.
   Raw<InT, RPG, RV> raw;
-  auto issue = [&](int t, int n) {
-    if (g < NG && r0 < n) {
-      const size_t base = (static_cast<size_t>(t) * H + h) * DK + c0p;
-      const InT* pk = gk + base;
-      const InT* pq = gq + base;
-      const InT* pa = ga + base;
-      const int rstride = H * DK;  // a chunk spans < 2^31 elements
+  auto issue = [&](int part, int t_, int n_) {
+    const int t = __builtin_amdgcn_readfirstlane(t_), n = __builtin_amdgcn_readfirstlane(n_);
+    const size_t row0 = static_cast<size_t>(t) * H + h;
+    if (part > 0) {
+      if (g < NG) {
+        const char* bx = reinterpret_cast<const char*>((part == 1 ? gk : gq) + row0 * DK);
+        const uint32_t okl = (n - 1) * rsk + c0p * ES;
 #pragma unroll
-      for (int rr = 0; rr < RPG; ++rr) {
-        const int off = min(r0 + rr, n - 1) * rstride;
-        raw.k[rr] = TR::load(pk, off);
-        raw.q[rr] = TR::load(pq, off);
-        raw.a[rr] = TR::load(pa, off);
+        for (int rr = 0; rr < RPG; ++rr) {
+          const Pair x = TR::load(bx + min(ok0 + rr * rsk, okl));
+          if (part == 1) raw.k[rr] = x;
+          else raw.q[rr] = x;
+        }
       }
+      return;
     }
-    if (rv0 < n && tid < (MAXC / RV) * VP) {
+    const char* bb = reinterpret_cast<const char*>(gb + row0);
+    const uint32_t obl = (n - 1) * rsb;
+    if (g < NG) {
+      const char* ba = reinterpret_cast<const char*>(ga + row0 * DK);
+      const uint32_t okl = (n - 1) * rsk + c0p * ES;
 #pragma unroll
-      for (int e = 0; e < RV; ++e) {
-        const size_t tr = static_cast<size_t>(t + min(rv0 + e, n - 1)) * H + h;
-        raw.v[e] = TR::load(gv, tr * dv + j0 + 2 * jp);
-        raw.vb[e] = ld1(gb, tr);
-      }
+      for (int rr = 0; rr < RPG; ++rr) raw.a[rr] = TR::load(ba + min(ok0 + rr * rsk, okl));
     }
-    if (tid < n) raw.b = ld1(gb, static_cast<size_t>(t + tid) * H + h);
+    if (tid < (MAXC / RV) * VP) {
+      const char* bv = reinterpret_cast<const char*>(gv + row0 * dv + j0);
+      const uint32_t ovl = (n - 1) * rsv + 2 * jp * ES;
+#pragma unroll
+      for (int e = 0; e < RV; ++e) raw.v[e] = TR::load(bv + min(ov0 + e * rsv, ovl));
+    }
+    if (tid < MAXC) raw.b = *reinterpret_cast<const InT*>(bb + min(tid * rsb, obl));
   };
 
   int t0 = lo, ck = ck_lo;
   int end = t0 < hi ? chunk_end(t0, ck) : t0;
-  if (t0 < hi) issue(t0, end - t0);
+  if (t0 < hi) {
+    issue(0, t0, end - t0);
+    issue(1, t0, end - t0);
+    issue(2, t0, end - t0);
+  }
 
   while (t0 < hi) {
     const int n = end - t0;
@@ -462,21 +490,21 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(Params p) {
       sm.tot[g][c0p] = run0;
       sm.tot[g][c0p + 1] = run1;
     }
-    if (tid < 16 * nb) sm.beta[tid] = tid < n ? raw.b : 0.f;
+    if (tid < 16 * nb) sm.beta[tid] = tid < n ? to_f32(raw.b) : 0.f;
     if (rv0 < 16 * nb && tid < (MAXC / RV) * VP) {
       float x0[RV], x1[RV];
 #pragma unroll
       for (int e = 0; e < RV; ++e) {
         const bool valid = rv0 + e < n;
         const float2 vv = TR::unpack(valid ? raw.v[e] : TR::zero());
-        const float b = valid ? raw.vb[e] : 0.f;
-        x0[e] = b * vv.x;
-        x1[e] = b * vv.y;
+        x0[e] = vv.x;
+        x1[e] = vv.y;
       }
-      putn<RV>(&sm.buf.bvT[2 * jp][rv0], x0);
-      putn<RV>(&sm.buf.bvT[2 * jp + 1][rv0], x1);
+      putn<RV>(&sm.buf.vT[2 * jp][rv0], x0);
+      putn<RV>(&sm.buf.vT[2 * jp + 1][rv0], x1);
     }
     __syncthreads();
+    if (t0n < hi) issue(0, t0n, endn - t0n);
 
     // ---- cumulative sums across groups; Gram operands ---------------------
     // Reference: end of 16-row block nb/2 - 1 (chunk start when nb = 1).
@@ -549,10 +577,11 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(Params p) {
     }
     __syncthreads();
 
-    // ---- T = (I + L)^{-1}, one block column per wave ----------------------
+    // ---- T = (I + L)^{-1}, one block column per wave; propagation operands
     if (wave < nb) {
       const int I = wave;
-      TScratch<ST>& ts = sm.u.ts[wave];
+      TScratch<ST>& ts = sm.ts[wave];
+      constexpr int LD = 16 + Op<ST>::PAD, LCT = MAXC + Op<ST>::PAD;
       // Diagonal inverses T_RR for R = I .. nb-1: lane = 16*(R-I) + column.
       {
         const int blk = lane >> 4, R = I + blk, j = lane & 15;
@@ -578,13 +607,10 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(Params p) {
             for (int r = i + 2; r < 16; ++r) lc[r] = ln[r];
           }
 #pragma unroll
-          for (int r = 0; r < 16; ++r) ts.diag[blk][r][j] = x[r];
+          for (int r = 0; r < 16; ++r) put(&ts.diag[blk][r][j], x[r]);
           if (blk == 0) {
 #pragma unroll
-            for (int r = 0; r < 16; r += 4) {
-              *reinterpret_cast<float4*>(&ts.colT[j][16 * I + r]) =
-                  make_float4(x[r], x[r + 1], x[r + 2], x[r + 3]);
-            }
+            for (int r = 0; r < 16; r += 4) put4(&ts.colT[j][16 * I + r], x + r);
 #pragma unroll
             for (int r = 0; r < 16; ++r) put(&sm.Tb[16 * I + r][16 * I + j], x[r]);
           }
@@ -593,103 +619,90 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(Params p) {
       wave_sync();
       // Block column: T_RI = -T_RR * sum_{J=I}^{R-1} L_RJ T_JI.
       for (int R = I + 1; R < nb; ++R) {
-        // bf16 inputs: one bf16 product (T is stored in bf16 anyway); fp32
-        // inputs: hi/lo split products.
-        const f32x4 P = kSplitT<ST>
-            ? tile_mma<float>(zero4(), &sm.lw.Lf[16 * R][16 * I], LF, &ts.colT[0][16 * I], MAXC + 4,
-                              16 * (R - I), lane)
-            : tile_mma_round(zero4(), &sm.lw.Lf[16 * R][16 * I], LF, &ts.colT[0][16 * I], MAXC + 4,
-                             16 * (R - I), lane);
-        *reinterpret_cast<float4*>(&ts.PT[lane & 15][4 * (lane >> 4)]) = make_float4(P[0], P[1], P[2], P[3]);
+        const f32x4 P = tile_mma_fb(zero4(), &sm.lw.Lf[16 * R][16 * I], LF, &ts.colT[0][16 * I], LCT,
+                                    16 * (R - I), lane);
+        const float pv[4] = {P[0], P[1], P[2], P[3]};
+        put4(&ts.PT[lane & 15][4 * (lane >> 4)], pv);
         wave_sync();
-        const f32x4 Tn = kSplitT<ST>
-            ? tile_mma<float>(zero4(), &ts.diag[R - I][0][0], 20, &ts.PT[0][0], 20, 16, lane)
-            : tile_mma_round(zero4(), &ts.diag[R - I][0][0], 20, &ts.PT[0][0], 20, 16, lane);
-        *reinterpret_cast<float4*>(&ts.colT[lane & 15][16 * R + 4 * (lane >> 4)]) =
-            make_float4(-Tn[0], -Tn[1], -Tn[2], -Tn[3]);
+        const f32x4 Tn = tile_mma<ST>(zero4(), &ts.diag[R - I][0][0], LD, &ts.PT[0][0], LD, 16, lane);
+        const float tv[4] = {-Tn[0], -Tn[1], -Tn[2], -Tn[3]};
+        put4(&ts.colT[lane & 15][16 * R + 4 * (lane >> 4)], tv);
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) put(&sm.Tb[16 * R + 4 * (lane >> 4) + rr][16 * I + (lane & 15)], -Tn[rr]);
+        for (int rr = 0; rr < 4; ++rr) put(&sm.Tb[16 * R + 4 * (lane >> 4) + rr][16 * I + (lane & 15)], tv[rr]);
         wave_sync();
       }
     }
-    __syncthreads();
-
-    // ---- propagation operands (chunk-start reference); next chunk's loads --
+    // (every thread, after its T work): chunk-start scaled operands; the
+    // next chunk's loads.
     if (act) {
       // e^{G} = e^{G - G_m} e^{G_m} and e^{G_n - G} = e^{G_m - G} e^{G_n - G_m}.
       const float em0 = fast_exp(rf0), em1 = fast_exp(rf1);
       const float en0 = fast_exp(ge0 - rf0), en1 = fast_exp(ge1 - rf1);
-      float bk0[RPG], bk1[RPG], kh0[RPG], kh1[RPG];
+      float kh0[RPG], kh1[RPG];
 #pragma unroll
       for (int rr = 0; rr < RPG; ++rr) {
         const int r = r0 + rr;
         const float e0 = gr[rr][0] * em0, e1 = gr[rr][1] * em1;
-        const float b = sm.beta[r];
         const float2 kk = TR::unpack(raw.k[rr]), qq = TR::unpack(raw.q[rr]);
-        bk0[rr] = b * kk.x * e0;
-        bk1[rr] = b * kk.y * e1;
         kh0[rr] = kk.x * (gd[rr][0] * en0);
         kh1[rr] = kk.y * (gd[rr][1] * en1);
+        put2(&sm.u.prop.kp[r][c0p], kk.x * e0, kk.y * e1);
         put2(&sm.u.prop.qp[r][c0p], qq.x * e0, qq.y * e1);
       }
-      putn<RPG>(&sm.u.prop.bkpT[c0p][r0], bk0);
-      putn<RPG>(&sm.u.prop.bkpT[c0p + 1][r0], bk1);
       putn<RPG>(&sm.u.prop.khT[c0p][r0], kh0);
       putn<RPG>(&sm.u.prop.khT[c0p + 1][r0], kh1);
     }
-    if (t0n < hi) issue(t0n, endn - t0n);
     __syncthreads();
+    if (t0n < hi) issue(1, t0n, endn - t0n);
 
-    // ---- W^T = (beta k g)^T T^T (stored as W row-major); Ut = T (beta V) ---
-    for (int x = wave; x < NCT * nb; x += NW) {
-      const int ct = x / nb, R = x % nb;
-      const f32x4 acc = tile_mma<ST>(zero4(), &sm.u.prop.bkpT[16 * ct][0], LC, &sm.Tb[16 * R][0], LC,
-                                     16 * (R + 1), lane);
-      const float v4[4] = {acc[0], acc[1], acc[2], acc[3]};
-      put4(&sm.lw.w[16 * R + (lane & 15)][16 * ct + 4 * (lane >> 4)], v4);
-    }
+    // ---- Z = beta V - (beta k g) S (stored transposed); QS = (q g) S --------
     // This wave's (row block, column tile) pairs: x = wave + NW*m < nb*NJT.
-    f32x4 ut[NUT];
+    f32x4 qs[NUT];
 #pragma unroll
     for (int m = 0; m < NUT; ++m) {
       const int x = wave + NW * m;
-      ut[m] = zero4();
+      qs[m] = zero4();
       if (x < nb * NJT) {
         const int R = x / NJT, jt = x % NJT;
-        ut[m] = tile_mma<ST>(ut[m], &sm.Tb[16 * R][0], LC, &sm.buf.bvT[16 * jt][0], LC, 16 * (R + 1), lane);
+        f32x4 acc[2] = {zero4(), zero4()};
+        const ST* A[2] = {&sm.u.prop.kp[16 * R][0], &sm.u.prop.qp[16 * R][0]};
+        const ST* B[2] = {&sm.sT[16 * jt][0], &sm.sT[16 * jt][0]};
+        tiles_mma<2>(acc, A, LDK, B, LDK, DK, lane);
+        qs[m] = acc[1];
+        const int jl = 16 * jt + (lane & 15), i0 = 16 * R + 4 * (lane >> 4);
+        float z[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          z[rr] = sm.beta[i0 + rr] * (static_cast<float>(sm.buf.vT[jl][i0 + rr]) - acc[0][rr]);
+        put4(&sm.zo.zT[jl][i0], z);
+      }
+    }
+    __syncthreads();
+    if (t0n < hi) issue(2, t0n, endn - t0n);
+
+    // ---- U = T Z  (stored transposed) --------------------------------------
+#pragma unroll
+    for (int m = 0; m < NUT; ++m) {
+      const int x = wave + NW * m;
+      if (x < nb * NJT) {
+        const int R = x / NJT, jt = x % NJT;
+        const f32x4 u4 = tile_mma<ST>(zero4(), &sm.Tb[16 * R][0], LC, &sm.zo.zT[16 * jt][0], LC, 16 * (R + 1), lane);
+        const float uv[4] = {u4[0], u4[1], u4[2], u4[3]};
+        put4(&sm.buf.uT[16 * jt + (lane & 15)][16 * R + 4 * (lane >> 4)], uv);
       }
     }
     __syncthreads();
 
-    // ---- U = Ut - W S  (stored transposed) --------------------------------
+    // ---- O = QS + Aqk U;  S <- diag(g_n) S + (k g_n/g)^T U -----------------
 #pragma unroll
     for (int m = 0; m < NUT; ++m) {
       const int x = wave + NW * m;
       if (x < nb * NJT) {
         const int R = x / NJT, jt = x % NJT;
-        const f32x4 ws = tile_mma<ST>(zero4(), &sm.lw.w[16 * R][0], LDK, &sm.sT[16 * jt][0], LDK, DK, lane);
-        float v4[4];
+        const f32x4 acc = tile_mma<ST>(qs[m], &sm.aqk[16 * R][0], LC, &sm.buf.uT[16 * jt][0], LC, 16 * (R + 1), lane);
+        const int jl = 16 * jt + (lane & 15), i0 = 16 * R + 4 * (lane >> 4);
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) v4[rr] = ut[m][rr] - ws[rr];
-        put4(&sm.buf.uT[16 * jt + (lane & 15)][16 * R + 4 * (lane >> 4)], v4);
-      }
-    }
-    __syncthreads();
-
-    // ---- O = (q g) S + Aqk U;  S <- diag(g_n) S + (k g_n/g)^T U ------------
-#pragma unroll
-    for (int m = 0; m < NUT; ++m) {
-      const int x = wave + NW * m;
-      if (x < nb * NJT) {
-        const int R = x / NJT, jt = x % NJT;
-        f32x4 acc = tile_mma<ST>(zero4(), &sm.u.prop.qp[16 * R][0], LDK, &sm.sT[16 * jt][0], LDK, DK, lane);
-        acc = tile_mma<ST>(acc, &sm.aqk[16 * R][0], LC, &sm.buf.uT[16 * jt][0], LC, 16 * (R + 1), lane);
-        const int j = j0 + 16 * jt + (lane & 15);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int r = 16 * R + 4 * (lane >> 4) + rr;
-          if (r < n) go[(static_cast<size_t>(t0 + r) * H + h) * dv + j] = from_f32<InT>(acc[rr]);
-        }
+        for (int rr = 0; rr < 4; ++rr) put(&sm.zo.o[i0 + rr][jl], acc[rr]);
       }
     }
     {
@@ -722,6 +735,14 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(Params p) {
     }
     __syncthreads();
     write_sT();
+    {  // this chunk's output rows, 16 bytes per thread and store
+      constexpr int PPR = DVT * static_cast<int>(ES) / 16;  // 16-byte pieces per row
+      char* bo = reinterpret_cast<char*>(go + (static_cast<size_t>(t0) * H + h) * dv + j0);
+      for (int x = tid; x < n * PPR; x += NT) {
+        const int r = x / PPR, c = (x % PPR) * (16 / static_cast<int>(ES));
+        *reinterpret_cast<i32x4*>(bo + r * rsv + c * ES) = *reinterpret_cast<const i32x4*>(&sm.zo.o[r][c]);
+      }
+    }
 
     if (is_ck) {
       store_state(p.page_pool + static_cast<int64_t>(p.ck_slot[ck]) * p.page_elems +
@@ -754,9 +775,6 @@ hipError_t launch_dvt(const PrefillArgs& a, const Params& prm) {
     case 16: return launch_dt<DK, 16>(a, prm);
     case 32: return launch_dt<DK, 32>(a, prm);
     case 64: return launch_dt<DK, 64>(a, prm);
-    case 128:
-      if (a.bf16) return launch_t<DK, 128, bf16raw>(a, prm);  // fp32 operands do not fit LDS
-      break;
   }
   return hipErrorInvalidValue;
 }

@@ -88,3 +88,46 @@ def test_pack_validation(L):
     assert L.kda_pack_heads(st, 5, 1, H, d, d, sl, pool, H * d * d, 4, None, None) == kda.KDA_EINVAL
     assert L.kda_pack_heads(st, 0, 1, H, d, d, sl, st, H * d * d, 4, None, None) == kda.KDA_EALIAS
     assert L.kda_unpack_heads(pool, H * d * d, 4, sl, 1, H, d, d, 0, pool, None, None) == kda.KDA_EALIAS
+
+
+def test_prefill_validation(L):
+    """Argument checks of the chunked prefill that run on host data only."""
+    q, k, v, a, b, o, ws = (_fake(i) for i in range(7))
+    I32 = ctypes.c_int32
+
+    def call(dtype=1, H=2, dk=128, dv=128, chunk=64, cu=(0, 40, 100), split=0, ck=None,
+             n_slots=0, o_ptr=o):
+        cu_a = (I32 * len(cu))(*cu)
+        n = len(cu) - 1
+        ck_cu = ck_pos = ck_slot = None
+        n_ck = 0
+        if ck is not None:
+            pos, slot, cuv = [], [], [0]
+            for p_s in ck:
+                pos += [p for p, _ in p_s]
+                slot += [s for _, s in p_s]
+                cuv.append(len(pos))
+            n_ck = len(pos)
+            ck_cu, ck_pos, ck_slot = ((I32 * max(len(x), 1))(*x) for x in (cuv, pos, slot))
+        pool = _fake(9) if ck is not None else None
+        return L.kda_chunk_prefill_split(q, k, v, a, b, dtype, H, dk, dv, chunk, cu_a, n, None, o_ptr,
+                                         None, ck_cu, ck_pos, ck_slot, n_ck, pool, H * dk * dv,
+                                         n_slots, ws, 1 << 20, split, None)
+
+    assert call(dk=24) == kda.KDA_EUNSUPPORTED
+    assert call(chunk=48 + 8) == kda.KDA_EUNSUPPORTED
+    assert call(chunk=80) == kda.KDA_EUNSUPPORTED
+    assert call(dtype=0, chunk=64) == kda.KDA_EUNSUPPORTED  # fp32 inputs: chunk <= 32
+    assert call(split=1) == kda.KDA_EUNSUPPORTED            # 128-column dv tile
+    assert call(split=3) == kda.KDA_EUNSUPPORTED
+    assert call(cu=(1, 40)) == kda.KDA_EINVAL
+    assert call(cu=(0, 40, 30)) == kda.KDA_EINVAL
+    assert call(ck=[[(41, 0)], []], n_slots=2) == kda.KDA_EINVAL          # past the sequence
+    assert call(ck=[[(20, 0), (10, 1)], []], n_slots=2) == kda.KDA_EINVAL  # not increasing
+    assert call(ck=[[(20, 0)], [(5, 0)]], n_slots=2) == kda.KDA_EINVAL     # slot repeated
+    assert call(ck=[[(20, 2)], []], n_slots=2) == kda.KDA_EINVAL           # slot out of range
+    assert b"slot" in L.kda_last_error()
+    assert call(o_ptr=P(o.value + 8)) == kda.KDA_EINVAL                   # o rows need 16 bytes
+    assert b"o must be 16-byte aligned" in L.kda_last_error()
+    assert call(H=(1 << 17) + 1, dk=16) == kda.KDA_EUNSUPPORTED           # 32-bit chunk offsets
+    assert b"2^24" in L.kda_last_error()
