@@ -229,7 +229,26 @@ struct Smem {
   static constexpr int LDK = DK + Op<ST>::PAD;   // row length of [*][DK] buffers
   static constexpr int LC = MAXC + Op<ST>::PAD;  // row length of [*][chunk] buffers
   static constexpr int LF = MAXC + 4;            // row length of fp32 [chunk][chunk]
-  union {
+  // Small, latency-critical buffers first (low LDS addresses).
+  __attribute__((aligned(16))) float beta[MAXC];
+  float gexp[DK];           // g_n
+  float tot[NG][DK];        // per-row-group sums of a
+  struct {
+    float Lf[MAXC][LF];     // diag(beta) strict_lower(A_kk), fp32
+  } lw;
+  TScratch<ST> ts[MAXC / 16];  // block columns of T (written while prop is)
+  ST Tb[MAXC][LC];          // T
+  ST aqk[MAXC][LC];         // lower(Qp Km^T)
+  ST sT[DVT][LDK];          // S^T
+  union {                   // v^T is dead once Z is formed; U^T follows it
+    ST vT[DVT][LC];         // v^T, this workgroup's columns
+    ST uT[DVT][LC];         // U^T
+  } buf;
+  union __attribute__((aligned(16))) {  // Z^T is dead once U is formed; O follows it
+    ST zT[DVT][LC];         // Z^T
+    ST o[MAXC][DVT + Op<ST>::PAD];  // this chunk's outputs, row-major
+  } zo;
+  union __attribute__((aligned(16))) {
     struct {  // key-side operands of the Gram products (mid-chunk reference)
       ST kpm[MAXC][LDK], qpm[MAXC][LDK], kmm[MAXC][LDK];
     } gram;
@@ -239,24 +258,6 @@ struct Smem {
       ST khT[DK][LC];       // (k * g_n / g)^T
     } prop;
   } u;
-  TScratch<ST> ts[MAXC / 16];  // block columns of T (written while prop is)
-  union {                   // v^T is dead once Z is formed; U^T follows it
-    ST vT[DVT][LC];         // v^T, this workgroup's columns
-    ST uT[DVT][LC];         // U^T
-  } buf;
-  union __attribute__((aligned(16))) {  // Z^T is dead once U is formed; O follows it
-    ST zT[DVT][LC];         // Z^T
-    ST o[MAXC][DVT + Op<ST>::PAD];  // this chunk's outputs, row-major
-  } zo;
-  ST sT[DVT][LDK];          // S^T
-  struct {
-    float Lf[MAXC][LF];     // diag(beta) strict_lower(A_kk), fp32
-  } lw;
-  ST Tb[MAXC][LC];          // T
-  ST aqk[MAXC][LC];         // lower(Qp Km^T)
-  float tot[NG][DK];        // per-row-group sums of a
-  float gexp[DK];           // g_n
-  __attribute__((aligned(16))) float beta[MAXC];
 };
 
 template <typename InT>
