@@ -167,12 +167,19 @@ int kda_unpack_heads(const float* page_pool, int64_t page_elems, int64_t n_slots
  *   page_pool      : fp32 [n_slots, page_elems], page_elems >= H*dk*dv; a slot
  *                    is written in the pack layout and zero-padded
  *   workspace      : device memory of at least kda_chunk_prefill_workspace_size
- *                    bytes, 256-byte aligned; contents on entry are ignored
- * Sizes: T_tot < 2^31 tokens, H*dk*dv < 2^31, H*max(dk, dv) <= 2^24.
+ *                    bytes, 256-byte aligned; contents on entry are ignored.  It
+ *                    holds the work list and, per (chunk, head), the chunk's
+ *                    T diag(beta) and lower(A_qk) tiles (2 * chunk^2 elements
+ *                    of in_dtype), written by a first kernel that handles all
+ *                    chunks at once and read by the sequential one: about
+ *                    (T_tot / chunk + n_seqs + n_ckpt) * H * 2 * chunk^2 * 2
+ *                    bytes for bf16 (0.9 GB for 128k tokens, H = 32, chunk 64).
+ * Sizes: T_tot < 2^31 tokens, H*dk*dv < 2^31, H*max(dk, dv) <= 2^24, and
+ * (number of chunks) * H < 2^31.
  */
 int kda_chunk_prefill_workspace_size(int32_t n_seqs, int64_t total_tokens, int32_t H,
                                      int32_t dk, int32_t dv, int32_t chunk, int64_t n_ckpt,
-                                     size_t* bytes);
+                                     kda_dtype in_dtype, size_t* bytes);
 
 int kda_chunk_prefill(const void* q, const void* k, const void* v, const void* a,
                       const void* beta, kda_dtype in_dtype, int32_t H, int32_t dk,
@@ -188,9 +195,10 @@ int kda_chunk_prefill(const void* q, const void* k, const void* v, const void* a
  * workgroups per (sequence, head) chain: the dv columns of the state are
  * independent in the recurrence (column j of S depends only on column j of
  * v), so a chain can be split into dv_split column tiles that each redo the
- * key-side chunk work.  dv_split in {1, 2, 4, 8} with dv / dv_split one of
- * 16, 32 or 64 (so dv = 128 takes at least 2), or 0 to let the library
- * choose from the sequence lengths.  Other values: KDA_EUNSUPPORTED.
+ * chunk's key-side scaling.  dv_split in {1, 2, 4, 8} with dv / dv_split one
+ * of 16, 32 or 64, or 128 for bf16 inputs (so fp32 inputs with dv = 128 take
+ * at least 2), or 0 to let the library choose from the sequence lengths.
+ * Other values: KDA_EUNSUPPORTED.
  */
 int kda_chunk_prefill_split(const void* q, const void* k, const void* v, const void* a,
                             const void* beta, kda_dtype in_dtype, int32_t H, int32_t dk,

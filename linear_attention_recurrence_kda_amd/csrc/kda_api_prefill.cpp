@@ -15,21 +15,35 @@ using namespace kda_host;
 
 namespace {
 
-constexpr int kCUs = 256;  // MI355X compute units (one prefill workgroup per CU)
+constexpr int kCUs = 256;  // MI355X compute units (one propagation workgroup per CU)
 
 int64_t round8(int64_t x) { return (x + 7) / 8 * 8; }
 
-size_t work_ints(int32_t n_seqs, int32_t H, int64_t n_ckpt) {
-  return static_cast<size_t>(2 * round8(static_cast<int64_t>(n_seqs) * H) + 4 * n_seqs + 2 * n_ckpt);
+// Chunks never cross a sequence end or a checkpoint, so a sequence of length
+// L with m checkpoints has at most L / chunk + m + 1 of them.
+int64_t max_chunks(int32_t n_seqs, int64_t total_tokens, int32_t chunk, int64_t n_ckpt) {
+  return total_tokens / chunk + n_seqs + n_ckpt;
 }
 
-// dv columns per workgroup: 16, 32 or 64 (a 128-column tile's operands do
-// not fit in LDS).
-bool valid_tile(int32_t dv, int32_t split) {
+// Workspace: the int32 work list, then (256-byte aligned) the per
+// (chunk, head) tiles T diag(beta) and lower(A_qk), chunk x chunk each, in
+// the operand precision (bf16 for bf16 inputs, fp32 for fp32 inputs).
+size_t work_ints(int32_t n_seqs, int32_t H, int64_t n_ckpt, int64_t n_chunks) {
+  return static_cast<size_t>(2 * round8(static_cast<int64_t>(n_seqs) * H) + 6 * n_seqs + 2 * n_ckpt +
+                             2 * n_chunks);
+}
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+size_t tile_bytes(int64_t n_chunks, int32_t H, int32_t chunk, size_t es) {
+  return static_cast<size_t>(n_chunks) * H * 2 * chunk * chunk * es;
+}
+
+// dv columns per workgroup: 16, 32 or 64, or 128 for bf16 inputs (fp32
+// operands of a 128-column tile do not fit in LDS).
+bool valid_tile(int32_t dv, int32_t split, bool bf16) {
   if (split != 1 && split != 2 && split != 4 && split != 8) return false;
   if (dv % split) return false;
   const int t = dv / split;
-  return t == 16 || t == 32 || t == 64;
+  return t == 16 || t == 32 || t == 64 || (t == 128 && bf16);
 }
 
 // Chunks of one sequence: chunks never cross a checkpoint position.
@@ -48,15 +62,15 @@ int64_t seq_chunks(int32_t len, const int32_t* pos, int32_t npos, int32_t chunk)
 // work (Gram products, T) is repeated by every split, value-side work scales
 // with the tile width; the chip time is the larger of the total work over the
 // CUs and the longest chain.
-int choose_split(int32_t dk, int32_t dv, int64_t total_chunks, int64_t max_chunks) {
+int choose_split(int32_t dk, int32_t dv, bool bf16, int64_t total_chunks, int64_t longest) {
   int best = 0;
   double best_t = 0;
   for (int split : {1, 2, 4, 8}) {
-    if (!valid_tile(dv, split)) continue;
+    if (!valid_tile(dv, split, bf16)) continue;
     const double tile = static_cast<double>(dv) / split;
     const double cost = 1.5 * dk + (3.0 * dk / 8 + 12.0) * tile / 16.0;
     const double t = std::max(static_cast<double>(total_chunks) * split * cost / kCUs,
-                              static_cast<double>(max_chunks) * cost);
+                              static_cast<double>(longest) * cost);
     if (best == 0 || t < best_t * 0.999) {
       best = split;
       best_t = t;
@@ -70,8 +84,10 @@ int choose_split(int32_t dk, int32_t dv, int64_t total_chunks, int64_t max_chunk
 extern "C" {
 
 int kda_chunk_prefill_workspace_size(int32_t n_seqs, int64_t total_tokens, int32_t H, int32_t dk,
-                                     int32_t dv, int32_t chunk, int64_t n_ckpt, size_t* bytes) {
+                                     int32_t dv, int32_t chunk, int64_t n_ckpt, kda_dtype in_dtype,
+                                     size_t* bytes) {
   if (!bytes) return fail(KDA_EINVAL, "bytes is null");
+  if (!valid_dtype(in_dtype)) return fail(KDA_EINVAL, "in_dtype %d", static_cast<int>(in_dtype));
   if (n_seqs < 0 || total_tokens < 0 || H <= 0 || n_ckpt < 0)
     return fail(KDA_EINVAL, "n_seqs=%d total_tokens=%lld H=%d n_ckpt=%lld", n_seqs,
                 static_cast<long long>(total_tokens), H, static_cast<long long>(n_ckpt));
@@ -79,7 +95,8 @@ int kda_chunk_prefill_workspace_size(int32_t n_seqs, int64_t total_tokens, int32
     return fail(KDA_EUNSUPPORTED, "dk=%d dv=%d (supported: 16, 32, 64, 128)", dk, dv);
   if (chunk < 16 || chunk > KDA_MAX_CHUNK || chunk % 16)
     return fail(KDA_EUNSUPPORTED, "chunk=%d (a multiple of 16 up to %d)", chunk, KDA_MAX_CHUNK);
-  *bytes = (work_ints(n_seqs, H, n_ckpt) * 4 + 255) / 256 * 256;
+  const int64_t mc = max_chunks(n_seqs, total_tokens, chunk, n_ckpt);
+  *bytes = align256(work_ints(n_seqs, H, n_ckpt, mc) * 4) + tile_bytes(mc, H, chunk, elem_size(in_dtype));
   return ok();
 }
 
@@ -145,19 +162,21 @@ int kda_chunk_prefill_split(const void* q, const void* k, const void* v, const v
   }
 
   // Split.
-  int64_t total_chunks = 0, max_chunks = 0;
+  int64_t n_chunks = 0, longest = 0;
   for (int32_t i = 0; i < n_seqs; ++i) {
     const int32_t len = cu[i + 1] - cu[i];
     const int32_t c0 = ck_cu ? ck_cu[i] : 0, c1 = ck_cu ? ck_cu[i + 1] : 0;
     const int64_t c = seq_chunks(len, ck_pos ? ck_pos + c0 : nullptr, c1 - c0, chunk);
-    total_chunks += c * H;
-    max_chunks = std::max(max_chunks, c);
+    n_chunks += c;
+    longest = std::max(longest, c);
   }
+  if (n_chunks * H >= (int64_t{1} << 31)) return fail(KDA_EUNSUPPORTED, "too many (chunk, head) pairs");
   int split = dv_split;
   const bool bf16 = in_dtype == KDA_BF16;
-  if (split == 0) split = choose_split(dk, dv, total_chunks, max_chunks);
-  if (!valid_tile(dv, split))
-    return fail(KDA_EUNSUPPORTED, "dv_split=%d with dv=%d (dv/split must be 16, 32 or 64)",
+  if (split == 0) split = choose_split(dk, dv, bf16, n_chunks * H, longest);
+  if (!valid_tile(dv, split, bf16))
+    return fail(KDA_EUNSUPPORTED,
+                "dv_split=%d with dv=%d (dv/split must be 16, 32 or 64, or 128 for bf16 inputs)",
                 dv_split, dv);
 
   // Buffers.
@@ -169,10 +188,12 @@ int kda_chunk_prefill_split(const void* q, const void* k, const void* v, const v
       return fail(KDA_EINVAL, "q, k, v, a must be aligned to two elements");
   // Output rows are written in 16-byte pieces.
   if (reinterpret_cast<uintptr_t>(o) % 16) return fail(KDA_EINVAL, "o must be 16-byte aligned");
-  const size_t need = (work_ints(n_seqs, H, n_ckpt) * 4 + 255) / 256 * 256;
+  const size_t list_bytes = align256(work_ints(n_seqs, H, n_ckpt, n_chunks) * 4);
+  const size_t need = list_bytes + tile_bytes(n_chunks, H, chunk, es);
   if (!workspace || workspace_bytes < need)
     return fail(KDA_EWORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
-  if (reinterpret_cast<uintptr_t>(workspace) & 3u) return fail(KDA_EINVAL, "workspace misaligned");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(KDA_EINVAL, "workspace must be 256-byte aligned");
   const size_t tok = static_cast<size_t>(T) * H;
   const size_t sbytes = static_cast<size_t>(n_seqs) * hkv * 4;
   const std::vector<Range> ins = {{q, tok * dk * es, "q"}, {k, tok * dk * es, "k"},
@@ -193,11 +214,12 @@ int kda_chunk_prefill_split(const void* q, const void* k, const void* v, const v
   });
   const int64_t n_chains = round8(static_cast<int64_t>(n_seqs) * H);
   if (n_chains * split >= (int64_t{1} << 31)) return fail(KDA_EUNSUPPORTED, "too many chains");
-  std::vector<int32_t> work(work_ints(n_seqs, H, n_ckpt), 0);
+  std::vector<int32_t> work(work_ints(n_seqs, H, n_ckpt, n_chunks), 0);
   int32_t* chains = work.data();
   int32_t* seqinfo = chains + 2 * n_chains;
-  int32_t* wpos = seqinfo + 4 * n_seqs;
+  int32_t* wpos = seqinfo + 6 * n_seqs;
   int32_t* wslot = wpos + n_ckpt;
+  int32_t* wchunks = wslot + n_ckpt;
   int64_t c = 0;
   for (int32_t s : order)
     for (int32_t h = 0; h < H; ++h, ++c) {
@@ -208,12 +230,30 @@ int kda_chunk_prefill_split(const void* q, const void* k, const void* v, const v
     chains[2 * c] = -1;
     chains[2 * c + 1] = 0;
   }
+  // Chunk table: each sequence's chunks in order, split at its checkpoints.
+  int64_t nc = 0;
   for (int32_t i = 0; i < n_seqs; ++i) {
-    seqinfo[4 * i] = cu[i];
-    seqinfo[4 * i + 1] = cu[i + 1];
-    seqinfo[4 * i + 2] = ck_cu ? ck_cu[i] : 0;
-    seqinfo[4 * i + 3] = ck_cu ? ck_cu[i + 1] : 0;
+    const int32_t c0 = ck_cu ? ck_cu[i] : 0, c1 = ck_cu ? ck_cu[i + 1] : 0;
+    int32_t* si = seqinfo + 6 * i;
+    si[0] = cu[i];
+    si[1] = cu[i + 1];
+    si[2] = c0;
+    si[3] = c1;
+    si[4] = static_cast<int32_t>(nc);
+    int32_t t = cu[i], c = c0;
+    while (t < cu[i + 1]) {
+      int32_t e = std::min(t + chunk, cu[i + 1]);
+      if (c < c1) e = std::min(e, cu[i] + ck_pos[c]);
+      wchunks[2 * nc] = t;
+      wchunks[2 * nc + 1] = e - t;
+      ++nc;
+      if (c < c1 && e == cu[i] + ck_pos[c]) ++c;
+      t = e;
+    }
+    si[5] = static_cast<int32_t>(nc);
   }
+  if (nc != n_chunks) return fail(KDA_EINVAL, "internal: chunk count %lld != %lld",
+                                  static_cast<long long>(nc), static_cast<long long>(n_chunks));
   for (int64_t i = 0; i < n_ckpt; ++i) {
     wpos[i] = ck_pos[i];
     wslot[i] = ck_slot[i];
@@ -233,8 +273,11 @@ int kda_chunk_prefill_split(const void* q, const void* k, const void* v, const v
   p.page_pool = page_pool; p.page_elems = page_elems;
   p.chains = dwork;
   p.seqinfo = dwork + 2 * n_chains;
-  p.ck_pos = p.seqinfo + 4 * n_seqs;
+  p.ck_pos = p.seqinfo + 6 * n_seqs;
   p.ck_slot = p.ck_pos + n_ckpt;
+  p.chunks = p.ck_slot + n_ckpt;
+  p.n_chunks = static_cast<int>(n_chunks);
+  p.tq = static_cast<char*>(workspace) + list_bytes;
   p.n_chains = static_cast<int>(n_chains);
   p.dv_tiles = split;
   p.stream = hs;

@@ -53,6 +53,9 @@ struct PrefillArgs {
   float* page_pool;
   int64_t page_elems;
   const int32_t *chains, *seqinfo, *ck_pos, *ck_slot;
+  const int32_t* chunks;  // [n_chunks][2] = (first token, rows)
+  void* tq;               // [n_chunks][H][2][chunk][chunk] T diag(beta) and lower(A_qk)
+  int n_chunks;
   int n_chains;  // padded
   int dv_tiles;  // workgroups per chain (split of dv)
   hipStream_t stream;

@@ -10,35 +10,43 @@
 //   G_r = sum_{i<=r} a_i (per key channel),  g_r = exp(G_r)
 //   L   = diag(beta) strict_lower(Kp Km^T),   Kp_r = k_r*e^{G_r-G_m}, Km_i = k_i*e^{G_m-G_i}
 //   T   = (I + L)^{-1}                        (unit lower triangular)
-//   Z   = diag(beta) (V - (k*g) S)            (the residual at the chunk start)
-//   U   = T Z
+//   U   = T diag(beta) (V - (k*g) S)          (T applied to the residual at the chunk start)
 //   O   = (q*g) S + lower(Qp Km^T) U,         Qp_r = q_r*e^{G_r-G_m}
 //   S  <- diag(g_n) S + (k*g_n/g)^T U
-// (U = T diag(beta) V - (T diag(beta) (k*g)) S is the WY form; taking the
-// residual first needs no W = T diag(beta) (k*g) at all.)
-// The reference G_m is the cumulative sum through the middle 16-row block
-// boundary, so every scaled Gram operand stays within e^{+-|a|*C/2}: finite in
-// bf16/fp32 for per-token log-decays a >= -2.5 at a chunk of 64.  Every other
-// scaled operand is bounded by 1.
+// (U = T diag(beta) V - (T diag(beta) (k*g)) S is the WY form; applying T to
+// the residual needs no W = T diag(beta) (k*g) at all.)  The reference G_m is
+// the cumulative sum through the middle 16-row block boundary, so every
+// scaled Gram operand stays within e^{+-|a|*C/2}: finite in bf16/fp32 for
+// per-token log-decays a >= -2.5 at a chunk of 64.  Every other scaled
+// operand is bounded by 1.
 //
-// Mapping.  One workgroup (4 waves) runs one (sequence, head) chain over a
+// Two kernels.  T diag(beta) and lower(Qp Km^T) depend on the chunk's own
+// keys, queries, decays and betas only, never on the state, so the "local"
+// kernel computes them for every (chunk, head) at once, with as many
+// workgroups as there are such pairs, and stores them in the workspace.  The
+// "propagation" kernel then runs each (sequence, head) chain through its
+// chunks in order and does only the state-dependent products; its per-chunk
+// latency, multiplied by the longest sequence's chunk count, is the critical
+// path of the whole prefill.
+//
+// Propagation mapping.  One workgroup (8 waves) runs one chain over a
 // DVT-wide tile of the dv columns (the columns of S are independent in the
-// recurrence, so a chain can be split over several workgroups that each redo
-// the key-side work).  The fp32 state tile lives in MFMA accumulators for the
-// whole sequence; a transposed copy in LDS feeds the contractions.  All
-// contractions use v_mfma_f32_16x16x32_bf16 with operands staged in LDS: bf16
-// inputs stage bf16 operands; fp32 inputs stage fp32 operands and split each
-// into a bf16 high and low part, taking three products (hi*hi + hi*lo +
-// lo*hi, about 2^-16 relative error) so that fp32 I/O keeps fp32-level
-// accuracy (fp32 operands double the LDS footprint, so that path caps the
-// chunk at 32 rows).
-// T is built per wave without workgroup barriers: wave I inverts the 16x16
-// diagonal blocks it needs by forward substitution (64 lanes = 4 blocks x 16
-// columns) and then its block column T_RI = -T_RR sum_J L_RJ T_JI with
-// fp32-split MFMA.
-// The next chunk's raw inputs are loaded into registers while the current
-// chunk computes.  Workgroups are placed so the tiles of one chain share an
-// XCD (and its L2), and chains run longest sequence first.
+// recurrence, so a chain can be split over several workgroups).  The fp32
+// state tile lives in MFMA accumulators for the whole sequence; a transposed
+// copy in LDS feeds the contractions.  All contractions use
+// v_mfma_f32_16x16x32_bf16 with operands staged in LDS: bf16 inputs stage
+// bf16 operands; fp32 inputs stage fp32 operands and split each into a bf16
+// high and low part, taking three products (hi*hi + hi*lo + lo*hi, about
+// 2^-16 relative error) so that fp32 I/O keeps fp32-level accuracy (fp32
+// operands double the LDS footprint, so that path caps the chunk at 32 rows).
+// The next chunk's inputs, T and A_qk are loaded into registers while the
+// current chunk computes.  Workgroups are placed so the tiles of one chain
+// share an XCD (and its L2), and chains run longest sequence first.
+//
+// Local mapping.  T is built per wave without workgroup barriers: wave I
+// inverts the 16x16 diagonal blocks it needs by forward substitution (64
+// lanes = 4 blocks x 16 columns) and then its block column
+// T_RI = -T_RR sum_J L_RJ T_JI with MFMA.
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
 
@@ -201,18 +209,27 @@ __device__ __forceinline__ f32x4 tile_mma_fb(f32x4 acc, const float* A, int lda,
   return tile_mma<float>(acc, A, lda, Bt, ldb, kvalid, lane);
 }
 
-struct Params {
-  const void *q, *k, *v, *a, *beta;
+struct LocalParams {
+  const void *q, *k, *a, *beta;
+  const int32_t* chunks;   // [n_chunks][2] = (first token, rows)
+  void* tq;                // [n_chunks][H][2][ld][ld]: T diag(beta), then lower(A_qk)
+  int H, ld;
+};
+
+struct PropParams {
+  const void *q, *k, *v, *a;
+  const void* tq;
   const float* s0;
   void* o;
   float* s_final;
   float* page_pool;
   int64_t page_elems;
   const int32_t* chains;   // [n_chains][2] = (sequence or -1, head)
-  const int32_t* seqinfo;  // [n_seqs][4]  = (tok_lo, tok_hi, ck_lo, ck_hi)
+  const int32_t* seqinfo;  // [n_seqs][6]  = (tok_lo, tok_hi, ck_lo, ck_hi, chunk_lo, chunk_hi)
   const int32_t* ck_pos;   // [n_ckpt] token counts from the sequence start
   const int32_t* ck_slot;  // [n_ckpt]
-  int H, dv, chunk, dv_tiles;
+  const int32_t* chunks;   // [n_chunks][2]
+  int H, dv, ld, dv_tiles;
 };
 
 template <typename ST>
@@ -223,21 +240,35 @@ struct TScratch {  // one wave's workspace for its block column of T
   ST PT[16][16 + PAD];        // P^T of the current step
 };
 
-template <int DK, int DVT, typename ST, int NG>
-struct Smem {
+template <int DK, typename ST, int NG>
+struct LocalSmem {
   static constexpr int MAXC = Op<ST>::MAXC;
   static constexpr int LDK = DK + Op<ST>::PAD;   // row length of [*][DK] buffers
   static constexpr int LC = MAXC + Op<ST>::PAD;  // row length of [*][chunk] buffers
   static constexpr int LF = MAXC + 4;            // row length of fp32 [chunk][chunk]
-  // Small, latency-critical buffers first (low LDS addresses).
   __attribute__((aligned(16))) float beta[MAXC];
+  float tot[NG][DK];        // per-row-group sums of a
+  float Lf[MAXC][LF];       // diag(beta) strict_lower(A_kk), fp32
+  union __attribute__((aligned(16))) {
+    struct {  // scaled Gram operands (mid-chunk reference)
+      ST kpm[MAXC][LDK], qpm[MAXC][LDK], kmm[MAXC][LDK];
+    } gram;
+    struct {  // after the Gram products
+      TScratch<ST> ts[MAXC / 16];  // block columns of T
+      ST tb[MAXC][LC];             // T diag(beta)
+      ST aqk[MAXC][LC];            // lower(Qp Km^T)
+    } out;
+  } u;
+};
+
+template <int DK, int DVT, typename ST, int NG>
+struct PropSmem {
+  static constexpr int MAXC = Op<ST>::MAXC;
+  static constexpr int LDK = DK + Op<ST>::PAD;
+  static constexpr int LC = MAXC + Op<ST>::PAD;
   float gexp[DK];           // g_n
   float tot[NG][DK];        // per-row-group sums of a
-  struct {
-    float Lf[MAXC][LF];     // diag(beta) strict_lower(A_kk), fp32
-  } lw;
-  TScratch<ST> ts[MAXC / 16];  // block columns of T (written while prop is)
-  ST Tb[MAXC][LC];          // T
+  ST tb[MAXC][LC];          // T diag(beta)
   ST aqk[MAXC][LC];         // lower(Qp Km^T)
   ST sT[DVT][LDK];          // S^T
   union {                   // v^T is dead once Z is formed; U^T follows it
@@ -245,19 +276,12 @@ struct Smem {
     ST uT[DVT][LC];         // U^T
   } buf;
   union __attribute__((aligned(16))) {  // Z^T is dead once U is formed; O follows it
-    ST zT[DVT][LC];         // Z^T
+    ST zT[DVT][LC];         // Z^T = (V - (k g) S)^T
     ST o[MAXC][DVT + Op<ST>::PAD];  // this chunk's outputs, row-major
   } zo;
-  union __attribute__((aligned(16))) {
-    struct {  // key-side operands of the Gram products (mid-chunk reference)
-      ST kpm[MAXC][LDK], qpm[MAXC][LDK], kmm[MAXC][LDK];
-    } gram;
-    struct {  // chunk-start scaled operands of the propagation
-      ST kp[MAXC][LDK];     // k * g
-      ST qp[MAXC][LDK];     // q * g
-      ST khT[DK][LC];       // (k * g_n / g)^T
-    } prop;
-  } u;
+  ST kp[MAXC][LDK];         // k * g
+  ST qp[MAXC][LDK];         // q * g
+  ST khT[DK][LC];           // (k * g_n / g)^T
 };
 
 template <typename InT>
@@ -285,17 +309,6 @@ struct Traits<float> {
   static __device__ __forceinline__ Pair zero() { return make_float2(0.f, 0.f); }
 };
 
-// Raw chunk inputs held in registers from the prefetch to their use.
-template <typename InT, int RPG, int RV>
-struct Raw {
-  using Pair = typename Traits<InT>::Pair;
-  Pair k[RPG], q[RPG], a[RPG];  // rows g*RPG .. +RPG, channels 2cp, 2cp+1
-  Pair v[RV];                   // rows rv0 .. rv0+RV-1, columns 2jp, 2jp+1 of the tile
-  InT b;                        // beta of row tid
-  // Values stay in their stored form until used: converting at the load
-  // would make the wave wait for the loads it has just issued.
-};
-
 // Thread and tile mappings of one workgroup of NW waves.
 template <int DK, int DVT, typename ST, int NW>
 struct Shape {
@@ -310,34 +323,247 @@ struct Shape {
   static constexpr int NST = NCT * NJT;               // state tiles
   static constexpr int NS = (NST + NW - 1) / NW;      // state tiles per wave
   static constexpr int NUT = (4 * NJT + NW - 1) / NW; // (row block, column tile) pairs per wave
+  static constexpr int NTRI = (MAXC / 16) * (MAXC / 16 + 1) / 2;  // lower block tiles
+  static constexpr int NGT = (NTRI + NW - 1) / NW;    // Gram tile pairs per wave
   static_assert(RPG <= 8 && RV <= 8 && 16 % RPG == 0, "mapping");
 };
 
+// ---------------------------------------------------------------------------
+// Local kernel: T diag(beta) and lower(A_qk) of one (chunk, head).
+
+template <int DK, typename InT, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void local_kernel(LocalParams p) {
+  using TR = Traits<InT>;
+  using ST = typename TR::ST;
+  using Pair = typename TR::Pair;
+  using SH = Shape<DK, 16, ST, NW>;
+  using SM = LocalSmem<DK, ST, SH::NG>;
+  constexpr int NT = SH::NT, MAXC = SH::MAXC, HK = SH::HK, RPG = SH::RPG, NG = SH::NG, NGT = SH::NGT;
+  constexpr int LDK = SM::LDK, LC = SM::LC, LF = SM::LF;
+  constexpr uint32_t ES = sizeof(InT);
+  __shared__ __attribute__((aligned(16))) SM sm;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int H = p.H;
+  const int unit = blockIdx.x, c = unit / H, h = unit - c * H;
+  const int t0 = p.chunks[2 * c], n = p.chunks[2 * c + 1];
+  const int nb = (n + 15) >> 4, ngc = 16 * nb / RPG;
+  const int cp = tid % HK, g = tid / HK;
+  const int c0p = 2 * cp, r0 = g * RPG;
+  const bool act = g < ngc;
+  const size_t row0 = static_cast<size_t>(t0) * H + h;
+  const InT* __restrict__ gb = static_cast<const InT*>(p.beta);
+
+  // ---- loads; per-group cumulative sums of a ------------------------------
+  Pair kr[RPG], qr[RPG];
+  float gr[RPG][2];
+  if (act) {
+    const uint32_t rsk = static_cast<uint32_t>(H) * DK * ES;
+    const uint32_t ok0 = r0 * rsk + c0p * ES, okl = (n - 1) * rsk + c0p * ES;
+    const char* bk = reinterpret_cast<const char*>(static_cast<const InT*>(p.k) + row0 * DK);
+    const char* bq = reinterpret_cast<const char*>(static_cast<const InT*>(p.q) + row0 * DK);
+    const char* ba = reinterpret_cast<const char*>(static_cast<const InT*>(p.a) + row0 * DK);
+    Pair ar[RPG];
+#pragma unroll
+    for (int rr = 0; rr < RPG; ++rr) {
+      const uint32_t off = min(ok0 + rr * rsk, okl);
+      kr[rr] = TR::load(bk + off);
+      qr[rr] = TR::load(bq + off);
+      ar[rr] = TR::load(ba + off);
+    }
+    float run0 = 0.f, run1 = 0.f;
+#pragma unroll
+    for (int rr = 0; rr < RPG; ++rr) {
+      const bool valid = r0 + rr < n;
+      if (!valid) { kr[rr] = TR::zero(); qr[rr] = TR::zero(); }
+      const float2 aa = TR::unpack(valid ? ar[rr] : TR::zero());
+      run0 += aa.x; run1 += aa.y;
+      gr[rr][0] = run0; gr[rr][1] = run1;
+    }
+    sm.tot[g][c0p] = run0;
+    sm.tot[g][c0p + 1] = run1;
+  }
+  if (tid < 16 * nb) sm.beta[tid] = tid < n ? to_f32(gb[row0 + static_cast<size_t>(tid) * H]) : 0.f;
+  __syncthreads();
+
+  // ---- scaled Gram operands; reference: end of 16-row block nb/2 - 1 -------
+  if (act) {
+    float pre0 = 0.f, pre1 = 0.f, rf0 = 0.f, rf1 = 0.f;
+    const int gref = 16 * (nb >> 1) / RPG;
+    // All group sums are read at once (one LDS latency, not one per group).
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) {
+      const float2 t = *reinterpret_cast<const float2*>(&sm.tot[gg][c0p]);
+      if (gg < g) { pre0 += t.x; pre1 += t.y; }
+      if (gg < gref) { rf0 += t.x; rf1 += t.y; }
+    }
+#pragma unroll
+    for (int rr = 0; rr < RPG; ++rr) {
+      const int r = r0 + rr;
+      const float d0 = gr[rr][0] + pre0 - rf0, d1 = gr[rr][1] + pre1 - rf1;
+      const float up0 = fast_exp(d0), up1 = fast_exp(d1);
+      const float dn0 = fast_exp(-d0), dn1 = fast_exp(-d1);
+      const float2 kk = TR::unpack(kr[rr]), qq = TR::unpack(qr[rr]);
+      put2(&sm.u.gram.kpm[r][c0p], kk.x * up0, kk.y * up1);
+      put2(&sm.u.gram.qpm[r][c0p], qq.x * up0, qq.y * up1);
+      put2(&sm.u.gram.kmm[r][c0p], kk.x * dn0, kk.y * dn1);
+    }
+  }
+  __syncthreads();
+
+  // ---- Gram products: L = diag(beta) strict_lower(A_kk) into LDS; A_qk kept
+  // in registers until the operands are dead.  Tile x of the lower triangle
+  // pairs the A_kk and A_qk products that share the Km block.
+  const int ntri = nb * (nb + 1) / 2;
+  f32x4 aq[NGT];
+  int aR[NGT], aI[NGT];
+#pragma unroll
+  for (int m = 0; m < NGT; ++m) {
+    const int x0 = wave + NW * m;
+    aq[m] = zero4();
+    aR[m] = 0; aI[m] = 0;
+    if (x0 < ntri) {
+      int x = x0, R = 0;
+      while (x > R) { x -= R + 1; ++R; }
+      aR[m] = R; aI[m] = x;
+      f32x4 acc[2] = {zero4(), zero4()};
+      const ST* A[2] = {&sm.u.gram.kpm[16 * R][0], &sm.u.gram.qpm[16 * R][0]};
+      const ST* B[2] = {&sm.u.gram.kmm[16 * x][0], &sm.u.gram.kmm[16 * x][0]};
+      tiles_mma<2>(acc, A, LDK, B, LDK, DK, lane);
+      aq[m] = acc[1];
+      const int col = 16 * x + (lane & 15), row0t = 16 * R + 4 * (lane >> 4);
+      const float4 bt = *reinterpret_cast<const float4*>(&sm.beta[row0t]);
+      const float b4[4] = {bt.x, bt.y, bt.z, bt.w};
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) sm.Lf[row0t + rr][col] = row0t + rr > col ? b4[rr] * acc[0][rr] : 0.f;
+    }
+  }
+  __syncthreads();
+
+#pragma unroll
+  for (int m = 0; m < NGT; ++m) {
+    if (wave + NW * m < ntri) {
+      const int col = 16 * aI[m] + (lane & 15), row0t = 16 * aR[m] + 4 * (lane >> 4);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) put(&sm.u.out.aqk[row0t + rr][col], row0t + rr >= col ? aq[m][rr] : 0.f);
+    }
+  }
+  // ---- T = (I + L)^{-1}, one block column per wave; stored as T diag(beta)
+  if (wave < nb) {
+    const int I = wave;
+    TScratch<ST>& ts = sm.u.out.ts[wave];
+    constexpr int LD = 16 + Op<ST>::PAD, LCT = MAXC + Op<ST>::PAD;
+    const float bcol = sm.beta[16 * I + (lane & 15)];
+    // Diagonal inverses T_RR for R = I .. nb-1: lane = 16*(R-I) + column.
+    {
+      const int blk = lane >> 4, R = I + blk, j = lane & 15;
+      if (R < nb) {
+        // Right-looking: once x[i] is final, fold it into every later row.
+        // Column i+1 of L is loaded while column i is applied; the
+        // scheduling barrier keeps at most two columns in registers.
+        float x[16], lc[16], ln[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = (r == j) ? 1.f : 0.f;
+#pragma unroll
+        for (int r = 1; r < 16; ++r) lc[r] = sm.Lf[16 * R + r][16 * R];
+#pragma unroll
+        for (int i = 0; i < 15; ++i) {
+          if (i + 1 < 15) {
+#pragma unroll
+            for (int r = i + 2; r < 16; ++r) ln[r] = sm.Lf[16 * R + r][16 * R + i + 1];
+          }
+#pragma unroll
+          for (int r = i + 1; r < 16; ++r) x[r] -= lc[r] * x[i];
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int r = i + 2; r < 16; ++r) lc[r] = ln[r];
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) put(&ts.diag[blk][r][j], x[r]);
+        if (blk == 0) {
+#pragma unroll
+          for (int r = 0; r < 16; r += 4) put4(&ts.colT[j][16 * I + r], x + r);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) put(&sm.u.out.tb[16 * I + r][16 * I + j], x[r] * bcol);
+        }
+      }
+    }
+    wave_sync();
+    // Block column: T_RI = -T_RR * sum_{J=I}^{R-1} L_RJ T_JI.
+    for (int R = I + 1; R < nb; ++R) {
+      const f32x4 P = tile_mma_fb(zero4(), &sm.Lf[16 * R][16 * I], LF, &ts.colT[0][16 * I], LCT,
+                                  16 * (R - I), lane);
+      const float pv[4] = {P[0], P[1], P[2], P[3]};
+      put4(&ts.PT[lane & 15][4 * (lane >> 4)], pv);
+      wave_sync();
+      const f32x4 Tn = tile_mma<ST>(zero4(), &ts.diag[R - I][0][0], LD, &ts.PT[0][0], LD, 16, lane);
+      const float tv[4] = {-Tn[0], -Tn[1], -Tn[2], -Tn[3]};
+      put4(&ts.colT[lane & 15][16 * R + 4 * (lane >> 4)], tv);
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        put(&sm.u.out.tb[16 * R + 4 * (lane >> 4) + rr][16 * I + (lane & 15)], tv[rr] * bcol);
+      wave_sync();
+    }
+  }
+  __syncthreads();
+
+  // ---- rows < 16 nb of both tiles to the workspace, 16 bytes per store ----
+  {
+    const int ld = p.ld, ppr = ld * static_cast<int>(ES) / 16;  // 16-byte pieces per row
+    constexpr int EP = 16 / static_cast<int>(ES);                // elements per piece
+    char* dst = static_cast<char*>(p.tq) + static_cast<size_t>(unit) * 2 * ld * ld * ES;
+    const int npc = 16 * nb * ppr;
+    for (int x = tid; x < 2 * npc; x += NT) {
+      const int m = x >= npc, y = x - m * npc, r = y / ppr, cc = (y - r * ppr) * EP;
+      const ST* src = m ? &sm.u.out.aqk[r][cc] : &sm.u.out.tb[r][cc];
+      *reinterpret_cast<i32x4*>(dst + (static_cast<size_t>(m) * ld * ld + r * ld + cc) * ES) =
+          *reinterpret_cast<const i32x4*>(src);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Propagation kernel: one (sequence, head, dv tile) chain through its chunks.
+
+// Raw chunk inputs held in registers from the prefetch to their use.  Values
+// stay in their stored form until used: converting at the load would make the
+// wave wait for the loads it has just issued.
+template <typename InT, int RPG, int RV>
+struct Raw {
+  using Pair = typename Traits<InT>::Pair;
+  Pair k[RPG], q[RPG], a[RPG];  // rows g*RPG .. +RPG, channels 2cp, 2cp+1
+  Pair v[RV];                   // rows rv0 .. rv0+RV-1, columns 2jp, 2jp+1 of the tile
+  i32x4 tp, ap;                 // one 16-byte piece of T diag(beta) and of lower(A_qk)
+};
+
 template <int DK, int DVT, typename InT, int NW>
-__global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(Params p) {
+__global__ __launch_bounds__(64 * NW, 1) void prop_kernel(PropParams p) {
   using TR = Traits<InT>;
   using ST = typename TR::ST;
   using Pair = typename TR::Pair;
   using SH = Shape<DK, DVT, ST, NW>;
-  using SM = Smem<DK, DVT, ST, SH::NG>;
+  using SM = PropSmem<DK, DVT, ST, SH::NG>;
   constexpr int NT = SH::NT, MAXC = SH::MAXC, HK = SH::HK, RPG = SH::RPG, NG = SH::NG;
-  constexpr int VP = SH::VP, RV = SH::RV, NCT = SH::NCT, NJT = SH::NJT;
+  constexpr int VP = SH::VP, RV = SH::RV, NJT = SH::NJT;
   constexpr int NST = SH::NST, NS = SH::NS, NUT = SH::NUT;
-  constexpr int LDK = SM::LDK, LC = SM::LC, LF = SM::LF;
+  constexpr int LDK = SM::LDK, LC = SM::LC;
+  constexpr uint32_t ES = sizeof(InT);
   __shared__ __attribute__((aligned(16))) SM sm;
 
   const int tid = threadIdx.x, lane = tid & 63;
   // Wave index in a scalar register, so per-wave tile loops branch on scalars.
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int H = p.H, dv = p.dv;
+  const int H = p.H, dv = p.dv, ld = p.ld;
 
   // Workgroup -> (chain, dv tile): the tiles of a chain land on one XCD.
   const int bid = blockIdx.x, xcd = bid & 7, local = bid >> 3;
   const int chain = 8 * (local / p.dv_tiles) + xcd, tile = local % p.dv_tiles;
   const int seq = p.chains[2 * chain], h = p.chains[2 * chain + 1];
   if (seq < 0) return;
-  const int lo = p.seqinfo[4 * seq], hi = p.seqinfo[4 * seq + 1];
-  const int ck_lo = p.seqinfo[4 * seq + 2], ck_hi = p.seqinfo[4 * seq + 3];
+  const int* si = p.seqinfo + 6 * seq;
+  const int lo = si[0], hi = si[1], ck_lo = si[2], ck_hi = si[3], c_lo = si[4], c_hi = si[5];
+  (void)hi;
   const int j0 = tile * DVT;
   const int64_t hkv = static_cast<int64_t>(H) * DK * dv;
   const size_t state_off = (static_cast<size_t>(seq) * H + h) * DK * dv;
@@ -346,7 +572,6 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(Params p) {
   const InT* __restrict__ gk = static_cast<const InT*>(p.k);
   const InT* __restrict__ gv = static_cast<const InT*>(p.v);
   const InT* __restrict__ ga = static_cast<const InT*>(p.a);
-  const InT* __restrict__ gb = static_cast<const InT*>(p.beta);
   InT* __restrict__ go = static_cast<InT*>(p.o);
 
   // State tile: accumulator tile s = wave + NW*u covers rows 16*(s/NJT) and
@@ -399,31 +624,25 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(Params p) {
   const int c0p = 2 * cp, r0 = g * RPG;
   // v-tile mapping: thread -> column pair jp, rows rv0 .. rv0+RV-1.
   const int jp = tid % VP, rv0 = (tid / VP) * RV;
+  // T / A_qk piece of this thread: row tr, elements tc .. tc+16/ES-1.
+  constexpr int EP = 16 / static_cast<int>(ES);
+  const int ppr = ld / EP, tr = tid / ppr, tc = (tid - tr * ppr) * EP;
+  const bool has_piece = tr < ld;
 
-  // Chunk end from its start: at most `chunk` rows, never past a checkpoint.
-  auto chunk_end = [&](int t, int c) {
-    int e = min(t + p.chunk, hi);
-    if (c < ck_hi) e = min(e, lo + p.ck_pos[c]);
-    return e;
-  };
-  // Issue the loads of rows [t, t+n) into registers.  Each chunk's base
-  // addresses are wave-uniform; per-lane byte offsets inside a chunk are
-  // loop-invariant 32-bit values (the host bounds H * max(dk, dv) so that a
-  // chunk spans less than 4 GiB), clamped to the chunk's last row.  Rows
-  // past n are masked when unpacked.
-  constexpr uint32_t ES = sizeof(InT);
+  // Issue the loads of chunk c into registers.  Each chunk's base addresses
+  // are wave-uniform; per-lane byte offsets inside a chunk are loop-invariant
+  // 32-bit values (the host bounds H * max(dk, dv) so that a chunk spans less
+  // than 4 GiB), clamped to the chunk's last row.  Rows past n are masked
+  // when unpacked.  The loads go out in three parts, each as soon as the
+  // previous chunk's values are dead, so that no phase queues a chunk's worth
+  // of loads: part 0 (a, v, T, A_qk) after the unpack, parts 1 (k) and 2 (q)
+  // after the propagation operands.
   const uint32_t rsk = static_cast<uint32_t>(H) * DK * ES;  // row strides, bytes
   const uint32_t rsv = static_cast<uint32_t>(H) * dv * ES;
-  const uint32_t rsb = static_cast<uint32_t>(H) * ES;
   const uint32_t ok0 = r0 * rsk + c0p * ES;
   const uint32_t ov0 = rv0 * rsv + 2 * jp * ES;
-  // The loads go out in three parts, each as soon as the previous chunk's
-  // values are dead, so that no phase queues a chunk's worth of loads:
-  // part 0 (a, v, beta) after the unpack, part 1 (k) and part 2 (q) after the
-  // propagation operands.
   Raw<InT, RPG, RV> raw;
-  auto issue = [&](int part, int t_, int n_) {
-    const int t = __builtin_amdgcn_readfirstlane(t_), n = __builtin_amdgcn_readfirstlane(n_);
+  auto issue = [&](int part, int c, int t, int n) {
     const size_t row0 = static_cast<size_t>(t) * H + h;
     if (part > 0) {
       if (g < NG) {
@@ -438,8 +657,6 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(Params p) {
       }
       return;
     }
-    const char* bb = reinterpret_cast<const char*>(gb + row0);
-    const uint32_t obl = (n - 1) * rsb;
     if (g < NG) {
       const char* ba = reinterpret_cast<const char*>(ga + row0 * DK);
       const uint32_t okl = (n - 1) * rsk + c0p * ES;
@@ -452,46 +669,50 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(Params p) {
 #pragma unroll
       for (int e = 0; e < RV; ++e) raw.v[e] = TR::load(bv + min(ov0 + e * rsv, ovl));
     }
-    if (tid < MAXC) raw.b = *reinterpret_cast<const InT*>(bb + min(tid * rsb, obl));
+    if (has_piece) {
+      const char* src = static_cast<const char*>(p.tq) +
+                        ((static_cast<size_t>(c) * H + h) * 2 * ld * ld + tr * ld + tc) * ES;
+      raw.tp = *reinterpret_cast<const i32x4*>(src);
+      raw.ap = *reinterpret_cast<const i32x4*>(src + static_cast<size_t>(ld) * ld * ES);
+    }
   };
 
-  int t0 = lo, ck = ck_lo;
-  int end = t0 < hi ? chunk_end(t0, ck) : t0;
-  if (t0 < hi) {
-    issue(0, t0, end - t0);
-    issue(1, t0, end - t0);
-    issue(2, t0, end - t0);
+  int ck = ck_lo;
+  // (first token, rows) of the current and the next chunk, read one chunk
+  // ahead so that no load waits on the chunk table.
+  int t0 = 0, n = 0;
+  if (c_lo < c_hi) {
+    t0 = __builtin_amdgcn_readfirstlane(p.chunks[2 * c_lo]);
+    n = __builtin_amdgcn_readfirstlane(p.chunks[2 * c_lo + 1]);
+    issue(0, c_lo, t0, n);
+    issue(1, c_lo, t0, n);
+    issue(2, c_lo, t0, n);
   }
 
-  while (t0 < hi) {
-    const int n = end - t0;
+  for (int c = c_lo; c < c_hi; ++c) {
+    const bool more = c + 1 < c_hi;
+    const int tn = more ? __builtin_amdgcn_readfirstlane(p.chunks[2 * c + 2]) : 0;
+    const int nn = more ? __builtin_amdgcn_readfirstlane(p.chunks[2 * c + 3]) : 0;
     const int nb = (n + 15) >> 4;
     const int ngc = 16 * nb / RPG;  // row groups covering the chunk's blocks
     const bool act = g < ngc;
-    const bool is_ck = ck < ck_hi && end == lo + p.ck_pos[ck];
-    const int ckn = ck + (is_ck ? 1 : 0);
-    const int t0n = end;
-    const int endn = t0n < hi ? chunk_end(t0n, ckn) : t0n;
+    const bool is_ck = ck < ck_hi && t0 + n == lo + p.ck_pos[ck];
 
-    // ---- unpack the chunk; per-group cumulative sums of a ----------------
-    // k and q stay packed in `raw` (rows past n zeroed) until the next
-    // chunk's loads are issued; gr holds the running sums of a.
-    float gr[RPG][2];   // cumulative log-decay, then e^{G - G_m} (after the Gram operands)
-    float gd[RPG][2];   // e^{G_m - G}
+    // ---- unpack the chunk; per-group sums of a; e^a per element -----------
+    float ea[RPG][2];   // e^{a} of each row (1 past the chunk)
+    float run0 = 0.f, run1 = 0.f;  // sum of a over this thread's rows
     if (act) {
-      float run0 = 0.f, run1 = 0.f;
 #pragma unroll
       for (int rr = 0; rr < RPG; ++rr) {
         const bool valid = r0 + rr < n;
         if (!valid) { raw.k[rr] = TR::zero(); raw.q[rr] = TR::zero(); }
         const float2 aa = TR::unpack(valid ? raw.a[rr] : TR::zero());
         run0 += aa.x; run1 += aa.y;
-        gr[rr][0] = run0; gr[rr][1] = run1;
+        ea[rr][0] = fast_exp(aa.x); ea[rr][1] = fast_exp(aa.y);
       }
       sm.tot[g][c0p] = run0;
       sm.tot[g][c0p + 1] = run1;
     }
-    if (tid < 16 * nb) sm.beta[tid] = tid < n ? to_f32(raw.b) : 0.f;
     if (rv0 < 16 * nb && tid < (MAXC / RV) * VP) {
       float x0[RV], x1[RV];
 #pragma unroll
@@ -504,159 +725,57 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(Params p) {
       putn<RV>(&sm.buf.vT[2 * jp][rv0], x0);
       putn<RV>(&sm.buf.vT[2 * jp + 1][rv0], x1);
     }
+    if (has_piece) {
+      *reinterpret_cast<i32x4*>(&sm.tb[tr][tc]) = raw.tp;
+      *reinterpret_cast<i32x4*>(&sm.aqk[tr][tc]) = raw.ap;
+    }
     __syncthreads();
-    if (t0n < hi) issue(0, t0n, endn - t0n);
+    if (more) issue(0, c + 1, tn, nn);
 
-    // ---- cumulative sums across groups; Gram operands ---------------------
-    // Reference: end of 16-row block nb/2 - 1 (chunk start when nb = 1).
-    float ge0 = 0.f, ge1 = 0.f;  // G at the chunk's last row
-    float rf0 = 0.f, rf1 = 0.f;  // G at the reference row
+    // ---- chunk-start scaled operands: k g, q g, (k g_n / g)^T; g_n --------
     if (act) {
-      float pre0 = 0.f, pre1 = 0.f;
-      const int gref = 16 * (nb >> 1) / RPG;
-      for (int gg = 0; gg < ngc; ++gg) {
-        const float t0v = sm.tot[gg][c0p], t1v = sm.tot[gg][c0p + 1];
-        if (gg < g) { pre0 += t0v; pre1 += t1v; }
-        if (gg < gref) { rf0 += t0v; rf1 += t1v; }
-        ge0 += t0v; ge1 += t1v;
+      float pre0 = 0.f, pre1 = 0.f, ge0 = 0.f, ge1 = 0.f;
+      // All group sums are read at once (one LDS latency, not one per group).
+#pragma unroll
+      for (int gg = 0; gg < NG; ++gg) {
+        const float2 t = *reinterpret_cast<const float2*>(&sm.tot[gg][c0p]);
+        if (gg < g) { pre0 += t.x; pre1 += t.y; }
+        if (gg < ngc) { ge0 += t.x; ge1 += t.y; }
       }
       if (g == 0) { sm.gexp[c0p] = fast_exp(ge0); sm.gexp[c0p + 1] = fast_exp(ge1); }
-#pragma unroll
-      for (int rr = 0; rr < RPG; ++rr) {
-        gr[rr][0] += pre0; gr[rr][1] += pre1;
-        const int r = r0 + rr;
-        const float d0 = gr[rr][0] - rf0, d1 = gr[rr][1] - rf1;
-        const float up0 = fast_exp(d0), up1 = fast_exp(d1);
-        const float dn0 = fast_exp(-d0), dn1 = fast_exp(-d1);
-        gr[rr][0] = up0; gr[rr][1] = up1;
-        gd[rr][0] = dn0; gd[rr][1] = dn1;
-        const float2 kk = TR::unpack(raw.k[rr]), qq = TR::unpack(raw.q[rr]);
-        put2(&sm.u.gram.kpm[r][c0p], kk.x * up0, kk.y * up1);
-        put2(&sm.u.gram.qpm[r][c0p], qq.x * up0, qq.y * up1);
-        put2(&sm.u.gram.kmm[r][c0p], kk.x * dn0, kk.y * dn1);
-      }
-    }
-    __syncthreads();
-
-    // ---- Gram products: L = diag(beta) strict_lower(A_kk), Aqk = lower(A_qk)
-    {
-      const int ntri = nb * (nb + 1) / 2, ntiles = 2 * ntri;
-      for (int t2 = wave; t2 < ntiles; t2 += 2 * NW) {
-        const int cnt = t2 + NW < ntiles ? 2 : 1;
-        int Rr[2], Ii[2];
-        bool qk[2];
-        const ST* A[2];
-        const ST* B[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int x0 = min(t2 + NW * t, ntiles - 1);
-          qk[t] = x0 >= ntri;
-          int x = qk[t] ? x0 - ntri : x0, R = 0;
-          while (x > R) { x -= R + 1; ++R; }
-          Rr[t] = R; Ii[t] = x;
-          A[t] = qk[t] ? &sm.u.gram.qpm[16 * R][0] : &sm.u.gram.kpm[16 * R][0];
-          B[t] = &sm.u.gram.kmm[16 * x][0];
-        }
-        f32x4 acc[2] = {zero4(), zero4()};
-        if (cnt == 2) tiles_mma<2>(acc, A, LDK, B, LDK, DK, lane);
-        else tiles_mma<1>(acc, A, LDK, B, LDK, DK, lane);
-        for (int t = 0; t < cnt; ++t) {
-          const int col = 16 * Ii[t] + (lane & 15), row0 = 16 * Rr[t] + 4 * (lane >> 4);
-          if (qk[t]) {
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr)
-              put(&sm.aqk[row0 + rr][col], row0 + rr >= col ? acc[t][rr] : 0.f);
-          } else {
-            const float4 bt = *reinterpret_cast<const float4*>(&sm.beta[row0]);
-            const float b4[4] = {bt.x, bt.y, bt.z, bt.w};
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr)
-              sm.lw.Lf[row0 + rr][col] = row0 + rr > col ? b4[rr] * acc[t][rr] : 0.f;
-          }
-        }
-      }
-    }
-    __syncthreads();
-
-    // ---- T = (I + L)^{-1}, one block column per wave; propagation operands
-    if (wave < nb) {
-      const int I = wave;
-      TScratch<ST>& ts = sm.ts[wave];
-      constexpr int LD = 16 + Op<ST>::PAD, LCT = MAXC + Op<ST>::PAD;
-      // Diagonal inverses T_RR for R = I .. nb-1: lane = 16*(R-I) + column.
-      {
-        const int blk = lane >> 4, R = I + blk, j = lane & 15;
-        if (R < nb) {
-          // Right-looking: once x[i] is final, fold it into every later row.
-          // Column i+1 of L is loaded while column i is applied; the
-          // scheduling barrier keeps at most two columns in registers.
-          float x[16], lc[16], ln[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) x[r] = (r == j) ? 1.f : 0.f;
-#pragma unroll
-          for (int r = 1; r < 16; ++r) lc[r] = sm.lw.Lf[16 * R + r][16 * R];
-#pragma unroll
-          for (int i = 0; i < 15; ++i) {
-            if (i + 1 < 15) {
-#pragma unroll
-              for (int r = i + 2; r < 16; ++r) ln[r] = sm.lw.Lf[16 * R + r][16 * R + i + 1];
-            }
-#pragma unroll
-            for (int r = i + 1; r < 16; ++r) x[r] -= lc[r] * x[i];
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int r = i + 2; r < 16; ++r) lc[r] = ln[r];
-          }
-#pragma unroll
-          for (int r = 0; r < 16; ++r) put(&ts.diag[blk][r][j], x[r]);
-          if (blk == 0) {
-#pragma unroll
-            for (int r = 0; r < 16; r += 4) put4(&ts.colT[j][16 * I + r], x + r);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) put(&sm.Tb[16 * I + r][16 * I + j], x[r]);
-          }
-        }
-      }
-      wave_sync();
-      // Block column: T_RI = -T_RR * sum_{J=I}^{R-1} L_RJ T_JI.
-      for (int R = I + 1; R < nb; ++R) {
-        const f32x4 P = tile_mma_fb(zero4(), &sm.lw.Lf[16 * R][16 * I], LF, &ts.colT[0][16 * I], LCT,
-                                    16 * (R - I), lane);
-        const float pv[4] = {P[0], P[1], P[2], P[3]};
-        put4(&ts.PT[lane & 15][4 * (lane >> 4)], pv);
-        wave_sync();
-        const f32x4 Tn = tile_mma<ST>(zero4(), &ts.diag[R - I][0][0], LD, &ts.PT[0][0], LD, 16, lane);
-        const float tv[4] = {-Tn[0], -Tn[1], -Tn[2], -Tn[3]};
-        put4(&ts.colT[lane & 15][16 * R + 4 * (lane >> 4)], tv);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) put(&sm.Tb[16 * R + 4 * (lane >> 4) + rr][16 * I + (lane & 15)], tv[rr]);
-        wave_sync();
-      }
-    }
-    // (every thread, after its T work): chunk-start scaled operands; the
-    // next chunk's loads.
-    if (act) {
-      // e^{G} = e^{G - G_m} e^{G_m} and e^{G_n - G} = e^{G_m - G} e^{G_n - G_m}.
-      const float em0 = fast_exp(rf0), em1 = fast_exp(rf1);
-      const float en0 = fast_exp(ge0 - rf0), en1 = fast_exp(ge1 - rf1);
+      // e^{G_r} as a running product from e^{G} before this thread's rows, and
+      // e^{G_n - G_r} as a suffix product from e^{G_n - G} after them.  A
+      // factor below the fp32 range flushes to 0, like e^{G} itself would.
       float kh0[RPG], kh1[RPG];
+      float s0v = fast_exp(ge0 - pre0 - run0), s1v = fast_exp(ge1 - pre1 - run1);
+#pragma unroll
+      for (int rr = RPG - 1; rr >= 0; --rr) {
+        const float2 kk = TR::unpack(raw.k[rr]);
+        kh0[rr] = kk.x * s0v;
+        kh1[rr] = kk.y * s1v;
+        s0v *= ea[rr][0];
+        s1v *= ea[rr][1];
+      }
+      float e0 = fast_exp(pre0), e1 = fast_exp(pre1);
 #pragma unroll
       for (int rr = 0; rr < RPG; ++rr) {
         const int r = r0 + rr;
-        const float e0 = gr[rr][0] * em0, e1 = gr[rr][1] * em1;
+        e0 *= ea[rr][0];
+        e1 *= ea[rr][1];
         const float2 kk = TR::unpack(raw.k[rr]), qq = TR::unpack(raw.q[rr]);
-        kh0[rr] = kk.x * (gd[rr][0] * en0);
-        kh1[rr] = kk.y * (gd[rr][1] * en1);
-        put2(&sm.u.prop.kp[r][c0p], kk.x * e0, kk.y * e1);
-        put2(&sm.u.prop.qp[r][c0p], qq.x * e0, qq.y * e1);
+        put2(&sm.kp[r][c0p], kk.x * e0, kk.y * e1);
+        put2(&sm.qp[r][c0p], qq.x * e0, qq.y * e1);
       }
-      putn<RPG>(&sm.u.prop.khT[c0p][r0], kh0);
-      putn<RPG>(&sm.u.prop.khT[c0p + 1][r0], kh1);
+      putn<RPG>(&sm.khT[c0p][r0], kh0);
+      putn<RPG>(&sm.khT[c0p + 1][r0], kh1);
     }
     __syncthreads();
-    if (t0n < hi) issue(1, t0n, endn - t0n);
+    if (more) {
+      issue(1, c + 1, tn, nn);
+      issue(2, c + 1, tn, nn);
+    }
 
-    // ---- Z = beta V - (beta k g) S (stored transposed); QS = (q g) S --------
+    // ---- Z = V - (k g) S (stored transposed); QS = (q g) S ----------------
     // This wave's (row block, column tile) pairs: x = wave + NW*m < nb*NJT.
     f32x4 qs[NUT];
 #pragma unroll
@@ -666,28 +785,26 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(Params p) {
       if (x < nb * NJT) {
         const int R = x / NJT, jt = x % NJT;
         f32x4 acc[2] = {zero4(), zero4()};
-        const ST* A[2] = {&sm.u.prop.kp[16 * R][0], &sm.u.prop.qp[16 * R][0]};
+        const ST* A[2] = {&sm.kp[16 * R][0], &sm.qp[16 * R][0]};
         const ST* B[2] = {&sm.sT[16 * jt][0], &sm.sT[16 * jt][0]};
         tiles_mma<2>(acc, A, LDK, B, LDK, DK, lane);
         qs[m] = acc[1];
         const int jl = 16 * jt + (lane & 15), i0 = 16 * R + 4 * (lane >> 4);
         float z[4];
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          z[rr] = sm.beta[i0 + rr] * (static_cast<float>(sm.buf.vT[jl][i0 + rr]) - acc[0][rr]);
+        for (int rr = 0; rr < 4; ++rr) z[rr] = static_cast<float>(sm.buf.vT[jl][i0 + rr]) - acc[0][rr];
         put4(&sm.zo.zT[jl][i0], z);
       }
     }
     __syncthreads();
-    if (t0n < hi) issue(2, t0n, endn - t0n);
 
-    // ---- U = T Z  (stored transposed) --------------------------------------
+    // ---- U = T diag(beta) Z  (stored transposed) ----------------------------
 #pragma unroll
     for (int m = 0; m < NUT; ++m) {
       const int x = wave + NW * m;
       if (x < nb * NJT) {
         const int R = x / NJT, jt = x % NJT;
-        const f32x4 u4 = tile_mma<ST>(zero4(), &sm.Tb[16 * R][0], LC, &sm.zo.zT[16 * jt][0], LC, 16 * (R + 1), lane);
+        const f32x4 u4 = tile_mma<ST>(zero4(), &sm.tb[16 * R][0], LC, &sm.zo.zT[16 * jt][0], LC, 16 * (R + 1), lane);
         const float uv[4] = {u4[0], u4[1], u4[2], u4[3]};
         put4(&sm.buf.uT[16 * jt + (lane & 15)][16 * R + 4 * (lane >> 4)], uv);
       }
@@ -718,7 +835,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(Params p) {
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) S[u][rr] *= sm.gexp[c0 + rr];
         }
-        A[u] = &sm.u.prop.khT[16 * ct][0];
+        A[u] = &sm.khT[16 * ct][0];
         B[u] = &sm.buf.uT[16 * jt][0];
       }
       // Batches of at most four tiles keep the operand fragments in registers.
@@ -740,42 +857,72 @@ __global__ __launch_bounds__(64 * NW, 1) void prefill_kernel(Params p) {
       constexpr int PPR = DVT * static_cast<int>(ES) / 16;  // 16-byte pieces per row
       char* bo = reinterpret_cast<char*>(go + (static_cast<size_t>(t0) * H + h) * dv + j0);
       for (int x = tid; x < n * PPR; x += NT) {
-        const int r = x / PPR, c = (x % PPR) * (16 / static_cast<int>(ES));
-        *reinterpret_cast<i32x4*>(bo + r * rsv + c * ES) = *reinterpret_cast<const i32x4*>(&sm.zo.o[r][c]);
+        const int r = x / PPR, cc = (x % PPR) * EP;
+        *reinterpret_cast<i32x4*>(bo + r * rsv + cc * ES) = *reinterpret_cast<const i32x4*>(&sm.zo.o[r][cc]);
       }
     }
 
     if (is_ck) {
       store_state(p.page_pool + static_cast<int64_t>(p.ck_slot[ck]) * p.page_elems +
                   static_cast<int64_t>(h) * DK * dv);
+      ++ck;
     }
-    t0 = t0n;
-    end = endn;
-    ck = ckn;
+    t0 = tn;
+    n = nn;
   }
   if (p.s_final != nullptr) store_state(p.s_final + state_off);
 }
 
 constexpr int kWaves = 8;
 
-template <int DK, int DVT, typename InT>
-hipError_t launch_t(const PrefillArgs& a, const Params& prm) {
-  const dim3 grid(static_cast<unsigned>(a.n_chains) * static_cast<unsigned>(a.dv_tiles));
-  hipLaunchKernelGGL((prefill_kernel<DK, DVT, InT, kWaves>), grid, dim3(64 * kWaves), 0, a.stream, prm);
+template <int DK, typename InT>
+hipError_t launch_local(const PrefillArgs& a) {
+  LocalParams prm;
+  prm.q = a.q; prm.k = a.k; prm.a = a.a; prm.beta = a.beta;
+  prm.chunks = a.chunks; prm.tq = a.tq; prm.H = a.H; prm.ld = a.chunk;
+  const dim3 grid(static_cast<unsigned>(a.n_chunks) * static_cast<unsigned>(a.H));
+  hipLaunchKernelGGL((local_kernel<DK, InT, kWaves>), grid, dim3(64 * kWaves), 0, a.stream, prm);
   return hipGetLastError();
 }
 
-template <int DK, int DVT>
-hipError_t launch_dt(const PrefillArgs& a, const Params& prm) {
-  return a.bf16 ? launch_t<DK, DVT, bf16raw>(a, prm) : launch_t<DK, DVT, float>(a, prm);
+template <int DK, int DVT, typename InT>
+hipError_t launch_prop(const PrefillArgs& a) {
+  PropParams prm;
+  prm.q = a.q; prm.k = a.k; prm.v = a.v; prm.a = a.a; prm.tq = a.tq;
+  prm.s0 = a.s0; prm.o = a.o; prm.s_final = a.s_final;
+  prm.page_pool = a.page_pool; prm.page_elems = a.page_elems;
+  prm.chains = a.chains; prm.seqinfo = a.seqinfo; prm.ck_pos = a.ck_pos; prm.ck_slot = a.ck_slot;
+  prm.chunks = a.chunks;
+  prm.H = a.H; prm.dv = a.dv; prm.ld = a.chunk; prm.dv_tiles = a.dv_tiles;
+  const dim3 grid(static_cast<unsigned>(a.n_chains) * static_cast<unsigned>(a.dv_tiles));
+  hipLaunchKernelGGL((prop_kernel<DK, DVT, InT, kWaves>), grid, dim3(64 * kWaves), 0, a.stream, prm);
+  return hipGetLastError();
 }
 
-template <int DK>
-hipError_t launch_dvt(const PrefillArgs& a, const Params& prm) {
+template <int DK, typename InT>
+hipError_t launch_dk(const PrefillArgs& a) {
+  if (a.n_chunks > 0) {
+    const hipError_t e = launch_local<DK, InT>(a);
+    if (e != hipSuccess) return e;
+  }
   switch (a.dv / a.dv_tiles) {
-    case 16: return launch_dt<DK, 16>(a, prm);
-    case 32: return launch_dt<DK, 32>(a, prm);
-    case 64: return launch_dt<DK, 64>(a, prm);
+    case 16: return launch_prop<DK, 16, InT>(a);
+    case 32: return launch_prop<DK, 32, InT>(a);
+    case 64: return launch_prop<DK, 64, InT>(a);
+    case 128:
+      if constexpr (sizeof(InT) == 2) return launch_prop<DK, 128, InT>(a);  // fp32 tiles do not fit LDS
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename InT>
+hipError_t launch_in(const PrefillArgs& a) {
+  switch (a.dk) {
+    case 16: return launch_dk<16, InT>(a);
+    case 32: return launch_dk<32, InT>(a);
+    case 64: return launch_dk<64, InT>(a);
+    case 128: return launch_dk<128, InT>(a);
   }
   return hipErrorInvalidValue;
 }
@@ -783,19 +930,7 @@ hipError_t launch_dvt(const PrefillArgs& a, const Params& prm) {
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a) {
-  Params prm;
-  prm.q = a.q; prm.k = a.k; prm.v = a.v; prm.a = a.a; prm.beta = a.beta;
-  prm.s0 = a.s0; prm.o = a.o; prm.s_final = a.s_final;
-  prm.page_pool = a.page_pool; prm.page_elems = a.page_elems;
-  prm.chains = a.chains; prm.seqinfo = a.seqinfo; prm.ck_pos = a.ck_pos; prm.ck_slot = a.ck_slot;
-  prm.H = a.H; prm.dv = a.dv; prm.chunk = a.chunk; prm.dv_tiles = a.dv_tiles;
-  switch (a.dk) {
-    case 16: return launch_dvt<16>(a, prm);
-    case 32: return launch_dvt<32>(a, prm);
-    case 64: return launch_dvt<64>(a, prm);
-    case 128: return launch_dvt<128>(a, prm);
-  }
-  return hipErrorInvalidValue;
+  return a.bf16 ? launch_in<bf16raw>(a) : launch_in<float>(a);
 }
 
 }  // namespace kda

@@ -35,7 +35,7 @@ SIGNATURES = {
     "kda_unpack_heads": (ctypes.c_int, [_vp, _i64, _i64, _vp, _i32, _i32, _i32, _i32, ctypes.c_int,
                                         _vp, _vp, _vp]),
     "kda_chunk_prefill_workspace_size": (ctypes.c_int, [_i32, _i64, _i32, _i32, _i32, _i32, _i64,
-                                                        ctypes.POINTER(_sz)]),
+                                                        ctypes.c_int, ctypes.POINTER(_sz)]),
     "kda_chunk_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int, _i32, _i32, _i32,
                                          _i32, _i32p, _i32, _vp, _vp, _vp, _i32p, _i32p, _i32p,
                                          _i64, _vp, _i64, _i64, _vp, _sz, _vp]),
@@ -205,10 +205,11 @@ def unpack_heads(page_pool, slot, H, dk, dv, layout=KDA_LAYOUT_KV, state=None, e
     return state
 
 
-def prefill_workspace_size(n_seqs, total_tokens, H, dk, dv, chunk, n_ckpt):
+def prefill_workspace_size(n_seqs, total_tokens, H, dk, dv, chunk, n_ckpt, dtype=torch.bfloat16):
     out = ctypes.c_size_t(0)
+    code = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32
     _check(lib().kda_chunk_prefill_workspace_size(n_seqs, total_tokens, H, dk, dv, chunk, n_ckpt,
-                                                  ctypes.byref(out)))
+                                                  code, ctypes.byref(out)))
     return out.value
 
 
@@ -259,7 +260,7 @@ def chunk_prefill(q, k, v, a, beta, cu_seqlens, s0=None, chunk=64, checkpoints=N
     n_slots, page_elems = (0, 0) if page_pool is None else page_pool.shape
     if page_pool is not None:
         _expect(page_pool, (n_slots, page_elems), torch.float32, "page_pool", dev)
-    need = prefill_workspace_size(N, T, H, dk, dv, chunk, n_ckpt)
+    need = prefill_workspace_size(N, T, H, dk, dv, chunk, n_ckpt, dt)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     fn = lib().kda_chunk_prefill_split
