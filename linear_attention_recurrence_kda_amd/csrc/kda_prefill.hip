@@ -173,6 +173,44 @@ __device__ __forceinline__ void tiles_mma(f32x4* acc, const float* const* A, int
   }
 }
 
+// acc_t += A_t * Bt^T for NT tiles that share one B operand: B's fragment is
+// read from LDS once per k-step instead of once per tile.
+template <int NT>
+__device__ __forceinline__ void tiles_mma_sb(f32x4* acc, const __bf16* const* A, int lda,
+                                             const __bf16* Bt, int ldb, int kvalid, int lane) {
+  const int row = lane & 15, kk = (lane >> 4) * 8;
+  for (int k0 = 0; k0 < kvalid; k0 += 32) {
+    const bool ok = k0 + kk < kvalid;
+    const bf16x8 fb = ok ? *reinterpret_cast<const bf16x8*>(Bt + row * ldb + kk + k0) : zero8();
+    bf16x8 fa[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      fa[t] = ok ? *reinterpret_cast<const bf16x8*>(A[t] + row * lda + kk + k0) : zero8();
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[t], fb, acc[t], 0, 0, 0);
+  }
+}
+
+template <int NT>
+__device__ __forceinline__ void tiles_mma_sb(f32x4* acc, const float* const* A, int lda,
+                                             const float* Bt, int ldb, int kvalid, int lane) {
+  const int row = lane & 15, kk = (lane >> 4) * 8;
+  for (int k0 = 0; k0 < kvalid; k0 += 32) {
+    const bool ok = k0 + kk < kvalid;
+    bf16x8 bh = zero8(), bl = zero8();
+    if (ok) split8(Bt + row * ldb + kk + k0, bh, bl);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      bf16x8 ah = zero8(), al = zero8();
+      if (ok) split8(A[t] + row * lda + kk + k0, ah, al);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc[t], 0, 0, 0);
+    }
+  }
+}
+
 // fp32 operands rounded once to bf16.
 __device__ __forceinline__ void round8(const float* p, bf16x8& hi) {
   const float4 x0 = *reinterpret_cast<const float4*>(p);
@@ -429,8 +467,7 @@ __global__ __launch_bounds__(64 * NW, 2) void local_kernel(LocalParams p) {
       aR[m] = R; aI[m] = x;
       f32x4 acc[2] = {zero4(), zero4()};
       const ST* A[2] = {&sm.u.gram.kpm[16 * R][0], &sm.u.gram.qpm[16 * R][0]};
-      const ST* B[2] = {&sm.u.gram.kmm[16 * x][0], &sm.u.gram.kmm[16 * x][0]};
-      tiles_mma<2>(acc, A, LDK, B, LDK, DK, lane);
+      tiles_mma_sb<2>(acc, A, LDK, &sm.u.gram.kmm[16 * x][0], LDK, DK, lane);
       aq[m] = acc[1];
       const int col = 16 * x + (lane & 15), row0t = 16 * R + 4 * (lane >> 4);
       const float4 bt = *reinterpret_cast<const float4*>(&sm.beta[row0t]);
@@ -508,7 +545,9 @@ __global__ __launch_bounds__(64 * NW, 2) void local_kernel(LocalParams p) {
   }
   __syncthreads();
 
-  // ---- rows < 16 nb of both tiles to the workspace, 16 bytes per store ----
+  // ---- rows < 16 nb of both tiles to the workspace, 16 bytes per store;
+  // entries right of the diagonal block are written as zeros, so a reader may
+  // run a row block's products over any column range -----------------------
   {
     const int ld = p.ld, ppr = ld * static_cast<int>(ES) / 16;  // 16-byte pieces per row
     constexpr int EP = 16 / static_cast<int>(ES);                // elements per piece
@@ -517,8 +556,9 @@ __global__ __launch_bounds__(64 * NW, 2) void local_kernel(LocalParams p) {
     for (int x = tid; x < 2 * npc; x += NT) {
       const int m = x >= npc, y = x - m * npc, r = y / ppr, cc = (y - r * ppr) * EP;
       const ST* src = m ? &sm.u.out.aqk[r][cc] : &sm.u.out.tb[r][cc];
-      *reinterpret_cast<i32x4*>(dst + (static_cast<size_t>(m) * ld * ld + r * ld + cc) * ES) =
-          *reinterpret_cast<const i32x4*>(src);
+      // Blocks above the block diagonal are zero (never built in LDS).
+      const i32x4 val = cc < 16 * (r / 16 + 1) ? *reinterpret_cast<const i32x4*>(src) : i32x4{0, 0, 0, 0};
+      *reinterpret_cast<i32x4*>(dst + (static_cast<size_t>(m) * ld * ld + r * ld + cc) * ES) = val;
     }
   }
 }
@@ -777,77 +817,139 @@ __global__ __launch_bounds__(64 * NW, 1) void prop_kernel(PropParams p) {
 
     // ---- Z = V - (k g) S (stored transposed); QS = (q g) S ----------------
     // This wave's (row block, column tile) pairs: x = wave + NW*m < nb*NJT.
+    // The pairs of a wave share the column tile jt = wave % NJT (NJT divides
+    // NW), so all their products read one B operand, S^T's tile jt.
+    static_assert(NW % NJT == 0, "pair mapping");
+    const int jtw = wave % NJT;
+    const bool all_pairs = wave + NW * (NUT - 1) < nb * NJT;  // wave-uniform
+    const int kmax = 16 * min(nb, (wave + NW * (NUT - 1)) / NJT + 1);  // row extent of the last pair
     f32x4 qs[NUT];
+    if (all_pairs) {
+      f32x4 acc[2 * NUT];
+      const ST* A[2 * NUT];
 #pragma unroll
-    for (int m = 0; m < NUT; ++m) {
-      const int x = wave + NW * m;
-      qs[m] = zero4();
-      if (x < nb * NJT) {
-        const int R = x / NJT, jt = x % NJT;
-        f32x4 acc[2] = {zero4(), zero4()};
-        const ST* A[2] = {&sm.kp[16 * R][0], &sm.qp[16 * R][0]};
-        const ST* B[2] = {&sm.sT[16 * jt][0], &sm.sT[16 * jt][0]};
-        tiles_mma<2>(acc, A, LDK, B, LDK, DK, lane);
-        qs[m] = acc[1];
-        const int jl = 16 * jt + (lane & 15), i0 = 16 * R + 4 * (lane >> 4);
+      for (int m = 0; m < NUT; ++m) {
+        const int R = (wave + NW * m) / NJT;
+        acc[2 * m] = zero4();
+        acc[2 * m + 1] = zero4();
+        A[2 * m] = &sm.kp[16 * R][0];
+        A[2 * m + 1] = &sm.qp[16 * R][0];
+      }
+      tiles_mma_sb<2 * NUT>(acc, A, LDK, &sm.sT[16 * jtw][0], LDK, DK, lane);
+#pragma unroll
+      for (int m = 0; m < NUT; ++m) {
+        const int R = (wave + NW * m) / NJT;
+        qs[m] = acc[2 * m + 1];
+        const int jl = 16 * jtw + (lane & 15), i0 = 16 * R + 4 * (lane >> 4);
         float z[4];
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) z[rr] = static_cast<float>(sm.buf.vT[jl][i0 + rr]) - acc[0][rr];
+        for (int rr = 0; rr < 4; ++rr) z[rr] = static_cast<float>(sm.buf.vT[jl][i0 + rr]) - acc[2 * m][rr];
         put4(&sm.zo.zT[jl][i0], z);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < NUT; ++m) {
+        const int x = wave + NW * m;
+        qs[m] = zero4();
+        if (x < nb * NJT) {
+          const int R = x / NJT;
+          f32x4 acc[2] = {zero4(), zero4()};
+          const ST* A[2] = {&sm.kp[16 * R][0], &sm.qp[16 * R][0]};
+          tiles_mma_sb<2>(acc, A, LDK, &sm.sT[16 * jtw][0], LDK, DK, lane);
+          qs[m] = acc[1];
+          const int jl = 16 * jtw + (lane & 15), i0 = 16 * R + 4 * (lane >> 4);
+          float z[4];
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) z[rr] = static_cast<float>(sm.buf.vT[jl][i0 + rr]) - acc[0][rr];
+          put4(&sm.zo.zT[jl][i0], z);
+        }
       }
     }
     __syncthreads();
 
     // ---- U = T diag(beta) Z  (stored transposed) ----------------------------
+    // T diag(beta) is zero right of each diagonal block, so the pairs of a
+    // wave can share one run over the last pair's row extent.
+    if (all_pairs) {
+      f32x4 acc[NUT];
+      const ST* A[NUT];
 #pragma unroll
-    for (int m = 0; m < NUT; ++m) {
-      const int x = wave + NW * m;
-      if (x < nb * NJT) {
-        const int R = x / NJT, jt = x % NJT;
-        const f32x4 u4 = tile_mma<ST>(zero4(), &sm.tb[16 * R][0], LC, &sm.zo.zT[16 * jt][0], LC, 16 * (R + 1), lane);
-        const float uv[4] = {u4[0], u4[1], u4[2], u4[3]};
-        put4(&sm.buf.uT[16 * jt + (lane & 15)][16 * R + 4 * (lane >> 4)], uv);
+      for (int m = 0; m < NUT; ++m) {
+        acc[m] = zero4();
+        A[m] = &sm.tb[16 * ((wave + NW * m) / NJT)][0];
+      }
+      tiles_mma_sb<NUT>(acc, A, LC, &sm.zo.zT[16 * jtw][0], LC, kmax, lane);
+#pragma unroll
+      for (int m = 0; m < NUT; ++m) {
+        const int R = (wave + NW * m) / NJT;
+        const float uv[4] = {acc[m][0], acc[m][1], acc[m][2], acc[m][3]};
+        put4(&sm.buf.uT[16 * jtw + (lane & 15)][16 * R + 4 * (lane >> 4)], uv);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < NUT; ++m) {
+        const int x = wave + NW * m;
+        if (x < nb * NJT) {
+          const int R = x / NJT;
+          const f32x4 u4 = tile_mma<ST>(zero4(), &sm.tb[16 * R][0], LC, &sm.zo.zT[16 * jtw][0], LC, 16 * (R + 1), lane);
+          const float uv[4] = {u4[0], u4[1], u4[2], u4[3]};
+          put4(&sm.buf.uT[16 * jtw + (lane & 15)][16 * R + 4 * (lane >> 4)], uv);
+        }
       }
     }
     __syncthreads();
 
     // ---- O = QS + Aqk U;  S <- diag(g_n) S + (k g_n/g)^T U -----------------
+    if (all_pairs) {
+      const ST* A[NUT];
 #pragma unroll
-    for (int m = 0; m < NUT; ++m) {
-      const int x = wave + NW * m;
-      if (x < nb * NJT) {
-        const int R = x / NJT, jt = x % NJT;
-        const f32x4 acc = tile_mma<ST>(qs[m], &sm.aqk[16 * R][0], LC, &sm.buf.uT[16 * jt][0], LC, 16 * (R + 1), lane);
-        const int jl = 16 * jt + (lane & 15), i0 = 16 * R + 4 * (lane >> 4);
+      for (int m = 0; m < NUT; ++m) A[m] = &sm.aqk[16 * ((wave + NW * m) / NJT)][0];
+      tiles_mma_sb<NUT>(qs, A, LC, &sm.buf.uT[16 * jtw][0], LC, kmax, lane);
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) put(&sm.zo.o[i0 + rr][jl], acc[rr]);
+      for (int m = 0; m < NUT; ++m) {
+        const int jl = 16 * jtw + (lane & 15), i0 = 16 * ((wave + NW * m) / NJT) + 4 * (lane >> 4);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) put(&sm.zo.o[i0 + rr][jl], qs[m][rr]);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < NUT; ++m) {
+        const int x = wave + NW * m;
+        if (x < nb * NJT) {
+          const int R = x / NJT;
+          const f32x4 acc = tile_mma<ST>(qs[m], &sm.aqk[16 * R][0], LC, &sm.buf.uT[16 * jtw][0], LC, 16 * (R + 1), lane);
+          const int jl = 16 * jtw + (lane & 15), i0 = 16 * R + 4 * (lane >> 4);
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) put(&sm.zo.o[i0 + rr][jl], acc[rr]);
+        }
       }
     }
     {
+      // The state tiles of a wave share the column tile jt = wave % NJT, so
+      // the update reads one B operand, U^T's tile jt.
       const ST* A[NS];
-      const ST* B[NS];
 #pragma unroll
       for (int u = 0; u < NS; ++u) {
         const int s = min(wave + NW * u, NST - 1);
-        const int ct = s / NJT, jt = s % NJT;
+        const int ct = s / NJT;
         const int c0 = 16 * ct + 4 * (lane >> 4);
         if (wave + NW * u < NST) {
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) S[u][rr] *= sm.gexp[c0 + rr];
         }
         A[u] = &sm.khT[16 * ct][0];
-        B[u] = &sm.buf.uT[16 * jt][0];
       }
+      const ST* B = &sm.buf.uT[16 * jtw][0];
       // Batches of at most four tiles keep the operand fragments in registers.
       constexpr int NB4 = NS < 4 ? NS : 4;
 #pragma unroll
       for (int u0 = 0; u0 < NS; u0 += NB4) {
         if (wave + NW * (u0 + NB4 - 1) < NST) {
-          tiles_mma<NB4>(S + u0, A + u0, LC, B + u0, LC, 16 * nb, lane);
+          tiles_mma_sb<NB4>(S + u0, A + u0, LC, B, LC, 16 * nb, lane);
         } else {
 #pragma unroll
           for (int u = u0; u < u0 + NB4; ++u)
-            if (wave + NW * u < NST) S[u] = tile_mma<ST>(S[u], A[u], LC, B[u], LC, 16 * nb, lane);
+            if (wave + NW * u < NST) S[u] = tile_mma<ST>(S[u], A[u], LC, B, LC, 16 * nb, lane);
         }
       }
     }
