@@ -196,9 +196,8 @@ int kda_chunk_prefill(const void* q, const void* k, const void* v, const void* a
  * independent in the recurrence (column j of S depends only on column j of
  * v), so a chain can be split into dv_split column tiles that each redo the
  * chunk's key-side scaling.  dv_split in {1, 2, 4, 8} with dv / dv_split one
- * of 16, 32 or 64, or 128 for bf16 inputs (so fp32 inputs with dv = 128 take
- * at least 2), or 0 to let the library choose from the sequence lengths.
- * Other values: KDA_EUNSUPPORTED.
+ * of 16, 32 or 64 (so dv = 128 takes at least 2), or 0 to let the library
+ * choose from the sequence lengths.  Other values: KDA_EUNSUPPORTED.
  */
 int kda_chunk_prefill_split(const void* q, const void* k, const void* v, const void* a,
                             const void* beta, kda_dtype in_dtype, int32_t H, int32_t dk,

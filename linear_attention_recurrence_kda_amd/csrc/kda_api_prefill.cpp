@@ -37,13 +37,14 @@ size_t tile_bytes(int64_t n_chunks, int32_t H, int32_t chunk, size_t es) {
   return static_cast<size_t>(n_chunks) * H * 2 * chunk * chunk * es;
 }
 
-// dv columns per workgroup: 16, 32 or 64, or 128 for bf16 inputs (fp32
-// operands of a 128-column tile do not fit in LDS).
+// dv columns per workgroup: 16, 32 or 64 (a 128-column tile's buffers do not
+// fit in LDS).
 bool valid_tile(int32_t dv, int32_t split, bool bf16) {
+  (void)bf16;
   if (split != 1 && split != 2 && split != 4 && split != 8) return false;
   if (dv % split) return false;
   const int t = dv / split;
-  return t == 16 || t == 32 || t == 64 || (t == 128 && bf16);
+  return t == 16 || t == 32 || t == 64;
 }
 
 // Chunks of one sequence: chunks never cross a checkpoint position.
@@ -176,7 +177,7 @@ int kda_chunk_prefill_split(const void* q, const void* k, const void* v, const v
   if (split == 0) split = choose_split(dk, dv, bf16, n_chunks * H, longest);
   if (!valid_tile(dv, split, bf16))
     return fail(KDA_EUNSUPPORTED,
-                "dv_split=%d with dv=%d (dv/split must be 16, 32 or 64, or 128 for bf16 inputs)",
+                "dv_split=%d with dv=%d (dv/split must be 16, 32 or 64)",
                 dv_split, dv);
 
   // Buffers.

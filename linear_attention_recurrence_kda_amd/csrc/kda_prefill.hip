@@ -313,10 +313,11 @@ struct PropSmem {
     ST vT[DVT][LC];         // v^T, this workgroup's columns
     ST uT[DVT][LC];         // U^T
   } buf;
-  union __attribute__((aligned(16))) {  // Z^T is dead once U is formed; O follows it
-    ST zT[DVT][LC];         // Z^T = (V - (k g) S)^T
-    ST o[MAXC][DVT + Op<ST>::PAD];  // this chunk's outputs, row-major
-  } zo;
+  ST zT[DVT][LC];           // Z^T = (V - (k g) S)^T
+  // This chunk's outputs, row-major.  They are written to HBM only after the
+  // next chunk's first barrier and loads, so that a later wait on those loads
+  // (vector-memory counters also count stores) never waits on fresh stores.
+  __attribute__((aligned(16))) ST o[MAXC][DVT + Op<ST>::PAD];
   ST kp[MAXC][LDK];         // k * g
   ST qp[MAXC][LDK];         // q * g
   ST khT[DK][LC];           // (k * g_n / g)^T
@@ -717,7 +718,19 @@ __global__ __launch_bounds__(64 * NW, 1) void prop_kernel(PropParams p) {
     }
   };
 
+  // Output rows of a chunk (first token t, n rows) from sm.o, 16 bytes per
+  // thread and store.
+  auto store_o = [&](int t, int n_) {
+    constexpr int PPR = DVT * static_cast<int>(ES) / 16;  // 16-byte pieces per row
+    char* bo = reinterpret_cast<char*>(go + (static_cast<size_t>(t) * H + h) * dv + j0);
+    for (int x = tid; x < n_ * PPR; x += NT) {
+      const int r = x / PPR, cc = (x % PPR) * EP;
+      *reinterpret_cast<i32x4*>(bo + r * rsv + cc * ES) = *reinterpret_cast<const i32x4*>(&sm.o[r][cc]);
+    }
+  };
+
   int ck = ck_lo;
+  int pt0 = 0, pn = 0;  // the previous chunk, whose outputs are still in sm.o
   // (first token, rows) of the current and the next chunk, read one chunk
   // ahead so that no load waits on the chunk table.
   int t0 = 0, n = 0;
@@ -771,6 +784,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prop_kernel(PropParams p) {
     }
     __syncthreads();
     if (more) issue(0, c + 1, tn, nn);
+    if (c > c_lo) store_o(pt0, pn);
 
     // ---- chunk-start scaled operands: k g, q g, (k g_n / g)^T; g_n --------
     if (act) {
@@ -844,7 +858,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prop_kernel(PropParams p) {
         float z[4];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) z[rr] = static_cast<float>(sm.buf.vT[jl][i0 + rr]) - acc[2 * m][rr];
-        put4(&sm.zo.zT[jl][i0], z);
+        put4(&sm.zT[jl][i0], z);
       }
     } else {
 #pragma unroll
@@ -861,7 +875,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prop_kernel(PropParams p) {
           float z[4];
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) z[rr] = static_cast<float>(sm.buf.vT[jl][i0 + rr]) - acc[0][rr];
-          put4(&sm.zo.zT[jl][i0], z);
+          put4(&sm.zT[jl][i0], z);
         }
       }
     }
@@ -878,7 +892,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prop_kernel(PropParams p) {
         acc[m] = zero4();
         A[m] = &sm.tb[16 * ((wave + NW * m) / NJT)][0];
       }
-      tiles_mma_sb<NUT>(acc, A, LC, &sm.zo.zT[16 * jtw][0], LC, kmax, lane);
+      tiles_mma_sb<NUT>(acc, A, LC, &sm.zT[16 * jtw][0], LC, kmax, lane);
 #pragma unroll
       for (int m = 0; m < NUT; ++m) {
         const int R = (wave + NW * m) / NJT;
@@ -891,7 +905,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prop_kernel(PropParams p) {
         const int x = wave + NW * m;
         if (x < nb * NJT) {
           const int R = x / NJT;
-          const f32x4 u4 = tile_mma<ST>(zero4(), &sm.tb[16 * R][0], LC, &sm.zo.zT[16 * jtw][0], LC, 16 * (R + 1), lane);
+          const f32x4 u4 = tile_mma<ST>(zero4(), &sm.tb[16 * R][0], LC, &sm.zT[16 * jtw][0], LC, 16 * (R + 1), lane);
           const float uv[4] = {u4[0], u4[1], u4[2], u4[3]};
           put4(&sm.buf.uT[16 * jtw + (lane & 15)][16 * R + 4 * (lane >> 4)], uv);
         }
@@ -909,7 +923,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prop_kernel(PropParams p) {
       for (int m = 0; m < NUT; ++m) {
         const int jl = 16 * jtw + (lane & 15), i0 = 16 * ((wave + NW * m) / NJT) + 4 * (lane >> 4);
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) put(&sm.zo.o[i0 + rr][jl], qs[m][rr]);
+        for (int rr = 0; rr < 4; ++rr) put(&sm.o[i0 + rr][jl], qs[m][rr]);
       }
     } else {
 #pragma unroll
@@ -920,7 +934,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prop_kernel(PropParams p) {
           const f32x4 acc = tile_mma<ST>(qs[m], &sm.aqk[16 * R][0], LC, &sm.buf.uT[16 * jtw][0], LC, 16 * (R + 1), lane);
           const int jl = 16 * jtw + (lane & 15), i0 = 16 * R + 4 * (lane >> 4);
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) put(&sm.zo.o[i0 + rr][jl], acc[rr]);
+          for (int rr = 0; rr < 4; ++rr) put(&sm.o[i0 + rr][jl], acc[rr]);
         }
       }
     }
@@ -955,23 +969,18 @@ __global__ __launch_bounds__(64 * NW, 1) void prop_kernel(PropParams p) {
     }
     __syncthreads();
     write_sT();
-    {  // this chunk's output rows, 16 bytes per thread and store
-      constexpr int PPR = DVT * static_cast<int>(ES) / 16;  // 16-byte pieces per row
-      char* bo = reinterpret_cast<char*>(go + (static_cast<size_t>(t0) * H + h) * dv + j0);
-      for (int x = tid; x < n * PPR; x += NT) {
-        const int r = x / PPR, cc = (x % PPR) * EP;
-        *reinterpret_cast<i32x4*>(bo + r * rsv + cc * ES) = *reinterpret_cast<const i32x4*>(&sm.zo.o[r][cc]);
-      }
-    }
 
     if (is_ck) {
       store_state(p.page_pool + static_cast<int64_t>(p.ck_slot[ck]) * p.page_elems +
                   static_cast<int64_t>(h) * DK * dv);
       ++ck;
     }
+    pt0 = t0;
+    pn = n;
     t0 = tn;
     n = nn;
   }
+  if (c_hi > c_lo) store_o(pt0, pn);
   if (p.s_final != nullptr) store_state(p.s_final + state_off);
 }
 
@@ -1011,9 +1020,6 @@ hipError_t launch_dk(const PrefillArgs& a) {
     case 16: return launch_prop<DK, 16, InT>(a);
     case 32: return launch_prop<DK, 32, InT>(a);
     case 64: return launch_prop<DK, 64, InT>(a);
-    case 128:
-      if constexpr (sizeof(InT) == 2) return launch_prop<DK, 128, InT>(a);  // fp32 tiles do not fit LDS
-      break;
   }
   return hipErrorInvalidValue;
 }

@@ -118,7 +118,8 @@ def test_prefill_validation(L):
     assert call(chunk=48 + 8) == kda.KDA_EUNSUPPORTED
     assert call(chunk=80) == kda.KDA_EUNSUPPORTED
     assert call(dtype=0, chunk=64) == kda.KDA_EUNSUPPORTED  # fp32 inputs: chunk <= 32
-    assert call(dtype=0, chunk=32, split=1) == kda.KDA_EUNSUPPORTED  # fp32 128-column tile
+    assert call(split=1) == kda.KDA_EUNSUPPORTED                     # 128-column tile
+    assert call(dtype=0, chunk=32, split=1) == kda.KDA_EUNSUPPORTED
     assert call(split=3) == kda.KDA_EUNSUPPORTED
     assert call(cu=(1, 40)) == kda.KDA_EINVAL
     assert call(cu=(0, 40, 30)) == kda.KDA_EINVAL

@@ -93,7 +93,7 @@ def test_varlen_ragged_with_checkpoints(dk, dv, dtype, chunk):
     _check(w, dtype, o, sf, pool, slots)
 
 
-@pytest.mark.parametrize("split", [1, 2, 4, 8])
+@pytest.mark.parametrize("split", [2, 4, 8])
 def test_explicit_dv_splits_agree(split):
     w = inputs.prefill_workload(40, [200, 77], 2, 128, 128, "bf16", s0_std=0.1, ckpt_every=64)
     o, sf, pool, slots = _run(w, "bf16", 64, dv_split=split)
@@ -160,12 +160,13 @@ def test_prefill_rejects_bad_checkpoints_and_alias():
     assert e.value.status == kda.KDA_EALIAS
 
 
-def test_prefill_rejects_wide_fp32_dv_tile():
-    """fp32 inputs take dv tiles of at most 64 columns (dv=128 needs a split >= 2)."""
-    w = inputs.prefill_workload(44, [40], 2, 128, 128, "fp32")
-    d = {n: dev_tensor(w[n], "fp32") for n in FIELDS}
+@pytest.mark.parametrize("dtype,chunk", [("bf16", 64), ("fp32", 32)])
+def test_prefill_rejects_wide_dv_tile(dtype, chunk):
+    """dv tiles are at most 64 columns wide (dv=128 needs a split >= 2)."""
+    w = inputs.prefill_workload(44, [40], 2, 128, 128, dtype)
+    d = {n: dev_tensor(w[n], dtype) for n in FIELDS}
     for split in (1, 3):
         with pytest.raises(kda.KDAError) as e:
             kda.chunk_prefill(d["q"], d["k"], d["v"], d["a"], d["beta"], w["cu_seqlens"],
-                              chunk=32, dv_split=split)
+                              chunk=chunk, dv_split=split)
         assert e.value.status == kda.KDA_EUNSUPPORTED
