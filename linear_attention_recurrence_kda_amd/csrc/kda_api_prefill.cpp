@@ -25,16 +25,16 @@ int64_t max_chunks(int32_t n_seqs, int64_t total_tokens, int32_t chunk, int64_t 
   return total_tokens / chunk + n_seqs + n_ckpt;
 }
 
-// Workspace: the int32 work list, then (256-byte aligned) the per
-// (chunk, head) tiles T diag(beta) and lower(A_qk), chunk x chunk each, in
-// the operand precision (bf16 for bf16 inputs, fp32 for fp32 inputs).
+// Workspace: the int32 work list, then (256-byte aligned) one record per
+// (chunk, head) (UnitLayout: T diag(beta), lower(A_qk) and the chunk's scaled
+// operands, in the operand precision: bf16 for bf16 inputs, fp32 for fp32).
 size_t work_ints(int32_t n_seqs, int32_t H, int64_t n_ckpt, int64_t n_chunks) {
   return static_cast<size_t>(2 * round8(static_cast<int64_t>(n_seqs) * H) + 6 * n_seqs + 2 * n_ckpt +
                              2 * n_chunks);
 }
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
-size_t tile_bytes(int64_t n_chunks, int32_t H, int32_t chunk, size_t es) {
-  return static_cast<size_t>(n_chunks) * H * 2 * chunk * chunk * es;
+size_t tile_bytes(int64_t n_chunks, int32_t H, int32_t chunk, int32_t dk, size_t es) {
+  return static_cast<size_t>(n_chunks) * H * kda::UnitLayout(chunk, dk, static_cast<int>(es)).bytes;
 }
 
 // dv columns per workgroup: 16, 32 or 64 (a 128-column tile's buffers do not
@@ -97,7 +97,7 @@ int kda_chunk_prefill_workspace_size(int32_t n_seqs, int64_t total_tokens, int32
   if (chunk < 16 || chunk > KDA_MAX_CHUNK || chunk % 16)
     return fail(KDA_EUNSUPPORTED, "chunk=%d (a multiple of 16 up to %d)", chunk, KDA_MAX_CHUNK);
   const int64_t mc = max_chunks(n_seqs, total_tokens, chunk, n_ckpt);
-  *bytes = align256(work_ints(n_seqs, H, n_ckpt, mc) * 4) + tile_bytes(mc, H, chunk, elem_size(in_dtype));
+  *bytes = align256(work_ints(n_seqs, H, n_ckpt, mc) * 4) + tile_bytes(mc, H, chunk, dk, elem_size(in_dtype));
   return ok();
 }
 
@@ -190,7 +190,7 @@ int kda_chunk_prefill_split(const void* q, const void* k, const void* v, const v
   // Output rows are written in 16-byte pieces.
   if (reinterpret_cast<uintptr_t>(o) % 16) return fail(KDA_EINVAL, "o must be 16-byte aligned");
   const size_t list_bytes = align256(work_ints(n_seqs, H, n_ckpt, n_chunks) * 4);
-  const size_t need = list_bytes + tile_bytes(n_chunks, H, chunk, es);
+  const size_t need = list_bytes + tile_bytes(n_chunks, H, chunk, dk, es);
   if (!workspace || workspace_bytes < need)
     return fail(KDA_EWORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
   if (reinterpret_cast<uintptr_t>(workspace) & 255u)

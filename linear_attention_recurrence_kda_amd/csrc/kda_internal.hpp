@@ -41,8 +41,27 @@ hipError_t launch_pack(const PackArgs& p);
 // layer (kda_api_prefill.cpp) builds it:
 //   chains [n_chains][2]  (sequence or -1 for padding, head), longest first,
 //                         n_chains a multiple of 8 (one XCD round)
-//   seqinfo [n_seqs][4]   (first token, end token, first ckpt, end ckpt)
+//   seqinfo [n_seqs][6]   (first token, end token, first ckpt, end ckpt,
+//                         first chunk, end chunk)
 //   ck_pos / ck_slot      per-sequence token counts and page slots
+//   chunks [n_chunks][2]  (first token, rows)
+// followed by one record per (chunk, head) unit, written by the local kernel
+// and read by the propagation kernel (elements of the operand type, bf16 for
+// bf16 inputs and fp32 for fp32 inputs; ld = chunk):
+//   T diag(beta) [ld][ld], lower(A_qk) [ld][ld], k*g [ld][dk], q*g [ld][dk],
+//   (k*g_n/g)^T [dk][ld], then g_n [dk] in fp32.
+struct UnitLayout {
+  size_t aqk, kp, qp, kh, gexp, bytes;  // byte offsets within a record, record size
+  __host__ __device__ UnitLayout(int ld, int dk, int es) {
+    const size_t sq = static_cast<size_t>(ld) * ld * es, rk = static_cast<size_t>(ld) * dk * es;
+    aqk = sq;
+    kp = 2 * sq;
+    qp = kp + rk;
+    kh = qp + rk;
+    gexp = kh + rk;
+    bytes = gexp + static_cast<size_t>(dk) * 4;
+  }
+};
 struct PrefillArgs {
   const void *q, *k, *v, *a, *beta;
   bool bf16;
@@ -54,7 +73,7 @@ struct PrefillArgs {
   int64_t page_elems;
   const int32_t *chains, *seqinfo, *ck_pos, *ck_slot;
   const int32_t* chunks;  // [n_chunks][2] = (first token, rows)
-  void* tq;               // [n_chunks][H][2][chunk][chunk] T diag(beta) and lower(A_qk)
+  void* tq;               // [n_chunks][H] unit records (UnitLayout)
   int n_chunks;
   int n_chains;  // padded
   int dv_tiles;  // workgroups per chain (split of dv)

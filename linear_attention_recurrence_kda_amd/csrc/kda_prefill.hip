@@ -250,13 +250,13 @@ __device__ __forceinline__ f32x4 tile_mma_fb(f32x4 acc, const float* A, int lda,
 struct LocalParams {
   const void *q, *k, *a, *beta;
   const int32_t* chunks;   // [n_chunks][2] = (first token, rows)
-  void* tq;                // [n_chunks][H][2][ld][ld]: T diag(beta), then lower(A_qk)
+  void* tq;                // [n_chunks][H] unit records (UnitLayout)
   int H, ld;
 };
 
 struct PropParams {
-  const void *q, *k, *v, *a;
-  const void* tq;
+  const void* v;
+  const void* tq;            // unit records (UnitLayout)
   const float* s0;
   void* o;
   float* s_final;
@@ -299,25 +299,25 @@ struct LocalSmem {
   } u;
 };
 
-template <int DK, int DVT, typename ST, int NG>
+template <int DK, int DVT, typename ST>
 struct PropSmem {
   static constexpr int MAXC = Op<ST>::MAXC;
   static constexpr int LDK = DK + Op<ST>::PAD;
   static constexpr int LC = MAXC + Op<ST>::PAD;
+  static constexpr int LV = DVT + Op<ST>::PAD;
   float gexp[DK];           // g_n
-  float tot[NG][DK];        // per-row-group sums of a
   ST tb[MAXC][LC];          // T diag(beta)
   ST aqk[MAXC][LC];         // lower(Qp Km^T)
   ST sT[DVT][LDK];          // S^T
-  union {                   // v^T is dead once Z is formed; U^T follows it
-    ST vT[DVT][LC];         // v^T, this workgroup's columns
+  union {                   // v is dead once Z is formed; U^T follows it
+    ST v[MAXC][LV];         // v, this workgroup's columns, row-major
     ST uT[DVT][LC];         // U^T
   } buf;
   ST zT[DVT][LC];           // Z^T = (V - (k g) S)^T
   // This chunk's outputs, row-major.  They are written to HBM only after the
   // next chunk's first barrier and loads, so that a later wait on those loads
   // (vector-memory counters also count stores) never waits on fresh stores.
-  __attribute__((aligned(16))) ST o[MAXC][DVT + Op<ST>::PAD];
+  __attribute__((aligned(16))) ST o[MAXC][LV];
   ST kp[MAXC][LDK];         // k * g
   ST qp[MAXC][LDK];         // q * g
   ST khT[DK][LC];           // (k * g_n / g)^T
@@ -426,9 +426,13 @@ __global__ __launch_bounds__(64 * NW, 2) void local_kernel(LocalParams p) {
   if (tid < 16 * nb) sm.beta[tid] = tid < n ? to_f32(gb[row0 + static_cast<size_t>(tid) * H]) : 0.f;
   __syncthreads();
 
-  // ---- scaled Gram operands; reference: end of 16-row block nb/2 - 1 -------
+  // ---- scaled Gram operands (reference: end of 16-row block nb/2 - 1) into
+  // LDS; the chunk-start operands k*g, q*g, (k*g_n/g)^T and g_n into this
+  // unit's record for the propagation kernel ---------------------------------
+  const UnitLayout lay(p.ld, DK, static_cast<int>(ES));
+  char* rec = static_cast<char*>(p.tq) + static_cast<size_t>(unit) * lay.bytes;
   if (act) {
-    float pre0 = 0.f, pre1 = 0.f, rf0 = 0.f, rf1 = 0.f;
+    float pre0 = 0.f, pre1 = 0.f, rf0 = 0.f, rf1 = 0.f, ge0 = 0.f, ge1 = 0.f;
     const int gref = 16 * (nb >> 1) / RPG;
     // All group sums are read at once (one LDS latency, not one per group).
 #pragma unroll
@@ -436,7 +440,20 @@ __global__ __launch_bounds__(64 * NW, 2) void local_kernel(LocalParams p) {
       const float2 t = *reinterpret_cast<const float2*>(&sm.tot[gg][c0p]);
       if (gg < g) { pre0 += t.x; pre1 += t.y; }
       if (gg < gref) { rf0 += t.x; rf1 += t.y; }
+      if (gg < ngc) { ge0 += t.x; ge1 += t.y; }
     }
+    // e^{G} = e^{G - G_m} e^{G_m},  e^{G_n - G} = e^{G_m - G} e^{G_n - G_m}.
+    const float em0 = fast_exp(rf0), em1 = fast_exp(rf1);
+    const float en0 = fast_exp(ge0 - rf0), en1 = fast_exp(ge1 - rf1);
+    ST* okp = reinterpret_cast<ST*>(rec + lay.kp);
+    ST* oqp = reinterpret_cast<ST*>(rec + lay.qp);
+    ST* okh = reinterpret_cast<ST*>(rec + lay.kh);
+    if (g == 0) {
+      float* ogx = reinterpret_cast<float*>(rec + lay.gexp);
+      ogx[c0p] = fast_exp(ge0);
+      ogx[c0p + 1] = fast_exp(ge1);
+    }
+    float kh0[RPG], kh1[RPG];
 #pragma unroll
     for (int rr = 0; rr < RPG; ++rr) {
       const int r = r0 + rr;
@@ -447,7 +464,14 @@ __global__ __launch_bounds__(64 * NW, 2) void local_kernel(LocalParams p) {
       put2(&sm.u.gram.kpm[r][c0p], kk.x * up0, kk.y * up1);
       put2(&sm.u.gram.qpm[r][c0p], qq.x * up0, qq.y * up1);
       put2(&sm.u.gram.kmm[r][c0p], kk.x * dn0, kk.y * dn1);
+      const float e0 = up0 * em0, e1 = up1 * em1;
+      put2(okp + r * DK + c0p, kk.x * e0, kk.y * e1);
+      put2(oqp + r * DK + c0p, qq.x * e0, qq.y * e1);
+      kh0[rr] = kk.x * (dn0 * en0);
+      kh1[rr] = kk.y * (dn1 * en1);
     }
+    putn<RPG>(okh + c0p * p.ld + r0, kh0);
+    putn<RPG>(okh + (c0p + 1) * p.ld + r0, kh1);
   }
   __syncthreads();
 
@@ -552,7 +576,7 @@ __global__ __launch_bounds__(64 * NW, 2) void local_kernel(LocalParams p) {
   {
     const int ld = p.ld, ppr = ld * static_cast<int>(ES) / 16;  // 16-byte pieces per row
     constexpr int EP = 16 / static_cast<int>(ES);                // elements per piece
-    char* dst = static_cast<char*>(p.tq) + static_cast<size_t>(unit) * 2 * ld * ld * ES;
+    char* dst = rec;
     const int npc = 16 * nb * ppr;
     for (int x = tid; x < 2 * npc; x += NT) {
       const int m = x >= npc, y = x - m * npc, r = y / ppr, cc = (y - r * ppr) * EP;
@@ -567,29 +591,34 @@ __global__ __launch_bounds__(64 * NW, 2) void local_kernel(LocalParams p) {
 // ---------------------------------------------------------------------------
 // Propagation kernel: one (sequence, head, dv tile) chain through its chunks.
 
-// Raw chunk inputs held in registers from the prefetch to their use.  Values
-// stay in their stored form until used: converting at the load would make the
-// wave wait for the loads it has just issued.
-template <typename InT, int RPG, int RV>
-struct Raw {
-  using Pair = typename Traits<InT>::Pair;
-  Pair k[RPG], q[RPG], a[RPG];  // rows g*RPG .. +RPG, channels 2cp, 2cp+1
-  Pair v[RV];                   // rows rv0 .. rv0+RV-1, columns 2jp, 2jp+1 of the tile
-  i32x4 tp, ap;                 // one 16-byte piece of T diag(beta) and of lower(A_qk)
+// The propagation kernel's per-chunk inputs, loaded into registers one chunk
+// ahead as 16-byte pieces: the unit record's scaled operands and tiles (see
+// UnitLayout) and this workgroup's columns of v.
+template <int NPK, int NPV>
+struct Pieces {
+  i32x4 kp[NPK], qp[NPK], kh[NPK];  // k*g, q*g rows; (k*g_n/g)^T rows
+  i32x4 t, a, g;                     // T diag(beta), lower(A_qk), g_n
+  i32x4 v[NPV];
 };
 
+// One chunk: copy its pieces into LDS; Z = V - (k g) S and QS = (q g) S;
+// U = T diag(beta) Z; O = QS + A_qk U and S <- diag(g_n) S + (k g_n/g)^T U;
+// then S^T, O and checkpoint stores (four workgroup barriers).
 template <int DK, int DVT, typename InT, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void prop_kernel(PropParams p) {
   using TR = Traits<InT>;
   using ST = typename TR::ST;
-  using Pair = typename TR::Pair;
   using SH = Shape<DK, DVT, ST, NW>;
-  using SM = PropSmem<DK, DVT, ST, SH::NG>;
-  constexpr int NT = SH::NT, MAXC = SH::MAXC, HK = SH::HK, RPG = SH::RPG, NG = SH::NG;
-  constexpr int VP = SH::VP, RV = SH::RV, NJT = SH::NJT;
+  using SM = PropSmem<DK, DVT, ST>;
+  constexpr int NT = SH::NT, MAXC = SH::MAXC, NJT = SH::NJT;
   constexpr int NST = SH::NST, NS = SH::NS, NUT = SH::NUT;
   constexpr int LDK = SM::LDK, LC = SM::LC;
   constexpr uint32_t ES = sizeof(InT);
+  constexpr int EP = 16 / static_cast<int>(ES);        // elements per 16-byte piece
+  constexpr int PKR = DK / EP;                         // pieces per [*][DK] row
+  constexpr int PVR = DVT / EP;                        // pieces per v row of the tile
+  constexpr int NPK = (MAXC * PKR + NT - 1) / NT;      // k*g pieces per thread
+  constexpr int NPV = (MAXC * PVR + NT - 1) / NT;      // v pieces per thread
   __shared__ __attribute__((aligned(16))) SM sm;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -603,17 +632,13 @@ __global__ __launch_bounds__(64 * NW, 1) void prop_kernel(PropParams p) {
   const int seq = p.chains[2 * chain], h = p.chains[2 * chain + 1];
   if (seq < 0) return;
   const int* si = p.seqinfo + 6 * seq;
-  const int lo = si[0], hi = si[1], ck_lo = si[2], ck_hi = si[3], c_lo = si[4], c_hi = si[5];
-  (void)hi;
+  const int lo = si[0], ck_lo = si[2], ck_hi = si[3], c_lo = si[4], c_hi = si[5];
   const int j0 = tile * DVT;
   const int64_t hkv = static_cast<int64_t>(H) * DK * dv;
   const size_t state_off = (static_cast<size_t>(seq) * H + h) * DK * dv;
-
-  const InT* __restrict__ gq = static_cast<const InT*>(p.q);
-  const InT* __restrict__ gk = static_cast<const InT*>(p.k);
   const InT* __restrict__ gv = static_cast<const InT*>(p.v);
-  const InT* __restrict__ ga = static_cast<const InT*>(p.a);
   InT* __restrict__ go = static_cast<InT*>(p.o);
+  const UnitLayout lay(ld, DK, static_cast<int>(ES));
 
   // State tile: accumulator tile s = wave + NW*u covers rows 16*(s/NJT) and
   // columns j0 + 16*(s%NJT).
@@ -660,181 +685,105 @@ __global__ __launch_bounds__(64 * NW, 1) void prop_kernel(PropParams p) {
     }
   }
 
-  // Prep mapping: thread -> channel pair cp, row group g (rows g*RPG ..).
-  const int cp = tid % HK, g = tid / HK;
-  const int c0p = 2 * cp, r0 = g * RPG;
-  // v-tile mapping: thread -> column pair jp, rows rv0 .. rv0+RV-1.
-  const int jp = tid % VP, rv0 = (tid / VP) * RV;
-  // T / A_qk piece of this thread: row tr, elements tc .. tc+16/ES-1.
-  constexpr int EP = 16 / static_cast<int>(ES);
-  const int ppr = ld / EP, tr = tid / ppr, tc = (tid - tr * ppr) * EP;
-  const bool has_piece = tr < ld;
+  // Piece mappings (loop-invariant).  T / A_qk / (k g_n/g)^T rows are ld
+  // elements long (ppr pieces); k*g / q*g rows DK elements; v rows DVT.
+  // Every load, LDS copy and output store below is unconditional: a thread
+  // past the end of a piece list takes the last piece again (the same data
+  // to the same place), and v / output rows past n repeat row n-1.  With no
+  // per-thread branches around them, the compiler can count exactly which
+  // memory operations are still in flight and wait only for the ones needed
+  // (a conditional load or store would make it wait for all of them,
+  // including the previous chunk's output stores).
+  const int ppr = ld / EP;
+  const int tpc = min(tid, ld * ppr - 1);
+  const int tr = tpc / ppr, tc = (tpc - tr * ppr) * EP;  // T, A_qk piece
+  const int gpc = min(tid, DK / 4 - 1);                   // g_n piece
+  const uint32_t rsv = static_cast<uint32_t>(H) * dv * ES;  // v row stride, bytes
 
-  // Issue the loads of chunk c into registers.  Each chunk's base addresses
-  // are wave-uniform; per-lane byte offsets inside a chunk are loop-invariant
-  // 32-bit values (the host bounds H * max(dk, dv) so that a chunk spans less
-  // than 4 GiB), clamped to the chunk's last row.  Rows past n are masked
-  // when unpacked.  The loads go out in three parts, each as soon as the
-  // previous chunk's values are dead, so that no phase queues a chunk's worth
-  // of loads: part 0 (a, v, T, A_qk) after the unpack, parts 1 (k) and 2 (q)
-  // after the propagation operands.
-  const uint32_t rsk = static_cast<uint32_t>(H) * DK * ES;  // row strides, bytes
-  const uint32_t rsv = static_cast<uint32_t>(H) * dv * ES;
-  const uint32_t ok0 = r0 * rsk + c0p * ES;
-  const uint32_t ov0 = rv0 * rsv + 2 * jp * ES;
-  Raw<InT, RPG, RV> raw;
-  auto issue = [&](int part, int c, int t, int n) {
-    const size_t row0 = static_cast<size_t>(t) * H + h;
-    if (part > 0) {
-      if (g < NG) {
-        const char* bx = reinterpret_cast<const char*>((part == 1 ? gk : gq) + row0 * DK);
-        const uint32_t okl = (n - 1) * rsk + c0p * ES;
+  // Issue all loads of chunk c (first token t, n rows) into registers.
+  Pieces<NPK, NPV> pc;
+  auto issue = [&](int c, int t, int n) {
+    const char* rc = static_cast<const char*>(p.tq) + (static_cast<size_t>(c) * H + h) * lay.bytes;
+    pc.t = *reinterpret_cast<const i32x4*>(rc + (tr * ld + tc) * ES);
+    pc.a = *reinterpret_cast<const i32x4*>(rc + lay.aqk + (tr * ld + tc) * ES);
+    pc.g = *reinterpret_cast<const i32x4*>(rc + lay.gexp + gpc * 16);
+    // v rows past n repeat row n-1: T diag(beta) has zero columns there, so
+    // they never reach U.
+    const char* bv = reinterpret_cast<const char*>(gv + (static_cast<size_t>(t) * H + h) * dv + j0);
 #pragma unroll
-        for (int rr = 0; rr < RPG; ++rr) {
-          const Pair x = TR::load(bx + min(ok0 + rr * rsk, okl));
-          if (part == 1) raw.k[rr] = x;
-          else raw.q[rr] = x;
-        }
-      }
-      return;
+    for (int i = 0; i < NPV; ++i) {
+      const int x = min(tid + NT * i, MAXC * PVR - 1), r = x / PVR, cc = (x - r * PVR) * EP;
+      pc.v[i] = *reinterpret_cast<const i32x4*>(bv + min(r, n - 1) * rsv + cc * ES);
     }
-    if (g < NG) {
-      const char* ba = reinterpret_cast<const char*>(ga + row0 * DK);
-      const uint32_t okl = (n - 1) * rsk + c0p * ES;
 #pragma unroll
-      for (int rr = 0; rr < RPG; ++rr) raw.a[rr] = TR::load(ba + min(ok0 + rr * rsk, okl));
-    }
-    if (tid < (MAXC / RV) * VP) {
-      const char* bv = reinterpret_cast<const char*>(gv + row0 * dv + j0);
-      const uint32_t ovl = (n - 1) * rsv + 2 * jp * ES;
-#pragma unroll
-      for (int e = 0; e < RV; ++e) raw.v[e] = TR::load(bv + min(ov0 + e * rsv, ovl));
-    }
-    if (has_piece) {
-      const char* src = static_cast<const char*>(p.tq) +
-                        ((static_cast<size_t>(c) * H + h) * 2 * ld * ld + tr * ld + tc) * ES;
-      raw.tp = *reinterpret_cast<const i32x4*>(src);
-      raw.ap = *reinterpret_cast<const i32x4*>(src + static_cast<size_t>(ld) * ld * ES);
+    for (int i = 0; i < NPK; ++i) {
+      const int xk = min(tid + NT * i, ld * PKR - 1), xh = min(tid + NT * i, DK * ppr - 1);
+      pc.kp[i] = *reinterpret_cast<const i32x4*>(rc + lay.kp + xk * 16);
+      pc.qp[i] = *reinterpret_cast<const i32x4*>(rc + lay.qp + xk * 16);
+      pc.kh[i] = *reinterpret_cast<const i32x4*>(rc + lay.kh + xh * 16);
     }
   };
-
   // Output rows of a chunk (first token t, n rows) from sm.o, 16 bytes per
   // thread and store.
   auto store_o = [&](int t, int n_) {
-    constexpr int PPR = DVT * static_cast<int>(ES) / 16;  // 16-byte pieces per row
     char* bo = reinterpret_cast<char*>(go + (static_cast<size_t>(t) * H + h) * dv + j0);
-    for (int x = tid; x < n_ * PPR; x += NT) {
-      const int r = x / PPR, cc = (x % PPR) * EP;
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      const int x = min(tid + NT * i, n_ * PVR - 1), r = x / PVR, cc = (x - r * PVR) * EP;
       *reinterpret_cast<i32x4*>(bo + r * rsv + cc * ES) = *reinterpret_cast<const i32x4*>(&sm.o[r][cc]);
     }
   };
 
   int ck = ck_lo;
-  int pt0 = 0, pn = 0;  // the previous chunk, whose outputs are still in sm.o
-  // (first token, rows) of the current and the next chunk, read one chunk
-  // ahead so that no load waits on the chunk table.
   int t0 = 0, n = 0;
   if (c_lo < c_hi) {
     t0 = __builtin_amdgcn_readfirstlane(p.chunks[2 * c_lo]);
     n = __builtin_amdgcn_readfirstlane(p.chunks[2 * c_lo + 1]);
-    issue(0, c_lo, t0, n);
-    issue(1, c_lo, t0, n);
-    issue(2, c_lo, t0, n);
+    issue(c_lo, t0, n);
   }
+  // The previous chunk, whose outputs are still in sm.o.  Before the first
+  // chunk it is the first chunk itself: its rows then receive whatever sm.o
+  // holds and are rewritten by the same threads with the real outputs one
+  // chunk later (one thread's stores to one address stay in order).
+  int pt0 = t0, pn = n;
 
+  static_assert(NW % NJT == 0, "pair mapping");
+  const int jtw = wave % NJT;  // the column tile shared by this wave's tiles
   for (int c = c_lo; c < c_hi; ++c) {
-    const bool more = c + 1 < c_hi;
-    const int tn = more ? __builtin_amdgcn_readfirstlane(p.chunks[2 * c + 2]) : 0;
-    const int nn = more ? __builtin_amdgcn_readfirstlane(p.chunks[2 * c + 3]) : 0;
+    // The next chunk, or this one again at the end of the chain (the loads
+    // stay unconditional).
+    const int cn = c + 1 < c_hi ? c + 1 : c;
+    const int tn = __builtin_amdgcn_readfirstlane(p.chunks[2 * cn]);
+    const int nn = __builtin_amdgcn_readfirstlane(p.chunks[2 * cn + 1]);
     const int nb = (n + 15) >> 4;
-    const int ngc = 16 * nb / RPG;  // row groups covering the chunk's blocks
-    const bool act = g < ngc;
     const bool is_ck = ck < ck_hi && t0 + n == lo + p.ck_pos[ck];
 
-    // ---- unpack the chunk; per-group sums of a; e^a per element -----------
-    float ea[RPG][2];   // e^{a} of each row (1 past the chunk)
-    float run0 = 0.f, run1 = 0.f;  // sum of a over this thread's rows
-    if (act) {
+    // ---- pieces into LDS ----------------------------------------------------
+    *reinterpret_cast<i32x4*>(&sm.tb[tr][tc]) = pc.t;
+    *reinterpret_cast<i32x4*>(&sm.aqk[tr][tc]) = pc.a;
+    *reinterpret_cast<i32x4*>(&sm.gexp[4 * gpc]) = pc.g;
 #pragma unroll
-      for (int rr = 0; rr < RPG; ++rr) {
-        const bool valid = r0 + rr < n;
-        if (!valid) { raw.k[rr] = TR::zero(); raw.q[rr] = TR::zero(); }
-        const float2 aa = TR::unpack(valid ? raw.a[rr] : TR::zero());
-        run0 += aa.x; run1 += aa.y;
-        ea[rr][0] = fast_exp(aa.x); ea[rr][1] = fast_exp(aa.y);
-      }
-      sm.tot[g][c0p] = run0;
-      sm.tot[g][c0p + 1] = run1;
+    for (int i = 0; i < NPV; ++i) {
+      const int x = min(tid + NT * i, MAXC * PVR - 1), r = x / PVR, cc = (x - r * PVR) * EP;
+      *reinterpret_cast<i32x4*>(&sm.buf.v[r][cc]) = pc.v[i];
     }
-    if (rv0 < 16 * nb && tid < (MAXC / RV) * VP) {
-      float x0[RV], x1[RV];
 #pragma unroll
-      for (int e = 0; e < RV; ++e) {
-        const bool valid = rv0 + e < n;
-        const float2 vv = TR::unpack(valid ? raw.v[e] : TR::zero());
-        x0[e] = vv.x;
-        x1[e] = vv.y;
-      }
-      putn<RV>(&sm.buf.vT[2 * jp][rv0], x0);
-      putn<RV>(&sm.buf.vT[2 * jp + 1][rv0], x1);
-    }
-    if (has_piece) {
-      *reinterpret_cast<i32x4*>(&sm.tb[tr][tc]) = raw.tp;
-      *reinterpret_cast<i32x4*>(&sm.aqk[tr][tc]) = raw.ap;
+    for (int i = 0; i < NPK; ++i) {
+      const int xk = min(tid + NT * i, ld * PKR - 1), xh = min(tid + NT * i, DK * ppr - 1);
+      const int rk = xk / PKR, ck_ = (xk - rk * PKR) * EP;
+      const int rh = xh / ppr, ch = (xh - rh * ppr) * EP;
+      *reinterpret_cast<i32x4*>(&sm.kp[rk][ck_]) = pc.kp[i];
+      *reinterpret_cast<i32x4*>(&sm.qp[rk][ck_]) = pc.qp[i];
+      *reinterpret_cast<i32x4*>(&sm.khT[rh][ch]) = pc.kh[i];
     }
     __syncthreads();
-    if (more) issue(0, c + 1, tn, nn);
-    if (c > c_lo) store_o(pt0, pn);
-
-    // ---- chunk-start scaled operands: k g, q g, (k g_n / g)^T; g_n --------
-    if (act) {
-      float pre0 = 0.f, pre1 = 0.f, ge0 = 0.f, ge1 = 0.f;
-      // All group sums are read at once (one LDS latency, not one per group).
-#pragma unroll
-      for (int gg = 0; gg < NG; ++gg) {
-        const float2 t = *reinterpret_cast<const float2*>(&sm.tot[gg][c0p]);
-        if (gg < g) { pre0 += t.x; pre1 += t.y; }
-        if (gg < ngc) { ge0 += t.x; ge1 += t.y; }
-      }
-      if (g == 0) { sm.gexp[c0p] = fast_exp(ge0); sm.gexp[c0p + 1] = fast_exp(ge1); }
-      // e^{G_r} as a running product from e^{G} before this thread's rows, and
-      // e^{G_n - G_r} as a suffix product from e^{G_n - G} after them.  A
-      // factor below the fp32 range flushes to 0, like e^{G} itself would.
-      float kh0[RPG], kh1[RPG];
-      float s0v = fast_exp(ge0 - pre0 - run0), s1v = fast_exp(ge1 - pre1 - run1);
-#pragma unroll
-      for (int rr = RPG - 1; rr >= 0; --rr) {
-        const float2 kk = TR::unpack(raw.k[rr]);
-        kh0[rr] = kk.x * s0v;
-        kh1[rr] = kk.y * s1v;
-        s0v *= ea[rr][0];
-        s1v *= ea[rr][1];
-      }
-      float e0 = fast_exp(pre0), e1 = fast_exp(pre1);
-#pragma unroll
-      for (int rr = 0; rr < RPG; ++rr) {
-        const int r = r0 + rr;
-        e0 *= ea[rr][0];
-        e1 *= ea[rr][1];
-        const float2 kk = TR::unpack(raw.k[rr]), qq = TR::unpack(raw.q[rr]);
-        put2(&sm.kp[r][c0p], kk.x * e0, kk.y * e1);
-        put2(&sm.qp[r][c0p], qq.x * e0, qq.y * e1);
-      }
-      putn<RPG>(&sm.khT[c0p][r0], kh0);
-      putn<RPG>(&sm.khT[c0p + 1][r0], kh1);
-    }
-    __syncthreads();
-    if (more) {
-      issue(1, c + 1, tn, nn);
-      issue(2, c + 1, tn, nn);
-    }
+    // The next chunk's loads, then the previous chunk's output stores.
+    issue(cn, tn, nn);
+    store_o(pt0, pn);
 
     // ---- Z = V - (k g) S (stored transposed); QS = (q g) S ----------------
-    // This wave's (row block, column tile) pairs: x = wave + NW*m < nb*NJT.
-    // The pairs of a wave share the column tile jt = wave % NJT (NJT divides
-    // NW), so all their products read one B operand, S^T's tile jt.
-    static_assert(NW % NJT == 0, "pair mapping");
-    const int jtw = wave % NJT;
+    // The pairs of a wave share the column tile jtw (NJT divides NW), so all
+    // their products read one B operand, S^T's tile jtw.
     const bool all_pairs = wave + NW * (NUT - 1) < nb * NJT;  // wave-uniform
     const int kmax = 16 * min(nb, (wave + NW * (NUT - 1)) / NJT + 1);  // row extent of the last pair
     f32x4 qs[NUT];
@@ -857,7 +806,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prop_kernel(PropParams p) {
         const int jl = 16 * jtw + (lane & 15), i0 = 16 * R + 4 * (lane >> 4);
         float z[4];
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) z[rr] = static_cast<float>(sm.buf.vT[jl][i0 + rr]) - acc[2 * m][rr];
+        for (int rr = 0; rr < 4; ++rr) z[rr] = static_cast<float>(sm.buf.v[i0 + rr][jl]) - acc[2 * m][rr];
         put4(&sm.zT[jl][i0], z);
       }
     } else {
@@ -874,7 +823,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prop_kernel(PropParams p) {
           const int jl = 16 * jtw + (lane & 15), i0 = 16 * R + 4 * (lane >> 4);
           float z[4];
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) z[rr] = static_cast<float>(sm.buf.vT[jl][i0 + rr]) - acc[0][rr];
+          for (int rr = 0; rr < 4; ++rr) z[rr] = static_cast<float>(sm.buf.v[i0 + rr][jl]) - acc[0][rr];
           put4(&sm.zT[jl][i0], z);
         }
       }
@@ -939,8 +888,8 @@ __global__ __launch_bounds__(64 * NW, 1) void prop_kernel(PropParams p) {
       }
     }
     {
-      // The state tiles of a wave share the column tile jt = wave % NJT, so
-      // the update reads one B operand, U^T's tile jt.
+      // The state tiles of a wave share the column tile jtw, so the update
+      // reads one B operand, U^T's tile jtw.
       const ST* A[NS];
 #pragma unroll
       for (int u = 0; u < NS; ++u) {
@@ -968,8 +917,9 @@ __global__ __launch_bounds__(64 * NW, 1) void prop_kernel(PropParams p) {
       }
     }
     __syncthreads();
-    write_sT();
 
+    // ---- S^T; this chunk's output rows (16 bytes per store); checkpoint -----
+    write_sT();
     if (is_ck) {
       store_state(p.page_pool + static_cast<int64_t>(p.ck_slot[ck]) * p.page_elems +
                   static_cast<int64_t>(h) * DK * dv);
@@ -999,7 +949,7 @@ hipError_t launch_local(const PrefillArgs& a) {
 template <int DK, int DVT, typename InT>
 hipError_t launch_prop(const PrefillArgs& a) {
   PropParams prm;
-  prm.q = a.q; prm.k = a.k; prm.v = a.v; prm.a = a.a; prm.tq = a.tq;
+  prm.v = a.v; prm.tq = a.tq;
   prm.s0 = a.s0; prm.o = a.o; prm.s_final = a.s_final;
   prm.page_pool = a.page_pool; prm.page_elems = a.page_elems;
   prm.chains = a.chains; prm.seqinfo = a.seqinfo; prm.ck_pos = a.ck_pos; prm.ck_slot = a.ck_slot;
