@@ -38,6 +38,14 @@ listed again, with the reason, in the design notes of the repository):
   R7  Replay with n_accepted = 0 leaves the state equal to the committed one
       and yields no output rows; for a batch with ragged n_accepted the output
       is padded to the draft length with zeros ([Serve demo] Tab 3 §6.4).
+  R8  Context parallelism (KCP): [Serve demo] §1.7 says its exchange does not
+      grow with the sequence length and §7.2 calls it a prefix scan, without
+      a formula.  Every step is affine in the state,
+      S_t = (I - beta_t k_t k_t^T) diag(exp(a_t)) S_{t-1} + beta_t k_t v_t^T,
+      so a segment of a sequence maps its start state to its end state by
+      S_end = A S_start + B (A is dk x dk, B is dk x dv, independent of the
+      length); segments compose by (A2, B2) o (A1, B1) = (A2 A1, A2 B1 + B2),
+      and the exchange is an exclusive scan of these pairs.
 """
 
 from fractions import Fraction
@@ -55,6 +63,8 @@ __all__ = [
     "snapshot_bytes_per_step",
     "projection_bytes_per_step",
     "kda_chunked_ref",
+    "segment_summary",
+    "compose_segments",
 ]
 
 
@@ -307,3 +317,45 @@ def kda_chunked_ref(q, k, v, a, beta, S0=None, chunk=64):
         o[lo:hi] = Qp @ S + np.tril(Qp @ Km.T) @ U
         S = g[n - 1][:, None] * S + Kh.T @ U
     return o, S
+
+
+# ---------------------------------------------------------------------------
+# Context-parallel segments (reading R8)
+
+def segment_summary(k, v, a, beta):
+    """Affine map of one segment of a sequence, per head.
+
+    k, a : (T, H, dk)   v : (T, H, dv)   beta : (T, H)
+    Returns (A, B), A (H, dk, dk) and B (H, dk, dv), with S_end = A @ S_start + B
+    for every start state.  Written as the plain product of the per-token maps
+    S <- (I - beta k k^T) diag(exp(a)) S + beta k v^T (decay, then error: R1).
+    """
+    k, v, a, beta = (_f64(x) for x in (k, v, a, beta))
+    T, H, dk = k.shape
+    dv = v.shape[2]
+    A = np.tile(np.eye(dk), (H, 1, 1))
+    B = np.zeros((H, dk, dv))
+    for t in range(T):
+        for h in range(H):
+            kk = k[t, h]
+            M = (np.eye(dk) - beta[t, h] * np.outer(kk, kk)) * np.exp(a[t, h])[None, :]
+            A[h] = M @ A[h]
+            B[h] = M @ B[h] + beta[t, h] * np.outer(kk, v[t, h])
+    return A, B
+
+
+def compose_segments(A, B, S_in=None):
+    """Exclusive scan of segment maps: the start state of every segment.
+
+    A : (n, H, dk, dk)   B : (n, H, dk, dv)   S_in : (H, dk, dv) or None (zero)
+    Returns (starts (n, H, dk, dv), S_end (H, dk, dv)) with starts[0] = S_in and
+    starts[i+1] = A[i] @ starts[i] + B[i].
+    """
+    A, B = _f64(A), _f64(B)
+    n, H, dk, dv = B.shape
+    S = np.zeros((H, dk, dv)) if S_in is None else _f64(S_in).copy()
+    starts = np.zeros((n, H, dk, dv))
+    for i in range(n):
+        starts[i] = S
+        S = A[i] @ S + B[i]
+    return starts, S

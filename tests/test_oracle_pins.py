@@ -12,9 +12,10 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
-from oracle import (kda_chunked_ref, kda_prefill, kda_recurrent, kda_step, pack_heads,
-                    projection_bytes_per_step, snapshot_bytes_per_step, snapshot_cost_ratio,
-                    unpack_heads, verify_and_replay)
+from oracle import (compose_segments, kda_chunked_ref, kda_prefill, kda_recurrent, kda_step,
+                    pack_heads, projection_bytes_per_step, segment_summary,
+                    snapshot_bytes_per_step, snapshot_cost_ratio, unpack_heads,
+                    verify_and_replay)
 from tests.conftest import GOLDEN
 
 
@@ -354,3 +355,67 @@ def test_snapshot_ratio_exceeds_one_grows_with_state_and_ignores_draft():
         s = draft * snapshot_bytes_per_step(2, 8, 8, 8)
         p = draft * projection_bytes_per_step(2, 8, 8, 8)
         assert Fraction(s, p) == snapshot_cost_ratio(2, 8, 8)
+
+
+# ------------------------------------------------- context-parallel segments
+@pytest.mark.parametrize("T,H,dk,dv", [(1, 1, 3, 2), (9, 2, 5, 4), (40, 2, 8, 8)])
+def test_segment_summary_is_the_affine_map_of_the_recurrence(T, H, dk, dv):
+    """A S0 + B equals the token-by-token recurrence from any S0 (and B alone
+    is the recurrence from S0 = 0)."""
+    rng = np.random.default_rng(60 + T)
+    q, k, v, a, beta = _rand_inputs(rng, T, H, dk, dv)
+    A, B = segment_summary(k, v, a, beta)
+    _, S_zero, _ = kda_recurrent(q, k, v, a, beta, np.zeros((H, dk, dv)))
+    np.testing.assert_allclose(B, S_zero, rtol=0, atol=1e-12)
+    for trial in range(2):
+        S0 = rng.standard_normal((H, dk, dv))
+        _, S_end, _ = kda_recurrent(q, k, v, a, beta, S0)
+        np.testing.assert_allclose(A @ S0 + B, S_end, rtol=0, atol=1e-12)
+
+
+def test_segment_summary_closed_forms():
+    rng = np.random.default_rng(61)
+    q, k, v, a, beta = _rand_inputs(rng, 6, 2, 4, 3)
+    # beta = 0: the state only decays, A = diag(exp(sum a)), B = 0.
+    A, B = segment_summary(k, v, a, np.zeros_like(beta))
+    for h in range(2):
+        np.testing.assert_allclose(A[h], np.diag(np.exp(a[:, h].sum(0))), rtol=1e-14, atol=0)
+    assert not B.any()
+    # One token, no decay, beta = 1, unit key: A = I - k k^T (a projector), B = k v^T.
+    k1 = np.array([[[0.6, 0.0, 0.8, 0.0]]])
+    v1 = np.array([[[1.0, -2.0, 0.5]]])
+    A, B = segment_summary(k1, v1, np.zeros((1, 1, 4)), np.ones((1, 1)))
+    np.testing.assert_allclose(A[0], np.eye(4) - np.outer(k1[0, 0], k1[0, 0]), atol=1e-15)
+    np.testing.assert_allclose(A[0] @ A[0], A[0], atol=1e-15)
+    np.testing.assert_allclose(A[0] @ k1[0, 0], 0.0, atol=1e-15)
+    np.testing.assert_allclose(B[0], np.outer(k1[0, 0], v1[0, 0]), atol=1e-15)
+
+
+def test_segment_maps_compose_and_scan_to_the_sequential_states():
+    """(A2, B2) o (A1, B1) = (A2 A1, A2 B1 + B2), and the exclusive scan of the
+    segment maps gives every segment's start state of the one-pass run."""
+    rng = np.random.default_rng(62)
+    T, H, dk, dv = 30, 2, 6, 5
+    q, k, v, a, beta = _rand_inputs(rng, T, H, dk, dv)
+    S_in = rng.standard_normal((H, dk, dv))
+    cuts = [0, 7, 8, 19, 30]
+    maps = [segment_summary(k[lo:hi], v[lo:hi], a[lo:hi], beta[lo:hi])
+            for lo, hi in zip(cuts[:-1], cuts[1:])]
+    A_all, B_all = segment_summary(k, v, a, beta)
+    A12 = maps[1][0] @ maps[0][0]
+    B12 = maps[1][0] @ maps[0][1] + maps[1][1]
+    A_ref, B_ref = segment_summary(k[:8], v[:8], a[:8], beta[:8])
+    np.testing.assert_allclose(A12, A_ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(B12, B_ref, rtol=0, atol=1e-12)
+    starts, S_end = compose_segments(np.stack([m[0] for m in maps]), np.stack([m[1] for m in maps]),
+                                     S_in)
+    for i, lo in enumerate(cuts[:-1]):
+        if lo == 0:
+            np.testing.assert_array_equal(starts[i], S_in)
+        else:
+            _, S_lo, _ = kda_recurrent(q[:lo], k[:lo], v[:lo], a[:lo], beta[:lo], S_in)
+            np.testing.assert_allclose(starts[i], S_lo, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(S_end, A_all @ S_in + B_all, rtol=0, atol=1e-12)
+    starts0, _ = compose_segments(np.stack([m[0] for m in maps]), np.stack([m[1] for m in maps]))
+    assert not starts0[0].any()
+
