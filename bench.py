@@ -9,7 +9,9 @@ slots) followed by packing the 16 final states into page slots.  `value` is
 that step's whole-job throughput in tokens/s with inputs resident in HBM.
 
 In the same run, and reported under "parts": the single-sequence prefill
-(T=8192, checkpoints every 512), 64 in-place decode steps (B=256 sessions),
+(T=8192, checkpoints every 512), the same sequence as 8 segments through
+segment summaries, composition and per-segment prefill (context-parallel
+prefill on one GPU), 64 in-place decode steps (B=256 sessions),
 verify-and-replay (B=64, H=16, d=32, 8 drafts) and pack/unpack of 16
 checkpoint states, each with its algorithmic bytes or flops against the
 MI355X peaks, plus the float64 CPU oracle timed on a bounded sample.
@@ -32,7 +34,9 @@ METRIC = "KDA prefill tokens/s (MFMA %) + decode/replay state GB/s (HBM %), H=32
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PROFILES = os.path.join(ROOT, "profiles")
-PREFILL_SRC = os.path.join(ROOT, "linear_attention_recurrence_kda_amd", "csrc", "kda_prefill.hip")
+CSRC = os.path.join(ROOT, "linear_attention_recurrence_kda_amd", "csrc")
+# The prefill kernels' sources (the traffic figure is stamped with their hash).
+PREFILL_SRC = [os.path.join(CSRC, "kda_prefill_kernels.hpp"), os.path.join(CSRC, "kda_prefill.hip")]
 
 
 def log(*a):
@@ -56,6 +60,14 @@ def prefill_bytes(tokens, H, dk, dv, n_seqs, n_ckpt, in_bytes=2, s0=True, final=
     b = tokens * H * ((3 * dk + dv + 1) * in_bytes + dv * in_bytes)
     b += n_ckpt * state + (n_seqs * state if s0 else 0) + (n_seqs * state if final else 0)
     return b
+
+
+def segment_flops(tokens, H, dk, dv, C):
+    """Algorithmic flops of the segment summaries per token-head: the k Gram
+    product 2C*dk and the triangular inverse C^2/3 (per chunk, shared by both
+    maps), then for each of the dv columns of B and the dk columns of A:
+    Z = V - (k g) S (2 dk), U = T Z (2C) and the state update (2 dk)."""
+    return tokens * H * (2 * C * dk + C * C / 3.0 + (dv + dk) * (4 * dk + 2 * C))
 
 
 def decode_bytes(B, H, dk, dv, in_bytes=2):
@@ -94,9 +106,12 @@ def run_steps(torch, fn, steps, warmup, kernel_fn=None):
     return wall / steps * 1e3, tm.kernel_ms()
 
 
-def src_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def src_hash(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def committed_traffic(name, kernel_src):
@@ -164,6 +179,94 @@ def bench_prefill(torch, kda, inputs, w, steps, warmup, pack_final, label):
     t_roof = max(flops / (BF16_PEAK_TFLOPS * 1e12), byts / (HBM_PEAK_GBS * 1e9))
     res["roofline_frac"] = t_roof / (kms * 1e-3)
     del d, pool, o, sf, ws
+    return res
+
+
+def bench_segments(torch, kda, inputs, w, steps, warmup, n_seg=8):
+    """Context-parallel prefill of one long sequence on one GPU: the sequence
+    cut into n_seg equal segments (the shares of n_seg ranks), then segment
+    summaries, their composition into start states, and the prefill of every
+    segment from its start (with the one-pass run's checkpoints, shifted into
+    segment coordinates).  The one-pass prefill is timed beside it."""
+    d = {n: torch.from_numpy(w[n]).to(torch.bfloat16).cuda() for n in ("q", "k", "v", "a", "beta")}
+    H, dk = w["k"].shape[1:]
+    dv = w["v"].shape[2]
+    T = int(w["cu_seqlens"][-1])
+    L = T // n_seg
+    cut = [i * L for i in range(n_seg)] + [T]
+    ck_all = w["checkpoints"][0]
+    ck = [[p - cut[i] for p in ck_all if cut[i] < p <= cut[i + 1]] for i in range(n_seg)]
+    n_ck = len(ck_all)
+    slots, j = [], 0
+    for c in ck:
+        slots.append(list(range(j, j + len(c))))
+        j += len(c)
+    pool = torch.zeros((n_ck, H * dk * dv), dtype=torch.float32, device="cuda")
+    A = torch.empty((n_seg, H, dk, dk), dtype=torch.float32, device="cuda")
+    B = torch.empty((n_seg, H, dk, dv), dtype=torch.float32, device="cuda")
+    starts = torch.empty((n_seg, H, dk, dv), dtype=torch.float32, device="cuda")
+    s_end = torch.empty((H, dk, dv), dtype=torch.float32, device="cuda")
+    o = torch.empty((T, H, dv), dtype=torch.bfloat16, device="cuda")
+    sf = torch.empty((n_seg, H, dk, dv), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(kda.segment_summary_workspace_size(n_seg, T, H, dk, dv, 64),
+                         kda.prefill_workspace_size(n_seg, T, H, dk, dv, 64, n_ck),
+                         kda.prefill_workspace_size(1, T, H, dk, dv, 64, n_ck)),
+                     dtype=torch.uint8, device="cuda")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+
+    def step(e):
+        if e is not None:
+            e[0].record()
+        kda.segment_summary(d["k"], d["v"], d["a"], d["beta"], cut, chunk=64, A=A, B=B, workspace=ws)
+        if e is not None:
+            e[1].record()
+        kda.compose_segments(A, B, None, starts=starts, s_end=s_end)
+        if e is not None:
+            e[2].record()
+        kda.chunk_prefill(d["q"], d["k"], d["v"], d["a"], d["beta"], cut, s0=starts, chunk=64,
+                          checkpoints=ck, ckpt_slots=slots, page_pool=pool, o=o, s_final=sf,
+                          workspace=ws)
+        if e is not None:
+            e[3].record()
+
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    ph = np.mean([[e[k].elapsed_time(e[k + 1]) for k in range(3)] for e in ev], axis=0)
+
+    o1 = torch.empty_like(o)
+    sf1 = torch.empty((1, H, dk, dv), dtype=torch.float32, device="cuda")
+
+    def one_pass(e):
+        if e is not None:
+            e[0].record()
+        kda.chunk_prefill(d["q"], d["k"], d["v"], d["a"], d["beta"], [0, T], chunk=64,
+                          checkpoints=[ck_all], ckpt_slots=[list(range(n_ck))], page_pool=pool,
+                          o=o1, s_final=sf1, workspace=ws)
+        if e is not None:
+            e[1].record()
+
+    _, ms1 = run_steps(torch, one_pass, steps, warmup)
+    # Agreement of the two paths on this workload (relative Frobenius).
+    rel = lambda x, y: float(torch.linalg.vector_norm((x - y).float()) / torch.linalg.vector_norm(y.float()))
+    flops = segment_flops(T, H, dk, dv, 64)
+    summ_ms = float(ph[0])
+    res = {"workload": f"context-parallel prefill on one GPU: T={T} (one sequence) in {n_seg} "
+                       f"segments of {L}, H={H}, dk=dv={dk}, bf16, S0=0, chunk 64, "
+                       f"ckpt every 512",
+           "ms_per_step": ms, "summary_ms": summ_ms, "compose_ms": float(ph[1]),
+           "rerun_ms": float(ph[2]), "one_pass_kernel_ms": ms1,
+           "tokens_per_s": T / (ms * 1e-3), "one_pass_tokens_per_s": T / (ms1 * 1e-3),
+           "summary_algo_gflop": flops / 1e9,
+           "summary_mfma_tflops": flops / (summ_ms * 1e-3) / 1e12,
+           "summary_mfma_frac": flops / (summ_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+           "o_rel_vs_one_pass": rel(o, o1), "s_end_rel_vs_one_pass": rel(s_end, sf1[0])}
+    del d, pool, A, B, starts, o, o1, sf, ws
     return res
 
 
@@ -334,8 +437,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--only", default="", help="comma list of: prefill4, prefill3, decode, replay, "
-                                               "replay_big, pack, copycal")
+    ap.add_argument("--only", default="", help="comma list of: prefill4, prefill3, segments, decode, "
+                                               "replay, replay_big, pack, copycal")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--json-out", default="")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -376,6 +479,10 @@ def main():
         parts["prefill_single"] = bench_prefill(
             torch, kda, inputs, inputs.workload3(), args.steps, args.warmup, False,
             "single-sequence prefill: T=8192, H=32, dk=dv=128, bf16, S0=0, chunk 64, ckpt every 512")
+    if want("segments"):
+        log("segments (context-parallel prefill on one GPU) ...")
+        parts["segments"] = bench_segments(torch, kda, inputs, inputs.workload3(), args.steps,
+                                           args.warmup)
     if want("decode"):
         log("decode ...")
         parts["decode"] = bench_decode(torch, kda, inputs, args.steps, args.warmup)

@@ -168,12 +168,15 @@ int kda_unpack_heads(const float* page_pool, int64_t page_elems, int64_t n_slots
  *                    is written in the pack layout and zero-padded
  *   workspace      : device memory of at least kda_chunk_prefill_workspace_size
  *                    bytes, 256-byte aligned; contents on entry are ignored.  It
- *                    holds the work list and, per (chunk, head), the chunk's
- *                    T diag(beta) and lower(A_qk) tiles (2 * chunk^2 elements
- *                    of in_dtype), written by a first kernel that handles all
- *                    chunks at once and read by the sequential one: about
- *                    (T_tot / chunk + n_seqs + n_ckpt) * H * 2 * chunk^2 * 2
- *                    bytes for bf16 (0.9 GB for 128k tokens, H = 32, chunk 64).
+ *                    holds the work list and one record per (chunk, head),
+ *                    written by a first kernel that handles all chunks at once
+ *                    and read by the sequential one: T diag(beta) and
+ *                    lower(A_qk) (chunk^2 elements each), k*g, q*g and
+ *                    (k*g_n/g)^T (chunk*dk elements each) in in_dtype, and g_n
+ *                    (dk fp32).  That is about
+ *                    (T_tot / chunk + n_seqs + n_ckpt) * H * (2 chunk^2 +
+ *                    3 chunk dk) * 2 bytes for bf16 (4.3 GB for 128k tokens,
+ *                    H = 32, dk = 128, chunk 64).
  * Sizes: T_tot < 2^31 tokens, H*dk*dv < 2^31, H*max(dk, dv) <= 2^24, and
  * (number of chunks) * H < 2^31.
  */
@@ -207,6 +210,51 @@ int kda_chunk_prefill_split(const void* q, const void* k, const void* v, const v
                             const int32_t* ckpt_slot_host, int64_t n_ckpt, float* page_pool,
                             int64_t page_elems, int64_t n_slots, void* workspace,
                             size_t workspace_bytes, int32_t dv_split, void* stream);
+
+/*
+ * Segment summaries for context-parallel prefill ([Serve demo] §7.2 "KCP 前缀扫描",
+ * §1.7: what a segment of a long sequence passes on has a size independent of
+ * its length).  Each token maps the state affinely,
+ *   S -> (I - beta k k^T) diag(exp(a)) S + beta k v^T,
+ * so a segment maps its start state to its end state as S_end = A S_start + B.
+ *
+ * kda_segment_summary — (A, B) of every segment of a token-packed input.
+ *   k, a : [T_tot, H, dk]   v : [T_tot, H, dv]   beta : [T_tot, H]   (in_dtype)
+ *   cu_seg_host : host int32 [n_seg + 1], segment boundaries as for cu_seqlens
+ *   A_out : [n_seg, H, dk, dk] fp32, the linear part (identity for an empty segment)
+ *   B_out : [n_seg, H, dk, dv] fp32, the end state from the zero start state
+ *   workspace : at least kda_segment_summary_workspace_size bytes, 256-byte aligned
+ * chunk, the decay bound, dtypes and size limits are those of kda_chunk_prefill
+ * (same chunk form: B is the prefill's final state from s0 = 0, and A is the
+ * same propagation run from the identity with v = 0), plus H*dk*dk < 2^31.
+ * Outputs must not overlap the inputs or each other (KDA_EALIAS).
+ */
+int kda_segment_summary_workspace_size(int32_t n_seg, int64_t total_tokens, int32_t H,
+                                       int32_t dk, int32_t dv, int32_t chunk,
+                                       kda_dtype in_dtype, size_t* bytes);
+
+int kda_segment_summary(const void* k, const void* v, const void* a, const void* beta,
+                        kda_dtype in_dtype, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
+                        const int32_t* cu_seg_host, int32_t n_seg, float* A_out, float* B_out,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kda_compose_segments — the exclusive scan of segment maps under
+ * (A2, B2) o (A1, B1) = (A2 A1, A2 B1 + B2): the start state of every segment
+ * of one sequence, given the sequence's start state.
+ *   A : [n_seg, H, dk, dk] fp32, 16-byte aligned   B : [n_seg, H, dk, dv] fp32
+ *   s_in     : [H, dk, dv] fp32 start state of segment 0, or NULL for zero
+ *   s_starts : [n_seg, H, dk, dv] fp32; s_starts[0] = s_in,
+ *              s_starts[i+1] = A[i] s_starts[i] + B[i]
+ *   s_end    : [H, dk, dv] fp32 or NULL; A[n-1] s_starts[n-1] + B[n-1]
+ *              (s_in when n_seg = 0)
+ * fp32 arithmetic, sums in a fixed order (deterministic).  Running
+ * kda_chunk_prefill over the segments as sequences with s0 = s_starts gives
+ * the outputs and states of one pass over the whole sequence.
+ */
+int kda_compose_segments(const float* A, const float* B, int32_t n_seg, int32_t H, int32_t dk,
+                         int32_t dv, const float* s_in, float* s_starts, float* s_end,
+                         void* stream);
 
 #ifdef __cplusplus
 }

@@ -159,4 +159,26 @@ int kda_unpack_heads(const float* page_pool, int64_t page_elems, int64_t n_slots
                      err_flag, true, stream);
 }
 
+int kda_compose_segments(const float* A, const float* B, int32_t n_seg, int32_t H, int32_t dk,
+                         int32_t dv, const float* s_in, float* s_starts, float* s_end,
+                         void* stream) {
+  if (n_seg < 0 || H <= 0) return fail(KDA_EINVAL, "n_seg=%d H=%d", n_seg, H);
+  if (!supported_dim(dk) || !supported_dim(dv))
+    return fail(KDA_EUNSUPPORTED, "dk=%d dv=%d (supported: 16, 32, 64, 128)", dk, dv);
+  const int64_t hkv = static_cast<int64_t>(H) * dk * dv, hkk = static_cast<int64_t>(H) * dk * dk;
+  if (std::max(hkv, hkk) >= (int64_t{1} << 31))
+    return fail(KDA_EUNSUPPORTED, "H*dk*max(dk, dv) must be below 2^31");
+  if (n_seg > 0 && (!A || !B || !s_starts)) return fail(KDA_EINVAL, "A, B and s_starts must not be null");
+  if (n_seg == 0 && !s_end) return ok();
+  if (!aligned16(A)) return fail(KDA_EINVAL, "A must be 16-byte aligned");
+  const size_t n = static_cast<size_t>(n_seg), sb = static_cast<size_t>(hkv) * 4;
+  const std::vector<Range> ins = {{A, n * static_cast<size_t>(hkk) * 4, "A"}, {B, n * sb, "B"},
+                                  {s_in, s_in ? sb : 0, "s_in"}};
+  const std::vector<Range> outs = {{s_starts, n * sb, "s_starts"}, {s_end, s_end ? sb : 0, "s_end"}};
+  const int st = check_disjoint(outs, ins);
+  if (st) return st;
+  kda::ComposeArgs p{A, B, s_in, s_starts, s_end, n_seg, H, dk, dv, static_cast<hipStream_t>(stream)};
+  return hip_status(kda::launch_compose(p), "compose launch");
+}
+
 }  // extern "C"

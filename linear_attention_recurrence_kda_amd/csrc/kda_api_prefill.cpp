@@ -80,35 +80,16 @@ int choose_split(int32_t dk, int32_t dv, bool bf16, int64_t total_chunks, int64_
   return best;
 }
 
-}  // namespace
-
-extern "C" {
-
-int kda_chunk_prefill_workspace_size(int32_t n_seqs, int64_t total_tokens, int32_t H, int32_t dk,
-                                     int32_t dv, int32_t chunk, int64_t n_ckpt, kda_dtype in_dtype,
-                                     size_t* bytes) {
-  if (!bytes) return fail(KDA_EINVAL, "bytes is null");
-  if (!valid_dtype(in_dtype)) return fail(KDA_EINVAL, "in_dtype %d", static_cast<int>(in_dtype));
-  if (n_seqs < 0 || total_tokens < 0 || H <= 0 || n_ckpt < 0)
-    return fail(KDA_EINVAL, "n_seqs=%d total_tokens=%lld H=%d n_ckpt=%lld", n_seqs,
-                static_cast<long long>(total_tokens), H, static_cast<long long>(n_ckpt));
-  if (!supported_dim(dk) || !supported_dim(dv))
-    return fail(KDA_EUNSUPPORTED, "dk=%d dv=%d (supported: 16, 32, 64, 128)", dk, dv);
-  if (chunk < 16 || chunk > KDA_MAX_CHUNK || chunk % 16)
-    return fail(KDA_EUNSUPPORTED, "chunk=%d (a multiple of 16 up to %d)", chunk, KDA_MAX_CHUNK);
-  const int64_t mc = max_chunks(n_seqs, total_tokens, chunk, n_ckpt);
-  *bytes = align256(work_ints(n_seqs, H, n_ckpt, mc) * 4) + tile_bytes(mc, H, chunk, dk, elem_size(in_dtype));
-  return ok();
-}
-
-int kda_chunk_prefill_split(const void* q, const void* k, const void* v, const void* a,
-                            const void* beta, kda_dtype in_dtype, int32_t H, int32_t dk,
-                            int32_t dv, int32_t chunk, const int32_t* cu, int32_t n_seqs,
-                            const float* s0, void* o, float* s_final, const int32_t* ck_cu,
-                            const int32_t* ck_pos, const int32_t* ck_slot, int64_t n_ckpt,
-                            float* page_pool, int64_t page_elems, int64_t n_slots,
-                            void* workspace, size_t workspace_bytes, int32_t dv_split,
-                            void* stream) {
+// Prefill (a_out == nullptr) or segment summaries (a_out != nullptr: q is
+// unused, o and s0 are null and s_final receives B; see kda_segment_summary).
+int prefill_impl(const void* q, const void* k, const void* v, const void* a, const void* beta,
+                 kda_dtype in_dtype, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
+                 const int32_t* cu, int32_t n_seqs, const float* s0, void* o, float* s_final,
+                 const int32_t* ck_cu, const int32_t* ck_pos, const int32_t* ck_slot,
+                 int64_t n_ckpt, float* page_pool, int64_t page_elems, int64_t n_slots,
+                 void* workspace, size_t workspace_bytes, int32_t dv_split, float* a_out,
+                 void* stream) {
+  const bool summary = a_out != nullptr;
   if (!valid_dtype(in_dtype)) return fail(KDA_EINVAL, "in_dtype %d", static_cast<int>(in_dtype));
   if (n_seqs < 0 || H <= 0 || n_ckpt < 0)
     return fail(KDA_EINVAL, "n_seqs=%d H=%d n_ckpt=%lld", n_seqs, H, static_cast<long long>(n_ckpt));
@@ -120,6 +101,8 @@ int kda_chunk_prefill_split(const void* q, const void* k, const void* v, const v
     return fail(KDA_EUNSUPPORTED, "chunk=%d: fp32 inputs take chunks of at most 32 rows", chunk);
   const int64_t hkv = static_cast<int64_t>(H) * dk * dv;
   if (hkv >= (int64_t{1} << 31)) return fail(KDA_EUNSUPPORTED, "H*dk*dv must be below 2^31");
+  const int64_t hkk = static_cast<int64_t>(H) * dk * dk;
+  if (summary && hkk >= (int64_t{1} << 31)) return fail(KDA_EUNSUPPORTED, "H*dk*dk must be below 2^31");
   // The kernel addresses one chunk's rows with 32-bit byte offsets.
   if (static_cast<int64_t>(H) * std::max(dk, dv) > (int64_t{1} << 24))
     return fail(KDA_EUNSUPPORTED, "H*max(dk, dv) must be at most 2^24");
@@ -179,16 +162,20 @@ int kda_chunk_prefill_split(const void* q, const void* k, const void* v, const v
     return fail(KDA_EUNSUPPORTED,
                 "dv_split=%d with dv=%d (dv/split must be 16, 32 or 64)",
                 dv_split, dv);
+  // The linear part A of a summary propagates dk identity columns.
+  const int a_split = summary ? choose_split(dk, dk, bf16, n_chunks * H, longest) : 0;
 
   // Buffers.
   const size_t es = elem_size(in_dtype);
-  if (T > 0 && (!q || !k || !v || !a || !beta || !o)) return fail(KDA_EINVAL, "null input or output");
+  if (summary && (!s_final || (n_seqs > 0 && !a_out))) return fail(KDA_EINVAL, "A_out and B_out must not be null");
+  if (T > 0 && (!q || !k || !v || !a || !beta || (!summary && !o)))
+    return fail(KDA_EINVAL, "null input or output");
   // The kernel reads q, k, a, v as pairs of consecutive elements.
   for (const void* ptr : {q, k, v, a})
     if (reinterpret_cast<uintptr_t>(ptr) % (2 * es))
       return fail(KDA_EINVAL, "q, k, v, a must be aligned to two elements");
   // Output rows are written in 16-byte pieces.
-  if (reinterpret_cast<uintptr_t>(o) % 16) return fail(KDA_EINVAL, "o must be 16-byte aligned");
+  if (!summary && reinterpret_cast<uintptr_t>(o) % 16) return fail(KDA_EINVAL, "o must be 16-byte aligned");
   const size_t list_bytes = align256(work_ints(n_seqs, H, n_ckpt, n_chunks) * 4);
   const size_t need = list_bytes + tile_bytes(n_chunks, H, chunk, dk, es);
   if (!workspace || workspace_bytes < need)
@@ -201,7 +188,8 @@ int kda_chunk_prefill_split(const void* q, const void* k, const void* v, const v
                                   {v, tok * dv * es, "v"}, {a, tok * dk * es, "a"},
                                   {beta, tok * es, "beta"}, {s0, s0 ? sbytes : 0, "s0"}};
   const std::vector<Range> outs = {
-      {o, tok * dv * es, "o"}, {s_final, s_final ? sbytes : 0, "s_final"},
+      {o, summary ? 0 : tok * dv * es, "o"}, {s_final, s_final ? sbytes : 0, summary ? "B_out" : "s_final"},
+      {a_out, summary ? static_cast<size_t>(n_seqs) * hkk * 4 : 0, "A_out"},
       {page_pool, n_ckpt > 0 ? static_cast<size_t>(n_slots) * page_elems * 4 : 0, "page_pool"},
       {workspace, need, "workspace"}};
   int st = check_disjoint(outs, ins);
@@ -282,7 +270,42 @@ int kda_chunk_prefill_split(const void* q, const void* k, const void* v, const v
   p.n_chains = static_cast<int>(n_chains);
   p.dv_tiles = split;
   p.stream = hs;
+  if (summary) return hip_status(kda::launch_segment_summary(p, a_out, a_split), "segment summary launch");
   return hip_status(kda::launch_prefill(p), "prefill launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_chunk_prefill_workspace_size(int32_t n_seqs, int64_t total_tokens, int32_t H, int32_t dk,
+                                     int32_t dv, int32_t chunk, int64_t n_ckpt, kda_dtype in_dtype,
+                                     size_t* bytes) {
+  if (!bytes) return fail(KDA_EINVAL, "bytes is null");
+  if (!valid_dtype(in_dtype)) return fail(KDA_EINVAL, "in_dtype %d", static_cast<int>(in_dtype));
+  if (n_seqs < 0 || total_tokens < 0 || H <= 0 || n_ckpt < 0)
+    return fail(KDA_EINVAL, "n_seqs=%d total_tokens=%lld H=%d n_ckpt=%lld", n_seqs,
+                static_cast<long long>(total_tokens), H, static_cast<long long>(n_ckpt));
+  if (!supported_dim(dk) || !supported_dim(dv))
+    return fail(KDA_EUNSUPPORTED, "dk=%d dv=%d (supported: 16, 32, 64, 128)", dk, dv);
+  if (chunk < 16 || chunk > KDA_MAX_CHUNK || chunk % 16)
+    return fail(KDA_EUNSUPPORTED, "chunk=%d (a multiple of 16 up to %d)", chunk, KDA_MAX_CHUNK);
+  const int64_t mc = max_chunks(n_seqs, total_tokens, chunk, n_ckpt);
+  *bytes = align256(work_ints(n_seqs, H, n_ckpt, mc) * 4) + tile_bytes(mc, H, chunk, dk, elem_size(in_dtype));
+  return ok();
+}
+
+int kda_chunk_prefill_split(const void* q, const void* k, const void* v, const void* a,
+                            const void* beta, kda_dtype in_dtype, int32_t H, int32_t dk,
+                            int32_t dv, int32_t chunk, const int32_t* cu, int32_t n_seqs,
+                            const float* s0, void* o, float* s_final, const int32_t* ck_cu,
+                            const int32_t* ck_pos, const int32_t* ck_slot, int64_t n_ckpt,
+                            float* page_pool, int64_t page_elems, int64_t n_slots,
+                            void* workspace, size_t workspace_bytes, int32_t dv_split,
+                            void* stream) {
+  return prefill_impl(q, k, v, a, beta, in_dtype, H, dk, dv, chunk, cu, n_seqs, s0, o, s_final,
+                      ck_cu, ck_pos, ck_slot, n_ckpt, page_pool, page_elems, n_slots, workspace,
+                      workspace_bytes, dv_split, nullptr, stream);
 }
 
 int kda_chunk_prefill(const void* q, const void* k, const void* v, const void* a,
@@ -296,6 +319,24 @@ int kda_chunk_prefill(const void* q, const void* k, const void* v, const void* a
                                  n_seqs, s0, o, s_final, ckpt_cu_host, ckpt_pos_host,
                                  ckpt_slot_host, n_ckpt, page_pool, page_elems, n_slots, workspace,
                                  workspace_bytes, 0, stream);
+}
+
+int kda_segment_summary_workspace_size(int32_t n_seg, int64_t total_tokens, int32_t H, int32_t dk,
+                                       int32_t dv, int32_t chunk, kda_dtype in_dtype,
+                                       size_t* bytes) {
+  return kda_chunk_prefill_workspace_size(n_seg, total_tokens, H, dk, dv, chunk, 0, in_dtype, bytes);
+}
+
+int kda_segment_summary(const void* k, const void* v, const void* a, const void* beta,
+                        kda_dtype in_dtype, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
+                        const int32_t* cu_seg_host, int32_t n_seg, float* A_out, float* B_out,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (n_seg > 0 && !A_out) return fail(KDA_EINVAL, "A_out must not be null");
+  if (n_seg == 0) return ok();
+  // The summary kernels read no q: the local kernel is handed k in its place.
+  return prefill_impl(k, k, v, a, beta, in_dtype, H, dk, dv, chunk, cu_seg_host, n_seg, nullptr,
+                      nullptr, B_out, nullptr, nullptr, nullptr, 0, nullptr, 0, 0, workspace,
+                      workspace_bytes, 0, A_out, stream);
 }
 
 }  // extern "C"

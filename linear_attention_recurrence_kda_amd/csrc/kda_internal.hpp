@@ -81,4 +81,19 @@ struct PrefillArgs {
 };
 hipError_t launch_prefill(const PrefillArgs& p);
 
+// Segment summaries: the work list and records of a prefill over the segments
+// (q unused, o and s0 null), then two propagations: p.s_final receives B (the
+// end state from the zero state) and a_out [n_seqs][H][dk][dk] receives A (the
+// end state from the identity with v = 0), propagated in a_tiles column tiles.
+hipError_t launch_segment_summary(const PrefillArgs& p, float* a_out, int a_tiles);
+
+// Exclusive scan of segment maps: starts[i] = A[i-1] starts[i-1] + B[i-1].
+struct ComposeArgs {
+  const float *A, *B, *s_in;
+  float *starts, *s_end;
+  int n, H, dk, dv;
+  hipStream_t stream;
+};
+hipError_t launch_compose(const ComposeArgs& p);
+
 }  // namespace kda

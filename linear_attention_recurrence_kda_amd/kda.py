@@ -42,6 +42,11 @@ SIGNATURES = {
     "kda_chunk_prefill_split": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int, _i32, _i32,
                                                _i32, _i32, _i32p, _i32, _vp, _vp, _vp, _i32p, _i32p,
                                                _i32p, _i64, _vp, _i64, _i64, _vp, _sz, _i32, _vp]),
+    "kda_segment_summary_workspace_size": (ctypes.c_int, [_i32, _i64, _i32, _i32, _i32, _i32,
+                                                          ctypes.c_int, ctypes.POINTER(_sz)]),
+    "kda_segment_summary": (ctypes.c_int, [_vp, _vp, _vp, _vp, ctypes.c_int, _i32, _i32, _i32, _i32,
+                                           _i32p, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "kda_compose_segments": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
 }
 
 _lib = None
@@ -269,3 +274,62 @@ def chunk_prefill(q, k, v, a, beta, cu_seqlens, s0=None, chunk=64, checkpoints=N
               _i32_array(ck_pos), _i32_array(ck_slot), n_ckpt, _ptr(page_pool), page_elems,
               n_slots, _ptr(workspace), workspace.numel(), dv_split, _stream(dev)))
     return o, s_final
+
+
+def segment_summary_workspace_size(n_seg, total_tokens, H, dk, dv, chunk, dtype=torch.bfloat16):
+    out = ctypes.c_size_t(0)
+    code = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32
+    _check(lib().kda_segment_summary_workspace_size(n_seg, total_tokens, H, dk, dv, chunk, code,
+                                                    ctypes.byref(out)))
+    return out.value
+
+
+def segment_summary(k, v, a, beta, cu_segments, chunk=64, A=None, B=None, workspace=None):
+    """Affine maps S_end = A S_start + B of the segments of a token-packed input.
+
+    k, a [T,H,dk], v [T,H,dv], beta [T,H] (float32 or bfloat16, same dtype);
+    cu_segments: host sequence of n+1 segment offsets.
+    Returns (A [n,H,dk,dk], B [n,H,dk,dv]), fp32.
+    """
+    T, H, dk = k.shape
+    dv = v.shape[-1]
+    dev, dt = k.device, k.dtype
+    for t, shp, nm in ((k, (T, H, dk), "k"), (a, (T, H, dk), "a"), (v, (T, H, dv), "v"),
+                       (beta, (T, H), "beta")):
+        _expect(t, shp, dt, nm, dev)
+    cu = [int(x) for x in cu_segments]
+    n = len(cu) - 1
+    if A is None:
+        A = torch.empty((n, H, dk, dk), dtype=torch.float32, device=dev)
+    if B is None:
+        B = torch.empty((n, H, dk, dv), dtype=torch.float32, device=dev)
+    _expect(A, (n, H, dk, dk), torch.float32, "A", dev)
+    _expect(B, (n, H, dk, dv), torch.float32, "B", dev)
+    need = segment_summary_workspace_size(n, T, H, dk, dv, chunk, dt)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(lib().kda_segment_summary(_ptr(k), _ptr(v), _ptr(a), _ptr(beta), _dtype_code(k), H, dk,
+                                     dv, chunk, _i32_array(cu), n, _ptr(A), _ptr(B),
+                                     _ptr(workspace), workspace.numel(), _stream(dev)))
+    return A, B
+
+
+def compose_segments(A, B, s_in=None, starts=None, s_end=None):
+    """Exclusive scan of segment maps: starts[0] = s_in (zero if None),
+    starts[i+1] = A[i] starts[i] + B[i].  A [n,H,dk,dk], B [n,H,dk,dv] fp32;
+    s_in [H,dk,dv] fp32 or None.  Returns (starts [n,H,dk,dv], s_end [H,dk,dv])."""
+    n, H, dk, dv = B.shape
+    dev = B.device
+    _expect(A, (n, H, dk, dk), torch.float32, "A", dev)
+    _expect(B, (n, H, dk, dv), torch.float32, "B", dev)
+    if s_in is not None:
+        _expect(s_in, (H, dk, dv), torch.float32, "s_in", dev)
+    if starts is None:
+        starts = torch.empty((n, H, dk, dv), dtype=torch.float32, device=dev)
+    if s_end is None:
+        s_end = torch.empty((H, dk, dv), dtype=torch.float32, device=dev)
+    _expect(starts, (n, H, dk, dv), torch.float32, "starts", dev)
+    _expect(s_end, (H, dk, dv), torch.float32, "s_end", dev)
+    _check(lib().kda_compose_segments(_ptr(A), _ptr(B), n, H, dk, dv, _ptr(s_in), _ptr(starts),
+                                      _ptr(s_end), _stream(dev)))
+    return starts, s_end

@@ -38,7 +38,7 @@ listed again, with the reason, in the design notes of the repository):
   R7  Replay with n_accepted = 0 leaves the state equal to the committed one
       and yields no output rows; for a batch with ragged n_accepted the output
       is padded to the draft length with zeros ([Serve demo] Tab 3 §6.4).
-  R8  Context parallelism (KCP): [Serve demo] §1.7 says its exchange does not
+  R13 Context parallelism (KCP): [Serve demo] §1.7 says its exchange does not
       grow with the sequence length and §7.2 calls it a prefix scan, without
       a formula.  Every step is affine in the state,
       S_t = (I - beta_t k_t k_t^T) diag(exp(a_t)) S_{t-1} + beta_t k_t v_t^T,
@@ -320,7 +320,7 @@ def kda_chunked_ref(q, k, v, a, beta, S0=None, chunk=64):
 
 
 # ---------------------------------------------------------------------------
-# Context-parallel segments (reading R8)
+# Context-parallel segments (reading R13)
 
 def segment_summary(k, v, a, beta):
     """Affine map of one segment of a sequence, per head.

@@ -132,3 +132,43 @@ def test_prefill_validation(L):
     assert b"o must be 16-byte aligned" in L.kda_last_error()
     assert call(H=(1 << 17) + 1, dk=16) == kda.KDA_EUNSUPPORTED           # 32-bit chunk offsets
     assert b"2^24" in L.kda_last_error()
+
+
+def test_segment_validation(L):
+    """Argument checks of the segment summary and the composition."""
+    k, v, a, b, A, B, ws = (_fake(i) for i in range(7))
+    I32 = ctypes.c_int32
+
+    def summ(dtype=1, H=2, dk=128, dv=128, chunk=64, cu=(0, 40, 100), A_ptr=A, B_ptr=B, ws_ptr=ws):
+        cu_a = (I32 * len(cu))(*cu)
+        return L.kda_segment_summary(k, v, a, b, dtype, H, dk, dv, chunk, cu_a, len(cu) - 1, A_ptr,
+                                     B_ptr, ws_ptr, 1 << 20, None)
+
+    assert summ(dk=24) == kda.KDA_EUNSUPPORTED
+    assert summ(dtype=0, chunk=64) == kda.KDA_EUNSUPPORTED
+    assert summ(cu=(0, 40, 30)) == kda.KDA_EINVAL
+    assert summ(A_ptr=None) == kda.KDA_EINVAL
+    assert summ(B_ptr=None) == kda.KDA_EINVAL
+    assert summ(A_ptr=P(B.value + 64)) == kda.KDA_EALIAS                 # A overlaps B
+    assert summ(ws_ptr=P(ws.value + 16)) == kda.KDA_EINVAL              # 256-byte alignment
+    assert summ(cu=(0, 4000, 10000)) == kda.KDA_EWORKSPACE              # 1 MiB is too small
+    sz = ctypes.c_size_t(0)
+    assert L.kda_segment_summary_workspace_size(3, 300, 2, 128, 128, 64, 1, ctypes.byref(sz)) == 0
+    want = ctypes.c_size_t(0)
+    assert L.kda_chunk_prefill_workspace_size(3, 300, 2, 128, 128, 64, 0, 1, ctypes.byref(want)) == 0
+    assert sz.value == want.value
+
+    s_in, st, end = _fake(7), _fake(8), _fake(9)
+
+    def comp(n=3, H=2, dk=64, dv=32, A_ptr=A, B_ptr=B, st_ptr=st, end_ptr=end):
+        return L.kda_compose_segments(A_ptr, B_ptr, n, H, dk, dv, s_in, st_ptr, end_ptr, None)
+
+    assert comp(dk=24) == kda.KDA_EUNSUPPORTED
+    assert comp(n=-1) == kda.KDA_EINVAL
+    assert comp(H=0) == kda.KDA_EINVAL
+    assert comp(A_ptr=None) == kda.KDA_EINVAL
+    assert comp(st_ptr=None) == kda.KDA_EINVAL
+    assert comp(A_ptr=P(A.value + 4)) == kda.KDA_EINVAL                  # float4 rows of A
+    assert comp(st_ptr=P(B.value + 128)) == kda.KDA_EALIAS               # starts overlap B
+    assert comp(end_ptr=P(st.value + 4)) == kda.KDA_EALIAS               # end overlaps starts
+    assert comp(n=0, end_ptr=None) == kda.KDA_OK                         # nothing to do
