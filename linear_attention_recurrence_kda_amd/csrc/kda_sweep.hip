@@ -1,4 +1,4 @@
-// Decode step and verify-and-replay: a bandwidth-bound sweep over per-head
+// Decode step and verify-and-replay: bandwidth-bound sweeps over per-head
 // fp32 states.
 //
 // One workgroup owns one (session, head) state S (DK x DV, fp32) for the whole
@@ -16,10 +16,15 @@
 // The sums over i (the key dimension) are split over row groups: partial sums
 // in registers, a cross-lane butterfly inside the wave, then LDS across
 // waves.  State stores are nontemporal (the state is streamed once per call
-// and is larger than the caches); an out-of-place sweep also loads the
-// committed state nontemporally, while an in-place one (decode) keeps plain
-// loads, which measured fastest on MI355X for the read-then-overwrite pattern.  Replay (the "verify_and_replay" of §1.2) runs n_accepted such steps
-// on the register-resident state, reading a committed state it never writes.
+// and is larger than the caches).
+//
+// Two kernels, each the faster of the variants measured for its case:
+//  - decode_kernel: one step, state updated in place, plain loads (fastest on
+//    MI355X for the read-then-overwrite pattern);
+//  - replay_kernel (the "verify_and_replay" of §1.2): n_accepted steps on the
+//    register-resident state, read from a committed state it never writes
+//    (nontemporal loads), with the next two steps' inputs in flight and one
+//    workgroup barrier per step.
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
 
@@ -47,8 +52,12 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-template <int DK, int DV, typename InT, bool INPLACE>
-__global__ __launch_bounds__((SweepShape<DK, DV>::NT)) void sweep_kernel(
+// The decode step, in place (s_in == s_out, t_draft = 1, no n_accepted).
+// This is the step loop in the shape that measured fastest for a single
+// in-place step: inputs one step ahead, two barriers per step, outputs stored
+// by row group 0.
+template <int DK, int DV, typename InT>
+__global__ __launch_bounds__((SweepShape<DK, DV>::NT)) void decode_kernel(
     const float* s_in, float* s_out, const InT* __restrict__ q, const InT* __restrict__ k,
     const InT* __restrict__ v, const InT* __restrict__ a, const InT* __restrict__ beta,
     const int32_t* __restrict__ n_accepted, int t_draft, int B, int H, InT* __restrict__ o,
@@ -86,7 +95,7 @@ __global__ __launch_bounds__((SweepShape<DK, DV>::NT)) void sweep_kernel(
   for (int m = 0; m < RPT; ++m) {
     const int r = rg + m * RG;
     const f32x4v* sp = reinterpret_cast<const f32x4v*>(s_in + sbase + static_cast<size_t>(r) * DV + 4 * cg);
-    const f32x4v x = INPLACE ? *sp : __builtin_nontemporal_load(sp);
+    const f32x4v x = *sp;
     S[m] = make_float4(x[0], x[1], x[2], x[3]);
   }
 
@@ -203,11 +212,223 @@ __global__ __launch_bounds__((SweepShape<DK, DV>::NT)) void sweep_kernel(
     if (rg == 0) {
       InT* op = o + (static_cast<size_t>(bh) * o_steps + i) * DV + 4 * cg;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) op[c] = from_f32<InT>(out[c]);
+      for (int c = 0; c < 4; ++c) op[c] = from_f32_int<InT>(out[c]);
     }
     if (i + 1 < n) stash(cur ^ 1);
     sync();  // step i's readers are done; step i+1's inputs are visible
   }
+
+  // Rows past the accepted prefix are zero.
+  if (rg == 0) {
+    for (int i = n; i < o_steps; ++i) {
+      InT* op = o + (static_cast<size_t>(bh) * o_steps + i) * DV + 4 * cg;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) op[c] = from_f32_int<InT>(0.f);
+    }
+  }
+
+#pragma unroll
+  for (int m = 0; m < RPT; ++m) {
+    const int r = rg + m * RG;
+    const f32x4v x = {S[m].x, S[m].y, S[m].z, S[m].w};
+    __builtin_nontemporal_store(x, reinterpret_cast<f32x4v*>(s_out + sbase + static_cast<size_t>(r) * DV + 4 * cg));
+  }
+}
+
+template <int DK, int DV, typename InT>
+__global__ __launch_bounds__((SweepShape<DK, DV>::NT)) void replay_kernel(
+    const float* s_in, float* s_out, const InT* __restrict__ q, const InT* __restrict__ k,
+    const InT* __restrict__ v, const InT* __restrict__ a, const InT* __restrict__ beta,
+    const int32_t* __restrict__ n_accepted, int t_draft, int B, int H, InT* __restrict__ o,
+    int o_steps, int32_t* __restrict__ err_flag) {
+  using Sh = SweepShape<DK, DV>;
+  constexpr int CG = Sh::CG, RG = Sh::RG, RPT = Sh::RPT, NW = Sh::NW, NT = Sh::NT;
+  constexpr int EK = Sh::EK, EV = Sh::EV;
+
+  const int bh = blockIdx.x;  // b * H + h
+  const int b = bh / H;
+  const int tid = threadIdx.x;
+  const int cg = tid % CG;
+  const int rg = tid / CG;
+  const int lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+
+  // Step inputs, triple-buffered (step i+1 is fetched while step i computes,
+  // and stashed before step i's barrier, while slower threads may still read
+  // step i-1's buffer), and the cross-wave partial sums, double-buffered: one
+  // workgroup barrier per step.
+  // Per key row r: s_p = (e k, e q, k q, e) for the sums over rows and
+  // s_u = (e, beta k) for the update, with e = exp(a_r).
+  __shared__ float4 s_p[3][DK];
+  __shared__ float2 s_u[3][DK];
+  __shared__ float s_v[3][DV];
+  __shared__ float s_beta[3];
+  __shared__ float s_red[2][NW][CG][9];
+
+  int n = t_draft;
+  if (n_accepted != nullptr) {
+    n = n_accepted[b];
+    if (n < 0 || n > t_draft) {
+      if (err_flag != nullptr && tid == 0) *err_flag = 1;
+      n = n < 0 ? 0 : t_draft;
+    }
+  }
+  n = __builtin_amdgcn_readfirstlane(n);
+
+  // Load the state once.
+  const size_t sbase = static_cast<size_t>(bh) * DK * DV;
+  float4 S[RPT];
+#pragma unroll
+  for (int m = 0; m < RPT; ++m) {
+    const int r = rg + m * RG;
+    const f32x4v* sp = reinterpret_cast<const f32x4v*>(s_in + sbase + static_cast<size_t>(r) * DV + 4 * cg);
+    const f32x4v x = __builtin_nontemporal_load(sp);
+    S[m] = make_float4(x[0], x[1], x[2], x[3]);
+  }
+
+  // Every load and LDS write inside the step loop is unconditional (threads
+  // past the end of an input row take its last element again: same value,
+  // same LDS address; steps past the last fetch the last one again), and the
+  // output store sits under a branch on a scalar, so the compiler can count
+  // which memory operations are still in flight and waits only for the ones
+  // it needs.
+  // Inputs are fetched two steps ahead into two register sets that take
+  // turns (the step loop is unrolled by two so that each set stays in fixed
+  // registers).
+  struct In {
+    float k[EK], q[EK], a[EK], v[EV], b;
+  };
+  auto fetch = [&](In& r, int i) {  // step i's inputs into registers
+    const size_t tok = static_cast<size_t>(i) * B * H + bh;  // (i, b, h) in (Td, B, H)
+#pragma unroll
+    for (int e = 0; e < EK; ++e) {
+      const int x = min(tid + e * NT, DK - 1);
+      r.k[e] = to_f32(k[tok * DK + x]);
+      r.q[e] = to_f32(q[tok * DK + x]);
+      r.a[e] = to_f32(a[tok * DK + x]);
+    }
+#pragma unroll
+    for (int e = 0; e < EV; ++e) r.v[e] = to_f32(v[tok * DV + min(tid + e * NT, DV - 1)]);
+    r.b = to_f32(beta[tok]);
+  };
+  auto stash = [&](const In& r, int buf) {  // registers -> LDS buffer
+#pragma unroll
+    for (int e = 0; e < EK; ++e) {
+      const int x = min(tid + e * NT, DK - 1);
+      const float ex = fast_exp(r.a[e]);
+      s_p[buf][x] = make_float4(ex * r.k[e], ex * r.q[e], r.k[e] * r.q[e], ex);
+      s_u[buf][x] = make_float2(ex, r.b * r.k[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < EV; ++e) s_v[buf][min(tid + e * NT, DV - 1)] = r.v[e];
+    s_beta[buf] = r.b;
+  };
+  auto sync = [&]() {
+    if constexpr (NW > 1) __syncthreads();
+    else wave_sync();
+  };
+
+  In in0, in1;
+  if (n > 0) {
+    fetch(in0, 0);
+    stash(in0, 0);
+    fetch(in1, min(1, n - 1));
+    sync();
+  }
+  int cur = 0;
+  // Step i: reads buffer cur, fetches step i+2 into `load_now`, stashes step
+  // i+1 (held in `pending` since the previous step) into the next buffer.
+  // That buffer was last read in step i-2, which every thread finished
+  // before the previous barrier; the partial sums alternate between two
+  // buffers for the same reason.
+  auto step = [&](int i, In& load_now, const In& pending) {
+    const int nxt = cur == 2 ? 0 : cur + 1;
+    fetch(load_now, min(i + 2, n - 1));
+
+    // Partial sums over this thread's rows.
+    float pk[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f}, kq = 0.f;
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+      const int r = rg + m * RG;
+      const float4 c = s_p[cur][r];
+      const float kr = c.x, qr = c.y;
+      kq += c.z;
+      pk[0] += kr * S[m].x; pk[1] += kr * S[m].y; pk[2] += kr * S[m].z; pk[3] += kr * S[m].w;
+      pq[0] += qr * S[m].x; pq[1] += qr * S[m].y; pq[2] += qr * S[m].z; pq[3] += qr * S[m].w;
+    }
+    // Butterfly over the row groups that share a wave (lanes cg, cg+CG, ...).
+#pragma unroll
+    for (int off = CG; off < kWave; off <<= 1) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        pk[c] += __shfl_xor(pk[c], off);
+        pq[c] += __shfl_xor(pq[c], off);
+      }
+      kq += __shfl_xor(kq, off);
+    }
+    stash(pending, nxt);
+    const int red = i & 1;
+    if constexpr (NW > 1) {
+      // Lanes of one column group hold equal sums after the butterfly; the
+      // lanes of row group 2w (lane < CG) publish them.
+      if (lane < CG) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          s_red[red][wave][lane][c] = pk[c];
+          s_red[red][wave][lane][4 + c] = pq[c];
+        }
+        s_red[red][wave][lane][8] = kq;
+      }
+    }
+    sync();  // partial sums and the next step's inputs are visible
+    if constexpr (NW > 1) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) { pk[c] = 0.f; pq[c] = 0.f; }
+      kq = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          pk[c] += s_red[red][w][cg][c];
+          pq[c] += s_red[red][w][cg][4 + c];
+        }
+        kq += s_red[red][w][cg][8];
+      }
+    }
+
+    const float bt = s_beta[cur];
+    float d[4], out[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      d[c] = s_v[cur][4 * cg + c] - pk[c];
+      out[c] = pq[c] + bt * d[c] * kq;
+    }
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+      const int r = rg + m * RG;
+      const float2 u = s_u[cur][r];
+      const float e = u.x, bk = u.y;
+      S[m].x = e * S[m].x + bk * d[0];
+      S[m].y = e * S[m].y + bk * d[1];
+      S[m].z = e * S[m].z + bk * d[2];
+      S[m].w = e * S[m].w + bk * d[3];
+    }
+    // Wave 0 (a branch on a scalar) stores its column groups' outputs; its
+    // row groups hold equal values, so their duplicate stores carry
+    // identical bits.
+    if (wave == 0) {
+      InT* op = o + (static_cast<size_t>(bh) * o_steps + i) * DV + 4 * cg;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) op[c] = from_f32<InT>(out[c]);
+    }
+    cur = nxt;
+  };
+  int i = 0;
+  for (; i + 1 < n; i += 2) {
+    step(i, in0, in1);
+    step(i + 1, in1, in0);
+  }
+  if (i < n) step(i, in0, in1);
 
   // Rows past the accepted prefix are zero.
   if (rg == 0) {
@@ -230,18 +451,20 @@ template <int DK, int DV, typename InT>
 hipError_t launch_sweep_t(const SweepArgs& p) {
   using Sh = SweepShape<DK, DV>;
   const dim3 grid(static_cast<unsigned>(p.B) * static_cast<unsigned>(p.H));
-  if (p.s_in == p.s_out)
-    hipLaunchKernelGGL((sweep_kernel<DK, DV, InT, true>), grid, dim3(Sh::NT), 0, p.stream, p.s_in,
-                       p.s_out, static_cast<const InT*>(p.q), static_cast<const InT*>(p.k),
-                       static_cast<const InT*>(p.v), static_cast<const InT*>(p.a),
-                       static_cast<const InT*>(p.beta), p.n_accepted, p.t_draft, p.B, p.H,
+  const InT *q = static_cast<const InT*>(p.q), *k = static_cast<const InT*>(p.k);
+  const InT *v = static_cast<const InT*>(p.v), *a = static_cast<const InT*>(p.a);
+  const InT* beta = static_cast<const InT*>(p.beta);
+  if (p.s_in == p.s_out) {
+    // In place is the decode step: one token, every session.
+    if (p.t_draft != 1 || p.n_accepted != nullptr || p.o_steps != 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((decode_kernel<DK, DV, InT>), grid, dim3(Sh::NT), 0, p.stream, p.s_in,
+                       p.s_out, q, k, v, a, beta, p.n_accepted, p.t_draft, p.B, p.H,
                        static_cast<InT*>(p.o), p.o_steps, p.err_flag);
-  else
-    hipLaunchKernelGGL((sweep_kernel<DK, DV, InT, false>), grid, dim3(Sh::NT), 0, p.stream, p.s_in,
-                       p.s_out, static_cast<const InT*>(p.q), static_cast<const InT*>(p.k),
-                       static_cast<const InT*>(p.v), static_cast<const InT*>(p.a),
-                       static_cast<const InT*>(p.beta), p.n_accepted, p.t_draft, p.B, p.H,
+  } else {
+    hipLaunchKernelGGL((replay_kernel<DK, DV, InT>), grid, dim3(Sh::NT), 0, p.stream, p.s_in,
+                       p.s_out, q, k, v, a, beta, p.n_accepted, p.t_draft, p.B, p.H,
                        static_cast<InT*>(p.o), p.o_steps, p.err_flag);
+  }
   return hipGetLastError();
 }
 
