@@ -11,7 +11,8 @@ that step's whole-job throughput in tokens/s with inputs resident in HBM.
 In the same run, and reported under "parts": the single-sequence prefill
 (T=8192, checkpoints every 512), the same sequence as 8 segments through
 segment summaries, composition and per-segment prefill (context-parallel
-prefill on one GPU), 64 in-place decode steps (B=256 sessions),
+prefill on one GPU), the front end (convolution, SiLU, L2Norm, gates) over the
+varlen workload's sequences, 64 in-place decode steps (B=256 sessions),
 verify-and-replay (B=64, H=16, d=32, 8 drafts) and pack/unpack of 16
 checkpoint states, each with its algorithmic bytes or flops against the
 MI355X peaks, plus the float64 CPU oracle timed on a bounded sample.
@@ -68,6 +69,15 @@ def segment_flops(tokens, H, dk, dv, C):
     maps), then for each of the dv columns of B and the dk columns of A:
     Z = V - (k g) S (2 dk), U = T Z (2C) and the state update (2 dk)."""
     return tokens * H * (2 * C * dk + C * C / 3.0 + (dv + dk) * (4 * dk + 2 * C))
+
+
+def front_end_bytes(T, H, dk, dv, K, n_seqs, n_windows_out, in_bytes=2):
+    """Compulsory bytes of the front end: x, z_a, z_b, the weights and the
+    carried windows read once; q, k, v, a, beta and the windows written once."""
+    C = H * (2 * dk + dv)
+    read = T * C + T * H * dk + T * H + C * K + n_seqs * (K - 1) * C
+    write = T * H * (3 * dk + dv + 1) + n_windows_out * (K - 1) * C
+    return (read + write) * in_bytes
 
 
 def decode_bytes(B, H, dk, dv, in_bytes=2):
@@ -270,6 +280,57 @@ def bench_segments(torch, kda, inputs, w, steps, warmup, n_seg=8):
     return res
 
 
+def bench_front_end(torch, kda, inputs, steps, warmup):
+    """The front end over the varlen workload's sequences (16 sequences,
+    108,886 tokens, H=32, dk=dv=128, K=4, bf16), carried windows in, end
+    windows out and the windows of the same checkpoints as the prefill into a
+    window pool.  Inputs are drawn on the device from a seeded generator."""
+    lengths = inputs.prefill_lengths(4)
+    cu = np.zeros(len(lengths) + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(lengths)
+    T, N = int(cu[-1]), len(lengths)
+    H, dk, dv, K = 32, 128, 128, 4
+    C = H * (2 * dk + dv)
+    g = torch.Generator(device="cuda").manual_seed(5)
+    bf = torch.bfloat16
+    rnd = lambda *shape: torch.randn(shape, generator=g, device="cuda", dtype=torch.float32).to(bf)
+    x, z_a, z_b = rnd(T, C), rnd(T, H, dk), rnd(T, H)
+    w = (rnd(C, K).float() * 0.5).to(bf)
+    win = rnd(N, K - 1, C)
+    ck = inputs.prefill_checkpoints(lengths, 4096, True)
+    n_ck = sum(len(c) for c in ck)
+    slots, i = [], 0
+    for c in ck:
+        slots.append(list(range(i, i + len(c))))
+        i += len(c)
+    pool = torch.zeros((n_ck, (K - 1) * C), dtype=bf, device="cuda")
+    out = {"q": torch.empty((T, H, dk), dtype=bf, device="cuda"),
+           "k": torch.empty((T, H, dk), dtype=bf, device="cuda"),
+           "v": torch.empty((T, H, dv), dtype=bf, device="cuda"),
+           "a": torch.empty((T, H, dk), dtype=bf, device="cuda"),
+           "beta": torch.empty((T, H), dtype=bf, device="cuda"),
+           "window": torch.empty((N, K - 1, C), dtype=bf, device="cuda")}
+    ws = torch.empty(kda.front_end_workspace_size(N, T, n_ck), dtype=torch.uint8, device="cuda")
+
+    def step(ev):
+        if ev is not None:
+            ev[0].record()
+        kda.front_end(x, z_a, z_b, w, H, dk, dv, -1.0, cu, win_in=win, checkpoints=ck,
+                      ckpt_slots=slots, conv_pool=pool, out=out, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+
+    ms, kms = run_steps(torch, step, steps, warmup)
+    byts = front_end_bytes(T, H, dk, dv, K, N, N + n_ck)
+    res = {"workload": f"front end: 16 seqs ({T} tokens, the varlen prefill's lengths), H=32, "
+                       f"dk=dv=128, K=4, bf16, windows carried in and out, {n_ck} checkpoint windows",
+           "tokens": T, "ms_per_step": ms, "kernel_ms": kms, "tokens_per_s": T / (kms * 1e-3),
+           "algo_gbytes": byts / 1e9, "hbm_gbs": byts / (kms * 1e-3) / 1e9,
+           "hbm_frac": byts / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    del x, z_a, z_b, w, win, pool, out, ws
+    return res
+
+
 def bench_decode(torch, kda, inputs, steps, warmup):
     B, H, dk, dv, n_tok = 256, 32, 128, 128, 64
     state = torch.from_numpy(inputs.decode_state(2, B, H, dk, dv, 0.05)).cuda()
@@ -437,8 +498,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--only", default="", help="comma list of: prefill4, prefill3, segments, decode, "
-                                               "replay, replay_big, pack, copycal")
+    ap.add_argument("--only", default="", help="comma list of: prefill4, prefill3, segments, front_end, "
+                                               "decode, replay, replay_big, pack, copycal")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--json-out", default="")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -483,6 +544,9 @@ def main():
         log("segments (context-parallel prefill on one GPU) ...")
         parts["segments"] = bench_segments(torch, kda, inputs, inputs.workload3(), args.steps,
                                            args.warmup)
+    if want("front_end"):
+        log("front end ...")
+        parts["front_end"] = bench_front_end(torch, kda, inputs, args.steps, args.warmup)
     if want("decode"):
         log("decode ...")
         parts["decode"] = bench_decode(torch, kda, inputs, args.steps, args.warmup)

@@ -256,6 +256,66 @@ int kda_compose_segments(const float* A, const float* B, int32_t n_seg, int32_t 
                          int32_t dv, const float* s_in, float* s_starts, float* s_end,
                          void* stream);
 
+/*
+ * The front end: from a layer's projections to the recurrence inputs, and the
+ * convolution window a checkpoint keeps next to the recurrent state
+ * ([KDA cache] "KDA 的递推与充分状态": projection, causal short convolution,
+ * activation, then L2Norm of Q and K, so the recurrent matrix alone cannot
+ * continue the next token; its checkpoint section: the convolution checkpoint
+ * is the last kernel_size - 1 rows of mixed_qkv before the boundary;
+ * [Serve demo] §1.3: a = g_min * sigmoid(.), beta = sigmoid(.)).  Readings:
+ *   - mixed rows x hold, per token, the q channels of all heads, then the k
+ *     channels, then the v channels: C = H*(2*dk + dv), head-major in a part;
+ *   - the convolution is depthwise and causal, kernel size K (1..4), weights
+ *     conv_w [C, K] with conv_w[c][K-1] on the current token, no bias:
+ *       u[t][c] = sum_j conv_w[c][j] * x[t-(K-1)+j][c];
+ *   - then SiLU, u * sigmoid(u), on all parts;
+ *   - q and k are divided per (token, head) by sqrt(sum over dk of u^2 + 1e-6);
+ *   - a = g_min * sigmoid(z_a) per key channel, beta = sigmoid(z_b) per head.
+ * A window is [K-1, C]: the K-1 raw rows before a boundary, oldest first,
+ * in dtype (rows before a fresh sequence are zero).  Arithmetic is fp32;
+ * outputs are rounded to dtype.
+ *
+ * kda_front_end — token-packed sequences.
+ *   x : [T_tot, C]   z_a : [T_tot, H, dk]   z_b : [T_tot, H]   conv_w : [C, K]
+ *   cu_seqlens_host : host int32 [n_seqs + 1] as for kda_chunk_prefill
+ *   win_in  : [n_seqs, K-1, C] windows carried into the sequences, or NULL (zero)
+ *   win_out : [n_seqs, K-1, C] the window after each sequence, or NULL
+ *   checkpoints (ckpt_cu/pos/slot as for kda_chunk_prefill): the window
+ *     after p tokens goes into slot ckpt_slot of conv_pool [n_slots,
+ *     conv_elems] (dtype), conv_elems >= (K-1)*C, the rest of the slot zero;
+ *     the same slot index as the state's page keeps the two halves of one
+ *     checkpoint together
+ *   q, k, a : [T_tot, H, dk]   v : [T_tot, H, dv]   beta : [T_tot, H]  (dtype)
+ *   workspace : kda_front_end_workspace_size bytes, 16-byte aligned
+ * x, z_a, win_in, q, k, v, a 16-byte aligned (rows move in 16-byte pieces).
+ * Outputs must not overlap the inputs or each other (KDA_EALIAS).
+ */
+int kda_front_end_workspace_size(int32_t n_seqs, int64_t total_tokens, int64_t n_ckpt,
+                                 size_t* bytes);
+
+int kda_front_end(const void* x, const void* z_a, const void* z_b, const void* conv_w,
+                  kda_dtype dtype, int32_t H, int32_t dk, int32_t dv, int32_t K, float g_min,
+                  const int32_t* cu_seqlens_host, int32_t n_seqs, const void* win_in,
+                  void* win_out, const int32_t* ckpt_cu_host, const int32_t* ckpt_pos_host,
+                  const int32_t* ckpt_slot_host, int64_t n_ckpt, void* conv_pool,
+                  int64_t conv_elems, int64_t n_slots, void* q, void* k, void* v, void* a,
+                  void* beta, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kda_front_end_step — one decode token per session, the window updated IN
+ * PLACE (it supplies the K-1 rows before the token and comes back shifted by
+ * one row, the token's raw row last).  x, z_a, window, q, k, v, a 16-byte
+ * aligned.
+ *   x : [B, C]   z_a : [B, H, dk]   z_b : [B, H]   conv_w : [C, K]
+ *   window : [B, K-1, C] (dtype), read and overwritten (may be NULL when K = 1)
+ *   q, k, a : [B, H, dk]   v : [B, H, dv]   beta : [B, H]
+ */
+int kda_front_end_step(const void* x, const void* z_a, const void* z_b, const void* conv_w,
+                       kda_dtype dtype, int32_t B, int32_t H, int32_t dk, int32_t dv, int32_t K,
+                       float g_min, void* window, void* q, void* k, void* v, void* a, void* beta,
+                       void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -96,4 +96,33 @@ struct ComposeArgs {
 };
 hipError_t launch_compose(const ComposeArgs& p);
 
+// Front end (convolution, SiLU, L2Norm, gates).  Prefill: one unit per tile
+// [n_tiles][4] = (sequence, first token, tokens, the sequence's first token),
+// carried windows win_in [N][K-1][C] or null.  Step: one unit per session,
+// x [B][C], the window win_in [B][K-1][C] read and written back to win_step.
+struct FrontParams {
+  const void *x, *z_a, *z_b, *w, *win_in;
+  void* win_step;
+  void *q, *k, *v, *a, *beta;
+  const int32_t* tiles;
+  float g_min;
+  int H, dk, dv, K, C;
+  bool bf16;
+  hipStream_t stream;
+};
+hipError_t launch_front(const FrontParams& p, int units, bool step);
+
+// Convolution windows at boundaries [n_bnd][4] = (sequence, token count p,
+// pool slot or -1 for win_out, the sequence's first token).
+struct WindowParams {
+  const void *x, *win_in;
+  void *win_out, *pool;
+  int64_t pool_elems;
+  const int32_t* bnd;
+  int n_bnd, K, C;
+  bool bf16;
+  hipStream_t stream;
+};
+hipError_t launch_windows(const WindowParams& p);
+
 }  // namespace kda

@@ -15,6 +15,10 @@ descriptions'):
   per key channel (the bounded log-decay in [g_min, 0] of the
   "【轻量化复刻大模型 / KIMI K3】Serve 模块交互式演示" page, §1.3);
   beta = sigmoid(z'), z' ~ N(0, 1), in [0, 1] (same section).
+
+Front-end inputs (the layer's side of the recurrence): mixed q|k|v
+projection rows x ~ N(0, 1), gate logits z_a, z_b ~ N(0, 1), depthwise
+convolution weights ~ N(0, 0.5^2), carried convolution windows ~ N(0, 1).
 """
 
 import concurrent.futures as cf
@@ -24,7 +28,7 @@ import os
 import numpy as np
 
 # Field ids of the seed key.
-_Q, _K, _V, _ZA, _ZB, _S0, _NACC, _LEN = range(8)
+_Q, _K, _V, _ZA, _ZB, _S0, _NACC, _LEN, _MIX, _GA, _GB, _CW, _WIN = range(13)
 
 WORKLOADS = {
     0: "tiny recurrence: 1 seq, H=2, dk=dv=16, T=128, fp32, S0=0, chunk 16",
@@ -196,3 +200,24 @@ def decode_state(wid=2, B=256, H=32, dk=128, dv=128, std=0.05):
 
 def decode_step_inputs(step, wid=2, B=256, H=32, dk=128, dv=128, dtype="bf16"):
     return token_inputs(wid, step, (B,), H, dk, dv, dtype)
+
+
+def front_end_inputs(wid, lengths, H, dk, dv, K, dtype, windows=True):
+    """Front-end inputs of a token-packed batch: x [T, H*(2dk+dv)] mixed
+    projection rows, z_a [T, H, dk], z_b [T, H], conv_w [C, K] and, with
+    windows=True, carried windows [N, K-1, C] (None otherwise)."""
+    cu = np.zeros(len(lengths) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lengths)
+    T = int(cu[-1])
+    C = H * (2 * dk + dv)
+
+    def draw(field, shape, scale=1.0, block=0):
+        x = _rng(wid, field, block).standard_normal(size=shape, dtype=np.float32)
+        if scale != 1.0:
+            x *= np.float32(scale)
+        return round_to_bf16(x, inplace=True) if dtype == "bf16" else x
+
+    return {"x": draw(_MIX, (T, C)), "z_a": draw(_GA, (T, H, dk)), "z_b": draw(_GB, (T, H)),
+            "conv_w": draw(_CW, (C, K), 0.5),
+            "windows": draw(_WIN, (len(lengths), K - 1, C)) if windows else None,
+            "cu_seqlens": cu}

@@ -47,6 +47,12 @@ SIGNATURES = {
     "kda_segment_summary": (ctypes.c_int, [_vp, _vp, _vp, _vp, ctypes.c_int, _i32, _i32, _i32, _i32,
                                            _i32p, _i32, _vp, _vp, _vp, _sz, _vp]),
     "kda_compose_segments": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "kda_front_end_workspace_size": (ctypes.c_int, [_i32, _i64, _i64, ctypes.POINTER(_sz)]),
+    "kda_front_end": (ctypes.c_int, [_vp, _vp, _vp, _vp, ctypes.c_int, _i32, _i32, _i32, _i32,
+                                     ctypes.c_float, _i32p, _i32, _vp, _vp, _i32p, _i32p, _i32p, _i64,
+                                     _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "kda_front_end_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, ctypes.c_int, _i32, _i32, _i32, _i32,
+                                          _i32, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
 }
 
 _lib = None
@@ -333,3 +339,84 @@ def compose_segments(A, B, s_in=None, starts=None, s_end=None):
     _check(lib().kda_compose_segments(_ptr(A), _ptr(B), n, H, dk, dv, _ptr(s_in), _ptr(starts),
                                       _ptr(s_end), _stream(dev)))
     return starts, s_end
+
+
+def front_end_workspace_size(n_seqs, total_tokens, n_ckpt=0):
+    out = ctypes.c_size_t(0)
+    _check(lib().kda_front_end_workspace_size(n_seqs, total_tokens, n_ckpt, ctypes.byref(out)))
+    return out.value
+
+
+def front_end(x, z_a, z_b, conv_w, H, dk, dv, g_min, cu_seqlens, win_in=None, want_window=True,
+              checkpoints=None, ckpt_slots=None, conv_pool=None, out=None, workspace=None):
+    """Front end of token-packed sequences: causal ShortConv, SiLU, L2Norm of
+    q and k, gates.  x [T, H*(2dk+dv)], z_a [T,H,dk], z_b [T,H], conv_w [C,K]
+    (one dtype, float32 or bfloat16); win_in [N,K-1,C] or None.
+    Returns a dict with q, k, v, a, beta and "window" [N,K-1,C] (or None)."""
+    T, C = x.shape
+    K = conv_w.shape[1]
+    dev, dt = x.device, x.dtype
+    for t, shp, nm in ((x, (T, C), "x"), (z_a, (T, H, dk), "z_a"), (z_b, (T, H), "z_b"),
+                       (conv_w, (C, K), "conv_w")):
+        _expect(t, shp, dt, nm, dev)
+    cu = [int(c) for c in cu_seqlens]
+    N = len(cu) - 1
+    if win_in is not None:
+        _expect(win_in, (N, K - 1, C), dt, "win_in", dev)
+    o = dict(out or {})
+    for nm, shp in (("q", (T, H, dk)), ("k", (T, H, dk)), ("v", (T, H, dv)), ("a", (T, H, dk)),
+                    ("beta", (T, H))):
+        if o.get(nm) is None:
+            o[nm] = torch.empty(shp, dtype=dt, device=dev)
+        _expect(o[nm], shp, dt, nm, dev)
+    if want_window and o.get("window") is None:
+        o["window"] = torch.empty((N, K - 1, C), dtype=dt, device=dev)
+    win_out = o.get("window") if want_window else None
+    ck_cu, ck_pos, ck_slot = [0] * (N + 1), [], []
+    if checkpoints is not None:
+        if ckpt_slots is None or conv_pool is None:
+            raise ValueError("checkpoints need ckpt_slots and conv_pool")
+        ck_cu = [0]
+        for pos, sl in zip(checkpoints, ckpt_slots):
+            if len(pos) != len(sl):
+                raise ValueError("each sequence needs one slot per checkpoint")
+            ck_pos += list(pos)
+            ck_slot += list(sl)
+            ck_cu.append(len(ck_pos))
+    n_ck = len(ck_pos)
+    n_slots, conv_elems = (0, 0) if conv_pool is None else conv_pool.shape
+    need = front_end_workspace_size(N, T, n_ck)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _check(lib().kda_front_end(_ptr(x), _ptr(z_a), _ptr(z_b), _ptr(conv_w), _dtype_code(x), H, dk,
+                               dv, K, float(g_min), _i32_array(cu), N, _ptr(win_in), _ptr(win_out),
+                               _i32_array(ck_cu), _i32_array(ck_pos), _i32_array(ck_slot), n_ck,
+                               _ptr(conv_pool), conv_elems, n_slots, _ptr(o["q"]), _ptr(o["k"]),
+                               _ptr(o["v"]), _ptr(o["a"]), _ptr(o["beta"]), _ptr(workspace),
+                               workspace.numel(), _stream(dev)))
+    o["window"] = win_out
+    return o
+
+
+def front_end_step(x, z_a, z_b, conv_w, H, dk, dv, g_min, window, out=None):
+    """One decode token per session; window [B,K-1,C] is shifted in place.
+    Returns a dict with q, k, v, a, beta of shape (B, H, *)."""
+    B, C = x.shape
+    K = conv_w.shape[1]
+    dev, dt = x.device, x.dtype
+    for t, shp, nm in ((x, (B, C), "x"), (z_a, (B, H, dk), "z_a"), (z_b, (B, H), "z_b"),
+                       (conv_w, (C, K), "conv_w")):
+        _expect(t, shp, dt, nm, dev)
+    if window is not None:
+        _expect(window, (B, K - 1, C), dt, "window", dev)
+    o = dict(out or {})
+    for nm, shp in (("q", (B, H, dk)), ("k", (B, H, dk)), ("v", (B, H, dv)), ("a", (B, H, dk)),
+                    ("beta", (B, H))):
+        if o.get(nm) is None:
+            o[nm] = torch.empty(shp, dtype=dt, device=dev)
+        _expect(o[nm], shp, dt, nm, dev)
+    _check(lib().kda_front_end_step(_ptr(x), _ptr(z_a), _ptr(z_b), _ptr(conv_w), _dtype_code(x), B,
+                                    H, dk, dv, K, float(g_min), _ptr(window), _ptr(o["q"]),
+                                    _ptr(o["k"]), _ptr(o["v"]), _ptr(o["a"]), _ptr(o["beta"]),
+                                    _stream(dev)))
+    return o

@@ -172,3 +172,50 @@ def test_segment_validation(L):
     assert comp(st_ptr=P(B.value + 128)) == kda.KDA_EALIAS               # starts overlap B
     assert comp(end_ptr=P(st.value + 4)) == kda.KDA_EALIAS               # end overlaps starts
     assert comp(n=0, end_ptr=None) == kda.KDA_OK                         # nothing to do
+
+
+def test_front_end_validation(L):
+    """Argument checks of the front end and its decode step."""
+    x, za, zb, w, q, k, v, a, b, ws = (_fake(i) for i in range(10))
+    I32 = ctypes.c_int32
+    F = ctypes.c_float
+
+    def fe(dtype=1, H=2, dk=64, dv=64, K=4, g=-1.0, cu=(0, 40, 100), win_in=None, win_out=None,
+           x_ptr=x, q_ptr=q, ws_ptr=ws, ck=None, conv_elems=0, n_slots=0):
+        cu_a = (I32 * len(cu))(*cu)
+        n = len(cu) - 1
+        ck_cu = ck_pos = ck_slot = None
+        n_ck = 0
+        if ck is not None:
+            pos, slot, cuv = [], [], [0]
+            for p_s in ck:
+                pos += [p for p, _ in p_s]
+                slot += [s for _, s in p_s]
+                cuv.append(len(pos))
+            n_ck = len(pos)
+            ck_cu, ck_pos, ck_slot = ((I32 * max(len(z), 1))(*z) for z in (cuv, pos, slot))
+        pool = _fake(11) if ck is not None else None
+        return L.kda_front_end(x_ptr, za, zb, w, dtype, H, dk, dv, K, F(g), cu_a, n, win_in, win_out,
+                               ck_cu, ck_pos, ck_slot, n_ck, pool, conv_elems, n_slots, q_ptr, k, v,
+                               a, b, ws_ptr, 1 << 20, None)
+
+    assert fe(dk=24) == kda.KDA_EUNSUPPORTED
+    assert fe(K=5) == kda.KDA_EUNSUPPORTED and fe(K=0) == kda.KDA_EUNSUPPORTED
+    assert fe(g=0.5) == kda.KDA_EINVAL and fe(g=float("nan")) == kda.KDA_EINVAL
+    assert fe(cu=(0, 40, 30)) == kda.KDA_EINVAL
+    assert fe(x_ptr=P(x.value + 2)) == kda.KDA_EINVAL                     # two-element alignment
+    assert fe(ws_ptr=P(ws.value + 8)) == kda.KDA_EINVAL                   # 16-byte workspace
+    assert fe(q_ptr=P(x.value + 64)) == kda.KDA_EALIAS                    # q overlaps x
+    assert fe(ck=[[(41, 0)], []], conv_elems=3 * 2 * 192, n_slots=2) == kda.KDA_EINVAL
+    assert fe(ck=[[(20, 0)], [(5, 0)]], conv_elems=3 * 2 * 192, n_slots=2) == kda.KDA_EINVAL
+    assert fe(ck=[[(20, 0)], []], conv_elems=10, n_slots=2) == kda.KDA_EINVAL   # slot too small
+    sz = ctypes.c_size_t(0)
+    assert L.kda_front_end_workspace_size(2, 100, 3, ctypes.byref(sz)) == 0 and sz.value > 0
+
+    def step(K=4, window=_fake(12), B=3, g=-1.0):
+        return L.kda_front_end_step(x, za, zb, w, 1, B, 2, 64, 64, K, F(g), window, q, k, v, a, b, None)
+
+    assert step(window=None) == kda.KDA_EINVAL          # K > 1 needs a window
+    assert step(B=-1) == kda.KDA_EINVAL
+    assert step(B=0) == kda.KDA_OK
+    assert step(window=P(x.value + 8)) == kda.KDA_EALIAS
