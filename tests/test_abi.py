@@ -203,7 +203,7 @@ def test_front_end_validation(L):
     assert fe(K=5) == kda.KDA_EUNSUPPORTED and fe(K=0) == kda.KDA_EUNSUPPORTED
     assert fe(g=0.5) == kda.KDA_EINVAL and fe(g=float("nan")) == kda.KDA_EINVAL
     assert fe(cu=(0, 40, 30)) == kda.KDA_EINVAL
-    assert fe(x_ptr=P(x.value + 2)) == kda.KDA_EINVAL                     # two-element alignment
+    assert fe(x_ptr=P(x.value + 8)) == kda.KDA_EINVAL                     # 16-byte alignment
     assert fe(ws_ptr=P(ws.value + 8)) == kda.KDA_EINVAL                   # 16-byte workspace
     assert fe(q_ptr=P(x.value + 64)) == kda.KDA_EALIAS                    # q overlaps x
     assert fe(ck=[[(41, 0)], []], conv_elems=3 * 2 * 192, n_slots=2) == kda.KDA_EINVAL
@@ -218,4 +218,5 @@ def test_front_end_validation(L):
     assert step(window=None) == kda.KDA_EINVAL          # K > 1 needs a window
     assert step(B=-1) == kda.KDA_EINVAL
     assert step(B=0) == kda.KDA_OK
-    assert step(window=P(x.value + 8)) == kda.KDA_EALIAS
+    assert step(window=P(x.value + 8)) == kda.KDA_EINVAL            # 16-byte alignment
+    assert step(window=P(x.value + 64)) == kda.KDA_EALIAS
