@@ -13,7 +13,9 @@ In the same run, and reported under "parts": the single-sequence prefill
 segment summaries, composition and per-segment prefill (context-parallel
 prefill on one GPU), the front end (convolution, SiLU, L2Norm, gates) over the
 varlen workload's sequences, 64 in-place decode steps (B=256 sessions),
-verify-and-replay (B=64, H=16, d=32, 8 drafts) and pack/unpack of 16
+verify-and-replay (B=64, H=16, d=32, 8 drafts), one speculative round's
+rollback through the raw-input ring against full state snapshots, and
+pack/unpack of 16
 checkpoint states, each with its algorithmic bytes or flops against the
 MI355X peaks, plus the float64 CPU oracle timed on a bounded sample.
 
@@ -331,6 +333,75 @@ def bench_front_end(torch, kda, inputs, steps, warmup):
     return res
 
 
+def bench_ring(torch, kda, inputs, steps, warmup):
+    """Rollback machinery of one speculative round at the large replay shape
+    (B=256, H=32, dk=dv=128, 8 draft steps, bf16 inputs, fp32 states, ragged
+    acceptance).  Route B, the raw-input ring: one push per draft step, then
+    window, verify-and-replay of the accepted prefix and reset.  Route A, full
+    snapshots: the state packed into a snapshot slot after every draft step,
+    then the accepted one unpacked.  The verification forward that produces
+    the per-step states is the same for both and is not part of either."""
+    w = inputs.replay_workload(wid=11, B=256, H=32, dk=128, dv=128, t_draft=8, dtype="bf16")
+    Td, B, H, dk = w["q"].shape
+    dv = w["v"].shape[-1]
+    bf = torch.bfloat16
+    d = {f: torch.from_numpy(w[f]).to(bf).cuda() for f in ("q", "k", "v", "a", "beta")}
+    steps_in = [{f: d[f][t].contiguous() for f in d} for t in range(Td)]
+    committed = torch.from_numpy(w["committed"]).cuda()
+    n = torch.from_numpy(w["n_accepted"]).cuda()
+    slots = torch.arange(B, dtype=torch.int32, device="cuda")
+    ring = kda.RawInputRing(B, Td, H, dk, dv, bf)
+    win = {f: torch.empty((Td,) + tuple(d[f].shape[1:]), dtype=bf, device="cuda") for f in d}
+    win["n_valid"] = torch.empty(B, dtype=torch.int32, device="cuda")
+    s_new = torch.empty_like(committed)
+    o = torch.empty((B, H, Td, dv), dtype=bf, device="cuda")
+
+    def route_b(ev):
+        if ev is not None:
+            ev[0].record()
+        for st in steps_in:
+            ring.push(slots, st["q"], st["k"], st["v"], st["a"], st["beta"])
+        ring.window(slots, out=win)
+        kda.verify_and_replay(committed, win["q"], win["k"], win["v"], win["a"], win["beta"], n,
+                              s_new, o)
+        ring.reset(slots)
+        if ev is not None:
+            ev[1].record()
+
+    page = H * dk * dv
+    pool = torch.empty((B * Td, page), dtype=torch.float32, device="cuda")
+    snap_slots = [torch.arange(B, dtype=torch.int32, device="cuda") * Td + t for t in range(Td)]
+    keep = (torch.arange(B, device="cuda") * Td + (n.long() - 1).clamp(min=0)).to(torch.int32)
+    restored = torch.empty_like(committed)
+
+    def route_a(ev):
+        if ev is not None:
+            ev[0].record()
+        for t in range(Td):
+            kda.pack_heads(committed, snap_slots[t], pool)  # the state after step t (same bytes)
+        kda.unpack_heads(pool, keep, H, dk, dv, state=restored)
+        if ev is not None:
+            ev[1].record()
+
+    _, ms_b = run_steps(torch, route_b, steps, warmup)
+    _, ms_a = run_steps(torch, route_a, steps, warmup)
+    n_sum = int(np.sum(w["n_accepted"]))
+    proj = B * H * (3 * dk + dv + 1) * 2       # one step's raw inputs, bf16
+    state = B * H * dk * dv * 4                # all sessions' states, fp32
+    bytes_b = Td * 2 * proj + 2 * Td * proj + replay_bytes(B, H, dk, dv, Td, w["n_accepted"], 2)
+    bytes_a = Td * 2 * state + 2 * state
+    res = {"workload": "speculative round: B=256, H=32, dk=dv=128, 8 draft steps, bf16 inputs, "
+                       f"fp32 states, {n_sum} accepted steps in all",
+           "route_b_ring_ms": ms_b, "route_a_snapshot_ms": ms_a, "time_ratio_a_over_b": ms_a / ms_b,
+           "route_b_gbytes": bytes_b / 1e9, "route_a_gbytes": bytes_a / 1e9,
+           "bytes_ratio_a_over_b": bytes_a / bytes_b,
+           "per_step_bytes_ratio": kda.snapshot_cost_ratio(H, dk, dv) * 4 / 2,
+           "route_b_hbm_gbs": bytes_b / (ms_b * 1e-3) / 1e9,
+           "route_a_hbm_gbs": bytes_a / (ms_a * 1e-3) / 1e9}
+    del d, steps_in, committed, ring, win, s_new, o, pool, restored
+    return res
+
+
 def bench_decode(torch, kda, inputs, steps, warmup):
     B, H, dk, dv, n_tok = 256, 32, 128, 128, 64
     state = torch.from_numpy(inputs.decode_state(2, B, H, dk, dv, 0.05)).cuda()
@@ -499,7 +570,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", default="", help="comma list of: prefill4, prefill3, segments, front_end, "
-                                               "decode, replay, replay_big, pack, copycal")
+                                               "decode, replay, replay_big, ring, pack, copycal")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--json-out", default="")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -556,6 +627,9 @@ def main():
     if want("replay_big"):
         log("replay (large) ...")
         parts["replay_large"] = bench_replay(torch, kda, inputs, args.steps, args.warmup, "big")
+    if want("ring"):
+        log("raw-input ring vs snapshots ...")
+        parts["ring"] = bench_ring(torch, kda, inputs, args.steps, args.warmup)
     if want("pack"):
         log("pack ...")
         parts["pack"] = bench_pack(torch, kda, args.steps, args.warmup)

@@ -316,6 +316,55 @@ int kda_front_end_step(const void* x, const void* z_a, const void* z_b, const vo
                        float g_min, void* window, void* q, void* k, void* v, void* a, void* beta,
                        void* stream);
 
+/*
+ * The raw-input ring ([Serve demo] Tab 4 "ReplaySSM", §7.1-7.3: during
+ * verification each draft step's raw inputs (q, k, v, g, beta) are written,
+ * as they arrive, into a per-slot ring window; once full a push overwrites
+ * the oldest entry; window() returns the held entries oldest first in the
+ * draft-projection layout (draft, B, H, D), row i the i-th entry; commit
+ * replays the accepted prefix with kda_verify_and_replay, the same engine as
+ * the batch path, and the ring starts over (kda_ring_reset)).  Rollback by
+ * full state snapshots (route A of [Serve demo] §1.1) needs no new call: it is
+ * kda_pack_heads of the state after every step and kda_unpack_heads of the
+ * accepted one.
+ *
+ * A ring is caller-owned device memory described by kda_ring:
+ *   q, k, a : [n_slots, capacity, H, dk]   v : [n_slots, capacity, H, dv]
+ *   beta    : [n_slots, capacity, H]      (dtype; each 16-byte aligned)
+ *   count   : int32 [n_slots], pushes since the last reset (zero it once
+ *             when the ring is created)
+ * Slot values live on the device: out-of-range slots are skipped and raise
+ * *err_flag (when not NULL).  The slots of one call must be distinct.
+ */
+#define KDA_RING_MAX_CAPACITY 1024
+
+typedef struct {
+  void *q, *k, *v, *a, *beta;
+  int32_t* count;
+  int64_t n_slots;
+  int32_t capacity, H, dk, dv;
+  kda_dtype dtype;
+} kda_ring;
+
+/* kda_ring_push — append one draft step: entry b (q, k, a [B, H, dk],
+ * v [B, H, dv], beta [B, H], 16-byte aligned, ring dtype) goes to slot slot[b]
+ * at position count % capacity, then count[slot[b]] += 1. */
+int kda_ring_push(const kda_ring* ring, const int32_t* slot, int32_t B, const void* q,
+                  const void* k, const void* v, const void* a, const void* beta,
+                  int32_t* err_flag, void* stream);
+
+/* kda_ring_window — the windows of B slots, oldest first: q, k, a
+ * [capacity, B, H, dk], v [capacity, B, H, dv], beta [capacity, B, H]
+ * (16-byte aligned); rows past the held entries are zero; n_valid [B] (may be
+ * NULL) receives min(count, capacity). */
+int kda_ring_window(const kda_ring* ring, const int32_t* slot, int32_t B, void* q, void* k,
+                    void* v, void* a, void* beta, int32_t* n_valid, int32_t* err_flag,
+                    void* stream);
+
+/* kda_ring_reset — empty the rings of B slots (count = 0). */
+int kda_ring_reset(const kda_ring* ring, const int32_t* slot, int32_t B, int32_t* err_flag,
+                   void* stream);
+
 #ifdef __cplusplus
 }
 #endif

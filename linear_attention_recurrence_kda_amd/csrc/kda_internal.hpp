@@ -125,4 +125,24 @@ struct WindowParams {
 };
 hipError_t launch_windows(const WindowParams& p);
 
+// Raw-input rings: field f in (q, k, v, a, beta) is [n_slots][capacity][elems[f]]
+// in elements of es bytes; count [n_slots].
+struct RingArgs {
+  void* field[5];
+  int64_t elems[5];
+  int32_t* count;
+  int64_t n_slots;
+  int capacity, es;
+  int32_t* err_flag;
+  hipStream_t stream;
+};
+// One step's inputs [B][elems[f]] (push) or the window [capacity][B][elems[f]].
+struct RingStep {
+  void* field[5];
+};
+hipError_t launch_ring_push(const RingArgs& r, const int32_t* slot, int B, const RingStep& in);
+hipError_t launch_ring_window(const RingArgs& r, const int32_t* slot, int B, const RingStep& out,
+                              int32_t* n_valid);
+hipError_t launch_ring_reset(const RingArgs& r, const int32_t* slot, int B);
+
 }  // namespace kda

@@ -22,6 +22,15 @@ _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c
 _i32p = ctypes.POINTER(ctypes.c_int32)
 
 # name -> (restype, argtypes); mirrors include/kda.h
+class KdaRing(ctypes.Structure):
+    """The kda_ring description of include/kda.h."""
+    _fields_ = [("q", _vp), ("k", _vp), ("v", _vp), ("a", _vp), ("beta", _vp), ("count", _vp),
+                ("n_slots", _i64), ("capacity", _i32), ("H", _i32), ("dk", _i32), ("dv", _i32),
+                ("dtype", ctypes.c_int)]
+
+
+_ringp = ctypes.POINTER(KdaRing)
+
 SIGNATURES = {
     "kda_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "kda_last_error": (ctypes.c_char_p, []),
@@ -53,6 +62,9 @@ SIGNATURES = {
                                      _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "kda_front_end_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, ctypes.c_int, _i32, _i32, _i32, _i32,
                                           _i32, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "kda_ring_push": (ctypes.c_int, [_ringp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "kda_ring_window": (ctypes.c_int, [_ringp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "kda_ring_reset": (ctypes.c_int, [_ringp, _vp, _i32, _vp, _vp]),
 }
 
 _lib = None
@@ -420,3 +432,53 @@ def front_end_step(x, z_a, z_b, conv_w, H, dk, dv, g_min, window, out=None):
                                     _ptr(o["k"]), _ptr(o["v"]), _ptr(o["a"]), _ptr(o["beta"]),
                                     _stream(dev)))
     return o
+
+
+class RawInputRing:
+    """Per-slot rings of raw draft inputs on the device (kda_ring_*): push one
+    step for a batch of slots, window() oldest first in the (draft, B, H, D)
+    layout verify_and_replay reads, reset at commit."""
+
+    FIELDS = ("q", "k", "v", "a", "beta")
+
+    def __init__(self, n_slots, capacity, H, dk, dv, dtype=torch.bfloat16, device="cuda"):
+        self.n_slots, self.capacity, self.H, self.dk, self.dv = n_slots, capacity, H, dk, dv
+        self.dtype, self.device = dtype, torch.device(device)
+        shp = {"q": (H, dk), "k": (H, dk), "v": (H, dv), "a": (H, dk), "beta": (H,)}
+        self.shapes = shp
+        self.t = {f: torch.zeros((n_slots, capacity) + shp[f], dtype=dtype, device=self.device)
+                  for f in self.FIELDS}
+        self.count = torch.zeros(n_slots, dtype=torch.int32, device=self.device)
+        self.device = self.count.device  # the concrete device ("cuda" -> "cuda:0")
+        self.desc = KdaRing(*(t.data_ptr() for t in (self.t[f] for f in self.FIELDS)),
+                            self.count.data_ptr(), n_slots, capacity, H, dk, dv,
+                            _dtype_code(self.t["q"]))
+
+    def push(self, slots, q, k, v, a, beta, err_flag=None):
+        B = slots.numel()
+        for t, f in zip((q, k, v, a, beta), self.FIELDS):
+            _expect(t, (B,) + self.shapes[f], self.dtype, f, self.device)
+        _expect(slots, (B,), torch.int32, "slots", self.device)
+        _check(lib().kda_ring_push(ctypes.byref(self.desc), _ptr(slots), B, _ptr(q), _ptr(k), _ptr(v),
+                                   _ptr(a), _ptr(beta), _ptr(err_flag), _stream(self.device)))
+
+    def window(self, slots, out=None, err_flag=None):
+        B = slots.numel()
+        _expect(slots, (B,), torch.int32, "slots", self.device)
+        o = dict(out or {})
+        for f in self.FIELDS:
+            shp = (self.capacity, B) + self.shapes[f]
+            if o.get(f) is None:
+                o[f] = torch.empty(shp, dtype=self.dtype, device=self.device)
+            _expect(o[f], shp, self.dtype, f, self.device)
+        if o.get("n_valid") is None:
+            o["n_valid"] = torch.empty(B, dtype=torch.int32, device=self.device)
+        _check(lib().kda_ring_window(ctypes.byref(self.desc), _ptr(slots), B, _ptr(o["q"]), _ptr(o["k"]),
+                                     _ptr(o["v"]), _ptr(o["a"]), _ptr(o["beta"]), _ptr(o["n_valid"]),
+                                     _ptr(err_flag), _stream(self.device)))
+        return o
+
+    def reset(self, slots, err_flag=None):
+        _expect(slots, (slots.numel(),), torch.int32, "slots", self.device)
+        _check(lib().kda_ring_reset(ctypes.byref(self.desc), _ptr(slots), slots.numel(), _ptr(err_flag),
+                                    _stream(self.device)))

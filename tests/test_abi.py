@@ -220,3 +220,33 @@ def test_front_end_validation(L):
     assert step(B=0) == kda.KDA_OK
     assert step(window=P(x.value + 8)) == kda.KDA_EINVAL            # 16-byte alignment
     assert step(window=P(x.value + 64)) == kda.KDA_EALIAS
+
+
+def test_ring_validation(L):
+    """Argument checks of the raw-input ring."""
+    base = [_fake(i) for i in range(6)]
+
+    def ring(**kw):
+        args = dict(q=base[0].value, k=base[1].value, v=base[2].value, a=base[3].value,
+                    beta=base[4].value, count=base[5].value, n_slots=4, capacity=8, H=2, dk=16, dv=16,
+                    dtype=1)
+        args.update(kw)
+        return kda.KdaRing(**args)
+
+    def push(r, B=2, q=_fake(8)):
+        return L.kda_ring_push(ctypes.byref(r), _fake(7), B, q, _fake(9), _fake(10), _fake(11),
+                               _fake(12), None, None)
+
+    assert push(ring(capacity=0)) == kda.KDA_EUNSUPPORTED
+    assert push(ring(capacity=2000)) == kda.KDA_EUNSUPPORTED
+    assert push(ring(dk=24)) == kda.KDA_EUNSUPPORTED
+    assert push(ring(q=None)) == kda.KDA_EINVAL
+    assert push(ring(q=base[0].value + 8)) == kda.KDA_EINVAL           # 16-byte alignment
+    assert push(ring(k=base[0].value + 256)) == kda.KDA_EALIAS          # ring arrays overlap
+    assert push(ring(), B=-1) == kda.KDA_EINVAL
+    assert push(ring(), B=0) == kda.KDA_OK
+    assert push(ring(), q=P(base[0].value + 64)) == kda.KDA_EALIAS     # step input inside the ring
+    assert push(ring(), q=P(_fake(8).value + 4)) == kda.KDA_EINVAL
+    assert L.kda_ring_window(ctypes.byref(ring()), _fake(7), 2, None, _fake(9), _fake(10), _fake(11),
+                             _fake(12), None, None, None) == kda.KDA_EINVAL
+    assert L.kda_ring_reset(None, _fake(7), 2, None, None) == kda.KDA_EINVAL
