@@ -38,6 +38,12 @@ listed again, with the reason, in the design notes of the repository):
   R7  Replay with n_accepted = 0 leaves the state equal to the committed one
       and yields no output rows; for a batch with ragged n_accepted the output
       is padded to the draft length with zeros ([Serve demo] Tab 3 §6.4).
+  R14 A bf16 state (a variant; the pages keep the recurrent state in FP32,
+      [KDA cache] "检查点状态池的内存成本": in the fixed vLLM snapshot the conv
+      state uses the cache dtype and the recurrent state FP32): the state is
+      stored in bfloat16 between calls, computed in wider precision within a
+      call, and rounded to the nearest bfloat16 (ties to even) when stored.
+      A decode call is one step; a replay call rounds once, at its end.
   R13 Context parallelism (KCP): [Serve demo] §1.7 says its exchange does not
       grow with the sequence length and §7.2 calls it a prefix scan, without
       a formula.  Every step is affine in the state,
@@ -65,6 +71,9 @@ __all__ = [
     "kda_chunked_ref",
     "segment_summary",
     "compose_segments",
+    "round_bf16",
+    "decode_bf16_state",
+    "verify_and_replay_bf16_state",
 ]
 
 
@@ -359,3 +368,34 @@ def compose_segments(A, B, S_in=None):
         starts[i] = S
         S = A[i] @ S + B[i]
     return starts, S
+
+
+# ---------------------------------------------------------------------------
+# A bfloat16 state (reading R14).
+# ---------------------------------------------------------------------------
+def round_bf16(x):
+    """Round to the nearest bfloat16 value, ties to even, returned as float64.
+
+    bfloat16 keeps 8 significant bits (7 stored) and float32's exponent range.
+    With x = m * 2**e, 0.5 <= |m| < 1, the nearest value with 8 significant
+    bits is rint(m * 2**8) * 2**(e - 8), rint rounding halves to even.  For
+    values in the normal range (|x| >= 2**-126) and below the overflow
+    threshold, which is where states live.
+    """
+    x = _f64(x)
+    m, e = np.frexp(x)
+    return np.ldexp(np.rint(m * 256.0), e - 8)
+
+
+def decode_bf16_state(q, k, v, a, beta, S_bf16):
+    """One decode step on a bfloat16 state: the step in float64 from the
+    stored values, the new state rounded to bfloat16 (R14).  Returns (o, S)."""
+    o, S = kda_step(q, k, v, a, beta, _f64(S_bf16))
+    return o, round_bf16(S)
+
+
+def verify_and_replay_bf16_state(committed_bf16, q, k, v, a, beta, n_accepted):
+    """verify_and_replay from a bfloat16 committed state; the replayed state
+    is rounded to bfloat16 once, at the end of the call (R14)."""
+    s_new, o = verify_and_replay(_f64(committed_bf16), q, k, v, a, beta, n_accepted)
+    return round_bf16(s_new), o
