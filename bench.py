@@ -82,12 +82,13 @@ def front_end_bytes(T, H, dk, dv, K, n_seqs, n_windows_out, in_bytes=2):
     return (read + write) * in_bytes
 
 
-def decode_bytes(B, H, dk, dv, in_bytes=2):
-    return 2 * B * H * dk * dv * 4 + B * H * (3 * dk + dv + 1) * in_bytes + B * H * dv * in_bytes
+def decode_bytes(B, H, dk, dv, in_bytes=2, state_bytes=4):
+    return (2 * B * H * dk * dv * state_bytes + B * H * (3 * dk + dv + 1) * in_bytes
+            + B * H * dv * in_bytes)
 
 
-def replay_bytes(B, H, dk, dv, t_draft, n_acc, in_bytes=4):
-    return (2 * B * H * dk * dv * 4 + int(np.sum(n_acc)) * H * (3 * dk + dv + 1) * in_bytes
+def replay_bytes(B, H, dk, dv, t_draft, n_acc, in_bytes=4, state_bytes=4):
+    return (2 * B * H * dk * dv * state_bytes + int(np.sum(n_acc)) * H * (3 * dk + dv + 1) * in_bytes
             + B * H * t_draft * dv * in_bytes)
 
 
@@ -402,9 +403,13 @@ def bench_ring(torch, kda, inputs, steps, warmup):
     return res
 
 
-def bench_decode(torch, kda, inputs, steps, warmup):
+def bench_decode(torch, kda, inputs, steps, warmup, state_dtype="fp32"):
     B, H, dk, dv, n_tok = 256, 32, 128, 128, 64
     state = torch.from_numpy(inputs.decode_state(2, B, H, dk, dv, 0.05)).cuda()
+    sb = 4
+    if state_dtype == "bf16":
+        state = state.to(torch.bfloat16)
+        sb = 2
     toks = []
     for s in range(n_tok):
         t = inputs.decode_step_inputs(s, 2, B, H, dk, dv, "bf16")
@@ -422,8 +427,8 @@ def bench_decode(torch, kda, inputs, steps, warmup):
 
     ms, kms = run_steps(torch, step, max(2, steps // 2), max(1, warmup // 2))
     per_launch_ms = kms / n_tok
-    byts = decode_bytes(B, H, dk, dv)
-    res = {"workload": "decode: B=256, H=32, dk=dv=128, bf16 in, fp32 state, 64 in-place steps",
+    byts = decode_bytes(B, H, dk, dv, 2, sb)
+    res = {"workload": f"decode: B=256, H=32, dk=dv=128, bf16 in, {state_dtype} state, 64 in-place steps",
            "us_per_decode_step": per_launch_ms * 1e3, "algo_gbytes_per_step": byts / 1e9,
            "hbm_gbs": byts / (per_launch_ms * 1e-3) / 1e9,
            "hbm_frac": byts / (per_launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -432,7 +437,7 @@ def bench_decode(torch, kda, inputs, steps, warmup):
     return res
 
 
-def bench_replay(torch, kda, inputs, steps, warmup, shape="pages"):
+def bench_replay(torch, kda, inputs, steps, warmup, shape="pages", state_dtype="fp32"):
     if shape == "pages":
         w = inputs.replay_workload()
         dt, tdt, label = "fp32", torch.float32, "replay: B=64, H=16, dk=dv=32, 8 drafts, fp32"
@@ -441,6 +446,11 @@ def bench_replay(torch, kda, inputs, steps, warmup, shape="pages"):
         dt, tdt, label = "bf16", torch.bfloat16, "replay: B=256, H=32, dk=dv=128, 8 drafts, bf16"
     d = {n: torch.from_numpy(w[n]).to(tdt).cuda() for n in ("q", "k", "v", "a", "beta")}
     committed = torch.from_numpy(w["committed"]).cuda()
+    sb = 4
+    if state_dtype == "bf16":
+        committed = committed.to(torch.bfloat16)
+        sb = 2
+        label += ", bf16 state"
     n = torch.from_numpy(w["n_accepted"]).cuda()
     s_new = torch.empty_like(committed)
     Td, B, H, dk = w["q"].shape
@@ -459,7 +469,7 @@ def bench_replay(torch, kda, inputs, steps, warmup, shape="pages"):
 
     ms, kms = run_steps(torch, step, steps, warmup)
     kms /= reps
-    byts = replay_bytes(B, H, dk, dv, Td, w["n_accepted"], 4 if dt == "fp32" else 2)
+    byts = replay_bytes(B, H, dk, dv, Td, w["n_accepted"], 4 if dt == "fp32" else 2, sb)
     return {"workload": label, "us_per_call": kms * 1e3, "algo_mbytes": byts / 1e6,
             "hbm_gbs": byts / (kms * 1e-3) / 1e9,
             "hbm_frac": byts / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS}
@@ -570,7 +580,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", default="", help="comma list of: prefill4, prefill3, segments, front_end, "
-                                               "decode, replay, replay_big, ring, pack, copycal")
+                                               "decode, decode_bf16, replay, replay_big, "
+                                               "replay_big_bf16, ring, pack, copycal")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--json-out", default="")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -621,12 +632,19 @@ def main():
     if want("decode"):
         log("decode ...")
         parts["decode"] = bench_decode(torch, kda, inputs, args.steps, args.warmup)
+    if want("decode_bf16"):
+        log("decode (bf16 state) ...")
+        parts["decode_bf16_state"] = bench_decode(torch, kda, inputs, args.steps, args.warmup, "bf16")
     if want("replay"):
         log("replay ...")
         parts["replay"] = bench_replay(torch, kda, inputs, args.steps, args.warmup)
     if want("replay_big"):
         log("replay (large) ...")
         parts["replay_large"] = bench_replay(torch, kda, inputs, args.steps, args.warmup, "big")
+    if want("replay_big_bf16"):
+        log("replay (large, bf16 state) ...")
+        parts["replay_large_bf16_state"] = bench_replay(torch, kda, inputs, args.steps, args.warmup,
+                                                        "big", "bf16")
     if want("ring"):
         log("raw-input ring vs snapshots ...")
         parts["ring"] = bench_ring(torch, kda, inputs, args.steps, args.warmup)

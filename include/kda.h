@@ -133,6 +133,37 @@ int kda_unpack_heads(const float* page_pool, int64_t page_elems, int64_t n_slots
                      kda_layout dst_layout, float* state, int32_t* err_flag, void* stream);
 
 /*
+ * bf16 states and pages (a variant: the pages keep the recurrent state in
+ * FP32, [KDA cache] "检查点状态池的内存成本"; a bf16 state halves the bytes
+ * decode streams).  With state_dtype = KDA_BF16 the state (and committed,
+ * s_new, the page pool) holds bfloat16 values: they are widened exactly on
+ * load, the arithmetic stays fp32, and stored values are rounded to the
+ * nearest bfloat16, ties to even.  A decode call rounds after its step; a
+ * replay call rounds once, at its end (n_accepted = 0 leaves a bit-exact
+ * copy).  Pages of a bf16 state hold bf16 elements in the pack layout; pack
+ * and unpack copy them bit for bit; page_elems must then be a multiple of 8.
+ * state_dtype = KDA_F32 is exactly the call without the suffix.
+ */
+int kda_decode_step_ex(const void* q, const void* k, const void* v, const void* a,
+                       const void* beta, kda_dtype in_dtype, int32_t B, int32_t H, int32_t dk,
+                       int32_t dv, kda_dtype state_dtype, void* state, void* o, void* stream);
+
+int kda_verify_and_replay_ex(const void* committed, const void* q, const void* k, const void* v,
+                             const void* a, const void* beta, kda_dtype in_dtype,
+                             const int32_t* n_accepted, int32_t B, int32_t H, int32_t dk,
+                             int32_t dv, int32_t t_draft, kda_dtype state_dtype, void* s_new,
+                             void* o, int32_t* err_flag, void* stream);
+
+int kda_pack_heads_ex(const void* state, kda_dtype state_dtype, kda_layout src_layout, int32_t B,
+                      int32_t H, int32_t dk, int32_t dv, const int32_t* slot, void* page_pool,
+                      int64_t page_elems, int64_t n_slots, int32_t* err_flag, void* stream);
+
+int kda_unpack_heads_ex(const void* page_pool, kda_dtype state_dtype, int64_t page_elems,
+                        int64_t n_slots, const int32_t* slot, int32_t B, int32_t H, int32_t dk,
+                        int32_t dv, kda_layout dst_layout, void* state, int32_t* err_flag,
+                        void* stream);
+
+/*
  * kda_chunk_prefill — token-packed variable-length prefill from committed
  * states, with exact checkpoints written into page slots.
  *

@@ -10,8 +10,9 @@ namespace kda {
 
 // Decode (t_draft = 1, n_accepted = nullptr, s_in == s_out) and replay.
 struct SweepArgs {
-  const float* s_in;
-  float* s_out;
+  const void* s_in;   // fp32, or bf16 when state_bf16
+  void* s_out;
+  bool state_bf16;
   const void *q, *k, *v, *a, *beta;
   const int32_t* n_accepted;  // nullptr: every session runs t_draft steps
   int t_draft, B, H, dk, dv;
@@ -25,8 +26,9 @@ hipError_t launch_sweep(const SweepArgs& p);
 
 // Pack (state -> pages) and unpack (pages -> state).
 struct PackArgs {
-  const float* src;
-  float* dst;
+  const void* src;  // elements of es bytes (4: fp32, 2: bf16)
+  void* dst;
+  int es;
   const int32_t* slot;
   int B, H, dk, dv;
   bool vk;      // the state side uses the [.., dv, dk] layout

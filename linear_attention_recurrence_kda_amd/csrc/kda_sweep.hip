@@ -16,7 +16,8 @@
 // The sums over i (the key dimension) are split over row groups: partial sums
 // in registers, a cross-lane butterfly inside the wave, then LDS across
 // waves.  State stores are nontemporal (the state is streamed once per call
-// and is larger than the caches).
+// and is larger than the caches).  The state is fp32, or bf16 (widened exactly
+// on load, rounded to nearest even on store; the arithmetic stays fp32).
 //
 // Two kernels, each the faster of the variants measured for its case:
 //  - decode_kernel: one step, state updated in place, plain loads (fastest on
@@ -32,6 +33,31 @@ namespace kda {
 namespace {
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+
+// Four consecutive state values: fp32 (16 bytes) or bf16 (8 bytes, widened
+// exactly; stores round to nearest even).
+template <bool NT>
+__device__ __forceinline__ float4 load_state4(const float* p) {
+  const f32x4v* v = reinterpret_cast<const f32x4v*>(p);
+  const f32x4v x = NT ? __builtin_nontemporal_load(v) : *v;
+  return make_float4(x[0], x[1], x[2], x[3]);
+}
+template <bool NT>
+__device__ __forceinline__ float4 load_state4(const bf16raw* p) {
+  const u32x2v* v = reinterpret_cast<const u32x2v*>(p);
+  const u32x2v u = NT ? __builtin_nontemporal_load(v) : *v;
+  return make_float4(__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u),
+                     __uint_as_float(u[1] << 16), __uint_as_float(u[1] & 0xffff0000u));
+}
+__device__ __forceinline__ void store_state4(float* p, float4 s) {
+  __builtin_nontemporal_store(f32x4v{s.x, s.y, s.z, s.w}, reinterpret_cast<f32x4v*>(p));
+}
+__device__ __forceinline__ void store_state4(bf16raw* p, float4 s) {
+  const u32x2v u = {static_cast<uint32_t>(f32_to_bf16_bits(s.x)) | (static_cast<uint32_t>(f32_to_bf16_bits(s.y)) << 16),
+                    static_cast<uint32_t>(f32_to_bf16_bits(s.z)) | (static_cast<uint32_t>(f32_to_bf16_bits(s.w)) << 16)};
+  __builtin_nontemporal_store(u, reinterpret_cast<u32x2v*>(p));
+}
 
 template <int DK, int DV>
 struct SweepShape {
@@ -56,9 +82,9 @@ __device__ __forceinline__ void wave_sync() {
 // This is the step loop in the shape that measured fastest for a single
 // in-place step: inputs one step ahead, two barriers per step, outputs stored
 // by row group 0.
-template <int DK, int DV, typename InT>
+template <int DK, int DV, typename InT, typename SS>
 __global__ __launch_bounds__((SweepShape<DK, DV>::NT)) void decode_kernel(
-    const float* s_in, float* s_out, const InT* __restrict__ q, const InT* __restrict__ k,
+    const SS* s_in, SS* s_out, const InT* __restrict__ q, const InT* __restrict__ k,
     const InT* __restrict__ v, const InT* __restrict__ a, const InT* __restrict__ beta,
     const int32_t* __restrict__ n_accepted, int t_draft, int B, int H, InT* __restrict__ o,
     int o_steps, int32_t* __restrict__ err_flag) {
@@ -94,9 +120,7 @@ __global__ __launch_bounds__((SweepShape<DK, DV>::NT)) void decode_kernel(
 #pragma unroll
   for (int m = 0; m < RPT; ++m) {
     const int r = rg + m * RG;
-    const f32x4v* sp = reinterpret_cast<const f32x4v*>(s_in + sbase + static_cast<size_t>(r) * DV + 4 * cg);
-    const f32x4v x = *sp;
-    S[m] = make_float4(x[0], x[1], x[2], x[3]);
+    S[m] = load_state4<false>(s_in + sbase + static_cast<size_t>(r) * DV + 4 * cg);
   }
 
   float rk[EK], rq[EK], ra[EK], rv[EV], rb = 0.f;
@@ -230,14 +254,13 @@ __global__ __launch_bounds__((SweepShape<DK, DV>::NT)) void decode_kernel(
 #pragma unroll
   for (int m = 0; m < RPT; ++m) {
     const int r = rg + m * RG;
-    const f32x4v x = {S[m].x, S[m].y, S[m].z, S[m].w};
-    __builtin_nontemporal_store(x, reinterpret_cast<f32x4v*>(s_out + sbase + static_cast<size_t>(r) * DV + 4 * cg));
+    store_state4(s_out + sbase + static_cast<size_t>(r) * DV + 4 * cg, S[m]);
   }
 }
 
-template <int DK, int DV, typename InT>
+template <int DK, int DV, typename InT, typename SS>
 __global__ __launch_bounds__((SweepShape<DK, DV>::NT)) void replay_kernel(
-    const float* s_in, float* s_out, const InT* __restrict__ q, const InT* __restrict__ k,
+    const SS* s_in, SS* s_out, const InT* __restrict__ q, const InT* __restrict__ k,
     const InT* __restrict__ v, const InT* __restrict__ a, const InT* __restrict__ beta,
     const int32_t* __restrict__ n_accepted, int t_draft, int B, int H, InT* __restrict__ o,
     int o_steps, int32_t* __restrict__ err_flag) {
@@ -281,9 +304,7 @@ __global__ __launch_bounds__((SweepShape<DK, DV>::NT)) void replay_kernel(
 #pragma unroll
   for (int m = 0; m < RPT; ++m) {
     const int r = rg + m * RG;
-    const f32x4v* sp = reinterpret_cast<const f32x4v*>(s_in + sbase + static_cast<size_t>(r) * DV + 4 * cg);
-    const f32x4v x = __builtin_nontemporal_load(sp);
-    S[m] = make_float4(x[0], x[1], x[2], x[3]);
+    S[m] = load_state4<true>(s_in + sbase + static_cast<size_t>(r) * DV + 4 * cg);
   }
 
   // Every load and LDS write inside the step loop is unconditional (threads
@@ -442,14 +463,15 @@ __global__ __launch_bounds__((SweepShape<DK, DV>::NT)) void replay_kernel(
 #pragma unroll
   for (int m = 0; m < RPT; ++m) {
     const int r = rg + m * RG;
-    const f32x4v x = {S[m].x, S[m].y, S[m].z, S[m].w};
-    __builtin_nontemporal_store(x, reinterpret_cast<f32x4v*>(s_out + sbase + static_cast<size_t>(r) * DV + 4 * cg));
+    store_state4(s_out + sbase + static_cast<size_t>(r) * DV + 4 * cg, S[m]);
   }
 }
 
-template <int DK, int DV, typename InT>
+template <int DK, int DV, typename InT, typename SS>
 hipError_t launch_sweep_t(const SweepArgs& p) {
   using Sh = SweepShape<DK, DV>;
+  const SS* s_in = static_cast<const SS*>(p.s_in);
+  SS* s_out = static_cast<SS*>(p.s_out);
   const dim3 grid(static_cast<unsigned>(p.B) * static_cast<unsigned>(p.H));
   const InT *q = static_cast<const InT*>(p.q), *k = static_cast<const InT*>(p.k);
   const InT *v = static_cast<const InT*>(p.v), *a = static_cast<const InT*>(p.a);
@@ -457,12 +479,12 @@ hipError_t launch_sweep_t(const SweepArgs& p) {
   if (p.s_in == p.s_out) {
     // In place is the decode step: one token, every session.
     if (p.t_draft != 1 || p.n_accepted != nullptr || p.o_steps != 1) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((decode_kernel<DK, DV, InT>), grid, dim3(Sh::NT), 0, p.stream, p.s_in,
-                       p.s_out, q, k, v, a, beta, p.n_accepted, p.t_draft, p.B, p.H,
+    hipLaunchKernelGGL((decode_kernel<DK, DV, InT, SS>), grid, dim3(Sh::NT), 0, p.stream, s_in,
+                       s_out, q, k, v, a, beta, p.n_accepted, p.t_draft, p.B, p.H,
                        static_cast<InT*>(p.o), p.o_steps, p.err_flag);
   } else {
-    hipLaunchKernelGGL((replay_kernel<DK, DV, InT>), grid, dim3(Sh::NT), 0, p.stream, p.s_in,
-                       p.s_out, q, k, v, a, beta, p.n_accepted, p.t_draft, p.B, p.H,
+    hipLaunchKernelGGL((replay_kernel<DK, DV, InT, SS>), grid, dim3(Sh::NT), 0, p.stream, s_in,
+                       s_out, q, k, v, a, beta, p.n_accepted, p.t_draft, p.B, p.H,
                        static_cast<InT*>(p.o), p.o_steps, p.err_flag);
   }
   return hipGetLastError();
@@ -470,7 +492,9 @@ hipError_t launch_sweep_t(const SweepArgs& p) {
 
 template <int DK, int DV>
 hipError_t launch_sweep_dt(const SweepArgs& p) {
-  return p.bf16 ? launch_sweep_t<DK, DV, bf16raw>(p) : launch_sweep_t<DK, DV, float>(p);
+  if (p.state_bf16)
+    return p.bf16 ? launch_sweep_t<DK, DV, bf16raw, bf16raw>(p) : launch_sweep_t<DK, DV, float, bf16raw>(p);
+  return p.bf16 ? launch_sweep_t<DK, DV, bf16raw, float>(p) : launch_sweep_t<DK, DV, float, float>(p);
 }
 
 template <int DK>

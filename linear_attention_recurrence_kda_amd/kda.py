@@ -62,6 +62,15 @@ SIGNATURES = {
                                      _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "kda_front_end_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, ctypes.c_int, _i32, _i32, _i32, _i32,
                                           _i32, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "kda_decode_step_ex": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int, _i32, _i32, _i32,
+                                          _i32, ctypes.c_int, _vp, _vp, _vp]),
+    "kda_verify_and_replay_ex": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp,
+                                                _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _vp, _vp,
+                                                _vp, _vp]),
+    "kda_pack_heads_ex": (ctypes.c_int, [_vp, ctypes.c_int, ctypes.c_int, _i32, _i32, _i32, _i32, _vp,
+                                         _vp, _i64, _i64, _vp, _vp]),
+    "kda_unpack_heads_ex": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _vp, _i32, _i32, _i32,
+                                           _i32, ctypes.c_int, _vp, _vp, _vp]),
     "kda_ring_push": (ctypes.c_int, [_ringp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "kda_ring_window": (ctypes.c_int, [_ringp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "kda_ring_reset": (ctypes.c_int, [_ringp, _vp, _i32, _vp, _vp]),
@@ -146,28 +155,37 @@ def snapshot_cost_ratio(H, dk, dv):
     return lib().kda_snapshot_cost_ratio(H, dk, dv)
 
 
+def _state_code(t, name):
+    if t.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"{name} must be float32 or bfloat16, got {t.dtype}")
+    return _dtype_code(t)
+
+
 def decode_step(q, k, v, a, beta, state, o=None):
-    """One token per session; state [B,H,dk,dv] fp32 is updated in place.
-    q, k, a [B,H,dk], v [B,H,dv], beta [B,H]; returns o [B,H,dv]."""
+    """One token per session; state [B,H,dk,dv] (float32, or bfloat16 for the
+    bf16-state variant) is updated in place.  q, k, a [B,H,dk], v [B,H,dv],
+    beta [B,H]; returns o [B,H,dv]."""
     B, H, dk = q.shape
     dv = v.shape[-1]
     dev, dt = q.device, q.dtype
     for t, shp, n in ((q, (B, H, dk), "q"), (k, (B, H, dk), "k"), (a, (B, H, dk), "a"),
                       (v, (B, H, dv), "v"), (beta, (B, H), "beta")):
         _expect(t, shp, dt, n, dev)
-    _expect(state, (B, H, dk, dv), torch.float32, "state", dev)
+    sd = _state_code(state, "state")
+    _expect(state, (B, H, dk, dv), state.dtype, "state", dev)
     if o is None:
         o = torch.empty((B, H, dv), dtype=dt, device=dev)
     _expect(o, (B, H, dv), dt, "o", dev)
-    _check(lib().kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta), _dtype_code(q),
-                                 B, H, dk, dv, _ptr(state), _ptr(o), _stream(dev)))
+    _check(lib().kda_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta), _dtype_code(q),
+                                    B, H, dk, dv, sd, _ptr(state), _ptr(o), _stream(dev)))
     return o
 
 
 def verify_and_replay(committed, q, k, v, a, beta, n_accepted, s_new=None, o=None, err_flag=None):
-    """Clone committed [B,H,dk,dv] and replay n_accepted[b] draft steps.
-    Projections in (t_draft, B, H, D) layout; n_accepted int32 [B] on the device.
-    Returns (s_new [B,H,dk,dv] fp32, o [B,H,t_draft,dv])."""
+    """Clone committed [B,H,dk,dv] (float32, or bfloat16) and replay
+    n_accepted[b] draft steps.  Projections in (t_draft, B, H, D) layout;
+    n_accepted int32 [B] on the device.  Returns (s_new [B,H,dk,dv] in the
+    committed state's dtype, o [B,H,t_draft,dv])."""
     Td, B, H, dk = q.shape
     dv = v.shape[-1]
     dev, dt = q.device, q.dtype
@@ -175,56 +193,62 @@ def verify_and_replay(committed, q, k, v, a, beta, n_accepted, s_new=None, o=Non
                       (a, (Td, B, H, dk), "a"), (v, (Td, B, H, dv), "v"),
                       (beta, (Td, B, H), "beta")):
         _expect(t, shp, dt, n, dev)
-    _expect(committed, (B, H, dk, dv), torch.float32, "committed", dev)
+    sd = _state_code(committed, "committed")
+    _expect(committed, (B, H, dk, dv), committed.dtype, "committed", dev)
     _expect(n_accepted, (B,), torch.int32, "n_accepted", dev)
     if s_new is None:
         s_new = torch.empty_like(committed)
     if o is None:
         o = torch.empty((B, H, Td, dv), dtype=dt, device=dev)
-    _expect(s_new, (B, H, dk, dv), torch.float32, "s_new", dev)
+    _expect(s_new, (B, H, dk, dv), committed.dtype, "s_new", dev)
     _expect(o, (B, H, Td, dv), dt, "o", dev)
     if err_flag is not None:
         _expect(err_flag, (1,), torch.int32, "err_flag", dev)
-    _check(lib().kda_verify_and_replay(_ptr(committed), _ptr(q), _ptr(k), _ptr(v), _ptr(a),
-                                       _ptr(beta), _dtype_code(q), _ptr(n_accepted), B, H, dk, dv,
-                                       Td, _ptr(s_new), _ptr(o), _ptr(err_flag), _stream(dev)))
+    _check(lib().kda_verify_and_replay_ex(_ptr(committed), _ptr(q), _ptr(k), _ptr(v), _ptr(a),
+                                          _ptr(beta), _dtype_code(q), _ptr(n_accepted), B, H, dk,
+                                          dv, Td, sd, _ptr(s_new), _ptr(o), _ptr(err_flag),
+                                          _stream(dev)))
     return s_new, o
 
 
 def pack_heads(state, slot, page_pool, layout=KDA_LAYOUT_KV, err_flag=None, dk=None, dv=None):
-    """state [B,H,dk,dv] (KV) or [B,H,dv,dk] (VK) fp32 -> page_pool[slot[b]] (zero padded)."""
+    """state [B,H,dk,dv] (KV) or [B,H,dv,dk] (VK) -> page_pool[slot[b]] (zero
+    padded); state and pages float32, or both bfloat16."""
     B, H = state.shape[:2]
     if layout == KDA_LAYOUT_KV:
         dk, dv = state.shape[2], state.shape[3]
     else:
         dv, dk = state.shape[2], state.shape[3]
     dev = state.device
-    _expect(state, tuple(state.shape), torch.float32, "state", dev)
+    sd = _state_code(state, "state")
+    _expect(state, tuple(state.shape), state.dtype, "state", dev)
     _expect(slot, (B,), torch.int32, "slot", dev)
     n_slots, page_elems = page_pool.shape
-    _expect(page_pool, (n_slots, page_elems), torch.float32, "page_pool", dev)
+    _expect(page_pool, (n_slots, page_elems), state.dtype, "page_pool", dev)
     if err_flag is not None:
         _expect(err_flag, (1,), torch.int32, "err_flag", dev)
-    _check(lib().kda_pack_heads(_ptr(state), layout, B, H, dk, dv, _ptr(slot), _ptr(page_pool),
-                                page_elems, n_slots, _ptr(err_flag), _stream(dev)))
+    _check(lib().kda_pack_heads_ex(_ptr(state), sd, layout, B, H, dk, dv, _ptr(slot),
+                                   _ptr(page_pool), page_elems, n_slots, _ptr(err_flag),
+                                   _stream(dev)))
     return page_pool
 
 
 def unpack_heads(page_pool, slot, H, dk, dv, layout=KDA_LAYOUT_KV, state=None, err_flag=None):
-    """page_pool[slot[b]] -> state [B,H,dk,dv] (KV) or [B,H,dv,dk] (VK) fp32."""
+    """page_pool[slot[b]] -> state [B,H,dk,dv] (KV) or [B,H,dv,dk] (VK), in
+    the pool's dtype (float32 or bfloat16)."""
     dev = page_pool.device
     B = slot.shape[0]
     n_slots, page_elems = page_pool.shape
-    _expect(page_pool, (n_slots, page_elems), torch.float32, "page_pool", dev)
+    sd = _state_code(page_pool, "page_pool")
     _expect(slot, (B,), torch.int32, "slot", dev)
     shp = (B, H, dk, dv) if layout == KDA_LAYOUT_KV else (B, H, dv, dk)
     if state is None:
-        state = torch.empty(shp, dtype=torch.float32, device=dev)
-    _expect(state, shp, torch.float32, "state", dev)
+        state = torch.empty(shp, dtype=page_pool.dtype, device=dev)
+    _expect(state, shp, page_pool.dtype, "state", dev)
     if err_flag is not None:
         _expect(err_flag, (1,), torch.int32, "err_flag", dev)
-    _check(lib().kda_unpack_heads(_ptr(page_pool), page_elems, n_slots, _ptr(slot), B, H, dk, dv,
-                                  layout, _ptr(state), _ptr(err_flag), _stream(dev)))
+    _check(lib().kda_unpack_heads_ex(_ptr(page_pool), sd, page_elems, n_slots, _ptr(slot), B, H, dk,
+                                     dv, layout, _ptr(state), _ptr(err_flag), _stream(dev)))
     return state
 
 
