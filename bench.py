@@ -141,8 +141,16 @@ def committed_traffic(name, kernel_src):
 
 
 # ---------------------------------------------------------------- parts
-def bench_prefill(torch, kda, inputs, w, steps, warmup, pack_final, label):
+def bench_prefill(torch, kda, inputs, w, steps, warmup, pack_final, label, gate=False):
     d = {n: torch.from_numpy(w[n]).to(torch.bfloat16).cuda() for n in ("q", "k", "v", "a", "beta")}
+    g_min = None
+    if gate:
+        # Gate logits in place of a and beta (z ~ N(0, 1), the distribution a
+        # and beta were drawn from), applied inside the prefill.
+        g = torch.Generator(device="cuda").manual_seed(6)
+        for n in ("a", "beta"):
+            d[n] = torch.randn(d[n].shape, generator=g, device="cuda").to(torch.bfloat16)
+        g_min = -1.0
     H, dk = w["k"].shape[1:]
     dv = w["v"].shape[2]
     cu = w["cu_seqlens"]
@@ -168,7 +176,7 @@ def bench_prefill(torch, kda, inputs, w, steps, warmup, pack_final, label):
             ev[0].record()
         kda.chunk_prefill(d["q"], d["k"], d["v"], d["a"], d["beta"], cu, s0=s0, chunk=64,
                           checkpoints=ck, ckpt_slots=slots, page_pool=pool, o=o, s_final=sf,
-                          workspace=ws)
+                          workspace=ws, gate_g_min=g_min)
         if ev is not None:
             ev[1].record()
         if pack_final:
@@ -579,7 +587,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--only", default="", help="comma list of: prefill4, prefill3, segments, front_end, "
+    ap.add_argument("--only", default="", help="comma list of: prefill4, prefill4_gated, prefill3, segments, front_end, "
                                                "decode, decode_bf16, replay, replay_big, "
                                                "replay_big_bf16, ring, pack, copycal")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -617,6 +625,15 @@ def main():
             torch, kda, inputs, w4, args.steps, args.warmup, True,
             "varlen prefill: 16 seqs, len~logU[1024,32768], H=32, dk=dv=128, bf16, S0~N(0,0.1^2), "
             "chunk 64, ckpt every 4096 + tail, final states packed")
+    if want("prefill4_gated"):
+        if w4 is None:
+            log("generating the varlen prefill workload ...")
+            w4 = inputs.workload4()
+        log("prefill (varlen, fused gate) ...")
+        parts["prefill_varlen_gated"] = bench_prefill(
+            torch, kda, inputs, w4, args.steps, args.warmup, True,
+            "varlen prefill as above with the gate fused in: a = -sigmoid(z_a), beta = sigmoid(z_b) "
+            "computed from bf16 logits inside the prefill", gate=True)
     if want("prefill3"):
         log("prefill (single sequence) ...")
         parts["prefill_single"] = bench_prefill(

@@ -243,6 +243,24 @@ int kda_chunk_prefill_split(const void* q, const void* k, const void* v, const v
                             size_t workspace_bytes, int32_t dv_split, void* stream);
 
 /*
+ * kda_chunk_prefill_gated — kda_chunk_prefill_split with the gate fused in
+ * (the [KDA cache] page's vLLM path calls its prefill "chunk_kda_with_fused_gate"):
+ * z_a [T_tot, H, dk] and z_b [T_tot, H] (in_dtype) are gate logits, and the
+ * prefill uses a = g_min * sigmoid(z_a), beta = sigmoid(z_b) ([Serve demo]
+ * §1.3), computed in fp32 as the logits are loaded.  g_min finite and <= 0.
+ * The decay bound of kda_chunk_prefill applies to the gated a (it holds for
+ * g_min >= -160/chunk).  Everything else is as for kda_chunk_prefill_split.
+ */
+int kda_chunk_prefill_gated(const void* q, const void* k, const void* v, const void* z_a,
+                            const void* z_b, float g_min, kda_dtype in_dtype, int32_t H,
+                            int32_t dk, int32_t dv, int32_t chunk, const int32_t* cu_seqlens_host,
+                            int32_t n_seqs, const float* s0, void* o, float* s_final,
+                            const int32_t* ckpt_cu_host, const int32_t* ckpt_pos_host,
+                            const int32_t* ckpt_slot_host, int64_t n_ckpt, float* page_pool,
+                            int64_t page_elems, int64_t n_slots, void* workspace,
+                            size_t workspace_bytes, int32_t dv_split, void* stream);
+
+/*
  * Segment summaries for context-parallel prefill ([Serve demo] §7.2 "KCP 前缀扫描",
  * §1.7: what a segment of a long sequence passes on has a size independent of
  * its length).  Each token maps the state affinely,

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <numeric>
 #include <unordered_set>
 #include <vector>
@@ -88,8 +89,10 @@ int prefill_impl(const void* q, const void* k, const void* v, const void* a, con
                  const int32_t* ck_cu, const int32_t* ck_pos, const int32_t* ck_slot,
                  int64_t n_ckpt, float* page_pool, int64_t page_elems, int64_t n_slots,
                  void* workspace, size_t workspace_bytes, int32_t dv_split, float* a_out,
-                 void* stream) {
+                 void* stream, bool gate = false, float g_min = 0.f) {
   const bool summary = a_out != nullptr;
+  if (gate && (!std::isfinite(g_min) || g_min > 0.f))
+    return fail(KDA_EINVAL, "g_min must be finite and <= 0");
   if (!valid_dtype(in_dtype)) return fail(KDA_EINVAL, "in_dtype %d", static_cast<int>(in_dtype));
   if (n_seqs < 0 || H <= 0 || n_ckpt < 0)
     return fail(KDA_EINVAL, "n_seqs=%d H=%d n_ckpt=%lld", n_seqs, H, static_cast<long long>(n_ckpt));
@@ -257,6 +260,8 @@ int prefill_impl(const void* q, const void* k, const void* v, const void* a, con
   kda::PrefillArgs p{};
   p.q = q; p.k = k; p.v = v; p.a = a; p.beta = beta;
   p.bf16 = in_dtype == KDA_BF16;
+  p.gate = gate;
+  p.g_min = g_min;
   p.H = H; p.dk = dk; p.dv = dv; p.chunk = chunk;
   p.s0 = s0; p.o = o; p.s_final = s_final;
   p.page_pool = page_pool; p.page_elems = page_elems;
@@ -319,6 +324,19 @@ int kda_chunk_prefill(const void* q, const void* k, const void* v, const void* a
                                  n_seqs, s0, o, s_final, ckpt_cu_host, ckpt_pos_host,
                                  ckpt_slot_host, n_ckpt, page_pool, page_elems, n_slots, workspace,
                                  workspace_bytes, 0, stream);
+}
+
+int kda_chunk_prefill_gated(const void* q, const void* k, const void* v, const void* z_a,
+                            const void* z_b, float g_min, kda_dtype in_dtype, int32_t H,
+                            int32_t dk, int32_t dv, int32_t chunk, const int32_t* cu, int32_t n_seqs,
+                            const float* s0, void* o, float* s_final, const int32_t* ck_cu,
+                            const int32_t* ck_pos, const int32_t* ck_slot, int64_t n_ckpt,
+                            float* page_pool, int64_t page_elems, int64_t n_slots,
+                            void* workspace, size_t workspace_bytes, int32_t dv_split,
+                            void* stream) {
+  return prefill_impl(q, k, v, z_a, z_b, in_dtype, H, dk, dv, chunk, cu, n_seqs, s0, o, s_final,
+                      ck_cu, ck_pos, ck_slot, n_ckpt, page_pool, page_elems, n_slots, workspace,
+                      workspace_bytes, dv_split, nullptr, stream, true, g_min);
 }
 
 int kda_segment_summary_workspace_size(int32_t n_seg, int64_t total_tokens, int32_t H, int32_t dk,

@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256) void front_kernel(FrontParams p) {
 // window where p < K-1) into page slot `slot` of the window pool (zero-padded
 // past (K-1)*C), or into win_out[seq] when slot < 0.
 template <typename InT>
-__global__ __launch_bounds__(256) void window_kernel(WindowParams p) {
+__global__ __launch_bounds__(256) void conv_window_kernel(WindowParams p) {
   for (int b = blockIdx.y; b < p.n_bnd; b += gridDim.y) {
   const int32_t* bd = p.bnd + 4 * b;
   const int seq = bd[0], pos = bd[1], slot = bd[2], s0 = bd[3];
@@ -295,8 +295,8 @@ hipError_t launch_windows(const WindowParams& p) {
   const int64_t per = std::max<int64_t>(p.pool_elems, static_cast<int64_t>(p.K - 1) * p.C);
   const dim3 grid(static_cast<unsigned>(std::max<int64_t>(1, std::min<int64_t>((per + 255) / 256, 64))),
                   static_cast<unsigned>(std::min(p.n_bnd, 65535)));
-  if (p.bf16) hipLaunchKernelGGL((window_kernel<bf16raw>), grid, dim3(256), 0, p.stream, p);
-  else hipLaunchKernelGGL((window_kernel<float>), grid, dim3(256), 0, p.stream, p);
+  if (p.bf16) hipLaunchKernelGGL((conv_window_kernel<bf16raw>), grid, dim3(256), 0, p.stream, p);
+  else hipLaunchKernelGGL((conv_window_kernel<float>), grid, dim3(256), 0, p.stream, p);
   return hipGetLastError();
 }
 

@@ -67,6 +67,8 @@ struct UnitLayout {
 struct PrefillArgs {
   const void *q, *k, *v, *a, *beta;
   bool bf16;
+  bool gate;    // a, beta are logits; a = g_min * sigmoid(a), beta = sigmoid(beta)
+  float g_min;
   int H, dk, dv, chunk;
   const float* s0;
   void* o;

@@ -252,7 +252,8 @@ __device__ __forceinline__ f32x4 tile_mma_fb(f32x4 acc, const float* A, int lda,
 }
 
 struct LocalParams {
-  const void *q, *k, *a, *beta;
+  const void *q, *k, *a, *beta;  // a, beta: gate logits when the gate is fused
+  float g_min;
   const int32_t* chunks;   // [n_chunks][2] = (first token, rows)
   void* tq;                // [n_chunks][H] unit records (UnitLayout)
   int H, ld;
@@ -374,7 +375,11 @@ struct Shape {
 // ---------------------------------------------------------------------------
 // Local kernel: T diag(beta) and lower(A_qk) of one (chunk, head).
 
-template <int DK, typename InT, int NW>
+// GATE: a and beta arrive as logits z_a, z_b and the gate is applied on load,
+// a = g_min * sigmoid(z_a), beta = sigmoid(z_b) ("Serve 模块交互式演示" page,
+// §1.3), in fp32 (the fused gate of the "Kimi Linear 的 KDA 缓存" page's vLLM
+// path, "chunk_kda_with_fused_gate").
+template <int DK, typename InT, int NW, bool GATE>
 __global__ __launch_bounds__(64 * NW, 2) void local_kernel(LocalParams p) {
   using TR = Traits<InT>;
   using ST = typename TR::ST;
@@ -420,14 +425,22 @@ __global__ __launch_bounds__(64 * NW, 2) void local_kernel(LocalParams p) {
     for (int rr = 0; rr < RPG; ++rr) {
       const bool valid = r0 + rr < n;
       if (!valid) { kr[rr] = TR::zero(); qr[rr] = TR::zero(); }
-      const float2 aa = TR::unpack(valid ? ar[rr] : TR::zero());
+      float2 aa = TR::unpack(valid ? ar[rr] : TR::zero());
+      if constexpr (GATE) {
+        aa.x = valid ? p.g_min / (1.f + fast_exp(-aa.x)) : 0.f;
+        aa.y = valid ? p.g_min / (1.f + fast_exp(-aa.y)) : 0.f;
+      }
       run0 += aa.x; run1 += aa.y;
       gr[rr][0] = run0; gr[rr][1] = run1;
     }
     sm.tot[g][c0p] = run0;
     sm.tot[g][c0p + 1] = run1;
   }
-  if (tid < 16 * nb) sm.beta[tid] = tid < n ? to_f32(gb[row0 + static_cast<size_t>(tid) * H]) : 0.f;
+  if (tid < 16 * nb) {
+    float b = tid < n ? to_f32(gb[row0 + static_cast<size_t>(tid) * H]) : 0.f;
+    if constexpr (GATE) b = tid < n ? 1.f / (1.f + fast_exp(-b)) : 0.f;
+    sm.beta[tid] = b;
+  }
   __syncthreads();
 
   // ---- scaled Gram operands (reference: end of 16-row block nb/2 - 1) into
@@ -972,10 +985,13 @@ constexpr int kWaves = 8;
 template <int DK, typename InT>
 hipError_t launch_local(const PrefillArgs& a) {
   LocalParams prm;
-  prm.q = a.q; prm.k = a.k; prm.a = a.a; prm.beta = a.beta;
+  prm.q = a.q; prm.k = a.k; prm.a = a.a; prm.beta = a.beta; prm.g_min = a.g_min;
   prm.chunks = a.chunks; prm.tq = a.tq; prm.H = a.H; prm.ld = a.chunk;
   const dim3 grid(static_cast<unsigned>(a.n_chunks) * static_cast<unsigned>(a.H));
-  hipLaunchKernelGGL((local_kernel<DK, InT, kWaves>), grid, dim3(64 * kWaves), 0, a.stream, prm);
+  if (a.gate)
+    hipLaunchKernelGGL((local_kernel<DK, InT, kWaves, true>), grid, dim3(64 * kWaves), 0, a.stream, prm);
+  else
+    hipLaunchKernelGGL((local_kernel<DK, InT, kWaves, false>), grid, dim3(64 * kWaves), 0, a.stream, prm);
   return hipGetLastError();
 }
 

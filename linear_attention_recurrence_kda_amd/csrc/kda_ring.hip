@@ -35,7 +35,7 @@ __device__ __forceinline__ void zero_elems(char* dst, int64_t n, int es) {
     reinterpret_cast<uint16_t*>(dst)[i] = 0;
 }
 
-__global__ __launch_bounds__(kRingThreads) void push_kernel(RingArgs r, const int32_t* __restrict__ slot,
+__global__ __launch_bounds__(kRingThreads) void ring_push_kernel(RingArgs r, const int32_t* __restrict__ slot,
                                                              int B, RingStep in) {
   const int b = blockIdx.x;
   const int s = slot[b];
@@ -53,7 +53,7 @@ __global__ __launch_bounds__(kRingThreads) void push_kernel(RingArgs r, const in
   if (threadIdx.x == 0) r.count[s] = r.count[s] + 1;
 }
 
-__global__ __launch_bounds__(kRingThreads) void window_kernel(RingArgs r, const int32_t* __restrict__ slot,
+__global__ __launch_bounds__(kRingThreads) void ring_window_kernel(RingArgs r, const int32_t* __restrict__ slot,
                                                                int B, RingStep out, int32_t* n_valid) {
   const int b = blockIdx.x, i = blockIdx.y;  // session, row of the window
   const int s = slot[b];
@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kRingThreads) void window_kernel(RingArgs r, const 
   }
 }
 
-__global__ void reset_kernel(RingArgs r, const int32_t* __restrict__ slot, int B) {
+__global__ void ring_reset_kernel(RingArgs r, const int32_t* __restrict__ slot, int B) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= B) return;
   const int s = slot[b];
@@ -89,21 +89,21 @@ __global__ void reset_kernel(RingArgs r, const int32_t* __restrict__ slot, int B
 
 hipError_t launch_ring_push(const RingArgs& r, const int32_t* slot, int B, const RingStep& in) {
   if (B == 0) return hipSuccess;
-  hipLaunchKernelGGL(push_kernel, dim3(B), dim3(kRingThreads), 0, r.stream, r, slot, B, in);
+  hipLaunchKernelGGL(ring_push_kernel, dim3(B), dim3(kRingThreads), 0, r.stream, r, slot, B, in);
   return hipGetLastError();
 }
 
 hipError_t launch_ring_window(const RingArgs& r, const int32_t* slot, int B, const RingStep& out,
                               int32_t* n_valid) {
   if (B == 0) return hipSuccess;
-  hipLaunchKernelGGL(window_kernel, dim3(B, r.capacity), dim3(kRingThreads), 0, r.stream, r, slot, B, out,
+  hipLaunchKernelGGL(ring_window_kernel, dim3(B, r.capacity), dim3(kRingThreads), 0, r.stream, r, slot, B, out,
                      n_valid);
   return hipGetLastError();
 }
 
 hipError_t launch_ring_reset(const RingArgs& r, const int32_t* slot, int B) {
   if (B == 0) return hipSuccess;
-  hipLaunchKernelGGL(reset_kernel, dim3((B + 255) / 256), dim3(256), 0, r.stream, r, slot, B);
+  hipLaunchKernelGGL(ring_reset_kernel, dim3((B + 255) / 256), dim3(256), 0, r.stream, r, slot, B);
   return hipGetLastError();
 }
 

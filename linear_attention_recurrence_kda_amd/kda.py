@@ -51,6 +51,10 @@ SIGNATURES = {
     "kda_chunk_prefill_split": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int, _i32, _i32,
                                                _i32, _i32, _i32p, _i32, _vp, _vp, _vp, _i32p, _i32p,
                                                _i32p, _i64, _vp, _i64, _i64, _vp, _sz, _i32, _vp]),
+    "kda_chunk_prefill_gated": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, ctypes.c_int,
+                                               _i32, _i32, _i32, _i32, _i32p, _i32, _vp, _vp, _vp,
+                                               _i32p, _i32p, _i32p, _i64, _vp, _i64, _i64, _vp, _sz,
+                                               _i32, _vp]),
     "kda_segment_summary_workspace_size": (ctypes.c_int, [_i32, _i64, _i32, _i32, _i32, _i32,
                                                           ctypes.c_int, ctypes.POINTER(_sz)]),
     "kda_segment_summary": (ctypes.c_int, [_vp, _vp, _vp, _vp, ctypes.c_int, _i32, _i32, _i32, _i32,
@@ -262,7 +266,7 @@ def prefill_workspace_size(n_seqs, total_tokens, H, dk, dv, chunk, n_ckpt, dtype
 
 def chunk_prefill(q, k, v, a, beta, cu_seqlens, s0=None, chunk=64, checkpoints=None,
                   ckpt_slots=None, page_pool=None, o=None, s_final=None, want_final=True,
-                  workspace=None, dv_split=0):
+                  workspace=None, dv_split=0, gate_g_min=None):
     """Token-packed varlen prefill.
 
     q, k, a [T,H,dk], v [T,H,dv], beta [T,H] (float32 or bfloat16, same dtype)
@@ -270,6 +274,8 @@ def chunk_prefill(q, k, v, a, beta, cu_seqlens, s0=None, chunk=64, checkpoints=N
     checkpoints: per sequence a list of token counts (or None);
     ckpt_slots: per sequence a list of page slots, same shape as checkpoints;
     page_pool [n_slots, page_elems] fp32 receives the checkpoint states.
+    gate_g_min: when given, a and beta are gate logits and the prefill uses
+    a = gate_g_min * sigmoid(a), beta = sigmoid(beta) (the fused gate).
     Returns (o [T,H,dv], s_final [N,H,dk,dv] or None).
     """
     T, H, dk = q.shape
@@ -310,11 +316,15 @@ def chunk_prefill(q, k, v, a, beta, cu_seqlens, s0=None, chunk=64, checkpoints=N
     need = prefill_workspace_size(N, T, H, dk, dv, chunk, n_ckpt, dt)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    fn = lib().kda_chunk_prefill_split
-    _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta), _dtype_code(q), H, dk, dv, chunk,
-              _i32_array(cu), N, _ptr(s0), _ptr(o), _ptr(s_final), _i32_array(ck_cu),
+    common = (H, dk, dv, chunk, _i32_array(cu), N, _ptr(s0), _ptr(o), _ptr(s_final), _i32_array(ck_cu),
               _i32_array(ck_pos), _i32_array(ck_slot), n_ckpt, _ptr(page_pool), page_elems,
-              n_slots, _ptr(workspace), workspace.numel(), dv_split, _stream(dev)))
+              n_slots, _ptr(workspace), workspace.numel(), dv_split, _stream(dev))
+    if gate_g_min is None:
+        _check(lib().kda_chunk_prefill_split(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta),
+                                             _dtype_code(q), *common))
+    else:
+        _check(lib().kda_chunk_prefill_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta),
+                                             float(gate_g_min), _dtype_code(q), *common))
     return o, s_final
 
 

@@ -170,3 +170,45 @@ def test_prefill_rejects_wide_dv_tile(dtype, chunk):
             kda.chunk_prefill(d["q"], d["k"], d["v"], d["a"], d["beta"], w["cu_seqlens"],
                               chunk=chunk, dv_split=split)
         assert e.value.status == kda.KDA_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("dtype,chunk,g_min", [("bf16", 64, -1.0), ("fp32", 32, -2.0), ("bf16", 16, -0.5)])
+def test_prefill_with_fused_gate(dtype, chunk, g_min):
+    """a and beta given as logits: the prefill applies a = g_min*sigmoid(z_a),
+    beta = sigmoid(z_b) itself; the oracle takes the gates in float64 from the
+    same logits."""
+    import oracle as orc
+    lens = [1, 17, 64, 0, 130, 200]
+    H, dk, dv = 2, 64, 128
+    w = inputs.prefill_workload(170, lens, H, dk, dv, dtype, s0_std=0.1)
+    rng = np.random.default_rng(171)
+    z_a = rng.standard_normal(w["a"].shape).astype(np.float32)
+    z_b = rng.standard_normal(w["beta"].shape).astype(np.float32)
+    if dtype == "bf16":
+        z_a, z_b = inputs.round_to_bf16(z_a), inputs.round_to_bf16(z_b)
+    d = {n: dev_tensor(w[n], dtype) for n in ("q", "k", "v")}
+    s0 = torch.from_numpy(w["s0"]).cuda()
+    ck = [sorted({p for p in (5, 64, L) if 1 <= p <= L}) for L in lens]
+    n_ck = sum(len(c) for c in ck)
+    slots, i = [], 0
+    for c in ck:
+        slots.append(list(range(i, i + len(c))))
+        i += len(c)
+    pool = torch.zeros((n_ck, H * dk * dv), device="cuda")
+    o, sf = kda.chunk_prefill(d["q"], d["k"], d["v"], dev_tensor(z_a, dtype), dev_tensor(z_b, dtype),
+                              w["cu_seqlens"], s0=s0, chunk=chunk, checkpoints=ck, ckpt_slots=slots,
+                              page_pool=pool, gate_g_min=g_min)
+    torch.cuda.synchronize()
+    a = g_min * orc.sigmoid(z_a)
+    beta = orc.sigmoid(z_b)
+    cu = w["cu_seqlens"]
+    for n in range(len(lens)):
+        lo, hi = int(cu[n]), int(cu[n + 1])
+        if hi == lo:
+            continue
+        o_r, S_r, saved = orc.kda_recurrent(w["q"][lo:hi], w["k"][lo:hi], w["v"][lo:hi], a[lo:hi],
+                                            beta[lo:hi], w["s0"][n], ck[n])
+        assert_parity(o[lo:hi], o_r, dtype, f"o seq {n}")
+        assert_parity(sf[n], S_r, dtype, f"s_final seq {n}")
+        for j, p in enumerate(ck[n]):
+            assert_parity(pool[slots[n][j]].reshape(H, dk, dv), saved[p], dtype, f"ckpt {p} seq {n}")
