@@ -229,9 +229,11 @@ int kda_chunk_prefill(const void* q, const void* k, const void* v, const void* a
  * workgroups per (sequence, head) chain: the dv columns of the state are
  * independent in the recurrence (column j of S depends only on column j of
  * v), so a chain can be split into dv_split column tiles that each redo the
- * chunk's key-side scaling.  dv_split in {1, 2, 4, 8} with dv / dv_split one
- * of 16, 32 or 64 (so dv = 128 takes at least 2), or 0 to let the library
- * choose from the sequence lengths.  Other values: KDA_EUNSUPPORTED.
+ * chunk's key-side work.  dv_split in {1, 2, 4, 8} with dv / dv_split one
+ * of 16, 32 or 64, and also 128 for bf16 inputs at chunk 64 with dk a
+ * multiple of 32 (the configurations served by the column-slab kernel, whose
+ * default is one tile per head), or 0 to let the library choose.  Other
+ * values: KDA_EUNSUPPORTED.
  */
 int kda_chunk_prefill_split(const void* q, const void* k, const void* v, const void* a,
                             const void* beta, kda_dtype in_dtype, int32_t H, int32_t dk,

@@ -31,9 +31,14 @@ def _hipcc():
     return h
 
 
+# Per-source additions: the column-slab kernel keeps MFMA results in ordinary
+# vector registers (it rescales and rounds them every chunk).
+EXTRA = {"kda_slab.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src, verbose):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [_hipcc()] + COMMON + ["-c", src, "-o", obj]
+    cmd = [_hipcc()] + COMMON + EXTRA.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
     if src.endswith(".hip"):
         cmd[1:1] = ["-x", "hip"]
     if verbose:

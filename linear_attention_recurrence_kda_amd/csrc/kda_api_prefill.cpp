@@ -40,12 +40,15 @@ size_t tile_bytes(int64_t n_chunks, int32_t H, int32_t chunk, int32_t dk, size_t
 
 // dv columns per workgroup: 16, 32 or 64 (a 128-column tile's buffers do not
 // fit in LDS).
-bool valid_tile(int32_t dv, int32_t split, bool bf16) {
-  (void)bf16;
+// Slab-format records and the column-slab propagation kernel: bf16 inputs,
+// chunk 64, dk a multiple of 32.
+bool slab_path(int32_t dk, bool bf16, int32_t chunk) { return bf16 && chunk == 64 && dk % 32 == 0; }
+
+bool valid_tile(int32_t dv, int32_t split, bool slab) {
   if (split != 1 && split != 2 && split != 4 && split != 8) return false;
   if (dv % split) return false;
   const int t = dv / split;
-  return t == 16 || t == 32 || t == 64;
+  return t == 16 || t == 32 || t == 64 || (slab && t == 128);
 }
 
 // Chunks of one sequence: chunks never cross a checkpoint position.
@@ -68,7 +71,7 @@ int choose_split(int32_t dk, int32_t dv, bool bf16, int64_t total_chunks, int64_
   int best = 0;
   double best_t = 0;
   for (int split : {1, 2, 4, 8}) {
-    if (!valid_tile(dv, split, bf16)) continue;
+    if (!valid_tile(dv, split, false)) continue;
     const double tile = static_cast<double>(dv) / split;
     const double cost = 1.5 * dk + (3.0 * dk / 8 + 12.0) * tile / 16.0;
     const double t = std::max(static_cast<double>(total_chunks) * split * cost / kCUs,
@@ -160,13 +163,17 @@ int prefill_impl(const void* q, const void* k, const void* v, const void* a, con
   if (n_chunks * H >= (int64_t{1} << 31)) return fail(KDA_EUNSUPPORTED, "too many (chunk, head) pairs");
   int split = dv_split;
   const bool bf16 = in_dtype == KDA_BF16;
-  if (split == 0) split = choose_split(dk, dv, bf16, n_chunks * H, longest);
-  if (!valid_tile(dv, split, bf16))
+  // The column-slab kernel runs a whole head per workgroup (its per-chunk
+  // latency hardly depends on the tile width, and every tile reloads the
+  // chunk's record); the LDS-staged kernel picks its split from a cost model.
+  const bool slab = slab_path(dk, bf16, chunk);
+  if (split == 0) split = slab ? 1 : choose_split(dk, dv, bf16, n_chunks * H, longest);
+  if (!valid_tile(dv, split, slab))
     return fail(KDA_EUNSUPPORTED,
-                "dv_split=%d with dv=%d (dv/split must be 16, 32 or 64)",
-                dv_split, dv);
+                "dv_split=%d with dv=%d (dv/split must be 16, 32 or 64%s)",
+                dv_split, dv, slab ? ", or 128" : "");
   // The linear part A of a summary propagates dk identity columns.
-  const int a_split = summary ? choose_split(dk, dk, bf16, n_chunks * H, longest) : 0;
+  const int a_split = !summary ? 0 : slab ? 1 : choose_split(dk, dk, bf16, n_chunks * H, longest);
 
   // Buffers.
   const size_t es = elem_size(in_dtype);
@@ -261,6 +268,7 @@ int prefill_impl(const void* q, const void* k, const void* v, const void* a, con
   p.q = q; p.k = k; p.v = v; p.a = a; p.beta = beta;
   p.bf16 = in_dtype == KDA_BF16;
   p.gate = gate;
+  p.slab = slab;
   p.g_min = g_min;
   p.H = H; p.dk = dk; p.dv = dv; p.chunk = chunk;
   p.s0 = s0; p.o = o; p.s_final = s_final;

@@ -68,6 +68,7 @@ struct PrefillArgs {
   const void *q, *k, *v, *a, *beta;
   bool bf16;
   bool gate;    // a, beta are logits; a = g_min * sigmoid(a), beta = sigmoid(beta)
+  bool slab;    // slab-format records and the column-slab propagation kernel
   float g_min;
   int H, dk, dv, chunk;
   const float* s0;
@@ -84,6 +85,8 @@ struct PrefillArgs {
   hipStream_t stream;
 };
 hipError_t launch_prefill(const PrefillArgs& p);
+// The column-slab propagation (p.slab): mode 0 prefill, 1 a segment's B, 2 its A.
+hipError_t launch_slab_prop(const PrefillArgs& p, int mode);
 
 // Segment summaries: the work list and records of a prefill over the segments
 // (q unused, o and s0 null), then two propagations: p.s_final receives B (the

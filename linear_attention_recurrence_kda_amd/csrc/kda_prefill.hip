@@ -1,6 +1,6 @@
 // Chunked KDA prefill: the local kernel over every (chunk, head), then the
 // propagation kernel over every (sequence, head, dv tile) chain (kernels in
-// kda_prefill_kernels.hpp).
+// kda_prefill_kernels.hpp; the column-slab kernel in kda_slab.hip).
 #include "kda_prefill_kernels.hpp"
 
 namespace kda {
@@ -12,6 +12,9 @@ hipError_t launch_dk(const PrefillArgs& a) {
     const hipError_t e = launch_local<DK, InT>(a);
     if (e != hipSuccess) return e;
   }
+  // Slab-format records (bf16 inputs, chunk 64, dk a multiple of 32): the
+  // column-slab kernel (kda_slab.hip).
+  if (a.slab) return launch_slab_prop(a, 0);
   switch (a.dv / a.dv_tiles) {
     case 16: return launch_prop<DK, 16, InT, 0>(a);
     case 32: return launch_prop<DK, 32, InT, 0>(a);

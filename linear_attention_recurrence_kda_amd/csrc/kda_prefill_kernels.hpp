@@ -62,6 +62,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 // Operand storage: bf16 (bf16 inputs, chunk up to 64) or fp32 (fp32 inputs,
 // chunk up to 32).  Rows of LDS operand buffers are padded by 16 bytes.
@@ -112,6 +113,28 @@ __device__ __forceinline__ void putn(ST* p, const float* x) {
   else if constexpr (N == 4) put4(p, x);
   else if constexpr (N == 2) put2(p, x[0], x[1]);
   else put(p, x[0]);
+}
+
+// Column order of records read by the column-slab propagation kernel: inside
+// every 32-column group, column 16h + 4g + i is stored at 8g + 4h + i, so
+// that lane group g of an MFMA operand fragment finds its eight contraction
+// indices {4g..4g+3, 16+4g..16+4g+3} in one 16-byte piece.
+__device__ __forceinline__ int slab_col(int c) {
+  return (c & ~31) | ((c & 12) << 1) | ((c & 16) >> 2) | (c & 3);
+}
+
+// N consecutive elements of a row starting at column c0 (a multiple of N, or
+// of 4 for N > 4), in natural or slab column order.
+template <int N, typename ST>
+__device__ __forceinline__ void putn_cols(ST* row, int c0, const float* x, bool perm) {
+  if (!perm) {
+    putn<N>(row + c0, x);
+  } else if constexpr (N > 4) {
+#pragma unroll
+    for (int q = 0; q < N; q += 4) put4(row + slab_col(c0 + q), x + q);
+  } else {
+    putn<N>(row + slab_col(c0), x);
+  }
 }
 
 __device__ __forceinline__ bf16x8 zero8() { return __builtin_bit_cast(bf16x8, i32x4{0, 0, 0, 0}); }
@@ -254,6 +277,7 @@ __device__ __forceinline__ f32x4 tile_mma_fb(f32x4 acc, const float* A, int lda,
 struct LocalParams {
   const void *q, *k, *a, *beta;  // a, beta: gate logits when the gate is fused
   float g_min;
+  int perm;                // record columns in the column-slab order (slab_col)
   const int32_t* chunks;   // [n_chunks][2] = (first token, rows)
   void* tq;                // [n_chunks][H] unit records (UnitLayout)
   int H, ld;
@@ -470,6 +494,7 @@ __global__ __launch_bounds__(64 * NW, 2) void local_kernel(LocalParams p) {
       ogx[c0p] = fast_exp(ge0);
       ogx[c0p + 1] = fast_exp(ge1);
     }
+    const int kc = p.perm ? slab_col(c0p) : c0p;  // c0p, c0p + 1 stay adjacent
     float kh0[RPG], kh1[RPG];
 #pragma unroll
     for (int rr = 0; rr < RPG; ++rr) {
@@ -482,13 +507,27 @@ __global__ __launch_bounds__(64 * NW, 2) void local_kernel(LocalParams p) {
       put2(&sm.u.gram.qpm[r][c0p], qq.x * up0, qq.y * up1);
       put2(&sm.u.gram.kmm[r][c0p], kk.x * dn0, kk.y * dn1);
       const float e0 = up0 * em0, e1 = up1 * em1;
-      put2(okp + r * DK + c0p, kk.x * e0, kk.y * e1);
-      put2(oqp + r * DK + c0p, qq.x * e0, qq.y * e1);
+      put2(okp + r * DK + kc, kk.x * e0, kk.y * e1);
+      put2(oqp + r * DK + kc, qq.x * e0, qq.y * e1);
       kh0[rr] = kk.x * (dn0 * en0);
       kh1[rr] = kk.y * (dn1 * en1);
     }
-    putn<RPG>(okh + c0p * p.ld + r0, kh0);
-    putn<RPG>(okh + (c0p + 1) * p.ld + r0, kh1);
+    putn_cols<RPG>(okh + c0p * p.ld, r0, kh0, p.perm);
+    putn_cols<RPG>(okh + (c0p + 1) * p.ld, r0, kh1, p.perm);
+  } else if (r0 < p.ld) {
+    // Rows past the chunk's last 16-row block are written as zeros, so a
+    // reader may run its products over the whole chunk.
+    ST* okp = reinterpret_cast<ST*>(rec + lay.kp);
+    ST* oqp = reinterpret_cast<ST*>(rec + lay.qp);
+    ST* okh = reinterpret_cast<ST*>(rec + lay.kh);
+    const float zr[RPG] = {};
+#pragma unroll
+    for (int rr = 0; rr < RPG; ++rr) {
+      put2(okp + (r0 + rr) * DK + c0p, 0.f, 0.f);  // a zero row is a zero row in any order
+      put2(oqp + (r0 + rr) * DK + c0p, 0.f, 0.f);
+    }
+    putn_cols<RPG>(okh + c0p * p.ld, r0, zr, p.perm);
+    putn_cols<RPG>(okh + (c0p + 1) * p.ld, r0, zr, p.perm);
   }
   __syncthreads();
 
@@ -587,20 +626,29 @@ __global__ __launch_bounds__(64 * NW, 2) void local_kernel(LocalParams p) {
   }
   __syncthreads();
 
-  // ---- rows < 16 nb of both tiles to the workspace, 16 bytes per store;
-  // entries right of the diagonal block are written as zeros, so a reader may
-  // run a row block's products over any column range -----------------------
+  // ---- both tiles to the workspace, 16 bytes per store; entries right of
+  // the diagonal block and rows past the chunk's last 16-row block are written
+  // as zeros, so a reader may run its products over any range ---------------
   {
     const int ld = p.ld, ppr = ld * static_cast<int>(ES) / 16;  // 16-byte pieces per row
     constexpr int EP = 16 / static_cast<int>(ES);                // elements per piece
     char* dst = rec;
-    const int npc = 16 * nb * ppr;
+    const int npc = ld * ppr;
     for (int x = tid; x < 2 * npc; x += NT) {
       const int m = x >= npc, y = x - m * npc, r = y / ppr, cc = (y - r * ppr) * EP;
       const ST* src = m ? &sm.u.out.aqk[r][cc] : &sm.u.out.tb[r][cc];
       // Blocks above the block diagonal are zero (never built in LDS).
-      const i32x4 val = cc < 16 * (r / 16 + 1) ? *reinterpret_cast<const i32x4*>(src) : i32x4{0, 0, 0, 0};
-      *reinterpret_cast<i32x4*>(dst + (static_cast<size_t>(m) * ld * ld + r * ld + cc) * ES) = val;
+      const i32x4 val = r < 16 * nb && cc < 16 * (r / 16 + 1) ? *reinterpret_cast<const i32x4*>(src)
+                                                              : i32x4{0, 0, 0, 0};
+      char* drow = dst + (static_cast<size_t>(m) * ld * ld + r * ld) * ES;
+      if constexpr (ES == 2) {
+        if (p.perm) {  // the two 4-column halves land 8 columns apart
+          *reinterpret_cast<i32x2*>(drow + slab_col(cc) * ES) = i32x2{val[0], val[1]};
+          *reinterpret_cast<i32x2*>(drow + slab_col(cc + 4) * ES) = i32x2{val[2], val[3]};
+          continue;
+        }
+      }
+      *reinterpret_cast<i32x4*>(drow + cc * ES) = val;
     }
   }
 }
@@ -986,6 +1034,7 @@ template <int DK, typename InT>
 hipError_t launch_local(const PrefillArgs& a) {
   LocalParams prm;
   prm.q = a.q; prm.k = a.k; prm.a = a.a; prm.beta = a.beta; prm.g_min = a.g_min;
+  prm.perm = a.slab ? 1 : 0;
   prm.chunks = a.chunks; prm.tq = a.tq; prm.H = a.H; prm.ld = a.chunk;
   const dim3 grid(static_cast<unsigned>(a.n_chunks) * static_cast<unsigned>(a.H));
   if (a.gate)

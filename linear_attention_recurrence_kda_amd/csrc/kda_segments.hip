@@ -18,6 +18,7 @@ namespace {
 
 template <int DK, typename InT, int MODE>
 hipError_t prop_cols(const PrefillArgs& a) {
+  if (a.slab) return launch_slab_prop(a, MODE);
   switch (a.dv / a.dv_tiles) {
     case 16: return launch_prop<DK, 16, InT, MODE>(a);
     case 32: if constexpr (MODE != 2 || DK >= 32) return launch_prop<DK, 32, InT, MODE>(a); break;

@@ -118,7 +118,11 @@ def test_prefill_validation(L):
     assert call(chunk=48 + 8) == kda.KDA_EUNSUPPORTED
     assert call(chunk=80) == kda.KDA_EUNSUPPORTED
     assert call(dtype=0, chunk=64) == kda.KDA_EUNSUPPORTED  # fp32 inputs: chunk <= 32
-    assert call(split=1) == kda.KDA_EUNSUPPORTED                     # 128-column tile
+    # 128-column tiles: only on the column-slab path (bf16, chunk 64, dk % 32 == 0),
+    # where the call then gets as far as the workspace (too small for 4000 tokens).
+    assert call(split=1, cu=(0, 4000)) == kda.KDA_EWORKSPACE
+    assert call(chunk=32, split=1) == kda.KDA_EUNSUPPORTED
+    assert call(dk=16, dv=128, split=1) == kda.KDA_EUNSUPPORTED
     assert call(dtype=0, chunk=32, split=1) == kda.KDA_EUNSUPPORTED
     assert call(split=3) == kda.KDA_EUNSUPPORTED
     assert call(cu=(1, 40)) == kda.KDA_EINVAL
