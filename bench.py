@@ -39,7 +39,8 @@ BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "linear_attention_recurrence_kda_amd", "csrc")
 # The prefill kernels' sources (the traffic figure is stamped with their hash).
-PREFILL_SRC = [os.path.join(CSRC, "kda_prefill_kernels.hpp"), os.path.join(CSRC, "kda_prefill.hip")]
+PREFILL_SRC = [os.path.join(CSRC, f) for f in
+               ("kda_prefill_kernels.hpp", "kda_prefill.hip", "kda_prefill_slab.hpp", "kda_slab.hip")]
 
 
 def log(*a):
@@ -557,12 +558,14 @@ def write_traffic(fetch_csv, write_csv, name="prefill_varlen"):
         return out
 
     fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
-    # One prefill call = one local_kernel and one prop_kernel dispatch.
-    knames = sorted(k for k in fetch if "local_kernel" in k or "prop_kernel" in k)
+    # One prefill call = one local_kernel and one propagation dispatch
+    # (slab_kernel for bf16 at chunk 64, else prop_kernel).
+    prop = lambda k: "local_kernel" in k or "prop_kernel" in k or "slab_kernel" in k
+    knames = sorted(k for k in fetch if prop(k))
     f_pre = sum(float(np.mean(fetch[k])) for k in knames)
     w_pre = sum(float(np.mean(write[k])) for k in knames)
     kname = " + ".join(knames)
-    ours = lambda k: "local_kernel" in k or "prop_kernel" in k or "pack" in k
+    ours = lambda k: prop(k) or "pack" in k
     f_cp = max(v for k, vals in fetch.items() if not ours(k) for v in vals)
     w_cp = max(v for k, vals in write.items() if not ours(k) for v in vals)
     copy_bytes = float(1 << 30)
@@ -570,7 +573,7 @@ def write_traffic(fetch_csv, write_csv, name="prefill_varlen"):
            "copy_fetch_bytes_raw": f_cp, "copy_write_bytes_raw": w_cp,
            "fetch_scale": copy_bytes / f_cp, "write_scale": copy_bytes / w_cp,
            "hbm_bytes_per_launch": f_pre * copy_bytes / f_cp + w_pre * copy_bytes / w_cp,
-           "unit": "one prefill call (local_kernel + prop_kernel dispatches)",
+           "unit": "one prefill call (local kernel + propagation kernel dispatches)",
            "kernel_src_sha256_16": src_hash(PREFILL_SRC),
            "command": "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out> -o fetch -- "
                       "python3 <repo>/bench.py --only prefill4,copycal --steps 1 --warmup 0 --no-cpu "
@@ -684,7 +687,7 @@ def main():
                           "n_ckpt": head["n_ckpt"], "parallelism": "single GPU"}
         kbytes = head["algo_gbytes"] * 1e9
         line["roofline"] = {
-            "kernel": "prefill call: local_kernel<128,bf16> + prop_kernel<128,64,bf16>",
+            "kernel": "prefill call: local_kernel<128,bf16> + slab_kernel<128> (64-column tiles: 4 compute + 2 loader waves)",
             "bound": "hbm",
             "achieved": head["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": head["hbm_frac"],

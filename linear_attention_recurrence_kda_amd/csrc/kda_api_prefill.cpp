@@ -84,6 +84,29 @@ int choose_split(int32_t dk, int32_t dv, bool bf16, int64_t total_chunks, int64_
   return best;
 }
 
+// The column-slab kernel's split: a workgroup per (chain, tile) holds a CU
+// (its LDS), and a chunk costs it about t(tile) whatever else runs, set by
+// how fast one CU streams the chunk's record from HBM and by its waves'
+// serial work (measured on MI355X: about 3.0, 2.4, 2.0 and 1.95 us per
+// chunk at 128, 64, 32 and 16 columns).  The call takes about the larger of
+// the longest chain and the total work over the CUs.
+int choose_split_slab(int32_t dv, int64_t total_chunks, int64_t longest) {
+  int best = 0;
+  double best_t = 0;
+  for (int split : {1, 2, 4, 8}) {
+    if (!valid_tile(dv, split, true)) continue;
+    const int tile = dv / split;
+    const double t = tile == 128 ? 3.0 : tile == 64 ? 2.4 : tile == 32 ? 2.0 : 1.95;
+    const double cost = std::max(static_cast<double>(total_chunks) * split * t / kCUs,
+                                 static_cast<double>(longest) * t);
+    if (best == 0 || cost < best_t * 0.999) {
+      best = split;
+      best_t = cost;
+    }
+  }
+  return best;
+}
+
 // Prefill (a_out == nullptr) or segment summaries (a_out != nullptr: q is
 // unused, o and s0 are null and s_final receives B; see kda_segment_summary).
 int prefill_impl(const void* q, const void* k, const void* v, const void* a, const void* beta,
@@ -163,17 +186,16 @@ int prefill_impl(const void* q, const void* k, const void* v, const void* a, con
   if (n_chunks * H >= (int64_t{1} << 31)) return fail(KDA_EUNSUPPORTED, "too many (chunk, head) pairs");
   int split = dv_split;
   const bool bf16 = in_dtype == KDA_BF16;
-  // The column-slab kernel runs a whole head per workgroup (its per-chunk
-  // latency hardly depends on the tile width, and every tile reloads the
-  // chunk's record); the LDS-staged kernel picks its split from a cost model.
   const bool slab = slab_path(dk, bf16, chunk);
-  if (split == 0) split = slab ? 1 : choose_split(dk, dv, bf16, n_chunks * H, longest);
+  if (split == 0)
+    split = slab ? choose_split_slab(dv, n_chunks * H, longest) : choose_split(dk, dv, bf16, n_chunks * H, longest);
   if (!valid_tile(dv, split, slab))
     return fail(KDA_EUNSUPPORTED,
                 "dv_split=%d with dv=%d (dv/split must be 16, 32 or 64%s)",
                 dv_split, dv, slab ? ", or 128" : "");
   // The linear part A of a summary propagates dk identity columns.
-  const int a_split = !summary ? 0 : slab ? 1 : choose_split(dk, dk, bf16, n_chunks * H, longest);
+  const int a_split = !summary ? 0 : slab ? choose_split_slab(dk, n_chunks * H, longest)
+                                         : choose_split(dk, dk, bf16, n_chunks * H, longest);
 
   // Buffers.
   const size_t es = elem_size(in_dtype);

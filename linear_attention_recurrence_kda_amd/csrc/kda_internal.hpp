@@ -52,6 +52,13 @@ hipError_t launch_pack(const PackArgs& p);
 // bf16 inputs and fp32 for fp32 inputs; ld = chunk):
 //   T diag(beta) [ld][ld], lower(A_qk) [ld][ld], k*g [ld][dk], q*g [ld][dk],
 //   (k*g_n/g)^T [dk][ld], then g_n [dk] in fp32.
+// Rows and columns past the chunk's last 16-row block are zero, and so are
+// the entries right of each diagonal 16x16 block of the two [ld][ld] tiles.
+// Slab-format records (PrefillArgs::slab: bf16, chunk 64, dk % 32 == 0, read
+// by the column-slab kernel) store the columns of the two tiles, k*g and q*g
+// in slab_col order ((k*g_n/g)^T keeps its token order) and leave the
+// upper-right 32x32 quadrant of the two tiles unwritten (that kernel never
+// reads it).
 struct UnitLayout {
   size_t aqk, kp, qp, kh, gexp, bytes;  // byte offsets within a record, record size
   __host__ __device__ UnitLayout(int ld, int dk, int es) {

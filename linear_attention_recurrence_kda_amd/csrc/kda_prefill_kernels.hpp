@@ -115,26 +115,13 @@ __device__ __forceinline__ void putn(ST* p, const float* x) {
   else put(p, x[0]);
 }
 
-// Column order of records read by the column-slab propagation kernel: inside
-// every 32-column group, column 16h + 4g + i is stored at 8g + 4h + i, so
-// that lane group g of an MFMA operand fragment finds its eight contraction
-// indices {4g..4g+3, 16+4g..16+4g+3} in one 16-byte piece.
+// Column order of the [*][DK] matrices and the two tiles of records read by
+// the column-slab propagation kernel: inside every 32-column group, column
+// 16h + 4g + i is stored at 8g + 4h + i, so that lane group g of an MFMA
+// operand fragment finds its eight contraction indices {4g..4g+3,
+// 16+4g..16+4g+3} in one 16-byte piece.
 __device__ __forceinline__ int slab_col(int c) {
   return (c & ~31) | ((c & 12) << 1) | ((c & 16) >> 2) | (c & 3);
-}
-
-// N consecutive elements of a row starting at column c0 (a multiple of N, or
-// of 4 for N > 4), in natural or slab column order.
-template <int N, typename ST>
-__device__ __forceinline__ void putn_cols(ST* row, int c0, const float* x, bool perm) {
-  if (!perm) {
-    putn<N>(row + c0, x);
-  } else if constexpr (N > 4) {
-#pragma unroll
-    for (int q = 0; q < N; q += 4) put4(row + slab_col(c0 + q), x + q);
-  } else {
-    putn<N>(row + slab_col(c0), x);
-  }
 }
 
 __device__ __forceinline__ bf16x8 zero8() { return __builtin_bit_cast(bf16x8, i32x4{0, 0, 0, 0}); }
@@ -512,8 +499,8 @@ __global__ __launch_bounds__(64 * NW, 2) void local_kernel(LocalParams p) {
       kh0[rr] = kk.x * (dn0 * en0);
       kh1[rr] = kk.y * (dn1 * en1);
     }
-    putn_cols<RPG>(okh + c0p * p.ld, r0, kh0, p.perm);
-    putn_cols<RPG>(okh + (c0p + 1) * p.ld, r0, kh1, p.perm);
+    putn<RPG>(okh + c0p * p.ld + r0, kh0);
+    putn<RPG>(okh + (c0p + 1) * p.ld + r0, kh1);
   } else if (r0 < p.ld) {
     // Rows past the chunk's last 16-row block are written as zeros, so a
     // reader may run its products over the whole chunk.
@@ -526,8 +513,8 @@ __global__ __launch_bounds__(64 * NW, 2) void local_kernel(LocalParams p) {
       put2(okp + (r0 + rr) * DK + c0p, 0.f, 0.f);  // a zero row is a zero row in any order
       put2(oqp + (r0 + rr) * DK + c0p, 0.f, 0.f);
     }
-    putn_cols<RPG>(okh + c0p * p.ld, r0, zr, p.perm);
-    putn_cols<RPG>(okh + (c0p + 1) * p.ld, r0, zr, p.perm);
+    putn<RPG>(okh + c0p * p.ld + r0, zr);
+    putn<RPG>(okh + (c0p + 1) * p.ld + r0, zr);
   }
   __syncthreads();
 
@@ -634,20 +621,27 @@ __global__ __launch_bounds__(64 * NW, 2) void local_kernel(LocalParams p) {
     constexpr int EP = 16 / static_cast<int>(ES);                // elements per piece
     char* dst = rec;
     const int npc = ld * ppr;
+    // Entry (r, c) is built in LDS when r < 16 nb and c is in a block on or
+    // left of the diagonal; the rest is zero.
+    auto built = [&](int r, int c) { return r < 16 * nb && c < 16 * (r / 16 + 1); };
     for (int x = tid; x < 2 * npc; x += NT) {
       const int m = x >= npc, y = x - m * npc, r = y / ppr, cc = (y - r * ppr) * EP;
-      const ST* src = m ? &sm.u.out.aqk[r][cc] : &sm.u.out.tb[r][cc];
-      // Blocks above the block diagonal are zero (never built in LDS).
-      const i32x4 val = r < 16 * nb && cc < 16 * (r / 16 + 1) ? *reinterpret_cast<const i32x4*>(src)
-                                                              : i32x4{0, 0, 0, 0};
+      const ST* row = m ? &sm.u.out.aqk[r][0] : &sm.u.out.tb[r][0];
       char* drow = dst + (static_cast<size_t>(m) * ld * ld + r * ld) * ES;
       if constexpr (ES == 2) {
-        if (p.perm) {  // the two 4-column halves land 8 columns apart
-          *reinterpret_cast<i32x2*>(drow + slab_col(cc) * ES) = i32x2{val[0], val[1]};
-          *reinterpret_cast<i32x2*>(drow + slab_col(cc + 4) * ES) = i32x2{val[2], val[3]};
+        if (p.perm) {
+          // Stored piece cc = 32s + 8g holds columns 32s + 4g .. +3 and
+          // 32s + 16 + 4g .. +3 (slab_col); the upper-right 32x32 quadrant
+          // is left unwritten (the slab kernel never reads it).
+          if (r < 32 && cc >= 32) continue;
+          const int c1 = (cc & ~31) + ((cc & 31) >> 1), c2 = c1 + 16;
+          const i32x2 h1 = built(r, c1) ? *reinterpret_cast<const i32x2*>(row + c1) : i32x2{0, 0};
+          const i32x2 h2 = built(r, c2) ? *reinterpret_cast<const i32x2*>(row + c2) : i32x2{0, 0};
+          *reinterpret_cast<i32x4*>(drow + cc * ES) = i32x4{h1[0], h1[1], h2[0], h2[1]};
           continue;
         }
       }
+      const i32x4 val = built(r, cc) ? *reinterpret_cast<const i32x4*>(row + cc) : i32x4{0, 0, 0, 0};
       *reinterpret_cast<i32x4*>(drow + cc * ES) = val;
     }
   }

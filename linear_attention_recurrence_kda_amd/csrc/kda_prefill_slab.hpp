@@ -15,9 +15,10 @@
 // eight k values of column l%16) and, read as S^T, its A operand, when the
 // k values of lane group g = l/16 are taken in the order {4g..4g+3,
 // 16+4g..16+4g+3}.  The local kernel writes the record with its columns in
-// that order (slab_col), so every fragment of a record matrix is one 16-byte
-// LDS read, and S, Z and U feed the next product straight from the
-// accumulators (rounded to bf16, as the LDS-staged path rounds them).
+// that order (slab_col), so a fragment of k*g, q*g or the two tiles is one
+// 16-byte LDS read ((k*g_n/g)^T keeps its token order: two 8-byte reads),
+// and S, Z and U feed the next product straight from the accumulators
+// (rounded to bf16, as the LDS-staged path rounds them).
 //
 // Two loader waves do every move between global memory and LDS
 // (global_load_lds_dwordx4 in, buffer stores out): a wave stalls while the
@@ -111,6 +112,17 @@ __device__ __forceinline__ int swz(int m, int q) {
 template <int BASE, int W, int DK>
 __device__ __forceinline__ bf16x8 frag(const SlabRec<DK>& r, int m, int q) {
   return __builtin_bit_cast(bf16x8, r.u[BASE + m * W + swz<W>(m, q)]);
+}
+// (k g_n/g)^T keeps the natural token order (its rows are written 16 bytes
+// at a time by the local kernel): the fragment's two halves, tokens
+// 32s + 4g .. +3 and 32s + 16 + 4g .. +3, are two 8-byte reads.
+template <int BASE, int DK>
+__device__ __forceinline__ bf16x8 frag_kh(const SlabRec<DK>& r, int m, int s, int g) {
+  const char* row = reinterpret_cast<const char*>(&r.u[BASE + 8 * m]);
+  const int q1 = 4 * s + (g >> 1), q2 = q1 + 2, off = 8 * (g & 1);
+  const i32x2 lo = *reinterpret_cast<const i32x2*>(row + 16 * swz<8>(m, q1) + off);
+  const i32x2 hi = *reinterpret_cast<const i32x2*>(row + 16 * swz<8>(m, q2) + off);
+  return __builtin_bit_cast(bf16x8, i32x4{lo[0], lo[1], hi[0], hi[1]});
 }
 // T diag(beta) or lower(A_qk) (LO, HI: the two stored parts), row block T,
 // k-step s <= T / 2.
@@ -528,8 +540,8 @@ __global__ __launch_bounds__(64 * (NWV + kLoaders), 1) void slab_kernel(PropPara
 #pragma unroll
         for (int R = 0; R < NR; ++R) {
           const float4 gn = *reinterpret_cast<const float4*>(&gx[b][16 * R + 4 * grp]);
-          const bf16x8 a0 = frag<Rec::KH, 8>(r, 16 * R + col, grp);
-          const bf16x8 a1 = frag<Rec::KH, 8>(r, 16 * R + col, 4 + grp);
+          const bf16x8 a0 = frag_kh<Rec::KH>(r, 16 * R + col, 0, grp);
+          const bf16x8 a1 = frag_kh<Rec::KH>(r, 16 * R + col, 1, grp);
 #pragma unroll
           for (int J = 0; J < NJ; ++J) {
             S[R][J][0] *= gn.x;
