@@ -550,8 +550,9 @@ __global__ __launch_bounds__(64 * NW, 2) void local_kernel(LocalParams p) {
   for (int m = 0; m < NGT; ++m) {
     if (wave + NW * m < ntri) {
       const int col = 16 * aI[m] + (lane & 15), row0t = 16 * aR[m] + 4 * (lane >> 4);
+      const int cs = p.perm ? slab_col(col) : col;  // the tiles are kept in the record's column order
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) put(&sm.u.out.aqk[row0t + rr][col], row0t + rr >= col ? aq[m][rr] : 0.f);
+      for (int rr = 0; rr < 4; ++rr) put(&sm.u.out.aqk[row0t + rr][cs], row0t + rr >= col ? aq[m][rr] : 0.f);
     }
   }
   // ---- T = (I + L)^{-1}, one block column per wave; stored as T diag(beta)
@@ -589,13 +590,15 @@ __global__ __launch_bounds__(64 * NW, 2) void local_kernel(LocalParams p) {
         if (blk == 0) {
 #pragma unroll
           for (int r = 0; r < 16; r += 4) put4(&ts.colT[j][16 * I + r], x + r);
+          const int cs = p.perm ? slab_col(16 * I + j) : 16 * I + j;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) put(&sm.u.out.tb[16 * I + r][16 * I + j], x[r] * bcol);
+          for (int r = 0; r < 16; ++r) put(&sm.u.out.tb[16 * I + r][cs], x[r] * bcol);
         }
       }
     }
     wave_sync();
     // Block column: T_RI = -T_RR * sum_{J=I}^{R-1} L_RJ T_JI.
+    const int tcol = p.perm ? slab_col(16 * I + (lane & 15)) : 16 * I + (lane & 15);
     for (int R = I + 1; R < nb; ++R) {
       const f32x4 P = tile_mma_fb(zero4(), &sm.Lf[16 * R][16 * I], LF, &ts.colT[0][16 * I], LCT,
                                   16 * (R - I), lane);
@@ -607,7 +610,7 @@ __global__ __launch_bounds__(64 * NW, 2) void local_kernel(LocalParams p) {
       put4(&ts.colT[lane & 15][16 * R + 4 * (lane >> 4)], tv);
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr)
-        put(&sm.u.out.tb[16 * R + 4 * (lane >> 4) + rr][16 * I + (lane & 15)], tv[rr] * bcol);
+        put(&sm.u.out.tb[16 * R + 4 * (lane >> 4) + rr][tcol], tv[rr] * bcol);
       wave_sync();
     }
   }
@@ -630,14 +633,15 @@ __global__ __launch_bounds__(64 * NW, 2) void local_kernel(LocalParams p) {
       char* drow = dst + (static_cast<size_t>(m) * ld * ld + r * ld) * ES;
       if constexpr (ES == 2) {
         if (p.perm) {
-          // Stored piece cc = 32s + 8g holds columns 32s + 4g .. +3 and
-          // 32s + 16 + 4g .. +3 (slab_col); the upper-right 32x32 quadrant
-          // is left unwritten (the slab kernel never reads it).
+          // The tiles are in LDS in slab_col order: piece cc = 32s + 8g holds
+          // columns 32s + 4g .. +3 and 32s + 16 + 4g .. +3.  The upper-right
+          // 32x32 quadrant is left unwritten (the slab kernel never reads it).
           if (r < 32 && cc >= 32) continue;
           const int c1 = (cc & ~31) + ((cc & 31) >> 1), c2 = c1 + 16;
-          const i32x2 h1 = built(r, c1) ? *reinterpret_cast<const i32x2*>(row + c1) : i32x2{0, 0};
-          const i32x2 h2 = built(r, c2) ? *reinterpret_cast<const i32x2*>(row + c2) : i32x2{0, 0};
-          *reinterpret_cast<i32x4*>(drow + cc * ES) = i32x4{h1[0], h1[1], h2[0], h2[1]};
+          i32x4 val = *reinterpret_cast<const i32x4*>(row + cc);
+          if (!built(r, c1)) val[0] = val[1] = 0;
+          if (!built(r, c2)) val[2] = val[3] = 0;
+          *reinterpret_cast<i32x4*>(drow + cc * ES) = val;
           continue;
         }
       }
