@@ -49,5 +49,8 @@ template <>
 __device__ __forceinline__ bf16raw from_f32_int<bf16raw>(float x) { return bf16raw{f32_to_bf16_bits_int(x)}; }
 
 __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
+// 1/x by v_rcp_f32 (about 1 ulp), in place of the correctly rounded division
+// (a scale, a reciprocal, four FMAs and a fix-up per element).
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
 }  // namespace kda

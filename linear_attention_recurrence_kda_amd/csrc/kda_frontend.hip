@@ -27,6 +27,7 @@
 // before it come from the session's window, and the window comes back
 // shifted by one row.
 #include <algorithm>
+#include <type_traits>
 
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
@@ -35,18 +36,33 @@ namespace kda {
 namespace {
 
 constexpr float kL2Eps = 1e-6f;
+constexpr int kBatch = 4;  // rows per load batch
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 
 // VEC consecutive elements (16 bytes) as floats.
 template <typename InT>
 struct Vec {
   static constexpr int N = 16 / static_cast<int>(sizeof(InT));
 };
-__device__ __forceinline__ void ld16(const float* p, float* v) {
-  const float4 x = *reinterpret_cast<const float4*>(p);
+// A lane's 16 bytes as loaded (raw) and as floats.
+template <typename InT>
+struct Raw;
+template <>
+struct Raw<float> {
+  using T = float4;
+};
+template <>
+struct Raw<bf16raw> {
+  using T = uint4;
+};
+template <typename InT>
+__device__ __forceinline__ typename Raw<InT>::T ldraw(const InT* p) {
+  return *reinterpret_cast<const typename Raw<InT>::T*>(p);
+}
+__device__ __forceinline__ void unpack(const float4& x, float* v) {
   v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
 }
-__device__ __forceinline__ void ld16(const bf16raw* p, float* v) {
-  const uint4 u = *reinterpret_cast<const uint4*>(p);
+__device__ __forceinline__ void unpack(const uint4& u, float* v) {
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -66,7 +82,7 @@ __device__ __forceinline__ void st16(bf16raw* p, const float* v) {
   *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-__device__ __forceinline__ float sigmoid_f(float z) { return 1.f / (1.f + fast_exp(-z)); }
+__device__ __forceinline__ float sigmoid_f(float z) { return fast_rcp(1.f + fast_exp(-z)); }
 
 struct Tile {
   int seq, t0, rows, s0;  // sequence, first token, tokens, the sequence's first token
@@ -119,44 +135,76 @@ __device__ __forceinline__ void conv_part(const FrontParams& p, const Tile& tl, 
       wr[s][v] = tap >= 0 ? wv : 0.f;
     }
   // The three raw rows before the tile: from x inside the sequence, else row j
-  // of the carried window (j = row - s0 + K - 1), else zero (a branch on
-  // values shared by the whole wave).
+  // of the carried window (j = row - s0 + K - 1), else zero.  The source is
+  // chosen per row (values shared by the whole wave) and the three loads are
+  // issued together; a zero row loads the tile's first row and drops it.
+  const size_t xrow0 = STEP ? static_cast<size_t>(tl.seq) : static_cast<size_t>(tl.t0);
   float prev[3][VEC];
+  {
+    typename Raw<InT>::T hr[3];
+    bool keep[3];
 #pragma unroll
-  for (int s = 1; s <= 3; ++s) {
-    const int row = tl.t0 - s;
-    const int j = row - tl.s0 + K - 1;
+    for (int s = 1; s <= 3; ++s) {
+      const int row = tl.t0 - s;
+      const int j = row - tl.s0 + K - 1;
+      const bool from_x = !STEP && row >= tl.s0;
+      const bool from_w = !from_x && win != nullptr && j >= 0 && s <= K - 1;
+      const InT* src = from_x ? x + static_cast<size_t>(row) * C + ch
+                       : from_w ? win + (static_cast<size_t>(tl.seq) * (K - 1) + j) * C + ch
+                                : x + xrow0 * C + ch;
+      hr[s - 1] = ldraw(src);
+      keep[s - 1] = from_x || from_w;
+    }
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) prev[s - 1][v] = 0.f;
-    if (!STEP && row >= tl.s0) ld16(x + static_cast<size_t>(row) * C + ch, prev[s - 1]);
-    else if (win != nullptr && j >= 0 && s <= K - 1)
-      ld16(win + (static_cast<size_t>(tl.seq) * (K - 1) + j) * C + ch, prev[s - 1]);
+    for (int s = 0; s < 3; ++s) {
+      unpack(hr[s], prev[s]);
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) prev[s][v] = keep[s] ? prev[s][v] : 0.f;
+    }
   }
 
-  const size_t xrow0 = STEP ? static_cast<size_t>(tl.seq) : static_cast<size_t>(tl.t0);
-#pragma unroll 4
-  for (int r = 0; r < tl.rows; ++r) {
-    float xc[VEC], y[VEC];
-    ld16(x + (xrow0 + r) * C + ch, xc);
-    float ss = 0.f;
+  // Rows go in batches of kBatch: the loads of the next batch are issued
+  // before the current batch is computed and stored, so a wave keeps a batch
+  // of loads in flight and never waits on its own stores (vector-memory
+  // counters also count stores).  Past the tile's end the loads repeat its
+  // last row.
+  const int last = tl.rows - 1;
+  using RT = typename Raw<InT>::T;
+  RT nxt[kBatch];
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) {
-      const float u = wr[0][v] * xc[v] + wr[1][v] * prev[0][v] + wr[2][v] * prev[1][v] +
-                      wr[3][v] * prev[2][v];
-      prev[2][v] = prev[1][v];
-      prev[1][v] = prev[0][v];
-      prev[0][v] = xc[v];
-      y[v] = u * sigmoid_f(u);  // SiLU
-      ss += y[v] * y[v];
+  for (int i = 0; i < kBatch; ++i) nxt[i] = ldraw(x + (xrow0 + min(i, last)) * C + ch);
+  for (int r0 = 0; r0 < tl.rows; r0 += kBatch) {
+    RT cur[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      cur[i] = nxt[i];
+      nxt[i] = ldraw(x + (xrow0 + min(r0 + kBatch + i, last)) * C + ch);
     }
-    if (l2) {
 #pragma unroll
-      for (int off = LPT / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
-      const float sc = rsqrtf(ss + kL2Eps);
+    for (int i = 0; i < kBatch; ++i) {
+      if (r0 + i > last) break;
+      float xc[VEC], y[VEC];
+      unpack(cur[i], xc);
+      float ss = 0.f;
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) y[v] *= sc;
+      for (int v = 0; v < VEC; ++v) {
+        const float u = wr[0][v] * xc[v] + wr[1][v] * prev[0][v] + wr[2][v] * prev[1][v] +
+                        wr[3][v] * prev[2][v];
+        prev[2][v] = prev[1][v];
+        prev[1][v] = prev[0][v];
+        prev[0][v] = xc[v];
+        y[v] = u * sigmoid_f(u);  // SiLU
+        ss += y[v] * y[v];
+      }
+      if (l2) {
+#pragma unroll
+        for (int off = LPT / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+        const float sc = rsqrtf(ss + kL2Eps);
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) y[v] *= sc;
+      }
+      st16(out + ((tl.t0 + r0 + i) * static_cast<size_t>(H) + h) * D + cl, y);
     }
-    st16(out + ((tl.t0 + r) * static_cast<size_t>(H) + h) * D + cl, y);
   }
 
   if constexpr (STEP) {
@@ -173,6 +221,150 @@ __device__ __forceinline__ void conv_part(const FrontParams& p, const Tile& tl, 
   }
 }
 
+// The bf16 form of conv_part.  A lane keeps its channels as packed bf16: for
+// channel c, the pair (x_t[c], x_{t-1}[c]) is one 32-bit word made with a byte
+// permute, and the convolution is two dot2 products, with the weights of the
+// current and previous rows (taps K-1, K-2) and with the pair of two rows
+// back and taps K-3, K-4 (products exact, sums in fp32).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, a), __builtin_bit_cast(bf16x2v, b), c,
+                                        false);
+}
+// Pairs of the even / odd channel of words cur (row t) and prv (row t-1):
+// low half from cur, high half from prv.
+__device__ __forceinline__ uint32_t pair_even(uint32_t prv, uint32_t cur) {
+  return __builtin_amdgcn_perm(prv, cur, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pair_odd(uint32_t prv, uint32_t cur) {
+  return __builtin_amdgcn_perm(prv, cur, 0x07060302u);
+}
+// The row in the high halves of the pairs of channels 2i (lo) and 2i+1 (hi).
+__device__ __forceinline__ uint32_t high_row(uint32_t hi, uint32_t lo) {
+  return __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+}
+
+template <int D, int HG, bool STEP>
+__device__ __forceinline__ void conv_part_bf16(const FrontParams& p, const Tile& tl, int h0, int cbase,
+                                               bf16raw* __restrict__ out, bool l2) {
+  using L = Lanes<D, bf16raw>;
+  constexpr int LPT = L::LPT;
+  static_assert(L::VEC == 8, "8 channels a lane");
+  const int lane = threadIdx.x & 63;
+  const int C = p.C, K = p.K, H = p.H;
+  const int h = min(h0 + min(lane / LPT, HG - 1), H - 1);
+  const int cl = (lane % LPT) * 8;
+  const int ch = cbase + h * D + cl;
+  const bf16raw* __restrict__ x = static_cast<const bf16raw*>(p.x);
+  const uint16_t* __restrict__ w = reinterpret_cast<const uint16_t*>(p.w);
+  const bf16raw* __restrict__ win = static_cast<const bf16raw*>(p.win_in);
+
+  // w1[c] = (tap K-1, tap K-2), w2[c] = (tap K-3, tap K-4); missing taps are 0.
+  uint32_t w1[8], w2[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    uint32_t tw[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int tap = K - 1 - s;
+      const uint32_t wv = w[static_cast<size_t>(ch + c) * K + max(tap, 0)];
+      tw[s] = tap >= 0 ? wv : 0u;
+    }
+    w1[c] = tw[0] | (tw[1] << 16);
+    w2[c] = tw[2] | (tw[3] << 16);
+  }
+  // The three raw rows before the tile, as in conv_part (zero rows are 0).
+  const size_t xrow0 = STEP ? static_cast<size_t>(tl.seq) : static_cast<size_t>(tl.t0);
+  uint32_t hw[3][4];
+  {
+    uint4 hr[3];
+    bool keep[3];
+#pragma unroll
+    for (int s = 1; s <= 3; ++s) {
+      const int row = tl.t0 - s;
+      const int j = row - tl.s0 + K - 1;
+      const bool from_x = !STEP && row >= tl.s0;
+      const bool from_w = !from_x && win != nullptr && j >= 0 && s <= K - 1;
+      const bf16raw* src = from_x ? x + static_cast<size_t>(row) * C + ch
+                           : from_w ? win + (static_cast<size_t>(tl.seq) * (K - 1) + j) * C + ch
+                                    : x + xrow0 * C + ch;
+      hr[s - 1] = ldraw(src);
+      keep[s - 1] = from_x || from_w;
+    }
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+      hw[s][0] = keep[s] ? hr[s].x : 0u;
+      hw[s][1] = keep[s] ? hr[s].y : 0u;
+      hw[s][2] = keep[s] ? hr[s].z : 0u;
+      hw[s][3] = keep[s] ? hr[s].w : 0u;
+    }
+  }
+  // History: r1 = raw row t-1; pa = pairs (t-1, t-2), pb = pairs (t-2, t-3).
+  uint32_t r1[4], pa[8], pb[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r1[i] = hw[0][i];
+    pa[2 * i] = pair_even(hw[1][i], hw[0][i]);
+    pa[2 * i + 1] = pair_odd(hw[1][i], hw[0][i]);
+    pb[2 * i] = pair_even(hw[2][i], hw[1][i]);
+    pb[2 * i + 1] = pair_odd(hw[2][i], hw[1][i]);
+  }
+
+  // Batched loads as in conv_part.
+  const int last = tl.rows - 1;
+  uint4 nxt[kBatch];
+#pragma unroll
+  for (int i = 0; i < kBatch; ++i) nxt[i] = ldraw(x + (xrow0 + min(i, last)) * C + ch);
+  for (int r0 = 0; r0 < tl.rows; r0 += kBatch) {
+    uint4 cur[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      cur[i] = nxt[i];
+      nxt[i] = ldraw(x + (xrow0 + min(r0 + kBatch + i, last)) * C + ch);
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if (r0 + i > last) break;
+      const uint32_t xw[4] = {cur[i].x, cur[i].y, cur[i].z, cur[i].w};
+      float y[8];
+      float ss = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const uint32_t pc = (c & 1) ? pair_odd(r1[c / 2], xw[c / 2]) : pair_even(r1[c / 2], xw[c / 2]);
+        const float u = dot2_bf16(pc, w1[c], dot2_bf16(pb[c], w2[c], 0.f));
+        pb[c] = pa[c];
+        pa[c] = pc;
+        y[c] = u * sigmoid_f(u);  // SiLU
+        ss += y[c] * y[c];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r1[j] = xw[j];
+      if (l2) {
+#pragma unroll
+        for (int off = LPT / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+        const float sc = rsqrtf(ss + kL2Eps);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) y[c] *= sc;
+      }
+      st16(out + ((tl.t0 + r0 + i) * static_cast<size_t>(H) + h) * D + cl, y);
+    }
+  }
+
+  if constexpr (STEP) {
+    // The window after the token: row j is the raw row K-2-j rows back: the
+    // token (r1), then the high halves of pa (row t-1) and pb (row t-2).
+    bf16raw* wout = static_cast<bf16raw*>(p.win_step);
+    for (int j = 0; j < K - 1; ++j) {
+      const int s = K - 2 - j;  // 0..2
+      uint32_t o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        o[i] = s == 0 ? r1[i] : (s == 1 ? high_row(pa[2 * i + 1], pa[2 * i]) : high_row(pb[2 * i + 1], pb[2 * i]));
+      *reinterpret_cast<uint4*>(wout + (static_cast<size_t>(tl.seq) * (K - 1) + j) * C + ch) =
+          make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  }
+}
+
 template <int DK, int HG, typename InT>
 __device__ __forceinline__ void gate_part(const FrontParams& p, const Tile& tl, int h0) {
   using L = Lanes<DK, InT>;
@@ -185,17 +377,43 @@ __device__ __forceinline__ void gate_part(const FrontParams& p, const Tile& tl, 
   const InT* __restrict__ zb = static_cast<const InT*>(p.z_b);
   InT* __restrict__ a = static_cast<InT*>(p.a);
   InT* __restrict__ beta = static_cast<InT*>(p.beta);
-#pragma unroll 4
-  for (int r = 0; r < tl.rows; ++r) {
-    const size_t th = static_cast<size_t>(tl.t0 + r) * H + h;
-    float z[VEC], gv[VEC];
-    ld16(za + th * DK + cl, z);
+  const int last = tl.rows - 1;
+  using RT = typename Raw<InT>::T;
+  auto za_at = [&](int r) { return za + (static_cast<size_t>(tl.t0 + min(r, last)) * H + h) * DK + cl; };
+  RT nxt[kBatch];
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) gv[v] = p.g_min * sigmoid_f(z[v]);
-    st16(a + th * DK + cl, gv);
-    // Every lane of the head's group writes its beta (same value, same address).
-    beta[th] = from_f32<InT>(sigmoid_f(to_f32(zb[th])));
+  for (int i = 0; i < kBatch; ++i) nxt[i] = ldraw(za_at(i));
+  for (int r0 = 0; r0 < tl.rows; r0 += kBatch) {
+    RT cur[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      cur[i] = nxt[i];
+      nxt[i] = ldraw(za_at(r0 + kBatch + i));
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if (r0 + i > last) break;
+      float z[VEC], gv[VEC];
+      unpack(cur[i], z);
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) gv[v] = p.g_min * sigmoid_f(z[v]);
+      st16(a + (static_cast<size_t>(tl.t0 + r0 + i) * H + h) * DK + cl, gv);
+    }
   }
+  // beta: one lane per (row, head) of the tile's HG heads.
+  for (int e = lane; e < tl.rows * HG; e += 64) {
+    const int hb = h0 + e % HG;
+    if (hb < H) {
+      const size_t th = static_cast<size_t>(tl.t0 + e / HG) * H + hb;
+      beta[th] = from_f32<InT>(sigmoid_f(to_f32(zb[th])));
+    }
+  }
+}
+
+template <int D, int HG, typename InT, bool STEP>
+__device__ __forceinline__ void conv(const FrontParams& p, const Tile& tl, int h0, int cbase, InT* out, bool l2) {
+  if constexpr (std::is_same<InT, bf16raw>::value) conv_part_bf16<D, HG, STEP>(p, tl, h0, cbase, out, l2);
+  else conv_part<D, HG, InT, STEP>(p, tl, h0, cbase, out, l2);
 }
 
 template <int DK, int DV, typename InT, bool STEP>
@@ -216,9 +434,9 @@ __global__ __launch_bounds__(256) void front_kernel(FrontParams p) {
   }
   const int H = p.H;
   switch (wave) {
-    case 0: conv_part<DK, HG, InT, STEP>(p, tl, h0, 0, static_cast<InT*>(p.q), true); break;
-    case 1: conv_part<DK, HG, InT, STEP>(p, tl, h0, H * DK, static_cast<InT*>(p.k), true); break;
-    case 2: conv_part<DV, HG, InT, STEP>(p, tl, h0, 2 * H * DK, static_cast<InT*>(p.v), false); break;
+    case 0: conv<DK, HG, InT, STEP>(p, tl, h0, 0, static_cast<InT*>(p.q), true); break;
+    case 1: conv<DK, HG, InT, STEP>(p, tl, h0, H * DK, static_cast<InT*>(p.k), true); break;
+    case 2: conv<DV, HG, InT, STEP>(p, tl, h0, 2 * H * DK, static_cast<InT*>(p.v), false); break;
     default: gate_part<DK, HG, InT>(p, tl, h0); break;
   }
 }

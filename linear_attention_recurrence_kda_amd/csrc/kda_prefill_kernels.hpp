@@ -438,8 +438,8 @@ __global__ __launch_bounds__(64 * NW, 2) void local_kernel(LocalParams p) {
       if (!valid) { kr[rr] = TR::zero(); qr[rr] = TR::zero(); }
       float2 aa = TR::unpack(valid ? ar[rr] : TR::zero());
       if constexpr (GATE) {
-        aa.x = valid ? p.g_min / (1.f + fast_exp(-aa.x)) : 0.f;
-        aa.y = valid ? p.g_min / (1.f + fast_exp(-aa.y)) : 0.f;
+        aa.x = valid ? p.g_min * fast_rcp(1.f + fast_exp(-aa.x)) : 0.f;
+        aa.y = valid ? p.g_min * fast_rcp(1.f + fast_exp(-aa.y)) : 0.f;
       }
       run0 += aa.x; run1 += aa.y;
       gr[rr][0] = run0; gr[rr][1] = run1;
@@ -449,7 +449,7 @@ __global__ __launch_bounds__(64 * NW, 2) void local_kernel(LocalParams p) {
   }
   if (tid < 16 * nb) {
     float b = tid < n ? to_f32(gb[row0 + static_cast<size_t>(tid) * H]) : 0.f;
-    if constexpr (GATE) b = tid < n ? 1.f / (1.f + fast_exp(-b)) : 0.f;
+    if constexpr (GATE) b = tid < n ? fast_rcp(1.f + fast_exp(-b)) : 0.f;
     sm.beta[tid] = b;
   }
   __syncthreads();
