@@ -36,7 +36,7 @@ namespace kda {
 namespace {
 
 constexpr float kL2Eps = 1e-6f;
-constexpr int kBatch = 4;  // rows per load batch
+constexpr int kBatch = 8;  // rows per load batch
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 
 // VEC consecutive elements (16 bytes) as floats.
