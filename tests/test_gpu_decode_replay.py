@@ -125,6 +125,45 @@ def test_replay_other_shapes(dk, dv):
     assert_parity(s_new, S_r, "bf16", "S_new")
 
 
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64), (64, 128)])
+@pytest.mark.parametrize("t_draft", [1, 5, 16])
+def test_replay_shapes_and_acceptance(dk, dv, t_draft):
+    """bf16 inputs over square and rectangular states and 1 to 16 draft steps,
+    n_accepted spanning 0 .. t_draft in one call; n = 0 returns the committed
+    state."""
+    w = inputs.replay_workload(wid=31, B=6, H=2, dk=dk, dv=dv, t_draft=t_draft, dtype="bf16")
+    n_acc = np.array([0, t_draft, 1, t_draft // 2, t_draft - 1, t_draft], dtype=np.int32)
+    s_new, o, flag = _replay(w, "bf16", n_acc)
+    assert flag == 0
+    S_r, O_r = oracle.verify_and_replay(w["committed"], w["q"], w["k"], w["v"], w["a"],
+                                        w["beta"], n_acc)
+    assert_parity(o, O_r, "bf16", "O")
+    assert_parity(s_new, S_r, "bf16", "S_new")
+    on = to_np(o)
+    for b, n in enumerate(n_acc):
+        assert not on[b, :, n:].any(), "rows past n_accepted must be zero"
+        if n == 0:
+            assert torch.equal(s_new[b].cpu(), torch.from_numpy(w["committed"][b]))
+
+
+def test_replay_full_size_sampled():
+    """The replay bench's configuration (B=256, H=32, dk=dv=128, 8 drafts,
+    bf16 inputs, fp32 state, n_accepted uniform in 0..8) in one call; eight
+    sampled sessions (all heads) checked against the oracle."""
+    w = inputs.replay_workload(wid=11, B=256, H=32, dk=128, dv=128, t_draft=8, dtype="bf16")
+    s_new, o, flag = _replay(w, "bf16")
+    assert flag == 0
+    sb = [0, 1, 37, 100, 128, 200, 254, 255]
+    sub = {f: w[f][:, sb] for f in ("q", "k", "v", "a", "beta")}
+    S_r, O_r = oracle.verify_and_replay(w["committed"][sb], sub["q"], sub["k"], sub["v"],
+                                        sub["a"], sub["beta"], w["n_accepted"][sb])
+    assert_parity(o[sb], O_r, "bf16", "O (sampled sessions)")
+    assert_parity(s_new[sb], S_r, "bf16", "S_new (sampled sessions)")
+    on = to_np(o[sb])
+    for i, b in enumerate(sb):
+        assert not on[i, :, w["n_accepted"][b]:].any(), "rows past n_accepted must be zero"
+
+
 def test_replay_clamps_out_of_range_n_and_flags():
     w = inputs.replay_workload(wid=23, B=3, H=2, dk=16, dv=16, t_draft=4)
     s_new, o, flag = _replay(w, "fp32", [-1, 9, 2])
