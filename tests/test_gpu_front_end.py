@@ -26,7 +26,8 @@ def _exact(got, want, what):
 
 @pytest.mark.parametrize("dk,dv,dtype,K", [(16, 16, "fp32", 4), (32, 64, "bf16", 4),
                                            (64, 32, "fp32", 3), (128, 128, "bf16", 4),
-                                           (128, 16, "bf16", 2), (64, 128, "fp32", 1)])
+                                           (128, 16, "bf16", 2), (64, 128, "fp32", 1),
+                                           (64, 32, "bf16", 3), (16, 64, "bf16", 1)])
 @pytest.mark.parametrize("carried", [True, False])
 def test_front_end_matches_oracle(dk, dv, dtype, K, carried):
     H = 2
@@ -60,7 +61,8 @@ def test_front_end_matches_oracle(dk, dv, dtype, K, carried):
 
 
 @pytest.mark.parametrize("dk,dv,dtype,K", [(128, 128, "bf16", 4), (32, 16, "fp32", 3),
-                                           (64, 64, "bf16", 1)])
+                                           (64, 64, "bf16", 1), (64, 32, "bf16", 3),
+                                           (32, 128, "bf16", 2)])
 def test_front_end_step_matches_oracle(dk, dv, dtype, K):
     B, H = 5, 3
     w = inputs.front_end_inputs(120 + dk + K, [1] * B, H, dk, dv, K, dtype)
