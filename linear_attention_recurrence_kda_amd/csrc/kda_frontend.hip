@@ -20,12 +20,15 @@
 // a token's row; a lane walks the tile's tokens in order with the three
 // previous raw rows in registers (each row is read once, plus a three-row
 // halo per tile), and q and k take their L2 sums with a butterfly inside the
-// head's lane group.  Loads and stores in the token loop are unconditional
-// (groups past the heads repeat the last one and store identical values), so
-// the compiler's waits count only what they
-// need.  In step mode a tile is one decode token of one session, the rows
-// before it come from the session's window, and the window comes back
-// shifted by one row.
+// head's lane group.  Rows are loaded in batches, the next batch before the
+// current one is computed and stored, and loads and stores in the token loop
+// are unconditional (groups past the heads repeat the last one and store
+// identical values; loads past a tile's end repeat its last row), so the
+// compiler's waits count only what they need.  For bf16 inputs the
+// convolution runs on packed bf16 pairs with dot2 products (conv_part_bf16).
+// In step mode a tile is one decode token of one session, the rows before it
+// come from the session's window, and the window comes back shifted by one
+// row.
 #include <algorithm>
 #include <type_traits>
 
