@@ -93,8 +93,11 @@ def test_varlen_ragged_with_checkpoints(dk, dv, dtype, chunk):
     _check(w, dtype, o, sf, pool, slots)
 
 
-@pytest.mark.parametrize("split", [2, 4, 8])
+@pytest.mark.parametrize("split", [1, 2, 4, 8])
 def test_explicit_dv_splits_agree(split):
+    """Every dv split of the column-slab kernel at dk = dv = 128, bf16, chunk
+    64: one 128-column tile (two column tiles per compute wave) down to eight
+    16-column tiles."""
     w = inputs.prefill_workload(40, [200, 77], 2, 128, 128, "bf16", s0_std=0.1, ckpt_every=64)
     o, sf, pool, slots = _run(w, "bf16", 64, dv_split=split)
     _check(w, "bf16", o, sf, pool, slots)
