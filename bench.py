@@ -604,7 +604,8 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the KDA hot path here has no multi-GPU step "
-              "(every GPU box has one MI355X); run it with --gpus 1.", file=sys.stderr)
+              "(how it would shard is described with the design); run it with --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
