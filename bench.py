@@ -559,8 +559,8 @@ def write_traffic(fetch_csv, write_csv, name="prefill_varlen"):
 
     fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
     # One prefill call = one local_kernel and one propagation dispatch
-    # (slab_kernel for bf16 at chunk 64, else prop_kernel).
-    prop = lambda k: "local_kernel" in k or "prop_kernel" in k or "slab_kernel" in k
+    # (slab_mixed_kernel or slab_kernel for bf16 at chunk 64, else prop_kernel).
+    prop = lambda k: "local_kernel" in k or "prop_kernel" in k or "slab_kernel" in k or "slab_mixed_kernel" in k
     knames = sorted(k for k in fetch if prop(k))
     f_pre = sum(float(np.mean(fetch[k])) for k in knames)
     w_pre = sum(float(np.mean(write[k])) for k in knames)
@@ -688,7 +688,7 @@ def main():
                           "n_ckpt": head["n_ckpt"], "parallelism": "single GPU"}
         kbytes = head["algo_gbytes"] * 1e9
         line["roofline"] = {
-            "kernel": "prefill call: local_kernel<128,bf16> + slab_kernel<128> (64-column tiles: 4 compute + 2 loader waves)",
+            "kernel": "prefill call: local_kernel<128,bf16> + slab_mixed_kernel<128> (a tile width per sequence: 32, 64 or 128 columns; 4 compute + 2 loader waves)",
             "bound": "hbm",
             "achieved": head["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": head["hbm_frac"],

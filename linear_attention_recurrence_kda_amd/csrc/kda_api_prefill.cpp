@@ -26,12 +26,45 @@ int64_t max_chunks(int32_t n_seqs, int64_t total_tokens, int32_t chunk, int64_t 
   return total_tokens / chunk + n_seqs + n_ckpt;
 }
 
-// Workspace: the int32 work list, then (256-byte aligned) one record per
+// Workspace: the int32 work list (chains, sequence table, checkpoints,
+// chunks, and room for a mixed-width workgroup list of up to four entries
+// per chain), then (256-byte aligned) one record per
 // (chunk, head) (UnitLayout: T diag(beta), lower(A_qk) and the chunk's scaled
 // operands, in the operand precision: bf16 for bf16 inputs, fp32 for fp32).
 size_t work_ints(int32_t n_seqs, int32_t H, int64_t n_ckpt, int64_t n_chunks) {
   return static_cast<size_t>(2 * round8(static_cast<int64_t>(n_seqs) * H) + 6 * n_seqs + 2 * n_ckpt +
-                             2 * n_chunks);
+                             2 * n_chunks + 4 * round8(static_cast<int64_t>(n_seqs) * H));
+}
+
+// Per-sequence tile widths for the column-slab prefill at dv = 128 (32, 64
+// or 128 columns), from per-chunk times measured with every CU busy: the
+// widest width whose chain fits a target time, the target chosen to balance
+// the longest chain against the total work over the CUs.  Returns the
+// predicted time (us) and fills width[s]; 0 if a single width is as good.
+double choose_widths(const std::vector<int64_t>& chunks, int32_t H, std::vector<int>& width) {
+  const int ws[3] = {128, 64, 32};
+  const double tw[3] = {3.8, 2.5, 2.0};
+  double best = 0;
+  std::vector<int> cur(chunks.size());
+  for (size_t cand = 0; cand < chunks.size() * 3; ++cand) {
+    const double T = static_cast<double>(chunks[cand / 3]) * tw[cand % 3];
+    double work = 0;
+    for (size_t s = 0; s < chunks.size(); ++s) {
+      int k = 2;
+      for (int j = 0; j < 3; ++j)
+        if (static_cast<double>(chunks[s]) * tw[j] <= T) { k = j; break; }
+      cur[s] = ws[k];
+      work += static_cast<double>(H) * (128 / ws[k]) * static_cast<double>(chunks[s]) * tw[k];
+    }
+    double longest = 0;
+    for (size_t s = 0; s < chunks.size(); ++s) {
+      const int k = cur[s] == 128 ? 0 : cur[s] == 64 ? 1 : 2;
+      longest = std::max(longest, static_cast<double>(chunks[s]) * tw[k]);
+    }
+    const double cost = std::max(longest, work / kCUs);
+    if (best == 0 || cost < best) { best = cost; width = cur; }
+  }
+  return best;
 }
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 size_t tile_bytes(int64_t n_chunks, int32_t H, int32_t chunk, int32_t dk, size_t es) {
@@ -280,6 +313,48 @@ int prefill_impl(const void* q, const void* k, const void* v, const void* a, con
     wslot[i] = ck_slot[i];
   }
 
+  // Mixed tile widths: at dv = 128 on the slab path (prefill, automatic
+  // split), when the per-sequence widths predict a time 3 % or more below
+  // the single width's, the propagation runs one workgroup list with a width
+  // per sequence (kda_prefill_slab.hpp, slab_mixed_kernel).
+  int64_t n_wg = 0;
+  int32_t* wgs = wchunks + 2 * n_chunks;
+  if (slab && !summary && dv == 128 && dv_split == 0) {
+    std::vector<int64_t> sc(n_seqs);
+    for (int32_t i = 0; i < n_seqs; ++i) sc[i] = seqinfo[6 * i + 5] - seqinfo[6 * i + 4];
+    std::vector<int> width;
+    const double tm = choose_widths(sc, H, width);
+    int64_t longest = 0, total = 0;
+    for (int64_t x : sc) { longest = std::max(longest, x); total += x; }
+    // The best single width by the same per-chunk times (16 columns: 1.95 us).
+    double tu = 0;
+    const int uw[4] = {16, 32, 64, 128};
+    const double ut[4] = {1.95, 2.0, 2.5, 3.8};
+    for (int j = 0; j < 4; ++j) {
+      const double c = std::max(static_cast<double>(longest) * ut[j],
+                                static_cast<double>(total) * H * (128 / uw[j]) * ut[j] / kCUs);
+      if (tu == 0 || c < tu) tu = c;
+    }
+    if (tm > 0 && tm < 0.97 * tu) {
+      for (int64_t g = 0; g < n_chains / 8; ++g) {
+        int rounds = 0;
+        for (int x = 0; x < 8; ++x) {
+          const int32_t sq = chains[2 * (8 * g + x)];
+          if (sq >= 0) rounds = std::max(rounds, 128 / width[sq]);
+        }
+        for (int r = 0; r < rounds; ++r)
+          for (int x = 0; x < 8; ++x) {
+            const int64_t ch = 8 * g + x;
+            const int32_t sq = chains[2 * ch];
+            const int w = sq >= 0 ? width[sq] : 0;
+            const int code = w == 32 ? 0 : w == 64 ? 1 : 2;
+            wgs[n_wg++] = (sq >= 0 && r < 128 / w) ? static_cast<int32_t>((ch << 8) | (code << 4) | r)
+                                                   : static_cast<int32_t>((ch << 8) | (15 << 4));
+          }
+      }
+    }
+  }
+
   hipStream_t hs = static_cast<hipStream_t>(stream);
   // Pageable source: the runtime has consumed it when the call returns.
   hipError_t e = hipMemcpyAsync(workspace, work.data(), work.size() * 4, hipMemcpyHostToDevice, hs);
@@ -304,6 +379,8 @@ int prefill_impl(const void* q, const void* k, const void* v, const void* a, con
   p.tq = static_cast<char*>(workspace) + list_bytes;
   p.n_chains = static_cast<int>(n_chains);
   p.dv_tiles = split;
+  p.wgs = p.chunks + 2 * n_chunks;
+  p.n_wg = static_cast<int>(n_wg);
   p.stream = hs;
   if (summary) return hip_status(kda::launch_segment_summary(p, a_out, a_split), "segment summary launch");
   return hip_status(kda::launch_prefill(p), "prefill launch");

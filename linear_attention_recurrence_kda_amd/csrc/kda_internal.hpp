@@ -89,6 +89,8 @@ struct PrefillArgs {
   int n_chunks;
   int n_chains;  // padded
   int dv_tiles;  // workgroups per chain (split of dv)
+  const int32_t* wgs;  // mixed tile widths (slab prefill): [n_wg] entries (slab_mixed_kernel), or n_wg = 0
+  int n_wg;
   hipStream_t stream;
 };
 hipError_t launch_prefill(const PrefillArgs& p);

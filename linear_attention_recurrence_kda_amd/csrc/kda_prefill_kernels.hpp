@@ -283,6 +283,7 @@ struct PropParams {
   const int32_t* ck_pos;   // [n_ckpt] token counts from the sequence start
   const int32_t* ck_slot;  // [n_ckpt]
   const int32_t* chunks;   // [n_chunks][2]
+  const int32_t* wgs;      // per-workgroup (chain, width, tile) of the mixed-width slab launch
   int H, dv, ld, dv_tiles;
 };
 

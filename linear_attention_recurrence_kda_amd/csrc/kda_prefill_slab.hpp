@@ -45,6 +45,13 @@
 // MODE 0: prefill.  MODE 1: a segment's B, the end state from s0 (zero when
 // null), no outputs.  MODE 2: a segment's A, the end state from the identity
 // (dv = dk) with v taken as zero, no outputs.
+//
+// slab_kernel runs one tile width for every chain.  slab_mixed_kernel (the
+// prefill at dv = 128) takes a width per workgroup from a host-built list,
+// so that the longest sequences run in narrow tiles (a shorter chain per
+// chunk) and the short ones in wide tiles (the record read once per chain):
+// with one long sequence among short ones the propagation is bounded by that
+// sequence's chain, not by the total work.
 #pragma once
 
 #include <climits>
@@ -188,7 +195,8 @@ __device__ __forceinline__ int slab_jcol(int J, int col) {
 // waves and NLW loader waves.
 constexpr int kLoaders = 2;
 template <int DK, int NWV, int NJ, int MODE>
-__global__ __launch_bounds__(64 * (NWV + kLoaders), 1) void slab_kernel(PropParams p) {
+__device__ __forceinline__ void slab_body(const PropParams& p, int chain, int tile, SlabRec<DK>* sm,
+                                          float (*gx)[256], __bf16* vbase) {
   constexpr int NLW = kLoaders;
   constexpr int NT = 64 * (NWV + NLW), DVT = 16 * NJ * NWV;
   constexpr int NR = DK / 16;   // 16-row blocks of S
@@ -198,9 +206,7 @@ __global__ __launch_bounds__(64 * (NWV + kLoaders), 1) void slab_kernel(PropPara
   constexpr int VPR = DVT / 8;                // 16-byte pieces per row of the v tile
   constexpr int VSW = VPR < 4 ? VPR - 1 : 3;  // v row swizzle: piece q of row r at q ^ ((r >> 2) & VSW)
   static_assert(DK % 32 == 0, "dk a multiple of 32");
-  __shared__ __attribute__((aligned(16))) Rec sm[2];
-  __shared__ __attribute__((aligned(16))) float gx[2][256];       // g_n, then landing room
-  __shared__ __attribute__((aligned(16))) __bf16 vb[2][64 * DVT];  // v of a chunk, this tile
+  __bf16 (*vb)[64 * DVT] = reinterpret_cast<__bf16 (*)[64 * DVT]>(vbase);  // v of a chunk, this tile
 
   const int tid = threadIdx.x, lane = tid & 63, grp = lane >> 4, col = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -208,9 +214,6 @@ __global__ __launch_bounds__(64 * (NWV + kLoaders), 1) void slab_kernel(PropPara
   const int lw = wave - NWV;         // loader index
   const int H = p.H, dv = p.dv;
 
-  // Workgroup -> (chain, dv tile): the tiles of a chain land on one XCD.
-  const int bid = blockIdx.x, xcd = bid & 7, local = bid >> 3;
-  const int chain = 8 * (local / p.dv_tiles) + xcd, tile = local % p.dv_tiles;
   const int seq = ld_const(p.chains, 2 * chain), h = ld_const(p.chains, 2 * chain + 1);
   if (seq < 0) return;
   const int lo = ld_const(p.seqinfo, 6 * seq), hi = ld_const(p.seqinfo, 6 * seq + 1);
@@ -564,6 +567,34 @@ __global__ __launch_bounds__(64 * (NWV + kLoaders), 1) void slab_kernel(PropPara
   if (!loader && p.s_final != nullptr) store_state(p.s_final + state_off);
 }
 
+// One tile width for every workgroup: workgroup -> (chain, dv tile), the
+// tiles of a chain on one XCD.
+template <int DK, int NWV, int NJ, int MODE>
+__global__ __launch_bounds__(64 * (NWV + kLoaders), 1) void slab_kernel(PropParams p) {
+  __shared__ __attribute__((aligned(16))) SlabRec<DK> sm[2];
+  __shared__ __attribute__((aligned(16))) float gx[2][256];                  // g_n, then landing room
+  __shared__ __attribute__((aligned(16))) __bf16 vb[2 * 64 * 16 * NJ * NWV];  // v of a chunk, this tile
+  const int bid = blockIdx.x, xcd = bid & 7, local = bid >> 3;
+  const int chain = 8 * (local / p.dv_tiles) + xcd, tile = local % p.dv_tiles;
+  slab_body<DK, NWV, NJ, MODE>(p, chain, tile, sm, gx, vb);
+}
+
+// A tile width per workgroup (prefill): entry bid of p.wgs is chain << 8 |
+// width code << 4 | tile (width code 0: 32 columns, 1: 64, 2: 128; 15: no
+// work).  Six waves for every width: a 32-column tile's two spare waves run
+// the loader loop with nothing to load.
+template <int DK>
+__global__ __launch_bounds__(64 * (4 + kLoaders), 1) void slab_mixed_kernel(PropParams p) {
+  __shared__ __attribute__((aligned(16))) SlabRec<DK> sm[2];
+  __shared__ __attribute__((aligned(16))) float gx[2][256];
+  __shared__ __attribute__((aligned(16))) __bf16 vb[2 * 64 * 128];
+  const int e = ld_const(p.wgs, blockIdx.x);
+  const int chain = e >> 8, code = (e >> 4) & 15, tile = e & 15;
+  if (code == 0) slab_body<DK, 2, 1, 0>(p, chain, tile, sm, gx, vb);
+  else if (code == 1) slab_body<DK, 4, 1, 0>(p, chain, tile, sm, gx, vb);
+  else if (code == 2) slab_body<DK, 4, 2, 0>(p, chain, tile, sm, gx, vb);
+}
+
 template <int DK, int NWV, int NJ, int MODE>
 hipError_t launch_slab_t(const PrefillArgs& a) {
   PropParams prm;
@@ -580,6 +611,20 @@ hipError_t launch_slab_t(const PrefillArgs& a) {
 
 // Tile widths 16, 32, 64 and 128 columns: one 16-column tile per compute
 // wave up to 64 columns (more waves share the chunk's work), two at 128.
+template <int DK>
+hipError_t launch_slab_mixed(const PrefillArgs& a) {
+  PropParams prm;
+  prm.v = a.v; prm.tq = a.tq;
+  prm.s0 = a.s0; prm.o = a.o; prm.s_final = a.s_final;
+  prm.page_pool = a.page_pool; prm.page_elems = a.page_elems;
+  prm.chains = a.chains; prm.seqinfo = a.seqinfo; prm.ck_pos = a.ck_pos; prm.ck_slot = a.ck_slot;
+  prm.chunks = a.chunks; prm.wgs = a.wgs;
+  prm.H = a.H; prm.dv = a.dv; prm.ld = a.chunk; prm.dv_tiles = a.dv_tiles;
+  hipLaunchKernelGGL((slab_mixed_kernel<DK>), dim3(static_cast<unsigned>(a.n_wg)), dim3(64 * (4 + kLoaders)), 0,
+                     a.stream, prm);
+  return hipGetLastError();
+}
+
 template <int DK, int MODE>
 hipError_t launch_slab(const PrefillArgs& a) {
   switch (a.dv / a.dv_tiles) {

@@ -8,6 +8,14 @@
 namespace kda {
 
 hipError_t launch_slab_prop(const PrefillArgs& a, int mode) {
+  if (mode == 0 && a.n_wg > 0) {
+    switch (a.dk) {
+      case 32: return launch_slab_mixed<32>(a);
+      case 64: return launch_slab_mixed<64>(a);
+      case 128: return launch_slab_mixed<128>(a);
+    }
+    return hipErrorInvalidValue;
+  }
   switch (a.dk) {
     case 32:
       return mode == 0 ? launch_slab<32, 0>(a) : mode == 1 ? launch_slab<32, 1>(a) : launch_slab<32, 2>(a);
