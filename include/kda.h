@@ -232,8 +232,11 @@ int kda_chunk_prefill(const void* q, const void* k, const void* v, const void* a
  * chunk's key-side work.  dv_split in {1, 2, 4, 8} with dv / dv_split one
  * of 16, 32 or 64, and also 128 for bf16 inputs at chunk 64 with dk a
  * multiple of 32 (the configurations served by the column-slab kernel, whose
- * default is one tile per head), or 0 to let the library choose.  Other
- * values: KDA_EUNSUPPORTED.
+ * default is one tile per head), or 0 to let the library choose, or -1 for a
+ * tile width per sequence (32, 64 or 128 columns, from the library's cost
+ * model, in one launch) where the column-slab kernel runs with dv = 128; the
+ * automatic choice (0) takes that form where the model predicts it faster.
+ * Other values: KDA_EUNSUPPORTED.
  */
 int kda_chunk_prefill_split(const void* q, const void* k, const void* v, const void* a,
                             const void* beta, kda_dtype in_dtype, int32_t H, int32_t dk,

@@ -220,7 +220,11 @@ int prefill_impl(const void* q, const void* k, const void* v, const void* a, con
   int split = dv_split;
   const bool bf16 = in_dtype == KDA_BF16;
   const bool slab = slab_path(dk, bf16, chunk);
-  if (split == 0)
+  // -1: a width per sequence (mixed launch), where the slab kernel runs at dv = 128.
+  const bool force_mixed = dv_split == -1;
+  if (force_mixed && (!slab || dv != 128 || summary))
+    return fail(KDA_EUNSUPPORTED, "dv_split=-1 needs bf16 inputs, chunk 64, dk a multiple of 32 and dv = 128");
+  if (split == 0 || force_mixed)
     split = slab ? choose_split_slab(dv, n_chunks * H, longest) : choose_split(dk, dv, bf16, n_chunks * H, longest);
   if (!valid_tile(dv, split, slab))
     return fail(KDA_EUNSUPPORTED,
@@ -319,7 +323,7 @@ int prefill_impl(const void* q, const void* k, const void* v, const void* a, con
   // per sequence (kda_prefill_slab.hpp, slab_mixed_kernel).
   int64_t n_wg = 0;
   int32_t* wgs = wchunks + 2 * n_chunks;
-  if (slab && !summary && dv == 128 && dv_split == 0) {
+  if (slab && !summary && dv == 128 && (dv_split == 0 || force_mixed)) {
     std::vector<int64_t> sc(n_seqs);
     for (int32_t i = 0; i < n_seqs; ++i) sc[i] = seqinfo[6 * i + 5] - seqinfo[6 * i + 4];
     std::vector<int> width;
@@ -335,7 +339,7 @@ int prefill_impl(const void* q, const void* k, const void* v, const void* a, con
                                 static_cast<double>(total) * H * (128 / uw[j]) * ut[j] / kCUs);
       if (tu == 0 || c < tu) tu = c;
     }
-    if (tm > 0 && tm < 0.97 * tu) {
+    if (tm > 0 && (force_mixed || tm < 0.97 * tu)) {
       for (int64_t g = 0; g < n_chains / 8; ++g) {
         int rounds = 0;
         for (int x = 0; x < 8; ++x) {

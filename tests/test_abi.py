@@ -121,6 +121,11 @@ def test_prefill_validation(L):
     # 128-column tiles: only on the column-slab path (bf16, chunk 64, dk % 32 == 0),
     # where the call then gets as far as the workspace (too small for 4000 tokens).
     assert call(split=1, cu=(0, 4000)) == kda.KDA_EWORKSPACE
+    # A width per sequence (-1) only where the column-slab kernel runs at dv = 128.
+    assert call(split=-1, dv=64) == kda.KDA_EUNSUPPORTED
+    assert call(split=-1, chunk=32) == kda.KDA_EUNSUPPORTED
+    assert call(split=-1, dtype=0, chunk=32) == kda.KDA_EUNSUPPORTED
+    assert call(split=-2) == kda.KDA_EUNSUPPORTED
     assert call(chunk=32, split=1) == kda.KDA_EUNSUPPORTED
     assert call(dk=16, dv=128, split=1) == kda.KDA_EUNSUPPORTED
     assert call(dtype=0, chunk=32, split=1) == kda.KDA_EUNSUPPORTED

@@ -103,6 +103,21 @@ def test_explicit_dv_splits_agree(split):
     _check(w, "bf16", o, sf, pool, slots)
 
 
+def test_mixed_tile_widths():
+    """dv_split = -1: a tile width per sequence in one launch.  With chunk
+    counts 20, 14, 6 and 2 (H = 2, so the total work is small) the cost model
+    gives the longest sequence 32-column tiles, the second 64 and the others
+    one 128-column tile, so every width of the mixed launch runs; checkpoints
+    every 256 tokens keep the chunks whole."""
+    w = inputs.prefill_workload(42, [64 * 20, 64 * 14, 64 * 6, 100], 2, 128, 128, "bf16",
+                                s0_std=0.1, ckpt_every=256)
+    o, sf, pool, slots = _run(w, "bf16", 64, dv_split=-1)
+    _check(w, "bf16", o, sf, pool, slots)
+    o1, sf1, _, _ = _run(w, "bf16", 64, dv_split=1)
+    assert_parity(o, o1.float(), "bf16", "o (mixed widths vs one tile per head)")
+    assert_parity(sf, sf1, "bf16", "s_final (mixed widths vs one tile per head)")
+
+
 def test_zero_state_and_no_final():
     w = inputs.prefill_workload(41, [90], 2, 64, 64, "bf16")
     d = {n: dev_tensor(w[n], "bf16") for n in FIELDS}
