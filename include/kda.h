@@ -178,9 +178,14 @@ int kda_unpack_heads_ex(const void* page_pool, kda_dtype state_dtype, int64_t pa
  *              bf16); fp32 inputs take at most 32 (their operands stay fp32,
  *              split into bf16 high and low parts, so fp32 I/O keeps
  *              fp32-level accuracy)
- *   Log-decays must satisfy a >= -160/chunk per token and channel (a >= -2.5
- *   at chunk 64): the chunk's scaled operands, referenced to the middle row of
- *   the chunk, then stay below e^80 and are finite in bf16 and fp32.
+ *   Log-decays must lie in [-160/chunk, 0] per token and channel ([Serve demo]
+ *   §1.3 bounds a to [g_min, 0]; the lower end is -2.5 at chunk 64, -5 at
+ *   chunk 32): the chunk's scaled operands, referenced to the middle row of
+ *   the chunk, then stay below e^80 and are finite in bf16 and fp32.  The
+ *   first kernel checks every a (a NaN fails the check too); if one is out
+ *   of range it raises *err_flag and the call writes nothing: o, s_final and
+ *   the page slots keep their contents (the [kv_prefix] page's rule that a
+ *   failure never leaves a partial record).
  *   cu_seqlens_host : host int32 [n_seqs + 1]; cu[0] = 0, non-decreasing,
  *              cu[n_seqs] = T_tot.  Zero-length sequences are allowed.
  *   s0       : [n_seqs, H, dk, dv] fp32 committed states, READ ONLY, or NULL
@@ -208,8 +213,13 @@ int kda_unpack_heads_ex(const void* page_pool, kda_dtype state_dtype, int64_t pa
  *                    (T_tot / chunk + n_seqs + n_ckpt) * H * (2 chunk^2 +
  *                    3 chunk dk) * 2 bytes for bf16 (4.3 GB for 128k tokens,
  *                    H = 32, dk = 128, chunk 64).
+ *   err_flag       : device int32, may be NULL; set to 1 when a log-decay is
+ *                    out of range (above); never cleared by the library
  * Sizes: T_tot < 2^31 tokens, H*dk*dv < 2^31, H*max(dk, dv) <= 2^24, and
  * (number of chunks) * H < 2^31.
+ * The work list is copied from pageable host memory into the workspace
+ * (hipMemcpyAsync), so the call may block the host while the runtime stages
+ * those few kilobytes; everything else is enqueued.
  */
 int kda_chunk_prefill_workspace_size(int32_t n_seqs, int64_t total_tokens, int32_t H,
                                      int32_t dk, int32_t dv, int32_t chunk, int64_t n_ckpt,
@@ -222,7 +232,7 @@ int kda_chunk_prefill(const void* q, const void* k, const void* v, const void* a
                       const int32_t* ckpt_cu_host, const int32_t* ckpt_pos_host,
                       const int32_t* ckpt_slot_host, int64_t n_ckpt, float* page_pool,
                       int64_t page_elems, int64_t n_slots, void* workspace,
-                      size_t workspace_bytes, void* stream);
+                      size_t workspace_bytes, int32_t* err_flag, void* stream);
 
 /*
  * kda_chunk_prefill_split — kda_chunk_prefill with an explicit number of
@@ -245,7 +255,22 @@ int kda_chunk_prefill_split(const void* q, const void* k, const void* v, const v
                             const int32_t* ckpt_cu_host, const int32_t* ckpt_pos_host,
                             const int32_t* ckpt_slot_host, int64_t n_ckpt, float* page_pool,
                             int64_t page_elems, int64_t n_slots, void* workspace,
-                            size_t workspace_bytes, int32_t dv_split, void* stream);
+                            size_t workspace_bytes, int32_t dv_split, int32_t* err_flag,
+                            void* stream);
+
+/*
+ * kda_chunk_prefill_plan — what kda_chunk_prefill_split would launch for these
+ * shapes, without launching anything: tile_cols_out [n_seqs] (may be NULL)
+ * receives the dv columns per workgroup of each sequence's chains, and
+ * kernels_out (may be NULL) the NUL-terminated names of the kernels, cut to
+ * kernels_bytes.  Validates the same arguments as the prefill (dtype, sizes,
+ * cu_seqlens, checkpoint offsets and positions) with the same status codes.
+ */
+int kda_chunk_prefill_plan(kda_dtype in_dtype, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
+                           const int32_t* cu_seqlens_host, int32_t n_seqs,
+                           const int32_t* ckpt_cu_host, const int32_t* ckpt_pos_host,
+                           int64_t n_ckpt, int32_t dv_split, int32_t* tile_cols_out,
+                           char* kernels_out, size_t kernels_bytes);
 
 /*
  * kda_chunk_prefill_gated — kda_chunk_prefill_split with the gate fused in
@@ -253,8 +278,10 @@ int kda_chunk_prefill_split(const void* q, const void* k, const void* v, const v
  * z_a [T_tot, H, dk] and z_b [T_tot, H] (in_dtype) are gate logits, and the
  * prefill uses a = g_min * sigmoid(z_a), beta = sigmoid(z_b) ([Serve demo]
  * §1.3), computed in fp32 as the logits are loaded.  g_min finite and <= 0.
- * The decay bound of kda_chunk_prefill applies to the gated a (it holds for
- * g_min >= -160/chunk).  Everything else is as for kda_chunk_prefill_split.
+ * The decay bound of kda_chunk_prefill applies to the gated a: g_min below
+ * -160/chunk is refused (KDA_EUNSUPPORTED), and a logit that makes a NaN
+ * raises *err_flag as for kda_chunk_prefill.  Everything else is as for
+ * kda_chunk_prefill_split.
  */
 int kda_chunk_prefill_gated(const void* q, const void* k, const void* v, const void* z_a,
                             const void* z_b, float g_min, kda_dtype in_dtype, int32_t H,
@@ -263,7 +290,8 @@ int kda_chunk_prefill_gated(const void* q, const void* k, const void* v, const v
                             const int32_t* ckpt_cu_host, const int32_t* ckpt_pos_host,
                             const int32_t* ckpt_slot_host, int64_t n_ckpt, float* page_pool,
                             int64_t page_elems, int64_t n_slots, void* workspace,
-                            size_t workspace_bytes, int32_t dv_split, void* stream);
+                            size_t workspace_bytes, int32_t dv_split, int32_t* err_flag,
+                            void* stream);
 
 /*
  * Segment summaries for context-parallel prefill ([Serve demo] §7.2 "KCP 前缀扫描",
@@ -278,8 +306,8 @@ int kda_chunk_prefill_gated(const void* q, const void* k, const void* v, const v
  *   A_out : [n_seg, H, dk, dk] fp32, the linear part (identity for an empty segment)
  *   B_out : [n_seg, H, dk, dv] fp32, the end state from the zero start state
  *   workspace : at least kda_segment_summary_workspace_size bytes, 256-byte aligned
- * chunk, the decay bound, dtypes and size limits are those of kda_chunk_prefill
- * (same chunk form: B is the prefill's final state from s0 = 0, and A is the
+ * chunk, the decay bound (here a precondition: the summary does not check
+ * it), dtypes and size limits are those of kda_chunk_prefill (same chunk form: B is the prefill's final state from s0 = 0, and A is the
  * same propagation run from the identity with v = 0), plus H*dk*dk < 2^31.
  * Outputs must not overlap the inputs or each other (KDA_EALIAS).
  */

@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cmath>
 #include <numeric>
+#include <string>
 #include <unordered_set>
 #include <vector>
 
@@ -26,44 +27,68 @@ int64_t max_chunks(int32_t n_seqs, int64_t total_tokens, int32_t chunk, int64_t 
   return total_tokens / chunk + n_seqs + n_ckpt;
 }
 
-// Workspace: the int32 work list (chains, sequence table, checkpoints,
-// chunks, and room for a mixed-width workgroup list of up to four entries
-// per chain), then (256-byte aligned) one record per
+// Workspace: the int32 work list (a header of kHeaderInts words whose first
+// is the decay-range flag, zero on entry; chains, sequence table,
+// checkpoints, chunks, and room for a mixed-width workgroup list of up to
+// four entries per chain), then (256-byte aligned) one record per
 // (chunk, head) (UnitLayout: T diag(beta), lower(A_qk) and the chunk's scaled
 // operands, in the operand precision: bf16 for bf16 inputs, fp32 for fp32).
+constexpr int64_t kHeaderInts = 64;
 size_t work_ints(int32_t n_seqs, int32_t H, int64_t n_ckpt, int64_t n_chunks) {
-  return static_cast<size_t>(2 * round8(static_cast<int64_t>(n_seqs) * H) + 6 * n_seqs + 2 * n_ckpt +
-                             2 * n_chunks + 4 * round8(static_cast<int64_t>(n_seqs) * H));
+  return static_cast<size_t>(kHeaderInts + 2 * round8(static_cast<int64_t>(n_seqs) * H) + 6 * n_seqs +
+                             2 * n_ckpt + 2 * n_chunks + 4 * round8(static_cast<int64_t>(n_seqs) * H));
 }
 
 // Per-sequence tile widths for the column-slab prefill at dv = 128 (32, 64
 // or 128 columns), from per-chunk times measured with every CU busy: the
 // widest width whose chain fits a target time, the target chosen to balance
-// the longest chain against the total work over the CUs.  Returns the
-// predicted time (us) and fills width[s]; 0 if a single width is as good.
+// the longest chain against the total work over the CUs.  The candidate
+// targets are the chains' own times at each width; with the chunk counts
+// sorted and summed once, each candidate costs two binary searches, so the
+// choice is O(n log n) in the number of sequences.  Returns the predicted
+// time (us) and fills width[s].
 double choose_widths(const std::vector<int64_t>& chunks, int32_t H, std::vector<int>& width) {
-  const int ws[3] = {128, 64, 32};
-  const double tw[3] = {3.8, 2.5, 2.0};
-  double best = 0;
-  std::vector<int> cur(chunks.size());
-  for (size_t cand = 0; cand < chunks.size() * 3; ++cand) {
-    const double T = static_cast<double>(chunks[cand / 3]) * tw[cand % 3];
-    double work = 0;
-    for (size_t s = 0; s < chunks.size(); ++s) {
-      int k = 2;
-      for (int j = 0; j < 3; ++j)
-        if (static_cast<double>(chunks[s]) * tw[j] <= T) { k = j; break; }
-      cur[s] = ws[k];
-      work += static_cast<double>(H) * (128 / ws[k]) * static_cast<double>(chunks[s]) * tw[k];
+  constexpr int ws[3] = {128, 64, 32};
+  constexpr double tw[3] = {3.8, 2.5, 2.0};
+  constexpr double mult[3] = {1, 2, 4};  // tiles per head
+  const size_t n = chunks.size();
+  std::vector<int64_t> c(chunks);
+  std::sort(c.begin(), c.end());
+  std::vector<double> pre(n + 1, 0.0);
+  for (size_t i = 0; i < n; ++i) pre[i + 1] = pre[i] + static_cast<double>(c[i]);
+  // Sequences [0, i_j) of the sorted list fit the target T at width j.
+  auto fits = [&](int j, double T) {
+    return static_cast<size_t>(std::partition_point(c.begin(), c.end(), [&](int64_t x) {
+                                 return static_cast<double>(x) * tw[j] <= T;
+                               }) - c.begin());
+  };
+  double best = 0, best_T = 0;
+  for (size_t i = 0; i < n; ++i) {
+    if (i > 0 && c[i] == c[i - 1]) continue;
+    for (int j = 0; j < 3; ++j) {
+      const double T = static_cast<double>(c[i]) * tw[j];
+      const size_t i0 = fits(0, T), i1 = std::max(i0, fits(1, T));
+      const double work = H * (mult[0] * tw[0] * pre[i0] + mult[1] * tw[1] * (pre[i1] - pre[i0]) +
+                               mult[2] * tw[2] * (pre[n] - pre[i1]));
+      double longest = 0;
+      if (i0 > 0) longest = std::max(longest, static_cast<double>(c[i0 - 1]) * tw[0]);
+      if (i1 > i0) longest = std::max(longest, static_cast<double>(c[i1 - 1]) * tw[1]);
+      if (n > i1) longest = std::max(longest, static_cast<double>(c[n - 1]) * tw[2]);
+      const double cost = std::max(longest, work / kCUs);
+      // On a tie the larger target wins: wider tiles, less total work.
+      if (best == 0 || cost < best * (1 - 1e-12) || (cost <= best * (1 + 1e-12) && T > best_T)) {
+        best = std::min(best == 0 ? cost : best, cost);
+        best_T = T;
+      }
     }
-    double longest = 0;
-    for (size_t s = 0; s < chunks.size(); ++s) {
-      const int k = cur[s] == 128 ? 0 : cur[s] == 64 ? 1 : 2;
-      longest = std::max(longest, static_cast<double>(chunks[s]) * tw[k]);
-    }
-    const double cost = std::max(longest, work / kCUs);
-    if (best == 0 || cost < best) { best = cost; width = cur; }
   }
+  width.assign(n, 32);
+  for (size_t s = 0; s < n; ++s)
+    for (int j = 0; j < 3; ++j)
+      if (static_cast<double>(chunks[s]) * tw[j] <= best_T) {
+        width[s] = ws[j];
+        break;
+      }
   return best;
 }
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -140,18 +165,20 @@ int choose_split_slab(int32_t dv, int64_t total_chunks, int64_t longest) {
   return best;
 }
 
-// Prefill (a_out == nullptr) or segment summaries (a_out != nullptr: q is
-// unused, o and s0 are null and s_final receives B; see kda_segment_summary).
-int prefill_impl(const void* q, const void* k, const void* v, const void* a, const void* beta,
-                 kda_dtype in_dtype, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
-                 const int32_t* cu, int32_t n_seqs, const float* s0, void* o, float* s_final,
-                 const int32_t* ck_cu, const int32_t* ck_pos, const int32_t* ck_slot,
-                 int64_t n_ckpt, float* page_pool, int64_t page_elems, int64_t n_slots,
-                 void* workspace, size_t workspace_bytes, int32_t dv_split, float* a_out,
-                 void* stream, bool gate = false, float g_min = 0.f) {
-  const bool summary = a_out != nullptr;
-  if (gate && (!std::isfinite(g_min) || g_min > 0.f))
-    return fail(KDA_EINVAL, "g_min must be finite and <= 0");
+// What a call will launch: validated shapes and offsets, chunk counts, the
+// dv split and (mixed launch) a tile width per sequence.
+struct Plan {
+  int64_t n_chunks = 0, longest = 0;
+  int split = 0, a_split = 0;
+  bool slab = false, mixed = false;
+  std::vector<int> width;  // columns per workgroup, per sequence
+};
+
+// Validates everything the plan depends on (dtype, sizes, cu_seqlens,
+// checkpoint offsets and positions; not buffers or slots) and makes the plan.
+int make_plan(kda_dtype in_dtype, int32_t H, int32_t dk, int32_t dv, int32_t chunk, const int32_t* cu,
+              int32_t n_seqs, const int32_t* ck_cu, const int32_t* ck_pos, int64_t n_ckpt, int32_t dv_split,
+              bool summary, Plan& pl) {
   if (!valid_dtype(in_dtype)) return fail(KDA_EINVAL, "in_dtype %d", static_cast<int>(in_dtype));
   if (n_seqs < 0 || H <= 0 || n_ckpt < 0)
     return fail(KDA_EINVAL, "n_seqs=%d H=%d n_ckpt=%lld", n_seqs, H, static_cast<long long>(n_ckpt));
@@ -168,21 +195,23 @@ int prefill_impl(const void* q, const void* k, const void* v, const void* a, con
   // The kernel addresses one chunk's rows with 32-bit byte offsets.
   if (static_cast<int64_t>(H) * std::max(dk, dv) > (int64_t{1} << 24))
     return fail(KDA_EUNSUPPORTED, "H*max(dk, dv) must be at most 2^24");
-  if (n_seqs == 0) return ok();
-  if (!cu) return fail(KDA_EINVAL, "cu_seqlens is null");
-  if (cu[0] != 0) return fail(KDA_EINVAL, "cu_seqlens[0] = %d, must be 0", cu[0]);
-  for (int32_t i = 0; i < n_seqs; ++i)
-    if (cu[i + 1] < cu[i]) return fail(KDA_EINVAL, "cu_seqlens decreases at %d", i);
-  const int64_t T = cu[n_seqs];
+  if (n_seqs > 0) {
+    if (!cu) return fail(KDA_EINVAL, "cu_seqlens is null");
+    if (cu[0] != 0) return fail(KDA_EINVAL, "cu_seqlens[0] = %d, must be 0", cu[0]);
+    for (int32_t i = 0; i < n_seqs; ++i)
+      if (cu[i + 1] < cu[i]) return fail(KDA_EINVAL, "cu_seqlens decreases at %d", i);
+  }
 
-  // Checkpoints.
-  if (n_ckpt > 0 && (!ck_cu || !ck_pos || !ck_slot || !page_pool))
-    return fail(KDA_EINVAL, "checkpoints need ckpt_cu, ckpt_pos, ckpt_slot and page_pool");
-  if (ck_cu) {
-    if (ck_cu[0] != 0 || ck_cu[n_seqs] != n_ckpt)
-      return fail(KDA_EINVAL, "ckpt_cu must start at 0 and end at n_ckpt");
+  // Checkpoints: the offsets first (all of them, so that no position is read
+  // through an offset a later entry would have refused), then the positions.
+  if (n_ckpt > 0 && (!ck_cu || !ck_pos)) return fail(KDA_EINVAL, "checkpoints need ckpt_cu and ckpt_pos");
+  if (ck_cu && n_seqs > 0) {
+    if (ck_cu[0] != 0) return fail(KDA_EINVAL, "ckpt_cu must start at 0");
+    for (int32_t i = 0; i < n_seqs; ++i)
+      if (ck_cu[i + 1] < ck_cu[i] || ck_cu[i + 1] > n_ckpt)
+        return fail(KDA_EINVAL, "ckpt_cu must be non-decreasing and at most n_ckpt (entry %d)", i + 1);
+    if (ck_cu[n_seqs] != n_ckpt) return fail(KDA_EINVAL, "ckpt_cu must end at n_ckpt");
     for (int32_t i = 0; i < n_seqs; ++i) {
-      if (ck_cu[i + 1] < ck_cu[i]) return fail(KDA_EINVAL, "ckpt_cu decreases at %d", i);
       const int32_t len = cu[i + 1] - cu[i];
       for (int32_t c = ck_cu[i]; c < ck_cu[i + 1]; ++c) {
         if (ck_pos[c] < 1 || ck_pos[c] > len)
@@ -195,6 +224,111 @@ int prefill_impl(const void* q, const void* k, const void* v, const void* a, con
   } else if (n_ckpt != 0) {
     return fail(KDA_EINVAL, "n_ckpt > 0 without ckpt_cu");
   }
+
+  // Chunks and split.
+  pl = Plan{};
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    const int32_t len = cu[i + 1] - cu[i];
+    const int32_t c0 = ck_cu ? ck_cu[i] : 0, c1 = ck_cu ? ck_cu[i + 1] : 0;
+    const int64_t c = seq_chunks(len, ck_pos ? ck_pos + c0 : nullptr, c1 - c0, chunk);
+    pl.n_chunks += c;
+    pl.longest = std::max(pl.longest, c);
+  }
+  if (pl.n_chunks * H >= (int64_t{1} << 31)) return fail(KDA_EUNSUPPORTED, "too many (chunk, head) pairs");
+  const bool bf16 = in_dtype == KDA_BF16;
+  pl.slab = slab_path(dk, bf16, chunk);
+  // -1: a width per sequence (mixed launch), where the slab kernel runs at dv = 128.
+  const bool force_mixed = dv_split == -1;
+  if (force_mixed && (!pl.slab || dv != 128 || summary))
+    return fail(KDA_EUNSUPPORTED, "dv_split=-1 needs bf16 inputs, chunk 64, dk a multiple of 32 and dv = 128");
+  pl.split = dv_split;
+  if (pl.split == 0 || force_mixed)
+    pl.split = pl.slab ? choose_split_slab(dv, pl.n_chunks * H, pl.longest)
+                       : choose_split(dk, dv, bf16, pl.n_chunks * H, pl.longest);
+  if (!valid_tile(dv, pl.split, pl.slab))
+    return fail(KDA_EUNSUPPORTED, "dv_split=%d with dv=%d (dv/split must be 16, 32 or 64%s)", dv_split, dv,
+                pl.slab ? ", or 128" : "");
+  const int64_t n_chains = round8(static_cast<int64_t>(n_seqs) * H);
+  if (n_chains * pl.split >= (int64_t{1} << 31)) return fail(KDA_EUNSUPPORTED, "too many chains");
+  // The linear part A of a summary propagates dk identity columns.
+  pl.a_split = !summary ? 0 : pl.slab ? choose_split_slab(dk, pl.n_chunks * H, pl.longest)
+                                      : choose_split(dk, dk, bf16, pl.n_chunks * H, pl.longest);
+  pl.width.assign(n_seqs, dv / pl.split);
+
+  // Mixed tile widths: at dv = 128 on the slab path (prefill, automatic
+  // split), when the per-sequence widths predict a time 3 % or more below
+  // the single width's, the propagation runs one workgroup list with a width
+  // per sequence (kda_prefill_slab.hpp, slab_mixed_kernel).  Its entries
+  // pack the chain index above 8 bits, so it needs fewer than 2^23 chains.
+  if (pl.slab && !summary && dv == 128 && (dv_split == 0 || force_mixed) && n_seqs > 0 &&
+      n_chains < (int64_t{1} << 23)) {
+    std::vector<int64_t> sc(n_seqs);
+    int64_t total = 0;
+    for (int32_t i = 0; i < n_seqs; ++i) {
+      const int32_t c0 = ck_cu ? ck_cu[i] : 0, c1 = ck_cu ? ck_cu[i + 1] : 0;
+      sc[i] = seq_chunks(cu[i + 1] - cu[i], ck_pos ? ck_pos + c0 : nullptr, c1 - c0, chunk);
+      total += sc[i];
+    }
+    std::vector<int> width;
+    const double tm = choose_widths(sc, H, width);
+    // The best single width by the same per-chunk times (16 columns: 1.95 us).
+    double tu = 0;
+    const int uw[4] = {16, 32, 64, 128};
+    const double ut[4] = {1.95, 2.0, 2.5, 3.8};
+    for (int j = 0; j < 4; ++j) {
+      const double c = std::max(static_cast<double>(pl.longest) * ut[j],
+                                static_cast<double>(total) * H * (128 / uw[j]) * ut[j] / kCUs);
+      if (tu == 0 || c < tu) tu = c;
+    }
+    if (tm > 0 && (force_mixed || tm < 0.97 * tu)) {
+      pl.mixed = true;
+      pl.width = width;
+    }
+  }
+  return KDA_OK;
+}
+
+// Names of the kernels a plan launches (for reports).
+std::string plan_kernels(const Plan& pl, kda_dtype in_dtype, int32_t dk, int32_t dv, bool gate) {
+  const char* t = in_dtype == KDA_BF16 ? "bf16" : "fp32";
+  char buf[256];
+  const std::string local = std::string("local_kernel<") + std::to_string(dk) + "," + t + (gate ? ",gated" : "") + ">";
+  if (pl.mixed)
+    snprintf(buf, sizeof(buf), "%s + slab_mixed_kernel<%d> (a tile width per sequence)", local.c_str(), dk);
+  else if (pl.slab)
+    snprintf(buf, sizeof(buf), "%s + slab_kernel<%d> (%d-column tiles)", local.c_str(), dk, dv / pl.split);
+  else
+    snprintf(buf, sizeof(buf), "%s + prop_kernel<%d,%d,%s>", local.c_str(), dk, dv / pl.split, t);
+  return buf;
+}
+
+// Prefill (a_out == nullptr) or segment summaries (a_out != nullptr: q is
+// unused, o and s0 are null and s_final receives B; see kda_segment_summary).
+int prefill_impl(const void* q, const void* k, const void* v, const void* a, const void* beta,
+                 kda_dtype in_dtype, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
+                 const int32_t* cu, int32_t n_seqs, const float* s0, void* o, float* s_final,
+                 const int32_t* ck_cu, const int32_t* ck_pos, const int32_t* ck_slot,
+                 int64_t n_ckpt, float* page_pool, int64_t page_elems, int64_t n_slots,
+                 void* workspace, size_t workspace_bytes, int32_t dv_split, float* a_out,
+                 int32_t* err_flag, void* stream, bool gate = false, float g_min = 0.f) {
+  const bool summary = a_out != nullptr;
+  Plan pl;
+  int st = make_plan(in_dtype, H, dk, dv, chunk, cu, n_seqs, ck_cu, ck_pos, n_ckpt, dv_split, summary, pl);
+  if (st) return st;
+  // The decay bound of the chunk form ([Serve demo] §1.3 bounds a to
+  // [g_min, 0]): a >= -160/chunk keeps every scaled operand below e^80.
+  const float a_lo = -160.f / static_cast<float>(chunk);
+  if (gate && (!std::isfinite(g_min) || g_min > 0.f))
+    return fail(KDA_EINVAL, "g_min must be finite and <= 0");
+  if (gate && g_min < a_lo)
+    return fail(KDA_EUNSUPPORTED, "g_min=%g below the decay bound -160/chunk = %g", g_min, a_lo);
+  if (n_seqs == 0) return ok();
+  const int64_t T = cu[n_seqs];
+  const int64_t hkv = static_cast<int64_t>(H) * dk * dv;
+  const int64_t hkk = static_cast<int64_t>(H) * dk * dk;
+
+  if (n_ckpt > 0 && (!ck_slot || !page_pool))
+    return fail(KDA_EINVAL, "checkpoints need ckpt_slot and page_pool");
   if (n_ckpt > 0) {
     if (page_elems < hkv) return fail(KDA_EINVAL, "page_elems %lld < H*dk*dv %lld",
                                       static_cast<long long>(page_elems), static_cast<long long>(hkv));
@@ -207,33 +341,6 @@ int prefill_impl(const void* q, const void* k, const void* v, const void* a, con
     }
   }
 
-  // Split.
-  int64_t n_chunks = 0, longest = 0;
-  for (int32_t i = 0; i < n_seqs; ++i) {
-    const int32_t len = cu[i + 1] - cu[i];
-    const int32_t c0 = ck_cu ? ck_cu[i] : 0, c1 = ck_cu ? ck_cu[i + 1] : 0;
-    const int64_t c = seq_chunks(len, ck_pos ? ck_pos + c0 : nullptr, c1 - c0, chunk);
-    n_chunks += c;
-    longest = std::max(longest, c);
-  }
-  if (n_chunks * H >= (int64_t{1} << 31)) return fail(KDA_EUNSUPPORTED, "too many (chunk, head) pairs");
-  int split = dv_split;
-  const bool bf16 = in_dtype == KDA_BF16;
-  const bool slab = slab_path(dk, bf16, chunk);
-  // -1: a width per sequence (mixed launch), where the slab kernel runs at dv = 128.
-  const bool force_mixed = dv_split == -1;
-  if (force_mixed && (!slab || dv != 128 || summary))
-    return fail(KDA_EUNSUPPORTED, "dv_split=-1 needs bf16 inputs, chunk 64, dk a multiple of 32 and dv = 128");
-  if (split == 0 || force_mixed)
-    split = slab ? choose_split_slab(dv, n_chunks * H, longest) : choose_split(dk, dv, bf16, n_chunks * H, longest);
-  if (!valid_tile(dv, split, slab))
-    return fail(KDA_EUNSUPPORTED,
-                "dv_split=%d with dv=%d (dv/split must be 16, 32 or 64%s)",
-                dv_split, dv, slab ? ", or 128" : "");
-  // The linear part A of a summary propagates dk identity columns.
-  const int a_split = !summary ? 0 : slab ? choose_split_slab(dk, n_chunks * H, longest)
-                                         : choose_split(dk, dk, bf16, n_chunks * H, longest);
-
   // Buffers.
   const size_t es = elem_size(in_dtype);
   if (summary && (!s_final || (n_seqs > 0 && !a_out))) return fail(KDA_EINVAL, "A_out and B_out must not be null");
@@ -245,6 +352,8 @@ int prefill_impl(const void* q, const void* k, const void* v, const void* a, con
       return fail(KDA_EINVAL, "q, k, v, a must be aligned to two elements");
   // Output rows are written in 16-byte pieces.
   if (!summary && reinterpret_cast<uintptr_t>(o) % 16) return fail(KDA_EINVAL, "o must be 16-byte aligned");
+  if (err_flag && reinterpret_cast<uintptr_t>(err_flag) % 4) return fail(KDA_EINVAL, "err_flag must be aligned");
+  const int64_t n_chunks = pl.n_chunks;
   const size_t list_bytes = align256(work_ints(n_seqs, H, n_ckpt, n_chunks) * 4);
   const size_t need = list_bytes + tile_bytes(n_chunks, H, chunk, dk, es);
   if (!workspace || workspace_bytes < need)
@@ -260,8 +369,8 @@ int prefill_impl(const void* q, const void* k, const void* v, const void* a, con
       {o, summary ? 0 : tok * dv * es, "o"}, {s_final, s_final ? sbytes : 0, summary ? "B_out" : "s_final"},
       {a_out, summary ? static_cast<size_t>(n_seqs) * hkk * 4 : 0, "A_out"},
       {page_pool, n_ckpt > 0 ? static_cast<size_t>(n_slots) * page_elems * 4 : 0, "page_pool"},
-      {workspace, need, "workspace"}};
-  int st = check_disjoint(outs, ins);
+      {workspace, need, "workspace"}, {err_flag, err_flag ? 4u : 0u, "err_flag"}};
+  st = check_disjoint(outs, ins);
   if (st) return st;
 
   // Work list: chains longest sequence first, padded to whole XCD rounds.
@@ -271,9 +380,9 @@ int prefill_impl(const void* q, const void* k, const void* v, const void* a, con
     return cu[x + 1] - cu[x] > cu[y + 1] - cu[y];
   });
   const int64_t n_chains = round8(static_cast<int64_t>(n_seqs) * H);
-  if (n_chains * split >= (int64_t{1} << 31)) return fail(KDA_EUNSUPPORTED, "too many chains");
+  const int split = pl.split;
   std::vector<int32_t> work(work_ints(n_seqs, H, n_ckpt, n_chunks), 0);
-  int32_t* chains = work.data();
+  int32_t* chains = work.data() + kHeaderInts;  // work[0]: the decay-range flag, 0
   int32_t* seqinfo = chains + 2 * n_chains;
   int32_t* wpos = seqinfo + 6 * n_seqs;
   int32_t* wslot = wpos + n_ckpt;
@@ -317,65 +426,52 @@ int prefill_impl(const void* q, const void* k, const void* v, const void* a, con
     wslot[i] = ck_slot[i];
   }
 
-  // Mixed tile widths: at dv = 128 on the slab path (prefill, automatic
-  // split), when the per-sequence widths predict a time 3 % or more below
-  // the single width's, the propagation runs one workgroup list with a width
-  // per sequence (kda_prefill_slab.hpp, slab_mixed_kernel).
+  // Mixed launch: one entry per workgroup, chain << 8 | width code << 4 |
+  // tile, the tiles of 8 neighbouring chains in rounds so that a chain's tiles
+  // share an XCD.
   int64_t n_wg = 0;
   int32_t* wgs = wchunks + 2 * n_chunks;
-  if (slab && !summary && dv == 128 && (dv_split == 0 || force_mixed)) {
-    std::vector<int64_t> sc(n_seqs);
-    for (int32_t i = 0; i < n_seqs; ++i) sc[i] = seqinfo[6 * i + 5] - seqinfo[6 * i + 4];
-    std::vector<int> width;
-    const double tm = choose_widths(sc, H, width);
-    int64_t longest = 0, total = 0;
-    for (int64_t x : sc) { longest = std::max(longest, x); total += x; }
-    // The best single width by the same per-chunk times (16 columns: 1.95 us).
-    double tu = 0;
-    const int uw[4] = {16, 32, 64, 128};
-    const double ut[4] = {1.95, 2.0, 2.5, 3.8};
-    for (int j = 0; j < 4; ++j) {
-      const double c = std::max(static_cast<double>(longest) * ut[j],
-                                static_cast<double>(total) * H * (128 / uw[j]) * ut[j] / kCUs);
-      if (tu == 0 || c < tu) tu = c;
-    }
-    if (tm > 0 && (force_mixed || tm < 0.97 * tu)) {
-      for (int64_t g = 0; g < n_chains / 8; ++g) {
-        int rounds = 0;
-        for (int x = 0; x < 8; ++x) {
-          const int32_t sq = chains[2 * (8 * g + x)];
-          if (sq >= 0) rounds = std::max(rounds, 128 / width[sq]);
-        }
-        for (int r = 0; r < rounds; ++r)
-          for (int x = 0; x < 8; ++x) {
-            const int64_t ch = 8 * g + x;
-            const int32_t sq = chains[2 * ch];
-            const int w = sq >= 0 ? width[sq] : 0;
-            const int code = w == 32 ? 0 : w == 64 ? 1 : 2;
-            wgs[n_wg++] = (sq >= 0 && r < 128 / w) ? static_cast<int32_t>((ch << 8) | (code << 4) | r)
-                                                   : static_cast<int32_t>((ch << 8) | (15 << 4));
-          }
+  if (pl.mixed) {
+    for (int64_t g = 0; g < n_chains / 8; ++g) {
+      int rounds = 0;
+      for (int x = 0; x < 8; ++x) {
+        const int32_t sq = chains[2 * (8 * g + x)];
+        if (sq >= 0) rounds = std::max(rounds, 128 / pl.width[sq]);
       }
+      for (int r = 0; r < rounds; ++r)
+        for (int x = 0; x < 8; ++x) {
+          const int64_t ch = 8 * g + x;
+          const int32_t sq = chains[2 * ch];
+          const int w = sq >= 0 ? pl.width[sq] : 0;
+          const int code = w == 32 ? 0 : w == 64 ? 1 : 2;
+          wgs[n_wg++] = (sq >= 0 && r < 128 / w) ? static_cast<int32_t>((ch << 8) | (code << 4) | r)
+                                                 : static_cast<int32_t>((ch << 8) | (15 << 4));
+        }
     }
   }
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  // Pageable source: the runtime has consumed it when the call returns.
+  // The work list is staged in pageable host memory: the runtime copies it
+  // before hipMemcpyAsync returns (so the call may block the host for that
+  // copy, a few KB), and the vector may then go.
   hipError_t e = hipMemcpyAsync(workspace, work.data(), work.size() * 4, hipMemcpyHostToDevice, hs);
   if (e != hipSuccess) return hip_status(e, "work list copy");
 
-  const int32_t* dwork = static_cast<const int32_t*>(workspace);
+  int32_t* dwork = static_cast<int32_t*>(workspace);
   kda::PrefillArgs p{};
   p.q = q; p.k = k; p.v = v; p.a = a; p.beta = beta;
   p.bf16 = in_dtype == KDA_BF16;
   p.gate = gate;
-  p.slab = slab;
+  p.slab = pl.slab;
   p.g_min = g_min;
   p.H = H; p.dk = dk; p.dv = dv; p.chunk = chunk;
   p.s0 = s0; p.o = o; p.s_final = s_final;
   p.page_pool = page_pool; p.page_elems = page_elems;
-  p.chains = dwork;
-  p.seqinfo = dwork + 2 * n_chains;
+  p.wsflag = dwork;
+  p.err_flag = err_flag;
+  p.a_lo = a_lo;
+  p.chains = dwork + kHeaderInts;
+  p.seqinfo = p.chains + 2 * n_chains;
   p.ck_pos = p.seqinfo + 6 * n_seqs;
   p.ck_slot = p.ck_pos + n_ckpt;
   p.chunks = p.ck_slot + n_ckpt;
@@ -386,7 +482,7 @@ int prefill_impl(const void* q, const void* k, const void* v, const void* a, con
   p.wgs = p.chunks + 2 * n_chunks;
   p.n_wg = static_cast<int>(n_wg);
   p.stream = hs;
-  if (summary) return hip_status(kda::launch_segment_summary(p, a_out, a_split), "segment summary launch");
+  if (summary) return hip_status(kda::launch_segment_summary(p, a_out, pl.a_split), "segment summary launch");
   return hip_status(kda::launch_prefill(p), "prefill launch");
 }
 
@@ -411,6 +507,23 @@ int kda_chunk_prefill_workspace_size(int32_t n_seqs, int64_t total_tokens, int32
   return ok();
 }
 
+int kda_chunk_prefill_plan(kda_dtype in_dtype, int32_t H, int32_t dk, int32_t dv, int32_t chunk,
+                           const int32_t* cu_seqlens_host, int32_t n_seqs, const int32_t* ckpt_cu_host,
+                           const int32_t* ckpt_pos_host, int64_t n_ckpt, int32_t dv_split,
+                           int32_t* tile_cols_out, char* kernels_out, size_t kernels_bytes) {
+  Plan pl;
+  const int st = make_plan(in_dtype, H, dk, dv, chunk, cu_seqlens_host, n_seqs, ckpt_cu_host, ckpt_pos_host,
+                           n_ckpt, dv_split, false, pl);
+  if (st) return st;
+  if (tile_cols_out)
+    for (int32_t i = 0; i < n_seqs; ++i) tile_cols_out[i] = pl.width[i];
+  if (kernels_out && kernels_bytes > 0) {
+    const std::string k = plan_kernels(pl, in_dtype, dk, dv, false);
+    snprintf(kernels_out, kernels_bytes, "%s", k.c_str());
+  }
+  return ok();
+}
+
 int kda_chunk_prefill_split(const void* q, const void* k, const void* v, const void* a,
                             const void* beta, kda_dtype in_dtype, int32_t H, int32_t dk,
                             int32_t dv, int32_t chunk, const int32_t* cu, int32_t n_seqs,
@@ -418,10 +531,10 @@ int kda_chunk_prefill_split(const void* q, const void* k, const void* v, const v
                             const int32_t* ck_pos, const int32_t* ck_slot, int64_t n_ckpt,
                             float* page_pool, int64_t page_elems, int64_t n_slots,
                             void* workspace, size_t workspace_bytes, int32_t dv_split,
-                            void* stream) {
+                            int32_t* err_flag, void* stream) {
   return prefill_impl(q, k, v, a, beta, in_dtype, H, dk, dv, chunk, cu, n_seqs, s0, o, s_final,
                       ck_cu, ck_pos, ck_slot, n_ckpt, page_pool, page_elems, n_slots, workspace,
-                      workspace_bytes, dv_split, nullptr, stream);
+                      workspace_bytes, dv_split, nullptr, err_flag, stream);
 }
 
 int kda_chunk_prefill(const void* q, const void* k, const void* v, const void* a,
@@ -430,11 +543,11 @@ int kda_chunk_prefill(const void* q, const void* k, const void* v, const void* a
                       const float* s0, void* o, float* s_final, const int32_t* ckpt_cu_host,
                       const int32_t* ckpt_pos_host, const int32_t* ckpt_slot_host, int64_t n_ckpt,
                       float* page_pool, int64_t page_elems, int64_t n_slots, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+                      size_t workspace_bytes, int32_t* err_flag, void* stream) {
   return kda_chunk_prefill_split(q, k, v, a, beta, in_dtype, H, dk, dv, chunk, cu_seqlens_host,
                                  n_seqs, s0, o, s_final, ckpt_cu_host, ckpt_pos_host,
                                  ckpt_slot_host, n_ckpt, page_pool, page_elems, n_slots, workspace,
-                                 workspace_bytes, 0, stream);
+                                 workspace_bytes, 0, err_flag, stream);
 }
 
 int kda_chunk_prefill_gated(const void* q, const void* k, const void* v, const void* z_a,
@@ -444,10 +557,10 @@ int kda_chunk_prefill_gated(const void* q, const void* k, const void* v, const v
                             const int32_t* ck_pos, const int32_t* ck_slot, int64_t n_ckpt,
                             float* page_pool, int64_t page_elems, int64_t n_slots,
                             void* workspace, size_t workspace_bytes, int32_t dv_split,
-                            void* stream) {
+                            int32_t* err_flag, void* stream) {
   return prefill_impl(q, k, v, z_a, z_b, in_dtype, H, dk, dv, chunk, cu, n_seqs, s0, o, s_final,
                       ck_cu, ck_pos, ck_slot, n_ckpt, page_pool, page_elems, n_slots, workspace,
-                      workspace_bytes, dv_split, nullptr, stream, true, g_min);
+                      workspace_bytes, dv_split, nullptr, err_flag, stream, true, g_min);
 }
 
 int kda_segment_summary_workspace_size(int32_t n_seg, int64_t total_tokens, int32_t H, int32_t dk,
@@ -465,7 +578,7 @@ int kda_segment_summary(const void* k, const void* v, const void* a, const void*
   // The summary kernels read no q: the local kernel is handed k in its place.
   return prefill_impl(k, k, v, a, beta, in_dtype, H, dk, dv, chunk, cu_seg_host, n_seg, nullptr,
                       nullptr, B_out, nullptr, nullptr, nullptr, 0, nullptr, 0, 0, workspace,
-                      workspace_bytes, 0, A_out, stream);
+                      workspace_bytes, 0, A_out, nullptr, stream);
 }
 
 }  // extern "C"

@@ -91,6 +91,13 @@ struct PrefillArgs {
   int dv_tiles;  // workgroups per chain (split of dv)
   const int32_t* wgs;  // mixed tile widths (slab prefill): [n_wg] entries (slab_mixed_kernel), or n_wg = 0
   int n_wg;
+  // Decay range: the local kernel raises *wsflag (a word of the workspace,
+  // zero on entry) and *err_flag (the caller's, or null) when a log-decay lies
+  // outside [a_lo, 0] or is not a number; the prefill's propagation then
+  // writes nothing.
+  int32_t* wsflag;
+  int32_t* err_flag;
+  float a_lo;
   hipStream_t stream;
 };
 hipError_t launch_prefill(const PrefillArgs& p);

@@ -268,6 +268,9 @@ struct LocalParams {
   const int32_t* chunks;   // [n_chunks][2] = (first token, rows)
   void* tq;                // [n_chunks][H] unit records (UnitLayout)
   int H, ld;
+  int32_t* wsflag;         // raised (with *err_flag when not null) on a decay outside [a_lo, 0]
+  int32_t* err_flag;
+  float a_lo;
 };
 
 struct PropParams {
@@ -284,6 +287,7 @@ struct PropParams {
   const int32_t* ck_slot;  // [n_ckpt]
   const int32_t* chunks;   // [n_chunks][2]
   const int32_t* wgs;      // per-workgroup (chain, width, tile) of the mixed-width slab launch
+  const int32_t* wsflag;   // nonzero: a decay was out of range, the prefill writes nothing
   int H, dv, ld, dv_tiles;
 };
 
@@ -418,6 +422,7 @@ __global__ __launch_bounds__(64 * NW, 2) void local_kernel(LocalParams p) {
   // ---- loads; per-group cumulative sums of a ------------------------------
   Pair kr[RPG], qr[RPG];
   float gr[RPG][2];
+  bool bad = false;  // a log-decay of this thread outside [a_lo, 0]
   if (act) {
     const uint32_t rsk = static_cast<uint32_t>(H) * DK * ES;
     const uint32_t ok0 = r0 * rsk + c0p * ES, okl = (n - 1) * rsk + c0p * ES;
@@ -442,6 +447,8 @@ __global__ __launch_bounds__(64 * NW, 2) void local_kernel(LocalParams p) {
         aa.x = valid ? p.g_min * fast_rcp(1.f + fast_exp(-aa.x)) : 0.f;
         aa.y = valid ? p.g_min * fast_rcp(1.f + fast_exp(-aa.y)) : 0.f;
       }
+      // (a NaN fails both comparisons)
+      bad |= !(aa.x >= p.a_lo && aa.x <= 0.f && aa.y >= p.a_lo && aa.y <= 0.f);
       run0 += aa.x; run1 += aa.y;
       gr[rr][0] = run0; gr[rr][1] = run1;
     }
@@ -452,6 +459,11 @@ __global__ __launch_bounds__(64 * NW, 2) void local_kernel(LocalParams p) {
     float b = tid < n ? to_f32(gb[row0 + static_cast<size_t>(tid) * H]) : 0.f;
     if constexpr (GATE) b = tid < n ? fast_rcp(1.f + fast_exp(-b)) : 0.f;
     sm.beta[tid] = b;
+  }
+  // One store per wave that saw a decay out of range.
+  if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) {
+    *p.wsflag = 1;
+    if (p.err_flag != nullptr) *p.err_flag = 1;
   }
   __syncthreads();
 
@@ -698,6 +710,7 @@ __global__ __launch_bounds__(64 * NW, 1) void prop_kernel(PropParams p) {
   const int chain = 8 * (local / p.dv_tiles) + xcd, tile = local % p.dv_tiles;
   const int seq = p.chains[2 * chain], h = p.chains[2 * chain + 1];
   if (seq < 0) return;
+  if (MODE == 0 && *p.wsflag != 0) return;  // a decay out of range: write nothing
   const int* si = p.seqinfo + 6 * seq;
   const int lo = si[0], ck_lo = si[2], ck_hi = si[3], c_lo = si[4], c_hi = si[5];
   const int j0 = tile * DVT;
@@ -1035,6 +1048,7 @@ hipError_t launch_local(const PrefillArgs& a) {
   prm.q = a.q; prm.k = a.k; prm.a = a.a; prm.beta = a.beta; prm.g_min = a.g_min;
   prm.perm = a.slab ? 1 : 0;
   prm.chunks = a.chunks; prm.tq = a.tq; prm.H = a.H; prm.ld = a.chunk;
+  prm.wsflag = a.wsflag; prm.err_flag = a.err_flag; prm.a_lo = a.a_lo;
   const dim3 grid(static_cast<unsigned>(a.n_chunks) * static_cast<unsigned>(a.H));
   if (a.gate)
     hipLaunchKernelGGL((local_kernel<DK, InT, kWaves, true>), grid, dim3(64 * kWaves), 0, a.stream, prm);
@@ -1050,7 +1064,7 @@ hipError_t launch_prop(const PrefillArgs& a) {
   prm.s0 = a.s0; prm.o = a.o; prm.s_final = a.s_final;
   prm.page_pool = a.page_pool; prm.page_elems = a.page_elems;
   prm.chains = a.chains; prm.seqinfo = a.seqinfo; prm.ck_pos = a.ck_pos; prm.ck_slot = a.ck_slot;
-  prm.chunks = a.chunks;
+  prm.chunks = a.chunks; prm.wsflag = a.wsflag;
   prm.H = a.H; prm.dv = a.dv; prm.ld = a.chunk; prm.dv_tiles = a.dv_tiles;
   const dim3 grid(static_cast<unsigned>(a.n_chains) * static_cast<unsigned>(a.dv_tiles));
   hipLaunchKernelGGL((prop_kernel<DK, DVT, InT, kWaves, MODE>), grid, dim3(64 * kWaves), 0, a.stream, prm);

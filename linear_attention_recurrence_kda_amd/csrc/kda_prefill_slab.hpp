@@ -216,6 +216,7 @@ __device__ __forceinline__ void slab_body(const PropParams& p, int chain, int ti
 
   const int seq = ld_const(p.chains, 2 * chain), h = ld_const(p.chains, 2 * chain + 1);
   if (seq < 0) return;
+  if (MODE == 0 && ld_const(p.wsflag, 0) != 0) return;  // a decay out of range: write nothing
   const int lo = ld_const(p.seqinfo, 6 * seq), hi = ld_const(p.seqinfo, 6 * seq + 1);
   const int ck_lo = ld_const(p.seqinfo, 6 * seq + 2);
   const int ck_hi = ld_const(p.seqinfo, 6 * seq + 3), c_lo = ld_const(p.seqinfo, 6 * seq + 4);
@@ -280,7 +281,16 @@ __device__ __forceinline__ void slab_body(const PropParams& p, int chain, int ti
   }
 
   if (c_lo < c_hi) {
-    if (loader) {
+    if (loader && lw >= NLW) {
+      // ---- spare wave (a narrow tile in a workgroup sized for a wider one):
+      // it issues no memory operation at all and only passes the same
+      // barriers as the loader waves (one before the chain, two per chunk).
+      slab_barrier();
+      for (int c = c_lo; c < c_hi; ++c) {
+        slab_barrier();
+        slab_barrier();
+      }
+    } else if (loader) {
       // ---- loader wave: every global->LDS move of the chain ----------------
       // Record of chunk c: LDS piece x of a stored part (W pieces per row,
       // rows from row R0 of a record matrix whose rows are GW pieces long)
@@ -581,8 +591,8 @@ __global__ __launch_bounds__(64 * (NWV + kLoaders), 1) void slab_kernel(PropPara
 
 // A tile width per workgroup (prefill): entry bid of p.wgs is chain << 8 |
 // width code << 4 | tile (width code 0: 32 columns, 1: 64, 2: 128; 15: no
-// work).  Six waves for every width: a 32-column tile's two spare waves run
-// the loader loop with nothing to load.
+// work).  Six waves for every width: a 32-column tile has two compute and
+// two loader waves, and its two spare waves only pass the barriers.
 template <int DK>
 __global__ __launch_bounds__(64 * (4 + kLoaders), 1) void slab_mixed_kernel(PropParams p) {
   __shared__ __attribute__((aligned(16))) SlabRec<DK> sm[2];
@@ -602,7 +612,7 @@ hipError_t launch_slab_t(const PrefillArgs& a) {
   prm.s0 = a.s0; prm.o = a.o; prm.s_final = a.s_final;
   prm.page_pool = a.page_pool; prm.page_elems = a.page_elems;
   prm.chains = a.chains; prm.seqinfo = a.seqinfo; prm.ck_pos = a.ck_pos; prm.ck_slot = a.ck_slot;
-  prm.chunks = a.chunks;
+  prm.chunks = a.chunks; prm.wsflag = a.wsflag;
   prm.H = a.H; prm.dv = a.dv; prm.ld = a.chunk; prm.dv_tiles = a.dv_tiles;
   const dim3 grid(static_cast<unsigned>(a.n_chains) * static_cast<unsigned>(a.dv_tiles));
   hipLaunchKernelGGL((slab_kernel<DK, NWV, NJ, MODE>), grid, dim3(64 * (NWV + kLoaders)), 0, a.stream, prm);
@@ -618,7 +628,7 @@ hipError_t launch_slab_mixed(const PrefillArgs& a) {
   prm.s0 = a.s0; prm.o = a.o; prm.s_final = a.s_final;
   prm.page_pool = a.page_pool; prm.page_elems = a.page_elems;
   prm.chains = a.chains; prm.seqinfo = a.seqinfo; prm.ck_pos = a.ck_pos; prm.ck_slot = a.ck_slot;
-  prm.chunks = a.chunks; prm.wgs = a.wgs;
+  prm.chunks = a.chunks; prm.wgs = a.wgs; prm.wsflag = a.wsflag;
   prm.H = a.H; prm.dv = a.dv; prm.ld = a.chunk; prm.dv_tiles = a.dv_tiles;
   hipLaunchKernelGGL((slab_mixed_kernel<DK>), dim3(static_cast<unsigned>(a.n_wg)), dim3(64 * (4 + kLoaders)), 0,
                      a.stream, prm);

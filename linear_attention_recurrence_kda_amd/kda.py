@@ -47,14 +47,18 @@ SIGNATURES = {
                                                         ctypes.c_int, ctypes.POINTER(_sz)]),
     "kda_chunk_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int, _i32, _i32, _i32,
                                          _i32, _i32p, _i32, _vp, _vp, _vp, _i32p, _i32p, _i32p,
-                                         _i64, _vp, _i64, _i64, _vp, _sz, _vp]),
+                                         _i64, _vp, _i64, _i64, _vp, _sz, _vp, _vp]),
     "kda_chunk_prefill_split": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int, _i32, _i32,
                                                _i32, _i32, _i32p, _i32, _vp, _vp, _vp, _i32p, _i32p,
-                                               _i32p, _i64, _vp, _i64, _i64, _vp, _sz, _i32, _vp]),
+                                               _i32p, _i64, _vp, _i64, _i64, _vp, _sz, _i32, _vp,
+                                               _vp]),
+    "kda_chunk_prefill_plan": (ctypes.c_int, [ctypes.c_int, _i32, _i32, _i32, _i32, _i32p, _i32,
+                                              _i32p, _i32p, _i64, _i32, _i32p, ctypes.c_char_p,
+                                              _sz]),
     "kda_chunk_prefill_gated": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, ctypes.c_int,
                                                _i32, _i32, _i32, _i32, _i32p, _i32, _vp, _vp, _vp,
                                                _i32p, _i32p, _i32p, _i64, _vp, _i64, _i64, _vp, _sz,
-                                               _i32, _vp]),
+                                               _i32, _vp, _vp]),
     "kda_segment_summary_workspace_size": (ctypes.c_int, [_i32, _i64, _i32, _i32, _i32, _i32,
                                                           ctypes.c_int, ctypes.POINTER(_sz)]),
     "kda_segment_summary": (ctypes.c_int, [_vp, _vp, _vp, _vp, ctypes.c_int, _i32, _i32, _i32, _i32,
@@ -264,9 +268,43 @@ def prefill_workspace_size(n_seqs, total_tokens, H, dk, dv, chunk, n_ckpt, dtype
     return out.value
 
 
+def _ckpt_arrays(checkpoints, ckpt_slots, N):
+    """Flatten per-sequence checkpoint lists into (ckpt_cu, ckpt_pos, ckpt_slot)."""
+    ck_cu, ck_pos, ck_slot = [0], [], []
+    if checkpoints is None:
+        return [0] * (N + 1), ck_pos, ck_slot
+    if ckpt_slots is None:
+        ckpt_slots = [[0] * len(p) for p in checkpoints]
+    if len(checkpoints) != N or len(ckpt_slots) != N:
+        raise ValueError("checkpoints and ckpt_slots need one list per sequence")
+    for pos, sl in zip(checkpoints, ckpt_slots):
+        if len(pos) != len(sl):
+            raise ValueError("each sequence needs one slot per checkpoint")
+        ck_pos += list(pos)
+        ck_slot += list(sl)
+        ck_cu.append(len(ck_pos))
+    return ck_cu, ck_pos, ck_slot
+
+
+def prefill_plan(cu_seqlens, H, dk, dv, chunk=64, checkpoints=None, dtype=torch.bfloat16,
+                 dv_split=0):
+    """What chunk_prefill would launch: (dv columns per workgroup of each
+    sequence, the kernels' names).  Nothing runs on the device."""
+    cu = [int(x) for x in cu_seqlens]
+    N = len(cu) - 1
+    ck_cu, ck_pos, _ = _ckpt_arrays(checkpoints, None, N)
+    cols = (ctypes.c_int32 * max(1, N))()
+    names = ctypes.create_string_buffer(256)
+    code = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32
+    _check(lib().kda_chunk_prefill_plan(code, H, dk, dv, chunk, _i32_array(cu), N, _i32_array(ck_cu),
+                                        _i32_array(ck_pos), len(ck_pos), dv_split, cols, names,
+                                        ctypes.sizeof(names)))
+    return [cols[i] for i in range(N)], names.value.decode()
+
+
 def chunk_prefill(q, k, v, a, beta, cu_seqlens, s0=None, chunk=64, checkpoints=None,
                   ckpt_slots=None, page_pool=None, o=None, s_final=None, want_final=True,
-                  workspace=None, dv_split=0, gate_g_min=None):
+                  workspace=None, dv_split=0, gate_g_min=None, err_flag=None):
     """Token-packed varlen prefill.
 
     q, k, a [T,H,dk], v [T,H,dv], beta [T,H] (float32 or bfloat16, same dtype)
@@ -276,6 +314,8 @@ def chunk_prefill(q, k, v, a, beta, cu_seqlens, s0=None, chunk=64, checkpoints=N
     page_pool [n_slots, page_elems] fp32 receives the checkpoint states.
     gate_g_min: when given, a and beta are gate logits and the prefill uses
     a = gate_g_min * sigmoid(a), beta = sigmoid(beta) (the fused gate).
+    err_flag: int32 [1] on the device, or None; set to 1 (and nothing is
+    written) when a log-decay lies outside [-160/chunk, 0].
     Returns (o [T,H,dv], s_final [N,H,dk,dv] or None).
     """
     T, H, dk = q.shape
@@ -295,21 +335,12 @@ def chunk_prefill(q, k, v, a, beta, cu_seqlens, s0=None, chunk=64, checkpoints=N
         s_final = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     if s_final is not None:
         _expect(s_final, (N, H, dk, dv), torch.float32, "s_final", dev)
-    ck_cu, ck_pos, ck_slot = [0], [], []
-    if checkpoints is not None:
-        if ckpt_slots is None or page_pool is None:
-            raise ValueError("checkpoints need ckpt_slots and page_pool")
-        if len(checkpoints) != N or len(ckpt_slots) != N:
-            raise ValueError("checkpoints and ckpt_slots need one list per sequence")
-        for pos, sl in zip(checkpoints, ckpt_slots):
-            if len(pos) != len(sl):
-                raise ValueError("each sequence needs one slot per checkpoint")
-            ck_pos += list(pos)
-            ck_slot += list(sl)
-            ck_cu.append(len(ck_pos))
-    else:
-        ck_cu = [0] * (N + 1)
+    if checkpoints is not None and (ckpt_slots is None or page_pool is None):
+        raise ValueError("checkpoints need ckpt_slots and page_pool")
+    ck_cu, ck_pos, ck_slot = _ckpt_arrays(checkpoints, ckpt_slots, N)
     n_ckpt = len(ck_pos)
+    if err_flag is not None:
+        _expect(err_flag, (1,), torch.int32, "err_flag", dev)
     n_slots, page_elems = (0, 0) if page_pool is None else page_pool.shape
     if page_pool is not None:
         _expect(page_pool, (n_slots, page_elems), torch.float32, "page_pool", dev)
@@ -318,7 +349,7 @@ def chunk_prefill(q, k, v, a, beta, cu_seqlens, s0=None, chunk=64, checkpoints=N
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     common = (H, dk, dv, chunk, _i32_array(cu), N, _ptr(s0), _ptr(o), _ptr(s_final), _i32_array(ck_cu),
               _i32_array(ck_pos), _i32_array(ck_slot), n_ckpt, _ptr(page_pool), page_elems,
-              n_slots, _ptr(workspace), workspace.numel(), dv_split, _stream(dev))
+              n_slots, _ptr(workspace), workspace.numel(), dv_split, _ptr(err_flag), _stream(dev))
     if gate_g_min is None:
         _check(lib().kda_chunk_prefill_split(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta),
                                              _dtype_code(q), *common))

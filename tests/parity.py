@@ -47,3 +47,15 @@ def dev_tensor(x, dtype, device="cuda"):
     if dtype == "bf16":
         t = t.to(torch.bfloat16)
     return t.to(device)
+
+
+def assert_parity_blocks(got, want, dtype, block, what=""):
+    """The bar applied to every run of `block` rows (the first axis) on its own,
+    so that an error confined to one chunk cannot hide in a long sequence's
+    norm.  Returns the largest per-block error."""
+    got, want = to_np(got), to_np(want)
+    worst = 0.0
+    for r in range(0, want.shape[0], block):
+        worst = max(worst, assert_parity(got[r:r + block], want[r:r + block], dtype,
+                                         f"{what} rows {r}..{min(r + block, want.shape[0]) - 1}"))
+    return worst

@@ -112,7 +112,7 @@ def test_prefill_validation(L):
         pool = _fake(9) if ck is not None else None
         return L.kda_chunk_prefill_split(q, k, v, a, b, dtype, H, dk, dv, chunk, cu_a, n, None, o_ptr,
                                          None, ck_cu, ck_pos, ck_slot, n_ck, pool, H * dk * dv,
-                                         n_slots, ws, 1 << 20, split, None)
+                                         n_slots, ws, 1 << 20, split, None, None)
 
     assert call(dk=24) == kda.KDA_EUNSUPPORTED
     assert call(chunk=48 + 8) == kda.KDA_EUNSUPPORTED
@@ -141,6 +141,71 @@ def test_prefill_validation(L):
     assert b"o must be 16-byte aligned" in L.kda_last_error()
     assert call(H=(1 << 17) + 1, dk=16) == kda.KDA_EUNSUPPORTED           # 32-bit chunk offsets
     assert b"2^24" in L.kda_last_error()
+
+
+def test_prefill_checkpoint_offsets_checked_before_positions(L):
+    """ckpt_cu = [0, 5, 2] with two checkpoints: refused from the offsets alone
+    (the five positions the second entry would name are never read)."""
+    I32 = ctypes.c_int32
+    cu = (I32 * 3)(0, 40, 100)
+    ck_cu, ck_pos, ck_slot = (I32 * 3)(0, 5, 2), (I32 * 2)(10, 20), (I32 * 2)(0, 1)
+    st = L.kda_chunk_prefill(*(_fake(i) for i in range(5)), 1, 2, 16, 16, 64, cu, 2, None, _fake(5), None,
+                             ck_cu, ck_pos, ck_slot, 2, _fake(9), 2 * 16 * 16, 4, _fake(6), 1 << 20,
+                             None, None)
+    assert st == kda.KDA_EINVAL
+    assert b"ckpt_cu" in L.kda_last_error()
+
+
+def test_gated_prefill_refuses_g_min_below_the_decay_bound(L):
+    """The gated a lies in [g_min, 0] ("Serve 模块交互式演示" §1.3); the chunk
+    form needs a >= -160/chunk, so g_min below that is refused on the host."""
+    I32 = ctypes.c_int32
+    cu = (I32 * 2)(0, 40)
+
+    def gated(g_min, chunk=64):
+        return L.kda_chunk_prefill_gated(*(_fake(i) for i in range(5)), ctypes.c_float(g_min), 1, 2, 16,
+                                         16, chunk, cu, 1, None, _fake(5), None, None, None, None, 0,
+                                         None, 0, 0, _fake(6), 1 << 10, 0, None, None)
+
+    assert gated(-2.6) == kda.KDA_EUNSUPPORTED
+    assert b"decay bound" in L.kda_last_error()
+    assert gated(-5.1, chunk=32) == kda.KDA_EUNSUPPORTED
+    assert gated(0.5) == kda.KDA_EINVAL
+    # at the bound the call gets as far as the (too small) workspace
+    assert gated(-2.5) == kda.KDA_EWORKSPACE
+    assert gated(-5.0, chunk=32) == kda.KDA_EWORKSPACE
+
+
+def test_prefill_plan_widths():
+    """The plan query reports each sequence's tile width.  Chunk counts 20,
+    14, 6 and 2 at H = 2 with a width per sequence: 32, 64, 128 and 128
+    columns (the cost model's balance of the longest chain against the total
+    work); one width everywhere for an explicit split."""
+    lens = [64 * 20, 64 * 14, 64 * 6, 100]
+    cu = [0]
+    for n in lens:
+        cu.append(cu[-1] + n)
+    ck = [list(range(256, n + 1, 256)) for n in lens]
+    cols, names = kda.prefill_plan(cu, 2, 128, 128, 64, ck, dv_split=-1)
+    assert cols == [32, 64, 128, 128]
+    assert "slab_mixed_kernel" in names
+    cols, names = kda.prefill_plan(cu, 2, 128, 128, 64, ck, dv_split=4)
+    assert cols == [32] * 4 and "slab_kernel<128> (32-column tiles)" in names
+    cols, names = kda.prefill_plan([0, 100, 150], 2, 64, 64, 32, dtype=__import__("torch").float32)
+    assert "prop_kernel" in names
+
+
+def test_prefill_plan_is_fast_for_many_sequences():
+    """The width choice is O(n log n): 4096 sequences plan in well under a
+    tenth of a second."""
+    import time
+    import numpy as np
+    lens = np.random.default_rng(5).integers(1, 4000, 4096)
+    cu = np.concatenate([[0], np.cumsum(lens)]).tolist()
+    t0 = time.perf_counter()
+    cols, _ = kda.prefill_plan(cu, 32, 128, 128, 64)
+    assert time.perf_counter() - t0 < 0.1
+    assert set(cols) <= {16, 32, 64, 128}
 
 
 def test_segment_validation(L):
