@@ -33,7 +33,8 @@ def _hipcc():
 
 # Per-source additions: the column-slab kernel keeps MFMA results in ordinary
 # vector registers (it rescales and rounds them every chunk).
-EXTRA = {"kda_slab.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+EXTRA = {"kda_slab.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "kda_fused.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src, verbose):

@@ -30,51 +30,54 @@ int64_t max_chunks(int32_t n_seqs, int64_t total_tokens, int32_t chunk, int64_t 
 // Workspace: the int32 work list (a header of kHeaderInts words whose first
 // is the decay-range flag, zero on entry; chains, sequence table,
 // checkpoints, chunks, and room for a mixed-width workgroup list of up to
-// four entries per chain), then (256-byte aligned) one record per
+// eight entries per chain), then (256-byte aligned) one record per
 // (chunk, head) (UnitLayout: T diag(beta), lower(A_qk) and the chunk's scaled
 // operands, in the operand precision: bf16 for bf16 inputs, fp32 for fp32).
 constexpr int64_t kHeaderInts = 64;
 size_t work_ints(int32_t n_seqs, int32_t H, int64_t n_ckpt, int64_t n_chunks) {
   return static_cast<size_t>(kHeaderInts + 2 * round8(static_cast<int64_t>(n_seqs) * H) + 6 * n_seqs +
-                             2 * n_ckpt + 2 * n_chunks + 4 * round8(static_cast<int64_t>(n_seqs) * H));
+                             2 * n_ckpt + 2 * n_chunks + 8 * round8(static_cast<int64_t>(n_seqs) * H));
 }
 
-// Per-sequence tile widths for the column-slab prefill at dv = 128 (32, 64
-// or 128 columns), from per-chunk times measured with every CU busy: the
-// widest width whose chain fits a target time, the target chosen to balance
-// the longest chain against the total work over the CUs.  The candidate
-// targets are the chains' own times at each width; with the chunk counts
-// sorted and summed once, each candidate costs two binary searches, so the
-// choice is O(n log n) in the number of sequences.  Returns the predicted
-// time (us) and fills width[s].
-double choose_widths(const std::vector<int64_t>& chunks, int32_t H, std::vector<int>& width) {
-  constexpr int ws[3] = {128, 64, 32};
-  constexpr double tw[3] = {3.8, 2.5, 2.0};
-  constexpr double mult[3] = {1, 2, 4};  // tiles per head
+// Per-sequence tile widths: nw widths ws[0] > ws[1] > ... (columns per
+// workgroup), with per-chunk times tw[j] measured with every CU busy
+// (decreasing with the width) and mult[j] workgroups per head.  Each sequence
+// takes the widest width whose chain fits a target time; the target is the
+// one that balances the longest chain against the total work over the CUs.
+// The candidate targets are the chains' own times at each width; with the
+// chunk counts sorted and summed once, each candidate costs nw - 1 binary
+// searches, so the choice is O(n log n) in the number of sequences.  Returns
+// the predicted time (us) and fills width[s].
+double choose_widths(const std::vector<int64_t>& chunks, int32_t H, const int* ws, const double* tw,
+                     const double* mult, int nw, std::vector<int>& width) {
   const size_t n = chunks.size();
   std::vector<int64_t> c(chunks);
   std::sort(c.begin(), c.end());
   std::vector<double> pre(n + 1, 0.0);
   for (size_t i = 0; i < n; ++i) pre[i + 1] = pre[i] + static_cast<double>(c[i]);
-  // Sequences [0, i_j) of the sorted list fit the target T at width j.
+  // Sequences [0, fits(j, T)) of the sorted list fit the target T at width j.
   auto fits = [&](int j, double T) {
     return static_cast<size_t>(std::partition_point(c.begin(), c.end(), [&](int64_t x) {
                                  return static_cast<double>(x) * tw[j] <= T;
                                }) - c.begin());
   };
+  auto cost_at = [&](double T) {
+    double work = 0, longest = 0;
+    size_t prev = 0;
+    for (int j = 0; j < nw; ++j) {
+      const size_t e = j + 1 < nw ? std::max(prev, fits(j, T)) : n;  // group j: [prev, e)
+      work += H * mult[j] * tw[j] * (pre[e] - pre[prev]);
+      if (e > prev) longest = std::max(longest, static_cast<double>(c[e - 1]) * tw[j]);
+      prev = e;
+    }
+    return std::max(longest, work / kCUs);
+  };
   double best = 0, best_T = 0;
   for (size_t i = 0; i < n; ++i) {
     if (i > 0 && c[i] == c[i - 1]) continue;
-    for (int j = 0; j < 3; ++j) {
+    for (int j = 0; j < nw; ++j) {
       const double T = static_cast<double>(c[i]) * tw[j];
-      const size_t i0 = fits(0, T), i1 = std::max(i0, fits(1, T));
-      const double work = H * (mult[0] * tw[0] * pre[i0] + mult[1] * tw[1] * (pre[i1] - pre[i0]) +
-                               mult[2] * tw[2] * (pre[n] - pre[i1]));
-      double longest = 0;
-      if (i0 > 0) longest = std::max(longest, static_cast<double>(c[i0 - 1]) * tw[0]);
-      if (i1 > i0) longest = std::max(longest, static_cast<double>(c[i1 - 1]) * tw[1]);
-      if (n > i1) longest = std::max(longest, static_cast<double>(c[n - 1]) * tw[2]);
-      const double cost = std::max(longest, work / kCUs);
+      const double cost = cost_at(T);
       // On a tie the larger target wins: wider tiles, less total work.
       if (best == 0 || cost < best * (1 - 1e-12) || (cost <= best * (1 + 1e-12) && T > best_T)) {
         best = std::min(best == 0 ? cost : best, cost);
@@ -82,15 +85,24 @@ double choose_widths(const std::vector<int64_t>& chunks, int32_t H, std::vector<
       }
     }
   }
-  width.assign(n, 32);
+  width.assign(n, ws[nw - 1]);
   for (size_t s = 0; s < n; ++s)
-    for (int j = 0; j < 3; ++j)
+    for (int j = 0; j < nw; ++j)
       if (static_cast<double>(chunks[s]) * tw[j] <= best_T) {
         width[s] = ws[j];
         break;
       }
   return best;
 }
+
+// The fused kernel's per-chunk times (us, 32-token chunks, every CU busy) at
+// 128, 64, 32 and 16 columns per workgroup.
+constexpr int kFusedW[4] = {128, 64, 32, 16};
+constexpr double kFusedT[4] = {1.4, 1.0, 0.8, 0.75};
+bool fused_path(kda_dtype in_dtype, int32_t dk, int32_t chunk) {
+  return in_dtype == KDA_BF16 && chunk == 32 && dk == 128;
+}
+
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 size_t tile_bytes(int64_t n_chunks, int32_t H, int32_t chunk, int32_t dk, size_t es) {
   return static_cast<size_t>(n_chunks) * H * kda::UnitLayout(chunk, dk, static_cast<int>(es)).bytes;
@@ -170,7 +182,7 @@ int choose_split_slab(int32_t dv, int64_t total_chunks, int64_t longest) {
 struct Plan {
   int64_t n_chunks = 0, longest = 0;
   int split = 0, a_split = 0;
-  bool slab = false, mixed = false;
+  bool slab = false, mixed = false, fused = false;
   std::vector<int> width;  // columns per workgroup, per sequence
 };
 
@@ -227,6 +239,7 @@ int make_plan(kda_dtype in_dtype, int32_t H, int32_t dk, int32_t dv, int32_t chu
 
   // Chunks and split.
   pl = Plan{};
+  const int64_t n_chains = round8(static_cast<int64_t>(n_seqs) * H);
   for (int32_t i = 0; i < n_seqs; ++i) {
     const int32_t len = cu[i + 1] - cu[i];
     const int32_t c0 = ck_cu ? ck_cu[i] : 0, c1 = ck_cu ? ck_cu[i + 1] : 0;
@@ -236,6 +249,38 @@ int make_plan(kda_dtype in_dtype, int32_t H, int32_t dk, int32_t dv, int32_t chu
   }
   if (pl.n_chunks * H >= (int64_t{1} << 31)) return fail(KDA_EUNSUPPORTED, "too many (chunk, head) pairs");
   const bool bf16 = in_dtype == KDA_BF16;
+  // The fused kernel (bf16, chunk 32, dk 128): a tile width per sequence,
+  // 16 to 128 columns, from its cost model, or one width dv / dv_split.
+  if (fused_path(in_dtype, dk, chunk) && !summary) {
+    pl.fused = true;
+    if (n_chains >= (int64_t{1} << 23)) return fail(KDA_EUNSUPPORTED, "too many chains");
+    if (dv_split > 0) {
+      const int w = dv % dv_split ? 0 : dv / dv_split;
+      if (w != 16 && w != 32 && w != 64 && w != 128)
+        return fail(KDA_EUNSUPPORTED, "dv_split=%d with dv=%d (dv/split must be 16, 32, 64 or 128)", dv_split, dv);
+      pl.split = dv_split;
+      pl.width.assign(n_seqs, w);
+      return KDA_OK;
+    }
+    if (dv_split != 0 && dv_split != -1) return fail(KDA_EUNSUPPORTED, "dv_split=%d", dv_split);
+    std::vector<int64_t> sc(n_seqs);
+    for (int32_t i = 0; i < n_seqs; ++i) {
+      const int32_t c0 = ck_cu ? ck_cu[i] : 0, c1 = ck_cu ? ck_cu[i + 1] : 0;
+      sc[i] = seq_chunks(cu[i + 1] - cu[i], ck_pos ? ck_pos + c0 : nullptr, c1 - c0, chunk);
+    }
+    int ws[4], nw = 0;
+    double tw[4], mult[4];
+    for (int j = 0; j < 4; ++j)
+      if (kFusedW[j] <= dv) {
+        ws[nw] = kFusedW[j];
+        tw[nw] = kFusedT[j];
+        mult[nw] = static_cast<double>(dv) / kFusedW[j];
+        ++nw;
+      }
+    if (n_seqs > 0) choose_widths(sc, H, ws, tw, mult, nw, pl.width);
+    pl.mixed = true;
+    return KDA_OK;
+  }
   pl.slab = slab_path(dk, bf16, chunk);
   // -1: a width per sequence (mixed launch), where the slab kernel runs at dv = 128.
   const bool force_mixed = dv_split == -1;
@@ -248,7 +293,6 @@ int make_plan(kda_dtype in_dtype, int32_t H, int32_t dk, int32_t dv, int32_t chu
   if (!valid_tile(dv, pl.split, pl.slab))
     return fail(KDA_EUNSUPPORTED, "dv_split=%d with dv=%d (dv/split must be 16, 32 or 64%s)", dv_split, dv,
                 pl.slab ? ", or 128" : "");
-  const int64_t n_chains = round8(static_cast<int64_t>(n_seqs) * H);
   if (n_chains * pl.split >= (int64_t{1} << 31)) return fail(KDA_EUNSUPPORTED, "too many chains");
   // The linear part A of a summary propagates dk identity columns.
   pl.a_split = !summary ? 0 : pl.slab ? choose_split_slab(dk, pl.n_chunks * H, pl.longest)
@@ -270,7 +314,9 @@ int make_plan(kda_dtype in_dtype, int32_t H, int32_t dk, int32_t dv, int32_t chu
       total += sc[i];
     }
     std::vector<int> width;
-    const double tm = choose_widths(sc, H, width);
+    const int ws[3] = {128, 64, 32};
+    const double tw[3] = {3.8, 2.5, 2.0}, mult[3] = {1, 2, 4};
+    const double tm = choose_widths(sc, H, ws, tw, mult, 3, width);
     // The best single width by the same per-chunk times (16 columns: 1.95 us).
     double tu = 0;
     const int uw[4] = {16, 32, 64, 128};
@@ -293,7 +339,12 @@ std::string plan_kernels(const Plan& pl, kda_dtype in_dtype, int32_t dk, int32_t
   const char* t = in_dtype == KDA_BF16 ? "bf16" : "fp32";
   char buf[256];
   const std::string local = std::string("local_kernel<") + std::to_string(dk) + "," + t + (gate ? ",gated" : "") + ">";
-  if (pl.mixed)
+  if (pl.fused) {
+    int lo = 1 << 30, hi = 0;
+    for (int w : pl.width) { lo = std::min(lo, w); hi = std::max(hi, w); }
+    snprintf(buf, sizeof(buf), "fused_kernel<%d> (32-token chunks, records in LDS; %d to %d columns per workgroup)",
+             dk, pl.width.empty() ? 0 : lo, hi);
+  } else if (pl.mixed)
     snprintf(buf, sizeof(buf), "%s + slab_mixed_kernel<%d> (a tile width per sequence)", local.c_str(), dk);
   else if (pl.slab)
     snprintf(buf, sizeof(buf), "%s + slab_kernel<%d> (%d-column tiles)", local.c_str(), dk, dv / pl.split);
@@ -355,7 +406,7 @@ int prefill_impl(const void* q, const void* k, const void* v, const void* a, con
   if (err_flag && reinterpret_cast<uintptr_t>(err_flag) % 4) return fail(KDA_EINVAL, "err_flag must be aligned");
   const int64_t n_chunks = pl.n_chunks;
   const size_t list_bytes = align256(work_ints(n_seqs, H, n_ckpt, n_chunks) * 4);
-  const size_t need = list_bytes + tile_bytes(n_chunks, H, chunk, dk, es);
+  const size_t need = list_bytes + (pl.fused ? 0 : tile_bytes(n_chunks, H, chunk, dk, es));
   if (!workspace || workspace_bytes < need)
     return fail(KDA_EWORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
   if (reinterpret_cast<uintptr_t>(workspace) & 255u)
@@ -436,18 +487,28 @@ int prefill_impl(const void* q, const void* k, const void* v, const void* a, con
       int rounds = 0;
       for (int x = 0; x < 8; ++x) {
         const int32_t sq = chains[2 * (8 * g + x)];
-        if (sq >= 0) rounds = std::max(rounds, 128 / pl.width[sq]);
+        if (sq >= 0) rounds = std::max(rounds, dv / pl.width[sq]);
       }
       for (int r = 0; r < rounds; ++r)
         for (int x = 0; x < 8; ++x) {
           const int64_t ch = 8 * g + x;
           const int32_t sq = chains[2 * ch];
           const int w = sq >= 0 ? pl.width[sq] : 0;
-          const int code = w == 32 ? 0 : w == 64 ? 1 : 2;
-          wgs[n_wg++] = (sq >= 0 && r < 128 / w) ? static_cast<int32_t>((ch << 8) | (code << 4) | r)
-                                                 : static_cast<int32_t>((ch << 8) | (15 << 4));
+          const int code = w == 32 ? 0 : w == 64 ? 1 : w == 128 ? 2 : 3;
+          wgs[n_wg++] = (sq >= 0 && r < dv / w) ? static_cast<int32_t>((ch << 8) | (code << 4) | r)
+                                                : static_cast<int32_t>((ch << 8) | (15 << 4));
         }
     }
+  } else if (pl.fused) {  // one width everywhere
+    for (int64_t g = 0; g < n_chains / 8; ++g)
+      for (int r = 0; r < pl.split; ++r)
+        for (int x = 0; x < 8; ++x) {
+          const int64_t ch = 8 * g + x;
+          const int w = dv / pl.split;
+          const int code = w == 32 ? 0 : w == 64 ? 1 : w == 128 ? 2 : 3;
+          wgs[n_wg++] = chains[2 * ch] >= 0 ? static_cast<int32_t>((ch << 8) | (code << 4) | r)
+                                            : static_cast<int32_t>((ch << 8) | (15 << 4));
+        }
   }
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -463,6 +524,7 @@ int prefill_impl(const void* q, const void* k, const void* v, const void* a, con
   p.bf16 = in_dtype == KDA_BF16;
   p.gate = gate;
   p.slab = pl.slab;
+  p.fused = pl.fused;
   p.g_min = g_min;
   p.H = H; p.dk = dk; p.dv = dv; p.chunk = chunk;
   p.s0 = s0; p.o = o; p.s_final = s_final;
@@ -503,7 +565,8 @@ int kda_chunk_prefill_workspace_size(int32_t n_seqs, int64_t total_tokens, int32
   if (chunk < 16 || chunk > KDA_MAX_CHUNK || chunk % 16)
     return fail(KDA_EUNSUPPORTED, "chunk=%d (a multiple of 16 up to %d)", chunk, KDA_MAX_CHUNK);
   const int64_t mc = max_chunks(n_seqs, total_tokens, chunk, n_ckpt);
-  *bytes = align256(work_ints(n_seqs, H, n_ckpt, mc) * 4) + tile_bytes(mc, H, chunk, dk, elem_size(in_dtype));
+  *bytes = align256(work_ints(n_seqs, H, n_ckpt, mc) * 4) +
+           (fused_path(in_dtype, dk, chunk) ? 0 : tile_bytes(mc, H, chunk, dk, elem_size(in_dtype)));
   return ok();
 }
 
@@ -566,7 +629,11 @@ int kda_chunk_prefill_gated(const void* q, const void* k, const void* v, const v
 int kda_segment_summary_workspace_size(int32_t n_seg, int64_t total_tokens, int32_t H, int32_t dk,
                                        int32_t dv, int32_t chunk, kda_dtype in_dtype,
                                        size_t* bytes) {
-  return kda_chunk_prefill_workspace_size(n_seg, total_tokens, H, dk, dv, chunk, 0, in_dtype, bytes);
+  // (the summaries always run the two-kernel path, with its records)
+  const int st = kda_chunk_prefill_workspace_size(n_seg, total_tokens, H, dk, dv, chunk, 0, in_dtype, bytes);
+  if (st == KDA_OK && fused_path(in_dtype, dk, chunk))
+    *bytes += tile_bytes(max_chunks(n_seg, total_tokens, chunk, 0), H, chunk, dk, elem_size(in_dtype));
+  return st;
 }
 
 int kda_segment_summary(const void* k, const void* v, const void* a, const void* beta,

@@ -76,6 +76,7 @@ struct PrefillArgs {
   bool bf16;
   bool gate;    // a, beta are logits; a = g_min * sigmoid(a), beta = sigmoid(beta)
   bool slab;    // slab-format records and the column-slab propagation kernel
+  bool fused;   // the fused kernel (kda_fused.hip): bf16, chunk 32, dk 128, no records
   float g_min;
   int H, dk, dv, chunk;
   const float* s0;
@@ -101,6 +102,10 @@ struct PrefillArgs {
   hipStream_t stream;
 };
 hipError_t launch_prefill(const PrefillArgs& p);
+// The fused prefill (one kernel, records in LDS): p.wgs lists one entry per
+// workgroup, chain << 8 | width code << 4 | tile (width code 0: 32 columns,
+// 1: 64, 2: 128, 3: 16).
+hipError_t launch_fused(const PrefillArgs& p);
 // The column-slab propagation (p.slab): mode 0 prefill, 1 a segment's B, 2 its A.
 hipError_t launch_slab_prop(const PrefillArgs& p, int mode);
 

@@ -37,6 +37,7 @@ hipError_t launch_in(const PrefillArgs& a) {
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a) {
+  if (a.fused) return launch_fused(a);
   return a.bf16 ? launch_in<bf16raw>(a) : launch_in<float>(a);
 }
 

@@ -123,10 +123,13 @@ def test_prefill_validation(L):
     assert call(split=1, cu=(0, 4000)) == kda.KDA_EWORKSPACE
     # A width per sequence (-1) only where the column-slab kernel runs at dv = 128.
     assert call(split=-1, dv=64) == kda.KDA_EUNSUPPORTED
-    assert call(split=-1, chunk=32) == kda.KDA_EUNSUPPORTED
+    assert call(split=-1, chunk=32, dk=64) == kda.KDA_EUNSUPPORTED
     assert call(split=-1, dtype=0, chunk=32) == kda.KDA_EUNSUPPORTED
     assert call(split=-2) == kda.KDA_EUNSUPPORTED
-    assert call(chunk=32, split=1) == kda.KDA_EUNSUPPORTED
+    assert call(chunk=32, split=1, dk=64) == kda.KDA_EUNSUPPORTED
+    # the fused kernel (bf16, chunk 32, dk 128) takes 16- to 128-column tiles
+    assert call(chunk=32, split=3) == kda.KDA_EUNSUPPORTED
+    assert call(chunk=32, split=-3) == kda.KDA_EUNSUPPORTED
     assert call(dk=16, dv=128, split=1) == kda.KDA_EUNSUPPORTED
     assert call(dtype=0, chunk=32, split=1) == kda.KDA_EUNSUPPORTED
     assert call(split=3) == kda.KDA_EUNSUPPORTED
@@ -193,6 +196,11 @@ def test_prefill_plan_widths():
     assert cols == [32] * 4 and "slab_kernel<128> (32-column tiles)" in names
     cols, names = kda.prefill_plan([0, 100, 150], 2, 64, 64, 32, dtype=__import__("torch").float32)
     assert "prop_kernel" in names
+    # bf16 at chunk 32 with dk = 128: the fused kernel, a width per sequence
+    cols, names = kda.prefill_plan([0, 3000, 3100, 3150], 2, 128, 128, 32)
+    assert "fused_kernel" in names and all(c in (16, 32, 64, 128) for c in cols)
+    cols, _ = kda.prefill_plan([0, 3000, 3100, 3150], 2, 128, 64, 32, dv_split=2)
+    assert cols == [32, 32, 32]
 
 
 def test_prefill_plan_is_fast_for_many_sequences():
