@@ -201,12 +201,13 @@ def test_prefill_rejects_bad_checkpoints_and_alias():
     assert e.value.status == kda.KDA_EALIAS
 
 
-@pytest.mark.parametrize("dtype,chunk,bad", [("bf16", 64, (3,)), ("bf16", 32, (1, 3)),
+@pytest.mark.parametrize("dtype,chunk,bad", [("bf16", 64, (3,)), ("bf16", 32, (3, 5)),
                                              ("fp32", 32, (1, 3))])
 def test_prefill_rejects_wide_dv_tile(dtype, chunk, bad):
     """dv tiles are at most 64 columns wide, except on the column-slab path
-    (bf16 at chunk 64), which also takes 128; splits that do not divide dv
-    into a supported width are refused."""
+    (bf16 at chunk 64) and the fused path (bf16 at chunk 32, dk = 128), which
+    also take 128; splits that do not divide dv into a supported width are
+    refused."""
     w = inputs.prefill_workload(44, [40], 2, 128, 128, dtype)
     d = {n: dev_tensor(w[n], dtype) for n in FIELDS}
     for split in bad:
