@@ -273,6 +273,35 @@ int kda_chunk_prefill_plan(kda_dtype in_dtype, int32_t H, int32_t dk, int32_t dv
                            char* kernels_out, size_t kernels_bytes);
 
 /*
+ * kda_chunk_prefill_static — kda_chunk_prefill without a workspace argument,
+ * for callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  The workspace is a
+ * device array of KDA_STATIC_SCRATCH_MB MiB inside the library, one per GPU
+ * (held until the process ends); the call allocates no device memory and
+ * calls no allocating routine.  A call whose workspace need (that of
+ * kda_chunk_prefill for the same arguments) exceeds the array is refused
+ * with KDA_EWORKSPACE before anything is enqueued.  The fused path (bf16,
+ * chunk 32, dk 128) needs only its work list (about 50 KB for 16 sequences,
+ * H = 32); the two-kernel path also needs its chunk records (66 KB per
+ * chunk and head at chunk 64, dk 128), so there it serves prefills of about
+ * a thousand (chunk, head) pairs.  Every call on one GPU uses that GPU's one
+ * array: calls that overlap on one GPU (other streams or host threads) race,
+ * and must be serialized by the caller.  Each call clears what must start at
+ * zero (its work list is rewritten from the host every call).
+ */
+#define KDA_STATIC_SCRATCH_MB 64
+int kda_chunk_prefill_static(const void* q, const void* k, const void* v, const void* a,
+                             const void* beta, kda_dtype in_dtype, int32_t H, int32_t dk,
+                             int32_t dv, int32_t chunk, const int32_t* cu_seqlens_host,
+                             int32_t n_seqs, const float* s0, void* o, float* s_final,
+                             const int32_t* ckpt_cu_host, const int32_t* ckpt_pos_host,
+                             const int32_t* ckpt_slot_host, int64_t n_ckpt, float* page_pool,
+                             int64_t page_elems, int64_t n_slots, int32_t* err_flag, void* stream);
+
+/* Size in bytes of the static workspace of kda_chunk_prefill_static. */
+size_t kda_static_scratch_bytes(void);
+
+/*
  * kda_chunk_prefill_gated — kda_chunk_prefill_split with the gate fused in
  * (the [KDA cache] page's vLLM path calls its prefill "chunk_kda_with_fused_gate"):
  * z_a [T_tot, H, dk] and z_b [T_tot, H] (in_dtype) are gate logits, and the

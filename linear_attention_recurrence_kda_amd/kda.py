@@ -52,6 +52,10 @@ SIGNATURES = {
                                                _i32, _i32, _i32p, _i32, _vp, _vp, _vp, _i32p, _i32p,
                                                _i32p, _i64, _vp, _i64, _i64, _vp, _sz, _i32, _vp,
                                                _vp]),
+    "kda_chunk_prefill_static": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, ctypes.c_int, _i32, _i32, _i32,
+                                                _i32, _i32p, _i32, _vp, _vp, _vp, _i32p, _i32p, _i32p,
+                                                _i64, _vp, _i64, _i64, _vp, _vp]),
+    "kda_static_scratch_bytes": (_sz, []),
     "kda_chunk_prefill_plan": (ctypes.c_int, [ctypes.c_int, _i32, _i32, _i32, _i32, _i32p, _i32,
                                               _i32p, _i32p, _i64, _i32, _i32p, ctypes.c_char_p,
                                               _sz]),
