@@ -1,53 +1,67 @@
 // Fused chunked prefill: one kernel, one workgroup per (sequence, head, dv
 // tile) chain, 32-token chunks, bf16 inputs, fp32 state, dk = 128.
 //
-// The chunk form is the one of kda_prefill_kernels.hpp (derived from the
-// per-token recurrence; "Kimi Linear 的 KDA 缓存" page, sections "KDA 的递推与
-// 充分状态" and "预填充为什么能分块并行"): per chunk of n <= 32 tokens, with
-// G the running sum of the log-decays inside the chunk and G_m the reference
-// (the sum over the first 16 rows when n > 16, else 0),
-//   L = diag(beta) strict_lower(Kp Km^T),  Kp = k e^{G - G_m},  Km = k e^{G_m - G}
-//   T = (I + L)^{-1}
-//   U = T diag(beta) (V - (k e^G) S)
-//   O = (q e^G) S + lower(Qp Km^T) U,       Qp = q e^{G - G_m}
-//   S <- diag(e^{G_n}) S + (k e^{G_n - G})^T U
+// The chunk form (derived from the per-token recurrence; "Kimi Linear 的 KDA
+// 缓存" page, sections "KDA 的递推与充分状态" and "预填充为什么能分块并行"):
+// per chunk of n <= 32 tokens, with G the running sum of the log-decays
+// inside the chunk, G_m its value after the first 16 rows (the reference)
+// and G_n its value at the chunk's end,
+//   Kp = k e^{G - G_m},  Qp = q e^{G - G_m},  Km = k e^{G_m - G}
+//   T  = (I + diag(beta) strict_lower(Kp Km^T))^{-1}
+//   S' = diag(e^{G_m}) S                       (the state at the reference)
+//   U  = T diag(beta) (V - Kp S'), by 16-row blocks:
+//        U_0 = T_00 diag(beta_0) Z_0,  U_1 = T_11 diag(beta_1) (Z_1 - A_10 U_0)
+//        (Z = V - Kp S', A = Kp Km^T; block 10 of T never needs forming)
+//   O  = Qp S' + lower(Qp Km^T) U
+//   S <- diag(e^{G_n - G_m}) (S' + Km^T U)
+// (Kp S' = (k e^G) S and Km^T U scaled by e^{G_n - G_m} is (k e^{G_n - G})^T U:
+// the same products as the per-token form, taken with one reference.)  The
+// scaled operands stay within e^{+-80} for a >= -160/32 = -5, and both
+// scalings of the state are applied one after the other, so neither
+// underflows where their product would.
 //
-// What is new here is where the chunk-local part runs.  The two-kernel path
-// computes T diag(beta), lower(A_qk) and the scaled operands of every chunk in
-// a first kernel and passes them through HBM (a 66 KB record per chunk and
-// head, written once and read back by the sequential kernel: more than twice
-// the compulsory bytes).  Here the workgroup that carries the state builds
-// each chunk's record in LDS ahead of use, so HBM sees only q, k, a, beta, v,
-// the outputs and the states.  A 32-token chunk keeps the records in flight
-// (three operand sets of 24.5 KB, two of the small tiles, two of the Gram
-// shares) inside 160 KB of LDS.
+// Why one kernel: the chunk-local work (the decay sums, the scaled operands,
+// the Gram products and the triangular solve) needs no state, but passing it
+// through HBM from a separate kernel costs more than twice the compulsory
+// bytes (a record of about 50 KB per chunk and head, written once and read
+// back).  Here the workgroup that carries the state builds each chunk's
+// record in LDS ahead of use, so HBM sees only q, k, a, beta, v, the outputs
+// and the states.  The operands Kp, Qp, Km are exactly the bf16 operands of
+// the Gram products, so a record costs two exponentials, three products and
+// the bf16 rounding per element, and the state carries the two per-channel
+// scalings.
 //
-// Eight waves, two per SIMD:
-//  - waves 0..3, the propagation ("P") waves: the column-slab chunk step of
-//    kda_prefill_slab.hpp on register-resident state (16 or 32 state columns
-//    per wave; narrow tiles leave some P waves idle);
-//  - waves 4..7, the local ("L") waves: wave w owns key channels 32w..32w+31.
-//    A lane holds one token row (16 lanes per 16-row block) and eight
-//    channels, loaded straight from HBM in 16-byte pieces, so the chunk's
-//    running sums of a are row scans across 16 lanes (DPP), the Gram operands
-//    are MFMA fragments already, and each wave forms its 32 channels' share
-//    of A_kk and A_qk with six MFMAs (as transposes, so that a lane ends with
+// Twelve waves, three per SIMD:
+//  - waves 0..3, the propagation ("P") waves: the column-slab chunk step on
+//    register-resident state (16 or 32 state columns per wave; narrow tiles
+//    leave some P waves without state), and (16 columns per wave) the
+//    diagonal solves of the next chunk's record;
+//  - waves 4..11, the local ("L") waves: L wave w builds token rows
+//    16 (w / 4) .. +15 of key channels 32 (w % 4) .. +31.  A lane holds one
+//    token row and eight channels, loaded from HBM in 16-byte pieces through
+//    a buffer resource that ends at the chunk's last row (rows past it read
+//    as zero: zero decay, zero key, query, value and beta, so they drop out of
+//    every product).  The running sums of a are row scans across 16 lanes
+//    (DPP); with the reference at row 16 the two halves need nothing from
+//    each other.  The Gram operands are MFMA fragments already: each wave
+//    forms its 32 channels' share of the diagonal blocks of A_kk and A_qk,
+//    and after M the first-half wave forms the off-diagonal ones from the
+//    other half's rows in LDS (all as transposes, so that a lane ends with
 //    one row of a block: the layout the triangular solve wants).
 //
 // Per chunk c every wave passes two barriers, M (mid-chunk) and A (the
-// hand-over); P runs chunk c's state-independent half before M and the rest
-// after.  In the same interval the L waves
-//  - finish chunk c+1: before M, L wave 0 inverts the diagonal block
-//    (I + L_00), L wave 1 the block (I + L_11) (forward substitution by rows,
-//    each step a DPP broadcast of one row within the lane row), L wave 2 adds
-//    the shares of A_qk and writes lower(A_qk), L wave 3 forms L_10; after M,
-//    L wave 3 forms the off-diagonal block T_10 = -T_11 L_10 T_00 with two
-//    fp32 MFMA products;
-//  - build chunk c+2's scaled operands and Gram shares, the first 16 token
-//    rows before M, the other 16 after;
-//  - store chunk c-1's outputs, move chunk c+1's v into LDS, and issue the
-//    loads of chunk c+3 (q, k, a, beta) and c+2 (v) into registers.
-// So a record is built over two chunk intervals and read in the third.
+// hand-over).  Before M: P runs chunk c's state-independent half and inverts
+// chunk c+1's diagonal blocks (I + L_RR), two waves per block, two of each
+// lane's four columns each (forward substitution by rows, each step a DPP
+// broadcast of one row within the lane row); the L waves issue the loads of
+// chunk c+3 (q, k, a, beta) and c+2 (v) and build chunk c+2.  After M: P runs
+// the rest of chunk c; the first-half L waves form chunk c+2's off-diagonal
+// Gram shares and two of them write chunk c+1's lower(A_qk) and A_10; all L
+// waves store chunk c-1's outputs and move chunk c+1's v into LDS.  (With
+// 32 state columns per P wave the second-half L waves do the inversion, after
+// M.)  So a
+// record is built in one interval, finished in the next and read in the
+// third.
 //
 // A decay outside [a_lo, 0] (or a NaN) found while building chunk x raises
 // the error flags and stops that chain at the barrier that would hand chunk x
@@ -63,32 +77,37 @@ namespace {
 
 constexpr int kFC = 32;  // tokens per chunk
 
-// One chunk's operands in LDS.  kg, qg: 32 token rows of 16 pieces (16
-// bytes, slab_col channel order), piece q of row m at q ^ (m & 7); kh: dk
-// channel rows of 4 pieces (32 tokens in slab_col order), piece q of row m at
-// q ^ ((m >> 1) & 3).
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// One chunk's operands in LDS.  kp, qp: 32 token rows of 16 pieces (16
+// bytes, slab_col channel order), piece q of row m at q ^ (m & 7); km: Km^T,
+// dk channel rows of 4 pieces (32 tokens in slab_col order), piece q of row m
+// at q ^ ((m >> 1) & 3); em, en: e^{G_m} and e^{G_n - G_m} per channel.
 template <int DK>
 struct FRec {
-  i32x4 kg[kFC * DK / 8];
-  i32x4 qg[kFC * DK / 8];
-  i32x4 kh[DK * 4];
-  float gn[DK];
+  i32x4 kp[kFC * DK / 8];
+  i32x4 qp[kFC * DK / 8];
+  i32x4 km[DK * 4];
+  float em[DK];
+  float en[DK];
 };
-// T diag(beta) and lower(A_qk) of one chunk: 32 rows of 4 pieces, columns in
-// slab_col order, swizzled as kh.
+// T diag(beta) with its block 10 zero, and lower(A_qk), of one chunk: 32 rows
+// of 4 pieces, columns in slab_col order, swizzled as km; A_10 (the Gram block
+// of rows 16.. against rows ..15): 16 rows of the left halves of 4 pieces (the
+// right halves, columns 16.., are zero and not stored).
 struct FTri {
   i32x4 tb[kFC * 4];
   i32x4 aq[kFC * 4];
+  i32x2 ka[16 * 4];
 };
 
 template <int DK>
 struct FusedSmem {
   FRec<DK> rec[3];
   FTri tri[2];
-  __bf16 vb[2][kFC * 128];        // v of a chunk ([32][DVT], row-swizzled pieces), then its outputs
-  f32x4 part[2][DK / 32][6][64];  // per chunk and L wave: shares of A_kk (tiles 00, 10, 11) and A_qk
-  float lr[2][16][20];            // full rows of diag(beta) strict_lower(A_kk): blocks 00 and 11
-  float t00[16][20], t11[16][20], l10[16][20];
+  __bf16 vb[2][kFC * 128];         // v of a chunk ([32][DVT], row-swizzled pieces), then its outputs
+  f32x4 part[2][DK / 32][6][64];   // per chunk and channel group: shares of A_kk (tiles 00, 10, 11) and A_qk
+  float lr[2][16][20];             // full rows of -diag(beta) strict_lower(A_kk): blocks 00 and 11
   float beta[2][kFC];
   // stop[x % 3]: a decay out of range in chunk x.  Set while chunk x is built
   // (two intervals before it is used), read by every wave after the barrier
@@ -115,11 +134,11 @@ __device__ __forceinline__ float row_scan(float x) {
   x += row_shr<8>(x);
   return x;
 }
-// The value of lane I of this lane's row of 16 lanes (DPP row_newbcast).
+// The value of lane I of this lane's row of 16 lanes (DPP row_newbcast; every
+// lane has a source, so the move can fold into the instruction that uses it).
 template <int I>
 __device__ __forceinline__ float row_bcast(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + I, 0xF, 0xF,
-                                                               false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + I, 0xF, 0xF, true));
 }
 __device__ __forceinline__ float row_last(float x) { return row_bcast<15>(x); }
 
@@ -132,8 +151,11 @@ __device__ __forceinline__ void static_for(Fn&& f) {
   }
 }
 
-__device__ __forceinline__ void st_bf16(void* base, int byte_off, float x) {
-  *reinterpret_cast<__bf16*>(static_cast<char*>(base) + byte_off) = static_cast<__bf16>(x);
+// (Vector elements reach these by value: a bit cast of a vector element in
+// place reads the wrong element with this compiler.)
+__device__ __forceinline__ u16x2 as_u16x2(int w) { return __builtin_bit_cast(u16x2, w); }
+__device__ __forceinline__ i32x4 ld128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
 struct FusedParams {
@@ -150,26 +172,18 @@ struct FusedParams {
   int H, dv;
 };
 
-// Loads of one chunk for one L lane: q, k, a of rows r16 and 16 + r16, this
-// wave's eight channels (16 bytes each), and one beta.
+// Loads of one chunk for one L lane: q, k, a of its token row (eight
+// channels, 16 bytes each), and one beta.
 struct Raw {
-  i32x4 q[2], k[2], a[2];
+  i32x4 q, k, a;
   uint32_t b;
-};
-// v of one chunk: at most two 16-byte pieces per L lane (128 columns).
-struct VRaw {
-  i32x4 x[2];
-};
-// What the first half of a chunk's build hands to the second.
-struct Mid {
-  float G1[8], em[8], en[8];
-  bf16x8 km0;
 };
 
 template <int DK>
 struct Fused {
-  static constexpr int NLW = DK / 32;  // L waves
-  static constexpr int NPW = 4;        // P waves
+  static constexpr int NCG = DK / 32;   // channel groups of 32
+  static constexpr int NLW = 2 * NCG;   // L waves: two token halves per channel group
+  static constexpr int NPW = 4;         // P waves
   static constexpr int NT = 64 * (NPW + NLW);
   static constexpr int NR = DK / 16, NKS = DK / 32;
 };
@@ -180,13 +194,16 @@ struct Fused {
 template <int DK, int NPA, int NJ>
 __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int tile, FusedSmem<DK>& sm) {
   using F = Fused<DK>;
-  constexpr int NR = F::NR, NKS = F::NKS, NLW = F::NLW;
+  constexpr int NR = F::NR, NKS = F::NKS, NCG = F::NCG, NLW = F::NLW;
   constexpr int DVT = 16 * NJ * NPA;
   constexpr int VPR = DVT / 8;                // 16-byte pieces per v row
   constexpr int VSW = VPR < 4 ? VPR - 1 : 3;  // v row swizzle: piece q of row r at q ^ ((r >> 2) & VSW)
-  constexpr int NVP = (kFC * VPR + 64 * NLW - 1) / (64 * NLW);  // v pieces per L lane
   static_assert(DK == 128, "the L waves cover 32 channels each: dk = 128 is the tuned shape");
-  static_assert(NVP <= 2, "v pieces per lane");
+  static_assert(kFC * VPR <= 64 * NLW, "one v piece per L lane");
+  // Who inverts the diagonal blocks: the P waves before M when a wave holds
+  // 16 state columns, the second-half L waves after M when it holds 32 (its
+  // registers are full).
+  constexpr bool kPSolve = NJ == 1;
 
   const int tid = threadIdx.x, lane = tid & 63, grp = lane >> 4, col = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -238,232 +255,246 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
     return;
   }
   if (tid < 3) sm.stop[tid] = 0;
-  slab_barrier();  // (every wave passes 4 + 2 * chunks barriers)
+  slab_barrier();  // (every wave passes 5 + 2 * chunks barriers)
 
+  // 8-byte piece of a [32][32] tile: row m, columns 4 g .. +3 of the left
+  // (hi = 0) or right (hi = 1) 16 columns (slab_col order puts them side by
+  // side in piece g).
+  auto piece8 = [&](i32x4* t, int m, int hi) {
+    return reinterpret_cast<char*>(&t[4 * m + swz4(m, grp)]) + 8 * hi;
+  };
+
+  // ---- finishing a chunk's record (shares B2 -> tiles tri[B2]) -------------
+  // "Row layout": lane (col, grp) holds row col of a 16x16 block, columns
+  // 4 grp .. 4 grp + 3.  The diagonal blocks are inverted by solve_half, the
+  // rest is written by the L waves after M (finish).
+  auto sum_part = [&](int B2, int t) {
+    f32x4 s = sm.part[B2][0][t][lane];
+#pragma unroll
+    for (int u = 1; u < NCG; ++u) s += sm.part[B2][u][t][lane];
+    return s;
+  };
+  auto pack4 = [](float a0, float a1, float a2, float a3) {
+    bf16x4 v;
+    v[0] = static_cast<__bf16>(a0); v[1] = static_cast<__bf16>(a1);
+    v[2] = static_cast<__bf16>(a2); v[3] = static_cast<__bf16>(a3);
+    return v;
+  };
+  // (I + L_RR)^{-1} diag(beta_R) of diagonal block R, columns
+  // 4 grp + NC hc .. + NC - 1 of each lane's four (NC = 2 or 4): by rows,
+  // step i folds row i (final by then; lane i of this lane's row of 16) into
+  // every row below it.  The rows of -L are gathered through LDS (two waves
+  // of a block write the same values).  The block beside it in tb is zero.
+  auto solve = [&](auto ncc, int B2, int R, int hc) {
+    constexpr int NC = decltype(ncc)::value;
+    FTri& tri = sm.tri[B2];
+    const float* beta = sm.beta[B2];
+    const f32x4 a = sum_part(B2, R == 0 ? 0 : 2);
+    const float br = -beta[16 * R + col];
+    float l[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) l[t] = 4 * grp + t < col ? br * a[t] : 0.f;
+    *reinterpret_cast<float4*>(&sm.lr[R][col][4 * grp]) = make_float4(l[0], l[1], l[2], l[3]);
+    wave_sync();
+    float nL[16];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float4 x4 = *reinterpret_cast<const float4*>(&sm.lr[R][col][4 * q4]);
+      nL[4 * q4] = x4.x; nL[4 * q4 + 1] = x4.y; nL[4 * q4 + 2] = x4.z; nL[4 * q4 + 3] = x4.w;
+    }
+    const int c0 = 4 * grp + NC * hc;
+    float T[NC];
+#pragma unroll
+    for (int u = 0; u < NC; ++u) T[u] = c0 + u == col ? 1.f : 0.f;
+    static_for<0, 15>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+#pragma unroll
+      for (int u = 0; u < NC; ++u) T[u] = fmaf(row_bcast<i>(T[u]), nL[i], T[u]);
+    });
+    using BV = std::conditional_t<NC == 4, bf16x4, bf16x2>;
+    using ZV = std::conditional_t<NC == 4, i32x2, int>;
+    BV tv;
+#pragma unroll
+    for (int u = 0; u < NC; ++u) tv[u] = static_cast<__bf16>(T[u] * beta[16 * R + c0 + u]);
+    *reinterpret_cast<BV*>(piece8(tri.tb, 16 * R + col, R) + 2 * NC * hc) = tv;
+    *reinterpret_cast<ZV*>(piece8(tri.tb, 16 * R + col, 1 - R) + 2 * NC * hc) = ZV{};
+  };
+  using I2 = std::integral_constant<int, 2>;
+  using I4 = std::integral_constant<int, 4>;
   if (lw) {
     // ======================= L waves ==========================================
-    const int w = wave - F::NPW, r16 = col, g4 = grp;
-    const int cb = 32 * w + 8 * g4;  // this lane's first channel
+    const int w = wave - F::NPW, X = w / NCG, cw = w % NCG;  // uniform
+    const int r16 = col, g4 = grp, m = 16 * X + r16;
+    const int cb = 32 * cw + 8 * g4;  // this lane's first channel
     const int ltid = tid - 64 * F::NPW;
-
+    const uint32_t rsk = static_cast<uint32_t>(H) * DK * 2;  // token row stride of q, k, a, bytes
+    const uint32_t vo = m * rsk + cb * 2;
+    const uint32_t vob = static_cast<uint32_t>(lane & 31) * H * 2;
+    // This lane's v / output piece: row ve / VPR, stored piece ve % VPR.
+    // Lanes past the tile's pieces move nothing: their global offset is out
+    // of every range (loads read zero, stores are dropped) and they skip the
+    // LDS write (the output piece they would read is refilled in the same
+    // interval by its own lane).
+    const bool vlane = ltid < kFC * VPR;
+    const int ve = min(ltid, kFC * VPR - 1), vrow = ve / VPR, vpq = ve % VPR;
+    const uint32_t vso = vlane ? vrow * rsv + 16 * (vpq ^ ((vrow >> 2) & VSW)) : 0x80000000u;
+    // Buffer resource over the chunk's rows of one head of a token-major
+    // tensor (rows past the chunk's end read as zero).
+    auto tok_rsrc = [&](const void* base, const ChunkWalk& x, uint32_t row_bytes, uint32_t lane_bytes,
+                        uint32_t head_off) {
+      return buf_rsrc(static_cast<const char*>(base) + static_cast<size_t>(x.t) * row_bytes + head_off,
+                      static_cast<uint32_t>(x.n - 1) * row_bytes + lane_bytes);
+    };
     auto load_raw = [&](const ChunkWalk& x, Raw& r) {
-#pragma unroll
-      for (int X = 0; X < 2; ++X) {
-        const int row = min(16 * X + r16, x.n - 1);
-        const size_t off = ((static_cast<size_t>(x.t + row) * H + h) * DK + cb) * 2;
-        r.q[X] = *reinterpret_cast<const i32x4*>(static_cast<const char*>(p.q) + off);
-        r.k[X] = *reinterpret_cast<const i32x4*>(static_cast<const char*>(p.k) + off);
-        r.a[X] = *reinterpret_cast<const i32x4*>(static_cast<const char*>(p.a) + off);
-      }
-      const int row = min(lane & 31, x.n - 1);
-      r.b = *reinterpret_cast<const uint16_t*>(static_cast<const char*>(p.beta) +
-                                               (static_cast<size_t>(x.t + row) * H + h) * 2);
+      const uint32_t ho = static_cast<uint32_t>(h) * DK * 2;
+      r.q = ld128(tok_rsrc(p.q, x, rsk, DK * 2, ho), vo);
+      r.k = ld128(tok_rsrc(p.k, x, rsk, DK * 2, ho), vo);
+      r.a = ld128(tok_rsrc(p.a, x, rsk, DK * 2, ho), vo);
+      const __amdgpu_buffer_rsrc_t rb = tok_rsrc(p.beta, x, static_cast<uint32_t>(H) * 2, 2, h * 2);
+      r.b = __builtin_amdgcn_raw_buffer_load_b16(rb, vob, 0, 0);
     };
-    // v piece e (of 32 * VPR): row e / VPR, stored piece e % VPR.
-    auto load_v = [&](const ChunkWalk& x, VRaw& vr) {
-      const char* vt = static_cast<const char*>(p.v) + (static_cast<size_t>(x.t) * H + h) * dv * 2 + tile * DVT * 2;
-#pragma unroll
-      for (int i = 0; i < NVP; ++i) {
-        const int e = min(ltid + 64 * NLW * i, kFC * VPR - 1), row = e / VPR, pq = e % VPR;
-        const int src = pq ^ ((row >> 2) & VSW);
-        vr.x[i] = *reinterpret_cast<const i32x4*>(vt + min(row, x.n - 1) * rsv + 16 * src);
-      }
+    auto load_v = [&](const ChunkWalk& x, i32x4& vr) {
+      vr = ld128(tok_rsrc(p.v, x, rsv, DVT * 2, (h * dv + tile * DVT) * 2), vso);
     };
-    auto put_v = [&](int b, const VRaw& vr) {
-#pragma unroll
-      for (int i = 0; i < NVP; ++i) {
-        const int e = min(ltid + 64 * NLW * i, kFC * VPR - 1);
-        *reinterpret_cast<i32x4*>(&sm.vb[b][8 * e]) = vr.x[i];
-      }
+    auto put_v = [&](int b, const i32x4& vr) {
+      if (vlane) *reinterpret_cast<i32x4*>(&sm.vb[b][8 * ve]) = vr;
     };
     // Outputs of a chunk from vb[b] to global memory through a buffer resource
     // that ends at the chunk's last row (any = false: an empty range, every
     // store is dropped, so the call sites need no branch around it).
-    auto store_o = [&](const ChunkWalk& x, int b, bool any) {
-      i32x4 ov[NVP];
-#pragma unroll
-      for (int i = 0; i < NVP; ++i) {
-        const int e = min(ltid + 64 * NLW * i, kFC * VPR - 1);
-        ov[i] = *reinterpret_cast<const i32x4*>(&sm.vb[b][8 * e]);
-      }
+    auto read_o = [&](int b) { return *reinterpret_cast<const i32x4*>(&sm.vb[b][8 * ve]); };
+    auto store_o = [&](const ChunkWalk& x, const i32x4& ov, bool any) {
       const __amdgpu_buffer_rsrc_t ro =
           buf_rsrc(static_cast<char*>(p.o) + (static_cast<size_t>(x.t) * H + h) * dv * 2 + tile * DVT * 2,
                    any ? (x.n - 1) * rsv + DVT * 2 : 0u);
-#pragma unroll
-      for (int i = 0; i < NVP; ++i) {
-        const int e = min(ltid + 64 * NLW * i, kFC * VPR - 1), r = e / VPR, pq = e % VPR;
-        __builtin_amdgcn_raw_buffer_store_b128(ov[i], ro, r * rsv + 16 * (pq ^ ((r >> 2) & VSW)), 0, 0);
-      }
+      __builtin_amdgcn_raw_buffer_store_b128(ov, ro, vso, 0, 0);
     };
 
     // ---- building a chunk's operands (chunk x, loads r, record set R3, shares B2)
     // The running sums of a are kept in log2 units (times log2 e), so every
-    // exponential is one v_exp_f32.  Rows past the chunk's end repeat its
-    // last row (finite values): their a counts as 0, their beta is 0, so every
-    // product they enter is zeroed by T diag(beta), and no k or q needs masking.
+    // exponential is one v_exp_f32.
     constexpr float kLog2e = 1.4426950408889634f;
     auto exp2f_ = [](float x) { return __builtin_amdgcn_exp2f(x); };
     auto unpack = [](const i32x4& v, int j) {
       const uint32_t u = static_cast<uint32_t>(v[j >> 1]);
       return __uint_as_float(j & 1 ? u & 0xffff0000u : u << 16);
     };
-    // Token rows 16 X + r16 (X = 0 or 1) of the record: kg, qg, kh, and the
-    // bf16 fragments kp, qp, km of the Gram products.
-    auto rows = [&](FRec<DK>& rec, int X, const Raw& r, const float* G, const float* em, const float* en,
-                    bf16x8& kp, bf16x8& qp, bf16x8& km) {
-      const int m = 16 * X + r16;
-      bf16x4 kg0, kg1, qg0, qg1;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float kv = unpack(r.k[X], j), qv = unpack(r.q[X], j);
-        const float up = exp2f_(G[j]), dn = exp2f_(-G[j]);
-        const float kpv = kv * up, qpv = qv * up, kmv = kv * dn;
-        kp[j] = static_cast<__bf16>(kpv);
-        qp[j] = static_cast<__bf16>(qpv);
-        km[j] = static_cast<__bf16>(kmv);
-        if (j < 4) {
-          kg0[j] = static_cast<__bf16>(kpv * em[j]);
-          qg0[j] = static_cast<__bf16>(qpv * em[j]);
-        } else {
-          kg1[j - 4] = static_cast<__bf16>(kpv * em[j]);
-          qg1[j - 4] = static_cast<__bf16>(qpv * em[j]);
-        }
-        // (k e^{G_n - G})^T: row = channel, token m at slab position
-        // 8 (m%16 / 4) + 4 X + m % 4.
-        const int ch = cb + j;
-        st_bf16(&rec.kh[4 * ch + swz4(ch, r16 >> 2)], 2 * (4 * X + (r16 & 3)), kmv * en[j]);
-      }
-      // Channels cb + 0..3 and cb + 4..7 in slab_col order: pieces
-      // 4w + 2 (g4 & 1) and the next, half g4 >> 1 of each.
-      const int q0 = 4 * w + 2 * (g4 & 1), half = 8 * (g4 >> 1);
-      char* kr = reinterpret_cast<char*>(&rec.kg[16 * m]);
-      char* qr = reinterpret_cast<char*>(&rec.qg[16 * m]);
-      *reinterpret_cast<bf16x4*>(kr + 16 * swz16(m, q0) + half) = kg0;
-      *reinterpret_cast<bf16x4*>(kr + 16 * swz16(m, q0 + 1) + half) = kg1;
-      *reinterpret_cast<bf16x4*>(qr + 16 * swz16(m, q0) + half) = qg0;
-      *reinterpret_cast<bf16x4*>(qr + 16 * swz16(m, q0 + 1) + half) = qg1;
+    // bf16 bit patterns of the decay range: a in [a_lo, 0] (-0 and +0 too) is
+    // a pattern u with u <= bits(a_lo) as unsigned, where u >= 0x8000, or u =
+    // 0; every positive value and every NaN fails one of the two tests below.
+    const uint32_t a_lo_bits = __float_as_uint(p.a_lo) >> 16;
+    // Slab_col positions of this lane's channels cb + 0..3 and cb + 4..7 in a
+    // row of kp or qp: pieces 4 cw + 2 (g4 & 1) and the next, half g4 >> 1.
+    const int q0 = 4 * cw + 2 * (g4 & 1), half = 8 * (g4 >> 1);
+    auto row_piece = [&](i32x4* base, int mm, int s) {
+      return reinterpret_cast<char*>(&base[16 * mm]) + 16 * swz16(mm, q0 + s) + half;
     };
-    // The shares of A_kk and A_qk over this wave's channels are formed as
-    // transposes (K- as the first operand): lane (r16, g4) then holds row r16
-    // of tile (R, I), columns 4 g4 .. 4 g4 + 3.  Tiles: 0 = A_kk 00,
-    // 1 = A_kk 10, 2 = A_kk 11, 3..5 = the same of A_qk.
-    auto build1 = [&](const ChunkWalk& x, int R3, int B2, const Raw& r, Mid& md) {
+    bf16x8 km0;  // (first-half waves) this lane's Km fragment, kept for the off-diagonal shares
+    // The part of chunk x's build that needs only this wave's rows: the
+    // decay range and sums (build1a), then the operands and Gram shares
+    // (build1b).
+    auto build1a = [&](int R3, const Raw& r, float* G) {
       FRec<DK>& rec = sm.rec[R3];
-      float G0[8];
-      float amin = 0.f, amax = 0.f;
-      const bool v0 = r16 < x.n, v1 = 16 + r16 < x.n;
+      // The decay range, on the bit patterns (two per word).
+      u16x2 mx = {0, 0}, mn = {0xffff, 0xffff};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float a0 = unpack(r.a[0], j), a1 = unpack(r.a[1], j);
-        amin = fminf(amin, fminf(a0, a1));  // (repeated rows hold real values too)
-        amax = fmaxf(amax, fmaxf(a0, a1));
-        G0[j] = v0 ? a0 * kLog2e : 0.f;
-        md.G1[j] = v1 ? a1 * kLog2e : 0.f;
+      for (int i = 0; i < 4; ++i) {
+        const u16x2 u = as_u16x2(r.a[i]);
+        mx = __builtin_elementwise_max(mx, u);
+        mn = __builtin_elementwise_min(mn, u - u16x2{1, 1});  // +0 -> 0xffff; positives below 0x7fff
       }
-      bool nan = false;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        G0[j] = row_scan(G0[j]);
-        const float c0 = row_last(G0[j]);  // sum over rows 0..15
-        md.G1[j] = row_scan(md.G1[j]) + c0;
-        const float gm = x.n > 16 ? c0 : 0.f;  // the reference G_m
-        const float gn = row_last(md.G1[j]);   // the sum over the chunk (NaN if any a is)
-        nan |= gn != gn;
-        md.em[j] = exp2f_(gm);
-        md.en[j] = exp2f_(gn - gm);
-        G0[j] -= gm;
-        md.G1[j] -= gm;
-      }
-      // (fminf/fmaxf drop NaNs; a NaN shows in the chunk's sums instead)
-      if (__builtin_amdgcn_ballot_w64(nan || !(amin >= p.a_lo) || !(amax <= 0.f)) != 0 && lane == 0) {
+      const uint32_t mx1 = max(static_cast<uint32_t>(mx.x), static_cast<uint32_t>(mx.y));
+      const uint32_t mn1 = min(static_cast<uint32_t>(mn.x), static_cast<uint32_t>(mn.y));
+      const bool bad = mx1 > a_lo_bits || mn1 < 0x7fffu;
+      if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) {
         *p.wsflag = 1;
         if (p.err_flag != nullptr) *p.err_flag = 1;
         sm.stop[R3] = 1;
       }
-      bf16x8 kp0, qp0;
-      rows(rec, 0, r, G0, md.em, md.en, kp0, qp0, md.km0);
-      if (r16 == 0) {
-        float4 g0, g1;
-        g0.x = md.em[0] * md.en[0]; g0.y = md.em[1] * md.en[1]; g0.z = md.em[2] * md.en[2]; g0.w = md.em[3] * md.en[3];
-        g1.x = md.em[4] * md.en[4]; g1.y = md.em[5] * md.en[5]; g1.z = md.em[6] * md.en[6]; g1.w = md.em[7] * md.en[7];
-        *reinterpret_cast<float4*>(&rec.gn[cb]) = g0;
-        *reinterpret_cast<float4*>(&rec.gn[cb + 4]) = g1;
+      // Running sums over this half's 16 rows.  The first half's total is G_m
+      // (with n <= 16 that is G_n: the zero rows add nothing): its rows take
+      // G - G_m, and the second half's own sums are already G - G_m.
+      float ref[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) G[j] = row_scan(unpack(r.a, j) * kLog2e);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        ref[j] = row_last(G[j]);  // G_m (first half) or G_n - G_m (second half)
+        if (X == 0) G[j] -= ref[j];
       }
-      const f32x4 z = zero4();
-      sm.part[B2][w][0][lane] = mma(md.km0, kp0, z);
-      sm.part[B2][w][3][lane] = mma(md.km0, qp0, z);
-      if (w == 0 && lane < 32) sm.beta[B2][lane] = lane < x.n ? __uint_as_float(r.b << 16) : 0.f;
+      // e^{G_m} (first half) or e^{G_n - G_m} (second half) of channel
+      // cb + (r16 & 7), stored by lanes 0..7 of the row: select the channel,
+      // then one exponential.
+      {
+        const bool s0 = r16 & 1, s1 = r16 & 2, s2 = r16 & 4;
+        const float a01 = s0 ? ref[1] : ref[0], a23 = s0 ? ref[3] : ref[2];
+        const float a45 = s0 ? ref[5] : ref[4], a67 = s0 ? ref[7] : ref[6];
+        const float b03 = s1 ? a23 : a01, b47 = s1 ? a67 : a45;
+        const float e = exp2f_(s2 ? b47 : b03);
+        if (r16 < 8) (X == 0 ? rec.em : rec.en)[cb + r16] = e;
+      }
     };
-    auto build2 = [&](int R3, int B2, const Raw& r, const Mid& md) {
-      bf16x8 kp1, qp1, km1;
-      rows(sm.rec[R3], 1, r, md.G1, md.em, md.en, kp1, qp1, km1);
+    auto build1b = [&](int R3, int B2, const Raw& r, const float* G) {
+      FRec<DK>& rec = sm.rec[R3];
+      // Kp, Qp rows (slab_col order) and Km^T, and the Gram fragments.
+      bf16x8 kp, qp, km;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float kv = unpack(r.k, j), qv = unpack(r.q, j);
+        const float up = exp2f_(G[j]), dn = exp2f_(-G[j]);
+        kp[j] = static_cast<__bf16>(kv * up);
+        qp[j] = static_cast<__bf16>(qv * up);
+        km[j] = static_cast<__bf16>(kv * dn);
+      }
+      const i32x4 kw = __builtin_bit_cast(i32x4, kp), qw = __builtin_bit_cast(i32x4, qp);
+      *reinterpret_cast<i32x2*>(row_piece(rec.kp, m, 0)) = i32x2{kw[0], kw[1]};
+      *reinterpret_cast<i32x2*>(row_piece(rec.kp, m, 1)) = i32x2{kw[2], kw[3]};
+      *reinterpret_cast<i32x2*>(row_piece(rec.qp, m, 0)) = i32x2{qw[0], qw[1]};
+      *reinterpret_cast<i32x2*>(row_piece(rec.qp, m, 1)) = i32x2{qw[2], qw[3]};
+      // Km^T: row = channel cb + j (cb is a multiple of 8, so the swizzle of
+      // row cb + j is j >> 1), token m at slab position 8 (m%16 / 4) + 4 X + m % 4.
+      char* kt = reinterpret_cast<char*>(&rec.km[4 * cb]) + 2 * (4 * X + (r16 & 3));
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        *reinterpret_cast<__bf16*>(kt + 16 * (4 * j + ((r16 >> 2) ^ (j >> 1)))) = km[j];
+      // Shares of the diagonal blocks over this wave's channels, formed as
+      // transposes (Km first): lane (r16, g4) then holds row r16 of the tile,
+      // columns 4 g4 .. 4 g4 + 3.  Tiles: 0 = A_kk 00, 1 = A_kk 10,
+      // 2 = A_kk 11, 3..5 = the same of A_qk.
       const f32x4 z = zero4();
-      sm.part[B2][w][1][lane] = mma(md.km0, kp1, z);
-      sm.part[B2][w][2][lane] = mma(km1, kp1, z);
-      sm.part[B2][w][4][lane] = mma(md.km0, qp1, z);
-      sm.part[B2][w][5][lane] = mma(km1, qp1, z);
+      sm.part[B2][cw][X == 0 ? 0 : 2][lane] = mma(km, kp, z);
+      sm.part[B2][cw][X == 0 ? 3 : 5][lane] = mma(km, qp, z);
+      if (X == 0) km0 = km;
+      if (w == 0 && lane < 32) sm.beta[B2][lane] = __uint_as_float(r.b << 16);
+    };
+    auto build1 = [&](int R3, int B2, const Raw& r) {
+      float G[8];
+      build1a(R3, r, G);
+      build1b(R3, B2, r, G);
+    };
+    // After M (first-half waves): the off-diagonal shares Km0 Kp1^T and
+    // Km0 Qp1^T, with rows 16.. of kp and qp read back from LDS.
+    auto build2 = [&](int R3, int B2) {
+      if (X != 0) return;
+      const FRec<DK>& rec = sm.rec[R3];
+      auto frag_of = [&](const i32x4* base) {
+        const i32x2 lo2 = *reinterpret_cast<const i32x2*>(row_piece(const_cast<i32x4*>(base), 16 + r16, 0));
+        const i32x2 hi2 = *reinterpret_cast<const i32x2*>(row_piece(const_cast<i32x4*>(base), 16 + r16, 1));
+        return __builtin_bit_cast(bf16x8, i32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
+      };
+      const bf16x8 kp1 = frag_of(rec.kp), qp1 = frag_of(rec.qp);
+      const f32x4 z = zero4();
+      sm.part[B2][cw][1][lane] = mma(km0, kp1, z);
+      sm.part[B2][cw][4][lane] = mma(km0, qp1, z);
     };
 
-    // ---- finishing a chunk (shares B2 -> tiles tri[B2]) ---------------------
-    // "Row layout": lane (r16, g4) holds row r16 of a 16x16 block, columns
-    // 4 g4 .. 4 g4 + 3; "column layout": column r16, rows 4 g4 .. 4 g4 + 3
-    // (the layout of an MFMA result).
-    auto sum_part = [&](int B2, int t) {
-      f32x4 s = sm.part[B2][0][t][lane];
-#pragma unroll
-      for (int u = 1; u < NLW; ++u) s += sm.part[B2][u][t][lane];
-      return s;
-    };
-    // 8-byte piece of a [32][32] tile: row m, columns 4 g4 .. +3 of the left
-    // (hi = 0) or right (hi = 1) 16 columns (slab_col order puts them side by
-    // side in piece g4).
-    auto piece8 = [&](i32x4* t, int m, int hi) {
-      return reinterpret_cast<bf16x4*>(reinterpret_cast<char*>(&t[4 * m + swz4(m, g4)]) + 8 * hi);
-    };
-    auto pack4 = [](float a0, float a1, float a2, float a3) {
-      bf16x4 v;
-      v[0] = static_cast<__bf16>(a0); v[1] = static_cast<__bf16>(a1);
-      v[2] = static_cast<__bf16>(a2); v[3] = static_cast<__bf16>(a3);
-      return v;
-    };
-    // (I + L_RR)^{-1} of diagonal block R (L wave R): by rows, step i folds
-    // row i (final by then; lane i of this lane's row of 16) into every row
-    // below it.
-    auto solve_diag = [&](int B2, int R) {
+    // After M: first-half wave 2 writes lower(A_qk), wave 3 A_10 (their SIMDs
+    // host the P waves that narrow tiles leave without state).
+    auto finish = [&](int B2) {
       FTri& tri = sm.tri[B2];
-      const float* beta = sm.beta[B2];
-      const f32x4 a = sum_part(B2, R == 0 ? 0 : 2);
-      const float br = beta[16 * R + r16];
-      const float4 bc = *reinterpret_cast<const float4*>(&beta[16 * R + 4 * g4]);
-      float l[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) l[t] = 4 * g4 + t < r16 ? br * a[t] : 0.f;
-      *reinterpret_cast<float4*>(&sm.lr[R][r16][4 * g4]) = make_float4(l[0], l[1], l[2], l[3]);
-      wave_sync();
-      float L[16];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 x4 = *reinterpret_cast<const float4*>(&sm.lr[R][r16][4 * q4]);
-        L[4 * q4] = x4.x; L[4 * q4 + 1] = x4.y; L[4 * q4 + 2] = x4.z; L[4 * q4 + 3] = x4.w;
-      }
-      float T[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) T[t] = 4 * g4 + t == r16 ? 1.f : 0.f;
-      static_for<0, 15>([&](auto ic) {
-        constexpr int i = decltype(ic)::value;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) T[t] -= L[i] * row_bcast<i>(T[t]);
-      });
-      float(*tt)[20] = R == 0 ? sm.t00 : sm.t11;
-      *reinterpret_cast<float4*>(&tt[r16][4 * g4]) = make_float4(T[0], T[1], T[2], T[3]);
-      *piece8(tri.tb, 16 * R + r16, R) = pack4(T[0] * bc.x, T[1] * bc.y, T[2] * bc.z, T[3] * bc.w);
-      if (R == 0) *piece8(tri.tb, r16, 1) = pack4(0.f, 0.f, 0.f, 0.f);  // the upper-right block
-    };
-    auto finish1 = [&](int B2) {  // before M
-      if (w == 0 || w == 1) {
-        solve_diag(B2, w);
-      } else if (w == 2) {
-        FTri& tri = sm.tri[B2];
+      if (!kPSolve && X == 1) {
+        solve(I2{}, B2, cw >> 1, cw & 1);
+      } else if (X == 0 && cw == 2) {
         const f32x4 a00 = sum_part(B2, 3), a10 = sum_part(B2, 4), a11 = sum_part(B2, 5);
         float m00[4], m11[4];
 #pragma unroll
@@ -472,67 +503,41 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
           m00[t] = on ? a00[t] : 0.f;
           m11[t] = on ? a11[t] : 0.f;
         }
-        *piece8(tri.aq, r16, 0) = pack4(m00[0], m00[1], m00[2], m00[3]);
-        *piece8(tri.aq, 16 + r16, 0) = pack4(a10[0], a10[1], a10[2], a10[3]);
-        *piece8(tri.aq, 16 + r16, 1) = pack4(m11[0], m11[1], m11[2], m11[3]);
-        *piece8(tri.aq, r16, 1) = pack4(0.f, 0.f, 0.f, 0.f);
-      } else {
+        *reinterpret_cast<bf16x4*>(piece8(tri.aq, r16, 0)) = pack4(m00[0], m00[1], m00[2], m00[3]);
+        *reinterpret_cast<bf16x4*>(piece8(tri.aq, 16 + r16, 0)) = pack4(a10[0], a10[1], a10[2], a10[3]);
+        *reinterpret_cast<bf16x4*>(piece8(tri.aq, 16 + r16, 1)) = pack4(m11[0], m11[1], m11[2], m11[3]);
+        *reinterpret_cast<bf16x4*>(piece8(tri.aq, r16, 1)) = pack4(0.f, 0.f, 0.f, 0.f);
+      } else if (X == 0 && cw == 3) {
         const f32x4 a10 = sum_part(B2, 1);
-        const float br = sm.beta[B2][16 + r16];
-        *reinterpret_cast<float4*>(&sm.l10[r16][4 * g4]) =
-            make_float4(br * a10[0], br * a10[1], br * a10[2], br * a10[3]);
-      }
-    };
-    // After M (L wave 3): T_10 = -T_11 (L_10 T_00), two fp32 MFMA products
-    // (16x16x4, contraction index 4 g4 + kb); the result is in column layout.
-    auto finish2 = [&](int B2) {
-      if (w != 3) return;
-      f32x4 W = zero4();
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        W = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.l10[r16][4 * g4 + kb], sm.t00[4 * g4 + kb][r16], W, 0, 0, 0);
-      f32x4 T10 = zero4();
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        T10 = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.t11[r16][4 * g4 + kb], W[kb], T10, 0, 0, 0);
-      const float bc = sm.beta[B2][r16];
-      char* tb = reinterpret_cast<char*>(sm.tri[B2].tb);
-      const int sp = slab_col(r16);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int row = 16 + 4 * g4 + t;
-        *reinterpret_cast<__bf16*>(tb + 16 * (4 * row + swz4(row, sp >> 3)) + 2 * (sp & 7)) =
-            static_cast<__bf16>(-T10[t] * bc);
+        tri.ka[4 * r16 + swz4(r16, g4)] = __builtin_bit_cast(i32x2, pack4(a10[0], a10[1], a10[2], a10[3]));
       }
     };
 
     // Walkers: wr the chunk whose q, k, a, beta are loaded next, wv whose v,
-    // wb whose operands are built next, wo whose outputs are stored next.
+    // wo whose outputs are stored next.
     Raw rs[2];
-    VRaw vs[2];
-    Mid md;
-    ChunkWalk wr = first_chunk(), wv = wr, wb = wr, wo = wr;
-    // Prologue: chunk c_lo complete and chunk c_lo + 1 built, in three steps.
+    i32x4 vs[2];
+    ChunkWalk wr = first_chunk(), wv = wr, wo = wr;
+    // Prologue: chunk c_lo complete and chunk c_lo + 1 built, in four steps.
     load_raw(wr, rs[0]);
     next_chunk(wr);
     load_raw(wr, rs[1]);
     next_chunk(wr);
     load_v(wv, vs[0]);
     next_chunk(wv);
+    build1(b3(c_lo), b2(c_lo), rs[0]);
+    slab_barrier();
+    build2(b3(c_lo), b2(c_lo));
+    put_v(b2(c_lo), vs[0]);
     load_v(wv, vs[1]);
     next_chunk(wv);
-    build1(wb, b3(c_lo), b2(c_lo), rs[0], md);
-    build2(b3(c_lo), b2(c_lo), rs[0], md);
     slab_barrier();
-    next_chunk(wb);
-    finish1(b2(c_lo));
-    build1(wb, b3(c_lo + 1), b2(c_lo + 1), rs[1], md);
+    build1(b3(c_lo + 1), b2(c_lo + 1), rs[1]);
+    slab_barrier();
+    build2(b3(c_lo + 1), b2(c_lo + 1));
+    finish(b2(c_lo));
     load_raw(wr, rs[0]);  // chunk c_lo + 2
     next_chunk(wr);
-    slab_barrier();
-    finish2(b2(c_lo));
-    build2(b3(c_lo + 1), b2(c_lo + 1), rs[1], md);
-    put_v(b2(c_lo), vs[0]);
     slab_barrier();  // A: chunk c_lo complete
     const bool live = sm.stop[b3(c_lo)] == 0;
     int last = c_lo;  // the last chunk the P waves processed
@@ -546,26 +551,26 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
       using std::integral_constant;
       auto iter = [&](auto kc, int c) {
         constexpr int K = decltype(kc)::value, K1 = K ^ 1;
+        const bool go = sm.stop[b3(c + 1)] == 0;  // (final since chunk c + 1 was built)
         // Every memory operation here is unconditional (the output store of
         // the first iteration has an empty range), so the compiler can count
         // what is in flight and waits for the loads it needs, not for
         // everything issued before.
-        store_o(wo, b2(c - 1), c > c_lo);
-        if (c > c_lo) next_chunk(wo);
         load_raw(wr, rs[K1]);  // chunk c + 3
         next_chunk(wr);
         load_v(wv, vs[K]);  // chunk c + 2
         next_chunk(wv);
-        finish1(b2(c + 1));
-        next_chunk(wb);
-        build1(wb, b3(c + 2), b2(c + 2), rs[K], md);
+        build1(b3(c + 2), b2(c + 2), rs[K]);
         slab_barrier();  // M
-        finish2(b2(c + 1));
-        build2(b3(c + 2), b2(c + 2), rs[K], md);
+        const i32x4 ov = read_o(b2(c - 1));  // (vb[b2(c + 1)], before put_v refills it)
+        build2(b3(c + 2), b2(c + 2));
+        finish(b2(c + 1));
+        store_o(wo, ov, c > c_lo);
+        if (c > c_lo) next_chunk(wo);
         put_v(b2(c + 1), vs[K1]);
         slab_barrier();  // A: chunk c + 1 complete
         last = c;
-        return sm.stop[b3(c + 1)] == 0;
+        return go;
       };
       for (int c = c_lo; c < c_hi; c += 2) {
         if (!iter(integral_constant<int, 0>{}, c)) break;
@@ -573,12 +578,24 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
       }
     }
     // The outputs of the last chunk the P waves processed (wo points at it).
-    if (live) store_o(wo, b2(last), true);
+    if (live) store_o(wo, read_o(b2(last)), true);
     return;
   }
 
   // ========================= P waves ==========================================
   const bool active = wave < NPA;
+  // The diagonal solves (16 columns per wave): with two or fewer waves holding
+  // state, waves 2 and 3 (none) invert a block each; otherwise every P wave
+  // takes two columns of a block.
+  auto p_solve = [&](int B2) {
+    if constexpr (kPSolve) {
+      if constexpr (NPA <= 2) {
+        if (wave >= 2) solve(I4{}, B2, wave - 2, 0);
+      } else {
+        solve(I2{}, B2, wave >> 1, wave & 1);
+      }
+    }
+  };
   const int jl = 16 * NJ * (active ? wave : 0);  // first column of this wave's slab within the tile
   const int jw = tile * DVT + jl;
 
@@ -611,6 +628,20 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(S[R][J][i]), rs, slane[i] + 16 * J, 0, 0);
     }
   };
+  // The state's rows scaled by a per-channel factor (rows 16R + 4 grp + i).
+  auto scale_rows = [&](const float* f) {
+#pragma unroll
+    for (int R = 0; R < NR; ++R) {
+      const float4 g = *reinterpret_cast<const float4*>(&f[16 * R + 4 * grp]);
+#pragma unroll
+      for (int J = 0; J < NJ; ++J) {
+        S[R][J][0] *= g.x;
+        S[R][J][1] *= g.y;
+        S[R][J][2] *= g.z;
+        S[R][J][3] *= g.w;
+      }
+    }
+  };
   using OV = std::conditional_t<NJ == 2, i32x4, i32x2>;
   auto vaddr = [&](int r, int j) { return r * DVT + (((j >> 3) ^ ((r >> 2) & VSW)) << 3) + (j & 7); };
   auto stage_o = [&](int b, int T, const OV& ov) {
@@ -622,9 +653,12 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
   auto frag16 = [&](const i32x4* base, int m, int q) { return __builtin_bit_cast(bf16x8, base[16 * m + swz16(m, q)]); };
   auto frag4 = [&](const i32x4* base, int m, int q) { return __builtin_bit_cast(bf16x8, base[4 * m + swz4(m, q)]); };
 
-  slab_barrier();  // the prologue's three steps
+  // The prologue's four steps (the L waves build chunks c_lo and c_lo + 1).
   slab_barrier();
-  slab_barrier();  // A: chunk c_lo complete (the L waves built it)
+  p_solve(b2(c_lo));
+  slab_barrier();
+  slab_barrier();
+  slab_barrier();  // A: chunk c_lo complete
   bool done = sm.stop[b3(c_lo)] != 0;
   ChunkWalk w = first_chunk();
   for (int c = c_lo; c < c_hi && !done; ++c) {
@@ -632,8 +666,15 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
     const FRec<DK>& r = sm.rec[b3(c)];
     const FTri& tri = sm.tri[b];
     const bool is_ck = w.t + w.n == w.nck;
+    const bool stop_next = sm.stop[b3(c + 1)] != 0;  // (final since chunk c + 1 was built)
+    bf16x8 bU[NJ];
+    // S' rounded to bf16 as MFMA operands (kept across M when a wave holds 16
+    // columns; rebuilt after it otherwise, for the registers).
+    constexpr bool kKeepS = NJ == 1;
+    bf16x8 bSk[NKS][NJ];
     if (active) {
-      // ---- P = (k g) S, Z = V - P, U = T diag(beta) Z --------------------------
+      scale_rows(r.em);  // S' = e^{G_m} S
+      // ---- P = Kp S', Z = V - P, U = T diag(beta) Z ---------------------------
       f32x4 P[2][NJ];
 #pragma unroll
       for (int T = 0; T < 2; ++T)
@@ -643,39 +684,43 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
       for (int s = 0; s < NKS; ++s) {
         bf16x8 bS[NJ];
 #pragma unroll
-        for (int J = 0; J < NJ; ++J) bS[J] = pack_frag(S[2 * s][J], S[2 * s + 1][J]);
+        for (int J = 0; J < NJ; ++J) {
+          bS[J] = pack_frag(S[2 * s][J], S[2 * s + 1][J]);
+          if (kKeepS) bSk[s][J] = bS[J];
+        }
 #pragma unroll
         for (int T = 0; T < 2; ++T) {
-          const bf16x8 ak = frag16(r.kg, 16 * T + col, 4 * s + grp);
+          const bf16x8 ak = frag16(r.kp, 16 * T + col, 4 * s + grp);
 #pragma unroll
           for (int J = 0; J < NJ; ++J) P[T][J] = mma(ak, bS[J], P[T][J]);
         }
       }
-      bf16x8 bU[NJ];
-      {
-        bf16x8 bZ[NJ];
+      // U_0 = T_00 diag(beta_0) Z_0 (row block 0 of tb: its block 01 is zero),
+      // Y = Z_1 - A_10 U_0, U_1 = T_11 diag(beta_1) Y (row block 1 of tb: its
+      // block 10 is zero); the zero halves of the A operands make the other
+      // halves of the B operands irrelevant.
+      const bf16x8 at0 = frag4(tri.tb, col, grp), at1 = frag4(tri.tb, 16 + col, grp);
+      const i32x2 kl = tri.ka[4 * col + swz4(col, grp)];
+      const bf16x8 a10 = __builtin_bit_cast(bf16x8, i32x4{kl[0], kl[1], 0, 0});
 #pragma unroll
-        for (int J = 0; J < NJ; ++J) {
-          f32x4 z0, z1;
+      for (int J = 0; J < NJ; ++J) {
+        f32x4 z0, z1;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            z0[i] = vval(b, 0, J, i) - P[0][J][i];
-            z1[i] = vval(b, 1, J, i) - P[1][J][i];
-          }
-          bZ[J] = pack_frag(z0, z1);
+        for (int i = 0; i < 4; ++i) {
+          z0[i] = vval(b, 0, J, i) - P[0][J][i];
+          z1[i] = vval(b, 1, J, i) - P[1][J][i];
         }
-        f32x4 U[2][NJ];
-#pragma unroll
-        for (int T = 0; T < 2; ++T) {
-          const bf16x8 at = frag4(tri.tb, 16 * T + col, grp);
-#pragma unroll
-          for (int J = 0; J < NJ; ++J) U[T][J] = mma(at, bZ[J], zero4());
-        }
-#pragma unroll
-        for (int J = 0; J < NJ; ++J) bU[J] = pack_frag(U[0][J], U[1][J]);
+        const f32x4 U0 = mma(at0, pack_frag(z0, z1), zero4());
+        const f32x4 W = mma(a10, pack_frag(U0, U0), zero4());
+        const f32x4 y = z1 - W;
+        const f32x4 U1 = mma(at1, pack_frag(y, y), zero4());
+        bU[J] = pack_frag(U0, U1);
       }
-      slab_barrier();  // M (v of this chunk is dead from here on: the outputs take its place)
-      // ---- O^T = S^T (q g)^T + U^T A_qk^T --------------------------------------
+    }
+    p_solve(b2(c + 1));
+    slab_barrier();  // M (v of this chunk is dead from here on: the outputs take its place)
+    if (active) {
+      // ---- O^T = S'^T Qp^T + U^T A_qk^T ---------------------------------------
       f32x4 OT[NJ][2];
 #pragma unroll
       for (int T = 0; T < 2; ++T)
@@ -685,10 +730,10 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
       for (int s = 0; s < NKS; ++s) {
         bf16x8 bS[NJ];
 #pragma unroll
-        for (int J = 0; J < NJ; ++J) bS[J] = pack_frag(S[2 * s][J], S[2 * s + 1][J]);
+        for (int J = 0; J < NJ; ++J) bS[J] = kKeepS ? bSk[s][J] : pack_frag(S[2 * s][J], S[2 * s + 1][J]);
 #pragma unroll
         for (int T = 0; T < 2; ++T) {
-          const bf16x8 aq = frag16(r.qg, 16 * T + col, 4 * s + grp);
+          const bf16x8 aq = frag16(r.qp, 16 * T + col, 4 * s + grp);
 #pragma unroll
           for (int J = 0; J < NJ; ++J) OT[J][T] = mma(bS[J], aq, OT[J][T]);
         }
@@ -705,28 +750,20 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
         }
         stage_o(b, T, __builtin_bit_cast(OV, ov));
       }
-      // ---- S <- diag(g_n) S + (k g_n/g)^T U -----------------------------------
+      // ---- S <- e^{G_n - G_m} (S' + Km^T U) -----------------------------------
 #pragma unroll
       for (int R = 0; R < NR; ++R) {
-        const float4 gn = *reinterpret_cast<const float4*>(&r.gn[16 * R + 4 * grp]);
-        const bf16x8 a0 = frag4(r.kh, 16 * R + col, grp);
+        const bf16x8 a0 = frag4(r.km, 16 * R + col, grp);
 #pragma unroll
-        for (int J = 0; J < NJ; ++J) {
-          S[R][J][0] *= gn.x;
-          S[R][J][1] *= gn.y;
-          S[R][J][2] *= gn.z;
-          S[R][J][3] *= gn.w;
-          S[R][J] = mma(a0, bU[J], S[R][J]);
-        }
+        for (int J = 0; J < NJ; ++J) S[R][J] = mma(a0, bU[J], S[R][J]);
       }
+      scale_rows(r.en);
       if (is_ck)
         store_state(p.page_pool + static_cast<int64_t>(ld_const(p.ck_slot, w.ck)) * p.page_elems +
                     static_cast<int64_t>(h) * DK * dv);
-    } else {
-      slab_barrier();  // M
     }
     slab_barrier();  // A
-    done = sm.stop[b3(c + 1)] != 0;
+    done = stop_next;
     next_chunk(w);
   }
   if (active && !done && p.s_final != nullptr) store_state(p.s_final + state_off);
