@@ -3,21 +3,24 @@
 
 A timed step is one pass of the prefill path over the variable-length
 workload (16 sequences with log-uniform lengths in [1024, 32768], H=32,
-dk=dv=128, bf16 inputs, fp32 states from nonzero committed S0, chunk 64,
-checkpoints at every 4096 tokens plus the exact tail written into page
-slots) followed by packing the 16 final states into page slots.  `value` is
-that step's whole-job throughput in tokens/s with inputs resident in HBM.
+dk=dv=128, bf16 inputs, fp32 states from nonzero committed S0, 32-token
+chunks (the fused kernel), checkpoints at every 4096 tokens plus the exact
+tail written into page slots) followed by packing the 16 final states into
+page slots.  `value` is that step's whole-job throughput in tokens/s with
+inputs resident in HBM.
 
-In the same run, and reported under "parts": the single-sequence prefill
-(T=8192, checkpoints every 512), the same sequence as 8 segments through
+In the same run, and reported under "parts": the same varlen prefill on the
+two-kernel path at chunk 64, the single-sequence prefill (T=8192, chunk 64,
+checkpoints every 512), the same sequence as 8 segments through
 segment summaries, composition and per-segment prefill (context-parallel
 prefill on one GPU), the front end (convolution, SiLU, L2Norm, gates) over the
 varlen workload's sequences, 64 in-place decode steps (B=256 sessions),
 verify-and-replay (B=64, H=16, d=32, 8 drafts), one speculative round's
 rollback through the raw-input ring against full state snapshots, and
-pack/unpack of 16
-checkpoint states, each with its algorithmic bytes or flops against the
-MI355X peaks, plus the float64 CPU oracle timed on a bounded sample.
+pack/unpack of the
+decode batch's 256 states (537 MB, past the 256 MB Infinity Cache), each
+with its algorithmic bytes or flops against the MI355X peaks, plus the
+float64 CPU oracle timed on a bounded sample on the host's cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only a,b] [--no-cpu]
 """
@@ -38,9 +41,11 @@ HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "linear_attention_recurrence_kda_amd", "csrc")
-# The prefill kernels' sources (the traffic figure is stamped with their hash).
+# The prefill kernels' sources (a traffic figure is stamped with their hash).
 PREFILL_SRC = [os.path.join(CSRC, f) for f in
                ("kda_prefill_kernels.hpp", "kda_prefill.hip", "kda_prefill_slab.hpp", "kda_slab.hip")]
+FUSED_SRC = [os.path.join(CSRC, f) for f in ("kda_prefill_kernels.hpp", "kda_prefill_slab.hpp", "kda_fused.hip")]
+HEAD_CHUNK = 32  # the headline prefill's chunk (the fused kernel)
 
 
 def log(*a):
@@ -142,7 +147,7 @@ def committed_traffic(name, kernel_src):
 
 
 # ---------------------------------------------------------------- parts
-def bench_prefill(torch, kda, inputs, w, steps, warmup, pack_final, label, gate=False):
+def bench_prefill(torch, kda, inputs, w, steps, warmup, pack_final, label, gate=False, chunk=64):
     d = {n: torch.from_numpy(w[n]).to(torch.bfloat16).cuda() for n in ("q", "k", "v", "a", "beta")}
     g_min = None
     if gate:
@@ -169,13 +174,14 @@ def bench_prefill(torch, kda, inputs, w, steps, warmup, pack_final, label, gate=
     final_slots = torch.arange(n_ck, n_ck + N, dtype=torch.int32, device="cuda")
     o = torch.empty((T, H, dv), dtype=torch.bfloat16, device="cuda")
     sf = torch.empty((N, H, dk, dv), dtype=torch.float32, device="cuda")
-    ws = torch.empty(kda.prefill_workspace_size(N, T, H, dk, dv, 64, n_ck), dtype=torch.uint8,
+    ws = torch.empty(kda.prefill_workspace_size(N, T, H, dk, dv, chunk, n_ck), dtype=torch.uint8,
                      device="cuda")
+    _, kernels = kda.prefill_plan(cu, H, dk, dv, chunk, ck)
 
     def step(ev):
         if ev is not None:
             ev[0].record()
-        kda.chunk_prefill(d["q"], d["k"], d["v"], d["a"], d["beta"], cu, s0=s0, chunk=64,
+        kda.chunk_prefill(d["q"], d["k"], d["v"], d["a"], d["beta"], cu, s0=s0, chunk=chunk,
                           checkpoints=ck, ckpt_slots=slots, page_pool=pool, o=o, s_final=sf,
                           workspace=ws, gate_g_min=g_min)
         if ev is not None:
@@ -184,10 +190,10 @@ def bench_prefill(torch, kda, inputs, w, steps, warmup, pack_final, label, gate=
             kda.pack_heads(sf, final_slots, pool)
 
     ms, kms = run_steps(torch, step, steps, warmup)
-    flops = prefill_flops(T, H, dk, dv, 64)
+    flops = prefill_flops(T, H, dk, dv, chunk)
     byts = prefill_bytes(T, H, dk, dv, N, n_ck, s0=s0 is not None)
     res = {
-        "workload": label, "tokens": T, "n_seqs": N, "n_ckpt": n_ck,
+        "workload": label, "kernels": kernels, "chunk": chunk, "tokens": T, "n_seqs": N, "n_ckpt": n_ck,
         "ms_per_step": ms, "kernel_ms": kms,
         "tokens_per_s": T / (ms * 1e-3),
         "kernel_tokens_per_s": T / (kms * 1e-3),
@@ -485,30 +491,39 @@ def bench_replay(torch, kda, inputs, steps, warmup, shape="pages", state_dtype="
 
 
 def bench_pack(torch, kda, steps, warmup):
-    B, H, d = 16, 32, 128
+    """Pack the decode batch's 256 fp32 states (H=32, dk=dv=128: 537 MB, past
+    the 256 MB Infinity Cache) into 256 page slots in a shuffled order, and
+    unpack them back, timed apart."""
+    B, H, d = 256, 32, 128
     g = torch.Generator(device="cuda").manual_seed(3)
     state = torch.randn((B, H, d, d), device="cuda", generator=g)
     pool = torch.zeros((B, H * d * d), device="cuda")
-    slots = torch.arange(B, dtype=torch.int32, device="cuda")
+    slots = torch.randperm(B, generator=g, device="cuda").to(torch.int32)
     back = torch.empty_like(state)
-
-    reps = 10
-
-    def step(ev):
-        if ev is not None:
-            ev[0].record()
-        for _ in range(reps):
-            kda.pack_heads(state, slots, pool)
-            kda.unpack_heads(pool, slots, H, d, d, state=back)
-        if ev is not None:
-            ev[1].record()
-
-    ms, kms = run_steps(torch, step, steps, warmup)
-    kms /= reps
-    byts = 2 * (2 * B * H * d * d * 4)  # pack and unpack, each reads and writes 16 states
-    return {"workload": "pack+unpack: 16 states of H=32, dk=dv=128 fp32 into 2 MiB pages",
-            "us_per_pack_unpack": kms * 1e3, "hbm_gbs": byts / (kms * 1e-3) / 1e9,
-            "hbm_frac": byts / (kms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    ev_p = Timer(torch, steps)
+    ev_u = Timer(torch, steps)
+    for i in range(warmup + steps):
+        j = i - warmup
+        if j >= 0:
+            ev_p.ev[j][0].record()
+        kda.pack_heads(state, slots, pool)
+        if j >= 0:
+            ev_p.ev[j][1].record()
+            ev_u.ev[j][0].record()
+        kda.unpack_heads(pool, slots, H, d, d, state=back)
+        if j >= 0:
+            ev_u.ev[j][1].record()
+    torch.cuda.synchronize()
+    assert torch.equal(back, state)
+    byts = 2 * B * H * d * d * 4  # one pass reads and writes 256 states
+    res = {"workload": "pack / unpack: 256 states of H=32, dk=dv=128 fp32 (537 MB) into 2 MiB page slots, "
+                       "shuffled slot order"}
+    for name, t in (("pack", ev_p), ("unpack", ev_u)):
+        ms = t.kernel_ms()
+        res[name] = {"us": ms * 1e3, "hbm_gbs": byts / (ms * 1e-3) / 1e9,
+                     "hbm_frac": byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    del state, pool, back
+    return res
 
 
 def copy_calibration(torch):
@@ -521,23 +536,62 @@ def copy_calibration(torch):
     return {"bytes_read": x.numel() * 4, "bytes_written": y.numel() * 4}
 
 
-def cpu_baseline(inputs, w):
-    """The float64 oracle, untouched, on the first 2048 tokens of the longest
-    sequence of the workload (all 32 heads), on one thread."""
+_CPU_W = None  # the workload the baseline's worker processes read (inherited by fork)
+
+
+def _oracle_unit(u):
+    """One unit of the CPU baseline: the float64 oracle, untouched, over the
+    first L tokens of sequence n for heads h0 .. h0 + HG - 1, on one thread."""
     import oracle
     from threadpoolctl import threadpool_limits
 
-    n = int(np.argmax(w["lengths"]))
+    n, h0, L, HG = u
+    w = _CPU_W
     lo = int(w["cu_seqlens"][n])
-    L = 2048
-    sl = {f: w[f][lo:lo + L] for f in ("q", "k", "v", "a", "beta")}
+    hi = min(int(w["cu_seqlens"][n + 1]), lo + L)
+    sl = [w[f][lo:hi, h0:h0 + HG] for f in ("q", "k", "v", "a", "beta")]
     with threadpool_limits(1):
+        oracle.kda_recurrent(*sl, w["s0"][n, h0:h0 + HG])
+    return (hi - lo) * HG
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, L=2048, HG=8):
+    """The float64 oracle on a bounded sample of the varlen workload: the first
+    L tokens of each of its 16 sequences, all 32 heads, as (sequence, group
+    of HG heads) units over the host's cores (one forked process per core, one
+    thread each; at most 16, the host share of one GPU).  The value is the
+    sample's token-heads per second over the wall time, divided by H: tokens
+    per second of the whole-head workload.  Runs before the GPU is touched."""
+    import multiprocessing as mp
+
+    global _CPU_W
+    _CPU_W = w
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    H = w["q"].shape[1]
+    units = [(n, h0, L, HG) for n in range(len(w["cu_seqlens"]) - 1) for h0 in range(0, H, HG)]
+    with mp.get_context("fork").Pool(cores) as pool:
+        pool.map(_oracle_unit, [(0, 0, 2, 1)] * cores)  # worker start-up and imports, untimed
         t0 = time.perf_counter()
-        oracle.kda_recurrent(sl["q"], sl["k"], sl["v"], sl["a"], sl["beta"], w["s0"][n])
+        token_heads = sum(pool.map(_oracle_unit, units, chunksize=1))
         dt = time.perf_counter() - t0
-    return {"value": L / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"float64 oracle kda_recurrent over the first {L} tokens of the longest "
-                      f"sequence (all 32 heads, dk=dv=128) of the same workload; {dt:.1f} s"}
+    _CPU_W = None
+    return {"value": token_heads / H / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": _cpu_model(),
+            "sample": f"float64 oracle kda_recurrent over the first {L} tokens of each of the "
+                      f"{len(w['cu_seqlens']) - 1} sequences of the same workload, all {H} heads "
+                      f"(dk=dv=128), as {len(units)} (sequence, {HG}-head) units on {cores} processes; "
+                      f"{token_heads / H:.0f} tokens in {dt:.1f} s wall, {dt * cores:.0f} core-s"}
 
 
 def write_traffic(fetch_csv, write_csv, name="prefill_varlen"):
@@ -558,9 +612,11 @@ def write_traffic(fetch_csv, write_csv, name="prefill_varlen"):
         return out
 
     fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
-    # One prefill call = one local_kernel and one propagation dispatch
-    # (slab_mixed_kernel or slab_kernel for bf16 at chunk 64, else prop_kernel).
-    prop = lambda k: "local_kernel" in k or "prop_kernel" in k or "slab_kernel" in k or "slab_mixed_kernel" in k
+    # One prefill call = one fused_kernel dispatch (bf16, chunk 32, dk 128), or
+    # one local_kernel and one propagation dispatch (slab_mixed_kernel or
+    # slab_kernel for bf16 at chunk 64, else prop_kernel).
+    prop = lambda k: any(n in k for n in ("fused_kernel", "local_kernel", "prop_kernel", "slab_kernel",
+                                          "slab_mixed_kernel"))
     knames = sorted(k for k in fetch if prop(k))
     f_pre = sum(float(np.mean(fetch[k])) for k in knames)
     w_pre = sum(float(np.mean(write[k])) for k in knames)
@@ -573,11 +629,11 @@ def write_traffic(fetch_csv, write_csv, name="prefill_varlen"):
            "copy_fetch_bytes_raw": f_cp, "copy_write_bytes_raw": w_cp,
            "fetch_scale": copy_bytes / f_cp, "write_scale": copy_bytes / w_cp,
            "hbm_bytes_per_launch": f_pre * copy_bytes / f_cp + w_pre * copy_bytes / w_cp,
-           "unit": "one prefill call (local kernel + propagation kernel dispatches)",
-           "kernel_src_sha256_16": src_hash(PREFILL_SRC),
+           "unit": "one prefill call (its kernel dispatches)",
+           "kernel_src_sha256_16": src_hash(FUSED_SRC if any("fused_kernel" in k for k in knames) else PREFILL_SRC),
            "command": "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out> -o fetch -- "
                       "python3 <repo>/bench.py --only prefill4,copycal --steps 1 --warmup 0 --no-cpu "
-                      "(then the same with WRITE_SIZE)"}
+                      "(then the same with WRITE_SIZE); python3 bench.py --traffic <fetch csv> <write csv>"}
     out = os.path.join(PROFILES, f"{name}_traffic.json")
     with open(out, "w") as f:
         json.dump(res, f, indent=1)
@@ -590,8 +646,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--only", default="", help="comma list of: prefill4, prefill4_gated, prefill3, segments, front_end, "
-                                               "decode, decode_bf16, replay, replay_big, "
+    ap.add_argument("--only", default="", help="comma list of: prefill4, prefill4_c64, prefill4_gated, prefill3, "
+                                               "segments, front_end, decode, decode_bf16, replay, replay_big, "
                                                "replay_big_bf16, ring, pack, copycal")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--json-out", default="")
@@ -608,27 +664,39 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    from linear_attention_recurrence_kda_amd import inputs
+
+    only = set(x for x in args.only.split(",") if x)
+    want = (lambda p: not only or p in only)
+    w4 = None
+    if want("prefill4") or want("prefill4_c64") or (not only and not args.no_cpu):
+        log("generating the varlen prefill workload ...")
+        w4 = inputs.workload4()
+    cpu = None
+    if not args.no_cpu and w4 is not None and not only:
+        # (before anything touches the GPU: the worker processes are spawned)
+        log("cpu baseline (float64 oracle) ...")
+        cpu = cpu_baseline(w4)
+
     import torch
-    from linear_attention_recurrence_kda_amd import inputs, kda
+    from linear_attention_recurrence_kda_amd import kda
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     kda.lib()  # fails loudly if the HIP library is not built
-    only = set(x for x in args.only.split(",") if x)
-    want = (lambda p: not only or p in only)
 
     parts = {}
-    w4 = None
-    if want("prefill4") or (not only and not args.no_cpu):
-        log("generating the varlen prefill workload ...")
-        w4 = inputs.workload4()
+    varlen = ("varlen prefill: 16 seqs, len~logU[1024,32768], H=32, dk=dv=128, bf16, S0~N(0,0.1^2), "
+              "chunk {}, ckpt every 4096 + tail, final states packed")
     if want("prefill4"):
         log("prefill (varlen) ...")
-        parts["prefill_varlen"] = bench_prefill(
-            torch, kda, inputs, w4, args.steps, args.warmup, True,
-            "varlen prefill: 16 seqs, len~logU[1024,32768], H=32, dk=dv=128, bf16, S0~N(0,0.1^2), "
-            "chunk 64, ckpt every 4096 + tail, final states packed")
+        parts["prefill_varlen"] = bench_prefill(torch, kda, inputs, w4, args.steps, args.warmup, True,
+                                                varlen.format(HEAD_CHUNK), chunk=HEAD_CHUNK)
+    if want("prefill4_c64"):
+        log("prefill (varlen, chunk 64) ...")
+        parts["prefill_varlen_chunk64"] = bench_prefill(torch, kda, inputs, w4, args.steps, args.warmup, True,
+                                                        varlen.format(64), chunk=64)
     if want("prefill4_gated"):
         if w4 is None:
             log("generating the varlen prefill workload ...")
@@ -684,21 +752,20 @@ def main():
         line["value"] = head["tokens_per_s"]
         line["ms_per_step"] = head["ms_per_step"]
         line["config"] = {"workload": head["workload"], "tokens": head["tokens"],
-                          "n_seqs": head["n_seqs"], "H": 32, "dk": 128, "dv": 128, "chunk": 64,
+                          "n_seqs": head["n_seqs"], "H": 32, "dk": 128, "dv": 128, "chunk": head["chunk"],
                           "n_ckpt": head["n_ckpt"], "parallelism": "single GPU"}
         kbytes = head["algo_gbytes"] * 1e9
         line["roofline"] = {
-            "kernel": "prefill call: local_kernel<128,bf16> + slab_mixed_kernel<128> (a tile width per sequence: 32, 64 or 128 columns; 4 compute + 2 loader waves)",
+            "kernel": "prefill call: " + head["kernels"],
             "bound": "hbm",
             "achieved": head["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": head["hbm_frac"],
-            "traffic": committed_traffic("prefill_varlen", PREFILL_SRC),
+            "traffic": committed_traffic("prefill_varlen", FUSED_SRC if head["chunk"] == 32 else PREFILL_SRC),
             "algo_bytes_per_launch": kbytes, "kernel_ms": head["kernel_ms"],
             "mfma_tflops": head["mfma_tflops"], "mfma_frac": head["mfma_frac"],
             "roofline_frac": head["roofline_frac"]}
-    if not args.no_cpu and w4 is not None and not only:
-        log("cpu baseline (float64 oracle) ...")
-        line["cpu_baseline"] = cpu_baseline(inputs, w4)
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
     line["parts"] = parts
     s = json.dumps(line)
     print(s, flush=True)

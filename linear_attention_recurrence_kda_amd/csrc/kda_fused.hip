@@ -63,6 +63,11 @@
 // record is built in one interval, finished in the next and read in the
 // third.
 //
+// With the gate fused in, a and beta arrive as logits and the L waves apply
+// a = g_min sigmoid(z_a), beta = sigmoid(z_b) in fp32 as they build ("Serve 模
+// 块交互式演示" page, §1.3, for the gates; the "Kimi Linear 的 KDA 缓存" page's
+// vLLM path fuses them the same way).
+//
 // A decay outside [a_lo, 0] (or a NaN) found while building chunk x raises
 // the error flags and stops that chain at the barrier that would hand chunk x
 // over: the outputs and checkpoints of the chunks before x stay written,
@@ -169,6 +174,8 @@ struct FusedParams {
   int32_t* wsflag;
   int32_t* err_flag;
   float a_lo;
+  bool gate;    // a, beta are logits: a = g_min * sigmoid(a), beta = sigmoid(beta)
+  float g_min;
   int H, dv;
 };
 
@@ -177,6 +184,7 @@ struct FusedParams {
 struct Raw {
   i32x4 q, k, a;
   uint32_t b;
+  int n;  // the chunk's rows
 };
 
 template <int DK>
@@ -352,6 +360,7 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
       r.a = ld128(tok_rsrc(p.a, x, rsk, DK * 2, ho), vo);
       const __amdgpu_buffer_rsrc_t rb = tok_rsrc(p.beta, x, static_cast<uint32_t>(H) * 2, 2, h * 2);
       r.b = __builtin_amdgcn_raw_buffer_load_b16(rb, vob, 0, 0);
+      r.n = x.n;
     };
     auto load_v = [&](const ChunkWalk& x, i32x4& vr) {
       vr = ld128(tok_rsrc(p.v, x, rsv, DVT * 2, (h * dv + tile * DVT) * 2), vso);
@@ -395,17 +404,34 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
     // (build1b).
     auto build1a = [&](int R3, const Raw& r, float* G) {
       FRec<DK>& rec = sm.rec[R3];
-      // The decay range, on the bit patterns (two per word).
-      u16x2 mx = {0, 0}, mn = {0xffff, 0xffff};
+      bool bad;
+      if (p.gate) {
+        // a = g_min sigmoid(z) (in [g_min, 0] for finite z; zero past the
+        // chunk's end), in log2 units; a NaN logit makes a NaN.
+        const float gl = p.g_min * kLog2e;
+        const bool in = m < r.n;
+        bad = false;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const u16x2 u = as_u16x2(r.a[i]);
-        mx = __builtin_elementwise_max(mx, u);
-        mn = __builtin_elementwise_min(mn, u - u16x2{1, 1});  // +0 -> 0xffff; positives below 0x7fff
+        for (int j = 0; j < 8; ++j) {
+          const float s = __builtin_amdgcn_rcpf(1.f + exp2f_(-kLog2e * unpack(r.a, j)));
+          G[j] = in ? gl * s : 0.f;
+          bad |= G[j] != G[j];
+        }
+      } else {
+        // The decay range, on the bit patterns (two per word).
+        u16x2 mx = {0, 0}, mn = {0xffff, 0xffff};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const u16x2 u = as_u16x2(r.a[i]);
+          mx = __builtin_elementwise_max(mx, u);
+          mn = __builtin_elementwise_min(mn, u - u16x2{1, 1});  // +0 -> 0xffff; positives below 0x7fff
+        }
+        const uint32_t mx1 = max(static_cast<uint32_t>(mx.x), static_cast<uint32_t>(mx.y));
+        const uint32_t mn1 = min(static_cast<uint32_t>(mn.x), static_cast<uint32_t>(mn.y));
+        bad = mx1 > a_lo_bits || mn1 < 0x7fffu;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) G[j] = unpack(r.a, j) * kLog2e;
       }
-      const uint32_t mx1 = max(static_cast<uint32_t>(mx.x), static_cast<uint32_t>(mx.y));
-      const uint32_t mn1 = min(static_cast<uint32_t>(mn.x), static_cast<uint32_t>(mn.y));
-      const bool bad = mx1 > a_lo_bits || mn1 < 0x7fffu;
       if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) {
         *p.wsflag = 1;
         if (p.err_flag != nullptr) *p.err_flag = 1;
@@ -416,7 +442,7 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
       // G - G_m, and the second half's own sums are already G - G_m.
       float ref[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) G[j] = row_scan(unpack(r.a, j) * kLog2e);
+      for (int j = 0; j < 8; ++j) G[j] = row_scan(G[j]);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         ref[j] = row_last(G[j]);  // G_m (first half) or G_n - G_m (second half)
@@ -465,7 +491,11 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
       sm.part[B2][cw][X == 0 ? 0 : 2][lane] = mma(km, kp, z);
       sm.part[B2][cw][X == 0 ? 3 : 5][lane] = mma(km, qp, z);
       if (X == 0) km0 = km;
-      if (w == 0 && lane < 32) sm.beta[B2][lane] = __uint_as_float(r.b << 16);
+      if (w == 0 && lane < 32) {
+        float b = __uint_as_float(r.b << 16);
+        if (p.gate) b = lane < r.n ? __builtin_amdgcn_rcpf(1.f + exp2f_(-kLog2e * b)) : 0.f;
+        sm.beta[B2][lane] = b;
+      }
     };
     auto build1 = [&](int R3, int B2, const Raw& r) {
       float G[8];
@@ -793,6 +823,7 @@ hipError_t launch_fused(const PrefillArgs& a) {
   prm.chains = a.chains; prm.seqinfo = a.seqinfo; prm.ck_pos = a.ck_pos; prm.ck_slot = a.ck_slot;
   prm.wgs = a.wgs;
   prm.wsflag = a.wsflag; prm.err_flag = a.err_flag; prm.a_lo = a.a_lo;
+  prm.gate = a.gate; prm.g_min = a.g_min;
   prm.H = a.H; prm.dv = a.dv;
   if (a.n_wg == 0) return hipSuccess;
   hipLaunchKernelGGL((fused_kernel<128>), dim3(static_cast<unsigned>(a.n_wg)), dim3(Fused<128>::NT), 0, a.stream,

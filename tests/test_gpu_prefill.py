@@ -217,14 +217,17 @@ def test_prefill_rejects_wide_dv_tile(dtype, chunk, bad):
         assert e.value.status == kda.KDA_EUNSUPPORTED
 
 
-@pytest.mark.parametrize("dtype,chunk,g_min", [("bf16", 64, -1.0), ("fp32", 32, -2.0), ("bf16", 16, -0.5)])
-def test_prefill_with_fused_gate(dtype, chunk, g_min):
+@pytest.mark.parametrize("dtype,chunk,g_min,dk", [("bf16", 64, -1.0, 64), ("fp32", 32, -2.0, 64),
+                                                 ("bf16", 16, -0.5, 64), ("bf16", 32, -1.0, 128),
+                                                 ("bf16", 32, -5.0, 128)])
+def test_prefill_with_fused_gate(dtype, chunk, g_min, dk):
     """a and beta given as logits: the prefill applies a = g_min*sigmoid(z_a),
     beta = sigmoid(z_b) itself; the oracle takes the gates in float64 from the
-    same logits."""
+    same logits.  (bf16 at chunk 32, dk = 128: the fused kernel, g_min up to its
+    decay bound -160/32.)"""
     import oracle as orc
     lens = [1, 17, 64, 0, 130, 200]
-    H, dk, dv = 2, 64, 128
+    H, dv = 2, 128
     w = inputs.prefill_workload(170, lens, H, dk, dv, dtype, s0_std=0.1)
     rng = np.random.default_rng(171)
     z_a = rng.standard_normal(w["a"].shape).astype(np.float32)
