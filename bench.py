@@ -595,13 +595,16 @@ def cpu_baseline(w, L=2048, HG=8):
 
 
 def write_traffic(fetch_csv, write_csv, name="prefill_varlen"):
-    """Turn two rocprofv3 counter passes into the traffic figure reported above.
+    """Turn two rocprofv3 counter passes into a traffic figure.
 
     fetch_csv / write_csv: counter_collection CSVs of a FETCH_SIZE pass and a
-    WRITE_SIZE pass over `bench.py --only prefill4,copycal --steps 1 --warmup 0
-    --no-cpu` (KiB per dispatch).  The calibration copy of that run (1 GiB
-    read and written) scales the counters to bytes.  Writes
-    profiles/<name>_traffic.json, stamped with the kernel source hash."""
+    WRITE_SIZE pass (KiB per dispatch) over `bench.py --only prefill4,copycal
+    --steps 1 --warmup 0 --no-cpu` (name prefill_varlen: the bytes of one
+    prefill call, its kernel dispatches summed) or `--only pack,copycal`
+    (name pack: the bytes of each pack / unpack dispatch).  The calibration
+    copy of that run (torch's copy of 1 GiB, the runtime's copyBuffer kernel)
+    scales the counters to bytes.
+    Writes profiles/<name>_traffic.json, stamped with the kernel source hash."""
     import csv
 
     def per_kernel(path, counter):
@@ -612,28 +615,39 @@ def write_traffic(fetch_csv, write_csv, name="prefill_varlen"):
         return out
 
     fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
-    # One prefill call = one fused_kernel dispatch (bf16, chunk 32, dk 128), or
-    # one local_kernel and one propagation dispatch (slab_mixed_kernel or
-    # slab_kernel for bf16 at chunk 64, else prop_kernel).
-    prop = lambda k: any(n in k for n in ("fused_kernel", "local_kernel", "prop_kernel", "slab_kernel",
-                                          "slab_mixed_kernel"))
-    knames = sorted(k for k in fetch if prop(k))
-    f_pre = sum(float(np.mean(fetch[k])) for k in knames)
-    w_pre = sum(float(np.mean(write[k])) for k in knames)
-    kname = " + ".join(knames)
-    ours = lambda k: prop(k) or "pack" in k
-    f_cp = max(v for k, vals in fetch.items() if not ours(k) for v in vals)
-    w_cp = max(v for k, vals in write.items() if not ours(k) for v in vals)
+    # (torch's device-to-device copy runs as the HIP runtime's blit kernel)
+    f_cp = max(v for k, vals in fetch.items() if "copyBuffer" in k for v in vals)
+    w_cp = max(v for k, vals in write.items() if "copyBuffer" in k for v in vals)
     copy_bytes = float(1 << 30)
-    res = {"kernel": kname, "fetch_bytes_raw": f_pre, "write_bytes_raw": w_pre,
-           "copy_fetch_bytes_raw": f_cp, "copy_write_bytes_raw": w_cp,
-           "fetch_scale": copy_bytes / f_cp, "write_scale": copy_bytes / w_cp,
-           "hbm_bytes_per_launch": f_pre * copy_bytes / f_cp + w_pre * copy_bytes / w_cp,
-           "unit": "one prefill call (its kernel dispatches)",
-           "kernel_src_sha256_16": src_hash(FUSED_SRC if any("fused_kernel" in k for k in knames) else PREFILL_SRC),
-           "command": "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out> -o fetch -- "
-                      "python3 <repo>/bench.py --only prefill4,copycal --steps 1 --warmup 0 --no-cpu "
-                      "(then the same with WRITE_SIZE); python3 bench.py --traffic <fetch csv> <write csv>"}
+    fs, ws = copy_bytes / f_cp, copy_bytes / w_cp
+    cmd = ("cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out> -o fetch -- python3 "
+           "<repo>/bench.py --only {},copycal --steps 1 --warmup 0 --no-cpu (then the same with WRITE_SIZE); "
+           "python3 bench.py --traffic <fetch csv> <write csv> {}")
+    res = {"copy_fetch_bytes_raw": f_cp, "copy_write_bytes_raw": w_cp, "fetch_scale": fs, "write_scale": ws}
+    if name == "prefill_varlen":
+        # One prefill call = one fused_kernel dispatch (bf16, chunk 32, dk 128),
+        # or one local_kernel and one propagation dispatch (slab_mixed_kernel or
+        # slab_kernel for bf16 at chunk 64, else prop_kernel).
+        prop = lambda k: any(n in k for n in ("fused_kernel", "local_kernel", "prop_kernel", "slab_kernel",
+                                              "slab_mixed_kernel"))
+        knames = sorted(k for k in fetch if prop(k))
+        f_pre = sum(float(np.mean(fetch[k])) for k in knames)
+        w_pre = sum(float(np.mean(write[k])) for k in knames)
+        fused = any("fused_kernel" in k for k in knames)
+        res.update({"kernel": " + ".join(knames), "fetch_bytes_raw": f_pre, "write_bytes_raw": w_pre,
+                    "hbm_bytes_per_launch": f_pre * fs + w_pre * ws,
+                    "unit": "one prefill call (its kernel dispatches)",
+                    "kernel_src_sha256_16": src_hash(FUSED_SRC if fused else PREFILL_SRC),
+                    "command": cmd.format("prefill4", name)})
+    else:
+        per = {}
+        for k in sorted(k for k in fetch if "kda::" in k):
+            short = k.split("::")[-1].split("(")[0]
+            f, w = float(np.mean(fetch[k])) * fs, float(np.mean(write.get(k, [0.0]))) * ws
+            per[short] = {"dispatches": len(fetch[k]), "fetch_bytes": f, "write_bytes": w, "hbm_bytes": f + w}
+        res.update({"kernels": per, "unit": "one dispatch",
+                    "kernel_src_sha256_16": src_hash([os.path.join(CSRC, "kda_pack.hip")]),
+                    "command": cmd.format("pack", name)})
     out = os.path.join(PROFILES, f"{name}_traffic.json")
     with open(out, "w") as f:
         json.dump(res, f, indent=1)
@@ -651,8 +665,9 @@ def main():
                                                "replay_big_bf16, ring, pack, copycal")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--json-out", default="")
-    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="write profiles/prefill_varlen_traffic.json from two counter passes")
+    ap.add_argument("--traffic", nargs="+", metavar="ARG",
+                    help="FETCH_CSV WRITE_CSV [prefill_varlen|pack]: write profiles/<name>_traffic.json from "
+                         "two counter passes")
     args = ap.parse_args()
     if args.traffic:
         write_traffic(*args.traffic)
