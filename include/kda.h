@@ -53,11 +53,19 @@ typedef enum {
   KDA_EHIP = -5          /* the HIP runtime reported an error on enqueue      */
 } kda_status;
 
-typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+/* The two range markers of each enum below make every int a value of the
+ * type, so an out-of-range value from a caller in another language is
+ * well-defined (and refused with KDA_EINVAL). */
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1, KDA_DTYPE_MIN_ = -2147483647 - 1, KDA_DTYPE_MAX_ = 2147483647 } kda_dtype;
 
 /* State layouts: KV = [.., dk, dv] (canonical), VK = [.., dv, dk] (the
  * transposed layout some kernels and state pools use, [KDA cache] "先统一记号"). */
-typedef enum { KDA_LAYOUT_KV = 0, KDA_LAYOUT_VK = 1 } kda_layout;
+typedef enum {
+  KDA_LAYOUT_KV = 0,
+  KDA_LAYOUT_VK = 1,
+  KDA_LAYOUT_MIN_ = -2147483647 - 1,
+  KDA_LAYOUT_MAX_ = 2147483647
+} kda_layout;
 
 /* Version of the page layout written by pack and by checkpoint emission. */
 #define KDA_PAGE_LAYOUT_VERSION 1

@@ -12,7 +12,8 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libkda.so")
+# (KDA_LIB names another build of the same library, e.g. the sanitized one.)
+LIB_PATH = os.environ.get("KDA_LIB") or os.path.join(_PKG, "libkda.so")
 
 KDA_OK, KDA_EINVAL, KDA_EUNSUPPORTED, KDA_EALIAS, KDA_EWORKSPACE, KDA_EHIP = 0, -1, -2, -3, -4, -5
 KDA_F32, KDA_BF16 = 0, 1
