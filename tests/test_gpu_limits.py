@@ -161,7 +161,7 @@ def _decay_only(w):
     return o, sf
 
 
-@pytest.mark.parametrize("dtype,chunk", [("bf16", 64), ("fp32", 32)])
+@pytest.mark.parametrize("dtype,chunk", [("bf16", 64), ("fp32", 32), ("bf16", 32)])
 def test_prefill_beta_zero_only_decays(dtype, chunk):
     w = _workload(330, dtype, g_min=-0.05)
     w["beta"][...] = 0.0
@@ -187,7 +187,7 @@ def _unit_write(w, seed=0):
     return w
 
 
-@pytest.mark.parametrize("dtype,chunk", [("bf16", 64), ("fp32", 32)])
+@pytest.mark.parametrize("dtype,chunk", [("bf16", 64), ("fp32", 32), ("bf16", 32)])
 def test_prefill_delta_write_reads_back_v(dtype, chunk):
     """a = 0, beta = 1, unit k and q = k: every output is its token's own v,
     and the state at a checkpoint p reproduces v_p through S_p^T k_p."""
@@ -209,10 +209,11 @@ def test_prefill_delta_write_reads_back_v(dtype, chunk):
                       w["v"][last].astype(np.float64), dtype, f"s_final^T k = v, seq {n}")
 
 
-@pytest.mark.parametrize("dtype,chunk", [("bf16", 64), ("fp32", 32)])
-def test_prefill_single_tokens_from_zero(dtype, chunk):
-    """Sequences of one token from S0 = 0: S = beta k v^T, o = beta (k . q) v."""
-    w = inputs.prefill_workload(332, [1] * 7, 2, 64, 128, dtype)
+@pytest.mark.parametrize("dtype,chunk,dk", [("bf16", 64, 64), ("fp32", 32, 64), ("bf16", 32, 128)])
+def test_prefill_single_tokens_from_zero(dtype, chunk, dk):
+    """Sequences of one token from S0 = 0: S = beta k v^T, o = beta (k . q) v.
+    (bf16 at chunk 32 with dk = 128 runs the fused kernel.)"""
+    w = inputs.prefill_workload(332, [1] * 7, 2, dk, 128, dtype)
     (o, sf), _ = _prefill(w, dtype, chunk)
     k, q, v, b = (w[n].astype(np.float64) for n in ("k", "q", "v", "beta"))
     S = b[..., None, None] * k[..., :, None] * v[..., None, :]
