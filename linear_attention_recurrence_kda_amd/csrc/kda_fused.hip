@@ -331,6 +331,11 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
   using I4 = std::integral_constant<int, 4>;
   if (lw) {
     // ======================= L waves ==========================================
+    // (with two or fewer P waves holding state, the L waves' build bounds the
+    // interval before M, where the P waves have slack: the L waves then take
+    // issue priority on their SIMDs; with four, priority only starves the P
+    // waves' longer step)
+    if constexpr (NPA <= 2) __builtin_amdgcn_s_setprio(2);
     const int w = wave - F::NPW, X = w / NCG, cw = w % NCG;  // uniform
     const int r16 = col, g4 = grp, m = 16 * X + r16;
     const int cb = 32 * cw + 8 * g4;  // this lane's first channel
