@@ -54,14 +54,15 @@
 // chunk c+1's diagonal blocks (I + L_RR), two waves per block, two of each
 // lane's four columns each (forward substitution by rows, each step a DPP
 // broadcast of one row within the lane row); the L waves issue the loads of
-// chunk c+3 (q, k, a, beta) and c+2 (v) and build chunk c+2.  After M: P runs
-// the rest of chunk c; the first-half L waves form chunk c+2's off-diagonal
-// Gram shares and two of them write chunk c+1's lower(A_qk) and A_10; all L
-// waves store chunk c-1's outputs and move chunk c+1's v into LDS.  (With
-// 32 state columns per P wave the second-half L waves do the inversion, after
-// M.)  So a
-// record is built in one interval, finished in the next and read in the
-// third.
+// chunk c+3 (q, k, a, beta) and c+2 (v) and build chunk c+2 (the second-half
+// waves only its Kp and Qp rows).  After M: P runs the rest of chunk c; the
+// first-half L waves form chunk c+2's off-diagonal Gram shares, the
+// second-half ones the rest of their build (Km^T, diagonal shares,
+// e^{G_n - G_m}), and two first-half waves write chunk c+1's lower(A_qk) and
+// A_10; all L waves store chunk c-1's outputs and move chunk c+1's v into
+// LDS.  (With 32 state columns per P wave the second-half L waves also do
+// the inversion, after M.)  So a record is built across one chunk's two
+// intervals, finished in the next chunk's and read in the one after.
 //
 // With the gate fused in, a and beta arrive as logits and the L waves apply
 // a = g_min sigmoid(z_a), beta = sigmoid(z_b) in fp32 as they build ("Serve 模
@@ -83,6 +84,7 @@ namespace {
 constexpr int kFC = 32;  // tokens per chunk
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 
 // One chunk's operands in LDS.  kp, qp: 32 token rows of 16 pieces (16
 // bytes, slab_col channel order), piece q of row m at q ^ (m & 7); km: Km^T,
@@ -331,11 +333,14 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
   using I4 = std::integral_constant<int, 4>;
   if (lw) {
     // ======================= L waves ==========================================
-    // (with two or fewer P waves holding state, the L waves' build bounds the
+    // With two or fewer P waves holding state, the L waves' build bounds the
     // interval before M, where the P waves have slack: the L waves then take
-    // issue priority on their SIMDs; with four, priority only starves the P
-    // waves' longer step)
-    if constexpr (NPA <= 2) __builtin_amdgcn_s_setprio(2);
+    // issue priority on their SIMDs before M, and give it back after M, where
+    // the P waves' step is the longer one.  (With four, priority only starves
+    // the P waves' longer step.)
+    auto prio = [](auto pc) {
+      if constexpr (NPA <= 2) __builtin_amdgcn_s_setprio(decltype(pc)::value);
+    };
     const int w = wave - F::NPW, X = w / NCG, cw = w % NCG;  // uniform
     const int r16 = col, g4 = grp, m = 16 * X + r16;
     const int cb = 32 * cw + 8 * g4;  // this lane's first channel
@@ -403,10 +408,23 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
     auto row_piece = [&](i32x4* base, int mm, int s) {
       return reinterpret_cast<char*>(&base[16 * mm]) + 16 * swz16(mm, q0 + s) + half;
     };
-    bf16x8 km0;  // (first-half waves) this lane's Km fragment, kept for the off-diagonal shares
+    bf16x8 km0;  // this lane's Km fragment, kept for the shares formed after M
+    bf16x8 kp1, qp1;  // (second-half waves) its Kp, Qp fragments, likewise
+    f32x8 ref1;       // (second-half waves) G_n - G_m of its channels
     // The part of chunk x's build that needs only this wave's rows: the
     // decay range and sums (build1a), then the operands and Gram shares
     // (build1b).
+    // e^{G_m} (first half) or e^{G_n - G_m} (second half) of channel
+    // cb + (r16 & 7), stored by lanes 0..7 of the row: select the channel,
+    // then one exponential.
+    auto put_scale = [&](float* dst, f32x8 ref) {
+      const bool s0 = r16 & 1, s1 = r16 & 2, s2 = r16 & 4;
+      const float a01 = s0 ? ref[1] : ref[0], a23 = s0 ? ref[3] : ref[2];
+      const float a45 = s0 ? ref[5] : ref[4], a67 = s0 ? ref[7] : ref[6];
+      const float b03 = s1 ? a23 : a01, b47 = s1 ? a67 : a45;
+      const float e = exp2f_(s2 ? b47 : b03);
+      if (r16 < 8) dst[cb + r16] = e;
+    };
     auto build1a = [&](int R3, const Raw& r, float* G) {
       FRec<DK>& rec = sm.rec[R3];
       bool bad;
@@ -453,17 +471,26 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
         ref[j] = row_last(G[j]);  // G_m (first half) or G_n - G_m (second half)
         if (X == 0) G[j] -= ref[j];
       }
-      // e^{G_m} (first half) or e^{G_n - G_m} (second half) of channel
-      // cb + (r16 & 7), stored by lanes 0..7 of the row: select the channel,
-      // then one exponential.
-      {
-        const bool s0 = r16 & 1, s1 = r16 & 2, s2 = r16 & 4;
-        const float a01 = s0 ? ref[1] : ref[0], a23 = s0 ? ref[3] : ref[2];
-        const float a45 = s0 ? ref[5] : ref[4], a67 = s0 ? ref[7] : ref[6];
-        const float b03 = s1 ? a23 : a01, b47 = s1 ? a67 : a45;
-        const float e = exp2f_(s2 ? b47 : b03);
-        if (r16 < 8) (X == 0 ? rec.em : rec.en)[cb + r16] = e;
-      }
+      const f32x8 rv = {ref[0], ref[1], ref[2], ref[3], ref[4], ref[5], ref[6], ref[7]};
+      if (X == 0) put_scale(rec.em, rv);
+      else ref1 = rv;
+    };
+    // Km^T: row = channel cb + j (cb is a multiple of 8, so the swizzle of
+    // row cb + j is j >> 1), token m at slab position 8 (m%16 / 4) + 4 X + m % 4.
+    auto put_km = [&](FRec<DK>& rec, const bf16x8& km) {
+      char* kt = reinterpret_cast<char*>(&rec.km[4 * cb]) + 2 * (4 * X + (r16 & 3));
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        *reinterpret_cast<__bf16*>(kt + 16 * (4 * j + ((r16 >> 2) ^ (j >> 1)))) = km[j];
+    };
+    // Shares of the diagonal blocks over this wave's channels, formed as
+    // transposes (Km first): lane (r16, g4) then holds row r16 of the tile,
+    // columns 4 g4 .. 4 g4 + 3.  Tiles: 0 = A_kk 00, 1 = A_kk 10,
+    // 2 = A_kk 11, 3..5 = the same of A_qk.
+    auto gram_diag = [&](int B2, const bf16x8& km, const bf16x8& kp, const bf16x8& qp) {
+      const f32x4 z = zero4();
+      sm.part[B2][cw][X == 0 ? 0 : 2][lane] = mma(km, kp, z);
+      sm.part[B2][cw][X == 0 ? 3 : 5][lane] = mma(km, qp, z);
     };
     auto build1b = [&](int R3, int B2, const Raw& r, const float* G) {
       FRec<DK>& rec = sm.rec[R3];
@@ -482,20 +509,14 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
       *reinterpret_cast<i32x2*>(row_piece(rec.kp, m, 1)) = i32x2{kw[2], kw[3]};
       *reinterpret_cast<i32x2*>(row_piece(rec.qp, m, 0)) = i32x2{qw[0], qw[1]};
       *reinterpret_cast<i32x2*>(row_piece(rec.qp, m, 1)) = i32x2{qw[2], qw[3]};
-      // Km^T: row = channel cb + j (cb is a multiple of 8, so the swizzle of
-      // row cb + j is j >> 1), token m at slab position 8 (m%16 / 4) + 4 X + m % 4.
-      char* kt = reinterpret_cast<char*>(&rec.km[4 * cb]) + 2 * (4 * X + (r16 & 3));
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        *reinterpret_cast<__bf16*>(kt + 16 * (4 * j + ((r16 >> 2) ^ (j >> 1)))) = km[j];
-      // Shares of the diagonal blocks over this wave's channels, formed as
-      // transposes (Km first): lane (r16, g4) then holds row r16 of the tile,
-      // columns 4 g4 .. 4 g4 + 3.  Tiles: 0 = A_kk 00, 1 = A_kk 10,
-      // 2 = A_kk 11, 3..5 = the same of A_qk.
-      const f32x4 z = zero4();
-      sm.part[B2][cw][X == 0 ? 0 : 2][lane] = mma(km, kp, z);
-      sm.part[B2][cw][X == 0 ? 3 : 5][lane] = mma(km, qp, z);
-      if (X == 0) km0 = km;
+      km0 = km;
+      if (X == 0) {
+        put_km(rec, km);
+        gram_diag(B2, km, kp, qp);
+      } else {
+        kp1 = kp;
+        qp1 = qp;
+      }
       if (w == 0 && lane < 32) {
         float b = __uint_as_float(r.b << 16);
         if (p.gate) b = lane < r.n ? __builtin_amdgcn_rcpf(1.f + exp2f_(-kLog2e * b)) : 0.f;
@@ -507,20 +528,28 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
       build1a(R3, r, G);
       build1b(R3, B2, r, G);
     };
-    // After M (first-half waves): the off-diagonal shares Km0 Kp1^T and
-    // Km0 Qp1^T, with rows 16.. of kp and qp read back from LDS.
+    // After M: (second-half waves) the rest of build1b and build1a, which
+    // the P waves need two intervals later at the earliest; (first-half
+    // waves) the off-diagonal shares Km0 Kp1^T and Km0 Qp1^T, with rows 16..
+    // of kp and qp read back from LDS.
     auto build2 = [&](int R3, int B2) {
-      if (X != 0) return;
+      if (X != 0) {
+        FRec<DK>& rec = sm.rec[R3];
+        put_km(rec, km0);
+        gram_diag(B2, km0, kp1, qp1);
+        put_scale(rec.en, ref1);
+        return;
+      }
       const FRec<DK>& rec = sm.rec[R3];
       auto frag_of = [&](const i32x4* base) {
         const i32x2 lo2 = *reinterpret_cast<const i32x2*>(row_piece(const_cast<i32x4*>(base), 16 + r16, 0));
         const i32x2 hi2 = *reinterpret_cast<const i32x2*>(row_piece(const_cast<i32x4*>(base), 16 + r16, 1));
         return __builtin_bit_cast(bf16x8, i32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
       };
-      const bf16x8 kp1 = frag_of(rec.kp), qp1 = frag_of(rec.qp);
+      const bf16x8 kpo = frag_of(rec.kp), qpo = frag_of(rec.qp);
       const f32x4 z = zero4();
-      sm.part[B2][cw][1][lane] = mma(km0, kp1, z);
-      sm.part[B2][cw][4][lane] = mma(km0, qp1, z);
+      sm.part[B2][cw][1][lane] = mma(km0, kpo, z);
+      sm.part[B2][cw][4][lane] = mma(km0, qpo, z);
     };
 
     // After M: first-half wave 2 writes lower(A_qk), wave 3 A_10 (their SIMDs
@@ -591,12 +620,14 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
         // the first iteration has an empty range), so the compiler can count
         // what is in flight and waits for the loads it needs, not for
         // everything issued before.
+        prio(integral_constant<int, 2>{});
         load_raw(wr, rs[K1]);  // chunk c + 3
         next_chunk(wr);
         load_v(wv, vs[K]);  // chunk c + 2
         next_chunk(wv);
         build1(b3(c + 2), b2(c + 2), rs[K]);
         slab_barrier();  // M
+        prio(integral_constant<int, 0>{});
         const i32x4 ov = read_o(b2(c - 1));  // (vb[b2(c + 1)], before put_v refills it)
         build2(b3(c + 2), b2(c + 2));
         finish(b2(c + 1));
@@ -690,8 +721,8 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
 
   // The prologue's four steps (the L waves build chunks c_lo and c_lo + 1).
   slab_barrier();
-  p_solve(b2(c_lo));
   slab_barrier();
+  p_solve(b2(c_lo));
   slab_barrier();
   slab_barrier();  // A: chunk c_lo complete
   bool done = sm.stop[b3(c_lo)] != 0;
