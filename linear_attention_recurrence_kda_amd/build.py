@@ -7,6 +7,7 @@ root) and linked into linear_attention_recurrence_kda_amd/libkda.so.
 import concurrent.futures as cf
 import glob
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -36,10 +37,21 @@ def _hipcc():
 EXTRA = {"kda_slab.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
          "kda_fused.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
+# Sources whose kernels must not use scratch memory: a spill or a
+# dynamically indexed private array there costs a memory round trip per
+# chunk on the longest chain (and its vmcnt waits hold every load in flight),
+# so the build fails instead of shipping a silently slower kernel.
+NO_SCRATCH = {"kda_fused.hip", "kda_slab.hip"}
+_SCRATCH_RE = re.compile(r"ScratchSize \[bytes/lane\]: (\d+)")
+_NAME_RE = re.compile(r"Function Name: (\S+)")
+
 
 def _compile(src, verbose):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [_hipcc()] + COMMON + EXTRA.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
+    base = os.path.basename(src)
+    cmd = [_hipcc()] + COMMON + EXTRA.get(base, []) + ["-c", src, "-o", obj]
+    if base in NO_SCRATCH:
+        cmd.append("-Rpass-analysis=kernel-resource-usage")
     if src.endswith(".hip"):
         cmd[1:1] = ["-x", "hip"]
     if verbose:
@@ -47,6 +59,15 @@ def _compile(src, verbose):
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
+    if base in NO_SCRATCH:
+        name = "?"
+        for line in r.stderr.splitlines():
+            m = _NAME_RE.search(line)
+            if m:
+                name = m.group(1)
+            m = _SCRATCH_RE.search(line)
+            if m and int(m.group(1)) != 0:
+                raise RuntimeError(f"{base}: kernel {name} uses {m.group(1)} bytes of scratch per lane")
     if verbose and r.stderr.strip():
         print(r.stderr, flush=True)
     return obj

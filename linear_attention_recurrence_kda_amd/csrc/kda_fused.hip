@@ -183,6 +183,11 @@ struct FusedParams {
 
 // Loads of one chunk for one L lane: q, k, a of its token row (eight
 // channels, 16 bytes each), and one beta.
+// Rows t .. t + n - 1 of a chunk.
+struct Span {
+  int t, n;
+};
+
 struct Raw {
   i32x4 q, k, a;
   uint32_t b;
@@ -245,6 +250,7 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
   };
   auto b2 = [&](int c) { return (c - c_lo) & 1; };
   auto b3 = [&](int c) { return (c - c_lo) % 3; };
+  auto inc3 = [](int r) { return r == 2 ? 0 : r + 1; };
 
   // Zero the page padding of this sequence's checkpoint slots (once per sequence).
   if (tile == 0 && h == 0 && p.page_elems > hkv) {
@@ -358,12 +364,12 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
     const uint32_t vso = vlane ? vrow * rsv + 16 * (vpq ^ ((vrow >> 2) & VSW)) : 0x80000000u;
     // Buffer resource over the chunk's rows of one head of a token-major
     // tensor (rows past the chunk's end read as zero).
-    auto tok_rsrc = [&](const void* base, const ChunkWalk& x, uint32_t row_bytes, uint32_t lane_bytes,
+    auto tok_rsrc = [&](const void* base, const auto& x, uint32_t row_bytes, uint32_t lane_bytes,
                         uint32_t head_off) {
       return buf_rsrc(static_cast<const char*>(base) + static_cast<size_t>(x.t) * row_bytes + head_off,
                       static_cast<uint32_t>(x.n - 1) * row_bytes + lane_bytes);
     };
-    auto load_raw = [&](const ChunkWalk& x, Raw& r) {
+    auto load_raw = [&](const auto& x, Raw& r) {
       const uint32_t ho = static_cast<uint32_t>(h) * DK * 2;
       r.q = ld128(tok_rsrc(p.q, x, rsk, DK * 2, ho), vo);
       r.k = ld128(tok_rsrc(p.k, x, rsk, DK * 2, ho), vo);
@@ -372,7 +378,7 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
       r.b = __builtin_amdgcn_raw_buffer_load_b16(rb, vob, 0, 0);
       r.n = x.n;
     };
-    auto load_v = [&](const ChunkWalk& x, i32x4& vr) {
+    auto load_v = [&](const auto& x, i32x4& vr) {
       vr = ld128(tok_rsrc(p.v, x, rsv, DVT * 2, (h * dv + tile * DVT) * 2), vso);
     };
     auto put_v = [&](int b, const i32x4& vr) {
@@ -382,7 +388,7 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
     // that ends at the chunk's last row (any = false: an empty range, every
     // store is dropped, so the call sites need no branch around it).
     auto read_o = [&](int b) { return *reinterpret_cast<const i32x4*>(&sm.vb[b][8 * ve]); };
-    auto store_o = [&](const ChunkWalk& x, const i32x4& ov, bool any) {
+    auto store_o = [&](const auto& x, const i32x4& ov, bool any) {
       const __amdgpu_buffer_rsrc_t ro =
           buf_rsrc(static_cast<char*>(p.o) + (static_cast<size_t>(x.t) * H + h) * dv * 2 + tile * DVT * 2,
                    any ? (x.n - 1) * rsv + DVT * 2 : 0u);
@@ -577,31 +583,36 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
       }
     };
 
-    // Walkers: wr the chunk whose q, k, a, beta are loaded next, wv whose v,
-    // wo whose outputs are stored next.
+    // The walker wr is on the chunk whose q, k, a, beta are loaded next; the
+    // spans of the chunks it passed are kept for the v loads and the output
+    // stores (in iteration c: h0 = chunk c + 2, h1 = c + 1, h2 = c,
+    // h3 = c - 1).
     Raw rs[2];
     i32x4 vs[2];
-    ChunkWalk wr = first_chunk(), wv = wr, wo = wr;
+    ChunkWalk wr = first_chunk();
+    auto take = [&]() {
+      const Span x{wr.t, wr.n};
+      next_chunk(wr);
+      return x;
+    };
     // Prologue: chunk c_lo complete and chunk c_lo + 1 built, in four steps.
     load_raw(wr, rs[0]);
-    next_chunk(wr);
+    const Span x0 = take();
     load_raw(wr, rs[1]);
-    next_chunk(wr);
-    load_v(wv, vs[0]);
-    next_chunk(wv);
+    const Span x1 = take();
+    load_v(x0, vs[0]);
     build1(b3(c_lo), b2(c_lo), rs[0]);
     slab_barrier();
     build2(b3(c_lo), b2(c_lo));
     put_v(b2(c_lo), vs[0]);
-    load_v(wv, vs[1]);
-    next_chunk(wv);
+    load_v(x1, vs[1]);
     slab_barrier();
     build1(b3(c_lo + 1), b2(c_lo + 1), rs[1]);
     slab_barrier();
     build2(b3(c_lo + 1), b2(c_lo + 1));
     finish(b2(c_lo));
     load_raw(wr, rs[0]);  // chunk c_lo + 2
-    next_chunk(wr);
+    Span h0 = take(), h1 = x1, h2 = x0, h3 = x0;
     slab_barrier();  // A: chunk c_lo complete
     const bool live = sm.stop[b3(c_lo)] == 0;
     int last = c_lo;  // the last chunk the P waves processed
@@ -613,38 +624,44 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
       // chunk c + 3's at once); v of chunk c + 1 (moved to LDS now) is in set
       // K ^ 1 and v of chunk c (in LDS already) leaves set K to chunk c + 2.
       using std::integral_constant;
-      auto iter = [&](auto kc, int c) {
+      auto iter = [&](auto kc, int c, int r3) {  // r3 = b3(c)
         constexpr int K = decltype(kc)::value, K1 = K ^ 1;
-        const bool go = sm.stop[b3(c + 1)] == 0;  // (final since chunk c + 1 was built)
+        const int r3n = inc3(r3), r3nn = inc3(r3n);
+        const bool go = sm.stop[r3n] == 0;  // (final since chunk c + 1 was built)
         // Every memory operation here is unconditional (the output store of
         // the first iteration has an empty range), so the compiler can count
         // what is in flight and waits for the loads it needs, not for
         // everything issued before.
         prio(integral_constant<int, 2>{});
         load_raw(wr, rs[K1]);  // chunk c + 3
-        next_chunk(wr);
-        load_v(wv, vs[K]);  // chunk c + 2
-        next_chunk(wv);
-        build1(b3(c + 2), b2(c + 2), rs[K]);
+        const Span x3 = take();
+        load_v(h0, vs[K]);  // chunk c + 2
+        build1(r3nn, b2(c + 2), rs[K]);
         slab_barrier();  // M
         prio(integral_constant<int, 0>{});
         const i32x4 ov = read_o(b2(c - 1));  // (vb[b2(c + 1)], before put_v refills it)
-        build2(b3(c + 2), b2(c + 2));
+        build2(r3nn, b2(c + 2));
         finish(b2(c + 1));
-        store_o(wo, ov, c > c_lo);
-        if (c > c_lo) next_chunk(wo);
+        store_o(h3, ov, c > c_lo);
         put_v(b2(c + 1), vs[K1]);
+        h3 = h2;
+        h2 = h1;
+        h1 = h0;
+        h0 = x3;
         slab_barrier();  // A: chunk c + 1 complete
         last = c;
         return go;
       };
+      int r3 = 0;
       for (int c = c_lo; c < c_hi; c += 2) {
-        if (!iter(integral_constant<int, 0>{}, c)) break;
-        if (c + 1 >= c_hi || !iter(integral_constant<int, 1>{}, c + 1)) break;
+        if (!iter(integral_constant<int, 0>{}, c, r3)) break;
+        r3 = inc3(r3);
+        if (c + 1 >= c_hi || !iter(integral_constant<int, 1>{}, c + 1, r3)) break;
+        r3 = inc3(r3);
       }
     }
-    // The outputs of the last chunk the P waves processed (wo points at it).
-    if (live) store_o(wo, read_o(b2(last)), true);
+    // The outputs of the last chunk the P waves processed (h3 is on it).
+    if (live) store_o(h3, read_o(b2(last)), true);
     return;
   }
 
