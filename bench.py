@@ -719,8 +719,9 @@ def main():
         log("prefill (varlen, fused gate) ...")
         parts["prefill_varlen_gated"] = bench_prefill(
             torch, kda, inputs, w4, args.steps, args.warmup, True,
-            "varlen prefill as above with the gate fused in: a = -sigmoid(z_a), beta = sigmoid(z_b) "
-            "computed from bf16 logits inside the prefill", gate=True)
+            "varlen prefill as above (chunk {}) with the gate fused in: a = -sigmoid(z_a), "
+            "beta = sigmoid(z_b) computed from bf16 logits inside the prefill".format(HEAD_CHUNK),
+            gate=True, chunk=HEAD_CHUNK)
     if want("prefill3"):
         log("prefill (single sequence) ...")
         parts["prefill_single"] = bench_prefill(
