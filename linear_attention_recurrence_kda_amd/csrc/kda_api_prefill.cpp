@@ -98,7 +98,7 @@ double choose_widths(const std::vector<int64_t>& chunks, int32_t H, const int* w
 // The fused kernel's per-chunk times (us, 32-token chunks) at 128, 64, 32
 // and 16 columns per workgroup, measured on MI355X (one workgroup per CU).
 constexpr int kFusedW[4] = {128, 64, 32, 16};
-constexpr double kFusedT[4] = {2.84, 2.32, 2.05, 2.22};
+constexpr double kFusedT[4] = {2.66, 2.27, 2.01, 2.14};
 bool fused_path(kda_dtype in_dtype, int32_t dk, int32_t chunk) {
   return in_dtype == KDA_BF16 && chunk == 32 && dk == 128;
 }
