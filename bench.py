@@ -210,7 +210,7 @@ def bench_prefill(torch, kda, inputs, w, steps, warmup, pack_final, label, gate=
     return res
 
 
-def bench_segments(torch, kda, inputs, w, steps, warmup, n_seg=8):
+def bench_segments(torch, kda, inputs, w, steps, warmup, n_seg=8, decay="g_min=-1"):
     """Context-parallel prefill of one long sequence on one GPU: the sequence
     cut into n_seg equal segments (the shares of n_seg ranks), then segment
     summaries, their composition into start states, and the prefill of every
@@ -286,7 +286,7 @@ def bench_segments(torch, kda, inputs, w, steps, warmup, n_seg=8):
     summ_ms = float(ph[0])
     res = {"workload": f"context-parallel prefill on one GPU: T={T} (one sequence) in {n_seg} "
                        f"segments of {L}, H={H}, dk=dv={dk}, bf16, S0=0, chunk 64, "
-                       f"ckpt every 512",
+                       f"ckpt every 512, {decay}",
            "ms_per_step": ms, "summary_ms": summ_ms, "compose_ms": float(ph[1]),
            "rerun_ms": float(ph[2]), "one_pass_kernel_ms": ms1,
            "tokens_per_s": T / (ms * 1e-3), "one_pass_tokens_per_s": T / (ms1 * 1e-3),
@@ -731,6 +731,15 @@ def main():
         log("segments (context-parallel prefill on one GPU) ...")
         parts["segments"] = bench_segments(torch, kda, inputs, inputs.workload3(), args.steps,
                                            args.warmup)
+        # The same with weak decay (a in [-0.001, 0]): the segments' start
+        # states then carry over, so the composed path's agreement with the
+        # one pass measures the composition rather than a decayed-away state.
+        log("segments, weak decay ...")
+        ww = inputs.prefill_workload(3, [8192], H=32, dk=128, dv=128, dtype="bf16", ckpt_every=512,
+                                     ckpt_tail=False, g_min=-0.001)
+        parts["segments_weak_decay"] = bench_segments(torch, kda, inputs, ww, args.steps, args.warmup,
+                                                      decay="g_min=-0.001")
+        del ww
     if want("front_end"):
         log("front end ...")
         parts["front_end"] = bench_front_end(torch, kda, inputs, args.steps, args.warmup)
