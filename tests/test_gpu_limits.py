@@ -69,7 +69,7 @@ def _oracle_check(w, dtype, o, sf, pool, slots, ck):
 
 # ---------------------------------------------------------------- decay edge
 EDGE = [("bf16", 64, "const"), ("bf16", 64, "uniform"), ("fp32", 32, "const"), ("fp32", 32, "uniform"),
-        ("bf16", 32, "const")]
+        ("bf16", 32, "const"), ("bf16", 32, "uniform")]
 
 
 @pytest.mark.parametrize("dtype,chunk,kind", EDGE)
