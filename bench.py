@@ -658,8 +658,8 @@ def write_traffic(fetch_csv, write_csv, name="prefill_varlen"):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", default="", help="comma list of: prefill4, prefill4_c64, prefill4_gated, prefill3, "
                                                "segments, front_end, decode, decode_bf16, replay, replay_big, "
                                                "replay_big_bf16, ring, pack, copycal")
