@@ -429,7 +429,7 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
       const float a45 = s0 ? ref[5] : ref[4], a67 = s0 ? ref[7] : ref[6];
       const float b03 = s1 ? a23 : a01, b47 = s1 ? a67 : a45;
       const float e = exp2f_(s2 ? b47 : b03);
-      if (r16 < 8) dst[cb + r16] = e;
+      dst[cb + (r16 & 7)] = e;  // (rows r16 and r16 + 8 write the same value)
     };
     auto build1a = [&](int R3, const Raw& r, float* G) {
       FRec<DK>& rec = sm.rec[R3];
@@ -523,10 +523,10 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
         kp1 = kp;
         qp1 = qp;
       }
-      if (w == 0 && lane < 32) {
+      if (w == 0) {  // (lanes 32.. hold the same tokens' beta as lanes ..31)
         float b = __uint_as_float(r.b << 16);
-        if (p.gate) b = lane < r.n ? __builtin_amdgcn_rcpf(1.f + exp2f_(-kLog2e * b)) : 0.f;
-        sm.beta[B2][lane] = b;
+        if (p.gate) b = (lane & 31) < r.n ? __builtin_amdgcn_rcpf(1.f + exp2f_(-kLog2e * b)) : 0.f;
+        sm.beta[B2][lane & 31] = b;
       }
     };
     auto build1 = [&](int R3, int B2, const Raw& r) {
