@@ -403,7 +403,7 @@ __global__ __launch_bounds__(64 * NW, 2) void local_kernel(LocalParams p) {
   using SH = Shape<DK, 16, ST, NW>;
   using SM = LocalSmem<DK, ST, SH::NG>;
   constexpr int NT = SH::NT, MAXC = SH::MAXC, HK = SH::HK, RPG = SH::RPG, NG = SH::NG, NGT = SH::NGT;
-  constexpr int LDK = SM::LDK, LC = SM::LC, LF = SM::LF;
+  constexpr int LDK = SM::LDK, LF = SM::LF;
   constexpr uint32_t ES = sizeof(InT);
   __shared__ __attribute__((aligned(16))) SM sm;
 
