@@ -41,7 +41,7 @@ EXTRA = {"kda_slab.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 # dynamically indexed private array there costs a memory round trip per
 # chunk on the longest chain (and its vmcnt waits hold every load in flight),
 # so the build fails instead of shipping a silently slower kernel.
-NO_SCRATCH = {"kda_fused.hip", "kda_slab.hip"}
+NO_SCRATCH = {"kda_fused.hip", "kda_slab.hip", "kda_cp.hip"}
 _SCRATCH_RE = re.compile(r"ScratchSize \[bytes/lane\]: (\d+)")
 _NAME_RE = re.compile(r"Function Name: (\S+)")
 

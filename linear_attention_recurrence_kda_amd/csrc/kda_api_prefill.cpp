@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstring>
 #include <numeric>
 #include <string>
 #include <unordered_set>
@@ -20,6 +21,18 @@ namespace {
 constexpr int kCUs = 256;  // MI355X compute units (one propagation workgroup per CU)
 
 int64_t round8(int64_t x) { return (x + 7) / 8 * 8; }
+
+// Chunks of one sequence: chunks never cross a checkpoint position.
+int64_t seq_chunks(int32_t len, const int32_t* pos, int32_t npos, int32_t chunk) {
+  int64_t c = 0;
+  int32_t prev = 0;
+  for (int32_t i = 0; i <= npos; ++i) {
+    const int32_t next = i < npos ? pos[i] : len;
+    c += (next - prev + chunk - 1) / chunk;
+    prev = next;
+  }
+  return c;
+}
 
 // Chunks never cross a sequence end or a checkpoint, so a sequence of length
 // L with m checkpoints has at most L / chunk + m + 1 of them.
@@ -49,7 +62,8 @@ size_t work_ints(int32_t n_seqs, int32_t H, int64_t n_ckpt, int64_t n_chunks) {
 // searches, so the choice is O(n log n) in the number of sequences.  Returns
 // the predicted time (us) and fills width[s].
 double choose_widths(const std::vector<int64_t>& chunks, int32_t H, const int* ws, const double* tw,
-                     const double* mult, int nw, std::vector<int>& width) {
+                     const double* mult, int nw, std::vector<int>& width, double fixed_work = 0,
+                     double fixed_longest = 0) {
   const size_t n = chunks.size();
   std::vector<int64_t> c(chunks);
   std::sort(c.begin(), c.end());
@@ -61,8 +75,9 @@ double choose_widths(const std::vector<int64_t>& chunks, int32_t H, const int* w
                                  return static_cast<double>(x) * tw[j] <= T;
                                }) - c.begin());
   };
+  // (fixed_work, fixed_longest: chains whose width is not chosen here)
   auto cost_at = [&](double T) {
-    double work = 0, longest = 0;
+    double work = fixed_work, longest = fixed_longest;
     size_t prev = 0;
     for (int j = 0; j < nw; ++j) {
       const size_t e = j + 1 < nw ? std::max(prev, fits(j, T)) : n;  // group j: [prev, e)
@@ -73,6 +88,7 @@ double choose_widths(const std::vector<int64_t>& chunks, int32_t H, const int* w
     return std::max(longest, work / kCUs);
   };
   double best = 0, best_T = 0;
+  if (n == 0) best = std::max(fixed_longest, fixed_work / kCUs);
   for (size_t i = 0; i < n; ++i) {
     if (i > 0 && c[i] == c[i - 1]) continue;
     for (int j = 0; j < nw; ++j) {
@@ -103,6 +119,72 @@ bool fused_path(kda_dtype in_dtype, int32_t dk, int32_t chunk) {
   return in_dtype == KDA_BF16 && chunk == 32 && dk == 128;
 }
 
+// Segments of long sequences in the fused launch (context parallelism on one
+// GPU; the "Serve 模块交互式演示" page's §1.7 and §7.2 reduce a segment to a
+// fixed-size map of its start state and compose the maps).  A split
+// sequence's first segment runs from s0 as usual; each later segment runs
+// twice beside it, from the zero state (kind 1) and from the identity with v
+// taken as zero (kind 2: its linear part, one 128-column tile); then
+// compose_kernel turns the maps into the segments' start states and
+// fix_kernel (kda_cp.hip) corrects the later segments' outputs and
+// checkpoints.  It pays where the longest chain bounds the call: each
+// segment's chain is shorter, for the identity chains' work and the
+// correction's traffic.
+constexpr int kMaxExtraSegs = 8;          // later segments per call (bounds the workspace)
+constexpr int kMinSegChunks = 16;         // chunks per segment, at least
+constexpr double kFixBytesPerUs = 5.0e6;  // the correction's streaming rate, bytes per us
+constexpr double kFixLaunchUs = 6.0;      // per extra launch
+
+// One chain set of the fused launch: a whole sequence, or a segment.
+struct Entry {
+  int32_t seq = 0, kind = 0, seg = 0;  // kind 0: a whole sequence or a first segment, 1: from zero, 2: from the identity
+  int32_t lo = 0, hi = 0;              // tokens [lo, hi) from the sequence's first
+  int32_t ck0 = 0, ck1 = 0;            // its checkpoints: the sequence's entries [ck0, ck1), positions in (lo, hi]
+  int64_t chunks = 0;
+  int width = 0;                       // columns per workgroup
+};
+
+// Cut points of len tokens into n segments, on multiples of the chunk
+// (len >= n * kMinSegChunks * chunk keeps them increasing and inside).
+std::vector<int32_t> seg_bounds(int32_t len, int n, int32_t chunk) {
+  std::vector<int32_t> b(n + 1, 0);
+  b[n] = len;
+  for (int i = 1; i < n; ++i) {
+    const int64_t t = static_cast<int64_t>(len) * i / n;
+    b[i] = static_cast<int32_t>((t + chunk / 2) / chunk * chunk);
+  }
+  return b;
+}
+
+// The entries of sequence s (len tokens, checkpoint positions pos[0..npos))
+// in n segments.
+void seq_entries(int32_t s, int32_t len, const int32_t* pos, int32_t npos, int n, int32_t chunk,
+                 std::vector<Entry>& out) {
+  const std::vector<int32_t> b = seg_bounds(len, n, chunk);
+  int32_t c = 0;
+  std::vector<int32_t> lp;
+  for (int k = 0; k < n; ++k) {
+    int32_t c1 = c;
+    lp.clear();
+    while (c1 < npos && pos[c1] <= b[k + 1]) lp.push_back(pos[c1++] - b[k]);
+    Entry e;
+    e.seq = s;
+    e.seg = k;
+    e.lo = b[k];
+    e.hi = b[k + 1];
+    e.ck0 = c;
+    e.ck1 = c1;
+    e.chunks = seq_chunks(b[k + 1] - b[k], lp.data(), c1 - c, chunk);
+    e.kind = k == 0 ? 0 : 1;
+    out.push_back(e);
+    if (k > 0) {
+      e.kind = 2;
+      out.push_back(e);
+    }
+    c = c1;
+  }
+}
+
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 size_t tile_bytes(int64_t n_chunks, int32_t H, int32_t chunk, int32_t dk, size_t es) {
   return static_cast<size_t>(n_chunks) * H * kda::UnitLayout(chunk, dk, static_cast<int>(es)).bytes;
@@ -119,18 +201,6 @@ bool valid_tile(int32_t dv, int32_t split, bool slab) {
   if (dv % split) return false;
   const int t = dv / split;
   return t == 16 || t == 32 || t == 64 || (slab && t == 128);
-}
-
-// Chunks of one sequence: chunks never cross a checkpoint position.
-int64_t seq_chunks(int32_t len, const int32_t* pos, int32_t npos, int32_t chunk) {
-  int64_t c = 0;
-  int32_t prev = 0;
-  for (int32_t i = 0; i <= npos; ++i) {
-    const int32_t next = i < npos ? pos[i] : len;
-    c += (next - prev + chunk - 1) / chunk;
-    prev = next;
-  }
-  return c;
 }
 
 // Pick the dv split from a per-chunk cost model (MFMA tile counts): key-side
@@ -183,14 +253,19 @@ struct Plan {
   int64_t n_chunks = 0, longest = 0;
   int split = 0, a_split = 0;
   bool slab = false, mixed = false, fused = false;
-  std::vector<int> width;  // columns per workgroup, per sequence
+  std::vector<int> width;  // columns per workgroup, per sequence (a split one: its first segment's)
+  // The fused launch: its chain sets, and the segments per sequence (cp: any
+  // sequence in more than one).
+  std::vector<Entry> ent;
+  std::vector<int> nseg;
+  bool cp = false;
 };
 
 // Validates everything the plan depends on (dtype, sizes, cu_seqlens,
 // checkpoint offsets and positions; not buffers or slots) and makes the plan.
 int make_plan(kda_dtype in_dtype, int32_t H, int32_t dk, int32_t dv, int32_t chunk, const int32_t* cu,
               int32_t n_seqs, const int32_t* ck_cu, const int32_t* ck_pos, int64_t n_ckpt, int32_t dv_split,
-              bool summary, Plan& pl) {
+              bool summary, Plan& pl, bool allow_cp = true) {
   if (!valid_dtype(in_dtype)) return fail(KDA_EINVAL, "in_dtype %d", static_cast<int>(in_dtype));
   if (n_seqs < 0 || H <= 0 || n_ckpt < 0)
     return fail(KDA_EINVAL, "n_seqs=%d H=%d n_ckpt=%lld", n_seqs, H, static_cast<long long>(n_ckpt));
@@ -250,19 +325,21 @@ int make_plan(kda_dtype in_dtype, int32_t H, int32_t dk, int32_t dv, int32_t chu
   if (pl.n_chunks * H >= (int64_t{1} << 31)) return fail(KDA_EUNSUPPORTED, "too many (chunk, head) pairs");
   const bool bf16 = in_dtype == KDA_BF16;
   // The fused kernel (bf16, chunk 32, dk 128): a tile width per sequence,
-  // 16 to 128 columns, from its cost model, or one width dv / dv_split.
+  // 16 to 128 columns, from its cost model, or one width dv / dv_split; long
+  // sequences possibly in segments (dv_split 0: where the model predicts it
+  // faster; -n, 2 <= n <= 8: every sequence of at least n * kMinSegChunks
+  // chunks in n segments, as far as kMaxExtraSegs allows).
   if (fused_path(in_dtype, dk, chunk) && !summary) {
     pl.fused = true;
-    if (n_chains >= (int64_t{1} << 23)) return fail(KDA_EUNSUPPORTED, "too many chains");
+    int fixed_w = 0;
     if (dv_split > 0) {
-      const int w = dv % dv_split ? 0 : dv / dv_split;
-      if (w != 16 && w != 32 && w != 64 && w != 128)
+      fixed_w = dv % dv_split ? 0 : dv / dv_split;
+      if (fixed_w != 16 && fixed_w != 32 && fixed_w != 64 && fixed_w != 128)
         return fail(KDA_EUNSUPPORTED, "dv_split=%d with dv=%d (dv/split must be 16, 32, 64 or 128)", dv_split, dv);
       pl.split = dv_split;
-      pl.width.assign(n_seqs, w);
-      return KDA_OK;
+    } else if (dv_split < -kMaxExtraSegs) {
+      return fail(KDA_EUNSUPPORTED, "dv_split=%d", dv_split);
     }
-    if (dv_split != 0 && dv_split != -1) return fail(KDA_EUNSUPPORTED, "dv_split=%d", dv_split);
     std::vector<int64_t> sc(n_seqs);
     for (int32_t i = 0; i < n_seqs; ++i) {
       const int32_t c0 = ck_cu ? ck_cu[i] : 0, c1 = ck_cu ? ck_cu[i + 1] : 0;
@@ -277,8 +354,93 @@ int make_plan(kda_dtype in_dtype, int32_t H, int32_t dk, int32_t dv, int32_t chu
         mult[nw] = static_cast<double>(dv) / kFusedW[j];
         ++nw;
       }
-    if (n_seqs > 0) choose_widths(sc, H, ws, tw, mult, nw, pl.width);
-    pl.mixed = true;
+    auto entries = [&](const std::vector<int>& ns) {
+      std::vector<Entry> ent;
+      for (int32_t i = 0; i < n_seqs; ++i) {
+        const int32_t c0 = ck_cu ? ck_cu[i] : 0, c1 = ck_cu ? ck_cu[i + 1] : 0;
+        seq_entries(i, cu[i + 1] - cu[i], ck_pos ? ck_pos + c0 : nullptr, c1 - c0, ns[i], chunk, ent);
+      }
+      return ent;
+    };
+    // Widths of the entries (identity chains: 128 columns) and the predicted
+    // time, the correction included.
+    auto assign = [&](std::vector<Entry>& ent) {
+      std::vector<int64_t> ch;
+      double fixed_work = 0, fixed_longest = 0, fix_bytes = 0;
+      int n_split = 0;
+      for (const Entry& e : ent) {
+        if (e.kind == 2) {
+          fixed_work += static_cast<double>(H) * kFusedT[0] * static_cast<double>(e.chunks);
+          fixed_longest = std::max(fixed_longest, kFusedT[0] * static_cast<double>(e.chunks));
+          fix_bytes += static_cast<double>(e.hi - e.lo) * H * (2.0 * dk + 4.0 * dv);
+        } else {
+          ch.push_back(e.chunks);
+        }
+        if (e.kind == 1 && e.seg == 1) ++n_split;
+      }
+      std::vector<int> w;
+      double t;
+      if (fixed_w) {
+        w.assign(ch.size(), fixed_w);
+        double work = fixed_work, longest = fixed_longest;
+        int j = 0;
+        while (ws[j] != fixed_w) ++j;
+        for (int64_t c : ch) {
+          work += H * mult[j] * tw[j] * static_cast<double>(c);
+          longest = std::max(longest, tw[j] * static_cast<double>(c));
+        }
+        t = std::max(longest, work / kCUs);
+      } else {
+        t = ch.empty() ? std::max(fixed_longest, fixed_work / kCUs)
+                       : choose_widths(ch, H, ws, tw, mult, nw, w, fixed_work, fixed_longest);
+      }
+      size_t j = 0;
+      for (Entry& e : ent) e.width = e.kind == 2 ? 128 : w[j++];
+      if (n_split > 0) t += fix_bytes / kFixBytesPerUs + kFixLaunchUs * (n_split + 1);
+      return t;
+    };
+    pl.nseg.assign(n_seqs, 1);
+    const bool cp_ok = allow_cp && dv == dk && dv == 128 && n_seqs > 0;
+    auto min_len = [&](int n) { return static_cast<int64_t>(n) * kMinSegChunks * chunk; };
+    if (cp_ok && dv_split <= -2) {
+      int extra = 0;
+      for (int32_t i = 0; i < n_seqs; ++i)
+        if (cu[i + 1] - cu[i] >= min_len(-dv_split) && extra + (-dv_split - 1) <= kMaxExtraSegs) {
+          pl.nseg[i] = -dv_split;
+          extra += -dv_split - 1;
+        }
+    } else if (cp_ok && dv_split == 0) {
+      // Greedy: give the sequence with the longest segments one more segment
+      // while the model predicts at least 2 % less time.
+      std::vector<Entry> ent = entries(pl.nseg);
+      double best = assign(ent);
+      for (int extra = 0; extra < kMaxExtraSegs; ++extra) {
+        int32_t top = -1;
+        for (int32_t i = 0; i < n_seqs; ++i)
+          if (cu[i + 1] - cu[i] >= min_len(pl.nseg[i] + 1) &&
+              (top < 0 || sc[i] * pl.nseg[top] > sc[top] * pl.nseg[i]))
+            top = i;
+        if (top < 0) break;
+        ++pl.nseg[top];
+        ent = entries(pl.nseg);
+        const double t = assign(ent);
+        if (t < 0.98 * best) {
+          best = t;
+        } else {
+          --pl.nseg[top];
+          break;
+        }
+      }
+    }
+    pl.ent = entries(pl.nseg);
+    assign(pl.ent);
+    pl.cp = std::any_of(pl.nseg.begin(), pl.nseg.end(), [](int n) { return n > 1; });
+    pl.width.assign(n_seqs, 0);
+    for (const Entry& e : pl.ent)
+      if (e.kind == 0) pl.width[e.seq] = e.width;
+    if (round8(static_cast<int64_t>(pl.ent.size()) * H) >= (int64_t{1} << 23))
+      return fail(KDA_EUNSUPPORTED, "too many chains");
+    pl.mixed = dv_split <= 0;
     return KDA_OK;
   }
   pl.slab = slab_path(dk, bf16, chunk);
@@ -344,6 +506,17 @@ std::string plan_kernels(const Plan& pl, kda_dtype in_dtype, int32_t dk, int32_t
     for (int w : pl.width) { lo = std::min(lo, w); hi = std::max(hi, w); }
     snprintf(buf, sizeof(buf), "fused_kernel<%d> (32-token chunks, records in LDS; %d to %d columns per workgroup)",
              dk, pl.width.empty() ? 0 : lo, hi);
+    if (pl.cp) {
+      int n_split = 0, n_seg = 0;
+      for (int n : pl.nseg)
+        if (n > 1) {
+          ++n_split;
+          n_seg += n;
+        }
+      const size_t len = strlen(buf);
+      snprintf(buf + len, sizeof(buf) - len, " + compose_kernel + fix_kernel (%d sequence%s in %d segments)", n_split,
+               n_split == 1 ? "" : "s", n_seg);
+    }
   } else if (pl.mixed)
     snprintf(buf, sizeof(buf), "%s + slab_mixed_kernel<%d> (a tile width per sequence)", local.c_str(), dk);
   else if (pl.slab)
@@ -351,6 +524,227 @@ std::string plan_kernels(const Plan& pl, kda_dtype in_dtype, int32_t dk, int32_t
   else
     snprintf(buf, sizeof(buf), "%s + prop_kernel<%d,%d,%s>", local.c_str(), dk, dv / pl.split, t);
   return buf;
+}
+
+
+// The fused launch's work list (copied into the workspace as one block of
+// int32) and the buffers that split sequences need behind it.
+struct FusedList {
+  std::vector<int32_t> w;
+  size_t chains = 0, seqinfo = 0, segx = 0, ck_pos = 0, ck_slot = 0, wgs = 0, segs = 0, owgs = 0, cks = 0;
+  int64_t n_chains = 0, n_wg = 0, n_owg = 0, n_cks = 0;
+  int64_t n_tstate = 0, n_xpool = 0, n_qrows = 0;  // states of H*dk*dv fp32; qhat rows of H*dk bf16
+  struct Comp {
+    int32_t seq, n;  // the sequence and its segments
+    int64_t base;    // its first tstate state: E1, then A, B and the start states of segments 1..n-1
+  };
+  std::vector<Comp> comp;
+  size_t list_bytes() const { return align256(w.size() * 4); }
+};
+
+// Builds the list (ck_slot may be null when only the sizes are wanted).
+FusedList fused_list(const Plan& pl, const int32_t* cu, const int32_t* ck_cu, const int32_t* ck_pos,
+                     const int32_t* ck_slot, int32_t H, int32_t dv) {
+  FusedList f;
+  const std::vector<Entry>& ent = pl.ent;
+  const int64_t n_ent = static_cast<int64_t>(ent.size());
+  // Per split sequence: its tstate block.
+  std::vector<int64_t> tbase(pl.nseg.size(), -1);
+  for (size_t s = 0; s < pl.nseg.size(); ++s)
+    if (pl.nseg[s] > 1) {
+      tbase[s] = f.n_tstate;
+      f.comp.push_back({static_cast<int32_t>(s), pl.nseg[s], f.n_tstate});
+      f.n_tstate += 3 * pl.nseg[s] - 2;
+    }
+  std::vector<int32_t> seqinfo(6 * n_ent), segx(pl.cp ? 4 * n_ent : 0), pos, slot, segs, owgs, cks;
+  int64_t nc = 0;
+  for (int64_t i = 0; i < n_ent; ++i) {
+    const Entry& e = ent[i];
+    const int32_t sq = e.seq, n = pl.nseg[sq], cb = ck_cu ? ck_cu[sq] : 0;
+    int32_t* si = &seqinfo[6 * i];
+    si[0] = cu[sq] + e.lo;
+    si[1] = cu[sq] + e.hi;
+    si[2] = static_cast<int32_t>(pos.size());
+    for (int32_t c = e.ck0; c < e.ck1; ++c) {
+      pos.push_back(ck_pos[cb + c] - e.lo);
+      int32_t sl = 0;
+      if (e.kind == 0) sl = ck_slot ? ck_slot[cb + c] : 0;
+      else sl = static_cast<int32_t>(f.n_xpool + 2 * (c - e.ck0) + (e.kind == 2));
+      slot.push_back(sl);
+    }
+    si[3] = static_cast<int32_t>(pos.size());
+    si[4] = static_cast<int32_t>(nc);
+    nc += e.chunks;
+    si[5] = static_cast<int32_t>(nc);
+    if (!pl.cp) continue;
+    int32_t* sx = &segx[4 * i];
+    const int64_t b = tbase[sq];
+    if (n == 1) {
+      sx[0] = sx[1] = sq;
+    } else if (e.kind == 0) {  // the first segment: from s0, its end state is E1
+      sx[0] = sq;
+      sx[1] = static_cast<int32_t>(b);
+      sx[2] = kda::kSegFinalTemp;
+    } else if (e.kind == 1) {  // from zero: B of segment e.seg
+      sx[1] = static_cast<int32_t>(b + (n - 1) + e.seg);
+      sx[2] = kda::kSegZeroStart | kda::kSegFinalTemp | kda::kSegCkTemp;
+    } else {  // from the identity: A of segment e.seg, outputs to qhat
+      const int32_t len = e.hi - e.lo, start = static_cast<int32_t>(b + 2 * (n - 1) + e.seg);
+      sx[1] = static_cast<int32_t>(b + e.seg);
+      sx[3] = static_cast<int32_t>(f.n_qrows);
+      const int32_t sg = static_cast<int32_t>(segs.size() / 4);
+      segs.insert(segs.end(), {cu[sq] + e.lo, len, static_cast<int32_t>(f.n_qrows), start});
+      for (int32_t h = 0; h < H; ++h)
+        for (int32_t t0 = 0; t0 < len; t0 += kda::kFixTokens) owgs.insert(owgs.end(), {sg, h, t0});
+      for (int32_t c = e.ck0; c < e.ck1; ++c)
+        cks.insert(cks.end(), {ck_slot ? ck_slot[cb + c] : 0, static_cast<int32_t>(f.n_xpool + 2 * (c - e.ck0)),
+                               static_cast<int32_t>(f.n_xpool + 2 * (c - e.ck0) + 1), start});
+      f.n_xpool += 2 * (e.ck1 - e.ck0);
+      f.n_qrows += len;
+    }
+  }
+  // Chains: the entries' heads, the longest chain first, padded to whole
+  // rounds of eight (one per XCD).
+  std::vector<int64_t> order(n_ent);
+  std::iota(order.begin(), order.end(), 0);
+  auto ctime = [&](int64_t i) {
+    const int w = ent[i].width;
+    const double t = w == 128 ? kFusedT[0] : w == 64 ? kFusedT[1] : w == 32 ? kFusedT[2] : kFusedT[3];
+    return t * static_cast<double>(ent[i].chunks);
+  };
+  std::stable_sort(order.begin(), order.end(), [&](int64_t x, int64_t y) { return ctime(x) > ctime(y); });
+  f.n_chains = round8(n_ent * H);
+  std::vector<int32_t> chains(2 * f.n_chains);
+  int64_t c = 0;
+  for (int64_t i : order)
+    for (int32_t h = 0; h < H; ++h, ++c) {
+      chains[2 * c] = static_cast<int32_t>(i);
+      chains[2 * c + 1] = h;
+    }
+  for (; c < f.n_chains; ++c) {
+    chains[2 * c] = -1;
+    chains[2 * c + 1] = 0;
+  }
+  // Workgroups: chain << 8 | width code << 4 | tile, the tiles of 8
+  // neighbouring chains in rounds so that a chain's tiles share an XCD.
+  std::vector<int32_t> wgs;
+  auto tiles = [&](int32_t sq) { return ent[sq].kind == 2 ? 1 : dv / ent[sq].width; };
+  for (int64_t g = 0; g < f.n_chains / 8; ++g) {
+    int rounds = 0;
+    for (int x = 0; x < 8; ++x) {
+      const int32_t sq = chains[2 * (8 * g + x)];
+      if (sq >= 0) rounds = std::max(rounds, tiles(sq));
+    }
+    for (int r = 0; r < rounds; ++r)
+      for (int x = 0; x < 8; ++x) {
+        const int64_t ch = 8 * g + x;
+        const int32_t sq = chains[2 * ch];
+        int code = 15;
+        if (sq >= 0 && r < tiles(sq)) {
+          const int w = ent[sq].width;
+          code = ent[sq].kind == 2 ? 4 : w == 32 ? 0 : w == 64 ? 1 : w == 128 ? 2 : 3;
+        }
+        wgs.push_back(static_cast<int32_t>((ch << 8) | (code << 4) | (code == 15 ? 0 : r)));
+      }
+  }
+  f.n_wg = static_cast<int64_t>(wgs.size());
+  f.n_owg = static_cast<int64_t>(owgs.size() / 3);
+  f.n_cks = static_cast<int64_t>(cks.size() / 4);
+  // One block: header (word 0: the decay-range flag, zero), then the parts.
+  f.w.assign(kHeaderInts, 0);
+  auto put = [&](const std::vector<int32_t>& v) {
+    const size_t off = f.w.size();
+    f.w.insert(f.w.end(), v.begin(), v.end());
+    return off;
+  };
+  f.chains = put(chains);
+  f.seqinfo = put(seqinfo);
+  f.segx = put(segx);
+  f.ck_pos = put(pos);
+  f.ck_slot = put(slot);
+  f.wgs = put(wgs);
+  f.segs = put(segs);
+  f.owgs = put(owgs);
+  f.cks = put(cks);
+  return f;
+}
+
+
+// The fused launch, then for split sequences the composition of their
+// segments (one launch per sequence) and the correction.
+int launch_fused_list(const FusedList& fl, const void* q, const void* k, const void* v, const void* a,
+                      const void* beta, int32_t H, int32_t dk, int32_t dv, const float* s0, void* o,
+                      float* s_final, float* page_pool, int64_t page_elems, void* workspace, int32_t* err_flag,
+                      float a_lo, bool gate, float g_min, void* stream) {
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  // The work list is staged in pageable host memory: the runtime copies it
+  // before hipMemcpyAsync returns (so the call may block the host for that
+  // copy), and the vector may then go.
+  hipError_t e = hipMemcpyAsync(workspace, fl.w.data(), fl.w.size() * 4, hipMemcpyHostToDevice, hs);
+  if (e != hipSuccess) return hip_status(e, "work list copy");
+  int32_t* dw = static_cast<int32_t*>(workspace);
+  const int64_t hkv = static_cast<int64_t>(H) * dk * dv;
+  float* tstate = reinterpret_cast<float*>(static_cast<char*>(workspace) + fl.list_bytes());
+  float* xpool = tstate + fl.n_tstate * hkv;
+  void* qhat = xpool + fl.n_xpool * hkv;
+  const bool cp = !fl.comp.empty();
+  kda::PrefillArgs p{};
+  p.q = q; p.k = k; p.v = v; p.a = a; p.beta = beta;
+  p.bf16 = true;
+  p.fused = true;
+  p.gate = gate;
+  p.g_min = g_min;
+  p.H = H; p.dk = dk; p.dv = dv; p.chunk = 32;
+  p.s0 = s0; p.o = o; p.s_final = s_final;
+  p.page_pool = page_pool; p.page_elems = page_elems;
+  p.wsflag = dw;
+  p.err_flag = err_flag;
+  p.a_lo = a_lo;
+  p.chains = dw + fl.chains;
+  p.seqinfo = dw + fl.seqinfo;
+  p.ck_pos = dw + fl.ck_pos;
+  p.ck_slot = dw + fl.ck_slot;
+  p.wgs = dw + fl.wgs;
+  p.n_wg = static_cast<int>(fl.n_wg);
+  p.n_chains = static_cast<int>(fl.n_chains);
+  p.segx = cp ? dw + fl.segx : nullptr;
+  p.qhat = qhat;
+  p.xpool = xpool;
+  p.tstate = tstate;
+  p.stream = hs;
+  e = kda::launch_prefill(p);
+  if (e != hipSuccess) return hip_status(e, "prefill launch");
+  if (!cp) return ok();
+  for (const FusedList::Comp& c : fl.comp) {
+    kda::ComposeArgs ca{};
+    ca.A = tstate + (c.base + 1) * hkv;
+    ca.B = tstate + (c.base + c.n) * hkv;
+    ca.s_in = tstate + c.base * hkv;
+    ca.starts = tstate + (c.base + 2 * c.n - 1) * hkv;
+    ca.s_end = s_final ? s_final + c.seq * hkv : nullptr;
+    ca.n = c.n - 1;
+    ca.H = H; ca.dk = dk; ca.dv = dv;
+    ca.flag = dw;
+    ca.stream = hs;
+    e = kda::launch_compose(ca);
+    if (e != hipSuccess) return hip_status(e, "segment composition launch");
+  }
+  kda::FixArgs fx{};
+  fx.o = o;
+  fx.qhat = qhat;
+  fx.tstate = tstate;
+  fx.xpool = xpool;
+  fx.page_pool = page_pool;
+  fx.page_elems = page_elems;
+  fx.segs = dw + fl.segs;
+  fx.owgs = dw + fl.owgs;
+  fx.cks = dw + fl.cks;
+  fx.n_owg = static_cast<int>(fl.n_owg);
+  fx.n_cks = static_cast<int>(fl.n_cks);
+  fx.H = H; fx.dk = dk; fx.dv = dv;
+  fx.flag = dw;
+  fx.stream = hs;
+  return hip_status(kda::launch_fix(fx), "segment correction launch");
 }
 
 // Prefill (a_out == nullptr) or segment summaries (a_out != nullptr: q is
@@ -405,8 +799,21 @@ int prefill_impl(const void* q, const void* k, const void* v, const void* a, con
   if (!summary && reinterpret_cast<uintptr_t>(o) % 16) return fail(KDA_EINVAL, "o must be 16-byte aligned");
   if (err_flag && reinterpret_cast<uintptr_t>(err_flag) % 4) return fail(KDA_EINVAL, "err_flag must be aligned");
   const int64_t n_chunks = pl.n_chunks;
-  const size_t list_bytes = align256(work_ints(n_seqs, H, n_ckpt, n_chunks) * 4);
-  const size_t need = list_bytes + (pl.fused ? 0 : tile_bytes(n_chunks, H, chunk, dk, es));
+  size_t list_bytes = align256(work_ints(n_seqs, H, n_ckpt, n_chunks) * 4);
+  size_t need = list_bytes + (pl.fused ? 0 : tile_bytes(n_chunks, H, chunk, dk, es));
+  FusedList fl;
+  if (pl.fused) {
+    // Split sequences only where the workspace holds their buffers.
+    fl = fused_list(pl, cu, ck_cu, ck_pos, ck_slot, H, dv);
+    need = fl.list_bytes() + (fl.n_tstate + fl.n_xpool) * hkv * 4 + align256(fl.n_qrows * H * dk * 2);
+    if (pl.cp && workspace_bytes < need) {
+      st = make_plan(in_dtype, H, dk, dv, chunk, cu, n_seqs, ck_cu, ck_pos, n_ckpt, dv_split, summary, pl, false);
+      if (st) return st;
+      fl = fused_list(pl, cu, ck_cu, ck_pos, ck_slot, H, dv);
+      need = fl.list_bytes();
+    }
+    list_bytes = fl.list_bytes();
+  }
   if (!workspace || workspace_bytes < need)
     return fail(KDA_EWORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
   if (reinterpret_cast<uintptr_t>(workspace) & 255u)
@@ -423,6 +830,8 @@ int prefill_impl(const void* q, const void* k, const void* v, const void* a, con
       {workspace, need, "workspace"}, {err_flag, err_flag ? 4u : 0u, "err_flag"}};
   st = check_disjoint(outs, ins);
   if (st) return st;
+  if (pl.fused) return launch_fused_list(fl, q, k, v, a, beta, H, dk, dv, s0, o, s_final, page_pool, page_elems,
+                                         workspace, err_flag, a_lo, gate, g_min, stream);
 
   // Work list: chains longest sequence first, padded to whole XCD rounds.
   std::vector<int32_t> order(n_seqs);
@@ -477,9 +886,9 @@ int prefill_impl(const void* q, const void* k, const void* v, const void* a, con
     wslot[i] = ck_slot[i];
   }
 
-  // Mixed launch: one entry per workgroup, chain << 8 | width code << 4 |
-  // tile, the tiles of 8 neighbouring chains in rounds so that a chain's tiles
-  // share an XCD.
+  // Mixed launch (slab_mixed_kernel): one entry per workgroup, chain << 8 |
+  // width code << 4 | tile, the tiles of 8 neighbouring chains in rounds so
+  // that a chain's tiles share an XCD.
   int64_t n_wg = 0;
   int32_t* wgs = wchunks + 2 * n_chunks;
   if (pl.mixed) {
@@ -499,16 +908,6 @@ int prefill_impl(const void* q, const void* k, const void* v, const void* a, con
                                                 : static_cast<int32_t>((ch << 8) | (15 << 4));
         }
     }
-  } else if (pl.fused) {  // one width everywhere
-    for (int64_t g = 0; g < n_chains / 8; ++g)
-      for (int r = 0; r < pl.split; ++r)
-        for (int x = 0; x < 8; ++x) {
-          const int64_t ch = 8 * g + x;
-          const int w = dv / pl.split;
-          const int code = w == 32 ? 0 : w == 64 ? 1 : w == 128 ? 2 : 3;
-          wgs[n_wg++] = chains[2 * ch] >= 0 ? static_cast<int32_t>((ch << 8) | (code << 4) | r)
-                                            : static_cast<int32_t>((ch << 8) | (15 << 4));
-        }
   }
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -567,6 +966,21 @@ int kda_chunk_prefill_workspace_size(int32_t n_seqs, int64_t total_tokens, int32
   const int64_t mc = max_chunks(n_seqs, total_tokens, chunk, n_ckpt);
   *bytes = align256(work_ints(n_seqs, H, n_ckpt, mc) * 4) +
            (fused_path(in_dtype, dk, chunk) ? 0 : tile_bytes(mc, H, chunk, dk, elem_size(in_dtype)));
+  if (fused_path(in_dtype, dk, chunk) && dv == dk) {
+    // Room to split long sequences into segments (at most kMaxExtraSegs
+    // later segments): their work list, start, end and linear-part states
+    // (at most 4 per later segment), checkpoints from zero and from the
+    // identity (2 per checkpoint), and qhat (at most one row per token).
+    const int64_t n_ent = static_cast<int64_t>(n_seqs) + 2 * kMaxExtraSegs, nch = round8(n_ent * H);
+    const int64_t ints = kHeaderInts + 10 * nch + 10 * n_ent + 4 * n_ckpt + 4 * kMaxExtraSegs +
+                         3 * static_cast<int64_t>(H) * (total_tokens / kda::kFixTokens + kMaxExtraSegs) +
+                         4 * n_ckpt;
+    const int64_t hkv = static_cast<int64_t>(H) * dk * dv;
+    const size_t cp = align256(static_cast<size_t>(ints) * 4) +
+                      static_cast<size_t>(4 * kMaxExtraSegs + 2 * n_ckpt) * hkv * 4 +
+                      align256(static_cast<size_t>(total_tokens) * H * dk * 2);
+    *bytes = std::max(*bytes, cp);
+  }
   return ok();
 }
 

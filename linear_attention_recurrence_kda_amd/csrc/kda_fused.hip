@@ -179,6 +179,17 @@ struct FusedParams {
   bool gate;    // a, beta are logits: a = g_min * sigmoid(a), beta = sigmoid(beta)
   float g_min;
   int H, dv;
+  // Sequences split into segments (null segx: none).  segx [entries][4] =
+  // (index of the start state in s0, index of the end state in s_final or
+  // tstate, mode bits kSeg*, first row in qhat) per entry of seqinfo; state
+  // indices count H*dk*dv elements.  Identity chains (width code 4) start from
+  // the identity with v taken as zero, write their outputs (q mapped through
+  // the segment's linear part) to qhat rows, their checkpoints to xpool and
+  // their end state to tstate.
+  const int32_t* segx;
+  void* qhat;
+  float* xpool;
+  float* tstate;
 };
 
 // Loads of one chunk for one L lane: q, k, a of its token row (eight
@@ -206,7 +217,7 @@ struct Fused {
 // ---------------------------------------------------------------------------
 // The chain of one workgroup.  NPA P waves are active with NJ column tiles of
 // 16 each (tile width DVT = 16 * NJ * NPA).
-template <int DK, int NPA, int NJ>
+template <int DK, int NPA, int NJ, bool ID = false>
 __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int tile, FusedSmem<DK>& sm) {
   using F = Fused<DK>;
   constexpr int NR = F::NR, NKS = F::NKS, NCG = F::NCG, NLW = F::NLW;
@@ -231,7 +242,11 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
   const int ck_lo = ld_const(p.seqinfo, 6 * seq + 2), ck_hi = ld_const(p.seqinfo, 6 * seq + 3);
   const int c_lo = ld_const(p.seqinfo, 6 * seq + 4), c_hi = ld_const(p.seqinfo, 6 * seq + 5);
   const int64_t hkv = static_cast<int64_t>(H) * DK * dv;
-  const size_t state_off = (static_cast<size_t>(seq) * H + h) * DK * dv;
+  // The entry's mode and state index (a sequence that is not split: its own
+  // index, mode 0).
+  auto seg_field = [&](int f, int dflt) { return p.segx != nullptr ? ld_const(p.segx, 4 * seq + f) : dflt; };
+  const int mode = ID ? kSegZeroStart | kSegFinalTemp | kSegCkTemp : seg_field(2, 0);
+  const size_t state_off = (static_cast<size_t>(seg_field(0, seq)) * H + h) * DK * dv;
   const uint32_t rsv = static_cast<uint32_t>(H) * dv * 2;  // token row stride of v and o, bytes
 
   auto ck_at = [&](int k) { return k < ck_hi ? lo + ld_const(p.ck_pos, k) : INT_MAX; };
@@ -253,14 +268,14 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
   auto inc3 = [](int r) { return r == 2 ? 0 : r + 1; };
 
   // Zero the page padding of this sequence's checkpoint slots (once per sequence).
-  if (tile == 0 && h == 0 && p.page_elems > hkv) {
+  if (tile == 0 && h == 0 && p.page_elems > hkv && !(mode & kSegCkTemp)) {
     for (int c = ck_lo; c < ck_hi; ++c) {
       float* pg = p.page_pool + static_cast<int64_t>(ld_const(p.ck_slot, c)) * p.page_elems;
       for (int64_t e = hkv + tid; e < p.page_elems; e += F::NT) pg[e] = 0.f;
     }
   }
-  if (c_lo >= c_hi) {  // an empty sequence: the final state is s0
-    if (!lw && wave < NPA && p.s_final != nullptr) {
+  if (c_lo >= c_hi) {  // an empty sequence: the final state is s0 (segments are never empty)
+    if (!ID && !lw && wave < NPA && p.s_final != nullptr && mode == 0) {
       const int jw = tile * DVT + 16 * NJ * wave;
       for (int e = lane; e < DK * 16 * NJ; e += 64) {
         const int c = e / (16 * NJ), j = jw + e % (16 * NJ);
@@ -379,7 +394,8 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
       r.n = x.n;
     };
     auto load_v = [&](const auto& x, i32x4& vr) {
-      vr = ld128(tok_rsrc(p.v, x, rsv, DVT * 2, (h * dv + tile * DVT) * 2), vso);
+      if constexpr (ID) vr = i32x4{0, 0, 0, 0};
+      else vr = ld128(tok_rsrc(p.v, x, rsv, DVT * 2, (h * dv + tile * DVT) * 2), vso);
     };
     auto put_v = [&](int b, const i32x4& vr) {
       if (vlane) *reinterpret_cast<i32x4*>(&sm.vb[b][8 * ve]) = vr;
@@ -388,9 +404,13 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
     // that ends at the chunk's last row (any = false: an empty range, every
     // store is dropped, so the call sites need no branch around it).
     auto read_o = [&](int b) { return *reinterpret_cast<const i32x4*>(&sm.vb[b][8 * ve]); };
+    // (identity chains: row t of the segment [lo, hi) goes to qhat row
+    // t - lo + its first row)
+    char* const obase = ID ? static_cast<char*>(p.qhat) + (static_cast<int64_t>(seg_field(3, 0)) - lo) * rsv
+                           : static_cast<char*>(p.o);
     auto store_o = [&](const auto& x, const i32x4& ov, bool any) {
       const __amdgpu_buffer_rsrc_t ro =
-          buf_rsrc(static_cast<char*>(p.o) + (static_cast<size_t>(x.t) * H + h) * dv * 2 + tile * DVT * 2,
+          buf_rsrc(obase + (static_cast<size_t>(x.t) * H + h) * dv * 2 + tile * DVT * 2,
                    any ? (x.n - 1) * rsv + DVT * 2 : 0u);
       __builtin_amdgcn_raw_buffer_store_b128(ov, ro, vso, 0, 0);
     };
@@ -689,7 +709,11 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
 #pragma unroll
     for (int J = 0; J < NJ; ++J) {
       S[R][J] = zero4();
-      if (active && p.s0 != nullptr) {
+      if constexpr (ID) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          S[R][J][i] = 16 * R + 4 * grp + i == jw + slab_jcol<NJ>(J, col) ? 1.f : 0.f;
+      } else if (active && p.s0 != nullptr && !(mode & kSegZeroStart)) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int c = 16 * R + 4 * grp + i, j = jw + slab_jcol<NJ>(J, col);
@@ -731,6 +755,7 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
     *reinterpret_cast<OV*>(&sm.vb[b][vaddr(16 * T + col, jl + 4 * NJ * grp)]) = ov;
   };
   auto vval = [&](int b, int T, int J, int i) {
+    if constexpr (ID) return 0.f;
     return static_cast<float>(sm.vb[b][vaddr(16 * T + 4 * grp + i, jl + slab_jcol<NJ>(J, col))]);
   };
   auto frag16 = [&](const i32x4* base, int m, int q) { return __builtin_bit_cast(bf16x8, base[16 * m + swz16(m, q)]); };
@@ -841,19 +866,26 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
         for (int J = 0; J < NJ; ++J) S[R][J] = mma(a0, bU[J], S[R][J]);
       }
       scale_rows(r.en);
-      if (is_ck)
-        store_state(p.page_pool + static_cast<int64_t>(ld_const(p.ck_slot, w.ck)) * p.page_elems +
+      if (is_ck) {
+        const int64_t slot = ld_const(p.ck_slot, w.ck);
+        store_state((ID || (seg_field(2, 0) & kSegCkTemp) ? p.xpool + slot * hkv
+                                                          : p.page_pool + slot * p.page_elems) +
                     static_cast<int64_t>(h) * DK * dv);
+      }
     }
     slab_barrier();  // A
     done = stop_next;
     next_chunk(w);
   }
-  if (active && !done && p.s_final != nullptr) store_state(p.s_final + state_off);
+  if (active && !done) {
+    float* const fin = ID || (seg_field(2, 0) & kSegFinalTemp) ? p.tstate : p.s_final;
+    if (fin != nullptr) store_state(fin + (static_cast<size_t>(seg_field(1, seq)) * H + h) * DK * dv);
+  }
 }
 
 // Entry bid of p.wgs: chain << 8 | width code << 4 | tile; width code 0: 32
-// columns, 1: 64, 2: 128, 3: 16, 15: no work.
+// columns, 1: 64, 2: 128, 3: 16, 4: 128 from the identity (a segment's
+// linear part), 15: no work.
 template <int DK>
 __global__ __launch_bounds__(Fused<DK>::NT, 1) void fused_kernel(FusedParams p) {
   __shared__ __attribute__((aligned(16))) FusedSmem<DK> sm;
@@ -863,6 +895,7 @@ __global__ __launch_bounds__(Fused<DK>::NT, 1) void fused_kernel(FusedParams p) 
   else if (code == 1) fused_chain<DK, 4, 1>(p, chain, tile, sm);
   else if (code == 2) fused_chain<DK, 4, 2>(p, chain, tile, sm);
   else if (code == 3) fused_chain<DK, 1, 1>(p, chain, tile, sm);
+  else if (code == 4) fused_chain<DK, 4, 2, true>(p, chain, tile, sm);
 }
 
 }  // namespace
@@ -878,6 +911,7 @@ hipError_t launch_fused(const PrefillArgs& a) {
   prm.wsflag = a.wsflag; prm.err_flag = a.err_flag; prm.a_lo = a.a_lo;
   prm.gate = a.gate; prm.g_min = a.g_min;
   prm.H = a.H; prm.dv = a.dv;
+  prm.segx = a.segx; prm.qhat = a.qhat; prm.xpool = a.xpool; prm.tstate = a.tstate;
   if (a.n_wg == 0) return hipSuccess;
   hipLaunchKernelGGL((fused_kernel<128>), dim3(static_cast<unsigned>(a.n_wg)), dim3(Fused<128>::NT), 0, a.stream,
                      prm);

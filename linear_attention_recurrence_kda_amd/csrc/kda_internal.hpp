@@ -99,12 +99,23 @@ struct PrefillArgs {
   int32_t* wsflag;
   int32_t* err_flag;
   float a_lo;
+  // Segments of split sequences (fused path; see launch_fused): null segx
+  // when no sequence is split.
+  const int32_t* segx;
+  void* qhat;
+  float* xpool;
+  float* tstate;
   hipStream_t stream;
 };
 hipError_t launch_prefill(const PrefillArgs& p);
+
+// Mode bits of a segment entry (PrefillArgs::segx): start from the zero state
+// instead of s0; end state to tstate instead of s_final; checkpoints to xpool
+// (stride H*dk*dv) instead of the page pool.
+enum : int { kSegZeroStart = 1, kSegFinalTemp = 2, kSegCkTemp = 4 };
 // The fused prefill (one kernel, records in LDS): p.wgs lists one entry per
 // workgroup, chain << 8 | width code << 4 | tile (width code 0: 32 columns,
-// 1: 64, 2: 128, 3: 16).
+// 1: 64, 2: 128, 3: 16, 4: 128 columns from the identity with v = 0).
 hipError_t launch_fused(const PrefillArgs& p);
 // The column-slab propagation (p.slab): mode 0 prefill, 1 a segment's B, 2 its A.
 hipError_t launch_slab_prop(const PrefillArgs& p, int mode);
@@ -120,8 +131,33 @@ struct ComposeArgs {
   const float *A, *B, *s_in;
   float *starts, *s_end;
   int n, H, dk, dv;
+  const int32_t* flag;  // null, or a word that, when nonzero, makes the kernel write nothing
   hipStream_t stream;
 };
+
+// Corrections after a fused prefill with split sequences.  A segment that
+// starts at state S_in was run from zero (outputs o0, checkpoints B_ck) and
+// from the identity (outputs qhat = the segment's linear part applied to q,
+// checkpoints X_ck); the true values are o = o0 + S_in^T qhat and
+// S_ck = X_ck S_in + B_ck.
+//   segs [n_segs][4]: (first token, tokens, first qhat row, tstate index of S_in)
+//   owgs [n_owg][3]:  (segment, head, first token within the segment), each
+//                     workgroup 256 tokens of one head
+//   cks [n_cks][4]:   (page slot, xpool index of B_ck, of X_ck, tstate index of S_in)
+// The whole launch writes nothing when *flag is nonzero.
+struct FixArgs {
+  void* o;
+  const void* qhat;
+  const float *tstate, *xpool;
+  float* page_pool;
+  int64_t page_elems;
+  const int32_t *segs, *owgs, *cks;
+  int n_owg, n_cks, H, dk, dv;
+  const int32_t* flag;
+  hipStream_t stream;
+};
+hipError_t launch_fix(const FixArgs& p);
+constexpr int kFixTokens = 256;  // tokens per o-correction workgroup
 hipError_t launch_compose(const ComposeArgs& p);
 
 // Front end (convolution, SiLU, L2Norm, gates).  Prefill: one unit per tile

@@ -129,7 +129,8 @@ def test_prefill_validation(L):
     assert call(chunk=32, split=1, dk=64) == kda.KDA_EUNSUPPORTED
     # the fused kernel (bf16, chunk 32, dk 128) takes 16- to 128-column tiles
     assert call(chunk=32, split=3) == kda.KDA_EUNSUPPORTED
-    assert call(chunk=32, split=-3) == kda.KDA_EUNSUPPORTED
+    # (-n, 2 <= n <= 8: sequences in n segments; beyond that refused)
+    assert call(chunk=32, split=-9) == kda.KDA_EUNSUPPORTED
     assert call(dk=16, dv=128, split=1) == kda.KDA_EUNSUPPORTED
     assert call(dtype=0, chunk=32, split=1) == kda.KDA_EUNSUPPORTED
     assert call(split=3) == kda.KDA_EUNSUPPORTED

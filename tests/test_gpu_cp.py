@@ -1,0 +1,118 @@
+"""GPU parity of the fused prefill with sequences split into segments inside
+one call (chains of later segments from the zero state and from the
+identity, then the composition of the segment maps and the correction of
+the later segments' outputs and checkpoints) against the float64 oracle.
+
+Weak decays (a in [-0.002, 0]) keep the start state of every segment far
+above rounding at its end, so a wrong composition or correction shows in
+every row after the cut, not only in the first few."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_attention_recurrence_kda_amd import inputs, kda
+from tests.parity import assert_parity_blocks, dev_tensor
+from tests.test_gpu_prefill import _check, _run
+
+pytestmark = pytest.mark.gpu
+
+WEAK = -0.002
+
+
+def _ckpts(lens):
+    """Checkpoints on both sides of the cuts (multiples of 32 near L i / n),
+    on odd positions, and at the end."""
+    out = []
+    for L in lens:
+        pos = {1, 31, 32, 33, 511, 512, 513, 700, 1023, 1024, 1025, 1056, 1500, 1535, 1536, 2047, L - 1, L}
+        out.append(sorted(p for p in pos if 1 <= p <= L))
+    return out
+
+
+@pytest.mark.parametrize("n_seg", [2, 3, 4])
+def test_forced_segments_match_oracle(n_seg):
+    """Sequences of at least n_seg * 512 tokens in n_seg segments (dv_split =
+    -n_seg), the rest whole, nonzero S0, H = 2: outputs (also per 32-token
+    chunk), final states and every checkpoint."""
+    lens = [2100, 1100, 45, 0, 1300, 2049]
+    w = inputs.prefill_workload(700 + n_seg, lens, 2, 128, 128, "bf16", s0_std=0.1, g_min=WEAK)
+    w["checkpoints"] = _ckpts(lens)
+    _, names = kda.prefill_plan(w["cu_seqlens"], 2, 128, 128, 32, w["checkpoints"], dv_split=-n_seg)
+    assert "fix_kernel" in names, names
+    o, sf, pool, slots = _run(w, "bf16", 32, page_extra=8, dv_split=-n_seg)
+    _check(w, "bf16", o, sf, pool, slots, block=32)
+
+
+def test_automatic_segments_match_oracle():
+    """One long sequence among short ones at H = 2: the cost model splits it
+    by itself (its chain alone would bound the call); no checkpoints, zero
+    S0 on a second call."""
+    lens = [6000, 300, 64, 17]
+    w = inputs.prefill_workload(710, lens, 2, 128, 128, "bf16", s0_std=0.1, g_min=WEAK, ckpt_every=1000)
+    _, names = kda.prefill_plan(w["cu_seqlens"], 2, 128, 128, 32, w["checkpoints"])
+    assert "fix_kernel" in names, names
+    o, sf, pool, slots = _run(w, "bf16", 32)
+    _check(w, "bf16", o, sf, pool, slots, block=32)
+    w["checkpoints"] = None
+    o, sf, pool, slots = _run(w, "bf16", 32, with_s0=False)
+    w["s0"] = None
+    _check(w, "bf16", o, sf, pool, slots, block=32)
+
+
+def test_segments_run_twice_bit_equal():
+    lens = [3000, 700]
+    w = inputs.prefill_workload(711, lens, 4, 128, 128, "bf16", s0_std=0.1, g_min=WEAK, ckpt_every=512)
+    o, sf, pool, _ = _run(w, "bf16", 32, dv_split=-3)
+    o2, sf2, pool2, _ = _run(w, "bf16", 32, dv_split=-3)
+    assert torch.equal(o, o2) and torch.equal(sf, sf2)
+    assert torch.equal(pool.nan_to_num(7.0), pool2.nan_to_num(7.0))
+
+
+def test_segments_without_final_state():
+    """want_final=False: the composition still runs (the later segments need
+    their start states) and no final state is written."""
+    lens = [1500, 40]
+    w = inputs.prefill_workload(712, lens, 2, 128, 128, "bf16", s0_std=0.1, g_min=WEAK)
+    d = {n: dev_tensor(w[n], "bf16") for n in ("q", "k", "v", "a", "beta")}
+    s0 = torch.from_numpy(w["s0"]).cuda()
+    o, sf = kda.chunk_prefill(d["q"], d["k"], d["v"], d["a"], d["beta"], w["cu_seqlens"], s0=s0, chunk=32,
+                              want_final=False, dv_split=-2)
+    torch.cuda.synchronize()
+    assert sf is None
+    o_r, _, _ = oracle.kda_prefill(w["q"], w["k"], w["v"], w["a"], w["beta"], w["cu_seqlens"], w["s0"])
+    for n, (lo, hi) in enumerate([(0, 1500), (1500, 1540)]):
+        for h in range(2):
+            assert_parity_blocks(o[lo:hi, h], o_r[lo:hi, h], "bf16", 32, f"o seq {n} head {h}")
+
+
+def test_segments_bad_decay_writes_no_record():
+    """A decay below the bound in the first segment of a split sequence: the
+    flag is raised, and neither the later segments' checkpoints nor that
+    sequence's final state are written (they keep the sentinel); the other
+    sequence is complete."""
+    lens = [1200, 90]
+    H, d = 2, 128
+    w = inputs.prefill_workload(713, lens, H, d, d, "bf16", s0_std=0.1, g_min=WEAK)
+    w["a"][100, 0, 3] = -6.0
+    ck = [[64, 300, 700, 1000, 1200], [50, 90]]
+    slots = [[0, 1, 2, 3, 4], [5, 6]]
+    T = int(w["cu_seqlens"][-1])
+    sentinel = 0.375
+    dd = {n: dev_tensor(w[n], "bf16") for n in ("q", "k", "v", "a", "beta")}
+    o = torch.full((T, H, d), sentinel, dtype=torch.bfloat16, device="cuda")
+    sf = torch.full((2, H, d, d), sentinel, device="cuda")
+    pool = torch.full((7, H * d * d), sentinel, device="cuda")
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    kda.chunk_prefill(dd["q"], dd["k"], dd["v"], dd["a"], dd["beta"], w["cu_seqlens"],
+                      s0=torch.from_numpy(w["s0"]).cuda(), chunk=32, checkpoints=ck, ckpt_slots=slots,
+                      page_pool=pool, o=o, s_final=sf, err_flag=flag, dv_split=-2)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 1
+    # the cut of 1200 tokens in two segments is at 608: checkpoints 700, 1000, 1200 lie after it
+    for j in (2, 3, 4):
+        assert bool((pool[j] == sentinel).all()), f"checkpoint slot {j} written"
+    assert bool((sf[0] == sentinel).all())
+    w2 = {f: w[f][1200:] for f in ("q", "k", "v", "a", "beta")}
+    w2.update(cu_seqlens=np.array([0, 90], np.int32), s0=w["s0"][1:], checkpoints=[ck[1]])
+    _check(w2, "bf16", o[1200:], sf[1:], pool, [slots[1]])

@@ -32,13 +32,15 @@ def test_fused_ragged_every_width(dv, split):
 
 
 def test_fused_mixed_widths_in_one_launch():
-    """Chunk counts 40, 20, 8, 2 and 1 at H = 2: the cost model gives the
-    sequences different widths, so several widths share one launch."""
+    """Chunk counts 40, 20, 8, 2 and 1 at H = 2, widths per sequence without
+    segments (dv_split = -1): the cost model gives the sequences different
+    widths, so several widths share one launch."""
     lens = [32 * 40, 32 * 20, 32 * 8, 50, 9]
     w = inputs.prefill_workload(420, lens, 2, 128, 128, "bf16", s0_std=0.1, ckpt_every=256)
-    cols, _ = kda.prefill_plan(w["cu_seqlens"], 2, 128, 128, 32, w["checkpoints"])
+    cols, names = kda.prefill_plan(w["cu_seqlens"], 2, 128, 128, 32, w["checkpoints"], dv_split=-1)
     assert len(set(cols)) >= 2, cols
-    o, sf, pool, slots = _run(w, "bf16", 32)
+    assert "fix_kernel" not in names
+    o, sf, pool, slots = _run(w, "bf16", 32, dv_split=-1)
     _check(w, "bf16", o, sf, pool, slots, block=32)
 
 
