@@ -131,6 +131,7 @@ bool fused_path(kda_dtype in_dtype, int32_t dk, int32_t chunk) {
 // segment's chain is shorter, for the identity chains' work and the
 // correction's traffic.
 constexpr int kMaxExtraSegs = 8;          // later segments per call (bounds the workspace)
+constexpr int32_t kTailTokens = 960;      // tokens per tail item of the correction
 constexpr int kMinSegChunks = 16;         // chunks per segment, at least
 constexpr double kFixBytesPerUs = 5.0e6;  // the correction's streaming rate, bytes per us
 constexpr double kFixLaunchUs = 6.0;      // per extra launch
@@ -532,11 +533,13 @@ std::string plan_kernels(const Plan& pl, kda_dtype in_dtype, int32_t dk, int32_t
 struct FusedList {
   std::vector<int32_t> w;
   size_t chains = 0, seqinfo = 0, segx = 0, ck_pos = 0, ck_slot = 0, wgs = 0, segs = 0, owgs = 0, cks = 0;
-  int64_t n_chains = 0, n_wg = 0, n_owg = 0, n_cks = 0;
+  size_t titems = 0, tcnt = 0;
+  int64_t n_chains = 0, n_wg = 0, n_owg = 0, n_cks = 0, n_cnt = 0;
   int64_t n_tstate = 0, n_xpool = 0, n_qrows = 0;  // states of H*dk*dv fp32; qhat rows of H*dk bf16
   struct Comp {
-    int32_t seq, n;  // the sequence and its segments
+    int32_t seq, n;  // a sequence in n > 2 segments (two: the correction composes them)
     int64_t base;    // its first tstate state: E1, then A, B and the start states of segments 1..n-1
+    int32_t cnt;     // its first counter
   };
   std::vector<Comp> comp;
   size_t list_bytes() const { return align256(w.size() * 4); }
@@ -544,19 +547,29 @@ struct FusedList {
 
 // Builds the list (ck_slot may be null when only the sizes are wanted).
 FusedList fused_list(const Plan& pl, const int32_t* cu, const int32_t* ck_cu, const int32_t* ck_pos,
-                     const int32_t* ck_slot, int32_t H, int32_t dv) {
+                     const int32_t* ck_slot, int32_t H, int32_t dv, bool want_final) {
   FusedList f;
   const std::vector<Entry>& ent = pl.ent;
   const int64_t n_ent = static_cast<int64_t>(ent.size());
-  // Per split sequence: its tstate block.
+  // Per split sequence: its tstate block, and a completion counter per head
+  // (its first in cbase), counted by the sequence's chains (0x10000 for one
+  // stopped at a decay out of range).  In two segments the tail items wait
+  // for the count (cwant); in more, the composition and the correction
+  // launches read it when all is done.
   std::vector<int64_t> tbase(pl.nseg.size(), -1);
+  std::vector<int32_t> cbase(pl.nseg.size(), -1), cwant(pl.nseg.size(), 0);
   for (size_t s = 0; s < pl.nseg.size(); ++s)
     if (pl.nseg[s] > 1) {
       tbase[s] = f.n_tstate;
-      f.comp.push_back({static_cast<int32_t>(s), pl.nseg[s], f.n_tstate});
+      cbase[s] = static_cast<int32_t>(f.n_cnt);
+      if (pl.nseg[s] > 2) f.comp.push_back({static_cast<int32_t>(s), pl.nseg[s], f.n_tstate, cbase[s]});
       f.n_tstate += 3 * pl.nseg[s] - 2;
+      f.n_cnt += H;
     }
-  std::vector<int32_t> seqinfo(6 * n_ent), segx(pl.cp ? 4 * n_ent : 0), pos, slot, segs, owgs, cks;
+  for (const Entry& e : ent)
+    if (pl.nseg[e.seq] == 2) cwant[e.seq] += e.kind == 2 ? 1 : dv / e.width;
+  std::vector<int32_t> seqinfo(6 * n_ent), segx(pl.cp ? kda::kSegxInts * n_ent : 0), pos, slot, segs, owgs, cks;
+  std::vector<int32_t> titems;
   int64_t nc = 0;
   for (int64_t i = 0; i < n_ent; ++i) {
     const Entry& e = ent[i];
@@ -577,8 +590,9 @@ FusedList fused_list(const Plan& pl, const int32_t* cu, const int32_t* ck_cu, co
     nc += e.chunks;
     si[5] = static_cast<int32_t>(nc);
     if (!pl.cp) continue;
-    int32_t* sx = &segx[4 * i];
+    int32_t* sx = &segx[kda::kSegxInts * i];
     const int64_t b = tbase[sq];
+    sx[4] = cbase[sq];
     if (n == 1) {
       sx[0] = sx[1] = sq;
     } else if (e.kind == 0) {  // the first segment: from s0, its end state is E1
@@ -589,16 +603,33 @@ FusedList fused_list(const Plan& pl, const int32_t* cu, const int32_t* ck_cu, co
       sx[1] = static_cast<int32_t>(b + (n - 1) + e.seg);
       sx[2] = kda::kSegZeroStart | kda::kSegFinalTemp | kda::kSegCkTemp;
     } else {  // from the identity: A of segment e.seg, outputs to qhat
-      const int32_t len = e.hi - e.lo, start = static_cast<int32_t>(b + 2 * (n - 1) + e.seg);
+      // (in two segments the second starts at E1 itself)
+      const int32_t len = e.hi - e.lo, start = static_cast<int32_t>(n == 2 ? b : b + 2 * (n - 1) + e.seg);
+      const int32_t qrow = static_cast<int32_t>(f.n_qrows);
       sx[1] = static_cast<int32_t>(b + e.seg);
-      sx[3] = static_cast<int32_t>(f.n_qrows);
-      const int32_t sg = static_cast<int32_t>(segs.size() / 4);
-      segs.insert(segs.end(), {cu[sq] + e.lo, len, static_cast<int32_t>(f.n_qrows), start});
-      for (int32_t h = 0; h < H; ++h)
-        for (int32_t t0 = 0; t0 < len; t0 += kda::kFixTokens) owgs.insert(owgs.end(), {sg, h, t0});
-      for (int32_t c = e.ck0; c < e.ck1; ++c)
-        cks.insert(cks.end(), {ck_slot ? ck_slot[cb + c] : 0, static_cast<int32_t>(f.n_xpool + 2 * (c - e.ck0)),
-                               static_cast<int32_t>(f.n_xpool + 2 * (c - e.ck0) + 1), start});
+      sx[3] = qrow;
+      auto xp = [&](int32_t c, int x) { return static_cast<int32_t>(f.n_xpool + 2 * (c - e.ck0) + x); };
+      if (n == 2) {  // corrected by tail items of the fused launch
+        for (int32_t h = 0; h < H; ++h) {
+          const int32_t cnt = cbase[sq] + h, want = cwant[sq];
+          for (int32_t t0 = 0; t0 < len; t0 += kTailTokens)
+            titems.insert(titems.end(), {0, cu[sq] + e.lo, len, qrow, start, h, t0, std::min(len, t0 + kTailTokens),
+                                         cnt, want});
+          for (int32_t c = e.ck0; c < e.ck1; ++c)
+            titems.insert(titems.end(), {1, ck_slot ? ck_slot[cb + c] : 0, xp(c, 0), xp(c, 1), start, 0, h, 0, cnt,
+                                         want});
+          if (want_final)  // the final state A E1 + B
+            titems.insert(titems.end(), {1, -1 - sq, static_cast<int32_t>(b + 2), static_cast<int32_t>(b + 1),
+                                         static_cast<int32_t>(b), 1, h, 0, cnt, want});
+        }
+      } else {  // corrected by fix_kernel after compose_kernel
+        const int32_t sg = static_cast<int32_t>(segs.size() / 5);
+        segs.insert(segs.end(), {cu[sq] + e.lo, len, qrow, start, cbase[sq]});
+        for (int32_t h = 0; h < H; ++h)
+          for (int32_t t0 = 0; t0 < len; t0 += kda::kFixTokens) owgs.insert(owgs.end(), {sg, h, t0});
+        for (int32_t c = e.ck0; c < e.ck1; ++c)
+          cks.insert(cks.end(), {ck_slot ? ck_slot[cb + c] : 0, xp(c, 0), xp(c, 1), start, 0, cbase[sq]});
+      }
       f.n_xpool += 2 * (e.ck1 - e.ck0);
       f.n_qrows += len;
     }
@@ -647,9 +678,11 @@ FusedList fused_list(const Plan& pl, const int32_t* cu, const int32_t* ck_cu, co
         wgs.push_back(static_cast<int32_t>((ch << 8) | (code << 4) | (code == 15 ? 0 : r)));
       }
   }
+  // Tail items last: each starts only after every chain has started.
+  for (size_t t = 0; t < titems.size() / 10; ++t) wgs.push_back(static_cast<int32_t>((t << 8) | (5 << 4)));
   f.n_wg = static_cast<int64_t>(wgs.size());
   f.n_owg = static_cast<int64_t>(owgs.size() / 3);
-  f.n_cks = static_cast<int64_t>(cks.size() / 4);
+  f.n_cks = static_cast<int64_t>(cks.size() / 6);
   // One block: header (word 0: the decay-range flag, zero), then the parts.
   f.w.assign(kHeaderInts, 0);
   auto put = [&](const std::vector<int32_t>& v) {
@@ -666,6 +699,8 @@ FusedList fused_list(const Plan& pl, const int32_t* cu, const int32_t* ck_cu, co
   f.segs = put(segs);
   f.owgs = put(owgs);
   f.cks = put(cks);
+  f.titems = put(titems);
+  f.tcnt = put(std::vector<int32_t>(f.n_cnt, 0));
   return f;
 }
 
@@ -687,7 +722,7 @@ int launch_fused_list(const FusedList& fl, const void* q, const void* k, const v
   float* tstate = reinterpret_cast<float*>(static_cast<char*>(workspace) + fl.list_bytes());
   float* xpool = tstate + fl.n_tstate * hkv;
   void* qhat = xpool + fl.n_xpool * hkv;
-  const bool cp = !fl.comp.empty();
+  const bool cp = fl.n_tstate > 0;
   kda::PrefillArgs p{};
   p.q = q; p.k = k; p.v = v; p.a = a; p.beta = beta;
   p.bf16 = true;
@@ -708,13 +743,15 @@ int launch_fused_list(const FusedList& fl, const void* q, const void* k, const v
   p.n_wg = static_cast<int>(fl.n_wg);
   p.n_chains = static_cast<int>(fl.n_chains);
   p.segx = cp ? dw + fl.segx : nullptr;
+  p.titems = dw + fl.titems;
+  p.tcnt = dw + fl.tcnt;
   p.qhat = qhat;
   p.xpool = xpool;
   p.tstate = tstate;
   p.stream = hs;
   e = kda::launch_prefill(p);
   if (e != hipSuccess) return hip_status(e, "prefill launch");
-  if (!cp) return ok();
+  if (fl.n_owg + fl.n_cks == 0) return ok();  // (sequences in two segments: corrected in the launch)
   for (const FusedList::Comp& c : fl.comp) {
     kda::ComposeArgs ca{};
     ca.A = tstate + (c.base + 1) * hkv;
@@ -724,7 +761,7 @@ int launch_fused_list(const FusedList& fl, const void* q, const void* k, const v
     ca.s_end = s_final ? s_final + c.seq * hkv : nullptr;
     ca.n = c.n - 1;
     ca.H = H; ca.dk = dk; ca.dv = dv;
-    ca.flag = dw;
+    ca.flag = dw + fl.tcnt + c.cnt;
     ca.stream = hs;
     e = kda::launch_compose(ca);
     if (e != hipSuccess) return hip_status(e, "segment composition launch");
@@ -736,13 +773,14 @@ int launch_fused_list(const FusedList& fl, const void* q, const void* k, const v
   fx.xpool = xpool;
   fx.page_pool = page_pool;
   fx.page_elems = page_elems;
+  fx.s_final = s_final;
   fx.segs = dw + fl.segs;
   fx.owgs = dw + fl.owgs;
   fx.cks = dw + fl.cks;
   fx.n_owg = static_cast<int>(fl.n_owg);
   fx.n_cks = static_cast<int>(fl.n_cks);
   fx.H = H; fx.dk = dk; fx.dv = dv;
-  fx.flag = dw;
+  fx.cnt = dw + fl.tcnt;
   fx.stream = hs;
   return hip_status(kda::launch_fix(fx), "segment correction launch");
 }
@@ -804,12 +842,12 @@ int prefill_impl(const void* q, const void* k, const void* v, const void* a, con
   FusedList fl;
   if (pl.fused) {
     // Split sequences only where the workspace holds their buffers.
-    fl = fused_list(pl, cu, ck_cu, ck_pos, ck_slot, H, dv);
+    fl = fused_list(pl, cu, ck_cu, ck_pos, ck_slot, H, dv, s_final != nullptr);
     need = fl.list_bytes() + (fl.n_tstate + fl.n_xpool) * hkv * 4 + align256(fl.n_qrows * H * dk * 2);
     if (pl.cp && workspace_bytes < need) {
       st = make_plan(in_dtype, H, dk, dv, chunk, cu, n_seqs, ck_cu, ck_pos, n_ckpt, dv_split, summary, pl, false);
       if (st) return st;
-      fl = fused_list(pl, cu, ck_cu, ck_pos, ck_slot, H, dv);
+      fl = fused_list(pl, cu, ck_cu, ck_pos, ck_slot, H, dv, s_final != nullptr);
       need = fl.list_bytes();
     }
     list_bytes = fl.list_bytes();
@@ -972,9 +1010,12 @@ int kda_chunk_prefill_workspace_size(int32_t n_seqs, int64_t total_tokens, int32
     // (at most 4 per later segment), checkpoints from zero and from the
     // identity (2 per checkpoint), and qhat (at most one row per token).
     const int64_t n_ent = static_cast<int64_t>(n_seqs) + 2 * kMaxExtraSegs, nch = round8(n_ent * H);
-    const int64_t ints = kHeaderInts + 10 * nch + 10 * n_ent + 4 * n_ckpt + 4 * kMaxExtraSegs +
+    // (tail items: rows of every token and head, states of every checkpoint
+    // and final state and head, each a workgroup entry too)
+    const int64_t items = static_cast<int64_t>(H) * (total_tokens / kTailTokens + 3 * kMaxExtraSegs + n_ckpt);
+    const int64_t ints = kHeaderInts + 10 * nch + (6 + kda::kSegxInts) * n_ent + 4 * n_ckpt + 5 * kMaxExtraSegs +
                          3 * static_cast<int64_t>(H) * (total_tokens / kda::kFixTokens + kMaxExtraSegs) +
-                         4 * n_ckpt;
+                         6 * (n_ckpt + kMaxExtraSegs) + 11 * items + static_cast<int64_t>(H) * kMaxExtraSegs;
     const int64_t hkv = static_cast<int64_t>(H) * dk * dv;
     const size_t cp = align256(static_cast<size_t>(ints) * 4) +
                       static_cast<size_t>(4 * kMaxExtraSegs + 2 * n_ckpt) * hkv * 4 +

@@ -1,0 +1,217 @@
+// Corrections for sequences split into segments inside one fused prefill
+// (context parallelism on one GPU): the device code, run by fix_kernel
+// (kda_cp.hip) and by the fused kernel's tail workgroups (kda_fused.hip).
+//
+// The recurrence is affine in the state ("Kimi Linear 的 KDA 缓存" page,
+// "KDA 的递推与充分状态"; the "Serve 模块交互式演示" page reduces a segment
+// of a long sequence to a fixed-size summary in §1.7 and composes them in
+// §7.2): after t tokens of a segment that starts at S_in,
+//   S_t = X_t S_in + B_t,
+// with X_t the product of the token maps' linear parts (the state reached
+// from the identity with v = 0) and B_t the state reached from zero.  The
+// output o_t = S_t^T q_t is then B_t^T q_t + S_in^T (X_t^T q_t).  The fused
+// prefill runs a split sequence's later segments from zero (giving B_t^T q_t
+// and the checkpoints B_ck) and from the identity (giving qhat_t = X_t^T q_t,
+// whose dk entries are that chain's outputs, and the checkpoints X_ck), all
+// at once beside the first segment; once the segments' start states are
+// known (the composition of the segment maps, compose_kernel), the
+// correction adds S_in^T qhat_t to every output row of the segment and writes every
+// checkpoint of it as X_ck S_in + B_ck (and, for a sequence in two segments,
+// its final state as A S_in + B: the composition of one map).
+//
+// o rows: bf16 MFMA (16x16x32) on S_in rounded to bf16, the operand
+// precision the prefill's own output products use, accumulated in fp32 onto
+// the stored row.  Formed transposed (o^T += S_in^T qhat^T), with the rows
+// of two column tiles interleaved so that a lane holds eight consecutive
+// columns of one output row and moves them as one 16-byte piece; qhat is read
+// as 16-byte pieces of one row.  States: fp32 MFMA (16x16x4).
+#pragma once
+
+#include "kda_prefill_slab.hpp"
+
+namespace kda {
+namespace {
+
+constexpr int kFixD = 128;      // dk = dv
+constexpr int kFixCkRows = 32;  // state rows per state block
+constexpr int kStPitch = kFixD + 8;  // bf16 per row of S_in^T in LDS (16 bytes of padding)
+// State blocks: X's rows (pitch 132) and a 32-row slab of S_in (pitch 144),
+// pitches that put the lanes of an MFMA operand read on distinct banks.
+constexpr int kXPitch = kFixD + 4, kSPitch = kFixD + 16;
+constexpr int kFixLds = 36864;  // bytes of LDS either role needs
+static_assert(kFixD * kStPitch * 2 <= kFixLds, "S_in^T fits the LDS block");
+static_assert((kXPitch + kSPitch) * kFixCkRows * 4 <= kFixLds, "state tiles fit the LDS block");
+
+struct FixView {
+  void* o;
+  const void* qhat;
+  const float *tstate, *xpool;
+  float* page_pool;
+  float* s_final;
+  int64_t page_elems;
+  int H;
+};
+
+// Output column of row r (0..15) of column tile 2p + j of S_in^T: the two
+// tiles of pair p give a lane (rows 4g .. 4g + 3 of each) the eight
+// consecutive columns 32p + 8g .. + 7 of its output row, one 16-byte piece.
+__device__ __forceinline__ int fix_col(int p, int j, int r) { return 32 * p + 8 * (r >> 2) + 4 * j + (r & 3); }
+
+// o += S_in^T qhat for tokens [t0, t1) of one head of one segment (first
+// token lo, len tokens, qhat rows from qrow, S_in = tstate state si), by the
+// NW waves of the workgroup, in blocks of 16 NW tokens: wave w takes tokens
+// 16w .. 16w + 15 of a block and every column.  S_in^T waits in LDS as bf16
+// (rows = output columns, 16-byte fragment reads, read again for every block
+// so that few registers stay live); the next two blocks' qhat and o are in
+// flight while a block is multiplied and stored.
+template <int NW>
+__device__ __forceinline__ void fix_rows(const FixView& p, int lo, int len, int qrow, int si, int h, int t0, int t1,
+                                         char* lds) {
+  constexpr int NB = 16 * NW;  // tokens per block
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const float* S = p.tstate + (static_cast<int64_t>(si) * p.H + h) * kFixD * kFixD;
+  __bf16* st = reinterpret_cast<__bf16*>(lds);
+  const uint32_t rs = static_cast<uint32_t>(p.H) * kFixD * 2;  // token row stride of qhat and o, bytes
+  const int end = min(len, t1);
+  const uint32_t row = static_cast<uint32_t>(16 * wave + l16) * rs;
+  struct Blk {
+    i32x4 q[4], o[4];
+  };
+  // Block starting at token r0 of the segment; rows past the range (or a
+  // block past it: r0 >= end) read as zero and are not written.
+  auto rsrc = [&](const void* base, int64_t first, int r0) {
+    const int n = min(NB, end - r0);
+    return buf_rsrc(static_cast<const char*>(base) + ((first + r0) * p.H + h) * kFixD * 2,
+                    n > 0 ? static_cast<uint32_t>(n - 1) * rs + kFixD * 2 : 0u);
+  };
+  auto load = [&](int r0, Blk& b) {
+    const __amdgpu_buffer_rsrc_t rq = rsrc(p.qhat, qrow, r0), ro = rsrc(p.o, lo, r0);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      b.q[ks] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, row + (32 * ks + 8 * g) * 2, 0, 0));
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp)
+      b.o[pp] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, row + (32 * pp + 8 * g) * 2, 0, 0));
+  };
+  Blk b0, b1, b2;
+  load(t0, b0);
+  load(t0 + NB, b1);
+  for (int e = tid; e < kFixD * kFixD / 4; e += 64 * NW) {
+    const int k = e / (kFixD / 4), n4 = 4 * (e % (kFixD / 4));
+    const float4 x = *reinterpret_cast<const float4*>(&S[k * kFixD + n4]);
+    st[(n4 + 0) * kStPitch + k] = static_cast<__bf16>(x.x);
+    st[(n4 + 1) * kStPitch + k] = static_cast<__bf16>(x.y);
+    st[(n4 + 2) * kStPitch + k] = static_cast<__bf16>(x.z);
+    st[(n4 + 3) * kStPitch + k] = static_cast<__bf16>(x.w);
+  }
+  __syncthreads();
+  for (int r0 = t0; r0 < end; r0 += NB) {
+    load(r0 + 2 * NB, b2);
+    asm volatile("" ::: "memory");  // (S_in^T is read from LDS per block, not held in registers)
+    const __amdgpu_buffer_rsrc_t ro = rsrc(p.o, lo, r0);
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      const bf16x8 o8 = __builtin_bit_cast(bf16x8, b0.o[pp]);
+      f32x4 acc[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[j][i] = static_cast<float>(o8[4 * j + i]);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 qb = __builtin_bit_cast(bf16x8, b0.q[ks]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const bf16x8 sa = *reinterpret_cast<const bf16x8*>(&st[fix_col(pp, j, l16) * kStPitch + 32 * ks + 8 * g]);
+          acc[j] = mma(sa, qb, acc[j]);
+        }
+      }
+      bf16x8 r8;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r8[4 * j + i] = static_cast<__bf16>(acc[j][i]);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, r8), ro, row + (32 * pp + 8 * g) * 2, 0, 0);
+    }
+    b0 = b1;
+    b1 = b2;
+  }
+}
+
+// Rows 32 rb .. 32 rb + 31 of one head of a state dst = X S_in + B in fp32
+// MFMA (16x16x4), by waves 0..3 of the workgroup (every thread of it passes
+// the barriers): wave w forms columns 32w .. 32w + 31 (two by two 16x16
+// tiles); X's rows and S_in, in slabs of 32 rows, pass through LDS.  dst,
+// X, B and S_in point at the head's [dk][dv] block.
+__device__ __forceinline__ void fix_state(float* dst, const float* X, const float* B, const float* S, int rb,
+                                          char* lds) {
+  float* xs = reinterpret_cast<float*>(lds);
+  float* ss = xs + kFixCkRows * kXPitch;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, g = lane >> 4;
+  const bool on = tid < 256;
+  const int r0 = kFixCkRows * rb;
+  auto copy_rows = [&](float* to, int pitch, const float* from) {  // 32 rows of 128
+    for (int e = tid; on && e < kFixCkRows * kFixD / 4; e += 256) {
+      const float4 x = *reinterpret_cast<const float4*>(&from[4 * e]);
+      float* d = &to[(e / (kFixD / 4)) * pitch + 4 * (e % (kFixD / 4))];
+      d[0] = x.x; d[1] = x.y; d[2] = x.z; d[3] = x.w;
+    }
+  };
+  __syncthreads();  // (the LDS block is free)
+  copy_rows(xs, kXPitch, X + r0 * kFixD);
+  // D tile (rt, ct): rows r0 + 16 rt + 4g + i, column 32 wave + 16 ct + l16.
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[rt][ct][i] = on ? B[(r0 + 16 * rt + 4 * g + i) * kFixD + 32 * wave + 16 * ct + l16] : 0.f;
+  for (int sl = 0; sl < kFixD / kFixCkRows; ++sl) {
+    __syncthreads();  // (the previous slab is consumed)
+    copy_rows(ss, kSPitch, S + sl * kFixCkRows * kFixD);
+    __syncthreads();
+    if (on) {
+#pragma unroll
+      for (int ks = 0; ks < kFixCkRows / 4; ++ks) {
+        const int k = 4 * ks + g;
+        float a[2], b[2];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) a[rt] = xs[(16 * rt + l16) * kXPitch + kFixCkRows * sl + k];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) b[ct] = ss[k * kSPitch + 32 * wave + 16 * ct + l16];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct)
+            acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[rt], b[ct], acc[rt][ct], 0, 0, 0);
+      }
+    }
+  }
+  if (on) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[(r0 + 16 * rt + 4 * g + i) * kFixD + 32 * wave + 16 * ct + l16] = acc[rt][ct][i];
+  }
+}
+
+// A state item (dsti: page slot, or -1 - n for the final state of sequence
+// n; B and X from tstate when in_t, else xpool; S_in = tstate state si):
+// row block rb of head h, and (h = rb = 0) the page's zero padding.
+__device__ __forceinline__ void fix_state_item(const FixView& p, int64_t dsti, int bi, int xi, int si, bool in_t,
+                                               int h, int rb, char* lds) {
+  const int64_t hkv = static_cast<int64_t>(p.H) * kFixD * kFixD, hoff = static_cast<int64_t>(h) * kFixD * kFixD;
+  const float* pool = in_t ? p.tstate : p.xpool;
+  float* dst = (dsti >= 0 ? p.page_pool + dsti * p.page_elems : p.s_final + (-1 - dsti) * hkv) + hoff;
+  fix_state(dst, pool + xi * hkv + hoff, pool + bi * hkv + hoff, p.tstate + si * hkv + hoff, rb, lds);
+  if (dsti >= 0 && h == 0 && rb == 0)
+    for (int64_t e = hkv + threadIdx.x; e < p.page_elems; e += blockDim.x) (p.page_pool + dsti * p.page_elems)[e] = 0.f;
+}
+
+}  // namespace
+}  // namespace kda

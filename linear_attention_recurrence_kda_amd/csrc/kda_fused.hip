@@ -74,8 +74,10 @@
 // over: the outputs and checkpoints of the chunks before x stay written,
 // nothing after them (nor the final state) is.
 #include <climits>
+#include <cstddef>
 #include <type_traits>
 
+#include "kda_cp.hpp"
 #include "kda_prefill_slab.hpp"
 
 namespace kda {
@@ -179,17 +181,23 @@ struct FusedParams {
   bool gate;    // a, beta are logits: a = g_min * sigmoid(a), beta = sigmoid(beta)
   float g_min;
   int H, dv;
-  // Sequences split into segments (null segx: none).  segx [entries][4] =
+  // Sequences split into segments (null segx: none).  segx [entries][6] =
   // (index of the start state in s0, index of the end state in s_final or
-  // tstate, mode bits kSeg*, first row in qhat) per entry of seqinfo; state
-  // indices count H*dk*dv elements.  Identity chains (width code 4) start from
-  // the identity with v taken as zero, write their outputs (q mapped through
-  // the segment's linear part) to qhat rows, their checkpoints to xpool and
-  // their end state to tstate.
+  // tstate, mode bits kSeg*, first row in qhat, completion counter of head 0
+  // or -1, unused) per entry of seqinfo; state indices count H*dk*dv
+  // elements.  Identity chains (width code 4) start from the identity with v
+  // taken as zero, write their outputs (q mapped through the segment's linear
+  // part) to qhat rows, their checkpoints to xpool and their end state to
+  // tstate.
   const int32_t* segx;
   void* qhat;
   float* xpool;
   float* tstate;
+  // Tail workgroups (width code 5): the correction of sequences in two
+  // segments, items titems [n][10] (see fused_tail), each waiting for the
+  // chains it reads through tcnt (counters in the workspace, zero on entry).
+  const int32_t* titems;
+  int32_t* tcnt;
 };
 
 // Loads of one chunk for one L lane: q, k, a of its token row (eight
@@ -244,7 +252,7 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
   const int64_t hkv = static_cast<int64_t>(H) * DK * dv;
   // The entry's mode and state index (a sequence that is not split: its own
   // index, mode 0).
-  auto seg_field = [&](int f, int dflt) { return p.segx != nullptr ? ld_const(p.segx, 4 * seq + f) : dflt; };
+  auto seg_field = [&](int f, int dflt) { return p.segx != nullptr ? ld_const(p.segx, kSegxInts * seq + f) : dflt; };
   const int mode = ID ? kSegZeroStart | kSegFinalTemp | kSegCkTemp : seg_field(2, 0);
   const size_t state_off = (static_cast<size_t>(seg_field(0, seq)) * H + h) * DK * dv;
   const uint32_t rsv = static_cast<uint32_t>(H) * dv * 2;  // token row stride of v and o, bytes
@@ -883,19 +891,85 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
   }
 }
 
+// ---------------------------------------------------------------------------
+// The tail: the correction of a sequence in two segments (kda_cp.hpp) by
+// workgroups listed after every chain, so that they start only once every
+// chain's workgroup has started (workgroups start in list order), and then
+// wait, as the chains they read finish, on a counter per (sequence, head)
+// that each of those chains raises when its stores are complete (1, or
+// 0x10000 for a chain that stopped at a decay out of range: then nothing is
+// corrected).  The wait is bounded: past kTailSpin polls the workgroup
+// raises the error flags and corrects nothing.  The chains of a sequence's
+// head finish well before the launch's last chains (they are the longest
+// and start first), so the correction runs beside the launch's tail.
+//   titems [10]: rows: (0, first token, tokens, first qhat row, tstate index
+//   of S_in, head, first and end token within the segment, counter, count);
+//   states: (1, page slot or -1 - sequence, B, X, tstate index of S_in, 1:
+//   B and X in tstate / 0: in xpool, head, unused, counter, count).
+constexpr int kTailSpin = 1 << 24;  // polls of about 0.3 us: a few seconds
+
+template <int DK>
+__device__ __forceinline__ void fused_tail(const FusedParams& p, int item, FusedSmem<DK>& sm) {
+  auto f = [&](int i) { return ld_const(p.titems, 10 * item + i); };
+  if (threadIdx.x == 0) {
+    const int want = f(9);
+    int c = 0;
+    for (int n = 0; n < kTailSpin; ++n) {
+      c = __hip_atomic_load(p.tcnt + f(8), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (c >= want) break;
+      __builtin_amdgcn_s_sleep(8);
+    }
+    if (c < want) {  // (never, while every chain of the launch ends)
+      *p.wsflag = 1;
+      if (p.err_flag != nullptr) *p.err_flag = 1;
+    }
+    __threadfence();  // acquire: the chains' stores are visible from here on
+    sm.stop[0] = c == want;
+  }
+  __syncthreads();
+  if (!sm.stop[0]) return;
+  const FixView v{p.o, p.qhat, p.tstate, p.xpool, p.page_pool, p.s_final, p.page_elems, p.H};
+  char* lds = reinterpret_cast<char*>(&sm);  // (kFixLds bytes from its start, clear of stop[])
+  if (f(0) == 0) {
+    fix_rows<Fused<DK>::NT / 64>(v, f(1), f(2), f(3), f(4), f(5), f(6), f(7), lds);
+  } else {
+    for (int rb = 0; rb < kFixD / kFixCkRows; ++rb) fix_state_item(v, f(1), f(2), f(3), f(4), f(5) != 0, f(6), rb, lds);
+  }
+}
+
 // Entry bid of p.wgs: chain << 8 | width code << 4 | tile; width code 0: 32
 // columns, 1: 64, 2: 128, 3: 16, 4: 128 from the identity (a segment's
-// linear part), 15: no work.
+// linear part), 5: tail item (in place of the chain), 15: no work.
 template <int DK>
 __global__ __launch_bounds__(Fused<DK>::NT, 1) void fused_kernel(FusedParams p) {
   __shared__ __attribute__((aligned(16))) FusedSmem<DK> sm;
+  static_assert(offsetof(FusedSmem<DK>, stop) >= kFixLds, "the tail's LDS block lies clear of stop[]");
   const int e = ld_const(p.wgs, blockIdx.x);
   const int chain = e >> 8, code = (e >> 4) & 15, tile = e & 15;
+  if (code == 5) {
+    fused_tail<DK>(p, chain, sm);
+    return;
+  }
   if (code == 0) fused_chain<DK, 2, 1>(p, chain, tile, sm);
   else if (code == 1) fused_chain<DK, 4, 1>(p, chain, tile, sm);
   else if (code == 2) fused_chain<DK, 4, 2>(p, chain, tile, sm);
   else if (code == 3) fused_chain<DK, 1, 1>(p, chain, tile, sm);
   else if (code == 4) fused_chain<DK, 4, 2, true>(p, chain, tile, sm);
+  // A chain that tail workgroups read: its stores complete (every wave),
+  // then one release and the count.
+  if (code <= 4 && p.segx != nullptr) {
+    const int seq = ld_const(p.chains, 2 * chain);
+    const int cb = seq >= 0 ? ld_const(p.segx, kSegxInts * seq + 4) : -1;
+    if (cb >= 0) {
+      vm_drain();
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        const bool stopped = (sm.stop[0] | sm.stop[1] | sm.stop[2]) != 0;
+        __threadfence();
+        atomicAdd(p.tcnt + cb + ld_const(p.chains, 2 * chain + 1), stopped ? 0x10000 : 1);
+      }
+    }
+  }
 }
 
 }  // namespace
@@ -912,6 +986,7 @@ hipError_t launch_fused(const PrefillArgs& a) {
   prm.gate = a.gate; prm.g_min = a.g_min;
   prm.H = a.H; prm.dv = a.dv;
   prm.segx = a.segx; prm.qhat = a.qhat; prm.xpool = a.xpool; prm.tstate = a.tstate;
+  prm.titems = a.titems; prm.tcnt = a.tcnt;
   if (a.n_wg == 0) return hipSuccess;
   hipLaunchKernelGGL((fused_kernel<128>), dim3(static_cast<unsigned>(a.n_wg)), dim3(Fused<128>::NT), 0, a.stream,
                      prm);

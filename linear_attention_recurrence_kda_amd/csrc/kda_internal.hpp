@@ -105,6 +105,8 @@ struct PrefillArgs {
   void* qhat;
   float* xpool;
   float* tstate;
+  const int32_t* titems;  // tail items of sequences in two segments
+  int32_t* tcnt;          // their completion counters (zero on entry)
   hipStream_t stream;
 };
 hipError_t launch_prefill(const PrefillArgs& p);
@@ -113,6 +115,7 @@ hipError_t launch_prefill(const PrefillArgs& p);
 // instead of s0; end state to tstate instead of s_final; checkpoints to xpool
 // (stride H*dk*dv) instead of the page pool.
 enum : int { kSegZeroStart = 1, kSegFinalTemp = 2, kSegCkTemp = 4 };
+constexpr int kSegxInts = 6;  // ints per segx entry
 // The fused prefill (one kernel, records in LDS): p.wgs lists one entry per
 // workgroup, chain << 8 | width code << 4 | tile (width code 0: 32 columns,
 // 1: 64, 2: 128, 3: 16, 4: 128 columns from the identity with v = 0).
@@ -131,7 +134,7 @@ struct ComposeArgs {
   const float *A, *B, *s_in;
   float *starts, *s_end;
   int n, H, dk, dv;
-  const int32_t* flag;  // null, or a word that, when nonzero, makes the kernel write nothing
+  const int32_t* flag;  // null, or a word per head: at 0x10000 or more that head is not written
   hipStream_t stream;
 };
 
@@ -140,24 +143,31 @@ struct ComposeArgs {
 // from the identity (outputs qhat = the segment's linear part applied to q,
 // checkpoints X_ck); the true values are o = o0 + S_in^T qhat and
 // S_ck = X_ck S_in + B_ck.
-//   segs [n_segs][4]: (first token, tokens, first qhat row, tstate index of S_in)
+//   segs [n_segs][5]: (first token, tokens, first qhat row, tstate index of S_in,
+//                     first counter)
 //   owgs [n_owg][3]:  (segment, head, first token within the segment), each
-//                     workgroup 256 tokens of one head
-//   cks [n_cks][4]:   (page slot, xpool index of B_ck, of X_ck, tstate index of S_in)
-// The whole launch writes nothing when *flag is nonzero.
+//                     workgroup kFixTokens tokens of one head
+//   cks [n_cks][6]:   states X S_in + B: (destination: page slot, or -1 - n for
+//                     the final state of sequence n; index of B, of X; tstate
+//                     index of S_in; 0: B and X in xpool, 1: in tstate; first
+//                     counter)
+// A (sequence, head) whose counter (cnt[first counter + head], raised by
+// its chains) is 0x10000 or more had a chain stopped at a decay out of
+// range: nothing of it is corrected.
 struct FixArgs {
   void* o;
   const void* qhat;
   const float *tstate, *xpool;
   float* page_pool;
+  float* s_final;
   int64_t page_elems;
   const int32_t *segs, *owgs, *cks;
   int n_owg, n_cks, H, dk, dv;
-  const int32_t* flag;
+  const int32_t* cnt;
   hipStream_t stream;
 };
 hipError_t launch_fix(const FixArgs& p);
-constexpr int kFixTokens = 256;  // tokens per o-correction workgroup
+constexpr int kFixTokens = 512;  // tokens per o-correction workgroup
 hipError_t launch_compose(const ComposeArgs& p);
 
 // Front end (convolution, SiLU, L2Norm, gates).  Prefill: one unit per tile

@@ -76,9 +76,9 @@ __global__ __launch_bounds__(kComposeThreads) void compose_kernel(ComposeArgs p)
   constexpr int KS = DK / 4;            // k-steps; lane group g covers k = KS g + s
   constexpr int NV = KS / 4;            // float4s of A per row tile and lane
   __shared__ float S[DK][kComposeCols + 1];
-  if (p.flag != nullptr && *p.flag != 0) return;  // (uniform: every wave leaves)
   const int tiles = p.dv / kComposeCols;
   const int h = blockIdx.x / tiles, j0 = (blockIdx.x % tiles) * kComposeCols;
+  if (p.flag != nullptr && p.flag[h] >= 0x10000) return;  // (uniform: every wave leaves)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, g = lane >> 4;

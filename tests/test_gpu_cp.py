@@ -12,7 +12,7 @@ import torch
 
 import oracle
 from linear_attention_recurrence_kda_amd import inputs, kda
-from tests.parity import assert_parity_blocks, dev_tensor
+from tests.parity import assert_parity, assert_parity_blocks, dev_tensor
 from tests.test_gpu_prefill import _check, _run
 
 pytestmark = pytest.mark.gpu
@@ -86,16 +86,18 @@ def test_segments_without_final_state():
             assert_parity_blocks(o[lo:hi, h], o_r[lo:hi, h], "bf16", 32, f"o seq {n} head {h}")
 
 
-def test_segments_bad_decay_writes_no_record():
-    """A decay below the bound in the first segment of a split sequence: the
-    flag is raised, and neither the later segments' checkpoints nor that
-    sequence's final state are written (they keep the sentinel); the other
-    sequence is complete."""
-    lens = [1200, 90]
+@pytest.mark.parametrize("n_seg", [2, 3])
+def test_segments_bad_decay_stops_that_head(n_seg):
+    """A decay below the bound in the first segment of a split sequence, head
+    0: the flag is raised; as without segments, that (sequence, head) keeps
+    what came before the bad chunk and writes no later checkpoint (those of
+    the later segments included) and no final state; head 1 of the same
+    sequence and the other sequence are complete."""
+    lens = [1700, 90]
     H, d = 2, 128
     w = inputs.prefill_workload(713, lens, H, d, d, "bf16", s0_std=0.1, g_min=WEAK)
     w["a"][100, 0, 3] = -6.0
-    ck = [[64, 300, 700, 1000, 1200], [50, 90]]
+    ck = [[64, 300, 900, 1200, 1700], [50, 90]]
     slots = [[0, 1, 2, 3, 4], [5, 6]]
     T = int(w["cu_seqlens"][-1])
     sentinel = 0.375
@@ -104,15 +106,28 @@ def test_segments_bad_decay_writes_no_record():
     sf = torch.full((2, H, d, d), sentinel, device="cuda")
     pool = torch.full((7, H * d * d), sentinel, device="cuda")
     flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    _, names = kda.prefill_plan(w["cu_seqlens"], H, d, d, 32, ck, dv_split=-n_seg)
+    assert "fix_kernel" in names
     kda.chunk_prefill(dd["q"], dd["k"], dd["v"], dd["a"], dd["beta"], w["cu_seqlens"],
                       s0=torch.from_numpy(w["s0"]).cuda(), chunk=32, checkpoints=ck, ckpt_slots=slots,
-                      page_pool=pool, o=o, s_final=sf, err_flag=flag, dv_split=-2)
+                      page_pool=pool, o=o, s_final=sf, err_flag=flag, dv_split=-n_seg)
     torch.cuda.synchronize()
     assert int(flag.item()) == 1
-    # the cut of 1200 tokens in two segments is at 608: checkpoints 700, 1000, 1200 lie after it
-    for j in (2, 3, 4):
-        assert bool((pool[j] == sentinel).all()), f"checkpoint slot {j} written"
-    assert bool((sf[0] == sentinel).all())
-    w2 = {f: w[f][1200:] for f in ("q", "k", "v", "a", "beta")}
-    w2.update(cu_seqlens=np.array([0, 90], np.int32), s0=w["s0"][1:], checkpoints=[ck[1]])
-    _check(w2, "bf16", o[1200:], sf[1:], pool, [slots[1]])
+    o_r, sf_r, ck_r = oracle.kda_prefill(w["q"], w["k"], w["v"], w["a"], w["beta"], w["cu_seqlens"], w["s0"], ck)
+    page = pool.reshape(7, H, d, d)
+    # head 0 of sequence 0: the chunk [96, 128) holds the bad value
+    assert_parity_blocks(o[:96, 0], o_r[:96, 0], "bf16", 32, "o seq 0 head 0 before the bad chunk")
+    assert_parity(page[0, 0], ck_r[0][64][0], "bf16", "ckpt 64 head 0")
+    for j in (1, 2, 3, 4):
+        assert bool((page[j, 0] == sentinel).all()), f"checkpoint slot {j} head 0 written"
+    assert bool((sf[0, 0] == sentinel).all())
+    # head 1 of sequence 0, and sequence 1
+    assert_parity_blocks(o[:1700, 1], o_r[:1700, 1], "bf16", 32, "o seq 0 head 1")
+    assert_parity(sf[0, 1], sf_r[0, 1], "bf16", "s_final seq 0 head 1")
+    for j, p in enumerate(ck[0]):
+        assert_parity(page[j, 1], ck_r[0][p][1], "bf16", f"ckpt {p} head 1")
+    for h in range(H):
+        assert_parity_blocks(o[1700:, h], o_r[1700:, h], "bf16", 32, f"o seq 1 head {h}")
+        assert_parity(sf[1, h], sf_r[1, h], "bf16", f"s_final seq 1 head {h}")
+        for j, p in enumerate(ck[1]):
+            assert_parity(page[slots[1][j], h], ck_r[1][p][h], "bf16", f"ckpt {p} seq 1 head {h}")
