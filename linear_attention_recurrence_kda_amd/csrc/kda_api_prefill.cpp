@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <functional>
 #include <numeric>
 #include <string>
 #include <unordered_set>
@@ -131,7 +132,7 @@ bool fused_path(kda_dtype in_dtype, int32_t dk, int32_t chunk) {
 // segment's chain is shorter, for the identity chains' work and the
 // correction's traffic.
 constexpr int kMaxExtraSegs = 8;          // later segments per call (bounds the workspace)
-constexpr int32_t kTailTokens = 960;      // tokens per tail item of the correction
+constexpr int32_t kTailTokens = 1536;     // tokens per tail item of the correction (8 blocks of 192)
 constexpr int kMinSegChunks = 16;         // chunks per segment, at least
 constexpr double kFixBytesPerUs = 5.0e6;  // the correction's streaming rate, bytes per us
 constexpr double kFixLaunchUs = 6.0;      // per extra launch
@@ -678,8 +679,41 @@ FusedList fused_list(const Plan& pl, const int32_t* cu, const int32_t* ck_cu, co
         wgs.push_back(static_cast<int32_t>((ch << 8) | (code << 4) | (code == 15 ? 0 : r)));
       }
   }
-  // Tail items last: each starts only after every chain has started.
-  for (size_t t = 0; t < titems.size() / 10; ++t) wgs.push_back(static_cast<int32_t>((t << 8) | (5 << 4)));
+  // Tail items: in the list after every chain they wait for (workgroups
+  // start in list order, so those have started when an item starts and its
+  // wait ends), at the point where, by the per-chunk times and list
+  // scheduling on the CUs, those chains are predicted to have ended: the
+  // items then take the CUs that the split sequence's chains leave, while
+  // the short chains after them fill the launch's end.
+  const size_t n_items = titems.size() / 10;
+  if (n_items > 0) {
+    auto wg_entry = [&](int32_t x) { return (x >> 4 & 15) == 15 ? -1 : chains[2 * (x >> 8)]; };
+    auto wg_time = [&](int32_t x) { const int32_t i = wg_entry(x); return i < 0 ? 0.0 : ctime(i); };
+    std::vector<double> cu_free(kCUs, 0.0);  // a min-heap of the CUs' free times
+    double ready = 0;
+    size_t last_dep = 0;
+    for (size_t k = 0; k < wgs.size(); ++k) {
+      const int32_t i = wg_entry(wgs[k]);
+      if (i >= 0 && pl.nseg[ent[i].seq] == 2) {
+        ready = std::max(ready, wg_time(wgs[k]));  // (these start at once: the longest chains come first)
+        last_dep = k + 1;
+      }
+    }
+    size_t at = wgs.size();
+    for (size_t k = 0; k < wgs.size(); ++k) {
+      std::pop_heap(cu_free.begin(), cu_free.end(), std::greater<double>());
+      const double start = cu_free.back();
+      if (k >= last_dep && start >= ready) {
+        at = k;
+        break;
+      }
+      cu_free.back() = start + wg_time(wgs[k]);
+      std::push_heap(cu_free.begin(), cu_free.end(), std::greater<double>());
+    }
+    std::vector<int32_t> items;
+    for (size_t t = 0; t < n_items; ++t) items.push_back(static_cast<int32_t>((t << 8) | (5 << 4)));
+    wgs.insert(wgs.begin() + static_cast<std::ptrdiff_t>(at), items.begin(), items.end());
+  }
   f.n_wg = static_cast<int64_t>(wgs.size());
   f.n_owg = static_cast<int64_t>(owgs.size() / 3);
   f.n_cks = static_cast<int64_t>(cks.size() / 6);

@@ -25,7 +25,7 @@ __global__ __launch_bounds__(kFixThreads) void fix_kernel(FixArgs p) {
     const int item = b - p.n_owg, rb = item % (kFixD / kFixCkRows);
     const int h = (item / (kFixD / kFixCkRows)) % p.H, ck = item / (kFixD / kFixCkRows) / p.H;
     if (stopped(ld_const(p.cks, 6 * ck + 5), h)) return;
-    fix_state_item(v, ld_const(p.cks, 6 * ck), ld_const(p.cks, 6 * ck + 1), ld_const(p.cks, 6 * ck + 2),
+    fix_state_item<kFixThreads / 64>(v, ld_const(p.cks, 6 * ck), ld_const(p.cks, 6 * ck + 1), ld_const(p.cks, 6 * ck + 2),
                    ld_const(p.cks, 6 * ck + 3), ld_const(p.cks, 6 * ck + 4) != 0, h, rb, lds);
   }
 }

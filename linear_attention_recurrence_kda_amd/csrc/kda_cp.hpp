@@ -39,6 +39,7 @@ constexpr int kStPitch = kFixD + 8;  // bf16 per row of S_in^T in LDS (16 bytes 
 // pitches that put the lanes of an MFMA operand read on distinct banks.
 constexpr int kXPitch = kFixD + 4, kSPitch = kFixD + 16;
 constexpr int kFixLds = 36864;  // bytes of LDS either role needs
+constexpr int kFixDepth = 4;     // row blocks in flight per wave
 static_assert(kFixD * kStPitch * 2 <= kFixLds, "S_in^T fits the LDS block");
 static_assert((kXPitch + kSPitch) * kFixCkRows * 4 <= kFixLds, "state tiles fit the LDS block");
 
@@ -62,8 +63,8 @@ __device__ __forceinline__ int fix_col(int p, int j, int r) { return 32 * p + 8 
 // NW waves of the workgroup, in blocks of 16 NW tokens: wave w takes tokens
 // 16w .. 16w + 15 of a block and every column.  S_in^T waits in LDS as bf16
 // (rows = output columns, 16-byte fragment reads, read again for every block
-// so that few registers stay live); the next two blocks' qhat and o are in
-// flight while a block is multiplied and stored.
+// so that few registers stay live); kFixDepth blocks' qhat and o are in
+// flight per wave.
 template <int NW>
 __device__ __forceinline__ void fix_rows(const FixView& p, int lo, int len, int qrow, int si, int h, int t0, int t1,
                                          char* lds) {
@@ -94,9 +95,9 @@ __device__ __forceinline__ void fix_rows(const FixView& p, int lo, int len, int 
     for (int pp = 0; pp < 4; ++pp)
       b.o[pp] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, row + (32 * pp + 8 * g) * 2, 0, 0));
   };
-  Blk b0, b1, b2;
-  load(t0, b0);
-  load(t0 + NB, b1);
+  Blk buf[kFixDepth];
+#pragma unroll
+  for (int j = 0; j < kFixDepth; ++j) load(t0 + j * NB, buf[j]);
   for (int e = tid; e < kFixD * kFixD / 4; e += 64 * NW) {
     const int k = e / (kFixD / 4), n4 = 4 * (e % (kFixD / 4));
     const float4 x = *reinterpret_cast<const float4*>(&S[k * kFixD + n4]);
@@ -106,36 +107,42 @@ __device__ __forceinline__ void fix_rows(const FixView& p, int lo, int len, int 
     st[(n4 + 3) * kStPitch + k] = static_cast<__bf16>(x.w);
   }
   __syncthreads();
-  for (int r0 = t0; r0 < end; r0 += NB) {
-    load(r0 + 2 * NB, b2);
-    asm volatile("" ::: "memory");  // (S_in^T is read from LDS per block, not held in registers)
-    const __amdgpu_buffer_rsrc_t ro = rsrc(p.o, lo, r0);
+  // Groups of kFixDepth blocks, unrolled so that every buffer is a fixed set
+  // of registers: block r0 + j NB comes from buf[j], which then takes block
+  // r0 + (j + kFixDepth) NB (operations past the range have empty ranges, so
+  // there is no branch and the waits count exactly what they need).
+  for (int r0 = t0; r0 < end; r0 += kFixDepth * NB) {
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
-      const bf16x8 o8 = __builtin_bit_cast(bf16x8, b0.o[pp]);
-      f32x4 acc[2];
+    for (int j = 0; j < kFixDepth; ++j) {
+      const int rb = r0 + j * NB;
+      asm volatile("" ::: "memory");  // (S_in^T is read from LDS per block, not held in registers)
+      const __amdgpu_buffer_rsrc_t ro = rsrc(p.o, lo, rb);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int pp = 0; pp < 4; ++pp) {
+        const bf16x8 o8 = __builtin_bit_cast(bf16x8, buf[j].o[pp]);
+        f32x4 acc[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[j][i] = static_cast<float>(o8[4 * j + i]);
+        for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 qb = __builtin_bit_cast(bf16x8, b0.q[ks]);
+          for (int i = 0; i < 4; ++i) acc[jj][i] = static_cast<float>(o8[4 * jj + i]);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const bf16x8 sa = *reinterpret_cast<const bf16x8*>(&st[fix_col(pp, j, l16) * kStPitch + 32 * ks + 8 * g]);
-          acc[j] = mma(sa, qb, acc[j]);
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x8 qb = __builtin_bit_cast(bf16x8, buf[j].q[ks]);
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const bf16x8 sa = *reinterpret_cast<const bf16x8*>(&st[fix_col(pp, jj, l16) * kStPitch + 32 * ks + 8 * g]);
+            acc[jj] = mma(sa, qb, acc[jj]);
+          }
         }
+        bf16x8 r8;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) r8[4 * jj + i] = static_cast<__bf16>(acc[jj][i]);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, r8), ro, row + (32 * pp + 8 * g) * 2, 0, 0);
       }
-      bf16x8 r8;
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) r8[4 * j + i] = static_cast<__bf16>(acc[j][i]);
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, r8), ro, row + (32 * pp + 8 * g) * 2, 0, 0);
+      load(rb + kFixDepth * NB, buf[j]);
     }
-    b0 = b1;
-    b1 = b2;
   }
 }
 
@@ -200,16 +207,64 @@ __device__ __forceinline__ void fix_state(float* dst, const float* X, const floa
   }
 }
 
+// A whole head's state dst = X S_in + B at once, for a workgroup with at
+// least 8 waves and kFullLds bytes of LDS: all of X (pitch 132) and S_in
+// (pitch 144) are loaded into LDS together (one memory round trip), then
+// wave w < 8 forms rows 16w .. 16w + 15, all 128 columns (eight 16x16
+// tiles), in fp32 MFMA (16x16x4).
+constexpr int kFullLds = kFixD * (kXPitch + kSPitch) * 4;
+template <int NW>
+__device__ __forceinline__ void fix_state_full(float* dst, const float* X, const float* B, const float* S, char* lds) {
+  static_assert(NW >= 8, "eight waves form the sixteen-row tiles");
+  float* xs = reinterpret_cast<float*>(lds);
+  float* ss = xs + kFixD * kXPitch;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, g = lane >> 4;
+  __syncthreads();  // (the LDS block is free)
+  for (int e = tid; e < kFixD * kFixD / 4; e += 64 * NW) {
+    const int r = e / (kFixD / 4), c4 = 4 * (e % (kFixD / 4));
+    const float4 x = *reinterpret_cast<const float4*>(&X[4 * e]);
+    const float4 y = *reinterpret_cast<const float4*>(&S[4 * e]);
+    float* dx = &xs[r * kXPitch + c4];
+    float* dy = &ss[r * kSPitch + c4];
+    dx[0] = x.x; dx[1] = x.y; dx[2] = x.z; dx[3] = x.w;
+    dy[0] = y.x; dy[1] = y.y; dy[2] = y.z; dy[3] = y.w;
+  }
+  __syncthreads();
+  if (wave >= 8) return;
+  // D tile ct: rows 16 wave + 4g + i, column 16 ct + l16.
+  f32x4 acc[8];
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[ct][i] = B[(16 * wave + 4 * g + i) * kFixD + 16 * ct + l16];
+  for (int ks = 0; ks < kFixD / 4; ++ks) {
+    const int k = 4 * ks + g;
+    const float a = xs[(16 * wave + l16) * kXPitch + k];
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+      acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, ss[k * kSPitch + 16 * ct + l16], acc[ct], 0, 0, 0);
+  }
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[(16 * wave + 4 * g + i) * kFixD + 16 * ct + l16] = acc[ct][i];
+}
+
 // A state item (dsti: page slot, or -1 - n for the final state of sequence
 // n; B and X from tstate when in_t, else xpool; S_in = tstate state si):
-// row block rb of head h, and (h = rb = 0) the page's zero padding.
+// row block rb of head h, and (h = 0, rb <= 0) the page's zero padding.
+// rb < 0: every row, by fix_state_full (NW >= 8 waves, kFullLds of LDS).
+template <int NW>
 __device__ __forceinline__ void fix_state_item(const FixView& p, int64_t dsti, int bi, int xi, int si, bool in_t,
                                                int h, int rb, char* lds) {
   const int64_t hkv = static_cast<int64_t>(p.H) * kFixD * kFixD, hoff = static_cast<int64_t>(h) * kFixD * kFixD;
   const float* pool = in_t ? p.tstate : p.xpool;
   float* dst = (dsti >= 0 ? p.page_pool + dsti * p.page_elems : p.s_final + (-1 - dsti) * hkv) + hoff;
-  fix_state(dst, pool + xi * hkv + hoff, pool + bi * hkv + hoff, p.tstate + si * hkv + hoff, rb, lds);
-  if (dsti >= 0 && h == 0 && rb == 0)
+  if constexpr (NW >= 8) {
+    if (rb < 0) fix_state_full<NW>(dst, pool + xi * hkv + hoff, pool + bi * hkv + hoff, p.tstate + si * hkv + hoff, lds);
+  }
+  if (rb >= 0) fix_state(dst, pool + xi * hkv + hoff, pool + bi * hkv + hoff, p.tstate + si * hkv + hoff, rb, lds);
+  if (dsti >= 0 && h == 0 && rb <= 0)
     for (int64_t e = hkv + threadIdx.x; e < p.page_elems; e += blockDim.x) (p.page_pool + dsti * p.page_elems)[e] = 0.f;
 }
 

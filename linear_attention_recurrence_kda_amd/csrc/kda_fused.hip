@@ -929,11 +929,11 @@ __device__ __forceinline__ void fused_tail(const FusedParams& p, int item, Fused
   __syncthreads();
   if (!sm.stop[0]) return;
   const FixView v{p.o, p.qhat, p.tstate, p.xpool, p.page_pool, p.s_final, p.page_elems, p.H};
-  char* lds = reinterpret_cast<char*>(&sm);  // (kFixLds bytes from its start, clear of stop[])
+  char* lds = reinterpret_cast<char*>(&sm);  // (up to kFullLds bytes from its start, clear of stop[])
   if (f(0) == 0) {
     fix_rows<Fused<DK>::NT / 64>(v, f(1), f(2), f(3), f(4), f(5), f(6), f(7), lds);
   } else {
-    for (int rb = 0; rb < kFixD / kFixCkRows; ++rb) fix_state_item(v, f(1), f(2), f(3), f(4), f(5) != 0, f(6), rb, lds);
+    fix_state_item<Fused<DK>::NT / 64>(v, f(1), f(2), f(3), f(4), f(5) != 0, f(6), -1, lds);
   }
 }
 
@@ -943,7 +943,8 @@ __device__ __forceinline__ void fused_tail(const FusedParams& p, int item, Fused
 template <int DK>
 __global__ __launch_bounds__(Fused<DK>::NT, 1) void fused_kernel(FusedParams p) {
   __shared__ __attribute__((aligned(16))) FusedSmem<DK> sm;
-  static_assert(offsetof(FusedSmem<DK>, stop) >= kFixLds, "the tail's LDS block lies clear of stop[]");
+  static_assert(offsetof(FusedSmem<DK>, stop) >= kFixLds && offsetof(FusedSmem<DK>, stop) >= kFullLds,
+                "the tail's LDS block lies clear of stop[]");
   const int e = ld_const(p.wgs, blockIdx.x);
   const int chain = e >> 8, code = (e >> 4) & 15, tile = e & 15;
   if (code == 5) {
