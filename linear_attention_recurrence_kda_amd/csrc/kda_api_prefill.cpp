@@ -134,8 +134,9 @@ bool fused_path(kda_dtype in_dtype, int32_t dk, int32_t chunk) {
 constexpr int kMaxExtraSegs = 8;          // later segments per call (bounds the workspace)
 constexpr int32_t kTailTokens = 1536;     // tokens per tail item of the correction (8 blocks of 192)
 constexpr int kMinSegChunks = 16;         // chunks per segment, at least
-constexpr double kFixBytesPerUs = 5.0e6;  // the correction's streaming rate, bytes per us
-constexpr double kFixLaunchUs = 6.0;      // per extra launch
+constexpr double kFixBytesPerUs = 3.5e6;     // the correction launch's streaming rate, bytes per us
+constexpr double kFixLaunchUs = 6.0;         // per extra launch
+constexpr double kTailBytesPerUs = 5.0e6;    // the tail items' cost, bytes per us of the call
 
 // One chain set of the fused launch: a whole sequence, or a segment.
 struct Entry {
@@ -366,19 +367,27 @@ int make_plan(kda_dtype in_dtype, int32_t H, int32_t dk, int32_t dv, int32_t chu
     };
     // Widths of the entries (identity chains: 128 columns) and the predicted
     // time, the correction included.
-    auto assign = [&](std::vector<Entry>& ent) {
+    // (the correction: in two segments, the launch's tail items, which lengthen
+    // the call by about their bytes at kTailBytesPerUs; in more, a launch of its
+    // own after the composition)
+    auto assign = [&](std::vector<Entry>& ent, const std::vector<int>& ns) {
       std::vector<int64_t> ch;
-      double fixed_work = 0, fixed_longest = 0, fix_bytes = 0;
+      double fixed_work = 0, fixed_longest = 0, fix_bytes = 0, tail = 0;
       int n_split = 0;
       for (const Entry& e : ent) {
         if (e.kind == 2) {
           fixed_work += static_cast<double>(H) * kFusedT[0] * static_cast<double>(e.chunks);
           fixed_longest = std::max(fixed_longest, kFusedT[0] * static_cast<double>(e.chunks));
-          fix_bytes += static_cast<double>(e.hi - e.lo) * H * (2.0 * dk + 4.0 * dv);
+          const double bytes = static_cast<double>(e.hi - e.lo) * H * (2.0 * dk + 4.0 * dv);
+          if (ns[e.seq] == 2) {
+            tail += bytes / kTailBytesPerUs;
+          } else {
+            fix_bytes += bytes;
+            if (e.seg == 1) ++n_split;
+          }
         } else {
           ch.push_back(e.chunks);
         }
-        if (e.kind == 1 && e.seg == 1) ++n_split;
       }
       std::vector<int> w;
       double t;
@@ -399,7 +408,7 @@ int make_plan(kda_dtype in_dtype, int32_t H, int32_t dk, int32_t dv, int32_t chu
       size_t j = 0;
       for (Entry& e : ent) e.width = e.kind == 2 ? 128 : w[j++];
       if (n_split > 0) t += fix_bytes / kFixBytesPerUs + kFixLaunchUs * (n_split + 1);
-      return t;
+      return t + tail;
     };
     pl.nseg.assign(n_seqs, 1);
     const bool cp_ok = allow_cp && dv == dk && dv == 128 && n_seqs > 0;
@@ -415,7 +424,7 @@ int make_plan(kda_dtype in_dtype, int32_t H, int32_t dk, int32_t dv, int32_t chu
       // Greedy: give the sequence with the longest segments one more segment
       // while the model predicts at least 2 % less time.
       std::vector<Entry> ent = entries(pl.nseg);
-      double best = assign(ent);
+      double best = assign(ent, pl.nseg);
       for (int extra = 0; extra < kMaxExtraSegs; ++extra) {
         int32_t top = -1;
         for (int32_t i = 0; i < n_seqs; ++i)
@@ -425,7 +434,7 @@ int make_plan(kda_dtype in_dtype, int32_t H, int32_t dk, int32_t dv, int32_t chu
         if (top < 0) break;
         ++pl.nseg[top];
         ent = entries(pl.nseg);
-        const double t = assign(ent);
+        const double t = assign(ent, pl.nseg);
         if (t < 0.98 * best) {
           best = t;
         } else {
@@ -435,7 +444,7 @@ int make_plan(kda_dtype in_dtype, int32_t H, int32_t dk, int32_t dv, int32_t chu
       }
     }
     pl.ent = entries(pl.nseg);
-    assign(pl.ent);
+    assign(pl.ent, pl.nseg);
     pl.cp = std::any_of(pl.nseg.begin(), pl.nseg.end(), [](int n) { return n > 1; });
     pl.width.assign(n_seqs, 0);
     for (const Entry& e : pl.ent)
@@ -510,14 +519,16 @@ std::string plan_kernels(const Plan& pl, kda_dtype in_dtype, int32_t dk, int32_t
              dk, pl.width.empty() ? 0 : lo, hi);
     if (pl.cp) {
       int n_split = 0, n_seg = 0;
+      bool more = false;
       for (int n : pl.nseg)
         if (n > 1) {
           ++n_split;
           n_seg += n;
+          more = more || n > 2;
         }
       const size_t len = strlen(buf);
-      snprintf(buf + len, sizeof(buf) - len, " + compose_kernel + fix_kernel (%d sequence%s in %d segments)", n_split,
-               n_split == 1 ? "" : "s", n_seg);
+      snprintf(buf + len, sizeof(buf) - len, "%s; %d sequence%s in %d segments", more ? " + compose_kernel + fix_kernel" : "",
+               n_split, n_split == 1 ? "" : "s", n_seg);
     }
   } else if (pl.mixed)
     snprintf(buf, sizeof(buf), "%s + slab_mixed_kernel<%d> (a tile width per sequence)", local.c_str(), dk);
