@@ -217,7 +217,7 @@ int kda_compose_segments(const float* A, const float* B, int32_t n_seg, int32_t 
   const std::vector<Range> outs = {{s_starts, n * sb, "s_starts"}, {s_end, s_end ? sb : 0, "s_end"}};
   const int st = check_disjoint(outs, ins);
   if (st) return st;
-  kda::ComposeArgs p{A, B, s_in, s_starts, s_end, n_seg, H, dk, dv, nullptr, static_cast<hipStream_t>(stream)};
+  kda::ComposeArgs p{A, B, s_in, s_starts, s_end, n_seg, H, dk, dv, static_cast<hipStream_t>(stream)};
   return hip_status(kda::launch_compose(p), "compose launch");
 }
 

@@ -125,18 +125,20 @@ bool fused_path(kda_dtype in_dtype, int32_t dk, int32_t chunk) {
 // fixed-size map of its start state and compose the maps).  A split
 // sequence's first segment runs from s0 as usual; each later segment runs
 // twice beside it, from the zero state (kind 1) and from the identity with v
-// taken as zero (kind 2: its linear part, one 128-column tile); then
-// compose_kernel turns the maps into the segments' start states and
-// fix_kernel (kda_cp.hip) corrects the later segments' outputs and
-// checkpoints.  It pays where the longest chain bounds the call: each
-// segment's chain is shorter, for the identity chains' work and the
+// taken as zero (kind 2: its linear part, one 128-column tile); workgroups at
+// the launch's tail then chain the maps into the segments' start states and
+// correct the later segments' outputs and checkpoints (kda_fused.hip,
+// fused_tail; kda_cp.hpp).  It pays where the longest chain bounds the call:
+// each segment's chain is shorter, for the identity chains' work and the
 // correction's traffic.
 constexpr int kMaxExtraSegs = 8;          // later segments per call (bounds the workspace)
-constexpr int32_t kTailTokens = 1536;     // tokens per tail item of the correction (8 blocks of 192)
+constexpr int32_t kTailBlock = 192;       // rows of a tail item's block (16 per wave of the fused kernel)
+constexpr int32_t kTailTokens = 1536;     // rows per tail item of the correction, at most (8 blocks)
 constexpr int kMinSegChunks = 16;         // chunks per segment, at least
-constexpr double kFixBytesPerUs = 3.5e6;     // the correction launch's streaming rate, bytes per us
-constexpr double kFixLaunchUs = 6.0;         // per extra launch
 constexpr double kTailBytesPerUs = 5.0e6;    // the tail items' cost, bytes per us of the call
+constexpr double kTailStateUs = 20.0;        // a tail item forming a start state (they run in turn)
+constexpr double kChainUs = 15.0;            // a chain's fixed cost (its prologue), us
+constexpr int64_t kMaxSimWgs = 200000;       // workgroups the plan's list scheduling models at most
 
 // One chain set of the fused launch: a whole sequence, or a segment.
 struct Entry {
@@ -367,24 +369,17 @@ int make_plan(kda_dtype in_dtype, int32_t H, int32_t dk, int32_t dv, int32_t chu
     };
     // Widths of the entries (identity chains: 128 columns) and the predicted
     // time, the correction included.
-    // (the correction: in two segments, the launch's tail items, which lengthen
-    // the call by about their bytes at kTailBytesPerUs; in more, a launch of its
-    // own after the composition)
+    // (the correction, the launch's tail items, lengthens the call by about
+    // their bytes at kTailBytesPerUs, and by the start states formed in turn)
     auto assign = [&](std::vector<Entry>& ent, const std::vector<int>& ns) {
       std::vector<int64_t> ch;
-      double fixed_work = 0, fixed_longest = 0, fix_bytes = 0, tail = 0;
-      int n_split = 0;
+      double fixed_work = 0, fixed_longest = 0, tail = 0, chain_states = 0;
       for (const Entry& e : ent) {
         if (e.kind == 2) {
           fixed_work += static_cast<double>(H) * kFusedT[0] * static_cast<double>(e.chunks);
           fixed_longest = std::max(fixed_longest, kFusedT[0] * static_cast<double>(e.chunks));
-          const double bytes = static_cast<double>(e.hi - e.lo) * H * (2.0 * dk + 4.0 * dv);
-          if (ns[e.seq] == 2) {
-            tail += bytes / kTailBytesPerUs;
-          } else {
-            fix_bytes += bytes;
-            if (e.seg == 1) ++n_split;
-          }
+          tail += static_cast<double>(e.hi - e.lo) * H * (2.0 * dk + 4.0 * dv) / kTailBytesPerUs;
+          chain_states = std::max(chain_states, kTailStateUs * (ns[e.seq] - 2));
         } else {
           ch.push_back(e.chunks);
         }
@@ -407,8 +402,32 @@ int make_plan(kda_dtype in_dtype, int32_t H, int32_t dk, int32_t dv, int32_t chu
       }
       size_t j = 0;
       for (Entry& e : ent) e.width = e.kind == 2 ? 128 : w[j++];
-      if (n_split > 0) t += fix_bytes / kFixBytesPerUs + kFixLaunchUs * (n_split + 1);
-      return t + tail;
+      // The chains' workgroups, longest first, list-scheduled on the CUs: a
+      // few hundred equal chains fill the CUs in whole rounds, which the
+      // work over the CUs does not show.
+      std::vector<double> d;
+      for (const Entry& e : ent) {
+        const int k = e.width == 128 ? 0 : e.width == 64 ? 1 : e.width == 32 ? 2 : 3;
+        const int tiles = e.kind == 2 ? 1 : dv / e.width;
+        if (static_cast<int64_t>(d.size()) + static_cast<int64_t>(tiles) * H > kMaxSimWgs) {
+          d.clear();
+          break;
+        }
+        d.insert(d.end(), static_cast<size_t>(tiles) * H, kFusedT[k] * static_cast<double>(e.chunks) + kChainUs);
+      }
+      if (!d.empty()) {
+        std::sort(d.begin(), d.end(), std::greater<double>());
+        std::vector<double> cus(kCUs, 0.0);
+        double span = 0;
+        for (double x : d) {
+          std::pop_heap(cus.begin(), cus.end(), std::greater<double>());
+          cus.back() += x;
+          span = std::max(span, cus.back());
+          std::push_heap(cus.begin(), cus.end(), std::greater<double>());
+        }
+        t = std::max(t, span);
+      }
+      return t + tail + chain_states;
     };
     pl.nseg.assign(n_seqs, 1);
     const bool cp_ok = allow_cp && dv == dk && dv == 128 && n_seqs > 0;
@@ -519,16 +538,14 @@ std::string plan_kernels(const Plan& pl, kda_dtype in_dtype, int32_t dk, int32_t
              dk, pl.width.empty() ? 0 : lo, hi);
     if (pl.cp) {
       int n_split = 0, n_seg = 0;
-      bool more = false;
       for (int n : pl.nseg)
         if (n > 1) {
           ++n_split;
           n_seg += n;
-          more = more || n > 2;
         }
       const size_t len = strlen(buf);
-      snprintf(buf + len, sizeof(buf) - len, "%s; %d sequence%s in %d segments", more ? " + compose_kernel + fix_kernel" : "",
-               n_split, n_split == 1 ? "" : "s", n_seg);
+      snprintf(buf + len, sizeof(buf) - len, "; %d sequence%s in %d segments", n_split, n_split == 1 ? "" : "s",
+               n_seg);
     }
   } else if (pl.mixed)
     snprintf(buf, sizeof(buf), "%s + slab_mixed_kernel<%d> (a tile width per sequence)", local.c_str(), dk);
@@ -544,16 +561,9 @@ std::string plan_kernels(const Plan& pl, kda_dtype in_dtype, int32_t dk, int32_t
 // int32) and the buffers that split sequences need behind it.
 struct FusedList {
   std::vector<int32_t> w;
-  size_t chains = 0, seqinfo = 0, segx = 0, ck_pos = 0, ck_slot = 0, wgs = 0, segs = 0, owgs = 0, cks = 0;
-  size_t titems = 0, tcnt = 0;
-  int64_t n_chains = 0, n_wg = 0, n_owg = 0, n_cks = 0, n_cnt = 0;
+  size_t chains = 0, seqinfo = 0, segx = 0, ck_pos = 0, ck_slot = 0, wgs = 0, titems = 0, tcnt = 0;
+  int64_t n_chains = 0, n_wg = 0, n_cnt = 0;
   int64_t n_tstate = 0, n_xpool = 0, n_qrows = 0;  // states of H*dk*dv fp32; qhat rows of H*dk bf16
-  struct Comp {
-    int32_t seq, n;  // a sequence in n > 2 segments (two: the correction composes them)
-    int64_t base;    // its first tstate state: E1, then A, B and the start states of segments 1..n-1
-    int32_t cnt;     // its first counter
-  };
-  std::vector<Comp> comp;
   size_t list_bytes() const { return align256(w.size() * 4); }
 };
 
@@ -563,25 +573,35 @@ FusedList fused_list(const Plan& pl, const int32_t* cu, const int32_t* ck_cu, co
   FusedList f;
   const std::vector<Entry>& ent = pl.ent;
   const int64_t n_ent = static_cast<int64_t>(ent.size());
-  // Per split sequence: its tstate block, and a completion counter per head
-  // (its first in cbase), counted by the sequence's chains (0x10000 for one
-  // stopped at a decay out of range).  In two segments the tail items wait
-  // for the count (cwant); in more, the composition and the correction
-  // launches read it when all is done.
+  // Per split sequence in n segments: its tstate block (E1, the end state of
+  // segment 0; A_j, B_j of segments 1..n-1; the start states S_j of segments
+  // 2..n-1), and per segment j >= 1 and head a completion counter (cbase +
+  // (j - 1) H + head): raised by the chains of segment j (from zero and from
+  // the identity) and by what forms its start state (segment 0's chain for
+  // j = 1, the tail item S_j = A_{j-1} S_{j-1} + B_{j-1} after), 0x10000 for
+  // one that stopped at a decay out of range; cwant[s][j] counts them.
   std::vector<int64_t> tbase(pl.nseg.size(), -1);
-  std::vector<int32_t> cbase(pl.nseg.size(), -1), cwant(pl.nseg.size(), 0);
+  std::vector<int32_t> cbase(pl.nseg.size(), -1);
+  std::vector<std::vector<int32_t>> cwant(pl.nseg.size());
   for (size_t s = 0; s < pl.nseg.size(); ++s)
     if (pl.nseg[s] > 1) {
       tbase[s] = f.n_tstate;
       cbase[s] = static_cast<int32_t>(f.n_cnt);
-      if (pl.nseg[s] > 2) f.comp.push_back({static_cast<int32_t>(s), pl.nseg[s], f.n_tstate, cbase[s]});
       f.n_tstate += 3 * pl.nseg[s] - 2;
-      f.n_cnt += H;
+      f.n_cnt += static_cast<int64_t>(pl.nseg[s] - 1) * H;
+      cwant[s].assign(pl.nseg[s], 0);
+      for (int j = 2; j < pl.nseg[s]; ++j) cwant[s][j] = 1;  // the tail item forming S_j
     }
+  auto seg_of = [](const Entry& e) { return e.kind == 0 ? 1 : e.seg; };  // (the counter a chain raises)
   for (const Entry& e : ent)
-    if (pl.nseg[e.seq] == 2) cwant[e.seq] += e.kind == 2 ? 1 : dv / e.width;
-  std::vector<int32_t> seqinfo(6 * n_ent), segx(pl.cp ? kda::kSegxInts * n_ent : 0), pos, slot, segs, owgs, cks;
-  std::vector<int32_t> titems;
+    if (pl.nseg[e.seq] > 1) cwant[e.seq][seg_of(e)] += e.kind == 2 ? 1 : dv / e.width;
+  // The later segments of split sequences, as the tail items need them.
+  struct Later {
+    int32_t seq, j, lo, len, qrow, ck0, ck1;
+    int64_t xp;  // xpool index of its first checkpoint's B (X at + 1)
+  };
+  std::vector<Later> later;
+  std::vector<int32_t> seqinfo(6 * n_ent), segx(pl.cp ? kda::kSegxInts * n_ent : 0), pos, slot;
   int64_t nc = 0;
   for (int64_t i = 0; i < n_ent; ++i) {
     const Entry& e = ent[i];
@@ -604,7 +624,7 @@ FusedList fused_list(const Plan& pl, const int32_t* cu, const int32_t* ck_cu, co
     if (!pl.cp) continue;
     int32_t* sx = &segx[kda::kSegxInts * i];
     const int64_t b = tbase[sq];
-    sx[4] = cbase[sq];
+    sx[4] = n > 1 ? cbase[sq] + (seg_of(e) - 1) * H : -1;
     if (n == 1) {
       sx[0] = sx[1] = sq;
     } else if (e.kind == 0) {  // the first segment: from s0, its end state is E1
@@ -615,35 +635,54 @@ FusedList fused_list(const Plan& pl, const int32_t* cu, const int32_t* ck_cu, co
       sx[1] = static_cast<int32_t>(b + (n - 1) + e.seg);
       sx[2] = kda::kSegZeroStart | kda::kSegFinalTemp | kda::kSegCkTemp;
     } else {  // from the identity: A of segment e.seg, outputs to qhat
-      // (in two segments the second starts at E1 itself)
-      const int32_t len = e.hi - e.lo, start = static_cast<int32_t>(n == 2 ? b : b + 2 * (n - 1) + e.seg);
-      const int32_t qrow = static_cast<int32_t>(f.n_qrows);
       sx[1] = static_cast<int32_t>(b + e.seg);
-      sx[3] = qrow;
-      auto xp = [&](int32_t c, int x) { return static_cast<int32_t>(f.n_xpool + 2 * (c - e.ck0) + x); };
-      if (n == 2) {  // corrected by tail items of the fused launch
-        for (int32_t h = 0; h < H; ++h) {
-          const int32_t cnt = cbase[sq] + h, want = cwant[sq];
-          for (int32_t t0 = 0; t0 < len; t0 += kTailTokens)
-            titems.insert(titems.end(), {0, cu[sq] + e.lo, len, qrow, start, h, t0, std::min(len, t0 + kTailTokens),
-                                         cnt, want});
-          for (int32_t c = e.ck0; c < e.ck1; ++c)
-            titems.insert(titems.end(), {1, ck_slot ? ck_slot[cb + c] : 0, xp(c, 0), xp(c, 1), start, 0, h, 0, cnt,
-                                         want});
-          if (want_final)  // the final state A E1 + B
-            titems.insert(titems.end(), {1, -1 - sq, static_cast<int32_t>(b + 2), static_cast<int32_t>(b + 1),
-                                         static_cast<int32_t>(b), 1, h, 0, cnt, want});
-        }
-      } else {  // corrected by fix_kernel after compose_kernel
-        const int32_t sg = static_cast<int32_t>(segs.size() / 5);
-        segs.insert(segs.end(), {cu[sq] + e.lo, len, qrow, start, cbase[sq]});
-        for (int32_t h = 0; h < H; ++h)
-          for (int32_t t0 = 0; t0 < len; t0 += kda::kFixTokens) owgs.insert(owgs.end(), {sg, h, t0});
-        for (int32_t c = e.ck0; c < e.ck1; ++c)
-          cks.insert(cks.end(), {ck_slot ? ck_slot[cb + c] : 0, xp(c, 0), xp(c, 1), start, 0, cbase[sq]});
-      }
+      sx[3] = static_cast<int32_t>(f.n_qrows);
+      later.push_back({sq, e.seg, cu[sq] + e.lo, e.hi - e.lo, static_cast<int32_t>(f.n_qrows), e.ck0, e.ck1, f.n_xpool});
       f.n_xpool += 2 * (e.ck1 - e.ck0);
-      f.n_qrows += len;
+      f.n_qrows += e.hi - e.lo;
+    }
+  }
+  // Tail items (kTailInts each; see fused_tail): the start states S_j (j >= 2)
+  // first, in order, then per segment and head its output rows, checkpoints
+  // and (last segment) the sequence's final state.  An item waits for the
+  // counter of its segment; an item forming S_j raises S_j's counter.
+  std::vector<int32_t> titems;
+  auto tstart = [&](const Later& g) {  // tstate index of the segment's start state
+    const int64_t b = tbase[g.seq];
+    return static_cast<int32_t>(g.j == 1 ? b : b + 2 * (pl.nseg[g.seq] - 1) + g.j);
+  };
+  auto cnt_of = [&](int32_t sq, int j, int32_t h) { return cbase[sq] + (j - 1) * H + h; };
+  for (const Later& g : later) {
+    const int32_t n = pl.nseg[g.seq];
+    if (g.j + 1 >= n) continue;
+    const int64_t b = tbase[g.seq];
+    Later nx = g;
+    nx.j = g.j + 1;
+    for (int32_t h = 0; h < H; ++h)  // S_{j+1} = A_j S_j + B_j
+      titems.insert(titems.end(), {1, 2, tstart(nx), static_cast<int32_t>(b + (n - 1) + g.j),
+                                   static_cast<int32_t>(b + g.j), tstart(g), 1, h, cnt_of(g.seq, g.j, h),
+                                   cwant[g.seq][g.j], cnt_of(g.seq, g.j + 1, h), 0});
+  }
+  // Rows per item: about two items per CU over all later segments' rows,
+  // in whole blocks of the tail's 192 rows, at most kTailTokens.
+  int64_t rows_total = 0;
+  for (const Later& g : later) rows_total += static_cast<int64_t>(g.len) * H;
+  const int32_t per_item = static_cast<int32_t>(std::min<int64_t>(
+      kTailTokens, std::max<int64_t>(1, (rows_total / (2 * kCUs) + kTailBlock - 1) / kTailBlock) * kTailBlock));
+  for (const Later& g : later) {
+    const int32_t n = pl.nseg[g.seq], cb = ck_cu ? ck_cu[g.seq] : 0, sin = tstart(g);
+    const int64_t b = tbase[g.seq];
+    for (int32_t h = 0; h < H; ++h) {
+      const int32_t cnt = cnt_of(g.seq, g.j, h), want = cwant[g.seq][g.j];
+      for (int32_t t0 = 0; t0 < g.len; t0 += per_item)
+        titems.insert(titems.end(), {0, g.lo, g.len, g.qrow, sin, h, t0, std::min(g.len, t0 + per_item), cnt,
+                                     want, -1, 0});
+      for (int32_t c = g.ck0; c < g.ck1; ++c)
+        titems.insert(titems.end(), {1, 0, ck_slot ? ck_slot[cb + c] : 0, static_cast<int32_t>(g.xp + 2 * (c - g.ck0)),
+                                     static_cast<int32_t>(g.xp + 2 * (c - g.ck0) + 1), sin, 0, h, cnt, want, -1, 0});
+      if (want_final && g.j == n - 1)  // the final state A_{n-1} S_{n-1} + B_{n-1}
+        titems.insert(titems.end(), {1, 1, g.seq, static_cast<int32_t>(b + (n - 1) + g.j),
+                                     static_cast<int32_t>(b + g.j), sin, 1, h, cnt, want, -1, 0});
     }
   }
   // Chains: the entries' heads, the longest chain first, padded to whole
@@ -696,7 +735,7 @@ FusedList fused_list(const Plan& pl, const int32_t* cu, const int32_t* ck_cu, co
   // scheduling on the CUs, those chains are predicted to have ended: the
   // items then take the CUs that the split sequence's chains leave, while
   // the short chains after them fill the launch's end.
-  const size_t n_items = titems.size() / 10;
+  const size_t n_items = titems.size() / kda::kTailInts;
   if (n_items > 0) {
     auto wg_entry = [&](int32_t x) { return (x >> 4 & 15) == 15 ? -1 : chains[2 * (x >> 8)]; };
     auto wg_time = [&](int32_t x) { const int32_t i = wg_entry(x); return i < 0 ? 0.0 : ctime(i); };
@@ -705,7 +744,7 @@ FusedList fused_list(const Plan& pl, const int32_t* cu, const int32_t* ck_cu, co
     size_t last_dep = 0;
     for (size_t k = 0; k < wgs.size(); ++k) {
       const int32_t i = wg_entry(wgs[k]);
-      if (i >= 0 && pl.nseg[ent[i].seq] == 2) {
+      if (i >= 0 && pl.nseg[ent[i].seq] > 1) {
         ready = std::max(ready, wg_time(wgs[k]));  // (these start at once: the longest chains come first)
         last_dep = k + 1;
       }
@@ -726,8 +765,6 @@ FusedList fused_list(const Plan& pl, const int32_t* cu, const int32_t* ck_cu, co
     wgs.insert(wgs.begin() + static_cast<std::ptrdiff_t>(at), items.begin(), items.end());
   }
   f.n_wg = static_cast<int64_t>(wgs.size());
-  f.n_owg = static_cast<int64_t>(owgs.size() / 3);
-  f.n_cks = static_cast<int64_t>(cks.size() / 6);
   // One block: header (word 0: the decay-range flag, zero), then the parts.
   f.w.assign(kHeaderInts, 0);
   auto put = [&](const std::vector<int32_t>& v) {
@@ -741,17 +778,13 @@ FusedList fused_list(const Plan& pl, const int32_t* cu, const int32_t* ck_cu, co
   f.ck_pos = put(pos);
   f.ck_slot = put(slot);
   f.wgs = put(wgs);
-  f.segs = put(segs);
-  f.owgs = put(owgs);
-  f.cks = put(cks);
   f.titems = put(titems);
   f.tcnt = put(std::vector<int32_t>(f.n_cnt, 0));
   return f;
 }
 
 
-// The fused launch, then for split sequences the composition of their
-// segments (one launch per sequence) and the correction.
+// The fused launch (split sequences included: their correction is its tail).
 int launch_fused_list(const FusedList& fl, const void* q, const void* k, const void* v, const void* a,
                       const void* beta, int32_t H, int32_t dk, int32_t dv, const float* s0, void* o,
                       float* s_final, float* page_pool, int64_t page_elems, void* workspace, int32_t* err_flag,
@@ -796,38 +829,7 @@ int launch_fused_list(const FusedList& fl, const void* q, const void* k, const v
   p.stream = hs;
   e = kda::launch_prefill(p);
   if (e != hipSuccess) return hip_status(e, "prefill launch");
-  if (fl.n_owg + fl.n_cks == 0) return ok();  // (sequences in two segments: corrected in the launch)
-  for (const FusedList::Comp& c : fl.comp) {
-    kda::ComposeArgs ca{};
-    ca.A = tstate + (c.base + 1) * hkv;
-    ca.B = tstate + (c.base + c.n) * hkv;
-    ca.s_in = tstate + c.base * hkv;
-    ca.starts = tstate + (c.base + 2 * c.n - 1) * hkv;
-    ca.s_end = s_final ? s_final + c.seq * hkv : nullptr;
-    ca.n = c.n - 1;
-    ca.H = H; ca.dk = dk; ca.dv = dv;
-    ca.flag = dw + fl.tcnt + c.cnt;
-    ca.stream = hs;
-    e = kda::launch_compose(ca);
-    if (e != hipSuccess) return hip_status(e, "segment composition launch");
-  }
-  kda::FixArgs fx{};
-  fx.o = o;
-  fx.qhat = qhat;
-  fx.tstate = tstate;
-  fx.xpool = xpool;
-  fx.page_pool = page_pool;
-  fx.page_elems = page_elems;
-  fx.s_final = s_final;
-  fx.segs = dw + fl.segs;
-  fx.owgs = dw + fl.owgs;
-  fx.cks = dw + fl.cks;
-  fx.n_owg = static_cast<int>(fl.n_owg);
-  fx.n_cks = static_cast<int>(fl.n_cks);
-  fx.H = H; fx.dk = dk; fx.dv = dv;
-  fx.cnt = dw + fl.tcnt;
-  fx.stream = hs;
-  return hip_status(kda::launch_fix(fx), "segment correction launch");
+  return ok();
 }
 
 // Prefill (a_out == nullptr) or segment summaries (a_out != nullptr: q is
@@ -1057,10 +1059,10 @@ int kda_chunk_prefill_workspace_size(int32_t n_seqs, int64_t total_tokens, int32
     const int64_t n_ent = static_cast<int64_t>(n_seqs) + 2 * kMaxExtraSegs, nch = round8(n_ent * H);
     // (tail items: rows of every token and head, states of every checkpoint
     // and final state and head, each a workgroup entry too)
-    const int64_t items = static_cast<int64_t>(H) * (total_tokens / kTailTokens + 3 * kMaxExtraSegs + n_ckpt);
-    const int64_t ints = kHeaderInts + 10 * nch + (6 + kda::kSegxInts) * n_ent + 4 * n_ckpt + 5 * kMaxExtraSegs +
-                         3 * static_cast<int64_t>(H) * (total_tokens / kda::kFixTokens + kMaxExtraSegs) +
-                         6 * (n_ckpt + kMaxExtraSegs) + 11 * items + static_cast<int64_t>(H) * kMaxExtraSegs;
+    const int64_t items =
+        2 * kCUs + static_cast<int64_t>(H) * (total_tokens / kTailTokens + 3 * kMaxExtraSegs + n_ckpt);
+    const int64_t ints = kHeaderInts + 10 * nch + (6 + kda::kSegxInts) * n_ent + 4 * n_ckpt +
+                         (kda::kTailInts + 1) * items + static_cast<int64_t>(H) * kMaxExtraSegs;
     const int64_t hkv = static_cast<int64_t>(H) * dk * dv;
     const size_t cp = align256(static_cast<size_t>(ints) * 4) +
                       static_cast<size_t>(4 * kMaxExtraSegs + 2 * n_ckpt) * hkv * 4 +

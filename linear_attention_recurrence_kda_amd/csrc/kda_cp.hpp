@@ -1,6 +1,6 @@
 // Corrections for sequences split into segments inside one fused prefill
-// (context parallelism on one GPU): the device code, run by fix_kernel
-// (kda_cp.hip) and by the fused kernel's tail workgroups (kda_fused.hip).
+// (context parallelism on one GPU): the device code that the fused kernel's
+// tail workgroups run (kda_fused.hip, fused_tail).
 //
 // The recurrence is affine in the state ("Kimi Linear 的 KDA 缓存" page,
 // "KDA 的递推与充分状态"; the "Serve 模块交互式演示" page reduces a segment
@@ -32,21 +32,20 @@
 namespace kda {
 namespace {
 
-constexpr int kFixD = 128;      // dk = dv
-constexpr int kFixCkRows = 32;  // state rows per state block
+constexpr int kFixD = 128;           // dk = dv
 constexpr int kStPitch = kFixD + 8;  // bf16 per row of S_in^T in LDS (16 bytes of padding)
-// State blocks: X's rows (pitch 132) and a 32-row slab of S_in (pitch 144),
-// pitches that put the lanes of an MFMA operand read on distinct banks.
+// States: X (pitch 132) and S_in (pitch 144) in LDS, pitches that put the
+// lanes of an MFMA operand read on distinct banks.
 constexpr int kXPitch = kFixD + 4, kSPitch = kFixD + 16;
-constexpr int kFixLds = 36864;  // bytes of LDS either role needs
-constexpr int kFixDepth = 4;     // row blocks in flight per wave
-static_assert(kFixD * kStPitch * 2 <= kFixLds, "S_in^T fits the LDS block");
-static_assert((kXPitch + kSPitch) * kFixCkRows * 4 <= kFixLds, "state tiles fit the LDS block");
+constexpr int kFixDepth = 3;  // row blocks in flight per wave
+constexpr int kRowsLds = kFixD * kStPitch * 2;              // bytes of LDS of the output rows
+constexpr int kFullLds = kFixD * (kXPitch + kSPitch) * 4;   // of a state
 
 struct FixView {
   void* o;
   const void* qhat;
-  const float *tstate, *xpool;
+  float* tstate;  // (start states are written into it)
+  const float* xpool;
   float* page_pool;
   float* s_final;
   int64_t page_elems;
@@ -146,80 +145,17 @@ __device__ __forceinline__ void fix_rows(const FixView& p, int lo, int len, int 
   }
 }
 
-// Rows 32 rb .. 32 rb + 31 of one head of a state dst = X S_in + B in fp32
-// MFMA (16x16x4), by waves 0..3 of the workgroup (every thread of it passes
-// the barriers): wave w forms columns 32w .. 32w + 31 (two by two 16x16
-// tiles); X's rows and S_in, in slabs of 32 rows, pass through LDS.  dst,
-// X, B and S_in point at the head's [dk][dv] block.
-__device__ __forceinline__ void fix_state(float* dst, const float* X, const float* B, const float* S, int rb,
-                                          char* lds) {
-  float* xs = reinterpret_cast<float*>(lds);
-  float* ss = xs + kFixCkRows * kXPitch;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, g = lane >> 4;
-  const bool on = tid < 256;
-  const int r0 = kFixCkRows * rb;
-  auto copy_rows = [&](float* to, int pitch, const float* from) {  // 32 rows of 128
-    for (int e = tid; on && e < kFixCkRows * kFixD / 4; e += 256) {
-      const float4 x = *reinterpret_cast<const float4*>(&from[4 * e]);
-      float* d = &to[(e / (kFixD / 4)) * pitch + 4 * (e % (kFixD / 4))];
-      d[0] = x.x; d[1] = x.y; d[2] = x.z; d[3] = x.w;
-    }
-  };
-  __syncthreads();  // (the LDS block is free)
-  copy_rows(xs, kXPitch, X + r0 * kFixD);
-  // D tile (rt, ct): rows r0 + 16 rt + 4g + i, column 32 wave + 16 ct + l16.
-  f32x4 acc[2][2];
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        acc[rt][ct][i] = on ? B[(r0 + 16 * rt + 4 * g + i) * kFixD + 32 * wave + 16 * ct + l16] : 0.f;
-  for (int sl = 0; sl < kFixD / kFixCkRows; ++sl) {
-    __syncthreads();  // (the previous slab is consumed)
-    copy_rows(ss, kSPitch, S + sl * kFixCkRows * kFixD);
-    __syncthreads();
-    if (on) {
-#pragma unroll
-      for (int ks = 0; ks < kFixCkRows / 4; ++ks) {
-        const int k = 4 * ks + g;
-        float a[2], b[2];
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) a[rt] = xs[(16 * rt + l16) * kXPitch + kFixCkRows * sl + k];
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) b[ct] = ss[k * kSPitch + 32 * wave + 16 * ct + l16];
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-          for (int ct = 0; ct < 2; ++ct)
-            acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[rt], b[ct], acc[rt][ct], 0, 0, 0);
-      }
-    }
-  }
-  if (on) {
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[(r0 + 16 * rt + 4 * g + i) * kFixD + 32 * wave + 16 * ct + l16] = acc[rt][ct][i];
-  }
-}
-
-// A whole head's state dst = X S_in + B at once, for a workgroup with at
-// least 8 waves and kFullLds bytes of LDS: all of X (pitch 132) and S_in
-// (pitch 144) are loaded into LDS together (one memory round trip), then
+// One head's state dst = X S_in + B (dst, X, B, S_in point at the head's
+// [dk][dv] block), by a workgroup of NW >= 8 waves with kFullLds bytes of
+// LDS: X and S_in are loaded into LDS together (one memory round trip), then
 // wave w < 8 forms rows 16w .. 16w + 15, all 128 columns (eight 16x16
 // tiles), in fp32 MFMA (16x16x4).
-constexpr int kFullLds = kFixD * (kXPitch + kSPitch) * 4;
 template <int NW>
-__device__ __forceinline__ void fix_state_full(float* dst, const float* X, const float* B, const float* S, char* lds) {
+__device__ __forceinline__ void fix_state(float* dst, const float* X, const float* B, const float* S, char* lds) {
   static_assert(NW >= 8, "eight waves form the sixteen-row tiles");
   float* xs = reinterpret_cast<float*>(lds);
   float* ss = xs + kFixD * kXPitch;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, g = lane >> 4;
-  __syncthreads();  // (the LDS block is free)
   for (int e = tid; e < kFixD * kFixD / 4; e += 64 * NW) {
     const int r = e / (kFixD / 4), c4 = 4 * (e % (kFixD / 4));
     const float4 x = *reinterpret_cast<const float4*>(&X[4 * e]);
@@ -250,22 +186,20 @@ __device__ __forceinline__ void fix_state_full(float* dst, const float* X, const
     for (int i = 0; i < 4; ++i) dst[(16 * wave + 4 * g + i) * kFixD + 16 * ct + l16] = acc[ct][i];
 }
 
-// A state item (dsti: page slot, or -1 - n for the final state of sequence
-// n; B and X from tstate when in_t, else xpool; S_in = tstate state si):
-// row block rb of head h, and (h = 0, rb <= 0) the page's zero padding.
-// rb < 0: every row, by fix_state_full (NW >= 8 waves, kFullLds of LDS).
+// A state item of head h: X S_in + B into a page slot (dkind 0, page zero
+// padding included), the final state of sequence didx (dkind 1) or tstate
+// state didx (dkind 2: a later segment's start state); B and X from tstate
+// when in_t, else from xpool; S_in = tstate state si.
 template <int NW>
-__device__ __forceinline__ void fix_state_item(const FixView& p, int64_t dsti, int bi, int xi, int si, bool in_t,
-                                               int h, int rb, char* lds) {
+__device__ __forceinline__ void fix_state_item(const FixView& p, int dkind, int64_t didx, int bi, int xi, int si,
+                                               bool in_t, int h, char* lds) {
   const int64_t hkv = static_cast<int64_t>(p.H) * kFixD * kFixD, hoff = static_cast<int64_t>(h) * kFixD * kFixD;
   const float* pool = in_t ? p.tstate : p.xpool;
-  float* dst = (dsti >= 0 ? p.page_pool + dsti * p.page_elems : p.s_final + (-1 - dsti) * hkv) + hoff;
-  if constexpr (NW >= 8) {
-    if (rb < 0) fix_state_full<NW>(dst, pool + xi * hkv + hoff, pool + bi * hkv + hoff, p.tstate + si * hkv + hoff, lds);
-  }
-  if (rb >= 0) fix_state(dst, pool + xi * hkv + hoff, pool + bi * hkv + hoff, p.tstate + si * hkv + hoff, rb, lds);
-  if (dsti >= 0 && h == 0 && rb <= 0)
-    for (int64_t e = hkv + threadIdx.x; e < p.page_elems; e += blockDim.x) (p.page_pool + dsti * p.page_elems)[e] = 0.f;
+  float* base = dkind == 0 ? p.page_pool + didx * p.page_elems
+                           : (dkind == 1 ? p.s_final : p.tstate) + didx * hkv;
+  fix_state<NW>(base + hoff, pool + xi * hkv + hoff, pool + bi * hkv + hoff, p.tstate + si * hkv + hoff, lds);
+  if (dkind == 0 && h == 0)
+    for (int64_t e = hkv + threadIdx.x; e < p.page_elems; e += 64 * NW) base[e] = 0.f;
 }
 
 }  // namespace

@@ -193,9 +193,9 @@ struct FusedParams {
   void* qhat;
   float* xpool;
   float* tstate;
-  // Tail workgroups (width code 5): the correction of sequences in two
-  // segments, items titems [n][10] (see fused_tail), each waiting for the
-  // chains it reads through tcnt (counters in the workspace, zero on entry).
+  // Tail workgroups (width code 5): the correction of split sequences,
+  // items titems [n][kTailInts] (see fused_tail), each waiting for what it
+  // reads through tcnt (counters in the workspace, zero on entry).
   const int32_t* titems;
   int32_t* tcnt;
 };
@@ -892,25 +892,29 @@ __device__ __forceinline__ void fused_chain(const FusedParams& p, int chain, int
 }
 
 // ---------------------------------------------------------------------------
-// The tail: the correction of a sequence in two segments (kda_cp.hpp) by
-// workgroups listed after every chain, so that they start only once every
-// chain's workgroup has started (workgroups start in list order), and then
-// wait, as the chains they read finish, on a counter per (sequence, head)
-// that each of those chains raises when its stores are complete (1, or
-// 0x10000 for a chain that stopped at a decay out of range: then nothing is
-// corrected).  The wait is bounded: past kTailSpin polls the workgroup
-// raises the error flags and corrects nothing.  The chains of a sequence's
-// head finish well before the launch's last chains (they are the longest
-// and start first), so the correction runs beside the launch's tail.
-//   titems [10]: rows: (0, first token, tokens, first qhat row, tstate index
-//   of S_in, head, first and end token within the segment, counter, count);
-//   states: (1, page slot or -1 - sequence, B, X, tstate index of S_in, 1:
-//   B and X in tstate / 0: in xpool, head, unused, counter, count).
+// The tail: the correction of split sequences (kda_cp.hpp) by workgroups
+// listed after every chain they read, so that they start only once those
+// have started (workgroups start in list order), and then wait, as the
+// chains finish, on a counter per (sequence, later segment, head).  The
+// chains of a segment raise it when their stores are complete (1, or
+// 0x10000 for a chain that stopped at a decay out of range), and so does the
+// item that forms the segment's start state; an item forming a start state
+// raises the next segment's counter when done (0x10000 when it corrected
+// nothing), so every wait ends.  The wait is bounded too: past kTailSpin
+// polls the workgroup raises the error flags and corrects nothing.  The
+// split chains are the longest and start first, so they end well before
+// the launch's last chains and the correction runs beside them.
+//   titems [kTailInts]: rows: (0, first token, tokens, first qhat row,
+//   tstate index of S_in, head, first and end token within the segment,
+//   counter, count, -1, 0); states: (1, destination kind, index, B, X,
+//   tstate index of S_in, 1: B and X in tstate / 0: in xpool, head,
+//   counter, count, counter raised when done or -1, 0).
 constexpr int kTailSpin = 1 << 24;  // polls of about 0.3 us: a few seconds
 
 template <int DK>
 __device__ __forceinline__ void fused_tail(const FusedParams& p, int item, FusedSmem<DK>& sm) {
-  auto f = [&](int i) { return ld_const(p.titems, 10 * item + i); };
+  constexpr int NW = Fused<DK>::NT / 64;
+  auto f = [&](int i) { return ld_const(p.titems, kTailInts * item + i); };
   if (threadIdx.x == 0) {
     const int want = f(9);
     int c = 0;
@@ -923,17 +927,27 @@ __device__ __forceinline__ void fused_tail(const FusedParams& p, int item, Fused
       *p.wsflag = 1;
       if (p.err_flag != nullptr) *p.err_flag = 1;
     }
-    __threadfence();  // acquire: the chains' stores are visible from here on
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the chains' stores are visible from here on
     sm.stop[0] = c == want;
   }
   __syncthreads();
-  if (!sm.stop[0]) return;
+  const bool good = sm.stop[0] != 0;
   const FixView v{p.o, p.qhat, p.tstate, p.xpool, p.page_pool, p.s_final, p.page_elems, p.H};
   char* lds = reinterpret_cast<char*>(&sm);  // (up to kFullLds bytes from its start, clear of stop[])
   if (f(0) == 0) {
-    fix_rows<Fused<DK>::NT / 64>(v, f(1), f(2), f(3), f(4), f(5), f(6), f(7), lds);
-  } else {
-    fix_state_item<Fused<DK>::NT / 64>(v, f(1), f(2), f(3), f(4), f(5) != 0, f(6), -1, lds);
+    if (good) fix_rows<NW>(v, f(1), f(2), f(3), f(4), f(5), f(6), f(7), lds);
+    return;
+  }
+  if (good) fix_state_item<NW>(v, f(1), f(2), f(3), f(4), f(5), f(6) != 0, f(7), lds);
+  const int sig = f(10);
+  if (sig >= 0) {  // a start state: its stores complete (every wave), then one release and the count
+    vm_drain();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // (L2 written back)
+      vm_drain();  // (and the write-back complete before the count)
+      atomicAdd(p.tcnt + sig, good ? 1 : 0x10000);
+    }
   }
 }
 
@@ -943,7 +957,7 @@ __device__ __forceinline__ void fused_tail(const FusedParams& p, int item, Fused
 template <int DK>
 __global__ __launch_bounds__(Fused<DK>::NT, 1) void fused_kernel(FusedParams p) {
   __shared__ __attribute__((aligned(16))) FusedSmem<DK> sm;
-  static_assert(offsetof(FusedSmem<DK>, stop) >= kFixLds && offsetof(FusedSmem<DK>, stop) >= kFullLds,
+  static_assert(offsetof(FusedSmem<DK>, stop) >= kRowsLds && offsetof(FusedSmem<DK>, stop) >= kFullLds,
                 "the tail's LDS block lies clear of stop[]");
   const int e = ld_const(p.wgs, blockIdx.x);
   const int chain = e >> 8, code = (e >> 4) & 15, tile = e & 15;
@@ -966,7 +980,8 @@ __global__ __launch_bounds__(Fused<DK>::NT, 1) void fused_kernel(FusedParams p) 
       __syncthreads();
       if (threadIdx.x == 0) {
         const bool stopped = (sm.stop[0] | sm.stop[1] | sm.stop[2]) != 0;
-        __threadfence();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // (L2 written back)
+        vm_drain();  // (and the write-back complete before the count)
         atomicAdd(p.tcnt + cb + ld_const(p.chains, 2 * chain + 1), stopped ? 0x10000 : 1);
       }
     }

@@ -134,40 +134,11 @@ struct ComposeArgs {
   const float *A, *B, *s_in;
   float *starts, *s_end;
   int n, H, dk, dv;
-  const int32_t* flag;  // null, or a word per head: at 0x10000 or more that head is not written
   hipStream_t stream;
 };
 
-// Corrections after a fused prefill with split sequences.  A segment that
-// starts at state S_in was run from zero (outputs o0, checkpoints B_ck) and
-// from the identity (outputs qhat = the segment's linear part applied to q,
-// checkpoints X_ck); the true values are o = o0 + S_in^T qhat and
-// S_ck = X_ck S_in + B_ck.
-//   segs [n_segs][5]: (first token, tokens, first qhat row, tstate index of S_in,
-//                     first counter)
-//   owgs [n_owg][3]:  (segment, head, first token within the segment), each
-//                     workgroup kFixTokens tokens of one head
-//   cks [n_cks][6]:   states X S_in + B: (destination: page slot, or -1 - n for
-//                     the final state of sequence n; index of B, of X; tstate
-//                     index of S_in; 0: B and X in xpool, 1: in tstate; first
-//                     counter)
-// A (sequence, head) whose counter (cnt[first counter + head], raised by
-// its chains) is 0x10000 or more had a chain stopped at a decay out of
-// range: nothing of it is corrected.
-struct FixArgs {
-  void* o;
-  const void* qhat;
-  const float *tstate, *xpool;
-  float* page_pool;
-  float* s_final;
-  int64_t page_elems;
-  const int32_t *segs, *owgs, *cks;
-  int n_owg, n_cks, H, dk, dv;
-  const int32_t* cnt;
-  hipStream_t stream;
-};
-hipError_t launch_fix(const FixArgs& p);
-constexpr int kFixTokens = 512;  // tokens per o-correction workgroup
+// Tail items of the fused launch (kda_fused.hip, fused_tail): int32 each.
+constexpr int kTailInts = 12;
 hipError_t launch_compose(const ComposeArgs& p);
 
 // Front end (convolution, SiLU, L2Norm, gates).  Prefill: one unit per tile

@@ -78,7 +78,6 @@ __global__ __launch_bounds__(kComposeThreads) void compose_kernel(ComposeArgs p)
   __shared__ float S[DK][kComposeCols + 1];
   const int tiles = p.dv / kComposeCols;
   const int h = blockIdx.x / tiles, j0 = (blockIdx.x % tiles) * kComposeCols;
-  if (p.flag != nullptr && p.flag[h] >= 0x10000) return;  // (uniform: every wave leaves)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, g = lane >> 4;
