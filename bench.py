@@ -666,7 +666,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", default="", help="comma list of: prefill4, prefill4_c64, prefill4_gated, prefill3, "
-                                               "segments, front_end, decode, decode_bf16, replay, replay_big, "
+                                               "prefill3_c32, segments, front_end, decode, decode_bf16, replay, replay_big, "
                                                "replay_big_bf16, ring, pack, copycal")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--json-out", default="")
@@ -732,6 +732,15 @@ def main():
         parts["prefill_single"] = bench_prefill(
             torch, kda, inputs, inputs.workload3(), args.steps, args.warmup, False,
             "single-sequence prefill: T=8192, H=32, dk=dv=128, bf16, S0=0, chunk 64, ckpt every 512")
+    if want("prefill3_c32"):
+        # The same workload on the fused kernel (chunk 32), where the one
+        # sequence is cut into segments whose chains run side by side and the
+        # launch's tail composes and corrects them.
+        log("prefill (single sequence, chunk 32) ...")
+        parts["prefill_single_c32"] = bench_prefill(
+            torch, kda, inputs, inputs.workload3(), args.steps, args.warmup, False,
+            "single-sequence prefill: T=8192, H=32, dk=dv=128, bf16, S0=0, chunk 32 (fused kernel, the "
+            "sequence in segments), ckpt every 512", chunk=HEAD_CHUNK)
     if want("segments"):
         log("segments (context-parallel prefill on one GPU) ...")
         parts["segments"] = bench_segments(torch, kda, inputs, inputs.workload3(), args.steps,

@@ -189,11 +189,18 @@ int kda_unpack_heads_ex(const void* page_pool, kda_dtype state_dtype, int64_t pa
  *   Log-decays must lie in [-160/chunk, 0] per token and channel ([Serve demo]
  *   §1.3 bounds a to [g_min, 0]; the lower end is -2.5 at chunk 64, -5 at
  *   chunk 32): the chunk's scaled operands, referenced to the middle row of
- *   the chunk, then stay below e^80 and are finite in bf16 and fp32.  The
- *   first kernel checks every a (a NaN fails the check too); if one is out
- *   of range it raises *err_flag and the call writes nothing: o, s_final and
- *   the page slots keep their contents (the [kv_prefix] page's rule that a
- *   failure never leaves a partial record).
+ *   the chunk, then stay below e^80 and are finite in bf16 and fp32.  Every
+ *   a is checked on the device (a NaN fails the check too); one out of range
+ *   raises *err_flag, and no wrong record is written (the [kv_prefix] page's
+ *   rule that a failure never leaves a partial or wrong record).  On the
+ *   two-kernel path (chunk other than 32, fp32 inputs or dk other than 128)
+ *   the call then writes nothing: o, s_final and the page slots keep their
+ *   contents.  On the fused path (bf16, chunk 32, dk = 128) the (sequence,
+ *   head) holding the value keeps the outputs and checkpoints of the chunks
+ *   before it and writes no later checkpoint and no final state; for a
+ *   sequence the call cuts into segments (kda_chunk_prefill_split) that
+ *   head's output rows after its first segment are then unspecified.  Every
+ *   other (sequence, head) is complete.
  *   cu_seqlens_host : host int32 [n_seqs + 1]; cu[0] = 0, non-decreasing,
  *              cu[n_seqs] = T_tot.  Zero-length sequences are allowed.
  *   s0       : [n_seqs, H, dk, dv] fp32 committed states, READ ONLY, or NULL
@@ -212,7 +219,8 @@ int kda_unpack_heads_ex(const void* page_pool, kda_dtype state_dtype, int64_t pa
  *                    is written in the pack layout and zero-padded
  *   workspace      : device memory of at least kda_chunk_prefill_workspace_size
  *                    bytes, 256-byte aligned; contents on entry are ignored.  It
- *                    holds the work list and one record per (chunk, head),
+ *                    holds the work list and, on the two-kernel path, one
+ *                    record per (chunk, head),
  *                    written by a first kernel that handles all chunks at once
  *                    and read by the sequential one: T diag(beta) and
  *                    lower(A_qk) (chunk^2 elements each), k*g, q*g and
@@ -220,7 +228,16 @@ int kda_unpack_heads_ex(const void* page_pool, kda_dtype state_dtype, int64_t pa
  *                    (dk fp32).  That is about
  *                    (T_tot / chunk + n_seqs + n_ckpt) * H * (2 chunk^2 +
  *                    3 chunk dk) * 2 bytes for bf16 (4.3 GB for 128k tokens,
- *                    H = 32, dk = 128, chunk 64).
+ *                    H = 32, dk = 128, chunk 64).  On the fused path it holds
+ *                    the work list and, where the call cuts long sequences
+ *                    into segments, their buffers: the later segments' rows
+ *                    of q mapped through their linear parts (bf16, H dk per
+ *                    token of those segments), their checkpoints from zero
+ *                    and from the identity, and a few states per segment.
+ *                    The size function's figure covers that for any lengths
+ *                    (about the size of q, plus 4 MiB per checkpoint at
+ *                    H = 32, d = 128); a smaller workspace that still holds
+ *                    the work list makes the call run without segments.
  *   err_flag       : device int32, may be NULL; set to 1 when a log-decay is
  *                    out of range (above); never cleared by the library
  * Sizes: T_tot < 2^31 tokens, H*dk*dv < 2^31, H*max(dk, dv) <= 2^24, and
@@ -254,6 +271,15 @@ int kda_chunk_prefill(const void* q, const void* k, const void* v, const void* a
  * tile width per sequence (32, 64 or 128 columns, from the library's cost
  * model, in one launch) where the column-slab kernel runs with dv = 128; the
  * automatic choice (0) takes that form where the model predicts it faster.
+ * On the fused path (bf16, chunk 32, dk = dv = 128) the automatic choice
+ * also cuts sequences whose chain would bound the call into segments
+ * ([Serve demo] §1.7: a segment is the affine map S_end = A S_start + B of its
+ * start state): a later segment's chains run from the zero state and from
+ * the identity beside the first one, and the launch's last workgroups
+ * compose the maps and correct the later segments' outputs and checkpoints
+ * (the same result up to rounding).  dv_split = -n, 2 <= n <= 8, cuts every
+ * sequence of at least n * 512 tokens into n segments (at most eight later
+ * segments per call), with the widths of the automatic choice.
  * Other values: KDA_EUNSUPPORTED.
  */
 int kda_chunk_prefill_split(const void* q, const void* k, const void* v, const void* a,

@@ -319,8 +319,12 @@ def chunk_prefill(q, k, v, a, beta, cu_seqlens, s0=None, chunk=64, checkpoints=N
     page_pool [n_slots, page_elems] fp32 receives the checkpoint states.
     gate_g_min: when given, a and beta are gate logits and the prefill uses
     a = gate_g_min * sigmoid(a), beta = sigmoid(beta) (the fused gate).
-    err_flag: int32 [1] on the device, or None; set to 1 (and nothing is
-    written) when a log-decay lies outside [-160/chunk, 0].
+    err_flag: int32 [1] on the device, or None; set to 1 when a log-decay
+    lies outside [-160/chunk, 0] (what is then written: see kda_chunk_prefill
+    in include/kda.h).
+    dv_split: 0 (the library's choice), 1/2/4/8 tiles per head, -1 a width
+    per sequence, -n (2..8) every sequence of at least n * 512 tokens in n
+    segments (fused path).
     Returns (o [T,H,dv], s_final [N,H,dk,dv] or None).
     """
     T, H, dk = q.shape

@@ -204,6 +204,25 @@ def test_prefill_plan_widths():
     assert cols == [32, 32, 32]
 
 
+def test_prefill_plan_segments():
+    """Fused path (bf16, chunk 32, dk = dv = 128): a sequence whose chain
+    would bound the call is cut into segments by the cost model; -n cuts
+    every sequence of at least n * 512 tokens into n; dv != dk, an explicit
+    tile width or -1 cut nothing."""
+    cu = [0, 30000, 31000, 31500]
+    _, names = kda.prefill_plan(cu, 32, 128, 128, 32)
+    assert "1 sequence in" in names, names
+    _, names = kda.prefill_plan([0, 2100, 3200, 3245, 3245, 4545], 2, 128, 128, 32, dv_split=-2)
+    assert "3 sequences in 6 segments" in names, names  # (2100, 1100 and 1300 tokens)
+    _, names = kda.prefill_plan([0, 2100, 3200, 3245, 3245, 4545], 2, 128, 128, 32, dv_split=-4)
+    assert "1 sequence in 4 segments" in names, names
+    for kw in ({"dv_split": -1}, {"dv_split": 1}):
+        _, names = kda.prefill_plan(cu, 32, 128, 128, 32, **kw)
+        assert "segments" not in names, names
+    _, names = kda.prefill_plan(cu, 32, 128, 64, 32)
+    assert "segments" not in names, names
+
+
 def test_prefill_plan_is_fast_for_many_sequences():
     """The width choice is O(n log n): 4096 sequences plan in well under a
     tenth of a second."""
@@ -214,6 +233,13 @@ def test_prefill_plan_is_fast_for_many_sequences():
     t0 = time.perf_counter()
     cols, _ = kda.prefill_plan(cu, 32, 128, 128, 64)
     assert time.perf_counter() - t0 < 0.1
+    assert set(cols) <= {16, 32, 64, 128}
+    # the fused path's plan (widths, segments and their list scheduling), with
+    # one long sequence among them
+    cu[-1] += 60000
+    t0 = time.perf_counter()
+    cols, _ = kda.prefill_plan(cu, 32, 128, 128, 32)
+    assert time.perf_counter() - t0 < 0.5
     assert set(cols) <= {16, 32, 64, 128}
 
 
