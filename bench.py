@@ -47,7 +47,7 @@ PREFILL_SRC = [os.path.join(CSRC, f) for f in
 # (the fused path: its kernel, the correction of split sequences, and the
 # host plan that decides the split and the tile widths)
 FUSED_SRC = [os.path.join(CSRC, f) for f in ("kda_prefill_kernels.hpp", "kda_prefill_slab.hpp", "kda_fused.hip",
-                                             "kda_cp.hpp", "kda_cp.hip", "kda_segments.hip", "kda_api_prefill.cpp")]
+                                             "kda_cp.hpp", "kda_api_prefill.cpp")]
 HEAD_CHUNK = 32  # the headline prefill's chunk (the fused kernel)
 
 
@@ -628,13 +628,11 @@ def write_traffic(fetch_csv, write_csv, name="prefill_varlen"):
            "python3 bench.py --traffic <fetch csv> <write csv> {}")
     res = {"copy_fetch_bytes_raw": f_cp, "copy_write_bytes_raw": w_cp, "fetch_scale": fs, "write_scale": ws}
     if name == "prefill_varlen":
-        # One prefill call = one fused_kernel dispatch (bf16, chunk 32, dk 128;
-        # with sequences in more than two segments also compose_kernel and
-        # fix_kernel), or one local_kernel and one propagation dispatch
-        # (slab_mixed_kernel or slab_kernel for bf16 at chunk 64, else
-        # prop_kernel).
+        # One prefill call = one fused_kernel dispatch (bf16, chunk 32, dk 128),
+        # or one local_kernel and one propagation dispatch (slab_mixed_kernel or
+        # slab_kernel for bf16 at chunk 64, else prop_kernel).
         prop = lambda k: any(n in k for n in ("fused_kernel", "local_kernel", "prop_kernel", "slab_kernel",
-                                              "slab_mixed_kernel", "compose_kernel", "fix_kernel"))
+                                              "slab_mixed_kernel"))
         knames = sorted(k for k in fetch if prop(k))
         f_pre = sum(float(np.mean(fetch[k])) for k in knames)
         w_pre = sum(float(np.mean(write[k])) for k in knames)

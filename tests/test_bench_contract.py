@@ -65,3 +65,14 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120, cwd=ROOT)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_traffic_stamps_name_existing_sources():
+    """The sources a traffic figure is stamped with exist (a missing one would
+    stop the bench before its line is printed), and the committed figures
+    parse."""
+    for p in bench.FUSED_SRC + bench.PREFILL_SRC:
+        assert os.path.exists(p), p
+    assert bench.src_hash(bench.FUSED_SRC) and bench.src_hash(bench.PREFILL_SRC)
+    for name in ("prefill_varlen", "pack"):
+        bench.committed_traffic(name, bench.FUSED_SRC)
