@@ -707,9 +707,14 @@ def main():
     parts = {}
     varlen = ("varlen prefill: 16 seqs, len~logU[1024,32768], H=32, dk=dv=128, bf16, S0~N(0,0.1^2), "
               "chunk {}, ckpt every 4096 + tail, final states packed")
-    # (The gated part runs first: the fused kernel's first calls in a process
-    # are slower, falling over some twenty calls to the steady state, so the
-    # part that runs first measures part of that slope.)
+    if want("prefill4"):
+        log("prefill (varlen) ...")
+        parts["prefill_varlen"] = bench_prefill(torch, kda, inputs, w4, args.steps, args.warmup, True,
+                                                varlen.format(HEAD_CHUNK), chunk=HEAD_CHUNK)
+    if want("prefill4_c64"):
+        log("prefill (varlen, chunk 64) ...")
+        parts["prefill_varlen_chunk64"] = bench_prefill(torch, kda, inputs, w4, args.steps, args.warmup, True,
+                                                        varlen.format(64), chunk=64)
     if want("prefill4_gated"):
         if w4 is None:
             log("generating the varlen prefill workload ...")
@@ -720,14 +725,6 @@ def main():
             "varlen prefill as above (chunk {}) with the gate fused in: a = -sigmoid(z_a), "
             "beta = sigmoid(z_b) computed from bf16 logits inside the prefill".format(HEAD_CHUNK),
             gate=True, chunk=HEAD_CHUNK)
-    if want("prefill4"):
-        log("prefill (varlen) ...")
-        parts["prefill_varlen"] = bench_prefill(torch, kda, inputs, w4, args.steps, args.warmup, True,
-                                                varlen.format(HEAD_CHUNK), chunk=HEAD_CHUNK)
-    if want("prefill4_c64"):
-        log("prefill (varlen, chunk 64) ...")
-        parts["prefill_varlen_chunk64"] = bench_prefill(torch, kda, inputs, w4, args.steps, args.warmup, True,
-                                                        varlen.format(64), chunk=64)
     if want("prefill3"):
         log("prefill (single sequence) ...")
         parts["prefill_single"] = bench_prefill(
