@@ -132,3 +132,69 @@ def test_segments_bad_decay_stops_that_head(n_seg):
         assert_parity(sf[1, h], sf_r[1, h], "bf16", f"s_final seq 1 head {h}")
         for j, p in enumerate(ck[1]):
             assert_parity(page[slots[1][j], h], ck_r[1][p][h], "bf16", f"ckpt {p} seq 1 head {h}")
+
+
+def test_segments_with_the_fused_gate():
+    """a and beta as logits (the gated entry, g_min = -0.01 so the start
+    states carry over) with a sequence in three segments: the identity and
+    zero-start chains apply the gate as the others do."""
+    lens = [1700, 200]
+    H, d, g_min = 2, 128, -0.01
+    w = inputs.prefill_workload(714, lens, H, d, d, "bf16", s0_std=0.1)
+    rng = np.random.default_rng(715)
+    z_a = inputs.round_to_bf16(rng.standard_normal(w["a"].shape).astype(np.float32))
+    z_b = inputs.round_to_bf16(rng.standard_normal(w["beta"].shape).astype(np.float32))
+    ck = [[300, 600, 1000, 1700], [200]]
+    slots = [[0, 1, 2, 3], [4]]
+    pool = torch.zeros((5, H * d * d), device="cuda")
+    dd = {n: dev_tensor(w[n], "bf16") for n in ("q", "k", "v")}
+    o, sf = kda.chunk_prefill(dd["q"], dd["k"], dd["v"], dev_tensor(z_a, "bf16"), dev_tensor(z_b, "bf16"),
+                              w["cu_seqlens"], s0=torch.from_numpy(w["s0"]).cuda(), chunk=32, checkpoints=ck,
+                              ckpt_slots=slots, page_pool=pool, gate_g_min=g_min, dv_split=-3)
+    torch.cuda.synchronize()
+    a = g_min * oracle.sigmoid(z_a)
+    beta = oracle.sigmoid(z_b)
+    o_r, sf_r, ck_r = oracle.kda_prefill(w["q"], w["k"], w["v"], a, beta, w["cu_seqlens"], w["s0"], ck)
+    page = pool.reshape(5, H, d, d)
+    for n, (lo, hi) in enumerate([(0, 1700), (1700, 1900)]):
+        for h in range(H):
+            assert_parity_blocks(o[lo:hi, h], o_r[lo:hi, h], "bf16", 32, f"o seq {n} head {h}")
+            assert_parity(sf[n, h], sf_r[n, h], "bf16", f"s_final seq {n} head {h}")
+            for j, p in enumerate(ck[n]):
+                assert_parity(page[slots[n][j], h], ck_r[n][p][h], "bf16", f"ckpt {p} seq {n} head {h}")
+
+
+def test_small_workspace_runs_without_segments():
+    """A workspace that holds the work list but not the segments' buffers:
+    the call runs without segments (same results), through the C entry."""
+    import ctypes
+    lens = [2100, 300]
+    H, d = 2, 128
+    w = inputs.prefill_workload(716, lens, H, d, d, "bf16", s0_std=0.1, g_min=WEAK, ckpt_every=700)
+    dd = {n: dev_tensor(w[n], "bf16") for n in ("q", "k", "v", "a", "beta")}
+    T = int(w["cu_seqlens"][-1])
+    ck = w["checkpoints"]
+    n_ck = sum(len(c) for c in ck)
+    s0 = torch.from_numpy(w["s0"]).cuda()
+    o = torch.empty((T, H, d), dtype=torch.bfloat16, device="cuda")
+    sf = torch.empty((2, H, d, d), device="cuda")
+    pool = torch.zeros((n_ck, H * d * d), device="cuda")
+    ws = torch.empty(1 << 16, dtype=torch.uint8, device="cuda")  # the work list fits, the buffers do not
+    assert kda.prefill_workspace_size(2, T, H, d, d, 32, n_ck) > ws.numel()
+    cu = (ctypes.c_int32 * 3)(*[int(x) for x in w["cu_seqlens"]])
+    ck_cu = (ctypes.c_int32 * 3)(0, len(ck[0]), n_ck)
+    ck_pos = (ctypes.c_int32 * n_ck)(*[p for c in ck for p in c])
+    ck_slot = (ctypes.c_int32 * n_ck)(*range(n_ck))
+    L = kda.lib()
+    st = L.kda_chunk_prefill_split(dd["q"].data_ptr(), dd["k"].data_ptr(), dd["v"].data_ptr(), dd["a"].data_ptr(),
+                                   dd["beta"].data_ptr(), kda.KDA_BF16, H, d, d, 32, cu, 2, s0.data_ptr(),
+                                   o.data_ptr(), sf.data_ptr(), ck_cu, ck_pos, ck_slot, n_ck, pool.data_ptr(),
+                                   H * d * d, n_ck, ws.data_ptr(), ws.numel(), -2, None,
+                                   torch.cuda.current_stream().cuda_stream)
+    assert st == 0, L.kda_last_error().decode()
+    torch.cuda.synchronize()
+    slots, i = [], 0
+    for c in ck:
+        slots.append(list(range(i, i + len(c))))
+        i += len(c)
+    _check(w, "bf16", o, sf, pool, slots, block=32)
