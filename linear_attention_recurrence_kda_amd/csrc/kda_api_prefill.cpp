@@ -694,7 +694,11 @@ FusedList fused_list(const Plan& pl, const int32_t* cu, const int32_t* ck_cu, co
     const double t = w == 128 ? kFusedT[0] : w == 64 ? kFusedT[1] : w == 32 ? kFusedT[2] : kFusedT[3];
     return t * static_cast<double>(ent[i].chunks);
   };
-  std::stable_sort(order.begin(), order.end(), [&](int64_t x, int64_t y) { return ctime(x) > ctime(y); });
+  // (split sequences' chains first: the tail waits for them)
+  auto split = [&](int64_t i) { return pl.nseg[ent[i].seq] > 1; };
+  std::stable_sort(order.begin(), order.end(), [&](int64_t x, int64_t y) {
+    return split(x) != split(y) ? split(x) : ctime(x) > ctime(y);
+  });
   f.n_chains = round8(n_ent * H);
   std::vector<int32_t> chains(2 * f.n_chains);
   int64_t c = 0;
@@ -739,27 +743,29 @@ FusedList fused_list(const Plan& pl, const int32_t* cu, const int32_t* ck_cu, co
   if (n_items > 0) {
     auto wg_entry = [&](int32_t x) { return (x >> 4 & 15) == 15 ? -1 : chains[2 * (x >> 8)]; };
     auto wg_time = [&](int32_t x) { const int32_t i = wg_entry(x); return i < 0 ? 0.0 : ctime(i); };
-    std::vector<double> cu_free(kCUs, 0.0);  // a min-heap of the CUs' free times
+    // Predicted starts of the chains' workgroups (list scheduling on the
+    // CUs, a min-heap of their free times), and the predicted end of the
+    // split sequences' chains.
+    std::vector<double> cu_free(kCUs, 0.0), start(wgs.size());
     double ready = 0;
     size_t last_dep = 0;
     for (size_t k = 0; k < wgs.size(); ++k) {
+      std::pop_heap(cu_free.begin(), cu_free.end(), std::greater<double>());
+      start[k] = cu_free.back();
+      cu_free.back() = start[k] + wg_time(wgs[k]);
+      std::push_heap(cu_free.begin(), cu_free.end(), std::greater<double>());
       const int32_t i = wg_entry(wgs[k]);
-      if (i >= 0 && pl.nseg[ent[i].seq] > 1) {
-        ready = std::max(ready, wg_time(wgs[k]));  // (these start at once: the longest chains come first)
+      if (i >= 0 && split(i)) {
+        ready = std::max(ready, start[k] + wg_time(wgs[k]));
         last_dep = k + 1;
       }
     }
     size_t at = wgs.size();
-    for (size_t k = 0; k < wgs.size(); ++k) {
-      std::pop_heap(cu_free.begin(), cu_free.end(), std::greater<double>());
-      const double start = cu_free.back();
-      if (k >= last_dep && start >= ready) {
+    for (size_t k = last_dep; k < wgs.size(); ++k)
+      if (start[k] >= ready) {
         at = k;
         break;
       }
-      cu_free.back() = start + wg_time(wgs[k]);
-      std::push_heap(cu_free.begin(), cu_free.end(), std::greater<double>());
-    }
     std::vector<int32_t> items;
     for (size_t t = 0; t < n_items; ++t) items.push_back(static_cast<int32_t>((t << 8) | (5 << 4)));
     wgs.insert(wgs.begin() + static_cast<std::ptrdiff_t>(at), items.begin(), items.end());
