@@ -198,3 +198,24 @@ def test_small_workspace_runs_without_segments():
         slots.append(list(range(i, i + len(c))))
         i += len(c)
     _check(w, "bf16", o, sf, pool, slots, block=32)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_segments_random_shapes(seed):
+    """Random lengths (zero and short ones among them), random checkpoint
+    positions (a cut and its neighbours among them), S0 or none, and a
+    segment count of 0 (the library's choice) or -2 .. -5: every output row
+    block, final state and checkpoint against the oracle."""
+    rng = np.random.default_rng(720 + seed)
+    lens = [int(x) for x in rng.integers(0, 2600, 5)] + [0, 31]
+    split = int(rng.choice([0, -2, -3, -4, -5]))
+    ck = []
+    for L in lens:
+        cand = {L, L // 2, (L // 2 + 16) // 32 * 32, (L // 3 + 16) // 32 * 32 + 1, 1}
+        cand |= set(int(x) for x in rng.integers(1, max(L, 1) + 1, 3))
+        ck.append(sorted(p for p in cand if 1 <= p <= L))
+    s0 = None if seed == 1 else 0.1
+    w = inputs.prefill_workload(730 + seed, lens, 2, 128, 128, "bf16", s0_std=s0, g_min=WEAK)
+    w["checkpoints"] = ck
+    o, sf, pool, slots = _run(w, "bf16", 32, page_extra=4, dv_split=split)
+    _check(w, "bf16", o, sf, pool, slots, block=32)
