@@ -316,7 +316,9 @@ int kda_chunk_prefill_plan(kda_dtype in_dtype, int32_t H, int32_t dk, int32_t dv
  * kda_chunk_prefill for the same arguments) exceeds the array is refused
  * with KDA_EWORKSPACE before anything is enqueued.  The fused path (bf16,
  * chunk 32, dk 128) needs only its work list (about 50 KB for 16 sequences,
- * H = 32); the two-kernel path also needs its chunk records (66 KB per
+ * H = 32), and cuts long sequences into segments only where the array also
+ * holds their buffers (else it runs them whole); the two-kernel path also
+ * needs its chunk records (66 KB per
  * chunk and head at chunk 64, dk 128), so there it serves prefills of about
  * a thousand (chunk, head) pairs.  Every call on one GPU uses that GPU's one
  * array: calls that overlap on one GPU (other streams or host threads) race,
