@@ -73,6 +73,13 @@
 // the error flags and stops that chain at the barrier that would hand chunk x
 // over: the outputs and checkpoints of the chunks before x stay written,
 // nothing after them (nor the final state) is.
+//
+// Long sequences may arrive cut into segments (the host decides): a later
+// segment's chains run from the zero state and, as width code 4, from the
+// identity with v taken as zero, whose outputs are q mapped through the
+// segment's linear part.  The workgroups listed after the chains (the tail,
+// fused_tail below) then compose the segments' maps into their start states
+// and correct the later segments' outputs and checkpoints (kda_cp.hpp).
 #include <climits>
 #include <cstddef>
 #include <type_traits>
