@@ -97,13 +97,23 @@ __device__ __forceinline__ void fix_rows(const FixView& p, int lo, int len, int 
   Blk buf[kFixDepth];
 #pragma unroll
   for (int j = 0; j < kFixDepth; ++j) load(t0 + j * NB, buf[j]);
-  for (int e = tid; e < kFixD * kFixD / 4; e += 64 * NW) {
+  // (every load of S_in issued before the first store: one memory round trip)
+  constexpr int N4 = kFixD * kFixD / 4, IT = (N4 + 64 * NW - 1) / (64 * NW);
+  float4 sx[IT];
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const int e = tid + i * 64 * NW;
+    if (e < N4) sx[i] = *reinterpret_cast<const float4*>(&S[4 * e]);
+  }
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const int e = tid + i * 64 * NW;
+    if (e >= N4) continue;
     const int k = e / (kFixD / 4), n4 = 4 * (e % (kFixD / 4));
-    const float4 x = *reinterpret_cast<const float4*>(&S[k * kFixD + n4]);
-    st[(n4 + 0) * kStPitch + k] = static_cast<__bf16>(x.x);
-    st[(n4 + 1) * kStPitch + k] = static_cast<__bf16>(x.y);
-    st[(n4 + 2) * kStPitch + k] = static_cast<__bf16>(x.z);
-    st[(n4 + 3) * kStPitch + k] = static_cast<__bf16>(x.w);
+    st[(n4 + 0) * kStPitch + k] = static_cast<__bf16>(sx[i].x);
+    st[(n4 + 1) * kStPitch + k] = static_cast<__bf16>(sx[i].y);
+    st[(n4 + 2) * kStPitch + k] = static_cast<__bf16>(sx[i].z);
+    st[(n4 + 3) * kStPitch + k] = static_cast<__bf16>(sx[i].w);
   }
   __syncthreads();
   // Groups of kFixDepth blocks, unrolled so that every buffer is a fixed set
@@ -156,23 +166,37 @@ __device__ __forceinline__ void fix_state(float* dst, const float* X, const floa
   float* xs = reinterpret_cast<float*>(lds);
   float* ss = xs + kFixD * kXPitch;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l16 = lane & 15, g = lane >> 4;
-  for (int e = tid; e < kFixD * kFixD / 4; e += 64 * NW) {
+  // Loads of B (into the accumulators: D tile ct holds rows 16 wave + 4g + i,
+  // column 16 ct + l16), X and S_in all issued before the first LDS store:
+  // one memory round trip.
+  f32x4 acc[8];
+  if (wave < 8)
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[ct][i] = B[(16 * wave + 4 * g + i) * kFixD + 16 * ct + l16];
+  constexpr int N4 = kFixD * kFixD / 4, IT = (N4 + 64 * NW - 1) / (64 * NW);
+  float4 x[IT], y[IT];
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const int e = tid + i * 64 * NW;
+    if (e < N4) {
+      x[i] = *reinterpret_cast<const float4*>(&X[4 * e]);
+      y[i] = *reinterpret_cast<const float4*>(&S[4 * e]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < IT; ++i) {
+    const int e = tid + i * 64 * NW;
+    if (e >= N4) continue;
     const int r = e / (kFixD / 4), c4 = 4 * (e % (kFixD / 4));
-    const float4 x = *reinterpret_cast<const float4*>(&X[4 * e]);
-    const float4 y = *reinterpret_cast<const float4*>(&S[4 * e]);
     float* dx = &xs[r * kXPitch + c4];
     float* dy = &ss[r * kSPitch + c4];
-    dx[0] = x.x; dx[1] = x.y; dx[2] = x.z; dx[3] = x.w;
-    dy[0] = y.x; dy[1] = y.y; dy[2] = y.z; dy[3] = y.w;
+    dx[0] = x[i].x; dx[1] = x[i].y; dx[2] = x[i].z; dx[3] = x[i].w;
+    dy[0] = y[i].x; dy[1] = y[i].y; dy[2] = y[i].z; dy[3] = y[i].w;
   }
   __syncthreads();
   if (wave >= 8) return;
-  // D tile ct: rows 16 wave + 4g + i, column 16 ct + l16.
-  f32x4 acc[8];
-#pragma unroll
-  for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[ct][i] = B[(16 * wave + 4 * g + i) * kFixD + 16 * ct + l16];
   for (int ks = 0; ks < kFixD / 4; ++ks) {
     const int k = 4 * ks + g;
     const float a = xs[(16 * wave + l16) * kXPitch + k];
