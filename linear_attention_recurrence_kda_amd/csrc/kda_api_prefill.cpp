@@ -733,43 +733,14 @@ FusedList fused_list(const Plan& pl, const int32_t* cu, const int32_t* ck_cu, co
         wgs.push_back(static_cast<int32_t>((ch << 8) | (code << 4) | (code == 15 ? 0 : r)));
       }
   }
-  // Tail items: in the list after every chain they wait for (workgroups
-  // start in list order, so those have started when an item starts and its
-  // wait ends), at the point where, by the per-chunk times and list
-  // scheduling on the CUs, those chains are predicted to have ended: the
-  // items then take the CUs that the split sequence's chains leave, while
-  // the short chains after them fill the launch's end.
+  // Tail items: in the list after every chain (workgroups start in list
+  // order, so every chain an item waits for has started when the item
+  // starts, and its wait ends).  Last, rather than where the split
+  // sequences' chains are predicted to end: the short chains then start
+  // before the items, and the items (about 30 us each) fill the launch's
+  // end, where a chain of 100 us or more started behind them would not.
   const size_t n_items = titems.size() / kda::kTailInts;
-  if (n_items > 0) {
-    auto wg_entry = [&](int32_t x) { return (x >> 4 & 15) == 15 ? -1 : chains[2 * (x >> 8)]; };
-    auto wg_time = [&](int32_t x) { const int32_t i = wg_entry(x); return i < 0 ? 0.0 : ctime(i); };
-    // Predicted starts of the chains' workgroups (list scheduling on the
-    // CUs, a min-heap of their free times), and the predicted end of the
-    // split sequences' chains.
-    std::vector<double> cu_free(kCUs, 0.0), start(wgs.size());
-    double ready = 0;
-    size_t last_dep = 0;
-    for (size_t k = 0; k < wgs.size(); ++k) {
-      std::pop_heap(cu_free.begin(), cu_free.end(), std::greater<double>());
-      start[k] = cu_free.back();
-      cu_free.back() = start[k] + wg_time(wgs[k]);
-      std::push_heap(cu_free.begin(), cu_free.end(), std::greater<double>());
-      const int32_t i = wg_entry(wgs[k]);
-      if (i >= 0 && split(i)) {
-        ready = std::max(ready, start[k] + wg_time(wgs[k]));
-        last_dep = k + 1;
-      }
-    }
-    size_t at = wgs.size();
-    for (size_t k = last_dep; k < wgs.size(); ++k)
-      if (start[k] >= ready) {
-        at = k;
-        break;
-      }
-    std::vector<int32_t> items;
-    for (size_t t = 0; t < n_items; ++t) items.push_back(static_cast<int32_t>((t << 8) | (5 << 4)));
-    wgs.insert(wgs.begin() + static_cast<std::ptrdiff_t>(at), items.begin(), items.end());
-  }
+  for (size_t t = 0; t < n_items; ++t) wgs.push_back(static_cast<int32_t>((t << 8) | (5 << 4)));
   f.n_wg = static_cast<int64_t>(wgs.size());
   // One block: header (word 0: the decay-range flag, zero), then the parts.
   f.w.assign(kHeaderInts, 0);
