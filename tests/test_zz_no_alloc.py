@@ -26,9 +26,10 @@ def _arr(xs):
     return (I32 * max(1, len(xs)))(*xs)
 
 
-def _call(w, chunk, static):
-    """One prefill of workload w (bf16, S0, a checkpoint per sequence) through
-    kda_chunk_prefill_static or kda_chunk_prefill with a fresh workspace."""
+def _call(w, chunk, static, ck=None):
+    """One prefill of workload w (bf16, S0; checkpoints ck per sequence, by
+    default one at min(length, 40)) through kda_chunk_prefill_static or
+    kda_chunk_prefill with a fresh workspace."""
     L = kda.lib()
     cu = [int(x) for x in w["cu_seqlens"]]
     N, T = len(cu) - 1, cu[-1]
@@ -36,10 +37,12 @@ def _call(w, chunk, static):
     dv = w["v"].shape[2]
     t = {n: dev_tensor(w[n], "bf16") for n in ("q", "k", "v", "a", "beta")}
     s0 = torch.from_numpy(w["s0"]).cuda()
-    ck_pos = [min(int(L_), 40) for L_ in np.diff(cu)]  # one checkpoint per sequence (no empty ones here)
+    if ck is None:
+        ck = [[min(int(L_), 40)] for L_ in np.diff(cu)]  # one checkpoint per sequence (no empty ones here)
+    ck_pos = [p for c in ck for p in c]
     assert min(ck_pos) > 0
-    ck_cu = list(range(N + 1))
-    n_ck = N
+    ck_cu = [0] + np.cumsum([len(c) for c in ck]).tolist()
+    n_ck = len(ck_pos)
     slots = list(range(n_ck))[::-1]
     pool = torch.full((n_ck, H * dk * dv), float("nan"), device="cuda")
     o = torch.full((T, H, dv), float("nan"), dtype=torch.bfloat16, device="cuda")
@@ -60,7 +63,6 @@ def _call(w, chunk, static):
     assert st == kda.KDA_OK, L.kda_last_error()
     torch.cuda.synchronize()
     assert int(flag.item()) == 0
-    ck = [[p] for p in ck_pos]
     return o, sf, pool, slots, ck
 
 
@@ -82,6 +84,30 @@ def test_static_matches_workspace_entry_twice(chunk):
         assert_parity(sf_s, sf_r, "bf16", "s_final")
         for n, (p,) in enumerate(ck):
             assert_parity(pool_s[slots[n]].reshape(sf_r[n].shape), ck_r[n][p], "bf16", f"ckpt seq {n}")
+
+
+def test_static_matches_workspace_entry_with_segments():
+    """A sequence long enough to be cut into segments (three, whose buffers fit
+    the static array at H=4), checkpoints in its first and later segments: two
+    calls in a row, the second smaller, bit for bit against the workspace
+    entry, and at the oracle's bar."""
+    big = inputs.prefill_workload(600, [3000, 40], 4, 128, 128, "bf16", s0_std=0.1)
+    small = inputs.prefill_workload(601, [2100, 9], 4, 128, 128, "bf16", s0_std=0.1)
+    for w, ck in ((big, [[500, 1500, 2900, 3000], [40]]), (small, [[700, 1900], [9]])):
+        _, names = kda.prefill_plan(w["cu_seqlens"], 4, 128, 128, 32, ck)
+        assert "segments" in names
+        o_s, sf_s, pool_s, slots, _ = _call(w, 32, static=True, ck=ck)
+        o_w, sf_w, pool_w, _, _ = _call(w, 32, static=False, ck=ck)
+        assert torch.equal(o_s, o_w) and torch.equal(sf_s, sf_w) and torch.equal(pool_s, pool_w)
+        o_r, sf_r, ck_r = oracle.kda_prefill(w["q"], w["k"], w["v"], w["a"], w["beta"], w["cu_seqlens"],
+                                             w["s0"], ck)
+        assert_parity(o_s, o_r, "bf16", "o")
+        assert_parity(sf_s, sf_r, "bf16", "s_final")
+        n = 0
+        for s, ps in enumerate(ck):
+            for p in ps:
+                assert_parity(pool_s[slots[n]].reshape(sf_r[s].shape), ck_r[s][p], "bf16", f"ckpt seq {s} at {p}")
+                n += 1
 
 
 def test_static_refuses_a_call_beyond_its_scratch():
