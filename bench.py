@@ -7,7 +7,9 @@ dk=dv=128, bf16 inputs, fp32 states from nonzero committed S0, 32-token
 chunks (the fused kernel), checkpoints at every 4096 tokens plus the exact
 tail written into page slots) followed by packing the 16 final states into
 page slots.  `value` is that step's whole-job throughput in tokens/s with
-inputs resident in HBM.
+inputs resident in HBM.  Outside the timed steps, that part also reports
+("settled") the same calls timed again after --settled more untimed ones:
+after idle time the GPU's clocks ramp over the first twenty or so calls.
 
 In the same run, and reported under "parts": the same varlen prefill on the
 two-kernel path at chunk 64, the single-sequence prefill (T=8192, chunk 64,
@@ -22,7 +24,7 @@ decode batch's 256 states (537 MB, past the 256 MB Infinity Cache), each
 with its algorithmic bytes or flops against the MI355X peaks, plus the
 float64 CPU oracle timed on a bounded sample on the host's cores.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only a,b] [--no-cpu]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only a,b] [--no-cpu] [--settled N]
 """
 import argparse
 import hashlib
@@ -150,7 +152,7 @@ def committed_traffic(name, kernel_src):
 
 
 # ---------------------------------------------------------------- parts
-def bench_prefill(torch, kda, inputs, w, steps, warmup, pack_final, label, gate=False, chunk=64):
+def bench_prefill(torch, kda, inputs, w, steps, warmup, pack_final, label, gate=False, chunk=64, settled=0):
     d = {n: torch.from_numpy(w[n]).to(torch.bfloat16).cuda() for n in ("q", "k", "v", "a", "beta")}
     g_min = None
     if gate:
@@ -195,6 +197,13 @@ def bench_prefill(torch, kda, inputs, w, steps, warmup, pack_final, label, gate=
     ms, kms = run_steps(torch, step, steps, warmup)
     flops = prefill_flops(T, H, dk, dv, chunk)
     byts = prefill_bytes(T, H, dk, dv, N, n_ck, s0=s0 is not None)
+    # (informational, outside the timed steps: the same call again after
+    # `settled` more untimed calls, once the clocks have left their ramp)
+    settled_res = None
+    if settled > 0:
+        _, kms2 = run_steps(torch, step, steps, settled)
+        settled_res = {"after_calls": warmup + steps + settled, "kernel_ms": kms2,
+                       "hbm_frac": byts / (kms2 * 1e-3) / 1e9 / HBM_PEAK_GBS}
     res = {
         "workload": label, "kernels": kernels, "chunk": chunk, "tokens": T, "n_seqs": N, "n_ckpt": n_ck,
         "ms_per_step": ms, "kernel_ms": kms,
@@ -209,6 +218,8 @@ def bench_prefill(torch, kda, inputs, w, steps, warmup, pack_final, label, gate=
     # roofline: min(peak MFMA, I * BW) with I = flops / bytes
     t_roof = max(flops / (BF16_PEAK_TFLOPS * 1e12), byts / (HBM_PEAK_GBS * 1e9))
     res["roofline_frac"] = t_roof / (kms * 1e-3)
+    if settled_res is not None:
+        res["settled"] = settled_res
     del d, pool, o, sf, ws
     return res
 
@@ -663,6 +674,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settled", type=int, default=100,
+                    help="after the timed steps of the headline prefill, this many more untimed calls, then the "
+                         "same steps timed again and reported beside them as 'settled' (informational; skipped "
+                         "for runs of fewer than 10 steps, such as the profiler's)")
     ap.add_argument("--only", default="", help="comma list of: prefill4, prefill4_c64, prefill4_gated, prefill3, "
                                                "prefill3_c32, segments, front_end, decode, decode_bf16, replay, replay_big, "
                                                "replay_big_bf16, ring, pack, copycal")
@@ -710,7 +725,8 @@ def main():
     if want("prefill4"):
         log("prefill (varlen) ...")
         parts["prefill_varlen"] = bench_prefill(torch, kda, inputs, w4, args.steps, args.warmup, True,
-                                                varlen.format(HEAD_CHUNK), chunk=HEAD_CHUNK)
+                                                varlen.format(HEAD_CHUNK), chunk=HEAD_CHUNK,
+                                                settled=args.settled if args.steps >= 10 else 0)
     if want("prefill4_c64"):
         log("prefill (varlen, chunk 64) ...")
         parts["prefill_varlen_chunk64"] = bench_prefill(torch, kda, inputs, w4, args.steps, args.warmup, True,
