@@ -564,6 +564,7 @@ struct FusedList {
   size_t chains = 0, seqinfo = 0, segx = 0, ck_pos = 0, ck_slot = 0, wgs = 0, titems = 0, tcnt = 0;
   int64_t n_chains = 0, n_wg = 0, n_cnt = 0;
   int64_t n_tstate = 0, n_xpool = 0, n_qrows = 0;  // states of H*dk*dv fp32; qhat rows of H*dk bf16
+  bool items_fit = true;  // the tail items' indices fit their 23 bits of a workgroup entry
   size_t list_bytes() const { return align256(w.size() * 4); }
 };
 
@@ -740,7 +741,8 @@ FusedList fused_list(const Plan& pl, const int32_t* cu, const int32_t* ck_cu, co
   // before the items, and the items (about 30 us each) fill the launch's
   // end, where a chain of 100 us or more started behind them would not.
   const size_t n_items = titems.size() / kda::kTailInts;
-  for (size_t t = 0; t < n_items; ++t) wgs.push_back(static_cast<int32_t>((t << 8) | (5 << 4)));
+  f.items_fit = n_items < (size_t{1} << 23);
+  for (size_t t = 0; t < n_items && f.items_fit; ++t) wgs.push_back(static_cast<int32_t>((t << 8) | (5 << 4)));
   f.n_wg = static_cast<int64_t>(wgs.size());
   // One block: header (word 0: the decay-range flag, zero), then the parts.
   f.w.assign(kHeaderInts, 0);
@@ -865,10 +867,11 @@ int prefill_impl(const void* q, const void* k, const void* v, const void* a, con
   size_t need = list_bytes + (pl.fused ? 0 : tile_bytes(n_chunks, H, chunk, dk, es));
   FusedList fl;
   if (pl.fused) {
-    // Split sequences only where the workspace holds their buffers.
+    // Split sequences only where the workspace holds their buffers (and
+    // their tail items can be indexed).
     fl = fused_list(pl, cu, ck_cu, ck_pos, ck_slot, H, dv, s_final != nullptr);
     need = fl.list_bytes() + (fl.n_tstate + fl.n_xpool) * hkv * 4 + align256(fl.n_qrows * H * dk * 2);
-    if (pl.cp && workspace_bytes < need) {
+    if (pl.cp && (workspace_bytes < need || !fl.items_fit)) {
       st = make_plan(in_dtype, H, dk, dv, chunk, cu, n_seqs, ck_cu, ck_pos, n_ckpt, dv_split, summary, pl, false);
       if (st) return st;
       fl = fused_list(pl, cu, ck_cu, ck_pos, ck_slot, H, dv, s_final != nullptr);
