@@ -219,3 +219,25 @@ def test_segments_random_shapes(seed):
     w["checkpoints"] = ck
     o, sf, pool, slots = _run(w, "bf16", 32, page_extra=4, dv_split=split)
     _check(w, "bf16", o, sf, pool, slots, block=32)
+
+
+@pytest.mark.parametrize("kind", ["const", "uniform"])
+def test_segments_at_the_decay_bound(kind):
+    """a = -5 (the bound at 32-token chunks) on every channel of every token,
+    or uniform in [-5, 0]: a sequence in three segments beside a whole one,
+    nonzero S0, checkpoints on both sides of the cuts; the identity chains
+    and the corrections at the widest exponents the chunk form admits, against
+    the oracle."""
+    lens = [2100, 700]
+    w = inputs.prefill_workload(720, lens, 2, 128, 128, "bf16", s0_std=0.1)
+    rng = np.random.default_rng(720)
+    a = np.full(w["a"].shape, -5.0, np.float32) if kind == "const" else \
+        rng.uniform(-5.0, 0.0, w["a"].shape).astype(np.float32)
+    w["a"] = torch.from_numpy(a).to(torch.bfloat16).float().numpy()  # (the values the device reads)
+    assert w["a"].min() >= -5.0
+    w["checkpoints"] = _ckpts(lens)
+    _, names = kda.prefill_plan(w["cu_seqlens"], 2, 128, 128, 32, w["checkpoints"], dv_split=-3)
+    assert "1 sequence in 3 segments" in names, names
+    o, sf, pool, slots = _run(w, "bf16", 32, page_extra=8, dv_split=-3)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(sf).all()
+    _check(w, "bf16", o, sf, pool, slots, block=32)
